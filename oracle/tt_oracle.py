@@ -1,0 +1,263 @@
+"""CPU oracle for TT-EmbeddingBag -- TEST INFRASTRUCTURE ONLY.
+
+Floating-point side: ``tt_oracle.c`` (plain double loops over the definition of
+the TT table, EmbeddingBag pooling, the product-rule backward and plain SGD),
+loaded here through ctypes.  Integer side (index split, bag ids, the grouping
+order, cache frequency counts, top-K selection, slot lookup): plain numpy / dict
+code in this file.
+
+Pages followed ("FBTT-Embedding" README unless stated):
+  * "Initialization": core shapes R_{k-1} x p_k x q_k x R_k, ranks [1]+tt_ranks+[1].
+  * "Parameters": prod(p) >= num_embeddings, prod(q) == embedding_dim; `sparse`
+    fuses the weight update into the backward pass.
+  * README intro + "EmbeddingBag and Product-Key Memory Layers" (tensorflow/addons
+    #2201): EmbeddingBag = gather + (weighted) sum per bag.
+  * "Software Cache": hits read decompressed rows; the frequency of every lookup
+    is counted and the cache is (re)filled from the most frequent rows on
+    `cache_populate()`, each row initialised from the TT cores.
+  * "TableBatchedTTEmbeddingBag": T tables of one shape in one call.
+
+Readings where the pages are silent: row-major mixed radix for the index split;
+offsets carry a terminal entry; duplicates sum; the cache is filled with the K
+most frequent indices, ties broken by the smaller index, slot = rank in that
+order; one count per occurrence.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "tt_oracle.c")
+_SO = os.path.join(_HERE, "libtt_oracle.so")
+
+__all__ = ["build", "forward", "backward", "sgd", "tt_row", "split_index", "bag_ids",
+           "route_order", "group_counts", "count_frequencies", "select_cache",
+           "lookup_slots", "populate_rows"]
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc (plain -O2, no fast-math)."""
+    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+        tmp = _SO + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared",
+                               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("num_tables", ctypes.c_int32), ("num_embeddings", ctypes.c_int64),
+                ("p", ctypes.c_int32 * 3), ("q", ctypes.c_int32 * 3),
+                ("r", ctypes.c_int32 * 2)]
+
+
+_lib = None
+
+
+def _L():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        P = ctypes.c_void_p
+        lib.oracle_forward.argtypes = [P, P, P, ctypes.c_int64, P, ctypes.c_int64, P, P, P,
+                                       ctypes.c_int64, P]
+        lib.oracle_forward.restype = ctypes.c_int
+        lib.oracle_backward.argtypes = [P, P, P, ctypes.c_int64, P, ctypes.c_int64, P, P,
+                                        ctypes.c_int64, P, P, P, P, P]
+        lib.oracle_backward.restype = ctypes.c_int
+        lib.oracle_sgd_core.argtypes = [P, ctypes.c_int, P, P, P, ctypes.c_double]
+        lib.oracle_sgd_rows.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_double]
+        lib.oracle_tt_row.argtypes = [P, P, P, P, ctypes.c_int64, P]
+        _lib = lib
+    return _lib
+
+
+def _shape(p, q, ranks, E, T):
+    s = _Shape()
+    s.num_tables = int(T)
+    s.num_embeddings = int(E)
+    for k in range(3):
+        s.p[k] = int(p[k])
+        s.q[k] = int(q[k])
+    s.r[0], s.r[1] = int(ranks[0]), int(ranks[1])
+    return s
+
+
+def _ptr(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _ptr_array(arrs):
+    arr = (ctypes.c_void_p * len(arrs))()
+    for i, a in enumerate(arrs):
+        arr[i] = a.ctypes.data
+    return arr
+
+
+def tt_row(p, q, ranks, cores3, i: int) -> np.ndarray:
+    """One row W[i, :] (float64) of a single table, straight from the definition."""
+    c = [_f32(x) for x in cores3]
+    s = _shape(p, q, ranks, int(np.prod(p)), 1)
+    out = np.zeros(int(np.prod(q)), dtype=np.float64)
+    _L().oracle_tt_row(ctypes.byref(s), _ptr(c[0]), _ptr(c[1]), _ptr(c[2]), int(i), _ptr(out))
+    return out
+
+
+def forward(p, q, ranks, E, cores, indices, offsets, num_bags, per_sample_weights=None,
+            slots=None, cache_rows=None):
+    """EmbeddingBag forward over the implicit TT table(s).
+
+    cores: list of T lists [G1, G2, G3] in the logical layout.  Returns Y as
+    float64 [T*num_bags, D]."""
+    T = len(cores)
+    flat = [_f32(c) for tbl in cores for c in tbl]
+    s = _shape(p, q, ranks, E, T)
+    idx = np.ascontiguousarray(indices, dtype=np.int64)
+    off = np.ascontiguousarray(offsets, dtype=np.int64)
+    psw = None if per_sample_weights is None else _f32(per_sample_weights)
+    sl = None if slots is None else np.ascontiguousarray(slots, dtype=np.int32)
+    cr = None if cache_rows is None else _f32(cache_rows)
+    csize = 0 if cr is None else cr.shape[0]
+    D = int(np.prod(q))
+    Y = np.zeros((T * num_bags, D), dtype=np.float64)
+    rc = _L().oracle_forward(ctypes.byref(s), _ptr_array(flat), _ptr(idx), len(idx), _ptr(off),
+                             int(num_bags), _ptr(psw), _ptr(sl), _ptr(cr), csize, _ptr(Y))
+    if rc != 0:
+        raise ValueError("oracle_forward: invalid input")
+    return Y
+
+
+def backward(p, q, ranks, E, cores, indices, offsets, num_bags, grad_out,
+             per_sample_weights=None, slots=None, cache_size=0):
+    """Gradients of L = sum_b <dY[b], Y[b]>.
+
+    Returns (grads, touched, grad_cache, touched_cache): grads is a list of T lists
+    of float64 arrays in the logical core layout, touched a list of T lists of
+    uint8 masks over the slices p_k."""
+    T = len(cores)
+    flat = [_f32(c) for tbl in cores for c in tbl]
+    s = _shape(p, q, ranks, E, T)
+    idx = np.ascontiguousarray(indices, dtype=np.int64)
+    off = np.ascontiguousarray(offsets, dtype=np.int64)
+    psw = None if per_sample_weights is None else _f32(per_sample_weights)
+    sl = None if slots is None else np.ascontiguousarray(slots, dtype=np.int32)
+    dY = _f32(grad_out)
+    grads = [[np.zeros(c.shape, dtype=np.float64) for c in tbl] for tbl in cores]
+    touched = [[np.zeros(p[k], dtype=np.uint8) for k in range(3)] for _ in cores]
+    D = int(np.prod(q))
+    gc = np.zeros((cache_size, D), dtype=np.float64) if sl is not None else None
+    tc = np.zeros(cache_size, dtype=np.uint8) if sl is not None else None
+    rc = _L().oracle_backward(ctypes.byref(s), _ptr_array(flat), _ptr(idx), len(idx), _ptr(off),
+                              int(num_bags), _ptr(psw), _ptr(sl), int(cache_size), _ptr(dY),
+                              _ptr_array([g for tbl in grads for g in tbl]),
+                              _ptr_array([m for tbl in touched for m in tbl]),
+                              _ptr(gc), _ptr(tc))
+    if rc != 0:
+        raise ValueError("oracle_backward: invalid input")
+    return grads, touched, gc, tc
+
+
+def sgd(p, q, ranks, E, cores, grads, touched, lr, cache_rows=None, grad_cache=None,
+        touched_cache=None):
+    """Plain SGD on touched slices (copies): returns (new_cores, new_cache_rows)."""
+    T = len(cores)
+    s = _shape(p, q, ranks, E, T)
+    new = [[_f32(c).copy() for c in tbl] for tbl in cores]
+    for t in range(T):
+        for k in range(3):
+            _L().oracle_sgd_core(ctypes.byref(s), k, _ptr(new[t][k]),
+                                 _ptr(np.ascontiguousarray(grads[t][k])),
+                                 _ptr(np.ascontiguousarray(touched[t][k])), float(lr))
+    rows = None
+    if cache_rows is not None:
+        rows = _f32(cache_rows).copy()
+        _L().oracle_sgd_rows(_ptr(rows), _ptr(np.ascontiguousarray(grad_cache)),
+                             _ptr(np.ascontiguousarray(touched_cache)), rows.shape[0],
+                             rows.shape[1], float(lr))
+    return new, rows
+
+
+# ---------------------------------------------------------------- integer side
+
+def split_index(p, indices):
+    """Row-major mixed-radix split i -> (i1, i2, i3) by div/mod."""
+    i = np.asarray(indices, dtype=np.int64)
+    return i // (p[1] * p[2]), (i // p[2]) % p[1], i % p[2]
+
+
+def bag_ids(offsets, nnz):
+    """bag(n) = upper_bound(offsets, n) - 1 over the CSR offsets."""
+    return np.searchsorted(np.asarray(offsets, dtype=np.int64), np.arange(nnz), side="right") - 1
+
+
+def route_order(p, E, num_tables, num_bags, indices, offsets, slots=None):
+    """The grouping order of the elements, as a plain stable sort.
+
+    Misses (no cache slot) first, ordered by (table, i2, i1) and, for equal keys,
+    by position n; then cache hits ordered by (slot, n).  Elements with an index
+    outside [0, E) are left out.  Returns (order, group_counts) where
+    group_counts[t*p2 + i2] counts the misses of each (table, i2) group."""
+    idx = np.asarray(indices, dtype=np.int64)
+    nnz = len(idx)
+    b = bag_ids(offsets, nnz)
+    t = b // num_bags
+    i1, i2, _ = split_index(p, idx)
+    keys_miss, keys_hit = [], []
+    for n in range(nnz):
+        hit = slots is not None and slots[n] >= 0
+        if hit:
+            keys_hit.append((int(slots[n]), n))
+        elif 0 <= idx[n] < E:
+            keys_miss.append((int(t[n]), int(i2[n]), int(i1[n]), n))
+    keys_miss.sort()
+    keys_hit.sort()
+    order = [k[-1] for k in keys_miss] + [k[-1] for k in keys_hit]
+    counts = np.zeros(num_tables * p[1], dtype=np.int64)
+    for k in keys_miss:
+        counts[k[0] * p[1] + k[1]] += 1
+    return np.asarray(order, dtype=np.int64), counts
+
+
+def group_counts(p, num_tables, num_bags, indices, offsets):
+    """Number of elements per (table, i2) group (misses only, no cache)."""
+    _, c = route_order(p, np.iinfo(np.int64).max, num_tables, num_bags, indices, offsets)
+    return c
+
+
+def count_frequencies(batches, counts=None):
+    """One count per occurrence of each index over the given index arrays."""
+    counts = {} if counts is None else counts
+    for arr in batches:
+        for v in np.asarray(arr, dtype=np.int64).tolist():
+            counts[v] = counts.get(v, 0) + 1
+    return counts
+
+
+def select_cache(counts: dict, cache_size: int):
+    """The cached indices in slot order: the cache_size most frequent ones,
+    ordered by count descending then index ascending; slot = position."""
+    items = sorted(counts.items(), key=lambda kv: (-kv[1], kv[0]))
+    return np.asarray([k for k, _ in items[:cache_size]], dtype=np.int64)
+
+
+def lookup_slots(cached, indices):
+    """slot of each index in the cached list, -1 for a miss."""
+    pos = {int(v): s for s, v in enumerate(np.asarray(cached).tolist())}
+    return np.asarray([pos.get(int(v), -1) for v in np.asarray(indices).tolist()], dtype=np.int32)
+
+
+def populate_rows(p, q, ranks, cores3, cached):
+    """Decompressed rows for the cached indices (float64 [K, D])."""
+    D = int(np.prod(q))
+    out = np.zeros((len(cached), D), dtype=np.float64)
+    for s, i in enumerate(np.asarray(cached).tolist()):
+        out[s] = tt_row(p, q, ranks, cores3, i)
+    return out

@@ -1,0 +1,468 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each test states what it pins the oracle against: a closed form, a textbook
+algorithm, a library routine on a special case, an invariant, brute force on
+tiny inputs, or a value printed on the pages (fixtures under tests/golden/).
+A plausible mistake in the oracle (a swapped index order, a transposed core, a
+dropped term, a wrong sign, a lost per-sample weight, an off-by-one bag) fails at
+least one of them; test_pins_catch_planted_mistakes checks that on purpose by
+planting such mistakes into a copy of the oracle's C source (on the CPU only).
+"""
+import itertools
+import os
+import subprocess
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tensor_train_compressed_ttembeddingbag_amd import metrics, workloads as W
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _rand_cores(rng, p, q, ranks, std=0.7):
+    full = (1,) + tuple(ranks) + (1,)
+    return [(rng.standard_normal((full[k], p[k], q[k], full[k + 1])) * std).astype(np.float32)
+            for k in range(3)]
+
+
+def _dense_rows(p, q, ranks, cores3, E=None):
+    E = int(np.prod(p)) if E is None else E
+    return np.stack([oracle.tt_row(p, q, ranks, cores3, i) for i in range(E)])
+
+
+# --------------------------------------------------------------- the table W
+
+def test_rank_one_table_is_kronecker_product():
+    """Closed form: with ranks (1,1), W = kron(M1, kron(M2, M3)) where M_k is core k
+    reshaped p_k x q_k.  numpy.kron orders rows and columns row-major, so this pins
+    the mixed-radix split of both i and j, and that every core enters once."""
+    rng = _rng(11)
+    p, q = (3, 4, 5), (2, 3, 2)
+    cores = _rand_cores(rng, p, q, (1, 1))
+    M = [c.reshape(p[k], q[k]).astype(np.float64) for k, c in enumerate(cores)]
+    Wk = np.kron(M[0], np.kron(M[1], M[2]))
+    Wo = _dense_rows(p, q, (1, 1), cores)
+    np.testing.assert_allclose(Wo, Wk, rtol=1e-13, atol=1e-15)
+
+
+def _tt_svd(Wt, p, q):
+    """TT-SVD (Oseledets 2011) of a (prod p) x (prod q) matrix viewed as a
+    3-way tensor with modes (i_k, j_k), full ranks: exact up to rounding."""
+    X = Wt.reshape(p[0], p[1], p[2], q[0], q[1], q[2]).transpose(0, 3, 1, 4, 2, 5)
+    C = X.reshape(p[0] * q[0], -1)
+    U, S, Vt = np.linalg.svd(C, full_matrices=False)
+    r1 = int(np.sum(S > 1e-12 * S[0]))
+    G1 = U[:, :r1].reshape(1, p[0], q[0], r1)
+    C = (S[:r1, None] * Vt[:r1]).reshape(r1 * p[1] * q[1], p[2] * q[2])
+    U, S, Vt = np.linalg.svd(C, full_matrices=False)
+    r2 = int(np.sum(S > 1e-12 * S[0]))
+    G2 = U[:, :r2].reshape(r1, p[1], q[1], r2)
+    G3 = (S[:r2, None] * Vt[:r2]).reshape(r2, p[2], q[2], 1)
+    return [G1, G2, G3], (r1, r2)
+
+
+def test_tt_svd_round_trip():
+    """Textbook algorithm: TT-SVD of a random dense 120 x 8 table (tiny workload
+    shape) gives cores of ranks (8, 12) whose oracle rows rebuild the table.  The
+    cores are rounded to fp32 for the oracle, so agreement is to fp32 rounding."""
+    rng = _rng(12)
+    p, q = (4, 5, 6), (2, 2, 2)
+    Wd = rng.standard_normal((120, 8))
+    cores64, ranks = _tt_svd(Wd, p, q)
+    assert ranks == (8, 12)
+    cores = [c.astype(np.float32) for c in cores64]
+    Wo = _dense_rows(p, q, ranks, cores)
+    assert np.max(np.abs(Wo - Wd)) < 1e-5 * np.max(np.abs(Wd))
+
+
+def test_degenerate_tt_is_plain_embedding_bag():
+    """Special case -> library routine: p=(E,1,1), q=(D,1,1), ranks=(1,1) and unit
+    cores 2 and 3 make W = core 1, so the oracle must equal torch's EmbeddingBag
+    (sum mode, per-sample weights) on that table."""
+    rng = _rng(13)
+    E, D = 37, 6
+    p, q = (E, 1, 1), (D, 1, 1)
+    G1 = rng.standard_normal((1, E, D, 1)).astype(np.float32)
+    G2 = np.ones((1, 1, 1, 1), np.float32)
+    G3 = np.ones((1, 1, 1, 1), np.float32)
+    idx = rng.integers(0, E, 50).astype(np.int64)
+    off = np.array([0, 3, 3, 10, 21, 50], dtype=np.int64)
+    w = rng.random(50).astype(np.float32)
+    Y = oracle.forward(p, q, (1, 1), E, [[G1, G2, G3]], idx, off, 5, per_sample_weights=w)
+    ref = torch.nn.functional.embedding_bag(
+        torch.from_numpy(idx), torch.from_numpy(G1.reshape(E, D).astype(np.float64)),
+        torch.from_numpy(off[:-1]), mode="sum",
+        per_sample_weights=torch.from_numpy(w.astype(np.float64)))
+    np.testing.assert_allclose(Y, ref.numpy(), rtol=1e-13, atol=1e-13)
+
+
+def test_pooling_matches_torch_embedding_bag_on_decompressed_table():
+    """Library routine: pool with torch's EmbeddingBag over the oracle's own rows.
+    Rows are pinned above; this pins bag membership, weights, empty bags and the
+    table-major layout of several tables."""
+    rng = _rng(14)
+    p, q, ranks, T, B = (3, 4, 2), (2, 1, 3), (3, 2), 2, 6
+    E = 22  # < prod(p) = 24: the last rows are unaddressable
+    cores = [_rand_cores(rng, p, q, ranks) for _ in range(T)]
+    lens = np.array([0, 2, 5, 1, 0, 3, 4, 4, 0, 1, 2, 7])
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    idx = rng.integers(0, E, off[-1]).astype(np.int64)
+    w = rng.random(off[-1]).astype(np.float32)
+    Y = oracle.forward(p, q, ranks, E, cores, idx, off, B, per_sample_weights=w)
+    for t in range(T):
+        dense = torch.from_numpy(_dense_rows(p, q, ranks, cores[t], E))
+        sl = slice(t * B, (t + 1) * B)
+        lo, hi = off[t * B], off[(t + 1) * B]
+        ref = torch.nn.functional.embedding_bag(
+            torch.from_numpy(idx[lo:hi]), dense, torch.from_numpy(off[t * B:(t + 1) * B] - lo),
+            mode="sum", per_sample_weights=torch.from_numpy(w[lo:hi].astype(np.float64)))
+        np.testing.assert_allclose(Y[sl], ref.numpy(), rtol=1e-13, atol=1e-13)
+    assert np.all(Y[lens == 0] == 0.0)
+
+
+def test_pooling_invariants():
+    """Invariants: a bag is the sum of its one-index bags; scaling weights scales
+    the output; permuting a bag's elements changes only rounding."""
+    rng = _rng(15)
+    wl = W.WORKLOADS["tiny"]
+    cores = W.make_cores(wl)
+    b = W.make_batch(wl, 0)
+    args = (wl.p, wl.q, wl.ranks, wl.E, cores)
+    Y = oracle.forward(*args, b["indices"], b["offsets"], 8)
+    ones = np.arange(len(b["indices"]) + 1, dtype=np.int64)
+    Y1 = oracle.forward(*args, b["indices"], ones, len(b["indices"]))
+    bag = oracle.bag_ids(b["offsets"], len(b["indices"]))
+    Ysum = np.zeros_like(Y)
+    np.add.at(Ysum, bag, Y1)
+    np.testing.assert_allclose(Y, Ysum, rtol=1e-12, atol=1e-14)
+    w = np.full(len(b["indices"]), 0.25, np.float32)
+    Yw = oracle.forward(*args, b["indices"], b["offsets"], 8, per_sample_weights=w)
+    np.testing.assert_allclose(Yw, 0.25 * Y, rtol=1e-14, atol=1e-15)
+    perm = np.concatenate([rng.permutation(np.arange(b["offsets"][k], b["offsets"][k + 1]))
+                           for k in range(8)])
+    Yp = oracle.forward(*args, b["indices"][perm], b["offsets"], 8)
+    np.testing.assert_allclose(Yp, Y, rtol=1e-12, atol=1e-14)
+
+
+def test_readme_embedding_sum_example_semantics():
+    """Value printed on the pages (semantics only; the printed numbers come from an
+    unseeded init): input [1,2,4,5,4,3,2,9], offsets [0,4] -> output [2,3], bag 0 =
+    rows {1,2,4,5}, bag 1 = rows {4,3,2,9}.  The shape p=(2,5,1), q=(3,1,1) is one
+    factorisation of a 10 x 3 table (the page lets the module choose it)."""
+    g = {}
+    for line in open(os.path.join(GOLD, "readme_embedding_sum_example.txt")):
+        if line.strip() and not line.startswith("#"):
+            k, *v = line.split()
+            g[k] = [int(x) for x in v]
+    E, D = g["num_embeddings"][0], g["embedding_dim"][0]
+    ranks = tuple(g["tt_ranks"])
+    p, q = (2, 5, 1), (3, 1, 1)
+    rng = _rng(16)
+    cores = _rand_cores(rng, p, q, ranks)
+    idx = np.array(g["input"], dtype=np.int64)
+    off = np.array(g["offsets"] + [len(idx)], dtype=np.int64)
+    Y = oracle.forward(p, q, ranks, E, [cores], idx, off, 2)
+    assert list(Y.shape) == g["out_shape"]
+    for b, key in enumerate(["bag0", "bag1"]):
+        ref = sum(oracle.tt_row(p, q, ranks, cores, i) for i in g[key])
+        np.testing.assert_allclose(Y[b], ref, rtol=1e-14, atol=1e-15)
+
+
+# --------------------------------------------------------------- backward
+
+def _loss(p, q, ranks, E, cores, idx, off, B, dY, w=None):
+    Y = oracle.forward(p, q, ranks, E, cores, idx, off, B, per_sample_weights=w)
+    return float(np.sum(Y * dY.astype(np.float64)))
+
+
+def test_backward_equals_exact_finite_differences():
+    """Invariant: L = sum <dY, Y> is affine in any single core entry (each term of W
+    has one factor per core), so a secant through two fp32-representable values
+    of that entry gives the partial derivative exactly up to rounding."""
+    rng = _rng(17)
+    p, q, ranks, E, B = (3, 2, 4), (2, 3, 2), (3, 2), 24, 5
+    cores = [_rand_cores(rng, p, q, ranks)]
+    lens = np.array([3, 0, 6, 2, 9])
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    idx = rng.integers(0, E, off[-1]).astype(np.int64)
+    idx[:4] = idx[4]  # duplicates must add up
+    w = rng.random(off[-1]).astype(np.float32)
+    dY = rng.standard_normal((B, 12)).astype(np.float32)
+    grads, touched, _, _ = oracle.backward(p, q, ranks, E, cores, idx, off, B, dY,
+                                           per_sample_weights=w)
+    for k in range(3):
+        G = cores[0][k]
+        for flat in rng.choice(G.size, size=min(G.size, 12), replace=False):
+            pert = [c.copy() for c in cores[0]]
+            a0 = float(G.flat[flat])
+            a1 = float(np.float32(a0 + 0.5))
+            pert[k].flat[flat] = np.float32(a1)
+            l0 = _loss(p, q, ranks, E, cores, idx, off, B, dY, w)
+            l1 = _loss(p, q, ranks, E, [pert], idx, off, B, dY, w)
+            fd = (l1 - l0) / (a1 - a0)
+            assert abs(fd - grads[0][k].flat[flat]) <= 1e-10 * (1 + abs(fd)), (k, flat)
+
+
+def test_backward_matches_torch_autograd():
+    """Library routine: torch.autograd (float64) through a dense rebuild of W
+    written as an einsum, then torch's EmbeddingBag.  Pins every core gradient,
+    two tables, per-sample weights and the touched masks."""
+    rng = _rng(18)
+    p, q, ranks, E, B, T = (4, 3, 2), (2, 2, 3), (3, 4), 23, 4, 2
+    cores = [_rand_cores(rng, p, q, ranks) for _ in range(T)]
+    lens = np.array([2, 5, 0, 4, 3, 1, 6, 2])
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    idx = rng.integers(0, E, off[-1]).astype(np.int64)
+    w = rng.random(off[-1]).astype(np.float32)
+    dY = rng.standard_normal((T * B, 12)).astype(np.float32)
+    grads, touched, _, _ = oracle.backward(p, q, ranks, E, cores, idx, off, B, dY,
+                                           per_sample_weights=w)
+    for t in range(T):
+        G = [torch.tensor(c.astype(np.float64), requires_grad=True) for c in cores[t]]
+        Wt = torch.einsum("aipr,rjqs,skvb->ijkpqv", *G).reshape(int(np.prod(p)), 12)[:E]
+        lo, hi = off[t * B], off[(t + 1) * B]
+        Y = torch.nn.functional.embedding_bag(
+            torch.from_numpy(idx[lo:hi]), Wt, torch.from_numpy(off[t * B:(t + 1) * B] - lo),
+            mode="sum", per_sample_weights=torch.from_numpy(w[lo:hi].astype(np.float64)))
+        (Y * torch.from_numpy(dY[t * B:(t + 1) * B].astype(np.float64))).sum().backward()
+        i1, i2, i3 = oracle.split_index(p, idx[lo:hi])
+        for k, ik in enumerate((i1, i2, i3)):
+            np.testing.assert_allclose(grads[t][k], G[k].grad.numpy(), rtol=1e-11, atol=1e-12)
+            assert set(np.flatnonzero(touched[t][k])) == set(ik.tolist())
+
+
+def test_sgd_step_invariants():
+    """Invariants of one SGD step: delta = -lr * grad on touched slices (to fp32
+    rounding of the new value), untouched slices bit-identical, and for small lr
+    the loss falls by lr * |grad|^2 to first order (L is multilinear in the cores)."""
+    wl = W.WORKLOADS["tiny"]
+    cores = W.make_cores(wl)
+    b = W.make_batch(wl, 0)
+    args = (wl.p, wl.q, wl.ranks, wl.E)
+    grads, touched, _, _ = oracle.backward(*args, cores, b["indices"], b["offsets"], 8,
+                                           b["grad_out"])
+    lr = 1e-3
+    new, _ = oracle.sgd(*args, cores, grads, touched, lr)
+    for k in range(3):
+        old, nw, g = cores[0][k], new[0][k], grads[0][k]
+        axis_slices = np.moveaxis(np.arange(old.size).reshape(old.shape), 1, 0)
+        for ik in range(wl.p[k]):
+            sel = axis_slices[ik].ravel()
+            if touched[0][k][ik]:
+                exp = (old.ravel()[sel].astype(np.float64) - lr * g.ravel()[sel]).astype(np.float32)
+                assert np.array_equal(nw.ravel()[sel], exp)
+            else:
+                assert np.array_equal(nw.ravel()[sel].view(np.uint32), old.ravel()[sel].view(np.uint32))
+    l0 = _loss(*args, cores, b["indices"], b["offsets"], 8, b["grad_out"])
+    eps = 1e-6
+    new_e, _ = oracle.sgd(*args, cores, grads, touched, eps)
+    new_e64 = [[c.astype(np.float64) for c in tbl] for tbl in new_e]
+    gnorm = sum(float(np.sum(g * g)) for g in grads[0])
+    l1 = _loss(*args, [[c.astype(np.float32) for c in new_e64[0]]], b["indices"], b["offsets"],
+               8, b["grad_out"])
+    assert abs((l0 - l1) - eps * gnorm) < 0.05 * eps * gnorm
+
+
+def test_cache_semantics():
+    """Right after populate, a hit reads exactly the TT row; its gradient goes to
+    the cache row (sum of w * dY) and not to the cores."""
+    rng = _rng(19)
+    wl = W.WORKLOADS["tiny"]
+    cores = W.make_cores(wl)
+    b = W.make_batch(wl, 0)
+    idx, off = b["indices"], b["offsets"]
+    counts = oracle.count_frequencies([idx, idx[:5]])
+    cached = oracle.select_cache(counts, 6)
+    rows = oracle.populate_rows(wl.p, wl.q, wl.ranks, cores[0], cached).astype(np.float32)
+    slots = oracle.lookup_slots(cached, idx)
+    assert np.any(slots >= 0) and np.any(slots < 0)
+    args = (wl.p, wl.q, wl.ranks, wl.E, cores, idx, off, 8)
+    Y0 = oracle.forward(*args)
+    Yc = oracle.forward(*args, slots=slots, cache_rows=rows)
+    np.testing.assert_allclose(Yc, Y0, rtol=1e-6, atol=1e-6)
+    w = rng.random(len(idx)).astype(np.float32)
+    g, tch, gc, tc = oracle.backward(*args, b["grad_out"], per_sample_weights=w, slots=slots,
+                                     cache_size=6)
+    bag = oracle.bag_ids(off, len(idx))
+    ref = np.zeros((6, wl.D))
+    for n in range(len(idx)):
+        if slots[n] >= 0:
+            ref[slots[n]] += float(w[n]) * b["grad_out"][bag[n]].astype(np.float64)
+    np.testing.assert_allclose(gc, ref, rtol=1e-14, atol=1e-15)
+    miss = slots < 0
+    g2, _, _, _ = oracle.backward(*args[:5], idx[miss],
+                                  np.concatenate([[0], np.cumsum(np.bincount(bag[miss], minlength=8))]),
+                                  8, b["grad_out"], per_sample_weights=w[miss])
+    for k in range(3):
+        np.testing.assert_allclose(g[0][k], g2[0][k], rtol=1e-13, atol=1e-15)
+
+
+# --------------------------------------------------------------- integer side
+
+def test_split_index_brute_force():
+    """Brute force: enumerating (i1,i2,i3) in itertools.product order lists the
+    rows in row-major mixed radix."""
+    p = (3, 4, 5)
+    allidx = list(itertools.product(range(p[0]), range(p[1]), range(p[2])))
+    i1, i2, i3 = oracle.split_index(p, np.arange(60))
+    assert list(zip(i1.tolist(), i2.tolist(), i3.tolist())) == allidx
+
+
+def test_bag_ids_and_route_order_brute_force():
+    """Brute force: bag ids by a linear walk over the offsets; the grouping order
+    by checking every adjacent pair and that it is a permutation of the valid
+    elements."""
+    rng = _rng(20)
+    p, E, T, B = (3, 4, 5), 55, 2, 7
+    lens = rng.integers(0, 5, T * B)
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    idx = rng.integers(-2, E + 3, off[-1]).astype(np.int64)
+    slots = np.where(rng.random(off[-1]) < 0.3, rng.integers(0, 4, off[-1]), -1).astype(np.int32)
+    bag = oracle.bag_ids(off, len(idx))
+    walk = []
+    for b in range(T * B):
+        walk += [b] * int(lens[b])
+    assert bag.tolist() == walk
+    order, counts = oracle.route_order(p, E, T, B, idx, off, slots)
+    valid = [n for n in range(len(idx)) if slots[n] >= 0 or 0 <= idx[n] < E]
+    assert sorted(order.tolist()) == valid
+
+    def key(n):
+        t = bag[n] // B
+        if slots[n] >= 0:
+            return (1, int(slots[n]), 0, n)
+        return (0, int(t * p[1] + (idx[n] // p[2]) % p[1]), int(idx[n] // (p[1] * p[2])), n)
+    ks = [key(n) for n in order]
+    assert all(a < b for a, b in zip(ks, ks[1:]))
+    assert counts.sum() == sum(1 for n in valid if slots[n] < 0)
+
+
+def test_cache_selection_brute_force():
+    """Brute force: every selected index is at least as frequent as every
+    unselected one, ties go to the smaller index, and slots follow (count desc,
+    index asc)."""
+    rng = _rng(21)
+    arr = rng.integers(0, 30, 200)
+    counts = {}
+    for v in arr.tolist():
+        counts[v] = counts.get(v, 0) + 1
+    assert oracle.count_frequencies([arr]) == counts
+    K = 9
+    sel = oracle.select_cache(counts, K).tolist()
+    assert len(sel) == K
+    rest = [v for v in counts if v not in sel]
+    for a in sel:
+        for b in rest:
+            assert counts[a] > counts[b] or (counts[a] == counts[b] and a < b)
+    for a, b in zip(sel, sel[1:]):
+        assert counts[a] > counts[b] or (counts[a] == counts[b] and a < b)
+    sl = oracle.lookup_slots(sel, np.array([sel[3], 999, sel[0]]))
+    assert sl.tolist() == [3, -1, 0]
+
+
+# --------------------------------------------------------------- pages' numbers
+
+def _kv(name):
+    g = {}
+    for line in open(os.path.join(GOLD, name)):
+        if line.strip() and not line.startswith("#"):
+            k, *v = line.split()
+            g[k] = v
+    return g
+
+
+def test_core_shapes_match_initialization_example():
+    """Value printed on the pages: the core shapes of the "Initialization" example."""
+    g = _kv("core_shapes_init_example.txt")
+    wl = W.custom(p=[int(x) for x in g["p"]], q=[int(x) for x in g["q"]],
+                  ranks=[int(x) for x in g["ranks"]])
+    shapes = W.core_shapes(wl)
+    for k in range(3):
+        assert tuple(shapes[k]) == tuple(int(x) for x in g["core%d" % k])
+
+
+def test_flop_convention_matches_readme_benchmark_line():
+    """Values printed on the pages: the README benchmark's GFLOPS / BW equals
+    (F1 + F2) / (4 D) = 144 at its shape, and GFLOPS x time/nnz is 30 (F1 + F2), i.e.
+    3 (F1 + F2) per fwd+bwd (the count the benchmark here uses) times 10."""
+    g = _kv("readme_benchmark_line.txt")
+    q = [int(x) for x in g["q_shapes"]]
+    ranks = [int(x) for x in g["ranks"]]
+    D = int(g["D"][0])
+    F = metrics.fwd_flops_per_nnz(q, ranks)
+    assert F == 36864
+    gflops, bw, t = float(g["gflops"][0]), float(g["bw"][0]), float(g["time_per_nnz_us"][0])
+    assert abs(gflops / bw - F / (4 * D)) < 0.01
+    ratio = gflops * 1e9 * t * 1e-6 / F
+    assert 29.9 < ratio < 30.1
+    assert metrics.step_flops_per_nnz(q, ranks) * 10 == 30 * F
+    assert int(g["nnz"][0]) == int(g["B"][0]) * 20
+    assert int(np.prod([int(x) for x in g["p_shapes"]])) == int(g["E"][0])
+
+
+# --------------------------------------------------------------- planted mistakes
+
+_MUTANTS = [
+    # wrong index order in the row split
+    ("out[2] = i % p[2];", "out[2] = i / ((int64_t)p[1] * p[0]) % p[2];"),
+    # transposed core-2 access (r1 <-> r2 roles)
+    ("* core_at(s, G2, 1, r1, ii[1], j2, r2)", "* core_at(s, G2, 1, r2 % s->r[0], ii[1], j2, r1 % s->r[1])"),
+    # column split in the wrong order
+    ("row[(j1 * q[1] + j2) * q[2] + j3] = acc;", "row[(j3 * q[1] + j2) * q[0] + j1] = acc;"),
+    # per-sample weight dropped in the forward
+    ("Y[b * D + j] += w * row[j];", "Y[b * D + j] += row[j];"),
+    # wrong sign of one gradient
+    ("d3[core_index(s, 2, r2, ii[2], j3, 0)] += g * a * m;",
+     "d3[core_index(s, 2, r2, ii[2], j3, 0)] -= g * a * m;"),
+    # dropped factor in the core-1 gradient
+    ("d1[core_index(s, 0, 0, ii[0], j1, r1)] += g * m * c;",
+     "d1[core_index(s, 0, 0, ii[0], j1, r1)] += g * m;"),
+    # off-by-one bag: table of a bag
+    ("const int64_t t = b / B;\n        for (int64_t n = off[b]; n < off[b + 1]; ++n) {\n            const double w = psw ? (double)psw[n] : 1.0;\n            if (slot && slot[n] >= 0) {\n                for (int64_t j = 0; j < D; ++j) row[j]",
+     "const int64_t t = (b + 1) / B % s->num_tables;\n        for (int64_t n = off[b]; n < off[b + 1]; ++n) {\n            const double w = psw ? (double)psw[n] : 1.0;\n            if (slot && slot[n] >= 0) {\n                for (int64_t j = 0; j < D; ++j) row[j]"),
+]
+
+
+def _load_mutant(src, tmp_path, i):
+    c = tmp_path / ("m%d.c" % i)
+    so = tmp_path / ("m%d.so" % i)
+    c.write_text(src)
+    subprocess.check_call(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", str(c), "-o", str(so)])
+    return str(so)
+
+
+@pytest.mark.parametrize("mi", range(len(_MUTANTS)))
+def test_pins_catch_planted_mistakes(mi, tmp_path, monkeypatch):
+    """Plant one mistake into a copy of the oracle (CPU only) and check that the
+    pin suite above fails on it."""
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "tt_oracle.c")).read()
+    old, new = _MUTANTS[mi]
+    assert old in src, old
+    so = _load_mutant(src.replace(old, new, 1), tmp_path, mi)
+    import oracle.tt_oracle as O
+    saved = O._lib
+    O._lib = None
+    monkeypatch.setattr(O, "build", lambda force=False: so)
+    failures = 0
+    pins = [test_rank_one_table_is_kronecker_product, test_tt_svd_round_trip,
+            test_degenerate_tt_is_plain_embedding_bag,
+            test_pooling_matches_torch_embedding_bag_on_decompressed_table,
+            test_pooling_invariants, test_backward_equals_exact_finite_differences,
+            test_backward_matches_torch_autograd, test_sgd_step_invariants]
+    try:
+        for f in pins:
+            try:
+                f()
+            except (AssertionError, ValueError):
+                failures += 1
+    finally:
+        O._lib = saved
+    assert failures > 0, "planted mistake %d went unnoticed" % mi
