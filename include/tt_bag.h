@@ -1,0 +1,184 @@
+/*
+ * tt_bag.h -- C ABI of libttbag: TT-EmbeddingBag on AMD MI355X (gfx950).
+ *
+ * An EmbeddingBag whose num_embeddings x embedding_dim table W is never stored.
+ * "FBTT-Embedding" README, sections "Parameters" and "Initialization": W is held
+ * as three Tensor-Train cores; core k has logical shape R_{k-1} x p_k x q_k x R_k
+ * with ranks {1, R1, R2, 1}, prod(p) >= num_embeddings and prod(q) == embedding_dim.
+ * Row i splits into (i1,i2,i3) and column j into (j1,j2,j3), both row-major mixed
+ * radix (i = (i1*p2 + i2)*p3 + i3), and
+ *     W[i][j] = sum_{r1,r2} G1[0][i1][j1][r1] G2[r1][i2][j2][r2] G3[r2][i3][j3][0].
+ * The forward pass pools the requested rows per bag like PyTorch's EmbeddingBag
+ * (README intro; "EmbeddingBag and Product-Key Memory Layers", tensorflow/addons
+ * #2201: gather + weighted sum, without materialising the gathered rows).  The
+ * backward pass forms the core gradients and applies SGD in place ("Parameters",
+ * entry `sparse`; "Fused Kernel").  An optional HBM cache of decompressed rows
+ * serves frequent indices ("Software Cache").  Several tables of one shape can be
+ * batched in one call ("TableBatchedTTEmbeddingBag").
+ *
+ * Conventions for every entry point
+ *  - Pointers are DEVICE pointers unless the comment says host.  `stream` is a
+ *    hipStream_t (NULL = the default stream).  Every call is asynchronous on
+ *    `stream` and does not synchronise the host, except tt_cache_populate.
+ *  - Ownership: the caller owns every buffer it passes, including the workspace.
+ *    The library allocates device memory only inside tt_cache_create and frees it
+ *    only in tt_cache_destroy; it keeps no caller pointer between calls.
+ *  - Return value: TT_OK (0) or a negative TT_E* code.  A negative return means
+ *    the arguments were rejected on the host and NOTHING was enqueued.
+ *  - Content errors that only the device can see (an index outside [0, E), a
+ *    non-CSR offsets array, a cache slot outside [0, cache_size), a full count
+ *    table) OR bits into the sticky word *dev_status (device memory, never
+ *    cleared by the library).  The offending elements are skipped without any
+ *    out-of-bounds access; the outputs are then unspecified.
+ *  - One workspace must not be used by two calls that may run concurrently.
+ *
+ * Core storage (device, fp32): cores[k] points to T consecutive tables of core k,
+ * each stored slice-major [p_k][R_{k-1}][q_k][R_k], so the slice for one index
+ * i_k is contiguous.  (The pages give only the logical order R_{k-1} x p_k x q_k
+ * x R_k; slice-major is that order with the first two axes swapped.)
+ *
+ * Supported shapes (others return TT_ESHAPE): 1 <= T; 1 <= R1, R2 <= 64;
+ * q1 in {1, 2, 4}; 1 <= q2; 1 <= q3 <= 16; D <= 1024; T*p_k + 1 <= 8192 for each
+ * k (with a cache: T*p1 + 513 <= 8192); num_embeddings <= prod(p) < 2^40.
+ */
+#ifndef TT_BAG_H
+#define TT_BAG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define TT_OK          0
+#define TT_EINVAL     (-1)  /* null pointer, negative size, lr not finite, ...  */
+#define TT_ESHAPE     (-2)  /* descriptor inconsistent or outside the envelope */
+#define TT_EWORKSPACE (-3)  /* workspace too small or not 256-byte aligned     */
+#define TT_EHIP       (-4)  /* a HIP runtime call failed                       */
+#define TT_EFULL      (-5)  /* cache capacity exceeded at create               */
+
+/* bits OR-ed into *dev_status by the device */
+#define TT_DEV_BAD_INDEX   1  /* index < 0 or >= num_embeddings (element skipped) */
+#define TT_DEV_BAD_OFFSETS 2  /* offsets[0] != 0, offsets not non-decreasing, or
+                                 offsets[T*B] != nnz                             */
+#define TT_DEV_BAD_SLOT    4  /* cache slot >= cache_size (element skipped)       */
+#define TT_DEV_HASH_FULL   8  /* frequency table full: new keys were not counted  */
+
+/* Shape of one TT table ("Parameters": num_embeddings, embedding_dim = prod(q),
+ * tt_p_shapes, tt_q_shapes, tt_ranks) and the number of tables batched
+ * ("TableBatchedTTEmbeddingBag": num_tables, all of one shape). */
+typedef struct tt_desc {
+    int32_t num_tables;      /* T >= 1                                        */
+    int64_t num_embeddings;  /* E, 1 <= E <= p[0]*p[1]*p[2]                    */
+    int32_t p[3];            /* tt_p_shapes                                    */
+    int32_t q[3];            /* tt_q_shapes; embedding_dim D = q[0]*q[1]*q[2]  */
+    int32_t ranks[2];        /* tt_ranks (R1, R2); full ranks {1, R1, R2, 1}   */
+} tt_desc;
+
+/* A view of the software cache for one forward/backward call ("Software Cache").
+ * slots[n] >= 0 makes element n a hit: the forward reads rows[slots[n]] instead
+ * of the TT row, and the backward applies SGD to that row instead of the cores
+ * (write-back).  slots[n] < 0 is a miss.  Only with num_tables == 1. */
+typedef struct tt_cache_view {
+    const int32_t *slots;    /* [nnz], from tt_cache_lookup                    */
+    float *rows;             /* [cache_size][D] decompressed rows              */
+    int64_t cache_size;
+} tt_cache_view;
+
+/* Bytes of workspace that tt_bag_forward / tt_bag_backward_sgd / tt_bag_route
+ * need for nnz indices, num_bags bags per table and a cache of cache_size rows
+ * (0 = no cache).  Returns 0 if the descriptor is rejected. */
+size_t tt_bag_workspace_size(const tt_desc *desc, int64_t nnz, int64_t num_bags,
+                             int64_t cache_size);
+
+/*
+ * Forward (README "How FBTT-Embedding works": same semantics as EmbeddingBag's
+ * sum mode, with optional per-sample weights as in tensorflow/addons #2201).
+ *   indices  [nnz] int64, rows of each table in [0, E)
+ *   offsets  [T*num_bags + 1] int64, CSR: bag b holds positions
+ *            [offsets[b], offsets[b+1]); offsets[0] = 0, offsets[T*num_bags] = nnz.
+ *            Bags are table-major: bag b belongs to table b / num_bags.
+ *   per_sample_weights [nnz] fp32 or NULL (all ones)
+ *   cache    NULL, or a cache view (hits are pooled from cache rows)
+ *   out      [T*num_bags][D] fp32, fully overwritten; an empty bag gives zeros.
+ *   ws       workspace of ws_bytes >= tt_bag_workspace_size(...), 256-B aligned
+ */
+int tt_bag_forward(const tt_desc *desc, const float *const cores[3],
+                   const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                   int64_t num_bags, const float *per_sample_weights,
+                   const tt_cache_view *cache, float *out,
+                   void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
+
+/*
+ * Backward with fused SGD ("Parameters", `sparse`=True with OptimType.SGD;
+ * "Fused Kernel"): with L = sum_b <grad_out[b], out[b]>, computes the gradient of
+ * every core slice and cache row touched by this batch at the current values and
+ * applies  x <- x - lr * dL/dx  in place to exactly those slices/rows.  Gradients
+ * are not returned.  Duplicate indices add up.  No gradient with respect to the
+ * per-sample weights is formed.  Same argument meaning as tt_bag_forward;
+ * grad_out is [T*num_bags][D] fp32.  The result is bit-reproducible run to run
+ * (the reductions have a fixed order).
+ */
+int tt_bag_backward_sgd(const tt_desc *desc, float *const cores[3],
+                        const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                        int64_t num_bags, const float *per_sample_weights,
+                        const tt_cache_view *cache, const float *grad_out, float lr,
+                        void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
+
+/*
+ * The grouping step of both passes, exposed for inspection and tests: splits
+ * every index, finds its bag, and sorts the elements stably so that misses come
+ * first ordered by (table, i2, i1, i3) and then by position, followed by cache hits
+ * ordered by (slot, position), followed by the skipped elements by position.
+ *   order_out     [nnz] int32: element positions in that order
+ *   group_off_out [T*p2 + 2] int32: misses of group g = table*p2 + i2 occupy
+ *                 order_out[group_off_out[g] .. group_off_out[g+1]); hits occupy
+ *                 [group_off_out[T*p2], group_off_out[T*p2+1]).
+ */
+int tt_bag_route(const tt_desc *desc, const int64_t *indices, int64_t nnz,
+                 const int64_t *offsets, int64_t num_bags, const int32_t *slots,
+                 int64_t cache_size, int32_t *order_out, int32_t *group_off_out,
+                 void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
+
+/* ---------------------------------------------------------------- cache
+ * "Software Cache": the access frequency of every looked-up index is counted in
+ * an open-addressing hash table of hashtbl_size entries; tt_cache_populate fills
+ * the cache with the (at most cache_size) most frequent indices, ties broken by
+ * the smaller index, slot = rank in that order, each row decompressed from the
+ * current cores.  Counts are never reset.  The pages describe a 32-way
+ * set-associative LFU; this cache is fully associative exact top-K (the
+ * replacement policy only decides which rows are cached, not the arithmetic).
+ */
+typedef struct tt_cache tt_cache;
+
+/* Allocates the count table, the index->slot map and populate's scratch for a
+ * table of shape *desc (num_tables must be 1).  *out receives a host handle. */
+int tt_cache_create(tt_cache **out, const tt_desc *desc, int64_t cache_size,
+                    int64_t hashtbl_size);
+
+/* slot_out[n] = slot of indices[n] in the cache, or -1.  With count_freq != 0 every
+ * element with an index in [0, E) also adds one to its index's count. */
+int tt_cache_lookup(tt_cache *c, const int64_t *indices, int64_t nnz, int32_t *slot_out,
+                    int count_freq, int32_t *dev_status, void *stream);
+
+/* Re-selects the cached indices from the counts and writes their decompressed
+ * rows into rows[0 .. n_filled) ([cache_size][D] fp32).  *n_filled is a HOST
+ * pointer; this call synchronises `stream`. */
+int tt_cache_populate(tt_cache *c, const float *const cores[3], float *rows,
+                      int64_t *n_filled, void *stream);
+
+/* cached_out[s] = index held in slot s for s < n_filled (int64 device buffer of
+ * cache_size entries; entries past n_filled are -1). */
+int tt_cache_cached_indices(tt_cache *c, int64_t *cached_out, void *stream);
+
+int tt_cache_destroy(tt_cache *c);
+
+/* Static description of a return code. */
+const char *tt_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TT_BAG_H */

@@ -201,22 +201,22 @@ def bag_ids(offsets, nnz):
 def route_order(p, E, num_tables, num_bags, indices, offsets, slots=None):
     """The grouping order of the elements, as a plain stable sort.
 
-    Misses (no cache slot) first, ordered by (table, i2, i1) and, for equal keys,
-    by position n; then cache hits ordered by (slot, n).  Elements with an index
+    Misses (no cache slot) first, ordered by (table, i2, i1, i3) and, for equal
+    keys, by position n; then cache hits ordered by (slot, n).  Elements with an index
     outside [0, E) are left out.  Returns (order, group_counts) where
     group_counts[t*p2 + i2] counts the misses of each (table, i2) group."""
     idx = np.asarray(indices, dtype=np.int64)
     nnz = len(idx)
     b = bag_ids(offsets, nnz)
     t = b // num_bags
-    i1, i2, _ = split_index(p, idx)
+    i1, i2, i3 = split_index(p, idx)
     keys_miss, keys_hit = [], []
     for n in range(nnz):
         hit = slots is not None and slots[n] >= 0
         if hit:
             keys_hit.append((int(slots[n]), n))
         elif 0 <= idx[n] < E:
-            keys_miss.append((int(t[n]), int(i2[n]), int(i1[n]), n))
+            keys_miss.append((int(t[n]), int(i2[n]), int(i1[n]), int(i3[n]), n))
     keys_miss.sort()
     keys_hit.sort()
     order = [k[-1] for k in keys_miss] + [k[-1] for k in keys_hit]

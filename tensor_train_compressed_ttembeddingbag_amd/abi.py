@@ -1,0 +1,268 @@
+"""Thin ctypes binding of libttbag (the C ABI in include/tt_bag.h).
+
+Argument marshalling only: every function checks device/dtype/contiguity of the
+torch tensors it is handed, passes their device pointers and the current HIP
+stream to the C entry point of the same name, and raises ``TTError`` on a
+negative return code.  No arithmetic of the method happens here.  Loading fails
+loudly (``RuntimeError``) when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libttbag.so")
+
+TT_OK = 0
+TT_DEV_BAD_INDEX = 1
+TT_DEV_BAD_OFFSETS = 2
+TT_DEV_BAD_SLOT = 4
+TT_DEV_HASH_FULL = 8
+
+
+class TTError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__("%s failed: %d (%s)" % (fn, code, status_string(code)))
+        self.code = code
+
+
+class TTDesc(ctypes.Structure):
+    _fields_ = [("num_tables", ctypes.c_int32), ("num_embeddings", ctypes.c_int64),
+                ("p", ctypes.c_int32 * 3), ("q", ctypes.c_int32 * 3),
+                ("ranks", ctypes.c_int32 * 2)]
+
+
+class TTCacheView(ctypes.Structure):
+    _fields_ = [("slots", ctypes.c_void_p), ("rows", ctypes.c_void_p),
+                ("cache_size", ctypes.c_int64)]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SIG = {
+    "tt_bag_workspace_size": (ctypes.c_size_t, [_P, _I64, _I64, _I64]),
+    "tt_bag_forward": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P, _P, ctypes.c_size_t,
+                                      _P, _P]),
+    "tt_bag_backward_sgd": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P, ctypes.c_float,
+                                           _P, ctypes.c_size_t, _P, _P]),
+    "tt_bag_route": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _I64, _P, _P, _P, ctypes.c_size_t,
+                                    _P, _P]),
+    "tt_cache_create": (ctypes.c_int, [_P, _P, _I64, _I64]),
+    "tt_cache_lookup": (ctypes.c_int, [_P, _P, _I64, _P, ctypes.c_int, _P, _P]),
+    "tt_cache_populate": (ctypes.c_int, [_P, _P, _P, _P, _P]),
+    "tt_cache_cached_indices": (ctypes.c_int, [_P, _P, _P]),
+    "tt_cache_destroy": (ctypes.c_int, [_P]),
+    "tt_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+EXPORTS = tuple(_SIG)
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libttbag; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libttbag.so is not built (%s); run __graft_entry__.build() or "
+                               "python -m tensor_train_compressed_ttembeddingbag_amd.build" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIG.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().tt_status_string(int(code)).decode()
+
+
+def make_desc(p, q, ranks, num_embeddings: Optional[int] = None, num_tables: int = 1) -> TTDesc:
+    d = TTDesc()
+    d.num_tables = int(num_tables)
+    d.num_embeddings = int(num_embeddings if num_embeddings is not None else p[0] * p[1] * p[2])
+    for k in range(3):
+        d.p[k] = int(p[k])
+        d.q[k] = int(q[k])
+    d.ranks[0], d.ranks[1] = int(ranks[0]), int(ranks[1])
+    return d
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, dtype, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn: str, rc: int):
+    if rc != TT_OK:
+        raise TTError(fn, rc)
+
+
+def tt_bag_workspace_size(desc: TTDesc, nnz: int, num_bags: int, cache_size: int = 0) -> int:
+    n = lib().tt_bag_workspace_size(ctypes.byref(desc), int(nnz), int(num_bags), int(cache_size))
+    if n == 0:
+        raise TTError("tt_bag_workspace_size", -2)
+    return int(n)
+
+
+def workspace(desc: TTDesc, nnz: int, num_bags: int, cache_size: int = 0, device=None) -> torch.Tensor:
+    """A workspace tensor of the required size (torch's allocations are 256-B aligned)."""
+    n = tt_bag_workspace_size(desc, nnz, num_bags, cache_size)
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def _cores(cores: Sequence[torch.Tensor]):
+    if len(cores) != 3:
+        raise ValueError("three cores expected")
+    for k, c in enumerate(cores):
+        _need(c, torch.float32, "cores[%d]" % k)
+    return (ctypes.c_void_p * 3)(*[c.data_ptr() for c in cores])
+
+
+def _cache_view(cache):
+    if cache is None:
+        return None, None
+    slots, rows = cache
+    _need(slots, torch.int32, "cache slots")
+    _need(rows, torch.float32, "cache rows")
+    v = TTCacheView()
+    v.slots = slots.data_ptr()
+    v.rows = rows.data_ptr()
+    v.cache_size = rows.shape[0]
+    return v, rows.shape[0]
+
+
+def tt_bag_forward(desc: TTDesc, cores, indices, offsets, num_bags: int,
+                   per_sample_weights=None, cache=None, out=None, ws=None,
+                   dev_status=None, stream=None) -> torch.Tensor:
+    """out[T*num_bags, D] = pooled rows (see tt_bag.h).  cache = (slots, rows) or None."""
+    _need(indices, torch.int64, "indices")
+    _need(offsets, torch.int64, "offsets")
+    if per_sample_weights is not None:
+        _need(per_sample_weights, torch.float32, "per_sample_weights")
+    D = desc.q[0] * desc.q[1] * desc.q[2]
+    if out is None:
+        out = torch.empty(desc.num_tables * num_bags, D, dtype=torch.float32, device=indices.device)
+    _need(out, torch.float32, "out")
+    view, csize = _cache_view(cache)
+    if ws is None:
+        ws = workspace(desc, indices.numel(), num_bags, csize or 0, indices.device)
+    _need(ws, torch.uint8, "ws")
+    if dev_status is not None:
+        _need(dev_status, torch.int32, "dev_status")
+    rc = lib().tt_bag_forward(ctypes.byref(desc), _cores(cores), _ptr(indices), indices.numel(),
+                              _ptr(offsets), int(num_bags), _ptr(per_sample_weights),
+                              None if view is None else ctypes.byref(view), _ptr(out), _ptr(ws),
+                              ws.numel(), _ptr(dev_status), _stream(stream))
+    _check("tt_bag_forward", rc)
+    return out
+
+
+def tt_bag_backward_sgd(desc: TTDesc, cores, indices, offsets, num_bags: int, grad_out,
+                        lr: float, per_sample_weights=None, cache=None, ws=None,
+                        dev_status=None, stream=None) -> None:
+    """In-place fused SGD on the cores (and cache rows) touched by this batch."""
+    _need(indices, torch.int64, "indices")
+    _need(offsets, torch.int64, "offsets")
+    _need(grad_out, torch.float32, "grad_out")
+    if per_sample_weights is not None:
+        _need(per_sample_weights, torch.float32, "per_sample_weights")
+    view, csize = _cache_view(cache)
+    if ws is None:
+        ws = workspace(desc, indices.numel(), num_bags, csize or 0, indices.device)
+    _need(ws, torch.uint8, "ws")
+    if dev_status is not None:
+        _need(dev_status, torch.int32, "dev_status")
+    rc = lib().tt_bag_backward_sgd(ctypes.byref(desc), _cores(cores), _ptr(indices), indices.numel(),
+                                   _ptr(offsets), int(num_bags), _ptr(per_sample_weights),
+                                   None if view is None else ctypes.byref(view), _ptr(grad_out),
+                                   float(lr), _ptr(ws), ws.numel(), _ptr(dev_status),
+                                   _stream(stream))
+    _check("tt_bag_backward_sgd", rc)
+
+
+def tt_bag_route(desc: TTDesc, indices, offsets, num_bags: int, slots=None, cache_size: int = 0,
+                 ws=None, dev_status=None, stream=None):
+    """(order[nnz] int32, group_off[T*p2+2] int32) -- the grouping order (tt_bag.h)."""
+    _need(indices, torch.int64, "indices")
+    _need(offsets, torch.int64, "offsets")
+    if slots is not None:
+        _need(slots, torch.int32, "slots")
+    dev = indices.device
+    order = torch.empty(indices.numel(), dtype=torch.int32, device=dev)
+    goff = torch.empty(desc.num_tables * desc.p[1] + 2, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(desc, indices.numel(), num_bags, cache_size if slots is not None else 0, dev)
+    rc = lib().tt_bag_route(ctypes.byref(desc), _ptr(indices), indices.numel(), _ptr(offsets),
+                            int(num_bags), _ptr(slots), int(cache_size), _ptr(order), _ptr(goff),
+                            _ptr(ws), ws.numel(), _ptr(dev_status), _stream(stream))
+    _check("tt_bag_route", rc)
+    return order, goff
+
+
+class Cache:
+    """Owner of a tt_cache handle (frequency table + index->slot map)."""
+
+    def __init__(self, desc: TTDesc, cache_size: int, hashtbl_size: int):
+        self.desc = desc
+        self.cache_size = int(cache_size)
+        self._h = ctypes.c_void_p()
+        _check("tt_cache_create", lib().tt_cache_create(ctypes.byref(self._h), ctypes.byref(desc),
+                                                        int(cache_size), int(hashtbl_size)))
+
+    def lookup(self, indices, slot_out=None, count_freq: bool = True, dev_status=None,
+               stream=None) -> torch.Tensor:
+        _need(indices, torch.int64, "indices")
+        if slot_out is None:
+            slot_out = torch.empty(indices.numel(), dtype=torch.int32, device=indices.device)
+        _need(slot_out, torch.int32, "slot_out")
+        _check("tt_cache_lookup", lib().tt_cache_lookup(self._h, _ptr(indices), indices.numel(),
+                                                        _ptr(slot_out), 1 if count_freq else 0,
+                                                        _ptr(dev_status), _stream(stream)))
+        return slot_out
+
+    def populate(self, cores, rows, stream=None) -> int:
+        _need(rows, torch.float32, "rows")
+        n = ctypes.c_int64(0)
+        _check("tt_cache_populate", lib().tt_cache_populate(self._h, _cores(cores), _ptr(rows),
+                                                            ctypes.byref(n), _stream(stream)))
+        return int(n.value)
+
+    def cached_indices(self, stream=None) -> torch.Tensor:
+        out = torch.empty(self.cache_size, dtype=torch.int64, device="cuda")
+        _check("tt_cache_cached_indices",
+               lib().tt_cache_cached_indices(self._h, _ptr(out), _stream(stream)))
+        return out
+
+    def close(self):
+        if self._h:
+            lib().tt_cache_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,419 @@
+// tt_api.hip -- the C ABI (include/tt_bag.h): argument checks, workspace layout,
+// launch sequence.  Device work lives in tt_route.hip, tt_fwd.hip, tt_bwd.hip and
+// tt_cache.hip.
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "tt_internal.h"
+
+namespace ttb {
+hipError_t cache_lookup_launch(const int64_t *idx, int nnz, int64_t E, long long *hkeys,
+                               int *hcnt, long long H, const long long *mkeys, const int *mslot,
+                               long long M, int32_t *slot_out, int count_freq, int32_t *status,
+                               hipStream_t s);
+hipError_t cache_compact_launch(const long long *hkeys, const int *hcnt, long long H, int kbits,
+                                unsigned long long *out, int *n_out, hipStream_t s);
+hipError_t radix_sort64(unsigned long long *a, unsigned long long *b, int n, int *hist,
+                        hipStream_t s);
+hipError_t cache_assign_launch(const unsigned long long *sorted, int nf, int kbits,
+                               int64_t cache_size, int64_t *cached, long long *mkeys, int *mslot,
+                               long long M, hipStream_t s);
+hipError_t iota64_launch(int64_t *a, long long n, hipStream_t s);
+}  // namespace ttb
+
+using namespace ttb;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+constexpr size_t LDS_LIMIT = 160 * 1024;
+std::atomic<unsigned> g_epoch{1};
+
+struct Plan {
+  DevArgs a;
+  int RP = 0;
+  size_t lds_fwd = 0, lds_bwd = 0;
+  size_t ws_total = 0;
+  // byte offsets inside the workspace
+  size_t o_ctr, o_hdr, o_einfo, o_histA, o_histB, o_histI3, o_orderI3, o_orderA, o_sn, o_sdA,
+      o_sdB, o_sdI3, o_sbag, o_pos, o_grp, o_chunk, o_f1, o_f3, o_p1, o_p3, o_frag, o_gacc;
+};
+
+size_t carve(size_t &cur, size_t bytes) {
+  const size_t o = cur;
+  cur += (bytes + ALIGN - 1) / ALIGN * ALIGN;
+  return o;
+}
+
+int make_plan(const tt_desc *d, int64_t nnz, int64_t num_bags, int64_t cache_size, Plan *P) {
+  if (!d || !P) return TT_EINVAL;
+  if (nnz < 0 || nnz >= (int64_t)1 << 30 || num_bags < 1 || cache_size < 0) return TT_EINVAL;
+  const int T = d->num_tables;
+  if (T < 1) return TT_ESHAPE;
+  for (int k = 0; k < 3; ++k)
+    if (d->p[k] < 1 || d->q[k] < 1) return TT_ESHAPE;
+  if (d->ranks[0] < 1 || d->ranks[1] < 1 || d->ranks[0] > 64 || d->ranks[1] > 64) return TT_ESHAPE;
+  if (!(d->q[0] == 1 || d->q[0] == 2 || d->q[0] == 4)) return TT_ESHAPE;
+  if (d->q[2] > MAXQ3) return TT_ESHAPE;
+  const int64_t D = (int64_t)d->q[0] * d->q[1] * d->q[2];
+  if (D > 1024) return TT_ESHAPE;
+  const double prodp = (double)d->p[0] * d->p[1] * d->p[2];
+  if (prodp >= 1099511627776.0) return TT_ESHAPE;  // 2^40
+  if (d->num_embeddings < 1 || (double)d->num_embeddings > prodp) return TT_ESHAPE;
+  const int has_cache = cache_size > 0;
+  if (has_cache && T != 1) return TT_ESHAPE;
+  const int64_t NB = (int64_t)T * num_bags;
+  if (NB >= (int64_t)1 << 30) return TT_EINVAL;
+  const int NHB = has_cache ? (int)((cache_size + HB - 1) / HB) : 0;
+  const int64_t binsA = (int64_t)T * d->p[0] + (has_cache ? HB : 0) + 1;
+  const int64_t binsB = (int64_t)T * d->p[1] + NHB + 1;
+  const int64_t binsI3 = (int64_t)T * d->p[2] + 1;
+  if (binsA > MAX_BINS || binsB > MAX_BINS || binsI3 > MAX_BINS) return TT_ESHAPE;
+
+  DevArgs &a = P->a;
+  memset(&a, 0, sizeof(a));
+  a.T = T;
+  a.p1 = d->p[0]; a.p2 = d->p[1]; a.p3 = d->p[2];
+  a.q1 = d->q[0]; a.q2 = d->q[1]; a.q3 = d->q[2];
+  a.R1 = d->ranks[0]; a.R2 = d->ranks[1];
+  a.D = (int)D;
+  a.E = d->num_embeddings;
+  a.B = (int)num_bags;
+  a.NB = (int)NB;
+  a.nnz = (int)nnz;
+  a.nblk = (int)((nnz + RB - 1) / RB);
+  a.binsA = (int)binsA; a.binsB = (int)binsB; a.binsI3 = (int)binsI3;
+  a.has_cache = has_cache;
+  a.cache_size = cache_size;
+  a.NHB = NHB;
+  const int Rmax = a.R1 > a.R2 ? a.R1 : a.R2;
+  P->RP = Rmax <= 16 ? 16 : (Rmax <= 32 ? 32 : 64);
+  P->lds_fwd = fwd_lds_bytes(P->RP);
+  int CHI = 64;
+  while (CHI > 1 && bwd_lds_bytes(P->RP, CHI, a.D, a.q3) > LDS_LIMIT) CHI >>= 1;
+  if (bwd_lds_bytes(P->RP, CHI, a.D, a.q3) > LDS_LIMIT || P->lds_fwd > LDS_LIMIT) return TT_ESHAPE;
+  a.CHI = CHI;
+  {
+    const int rows = NW * 16 * bwd_mbw(P->RP);
+    const int pairs = rows / a.q1;
+    a.CHPb = pairs < CHP ? pairs : CHP;
+  }
+  P->lds_bwd = bwd_lds_bytes(P->RP, CHI, a.D, a.q3);
+
+  const size_t n = (size_t)nnz, nb = (size_t)a.nblk, G = (size_t)T * a.p2;
+  size_t cur = 0;
+  P->o_ctr = carve(cur, 3 * sizeof(unsigned long long));
+  P->o_hdr = carve(cur, H_WORDS * sizeof(int));
+  P->o_einfo = carve(cur, n * sizeof(int4));
+  P->o_histA = carve(cur, (size_t)binsA * nb * 4);
+  P->o_histB = carve(cur, (size_t)binsB * nb * 4);
+  P->o_histI3 = carve(cur, (size_t)binsI3 * nb * 4);
+  P->o_orderI3 = carve(cur, n * 4);
+  P->o_orderA = carve(cur, n * 4);
+  P->o_sn = carve(cur, n * 4);
+  P->o_sdA = carve(cur, n * 4);
+  P->o_sdB = carve(cur, n * 4);
+  P->o_sdI3 = carve(cur, n * 4);
+  P->o_sbag = carve(cur, n * 4);
+  P->o_pos = carve(cur, n * 4);
+  P->o_grp = carve(cur, ((size_t)binsB + 1) * 4);
+  P->o_chunk = carve(cur, (G + 1) * 4);
+  P->o_f1 = carve(cur, n * 4);
+  P->o_f3 = carve(cur, n * 4);
+  P->o_p1 = carve(cur, n * (size_t)a.q1 * a.R1 * 4);
+  P->o_p3 = carve(cur, n * (size_t)a.R2 * a.q3 * 4);
+  P->o_frag = carve(cur, n * (size_t)a.D * 4);
+  P->o_gacc = carve(cur, G * (size_t)a.R1 * a.q2 * a.R2 * 4);
+  P->ws_total = cur;
+  return TT_OK;
+}
+
+void bind_ws(Plan *P, void *ws) {
+  char *b = (char *)ws;
+  DevArgs &a = P->a;
+  a.ctr = (unsigned long long *)(b + P->o_ctr);
+  a.hdr = (int *)(b + P->o_hdr);
+  a.einfo = (int4 *)(b + P->o_einfo);
+  a.histA = (int *)(b + P->o_histA);
+  a.histB = (int *)(b + P->o_histB);
+  a.histI3 = (int *)(b + P->o_histI3);
+  a.orderI3 = (int *)(b + P->o_orderI3);
+  a.orderA = (int *)(b + P->o_orderA);
+  a.s_n = (int *)(b + P->o_sn);
+  a.s_dA = (int *)(b + P->o_sdA);
+  a.s_dB = (int *)(b + P->o_sdB);
+  a.s_dI3 = (int *)(b + P->o_sdI3);
+  a.s_bag = (int *)(b + P->o_sbag);
+  a.pos_of = (int *)(b + P->o_pos);
+  a.grp_off = (int *)(b + P->o_grp);
+  a.chunk_pre = (int *)(b + P->o_chunk);
+  a.flag1 = (int *)(b + P->o_f1);
+  a.flag3 = (int *)(b + P->o_f3);
+  a.part1 = (float *)(b + P->o_p1);
+  a.part3 = (float *)(b + P->o_p3);
+  a.frag = (float *)(b + P->o_frag);
+  a.gacc = (float *)(b + P->o_gacc);
+  a.epoch = g_epoch.fetch_add(1);
+  if (a.epoch == 0) a.epoch = g_epoch.fetch_add(1);
+}
+
+int check_ws(const Plan &P, void *ws, size_t ws_bytes) {
+  if (!ws) return TT_EINVAL;
+  if (((uintptr_t)ws) % ALIGN) return TT_EWORKSPACE;
+  if (ws_bytes < P.ws_total) return TT_EWORKSPACE;
+  return TT_OK;
+}
+
+int set_cache(Plan *P, const tt_cache_view *cache, int64_t nnz) {
+  DevArgs &a = P->a;
+  if (!cache) return TT_OK;
+  if (cache->cache_size != a.cache_size) return TT_EINVAL;
+  if (cache->cache_size > 0 && (!cache->rows || (nnz > 0 && !cache->slots))) return TT_EINVAL;
+  a.slots = cache->slots;
+  a.crows = cache->rows;
+  return TT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *tt_status_string(int code) {
+  switch (code) {
+    case TT_OK: return "ok";
+    case TT_EINVAL: return "invalid argument (null pointer, negative size or non-finite value)";
+    case TT_ESHAPE: return "descriptor inconsistent or outside the supported shapes";
+    case TT_EWORKSPACE: return "workspace too small or not 256-byte aligned";
+    case TT_EHIP: return "HIP runtime error";
+    case TT_EFULL: return "cache capacity exceeded";
+    default: return "unknown status";
+  }
+}
+
+size_t tt_bag_workspace_size(const tt_desc *desc, int64_t nnz, int64_t num_bags,
+                             int64_t cache_size) {
+  Plan P;
+  if (make_plan(desc, nnz, num_bags, cache_size, &P) != TT_OK) return 0;
+  return P.ws_total;
+}
+
+static int finish(hipError_t e) { return e == hipSuccess ? TT_OK : TT_EHIP; }
+
+int tt_bag_forward(const tt_desc *desc, const float *const cores[3], const int64_t *indices,
+                   int64_t nnz, const int64_t *offsets, int64_t num_bags,
+                   const float *per_sample_weights, const tt_cache_view *cache, float *out,
+                   void *ws, size_t ws_bytes, int32_t *dev_status, void *stream) {
+  Plan P;
+  const int64_t csize = cache ? cache->cache_size : 0;
+  int rc = make_plan(desc, nnz, num_bags, csize, &P);
+  if (rc) return rc;
+  if (!cores || !cores[0] || !cores[1] || !cores[2] || !offsets || !out) return TT_EINVAL;
+  if (nnz > 0 && !indices) return TT_EINVAL;
+  if ((rc = check_ws(P, ws, ws_bytes))) return rc;
+  if ((rc = set_cache(&P, cache, nnz))) return rc;
+  bind_ws(&P, ws);
+  DevArgs &a = P.a;
+  a.idx = indices; a.off = offsets; a.psw = per_sample_weights;
+  a.G1 = (float *)cores[0]; a.G2 = (float *)cores[1]; a.G3 = (float *)cores[2];
+  a.Y = out; a.status = dev_status; a.fwd_mode = 1;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_route(a, s);
+  if (e == hipSuccess && a.nnz > 0) e = launch_fwd(a, P.RP, P.lds_fwd, s);
+  return finish(e);
+}
+
+int tt_bag_backward_sgd(const tt_desc *desc, float *const cores[3], const int64_t *indices,
+                        int64_t nnz, const int64_t *offsets, int64_t num_bags,
+                        const float *per_sample_weights, const tt_cache_view *cache,
+                        const float *grad_out, float lr, void *ws, size_t ws_bytes,
+                        int32_t *dev_status, void *stream) {
+  Plan P;
+  const int64_t csize = cache ? cache->cache_size : 0;
+  int rc = make_plan(desc, nnz, num_bags, csize, &P);
+  if (rc) return rc;
+  if (!cores || !cores[0] || !cores[1] || !cores[2] || !offsets || !grad_out) return TT_EINVAL;
+  if (nnz > 0 && !indices) return TT_EINVAL;
+  if (!std::isfinite(lr)) return TT_EINVAL;
+  if ((rc = check_ws(P, ws, ws_bytes))) return rc;
+  if ((rc = set_cache(&P, cache, nnz))) return rc;
+  if (nnz == 0) return TT_OK;
+  bind_ws(&P, ws);
+  DevArgs &a = P.a;
+  a.idx = indices; a.off = offsets; a.psw = per_sample_weights;
+  a.G1 = cores[0]; a.G2 = cores[1]; a.G3 = cores[2];
+  a.dY = grad_out; a.lr = lr; a.status = dev_status; a.fwd_mode = 0;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_route(a, s);
+  if (e == hipSuccess) e = launch_runsum(a, s);
+  if (e == hipSuccess) e = launch_bwd(a, P.RP, P.lds_bwd, s);
+  if (e == hipSuccess) e = launch_seg(a, s);
+  return finish(e);
+}
+
+// copies the grouping order: valid elements first (see tt_bag.h)
+__global__ void k_copy_route(const int *s_n, int nnz, const int *grp_off, int G, int binsB,
+                             int *order_out, int *group_off_out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nnz) order_out[i] = s_n[i];
+  if (i <= G) group_off_out[i] = grp_off[i];
+  if (i == G + 1) group_off_out[G + 1] = grp_off[binsB - 1];
+}
+
+int tt_bag_route(const tt_desc *desc, const int64_t *indices, int64_t nnz,
+                 const int64_t *offsets, int64_t num_bags, const int32_t *slots,
+                 int64_t cache_size, int32_t *order_out, int32_t *group_off_out, void *ws,
+                 size_t ws_bytes, int32_t *dev_status, void *stream) {
+  Plan P;
+  int rc = make_plan(desc, nnz, num_bags, slots ? cache_size : 0, &P);
+  if (rc) return rc;
+  if (!offsets || !order_out || !group_off_out || (nnz > 0 && !indices)) return TT_EINVAL;
+  if ((rc = check_ws(P, ws, ws_bytes))) return rc;
+  bind_ws(&P, ws);
+  DevArgs &a = P.a;
+  a.idx = indices; a.off = offsets; a.slots = slots; a.status = dev_status; a.fwd_mode = 0;
+  hipStream_t s = (hipStream_t)stream;
+  const int G = a.T * a.p2;
+  hipError_t e = hipSuccess;
+  if (nnz == 0) {
+    e = hipMemsetAsync(group_off_out, 0, (G + 2) * sizeof(int32_t), s);
+    return finish(e);
+  }
+  e = launch_route(a, s);
+  if (e == hipSuccess) {
+    const int n = (int)nnz > G + 2 ? (int)nnz : G + 2;
+    hipLaunchKernelGGL(k_copy_route, dim3((n + 255) / 256), dim3(256), 0, s, a.s_n, a.nnz,
+                       a.grp_off, G, a.binsB, order_out, group_off_out);
+    e = hipGetLastError();
+  }
+  return finish(e);
+}
+
+// ---------------------------------------------------------------- cache
+struct tt_cache {
+  tt_desc desc;
+  int64_t cache_size = 0, H = 0, M = 0;
+  int kbits = 1;
+  long long *hkeys = nullptr;
+  int *hcnt = nullptr;
+  long long *mkeys = nullptr;
+  int *mslot = nullptr;
+  int64_t *cached = nullptr;
+  unsigned long long *sk0 = nullptr, *sk1 = nullptr;
+  int *shist = nullptr;
+  int *nent = nullptr;
+  int64_t *bag_off = nullptr;
+  void *fws = nullptr;
+  size_t fws_bytes = 0;
+  int device = 0;
+};
+
+static void cache_free(tt_cache *c) {
+  if (!c) return;
+  void *ptrs[] = {c->hkeys, c->hcnt, c->mkeys, c->mslot, c->cached, c->sk0, c->sk1,
+                  c->shist, c->nent, c->bag_off, c->fws};
+  for (void *p : ptrs)
+    if (p) (void)hipFree(p);
+  delete c;
+}
+
+int tt_cache_create(tt_cache **out, const tt_desc *desc, int64_t cache_size,
+                    int64_t hashtbl_size) {
+  if (!out || !desc || cache_size < 1 || hashtbl_size < 1) return TT_EINVAL;
+  if (desc->num_tables != 1) return TT_ESHAPE;
+  if (cache_size >= (int64_t)1 << 29 || hashtbl_size >= (int64_t)1 << 31) return TT_EFULL;
+  Plan P;
+  int rc = make_plan(desc, cache_size, cache_size, 0, &P);
+  if (rc) return rc;
+  tt_cache *c = new (std::nothrow) tt_cache();
+  if (!c) return TT_EINVAL;
+  c->desc = *desc;
+  c->cache_size = cache_size;
+  c->H = hashtbl_size;
+  int64_t M = 1;
+  while (M < 2 * cache_size) M <<= 1;
+  c->M = M;
+  int kb = 1;
+  while (kb < 63 && ((int64_t)1 << kb) < desc->num_embeddings) ++kb;
+  c->kbits = kb;
+  c->fws_bytes = P.ws_total;
+  const size_t nsort = (size_t)hashtbl_size;
+  const size_t nblk = (nsort + RB - 1) / RB;
+  bool ok = hipGetDevice(&c->device) == hipSuccess;
+  ok = ok && hipMalloc(&c->hkeys, (size_t)c->H * 8) == hipSuccess;
+  ok = ok && hipMalloc(&c->hcnt, (size_t)c->H * 4) == hipSuccess;
+  ok = ok && hipMalloc(&c->mkeys, (size_t)M * 8) == hipSuccess;
+  ok = ok && hipMalloc(&c->mslot, (size_t)M * 4) == hipSuccess;
+  ok = ok && hipMalloc(&c->cached, (size_t)cache_size * 8) == hipSuccess;
+  ok = ok && hipMalloc(&c->sk0, nsort * 8) == hipSuccess;
+  ok = ok && hipMalloc(&c->sk1, nsort * 8) == hipSuccess;
+  ok = ok && hipMalloc(&c->shist, 256 * nblk * 4 + 4) == hipSuccess;
+  ok = ok && hipMalloc(&c->nent, 4) == hipSuccess;
+  ok = ok && hipMalloc(&c->bag_off, (size_t)(cache_size + 1) * 8) == hipSuccess;
+  ok = ok && hipMalloc(&c->fws, c->fws_bytes) == hipSuccess;
+  ok = ok && hipMemset(c->hkeys, 0xff, (size_t)c->H * 8) == hipSuccess;
+  ok = ok && hipMemset(c->hcnt, 0, (size_t)c->H * 4) == hipSuccess;
+  ok = ok && hipMemset(c->mkeys, 0xff, (size_t)M * 8) == hipSuccess;
+  ok = ok && hipMemset(c->cached, 0xff, (size_t)cache_size * 8) == hipSuccess;
+  ok = ok && iota64_launch(c->bag_off, cache_size + 1, nullptr) == hipSuccess;
+  ok = ok && hipDeviceSynchronize() == hipSuccess;
+  if (!ok) {
+    cache_free(c);
+    return TT_EHIP;
+  }
+  *out = c;
+  return TT_OK;
+}
+
+int tt_cache_lookup(tt_cache *c, const int64_t *indices, int64_t nnz, int32_t *slot_out,
+                    int count_freq, int32_t *dev_status, void *stream) {
+  if (!c || nnz < 0 || nnz >= (int64_t)1 << 30) return TT_EINVAL;
+  if (nnz > 0 && (!indices || !slot_out)) return TT_EINVAL;
+  return finish(cache_lookup_launch(indices, (int)nnz, c->desc.num_embeddings, c->hkeys, c->hcnt,
+                                    c->H, c->mkeys, c->mslot, c->M, slot_out, count_freq ? 1 : 0,
+                                    dev_status, (hipStream_t)stream));
+}
+
+int tt_cache_populate(tt_cache *c, const float *const cores[3], float *rows, int64_t *n_filled,
+                      void *stream) {
+  if (!c || !cores || !cores[0] || !cores[1] || !cores[2] || !rows || !n_filled) return TT_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemsetAsync(c->nent, 0, 4, s);
+  if (e == hipSuccess) e = cache_compact_launch(c->hkeys, c->hcnt, c->H, c->kbits, c->sk0, c->nent, s);
+  int n = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&n, c->nent, 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return TT_EHIP;
+  e = radix_sort64(c->sk0, c->sk1, n, c->shist, s);
+  const int nf = (int)(n < c->cache_size ? n : c->cache_size);
+  if (e == hipSuccess) e = hipMemsetAsync(c->mkeys, 0xff, (size_t)c->M * 8, s);
+  if (e == hipSuccess)
+    e = cache_assign_launch(c->sk0, nf, c->kbits, c->cache_size, c->cached, c->mkeys, c->mslot,
+                            c->M, s);
+  if (e != hipSuccess) return TT_EHIP;
+  if (nf > 0) {
+    int rc = tt_bag_forward(&c->desc, cores, c->cached, nf, c->bag_off, nf, nullptr, nullptr, rows,
+                            c->fws, c->fws_bytes, nullptr, stream);
+    if (rc) return rc;
+  }
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return TT_EHIP;
+  *n_filled = nf;
+  return TT_OK;
+}
+
+int tt_cache_cached_indices(tt_cache *c, int64_t *cached_out, void *stream) {
+  if (!c || !cached_out) return TT_EINVAL;
+  return finish(hipMemcpyAsync(cached_out, c->cached, (size_t)c->cache_size * 8,
+                               hipMemcpyDeviceToDevice, (hipStream_t)stream));
+}
+
+int tt_cache_destroy(tt_cache *c) {
+  if (!c) return TT_EINVAL;
+  (void)hipDeviceSynchronize();
+  cache_free(c);
+  return TT_OK;
+}
+
+}  // extern "C"

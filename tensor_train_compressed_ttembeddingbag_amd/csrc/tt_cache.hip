@@ -1,0 +1,221 @@
+// tt_cache.hip -- the software cache of decompressed rows.
+//
+// "FBTT-Embedding" README, "Software Cache": the most frequently queried rows are
+// kept uncompressed so that a hit skips the TT arithmetic; access frequencies are
+// counted in an open-addressing hash table (hashtbl_size entries) during lookups,
+// and the cache content changes only when populate is called, which picks rows by
+// frequency and initialises each from the TT cores.  Here: exact top-K by (count
+// descending, index ascending), slot = rank in that order; a second open-addressing
+// table maps index -> slot for lookups.
+#include "tt_device.h"
+
+namespace ttb {
+
+constexpr long long EMPTY_KEY = -1;
+
+// splitmix64 finalizer (Steele, Lea, Flood 2014) as the hash of an index.
+static __device__ __forceinline__ unsigned long long mix64(unsigned long long x) {
+  x ^= x >> 30;
+  x *= 0xbf58476d1ce4e5b9ull;
+  x ^= x >> 27;
+  x *= 0x94d049bb133111ebull;
+  x ^= x >> 31;
+  return x;
+}
+
+// find or insert key in the count table; returns the entry or -1 if the table is full
+static __device__ long long count_slot(long long *keys, long long H, long long key) {
+  long long h = (long long)(mix64((unsigned long long)key) % (unsigned long long)H);
+  for (long long probe = 0; probe < H; ++probe) {
+    const long long k = __atomic_load_n(&keys[h], __ATOMIC_RELAXED);
+    if (k == key) return h;
+    if (k == EMPTY_KEY) {
+      const long long prev = (long long)atomicCAS((unsigned long long *)&keys[h],
+                                                  (unsigned long long)EMPTY_KEY,
+                                                  (unsigned long long)key);
+      if (prev == EMPTY_KEY || prev == key) return h;
+    }
+    h = (h + 1 == H) ? 0 : h + 1;
+  }
+  return -1;
+}
+
+static __device__ int map_find(const long long *mkeys, const int *mslot, long long M,
+                               long long key) {
+  long long h = (long long)(mix64((unsigned long long)key) & (unsigned long long)(M - 1));
+  for (long long probe = 0; probe < M; ++probe) {
+    const long long k = mkeys[h];
+    if (k == key) return mslot[h];
+    if (k == EMPTY_KEY) return -1;
+    h = (h + 1) & (M - 1);
+  }
+  return -1;
+}
+
+// slot lookup + frequency count.  Duplicated keys inside a wave are merged first
+// (match on 16 hash bits with ballots, confirmed against the group leader's key), so
+// a hot index costs one atomic per wave instead of one per occurrence.
+__global__ __launch_bounds__(256) void k_cache_lookup(const int64_t *idx, int nnz, int64_t E,
+                                                       long long *hkeys, int *hcnt, long long H,
+                                                       const long long *mkeys, const int *mslot,
+                                                       long long M, int32_t *slot_out,
+                                                       int count_freq, int32_t *status) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const bool in = n < nnz;
+  const long long key = in ? (long long)idx[n] : -1;
+  const bool valid = in && key >= 0 && key < E;
+  if (count_freq) {
+    const unsigned h16 = (unsigned)(mix64((unsigned long long)key) >> 48);
+    unsigned long long m = __ballot(valid);
+    for (int b = 0; b < 16; ++b) {
+      const bool bit = valid && ((h16 >> b) & 1u);
+      const unsigned long long bb = __ballot(bit);
+      m &= bit ? bb : ~bb;
+    }
+    const int leader = valid ? (__ffsll((long long)m) - 1) : lane;
+    const long long lk = __shfl(key, leader);
+    const unsigned long long same = m & __ballot(valid && key == lk);
+    int add = 0;
+    if (valid) {
+      if (lane == leader) add = __popcll(same);
+      else if (key != lk) add = 1;
+    }
+    if (add > 0) {
+      const long long e = count_slot(hkeys, H, key);
+      if (e < 0) { if (status) atomicOr(status, TT_DEV_HASH_FULL); }
+      else atomicAdd(&hcnt[e], add);
+    }
+  }
+  if (in) slot_out[n] = valid ? map_find(mkeys, mslot, M, key) : -1;
+}
+
+// populate, step 1: compact the used count entries into sortable 64-bit keys
+// ((cmax - count) << kbits) | index, so ascending order = count desc, index asc.
+__global__ __launch_bounds__(256) void k_cache_compact(const long long *hkeys, const int *hcnt,
+                                                        long long H, int kbits,
+                                                        unsigned long long *out, int *n_out) {
+  const long long h = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= H) return;
+  const long long k = hkeys[h];
+  if (k == EMPTY_KEY) return;
+  const unsigned long long cmax = (kbits >= 64) ? 0ull : ((~0ull) >> kbits);
+  unsigned long long c = (unsigned long long)(unsigned)hcnt[h];
+  if (c > cmax) c = cmax;
+  const int pos = atomicAdd(n_out, 1);
+  out[pos] = ((cmax - c) << kbits) | (unsigned long long)k;
+}
+
+// LSD radix sort of 64-bit keys, 8 bits per pass: block histograms ...
+__global__ __launch_bounds__(RT) void k_sort_hist(const unsigned long long *keys, int n,
+                                                   int shift, int *hist, int nblk) {
+  __shared__ int h[256];
+  const int tid = threadIdx.x;
+  h[tid] = 0;
+  __syncthreads();
+  for (int r = 0; r < 4; ++r) {
+    const int i = blockIdx.x * RB + r * 256 + tid;
+    if (i < n) atomicAdd(&h[(int)((keys[i] >> shift) & 255ull)], 1);
+  }
+  __syncthreads();
+  hist[tid * nblk + blockIdx.x] = h[tid];
+}
+
+// ... one-block exclusive scan ...
+__global__ __launch_bounds__(RT) void k_sort_scan(int *hist, int len) {
+  __shared__ int s[RT + 1];
+  block_exclusive_scan(hist, len, s);
+}
+
+// ... and a stable scatter (ranks inside the block keep the input order).
+__global__ __launch_bounds__(RT) void k_sort_scatter(const unsigned long long *in, int n,
+                                                      int shift, const int *off, int nblk,
+                                                      unsigned long long *out) {
+  __shared__ unsigned short cnt[4 * 256];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int d[4], rk[4];
+  unsigned long long k[4];
+  for (int r = 0; r < 4; ++r) {
+    const int i = blockIdx.x * RB + w * 256 + r * 64 + lane;
+    k[r] = 0;
+    d[r] = -1;
+    if (i < n) { k[r] = in[i]; d[r] = (int)((k[r] >> shift) & 255ull); }
+  }
+  block_rank4(d, rk, cnt, 256, 8, nullptr, nblk);
+  for (int r = 0; r < 4; ++r)
+    if (d[r] >= 0) out[off[d[r] * nblk + blockIdx.x] + rk[r]] = k[r];
+}
+
+// populate, step 3: slots 0..n_filled-1 take the sorted indices; fill the map.
+__global__ __launch_bounds__(256) void k_cache_assign(const unsigned long long *sorted, int nf,
+                                                       int kbits, int64_t cache_size,
+                                                       int64_t *cached, long long *mkeys,
+                                                       int *mslot, long long M) {
+  const long long s = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= cache_size) return;
+  if (s >= nf) { cached[s] = -1; return; }
+  const unsigned long long mask = (kbits >= 64) ? ~0ull : ((1ull << kbits) - 1ull);
+  const long long key = (long long)(sorted[s] & mask);
+  cached[s] = key;
+  long long h = (long long)(mix64((unsigned long long)key) & (unsigned long long)(M - 1));
+  for (long long probe = 0; probe < M; ++probe) {
+    const long long prev = (long long)atomicCAS((unsigned long long *)&mkeys[h],
+                                                (unsigned long long)EMPTY_KEY,
+                                                (unsigned long long)key);
+    if (prev == EMPTY_KEY) { mslot[h] = (int)s; return; }
+    h = (h + 1) & (M - 1);
+  }
+}
+
+__global__ void k_iota64(int64_t *a, long long n) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) a[i] = i;
+}
+
+// ---------------------------------------------------------------- host side
+hipError_t cache_lookup_launch(const int64_t *idx, int nnz, int64_t E, long long *hkeys,
+                               int *hcnt, long long H, const long long *mkeys, const int *mslot,
+                               long long M, int32_t *slot_out, int count_freq, int32_t *status,
+                               hipStream_t s) {
+  if (nnz > 0)
+    hipLaunchKernelGGL(k_cache_lookup, dim3((nnz + 255) / 256), dim3(256), 0, s, idx, nnz, E,
+                       hkeys, hcnt, H, mkeys, mslot, M, slot_out, count_freq, status);
+  return hipGetLastError();
+}
+
+hipError_t cache_compact_launch(const long long *hkeys, const int *hcnt, long long H, int kbits,
+                                unsigned long long *out, int *n_out, hipStream_t s) {
+  hipLaunchKernelGGL(k_cache_compact, dim3((unsigned)((H + 255) / 256)), dim3(256), 0, s, hkeys,
+                     hcnt, H, kbits, out, n_out);
+  return hipGetLastError();
+}
+
+// sorts n keys in place (a is input and output, b scratch), 64 bits
+hipError_t radix_sort64(unsigned long long *a, unsigned long long *b, int n, int *hist,
+                        hipStream_t s) {
+  const int nblk = (n + RB - 1) / RB;
+  if (nblk == 0) return hipSuccess;
+  for (int shift = 0; shift < 64; shift += 8) {
+    hipLaunchKernelGGL(k_sort_hist, dim3(nblk), dim3(RT), 0, s, a, n, shift, hist, nblk);
+    hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(RT), 0, s, hist, 256 * nblk);
+    hipLaunchKernelGGL(k_sort_scatter, dim3(nblk), dim3(RT), 0, s, a, n, shift, hist, nblk, b);
+    unsigned long long *t = a; a = b; b = t;
+  }
+  return hipGetLastError();  // 8 passes: the result is back in the first buffer
+}
+
+hipError_t cache_assign_launch(const unsigned long long *sorted, int nf, int kbits,
+                               int64_t cache_size, int64_t *cached, long long *mkeys, int *mslot,
+                               long long M, hipStream_t s) {
+  if (cache_size > 0)
+    hipLaunchKernelGGL(k_cache_assign, dim3((unsigned)((cache_size + 255) / 256)), dim3(256), 0,
+                       s, sorted, nf, kbits, cache_size, cached, mkeys, mslot, M);
+  return hipGetLastError();
+}
+
+hipError_t iota64_launch(int64_t *a, long long n, hipStream_t s) {
+  if (n > 0) hipLaunchKernelGGL(k_iota64, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, n);
+  return hipGetLastError();
+}
+
+}  // namespace ttb

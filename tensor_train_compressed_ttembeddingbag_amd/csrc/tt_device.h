@@ -1,0 +1,113 @@
+// tt_device.h -- device helpers shared by the routing and cache kernels.
+#pragma once
+#include "tt_internal.h"
+
+namespace ttb {
+
+// exclusive scan of arr[0..len) in global memory by one whole block.
+static __device__ void block_exclusive_scan(int *arr, int len, int *s_tmp) {
+  const int nt = blockDim.x, tid = threadIdx.x;
+  const int per = (len + nt - 1) / nt;
+  const int beg = min(tid * per, len), end = min(beg + per, len);
+  int sum = 0;
+  for (int i = beg; i < end; ++i) sum += arr[i];
+  s_tmp[tid] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < nt; ++i) {
+      const int v = s_tmp[i];
+      s_tmp[i] = run;
+      run += v;
+    }
+    s_tmp[nt] = run;
+  }
+  __syncthreads();
+  int run = s_tmp[tid];
+  for (int i = beg; i < end; ++i) {
+    const int v = arr[i];
+    arr[i] = run;
+    run += v;
+  }
+  __threadfence_block();
+  __syncthreads();
+}
+
+static __device__ void block_rank4(const int d[4], int rank[4], unsigned short *cnt, int nbins,
+                            int nbits, int *hist_out, int nblk) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int i = threadIdx.x; i < 4 * nbins; i += blockDim.x) cnt[i] = 0;
+  __syncthreads();
+  int rw[4];
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const bool act = d[r] >= 0;
+    unsigned long long m = __ballot(act);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = act && ((d[r] >> b) & 1);
+      const unsigned long long bb = __ballot(bit);
+      m &= bit ? bb : ~bb;
+    }
+    const int before = __popcll(m & lt);
+    int base = 0;
+    if (act) base = cnt[w * nbins + d[r]];
+    rw[r] = base + before;
+    // every lane of the group has read `base` before the leader writes it back
+    __builtin_amdgcn_wave_barrier();
+    if (act && before == 0) cnt[w * nbins + d[r]] = (unsigned short)(base + __popcll(m));
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  for (int bin = threadIdx.x; bin < nbins; bin += blockDim.x) {
+    const int a0 = cnt[bin], a1 = cnt[nbins + bin], a2 = cnt[2 * nbins + bin],
+              a3 = cnt[3 * nbins + bin];
+    cnt[bin] = 0;
+    cnt[nbins + bin] = (unsigned short)a0;
+    cnt[2 * nbins + bin] = (unsigned short)(a0 + a1);
+    cnt[3 * nbins + bin] = (unsigned short)(a0 + a1 + a2);
+    if (hist_out) hist_out[(size_t)bin * nblk + blockIdx.x] = a0 + a1 + a2 + a3;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) rank[r] = d[r] >= 0 ? (int)cnt[w * nbins + d[r]] + rw[r] : 0;
+}
+
+static __device__ __forceinline__ int nbits_for(int nbins) {
+  return nbins <= 1 ? 1 : 32 - __clz(nbins - 1);
+}
+
+// bag of position n: the last b with off[b] <= n (off clamped to [0, nnz]).
+static __device__ __forceinline__ int find_bag(const int64_t *off, int NB, int n) {
+  int lo = 0, hi = NB;  // answer in [0, NB-1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (off[mid] <= (int64_t)n) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// last-block detection: returns true in every thread of the block that finishes last.
+// The counter word holds (epoch << 32 | count); a word left by another call (or
+// garbage) carries another epoch and counts as zero, so it never needs clearing.
+static __device__ bool last_block(unsigned long long *ctr, int nblocks, unsigned epoch) {
+  __shared__ int s_last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long old = *(volatile unsigned long long *)ctr, nw;
+    while (true) {
+      nw = ((unsigned)(old >> 32) == epoch) ? old + 1ull
+                                              : (((unsigned long long)epoch << 32) | 1ull);
+      const unsigned long long prev = atomicCAS(ctr, old, nw);
+      if (prev == old) break;
+      old = prev;
+    }
+    s_last = ((nw & 0xffffffffull) == (unsigned long long)nblocks);
+  }
+  __syncthreads();
+  if (s_last) __threadfence();
+  return s_last != 0;
+}
+
+}  // namespace ttb

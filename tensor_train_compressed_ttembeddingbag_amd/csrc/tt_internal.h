@@ -1,0 +1,100 @@
+// tt_internal.h -- shared declarations of the libttbag HIP sources (not installed).
+//
+// Pipeline of one call (all kernels on the caller's stream):
+//   route:  k_route_first   split indices, find bags, validate, histogram of the
+//                           (table,i3) digit; forward mode also initialises out
+//                           (zeros, or the pooled cache hits); last block scans.
+//           k_route_pass x2 stable scatter by (table,i3) then by (table,i1), each
+//                           histogramming the next digit over destination blocks;
+//                           last block scans (and, after the second, builds the
+//                           group table).
+//           k_route_final   stable scatter by (table,i2) -> final order
+//                           (table, i2, i1, i3, position); hits after misses by
+//                           (slot, position); skipped elements last.
+//   forward: k_fwd          one workgroup per 64-element chunk of an i2 group.
+//   backward: k_runsum      w * dY summed over runs of equal index (fixed pieces).
+//             k_bwd         one workgroup per i2 group.
+//             k_seg         core-1 / core-3 segment sums + SGD; cache-row SGD.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tt_bag.h"
+
+namespace ttb {
+
+constexpr int RB = 1024;        // routing block: elements per block
+constexpr int RT = 256;         // routing block: threads (4 elements each)
+constexpr int HB = 512;         // cache slots per hit bin
+constexpr int MAX_BINS = 8192;  // digit range of one counting-sort pass
+constexpr int PIECE = 64;       // run-sum piece length (positions)
+constexpr int FWD_CHE = 64;     // forward chunk: elements per workgroup
+constexpr int WG = 512;         // contraction workgroup: 8 waves
+constexpr int NW = WG / 64;
+constexpr int MBW = 2;          // forward: M-blocks (16 rows of (pair, j1)) per wave
+constexpr int CHP = 64;         // backward chunk: most (i1,i2) pairs held in LDS
+// backward: M-blocks per wave (register budget: one for rank-64 tiles)
+constexpr int bwd_mbw(int RP) { return RP == 64 ? 1 : 2; }
+constexpr int MAXQ3 = 16;
+
+// header words inside the workspace (after three 64-bit "last block" counters)
+enum {
+  H_NFWD = 3,       // number of forward work items
+  H_HIT_BEG = 4, H_HIT_END = 5,  // hit region [beg, end) of the final order
+  H_VALID = 6,      // number of valid (non-skipped) elements
+  H_WORDS = 64
+};
+
+struct DevArgs {
+  // shape
+  int T, p1, p2, p3, q1, q2, q3, R1, R2, D;
+  int64_t E;
+  int B, NB;
+  int nnz, nblk;
+  int binsA, binsB, binsI3;
+  int has_cache;
+  int64_t cache_size;
+  int NHB;
+  int CHI;          // backward chunk: max items (distinct indices)
+  int CHPb;         // backward chunk: max pairs (<= CHP)
+  int fwd_mode;     // route: initialise out
+  // inputs / outputs
+  const int64_t *idx;
+  const int64_t *off;
+  const float *psw;
+  const int32_t *slots;
+  float *crows;
+  float *G1, *G2, *G3;
+  float *Y;
+  const float *dY;
+  float lr;
+  int32_t *status;
+  // workspace
+  unsigned long long *ctr;  // [3] epoch-tagged completion counters (no zeroing needed)
+  unsigned epoch;           // unique per call
+  int *hdr;
+  int4 *einfo;      // per element: dA (t,i1), dB (t,i2), dI3 (t,i3), bag
+  int *histA, *histB, *histI3;
+  int *orderI3, *orderA;
+  int *s_n, *s_dA, *s_dB, *s_dI3, *s_bag, *pos_of;
+  int *grp_off;     // [binsB + 1]
+  int *chunk_pre;   // [T*p2 + 1]
+  int *flag1, *flag3;
+  float *part1, *part3, *frag, *gacc;
+};
+
+// ---------------------------------------------------------------- helpers
+__device__ __forceinline__ void set_status(int32_t *st, int bit) {
+  if (st) atomicOr(st, bit);
+}
+
+// host launchers (each kernel is launched from the file that defines it)
+hipError_t launch_route(const DevArgs &a, hipStream_t s);   // the four grouping kernels
+hipError_t launch_runsum(const DevArgs &a, hipStream_t s);
+hipError_t launch_seg(const DevArgs &a, hipStream_t s);
+hipError_t launch_fwd(const DevArgs &a, int RP, size_t lds, hipStream_t s);
+hipError_t launch_bwd(const DevArgs &a, int RP, size_t lds, hipStream_t s);
+size_t fwd_lds_bytes(int RP);
+size_t bwd_lds_bytes(int RP, int CHI, int D, int q3);
+
+}  // namespace ttb

@@ -1,0 +1,237 @@
+// tt_route.hip -- grouping of the looked-up indices (index split, bag ids,
+// validation, stable counting sorts) and the per-run sums of the upstream grad.
+//
+// "FBTT-Embedding" README, "Parameters"/"Initialization": row i of a table is
+// addressed by (i1,i2,i3), a mixed-radix split of i over tt_p_shapes (row-major:
+// i = (i1*p2 + i2)*p3 + i3).  Bags follow EmbeddingBag's CSR offsets.  Grouping
+// the elements by the core-2 slice i2 lets one workgroup reuse a G2 slice for all
+// its elements and share the G1*G2 product between elements with the same
+// (i1,i2); the page's kernel relies on cub for its device-wide primitives, here
+// each pass is a hand-written stable counting sort (LSD, three digits).
+#include "tt_device.h"
+
+namespace ttb {
+
+__global__ __launch_bounds__(RT) void k_route_first(DevArgs a) {
+  extern __shared__ int lds_i[];
+  __shared__ int s_scan[RT + 1];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  if ((int)blockIdx.x >= a.nblk) {
+    // forward only: out[b] = sum of the weighted cache rows of bag b (zero if none)
+    const int b = (blockIdx.x - a.nblk) * (RT / 64) + w;
+    if (b >= a.NB) return;
+    int64_t lo = a.off[b], hi = a.off[b + 1];
+    lo = lo < 0 ? 0 : (lo > a.nnz ? a.nnz : lo);
+    hi = hi < lo ? lo : (hi > a.nnz ? a.nnz : hi);
+    for (int d = lane; d < a.D; d += 64) {
+      float acc = 0.f;
+      if (a.has_cache) {
+        for (int64_t n = lo; n < hi; ++n) {
+          const int s = a.slots[n];
+          if (s >= 0 && s < a.cache_size) {
+            const float wt = a.psw ? a.psw[n] : 1.f;
+            acc += wt * a.crows[(size_t)s * a.D + d];
+          }
+        }
+      }
+      a.Y[(size_t)b * a.D + d] = acc;
+    }
+    return;
+  }
+  const int blk = blockIdx.x;
+  for (int i = tid; i < a.binsI3; i += RT) lds_i[i] = 0;
+  __syncthreads();
+  const int dropA = a.binsA - 1, dropB = a.binsB - 1, dropI = a.binsI3 - 1;
+  for (int r = 0; r < 4; ++r) {
+    const int e = blk * RB + w * 256 + r * 64 + lane;
+    if (e >= a.nnz) continue;
+    const int b = find_bag(a.off, a.NB, e);
+    const int t = b / a.B;
+    int dA, dB, dI;
+    const int slot = (a.has_cache && a.slots) ? a.slots[e] : -1;
+    if (slot >= 0) {
+      if (slot >= a.cache_size) {
+        set_status(a.status, TT_DEV_BAD_SLOT);
+        dA = dropA; dB = dropB; dI = dropI;
+      } else {
+        dA = a.T * a.p1 + slot % HB;
+        dB = a.T * a.p2 + slot / HB;
+        dI = dropI;
+      }
+    } else {
+      const int64_t i = a.idx[e];
+      if (i < 0 || i >= a.E) {
+        set_status(a.status, TT_DEV_BAD_INDEX);
+        dA = dropA; dB = dropB; dI = dropI;
+      } else {
+        const int64_t p23 = (int64_t)a.p2 * a.p3;
+        const int i1 = (int)(i / p23);
+        const int i2 = (int)((i / a.p3) % a.p2);
+        const int i3 = (int)(i % a.p3);
+        dA = t * a.p1 + i1;
+        dB = t * a.p2 + i2;
+        dI = t * a.p3 + i3;
+      }
+    }
+    a.einfo[e] = make_int4(dA, dB, dI, b);
+    atomicAdd(&lds_i[dI], 1);
+  }
+  // offsets must be a CSR over [0, nnz]
+  const int gt = blk * RT + tid, gn = a.nblk * RT;
+  for (int k = gt; k <= a.NB; k += gn) {
+    bool bad = false;
+    if (k == 0 && a.off[0] != 0) bad = true;
+    if (k == a.NB && a.off[a.NB] != (int64_t)a.nnz) bad = true;
+    if (k < a.NB && a.off[k + 1] < a.off[k]) bad = true;
+    if (bad) set_status(a.status, TT_DEV_BAD_OFFSETS);
+  }
+  // the two later digits are histogrammed with atomics: clear them here
+  for (int k = gt; k < a.binsA * a.nblk; k += gn) a.histA[k] = 0;
+  for (int k = gt; k < a.binsB * a.nblk; k += gn) a.histB[k] = 0;
+  __syncthreads();
+  for (int i = tid; i < a.binsI3; i += RT) a.histI3[(size_t)i * a.nblk + blk] = lds_i[i];
+  if (last_block(&a.ctr[0], a.nblk, a.epoch)) block_exclusive_scan(a.histI3, a.binsI3 * a.nblk, s_scan);
+}
+
+// pass 1: original order -> orderI3 by (t,i3); histogram (t,i1) over destination blocks.
+// pass 2: orderI3 -> orderA by (t,i1); histogram (t,i2) over destination blocks, then
+//         the group table.
+__global__ __launch_bounds__(RT) void k_route_pass(DevArgs a, int pass) {
+  extern __shared__ unsigned short lds_c[];
+  __shared__ int s_scan[RT + 1];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, blk = blockIdx.x;
+  const int *in = pass == 1 ? nullptr : a.orderI3;
+  int *out = pass == 1 ? a.orderI3 : a.orderA;
+  const int *offs = pass == 1 ? a.histI3 : a.histA;
+  int *hnext = pass == 1 ? a.histA : a.histB;
+  const int nbins = pass == 1 ? a.binsI3 : a.binsA;
+  int e[4], d[4], dn[4], rk[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int s = blk * RB + w * 256 + r * 64 + lane;
+    e[r] = -1; d[r] = -1; dn[r] = 0;
+    if (s < a.nnz) {
+      e[r] = in ? in[s] : s;
+      const int4 info = a.einfo[e[r]];
+      d[r] = pass == 1 ? info.z : info.x;
+      dn[r] = pass == 1 ? info.x : info.y;
+    }
+  }
+  block_rank4(d, rk, lds_c, nbins, nbits_for(nbins), nullptr, a.nblk);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (e[r] < 0) continue;
+    const int pos = offs[(size_t)d[r] * a.nblk + blk] + rk[r];
+    out[pos] = e[r];
+    atomicAdd(&hnext[(size_t)dn[r] * a.nblk + pos / RB], 1);
+  }
+  if (!last_block(&a.ctr[pass], a.nblk, a.epoch)) return;
+  const int binsN = pass == 1 ? a.binsA : a.binsB;
+  block_exclusive_scan(hnext, binsN * a.nblk, s_scan);
+  if (pass == 2) {
+    const int G = a.T * a.p2;
+    for (int b = tid; b < a.binsB; b += RT) a.grp_off[b] = a.histB[(size_t)b * a.nblk];
+    if (tid == 0) a.grp_off[a.binsB] = a.nnz;
+    __threadfence_block();
+    __syncthreads();
+    for (int g = tid; g <= G; g += RT)
+      a.chunk_pre[g] = g < G ? (a.grp_off[g + 1] - a.grp_off[g] + FWD_CHE - 1) / FWD_CHE : 0;
+    __threadfence_block();
+    __syncthreads();
+    block_exclusive_scan(a.chunk_pre, G + 1, s_scan);
+    if (tid == 0) {
+      a.hdr[H_NFWD] = a.chunk_pre[G];
+      a.hdr[H_HIT_BEG] = a.grp_off[G];
+      a.hdr[H_HIT_END] = a.grp_off[a.binsB - 1];
+      a.hdr[H_VALID] = a.grp_off[a.binsB - 1];
+    }
+  }
+}
+
+__global__ __launch_bounds__(RT) void k_route_final(DevArgs a) {
+  extern __shared__ unsigned short lds_c[];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, blk = blockIdx.x;
+  int e[4], d[4], rk[4];
+  int4 info[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int s = blk * RB + w * 256 + r * 64 + lane;
+    e[r] = -1; d[r] = -1;
+    info[r] = make_int4(0, 0, 0, 0);
+    if (s < a.nnz) {
+      e[r] = a.orderA[s];
+      info[r] = a.einfo[e[r]];
+      d[r] = info[r].y;
+    }
+  }
+  block_rank4(d, rk, lds_c, a.binsB, nbits_for(a.binsB), nullptr, a.nblk);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (e[r] < 0) continue;
+    const int pos = a.histB[(size_t)d[r] * a.nblk + blk] + rk[r];
+    a.s_n[pos] = e[r];
+    a.s_dA[pos] = info[r].x;
+    a.s_dB[pos] = info[r].y;
+    a.s_dI3[pos] = info[r].z;
+    a.s_bag[pos] = info[r].w;
+    a.pos_of[e[r]] = pos;
+  }
+}
+
+// Backward: frag[s] = sum over positions of one run fragment of w_n * dY[bag n], where a
+// run is a maximal range of equal (dB, dA, dI3) in the final order (one index of one
+// table, or one cache slot) and fragments are the pieces of a run inside fixed
+// 64-position pieces.  One wave per piece; the summation order is the position order.
+__global__ __launch_bounds__(RT) void k_runsum(DevArgs a) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int piece = blockIdx.x * (RT / 64) + w;
+  const int V = a.hdr[H_VALID];
+  const int beg = piece * PIECE;
+  if (beg >= V) return;
+  const int len = min(PIECE, V - beg);
+  int kA = -1, kB = -1, kI = -1, bag = 0;
+  float wt = 0.f;
+  if (lane < len) {
+    const int s = beg + lane;
+    kA = a.s_dA[s]; kB = a.s_dB[s]; kI = a.s_dI3[s]; bag = a.s_bag[s];
+    wt = a.psw ? a.psw[a.s_n[s]] : 1.f;
+  }
+  const int pA = __shfl_up(kA, 1), pB = __shfl_up(kB, 1), pI = __shfl_up(kI, 1);
+  const int start = (lane == 0) || kA != pA || kB != pB || kI != pI;
+  for (int d0 = 0; d0 < a.D; d0 += 64) {
+    const int d = d0 + lane;
+    float acc = 0.f;
+    int cur = beg;
+    for (int l = 0; l < len; ++l) {
+      const int st = __shfl(start, l);
+      if (st && l > 0) {
+        if (d < a.D) a.frag[(size_t)cur * a.D + d] = acc;
+        acc = 0.f;
+        cur = beg + l;
+      }
+      const int b = __shfl(bag, l);
+      const float wv = __shfl(wt, l);
+      if (d < a.D) acc += wv * a.dY[(size_t)b * a.D + d];
+    }
+    if (d < a.D) a.frag[(size_t)cur * a.D + d] = acc;
+  }
+}
+
+hipError_t launch_route(const DevArgs &a, hipStream_t s) {
+  const int extra = a.fwd_mode ? (a.NB + RT / 64 - 1) / (RT / 64) : 0;
+  if (a.nblk + extra > 0)
+    hipLaunchKernelGGL(k_route_first, dim3(a.nblk + extra), dim3(RT), (size_t)a.binsI3 * 4, s, a);
+  if (a.nblk == 0) return hipGetLastError();
+  hipLaunchKernelGGL(k_route_pass, dim3(a.nblk), dim3(RT), (size_t)a.binsI3 * 8, s, a, 1);
+  hipLaunchKernelGGL(k_route_pass, dim3(a.nblk), dim3(RT), (size_t)a.binsA * 8, s, a, 2);
+  hipLaunchKernelGGL(k_route_final, dim3(a.nblk), dim3(RT), (size_t)a.binsB * 8, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_runsum(const DevArgs &a, hipStream_t s) {
+  const int pieces = (a.nnz + PIECE - 1) / PIECE;
+  if (pieces > 0) hipLaunchKernelGGL(k_runsum, dim3((pieces + 3) / 4), dim3(RT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ttb

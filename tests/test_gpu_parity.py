@@ -1,0 +1,286 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer work (the grouping order, cache selection, slots) must match bit for bit;
+floating point within 1e-4 of the oracle's fp64 result, per tensor, measured as
+max|x - x*| / max|x*| (core and cache-row updates are compared as deltas
+new - old against -lr * gradient).  Slices the batch does not touch must keep
+their bits.  Every input is seeded and synthetic (tensor_train_compressed_ttembeddingbag_amd.workloads).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tensor_train_compressed_ttembeddingbag_amd import abi, workloads as W
+from helpers import TOL, gpu_cores, host_cores, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _run_step(wl, cores, batch, with_fwd=True, lr=None, status=None):
+    """Forward then backward+SGD on the GPU.  Returns (Y, new logical cores)."""
+    lr = wl.lr if lr is None else lr
+    g = gpu_cores(wl, cores)
+    d = to_dev(batch)
+    desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E, wl.num_tables)
+    B = batch["num_bags"]
+    ws = abi.workspace(desc, d["indices"].numel(), B)
+    Y = None
+    if with_fwd:
+        Y = abi.tt_bag_forward(desc, g, d["indices"], d["offsets"], B, d["per_sample_weights"],
+                               ws=ws, dev_status=status).cpu().numpy()
+    abi.tt_bag_backward_sgd(desc, g, d["indices"], d["offsets"], B, d["grad_out"], lr,
+                            d["per_sample_weights"], ws=ws, dev_status=status)
+    torch.cuda.synchronize()
+    return Y, host_cores(wl, g), g
+
+
+def _check_update(wl, cores, new, grads, touched, lr):
+    for t in range(wl.num_tables):
+        for k in range(3):
+            old = cores[t][k].astype(np.float64)
+            nw = new[t][k].astype(np.float64)
+            delta = nw - old
+            exp = -lr * grads[t][k]
+            e = rel_err(delta, exp)
+            assert e <= TOL, "table %d core %d: delta rel err %.3g" % (t, k, e)
+            # untouched slices keep their bits
+            o_sl = np.moveaxis(cores[t][k], 1, 0)
+            n_sl = np.moveaxis(new[t][k], 1, 0)
+            for ik in np.flatnonzero(touched[t][k] == 0):
+                assert np.array_equal(o_sl[ik].view(np.uint32), n_sl[ik].view(np.uint32)), (t, k, ik)
+
+
+def _full_parity(wl, batch, seed=None):
+    cores = W.make_cores(wl, seed)
+    B = batch["num_bags"]
+    Y, new, _ = _run_step(wl, cores, batch)
+    Yo = oracle.forward(wl.p, wl.q, wl.ranks, wl.E, cores, batch["indices"], batch["offsets"], B,
+                        per_sample_weights=batch["per_sample_weights"])
+    e = rel_err(Y, Yo)
+    assert e <= TOL, "forward rel err %.3g" % e
+    grads, touched, _, _ = oracle.backward(wl.p, wl.q, wl.ranks, wl.E, cores, batch["indices"],
+                                           batch["offsets"], B, batch["grad_out"],
+                                           per_sample_weights=batch["per_sample_weights"])
+    _check_update(wl, cores, new, grads, touched, wl.lr)
+
+
+SMALL = [
+    W.WORKLOADS["tiny"],
+    W.custom("q1=4 r=32", p=(7, 9, 5), q=(4, 4, 4), ranks=(32, 32), bags_per_table=40,
+             lengths=("uniform", 0, 9), init_std=0.2, lr=0.05, weighted=True),
+    W.custom("q1=1 r=(3,5)", p=(11, 6, 4), q=(1, 3, 5), ranks=(3, 5), bags_per_table=30,
+             lengths=("uniform", 1, 6), lr=0.1, num_embeddings=250),
+    W.custom("q1=2 r=(20,12)", p=(5, 13, 7), q=(2, 5, 3), ranks=(20, 12), bags_per_table=25,
+             lengths=("uniform", 0, 12), init_std=0.3, lr=0.05, weighted=True),
+    W.custom("multi r=64", p=(6, 5, 4), q=(4, 2, 3), ranks=(64, 40), num_tables=3,
+             bags_per_table=20, lengths=("uniform", 1, 8), init_std=0.15, lr=0.02),
+    W.custom("rank1", p=(30, 1, 1), q=(4, 1, 1), ranks=(1, 1), bags_per_table=12,
+             lengths=("uniform", 0, 5), lr=0.1),
+    W.custom("dup-heavy", p=(3, 2, 2), q=(4, 4, 2), ranks=(16, 16), bags_per_table=300,
+             lengths=("uniform", 1, 30), init_std=0.3, lr=0.01, weighted=True),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_small_shapes_forward_backward(wl):
+    _say("case", wl.name)
+    _full_parity(wl, W.make_batch(wl, 0))
+
+
+def test_readme_shape_full():
+    wl = W.WORKLOADS["readme"]
+    _say("case readme full")
+    _full_parity(wl, W.make_batch(wl, 0))
+
+
+def test_multitable_full():
+    wl = W.WORKLOADS["multitable"]
+    _say("case multitable full")
+    _full_parity(wl, W.make_batch(wl, 0))
+
+
+def test_skewed_full_size_sampled():
+    """Full-size skewed workload (D=128, ranks 64, Zipf, weights).  The oracle
+    checks sampled bags of the forward and sampled slices of each core."""
+    wl = W.WORKLOADS["skewed"]
+    _say("case skewed full (sampled)")
+    cores = W.make_cores(wl)
+    b = W.make_batch(wl, 0)
+    B = b["num_bags"]
+    Y, new, _ = _run_step(wl, cores, b)
+    rng = np.random.Generator(np.random.PCG64(7))
+    bags = np.sort(rng.choice(B, 48, replace=False))
+    off = b["offsets"]
+    sel = np.concatenate([np.arange(off[x], off[x + 1]) for x in bags])
+    sub_off = np.concatenate([[0], np.cumsum(off[bags + 1] - off[bags])])
+    Yo = oracle.forward(wl.p, wl.q, wl.ranks, wl.E, cores, b["indices"][sel], sub_off, len(bags),
+                        per_sample_weights=b["per_sample_weights"][sel])
+    assert rel_err(Y[bags], Yo) <= TOL
+    # sampled slices: the gradient of slice a of core k only involves the elements with i_k = a
+    i1, i2, i3 = oracle.split_index(wl.p, b["indices"])
+    bag = oracle.bag_ids(off, len(b["indices"]))
+    for k, ik in enumerate((i1, i2, i3)):
+        touched = np.unique(ik)
+        pick = rng.choice(touched, 3, replace=False)
+        for a in pick:
+            m = np.flatnonzero(ik == a)
+            lens = np.bincount(bag[m], minlength=B)
+            sub_off = np.concatenate([[0], np.cumsum(lens)])
+            grads, tch, _, _ = oracle.backward(wl.p, wl.q, wl.ranks, wl.E, cores, b["indices"][m],
+                                               sub_off, B, b["grad_out"],
+                                               per_sample_weights=b["per_sample_weights"][m])
+            old = np.moveaxis(cores[0][k], 1, 0)[a].astype(np.float64)
+            nw = np.moveaxis(new[0][k], 1, 0)[a].astype(np.float64)
+            exp = -wl.lr * np.moveaxis(grads[0][k], 1, 0)[a]
+            e = rel_err(nw - old, exp)
+            assert e <= TOL, (k, a, e)
+
+
+def test_route_order_bit_exact():
+    for wl in (W.WORKLOADS["tiny"], W.WORKLOADS["readme"], W.WORKLOADS["multitable"], SMALL[4]):
+        _say("route", wl.name)
+        b = W.make_batch(wl, 1)
+        d = to_dev(b)
+        desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E, wl.num_tables)
+        order, goff = abi.tt_bag_route(desc, d["indices"], d["offsets"], b["num_bags"])
+        ref, counts = oracle.route_order(wl.p, wl.E, wl.num_tables, b["num_bags"], b["indices"],
+                                         b["offsets"])
+        assert np.array_equal(order.cpu().numpy()[:len(ref)], ref)
+        g = goff.cpu().numpy()
+        assert np.array_equal(np.diff(g[:wl.num_tables * wl.p[1] + 1]), counts)
+
+
+def test_route_with_cache_slots_bit_exact():
+    wl = SMALL[1]
+    b = W.make_batch(wl, 3)
+    rng = np.random.Generator(np.random.PCG64(5))
+    n = len(b["indices"])
+    slots = np.where(rng.random(n) < 0.4, rng.integers(0, 700, n), -1).astype(np.int32)
+    b["indices"][rng.random(n) < 0.05] = wl.E + 3  # invalid indices are skipped
+    d = to_dev(b)
+    desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E, wl.num_tables)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    order, goff = abi.tt_bag_route(desc, d["indices"], d["offsets"], b["num_bags"],
+                                   slots=torch.from_numpy(slots).cuda(), cache_size=700,
+                                   dev_status=st)
+    ref, counts = oracle.route_order(wl.p, wl.E, 1, b["num_bags"], b["indices"], b["offsets"], slots)
+    assert np.array_equal(order.cpu().numpy()[:len(ref)], ref)
+    g = goff.cpu().numpy()
+    G = wl.p[1]
+    assert g[G + 1] - g[G] == int(np.sum(slots >= 0))
+    invalid = (slots < 0) & ((b["indices"] < 0) | (b["indices"] >= wl.E))
+    assert (int(st.item()) & abi.TT_DEV_BAD_INDEX) == (abi.TT_DEV_BAD_INDEX if invalid.any() else 0)
+
+
+def test_backward_is_bit_reproducible():
+    wl = W.WORKLOADS["readme"]
+    cores = W.make_cores(wl)
+    b = W.make_batch(wl, 2)
+    _, n1, _ = _run_step(wl, cores, b, with_fwd=False)
+    _, n2, _ = _run_step(wl, cores, b, with_fwd=False)
+    for k in range(3):
+        assert np.array_equal(n1[0][k].view(np.uint32), n2[0][k].view(np.uint32))
+
+
+def test_invalid_indices_and_offsets_set_status():
+    wl = SMALL[1]
+    cores = W.make_cores(wl)
+    b = W.make_batch(wl, 4)
+    bad = b["indices"].copy()
+    bad[3] = -1
+    bad[7] = wl.E
+    b2 = dict(b, indices=bad)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    Y, _, _ = _run_step(wl, cores, b2, status=st)
+    assert int(st.item()) & abi.TT_DEV_BAD_INDEX
+    # the valid elements still pool correctly (bad ones are skipped)
+    keep = (bad >= 0) & (bad < wl.E)
+    bag = oracle.bag_ids(b["offsets"], len(bad))
+    lens = np.bincount(bag[keep], minlength=b["num_bags"])
+    off2 = np.concatenate([[0], np.cumsum(lens)])
+    Yo = oracle.forward(wl.p, wl.q, wl.ranks, wl.E, cores, bad[keep], off2, b["num_bags"],
+                        per_sample_weights=b["per_sample_weights"][keep])
+    assert rel_err(Y, Yo) <= TOL
+    off = b["offsets"].copy()
+    off[-1] += 1
+    st.zero_()
+    _run_step(wl, cores, dict(b, offsets=off), status=st)
+    assert int(st.item()) & abi.TT_DEV_BAD_OFFSETS
+
+
+def test_empty_batch_and_empty_bags():
+    wl = SMALL[0]
+    cores = W.make_cores(wl)
+    desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E)
+    g = gpu_cores(wl, cores)
+    idx = torch.zeros(0, dtype=torch.int64, device="cuda")
+    off = torch.zeros(6, dtype=torch.int64, device="cuda")
+    Y = abi.tt_bag_forward(desc, g, idx, off, 5)
+    assert torch.all(Y == 0)
+    abi.tt_bag_backward_sgd(desc, g, idx, off, 5, torch.ones(5, wl.D, device="cuda"), 0.1)
+    torch.cuda.synchronize()
+    new = host_cores(wl, g)
+    for k in range(3):
+        assert np.array_equal(new[0][k], cores[0][k])
+
+
+def test_cache_path_matches_oracle():
+    """Warm-up lookups count frequencies; populate picks the top-K (bit-exact against
+    the oracle); then forward/backward with hits read and update cache rows."""
+    wl = W.custom("cache", p=(20, 22, 25), q=(4, 4, 4), ranks=(32, 32), bags_per_table=256,
+                  lengths=("fixed", 20), dist=("zipf", 1.2), init_std=1 / 32 ** 0.5, lr=0.01,
+                  weighted=True)
+    K = 900
+    cores = W.make_cores(wl)
+    desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E)
+    cache = abi.Cache(desc, K, 1 << 14)
+    warm = [W.make_batch(wl, 100 + i) for i in range(4)]
+    for bt in warm:
+        cache.lookup(torch.from_numpy(bt["indices"]).cuda(), count_freq=True)
+    g = gpu_cores(wl, cores)
+    rows = torch.zeros(K, wl.D, device="cuda")
+    nf = cache.populate(g, rows)
+    counts = oracle.count_frequencies([bt["indices"] for bt in warm])
+    sel = oracle.select_cache(counts, K)
+    assert nf == len(sel)
+    got = cache.cached_indices().cpu().numpy()
+    assert np.array_equal(got[:nf], sel)
+    assert np.all(got[nf:] == -1)
+    ref_rows = oracle.populate_rows(wl.p, wl.q, wl.ranks, cores[0], sel)
+    assert rel_err(rows.cpu().numpy()[:nf], ref_rows) <= TOL
+    b = W.make_batch(wl, 0)
+    d = to_dev(b)
+    slots = cache.lookup(d["indices"], count_freq=False)
+    ref_slots = oracle.lookup_slots(sel, b["indices"])
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
+    assert (ref_slots >= 0).any() and (ref_slots < 0).any()
+    rows_old = rows.cpu().numpy().copy()
+    ws = abi.workspace(desc, d["indices"].numel(), 256, K)
+    Y = abi.tt_bag_forward(desc, g, d["indices"], d["offsets"], 256, d["per_sample_weights"],
+                           cache=(slots, rows), ws=ws).cpu().numpy()
+    Yo = oracle.forward(wl.p, wl.q, wl.ranks, wl.E, cores, b["indices"], b["offsets"], 256,
+                        per_sample_weights=b["per_sample_weights"], slots=ref_slots,
+                        cache_rows=rows_old)
+    assert rel_err(Y, Yo) <= TOL
+    abi.tt_bag_backward_sgd(desc, g, d["indices"], d["offsets"], 256, d["grad_out"], wl.lr,
+                            d["per_sample_weights"], cache=(slots, rows), ws=ws)
+    torch.cuda.synchronize()
+    grads, touched, gc, tc = oracle.backward(wl.p, wl.q, wl.ranks, wl.E, cores, b["indices"],
+                                             b["offsets"], 256, b["grad_out"],
+                                             per_sample_weights=b["per_sample_weights"],
+                                             slots=ref_slots, cache_size=K)
+    _check_update(wl, cores, host_cores(wl, g), grads, touched, wl.lr)
+    drows = rows.cpu().numpy().astype(np.float64) - rows_old
+    assert rel_err(drows, -wl.lr * gc) <= TOL
+    untouched = np.flatnonzero(tc == 0)
+    assert np.array_equal(rows.cpu().numpy()[untouched].view(np.uint32),
+                          rows_old[untouched].view(np.uint32))
+    cache.close()
