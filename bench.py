@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""TT-EmbeddingBag fwd+bwd (fused sparse SGD) benchmark on one MI355X.
+
+A step is one full pass of the hot path over one batch: tt_bag_forward then
+tt_bag_backward_sgd (and tt_cache_lookup first for the cached workload), all
+inputs resident in HBM.  Default workload: the README benchmark shape
+(p=[200,220,250], q=[4,4,4], ranks=[32,32], E=11,000,000, D=64, 512 bags of 20
+uniform indices, SGD lr=0.01) with seeded synthetic data.
+
+Printed (one JSON line): value = microseconds per looked-up index (nnz) of a
+whole fwd+bwd step; GFLOPS with 3*(F1+F2) flop per nnz; the roofline of the
+dominant kernel from HIP events recorded around each library launch on its own
+stream (a separate pass of the same steps); and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+README_US_PER_NNZ = 0.416       # the pages' benchmark line for this workload (hardware unstated)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="readme",
+                    choices=["tiny", "readme", "skewed", "multitable", "cached"])
+    ap.add_argument("--batches", type=int, default=8, help="distinct batches cycled through")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--no-roofline", action="store_true")
+    return ap.parse_args()
+
+
+def _dev(batch, torch):
+    d = {k: torch.from_numpy(batch[k]).cuda() for k in ("indices", "offsets", "grad_out")}
+    d["per_sample_weights"] = (torch.from_numpy(batch["per_sample_weights"]).cuda()
+                               if batch["per_sample_weights"] is not None else None)
+    d["num_bags"] = batch["num_bags"]
+    d["np"] = batch
+    return d
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tensor_train_compressed_ttembeddingbag_amd import abi, metrics, workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    abi.lib()
+    wl = W.WORKLOADS[args.workload]
+    cores = W.make_cores(wl)
+    g = [torch.from_numpy(np.concatenate([W.slice_major(cores[t][k]).ravel()
+                                          for t in range(wl.num_tables)])).cuda()
+         for k in range(3)]
+    desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E, wl.num_tables)
+    batches = [_dev(W.make_batch(wl, k), torch) for k in range(args.batches)]
+    max_nnz = max(b["indices"].numel() for b in batches)
+    B = wl.bags_per_table
+    cache = None
+    if wl.cache_size:
+        cache = abi.Cache(desc, wl.cache_size, wl.hashtbl_size)
+        for k in range(wl.warmup_batches):
+            wb = W.make_batch(wl, 500 + k)
+            cache.lookup(torch.from_numpy(wb["indices"]).cuda(), count_freq=True)
+        rows = torch.zeros(wl.cache_size, wl.D, device="cuda")
+        n_filled = cache.populate(g, rows)
+        slots = [torch.empty(b["indices"].numel(), dtype=torch.int32, device="cuda") for b in batches]
+    ws = abi.workspace(desc, max_nnz, B, wl.cache_size)
+    out = torch.empty(wl.num_tables * B, wl.D, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def step(i):
+        b = batches[i % len(batches)]
+        cv = None
+        if cache is not None:
+            s = slots[i % len(batches)]
+            cache.lookup(b["indices"], slot_out=s, count_freq=True, dev_status=status)
+            cv = (s, rows)
+        abi.tt_bag_forward(desc, g, b["indices"], b["offsets"], B, b["per_sample_weights"],
+                           cache=cv, out=out, ws=ws, dev_status=status)
+        abi.tt_bag_backward_sgd(desc, g, b["indices"], b["offsets"], B, b["grad_out"], wl.lr,
+                                b["per_sample_weights"], cache=cv, ws=ws, dev_status=status)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if int(status.item()) != 0:
+        print("device status %d during the benchmark" % int(status.item()), file=sys.stderr)
+        sys.exit(1)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    nnz_mean = float(np.mean([batches[i % len(batches)]["indices"].numel()
+                              for i in range(args.steps)]))
+    us_per_nnz = ms_per_step * 1e3 / nnz_mean
+    f1, f2 = metrics.stage_flops(wl.q, wl.ranks)
+    step_flops = metrics.step_flops_per_nnz(wl.q, wl.ranks) * nnz_mean
+    gflops = step_flops / (ms_per_step * 1e-3) / 1e9
+
+    res = {
+        "metric": "TT-EmbeddingBag fwd+bwd µs/nnz and GFLOPS (E=11M, D=64, R=32, B=512)",
+        "value": round(us_per_nnz, 6),
+        "unit": "us/nnz",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": (round(us_per_nnz / README_US_PER_NNZ, 6) if args.workload == "readme" else None),
+        "dtype": "f32",
+        "data": "synthetic (seeded numpy PCG64; random-normal cores)",
+        "gflops": round(gflops, 3),
+        "gflops_convention": "3*(F1+F2)=%d flop per nnz per fwd+bwd step" % (3 * (f1 + f2)),
+        "config": {"workload": "%s: p=%s q=%s ranks=%s E=%d D=%d tables=%d bags/table=%d "
+                               "nnz/step=%.0f lengths=%s indices=%s weighted=%s lr=%g cache=%d"
+                               % (wl.name, list(wl.p), list(wl.q), list(wl.ranks), wl.E, wl.D,
+                                  wl.num_tables, B, nnz_mean, list(wl.lengths), list(wl.dist),
+                                  wl.weighted, wl.lr, wl.cache_size),
+                   "nnz": nnz_mean, "global_batch": wl.num_tables * B},
+    }
+    if cache is not None:
+        res["config"]["cache_rows_filled"] = n_filled
+
+    if not args.no_roofline:
+        res["roofline"], res["kernels"] = roofline(args, wl, batches, step, torch, abi, metrics,
+                                                   None if cache is None else slots)
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(wl, cores, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def roofline(args, wl, batches, step, torch, abi, metrics, slots):
+    """Dominant kernel's achieved rate from HIP events around each launch."""
+    nsteps = min(args.steps, 400)
+    abi.tt_profile_enable(True)
+    for i in range(nsteps):
+        step(i)
+    torch.cuda.synchronize()
+    prof = abi.tt_profile_read()
+    abi.tt_profile_enable(False)
+    kernels = {k: {"total_ms": round(v[0], 4), "launches": v[1],
+                   "avg_us": round(1e3 * v[0] / v[1], 3) if v[1] else None}
+               for k, v in prof.items() if v[1]}
+    dom = max(kernels, key=lambda k: kernels[k]["total_ms"])
+    # algorithmic work of the contraction kernels, averaged over the batches stepped
+    per_batch = []
+    for j, b in enumerate(batches):
+        nb = b["np"]
+        sl = None if slots is None else slots[j].cpu().numpy()
+        per_batch.append((metrics.unique_pairs(wl.p, wl.num_tables, wl.bags_per_table,
+                                               nb["indices"], nb["offsets"], sl, wl.E),
+                          int(np.sum(sl < 0)) if sl is not None else len(nb["indices"])))
+    U = float(np.mean([per_batch[i % len(batches)][0] for i in range(nsteps)]))
+    N = float(np.mean([per_batch[i % len(batches)][1] for i in range(nsteps)]))
+    work = {"k_bwd": metrics.bwd_kernel_flops(wl.q, wl.ranks, N, U),
+            "k_fwd": metrics.fwd_kernel_flops(wl.q, wl.ranks, N, U)}
+    avg_s = kernels[dom]["avg_us"] * 1e-6
+    if dom in work:
+        ach = work[dom] / avg_s / 1e12
+        rf = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 3),
+              "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+              "frac": round(ach / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": None,
+              "work_per_launch": "%.4g flop (2*F1 per distinct (i1,i2) pair x %.1f pairs + "
+                                 "2*F2 per element x %.1f elements)" % (work[dom], U, N)
+              if dom == "k_bwd" else "%.4g flop (F1 x %.1f pairs + F2 x %.1f elements)"
+                                     % (work[dom], U, N)}
+    else:
+        rf = {"bound": "hbm", "kernel": dom, "achieved": None, "peak": PEAK_HBM_GBS,
+              "unit": "GB/s", "frac": None, "traffic": None}
+    for k in ("k_fwd", "k_bwd"):
+        if k in kernels:
+            kernels[k]["tflops"] = round(work[k] / (kernels[k]["avg_us"] * 1e-6) / 1e12, 3)
+    return rf, kernels
+
+
+def cpu_baseline(wl, cores, budget_s):
+    """The oracle, as it stands, on a prefix of the bags of batch 0 of the same
+    workload: the prefix doubles until one fwd+bwd run takes >= budget/8 (or covers
+    the batch), then runs repeat until the budget is spent.  Single-threaded C."""
+    import oracle
+    from tensor_train_compressed_ttembeddingbag_amd import workloads as W
+    oracle.build()
+    b = W.make_batch(wl, 0)
+    off = b["offsets"]
+    all_bags = wl.num_tables * wl.bags_per_table
+    bags, t_used, nnz_done, runs, sized = min(16, all_bags), 0.0, 0, 0, False
+    while True:
+        n = int(off[bags])
+        psw = None if b["per_sample_weights"] is None else b["per_sample_weights"][:n]
+        t0 = time.perf_counter()
+        oracle.forward(wl.p, wl.q, wl.ranks, wl.E, cores, b["indices"][:n], off[:bags + 1], bags,
+                       psw)
+        oracle.backward(wl.p, wl.q, wl.ranks, wl.E, cores, b["indices"][:n], off[:bags + 1], bags,
+                        b["grad_out"][:bags], psw)
+        dt = time.perf_counter() - t0
+        t_used += dt
+        nnz_done += n
+        runs += 1
+        if not sized:
+            if dt >= budget_s / 8 or bags == all_bags:
+                sized = True
+            else:
+                bags = min(all_bags, bags * 2)
+        if sized and t_used >= budget_s:
+            break
+    return {"value": round(t_used * 1e6 / nnz_done, 3), "unit": "us/nnz", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d fwd+bwd runs over prefixes of batch 0 (final prefix %d of %d bags, "
+                      "%d nnz in total, %.1f s), fp64 C oracle, one thread; host %s, %d CPUs"
+                      % (runs, bags, all_bags, nnz_done, t_used,
+                         platform.processor() or platform.machine(), os.cpu_count() or 0)}
+
+
+if __name__ == "__main__":
+    main()

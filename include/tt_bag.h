@@ -175,6 +175,18 @@ int tt_cache_cached_indices(tt_cache *c, int64_t *cached_out, void *stream);
 
 int tt_cache_destroy(tt_cache *c);
 
+/* ---------------------------------------------------------------- timing
+ * Optional per-kernel timing for benchmarks: while enabled, every kernel the
+ * library enqueues is bracketed by two HIP events recorded on the stream it is
+ * launched on (this adds a little time between kernels).  tt_profile_enable
+ * clears the totals; tt_profile_read waits for the recorded events (host
+ * blocking) and returns the summed milliseconds and the number of launches of
+ * kernel kernel_id in [0, tt_profile_num_kernels()). */
+int tt_profile_enable(int on);
+int tt_profile_num_kernels(void);
+const char *tt_profile_kernel_name(int kernel_id);
+int tt_profile_read(int kernel_id, double *total_ms, int64_t *launches);
+
 /* Static description of a return code. */
 const char *tt_status_string(int code);
 

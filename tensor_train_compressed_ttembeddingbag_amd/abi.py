@@ -56,6 +56,10 @@ _SIG = {
     "tt_cache_populate": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "tt_cache_cached_indices": (ctypes.c_int, [_P, _P, _P]),
     "tt_cache_destroy": (ctypes.c_int, [_P]),
+    "tt_profile_enable": (ctypes.c_int, [ctypes.c_int]),
+    "tt_profile_num_kernels": (ctypes.c_int, []),
+    "tt_profile_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
+    "tt_profile_read": (ctypes.c_int, [ctypes.c_int, _P, _P]),
     "tt_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 EXPORTS = tuple(_SIG)
@@ -220,6 +224,23 @@ def tt_bag_route(desc: TTDesc, indices, offsets, num_bags: int, slots=None, cach
                             _ptr(ws), ws.numel(), _ptr(dev_status), _stream(stream))
     _check("tt_bag_route", rc)
     return order, goff
+
+
+def tt_profile_enable(on: bool = True) -> None:
+    """Start (clearing totals) or stop per-kernel event timing inside the library."""
+    _check("tt_profile_enable", lib().tt_profile_enable(1 if on else 0))
+
+
+def tt_profile_read() -> dict:
+    """{kernel name: (total_ms, launches)} for every kernel timed since enabling."""
+    L = lib()
+    out = {}
+    for k in range(L.tt_profile_num_kernels()):
+        ms = ctypes.c_double(0.0)
+        n = ctypes.c_int64(0)
+        _check("tt_profile_read", L.tt_profile_read(k, ctypes.byref(ms), ctypes.byref(n)))
+        out[L.tt_profile_kernel_name(k).decode()] = (ms.value, n.value)
+    return out
 
 
 class Cache:

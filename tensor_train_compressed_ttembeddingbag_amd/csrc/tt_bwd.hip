@@ -351,7 +351,9 @@ static hipError_t launch_bwd_t(const DevArgs &a, size_t lds, hipStream_t s) {
                               160 * 1024);
     attr_set = true;
   }
+  prof_begin(K_BWD, s);
   hipLaunchKernelGGL(k_bwd<RP>, dim3(a.T * a.p2), dim3(WG), lds, s, a);
+  prof_end(K_BWD, s);
   return hipGetLastError();
 }
 
@@ -433,7 +435,9 @@ __global__ __launch_bounds__(256) void k_seg(DevArgs a) {
 
 hipError_t launch_seg(const DevArgs &a, hipStream_t s) {
   const int tasks = a.T * a.p1 + a.T * a.p3 + (a.has_cache ? (a.nnz + PIECE - 1) / PIECE : 0);
+  prof_begin(K_SEG, s);
   hipLaunchKernelGGL(k_seg, dim3((tasks + 3) / 4), dim3(256), 0, s, a);
+  prof_end(K_SEG, s);
   return hipGetLastError();
 }
 

@@ -182,7 +182,9 @@ static hipError_t launch_fwd_t(const DevArgs &a, size_t lds, hipStream_t s) {
     attr_set = true;
   }
   const int grid = a.T * a.p2 + (a.nnz + FWD_CHE - 1) / FWD_CHE;
+  prof_begin(K_FWD, s);
   hipLaunchKernelGGL(k_fwd<RP>, dim3(grid), dim3(WG), lds, s, a);
+  prof_end(K_FWD, s);
   return hipGetLastError();
 }
 

@@ -88,6 +88,14 @@ __device__ __forceinline__ void set_status(int32_t *st, int bit) {
   if (st) atomicOr(st, bit);
 }
 
+// kernels named by the optional per-kernel timer (tt_prof.hip)
+enum KernelId {
+  K_ROUTE_FIRST, K_ROUTE_PASS1, K_ROUTE_PASS2, K_ROUTE_FINAL, K_FWD, K_RUNSUM, K_BWD, K_SEG,
+  K_CACHE_LOOKUP, K_COUNT
+};
+void prof_begin(int id, hipStream_t s);
+void prof_end(int id, hipStream_t s);
+
 // host launchers (each kernel is launched from the file that defines it)
 hipError_t launch_route(const DevArgs &a, hipStream_t s);   // the four grouping kernels
 hipError_t launch_runsum(const DevArgs &a, hipStream_t s);

@@ -1,0 +1,104 @@
+// tt_prof.hip -- optional per-kernel timing: while enabled, every kernel the
+// library enqueues is bracketed by a pair of HIP events recorded on the stream it
+// is launched on; tt_profile_read waits for the events and sums the elapsed times.
+#include <mutex>
+#include <vector>
+
+#include "tt_internal.h"
+
+namespace ttb {
+namespace {
+
+struct Rec {
+  int id;
+  hipEvent_t a, b;
+};
+
+std::mutex g_mu;
+bool g_on = false;
+std::vector<Rec> g_pending;
+std::vector<hipEvent_t> g_pool;
+double g_ms[K_COUNT] = {0};
+long long g_n[K_COUNT] = {0};
+hipEvent_t g_open[K_COUNT] = {nullptr};
+
+const char *g_names[K_COUNT] = {"k_route_first", "k_route_pass1", "k_route_pass2",
+                                "k_route_final", "k_fwd", "k_runsum", "k_bwd", "k_seg",
+                                "k_cache_lookup"};
+
+hipEvent_t take() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void drain() {
+  for (Rec &r : g_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      g_ms[r.id] += ms;
+      g_n[r.id] += 1;
+    }
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_pending.clear();
+}
+
+}  // namespace
+
+void prof_begin(int id, hipStream_t s) {
+  if (!g_on) return;
+  std::lock_guard<std::mutex> lk(g_mu);
+  hipEvent_t e = take();
+  if (e && hipEventRecord(e, s) == hipSuccess) g_open[id] = e;
+}
+
+void prof_end(int id, hipStream_t s) {
+  if (!g_on) return;
+  std::lock_guard<std::mutex> lk(g_mu);
+  hipEvent_t a = g_open[id];
+  g_open[id] = nullptr;
+  if (!a) return;
+  hipEvent_t b = take();
+  if (b && hipEventRecord(b, s) == hipSuccess) g_pending.push_back({id, a, b});
+  if (g_pending.size() > 4096) drain();
+}
+
+}  // namespace ttb
+
+extern "C" {
+
+int tt_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(ttb::g_mu);
+  ttb::drain();
+  for (int i = 0; i < ttb::K_COUNT; ++i) {
+    ttb::g_ms[i] = 0.0;
+    ttb::g_n[i] = 0;
+  }
+  ttb::g_on = on != 0;
+  return TT_OK;
+}
+
+int tt_profile_read(int kernel_id, double *total_ms, int64_t *launches) {
+  if (kernel_id < 0 || kernel_id >= ttb::K_COUNT || !total_ms || !launches) return TT_EINVAL;
+  std::lock_guard<std::mutex> lk(ttb::g_mu);
+  ttb::drain();
+  *total_ms = ttb::g_ms[kernel_id];
+  *launches = ttb::g_n[kernel_id];
+  return TT_OK;
+}
+
+const char *tt_profile_kernel_name(int kernel_id) {
+  if (kernel_id < 0 || kernel_id >= ttb::K_COUNT) return nullptr;
+  return ttb::g_names[kernel_id];
+}
+
+}  // extern "C"
+
+extern "C" int tt_profile_num_kernels(void) { return ttb::K_COUNT; }

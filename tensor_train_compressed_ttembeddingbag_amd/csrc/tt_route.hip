@@ -219,18 +219,31 @@ __global__ __launch_bounds__(RT) void k_runsum(DevArgs a) {
 
 hipError_t launch_route(const DevArgs &a, hipStream_t s) {
   const int extra = a.fwd_mode ? (a.NB + RT / 64 - 1) / (RT / 64) : 0;
-  if (a.nblk + extra > 0)
+  if (a.nblk + extra > 0) {
+    prof_begin(K_ROUTE_FIRST, s);
     hipLaunchKernelGGL(k_route_first, dim3(a.nblk + extra), dim3(RT), (size_t)a.binsI3 * 4, s, a);
+    prof_end(K_ROUTE_FIRST, s);
+  }
   if (a.nblk == 0) return hipGetLastError();
+  prof_begin(K_ROUTE_PASS1, s);
   hipLaunchKernelGGL(k_route_pass, dim3(a.nblk), dim3(RT), (size_t)a.binsI3 * 8, s, a, 1);
+  prof_end(K_ROUTE_PASS1, s);
+  prof_begin(K_ROUTE_PASS2, s);
   hipLaunchKernelGGL(k_route_pass, dim3(a.nblk), dim3(RT), (size_t)a.binsA * 8, s, a, 2);
+  prof_end(K_ROUTE_PASS2, s);
+  prof_begin(K_ROUTE_FINAL, s);
   hipLaunchKernelGGL(k_route_final, dim3(a.nblk), dim3(RT), (size_t)a.binsB * 8, s, a);
+  prof_end(K_ROUTE_FINAL, s);
   return hipGetLastError();
 }
 
 hipError_t launch_runsum(const DevArgs &a, hipStream_t s) {
   const int pieces = (a.nnz + PIECE - 1) / PIECE;
-  if (pieces > 0) hipLaunchKernelGGL(k_runsum, dim3((pieces + 3) / 4), dim3(RT), 0, s, a);
+  if (pieces > 0) {
+    prof_begin(K_RUNSUM, s);
+    hipLaunchKernelGGL(k_runsum, dim3((pieces + 3) / 4), dim3(RT), 0, s, a);
+    prof_end(K_RUNSUM, s);
+  }
   return hipGetLastError();
 }
 
