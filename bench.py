@@ -1,9 +1,9 @@
 #!/usr/bin/env python3
 """TT-EmbeddingBag fwd+bwd (fused sparse SGD) benchmark on one MI355X.
 
-A step is one full pass of the hot path over one batch: tt_bag_forward then
-tt_bag_backward_sgd (and tt_cache_lookup first for the cached workload), all
-inputs resident in HBM.  Default workload: the README benchmark shape
+A step is one full pass of the hot path over one batch: tt_bag_plan (grouping),
+tt_bag_forward_planned, tt_bag_backward_sgd_planned (and tt_cache_lookup first for
+the cached workload), all inputs resident in HBM.  Default workload: the README benchmark shape
 (p=[200,220,250], q=[4,4,4], ranks=[32,32], E=11,000,000, D=64, 512 bags of 20
 uniform indices, SGD lr=0.01) with seeded synthetic data.
 
@@ -99,10 +99,13 @@ def main():
             s = slots[i % len(batches)]
             cache.lookup(b["indices"], slot_out=s, count_freq=True, dev_status=status)
             cv = (s, rows)
+        abi.tt_bag_plan(desc, b["indices"], b["offsets"], B, b["per_sample_weights"], cache=cv,
+                        ws=ws, dev_status=status)
         abi.tt_bag_forward(desc, g, b["indices"], b["offsets"], B, b["per_sample_weights"],
-                           cache=cv, out=out, ws=ws, dev_status=status)
+                           cache=cv, out=out, ws=ws, dev_status=status, planned=True)
         abi.tt_bag_backward_sgd(desc, g, b["indices"], b["offsets"], B, b["grad_out"], wl.lr,
-                                b["per_sample_weights"], cache=cv, ws=ws, dev_status=status)
+                                b["per_sample_weights"], cache=cv, ws=ws, dev_status=status,
+                                planned=True)
 
     for i in range(args.warmup):
         step(i)

@@ -65,6 +65,7 @@ extern "C" {
                                  offsets[T*B] != nnz                             */
 #define TT_DEV_BAD_SLOT    4  /* cache slot >= cache_size (element skipped)       */
 #define TT_DEV_HASH_FULL   8  /* frequency table full: new keys were not counted  */
+#define TT_DEV_STALE_PLAN 16  /* a planned call found another call's plan in ws  */
 
 /* Shape of one TT table ("Parameters": num_embeddings, embedding_dim = prod(q),
  * tt_p_shapes, tt_q_shapes, tt_ranks) and the number of tables batched
@@ -126,6 +127,37 @@ int tt_bag_backward_sgd(const tt_desc *desc, float *const cores[3],
                         int64_t num_bags, const float *per_sample_weights,
                         const tt_cache_view *cache, const float *grad_out, float lr,
                         void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
+
+/*
+ * Split of one training step into its grouping and its arithmetic.  tt_bag_plan
+ * runs the grouping step (index split, bag ids, validation, the stable sorts) and
+ * leaves the result in `ws`.  tt_bag_forward_planned / tt_bag_backward_sgd_planned
+ * take exactly the arguments of tt_bag_forward / tt_bag_backward_sgd but reuse
+ * that grouping, so a forward and backward over one batch group it only once.
+ * The plan also holds each element's per-sample weight (NULL = all ones).
+ * The workspace records a fingerprint of the plan's shape, sizes and input
+ * pointers (indices, offsets, weights, cache slots); a planned call whose arguments do not
+ * match it does nothing but set TT_DEV_STALE_PLAN in *dev_status.  The caller
+ * must re-plan after changing the CONTENTS of those buffers (the fingerprint
+ * cannot see that).  tt_bag_forward = plan + forward_planned, and
+ * tt_bag_backward_sgd = plan + backward_sgd_planned.
+ */
+int tt_bag_plan(const tt_desc *desc, const int64_t *indices, int64_t nnz,
+                const int64_t *offsets, int64_t num_bags, const float *per_sample_weights,
+                const tt_cache_view *cache, void *ws, size_t ws_bytes, int32_t *dev_status,
+                void *stream);
+
+int tt_bag_forward_planned(const tt_desc *desc, const float *const cores[3],
+                           const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                           int64_t num_bags, const float *per_sample_weights,
+                           const tt_cache_view *cache, float *out,
+                           void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
+
+int tt_bag_backward_sgd_planned(const tt_desc *desc, float *const cores[3],
+                                const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                                int64_t num_bags, const float *per_sample_weights,
+                                const tt_cache_view *cache, const float *grad_out, float lr,
+                                void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
 
 /*
  * The grouping step of both passes, exposed for inspection and tests: splits

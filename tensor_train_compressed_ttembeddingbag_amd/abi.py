@@ -22,6 +22,7 @@ TT_DEV_BAD_INDEX = 1
 TT_DEV_BAD_OFFSETS = 2
 TT_DEV_BAD_SLOT = 4
 TT_DEV_HASH_FULL = 8
+TT_DEV_STALE_PLAN = 16
 
 
 class TTError(RuntimeError):
@@ -49,6 +50,11 @@ _SIG = {
                                       _P, _P]),
     "tt_bag_backward_sgd": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P, ctypes.c_float,
                                            _P, ctypes.c_size_t, _P, _P]),
+    "tt_bag_plan": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _P, _P, ctypes.c_size_t, _P, _P]),
+    "tt_bag_forward_planned": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P, _P,
+                                              ctypes.c_size_t, _P, _P]),
+    "tt_bag_backward_sgd_planned": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P,
+                                                   ctypes.c_float, _P, ctypes.c_size_t, _P, _P]),
     "tt_bag_route": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _I64, _P, _P, _P, ctypes.c_size_t,
                                     _P, _P]),
     "tt_cache_create": (ctypes.c_int, [_P, _P, _I64, _I64]),
@@ -158,10 +164,32 @@ def _cache_view(cache):
     return v, rows.shape[0]
 
 
+def tt_bag_plan(desc: TTDesc, indices, offsets, num_bags: int, per_sample_weights=None,
+                cache=None, ws=None, dev_status=None, stream=None) -> torch.Tensor:
+    """Run the grouping step into ws (allocated if None) and return ws."""
+    _need(indices, torch.int64, "indices")
+    _need(offsets, torch.int64, "offsets")
+    if per_sample_weights is not None:
+        _need(per_sample_weights, torch.float32, "per_sample_weights")
+    view, csize = _cache_view(cache)
+    if ws is None:
+        ws = workspace(desc, indices.numel(), num_bags, csize or 0, indices.device)
+    _need(ws, torch.uint8, "ws")
+    if dev_status is not None:
+        _need(dev_status, torch.int32, "dev_status")
+    rc = lib().tt_bag_plan(ctypes.byref(desc), _ptr(indices), indices.numel(), _ptr(offsets),
+                           int(num_bags), _ptr(per_sample_weights),
+                           None if view is None else ctypes.byref(view), _ptr(ws),
+                           ws.numel(), _ptr(dev_status), _stream(stream))
+    _check("tt_bag_plan", rc)
+    return ws
+
+
 def tt_bag_forward(desc: TTDesc, cores, indices, offsets, num_bags: int,
                    per_sample_weights=None, cache=None, out=None, ws=None,
-                   dev_status=None, stream=None) -> torch.Tensor:
-    """out[T*num_bags, D] = pooled rows (see tt_bag.h).  cache = (slots, rows) or None."""
+                   dev_status=None, stream=None, planned: bool = False) -> torch.Tensor:
+    """out[T*num_bags, D] = pooled rows (see tt_bag.h).  cache = (slots, rows) or None.
+    planned=True reuses the grouping that tt_bag_plan left in ws."""
     _need(indices, torch.int64, "indices")
     _need(offsets, torch.int64, "offsets")
     if per_sample_weights is not None:
@@ -176,18 +204,20 @@ def tt_bag_forward(desc: TTDesc, cores, indices, offsets, num_bags: int,
     _need(ws, torch.uint8, "ws")
     if dev_status is not None:
         _need(dev_status, torch.int32, "dev_status")
-    rc = lib().tt_bag_forward(ctypes.byref(desc), _cores(cores), _ptr(indices), indices.numel(),
+    fn = lib().tt_bag_forward_planned if planned else lib().tt_bag_forward
+    rc = fn(ctypes.byref(desc), _cores(cores), _ptr(indices), indices.numel(),
                               _ptr(offsets), int(num_bags), _ptr(per_sample_weights),
                               None if view is None else ctypes.byref(view), _ptr(out), _ptr(ws),
                               ws.numel(), _ptr(dev_status), _stream(stream))
-    _check("tt_bag_forward", rc)
+    _check("tt_bag_forward_planned" if planned else "tt_bag_forward", rc)
     return out
 
 
 def tt_bag_backward_sgd(desc: TTDesc, cores, indices, offsets, num_bags: int, grad_out,
                         lr: float, per_sample_weights=None, cache=None, ws=None,
-                        dev_status=None, stream=None) -> None:
-    """In-place fused SGD on the cores (and cache rows) touched by this batch."""
+                        dev_status=None, stream=None, planned: bool = False) -> None:
+    """In-place fused SGD on the cores (and cache rows) touched by this batch.
+    planned=True reuses the grouping that tt_bag_plan left in ws."""
     _need(indices, torch.int64, "indices")
     _need(offsets, torch.int64, "offsets")
     _need(grad_out, torch.float32, "grad_out")
@@ -199,12 +229,13 @@ def tt_bag_backward_sgd(desc: TTDesc, cores, indices, offsets, num_bags: int, gr
     _need(ws, torch.uint8, "ws")
     if dev_status is not None:
         _need(dev_status, torch.int32, "dev_status")
-    rc = lib().tt_bag_backward_sgd(ctypes.byref(desc), _cores(cores), _ptr(indices), indices.numel(),
+    fn = lib().tt_bag_backward_sgd_planned if planned else lib().tt_bag_backward_sgd
+    rc = fn(ctypes.byref(desc), _cores(cores), _ptr(indices), indices.numel(),
                                    _ptr(offsets), int(num_bags), _ptr(per_sample_weights),
                                    None if view is None else ctypes.byref(view), _ptr(grad_out),
                                    float(lr), _ptr(ws), ws.numel(), _ptr(dev_status),
                                    _stream(stream))
-    _check("tt_bag_backward_sgd", rc)
+    _check("tt_bag_backward_sgd_planned" if planned else "tt_bag_backward_sgd", rc)
 
 
 def tt_bag_route(desc: TTDesc, indices, offsets, num_bags: int, slots=None, cache_size: int = 0,

@@ -38,7 +38,8 @@ struct Plan {
   size_t ws_total = 0;
   // byte offsets inside the workspace
   size_t o_ctr, o_hdr, o_einfo, o_histA, o_histB, o_histI3, o_orderI3, o_orderA, o_sn, o_sdA,
-      o_sdB, o_sdI3, o_sbag, o_pos, o_grp, o_chunk, o_f1, o_f3, o_p1, o_p3, o_frag, o_gacc;
+      o_sdB, o_sdI3, o_sbag, o_sw, o_posI3, o_posA, o_sposI3, o_sposA, o_fitem, o_grp, o_chunk,
+      o_l1, o_l3, o_p1, o_p3, o_frag, o_p2;
 };
 
 size_t carve(size_t &cur, size_t bytes) {
@@ -90,17 +91,31 @@ int make_plan(const tt_desc *d, int64_t nnz, int64_t num_bags, int64_t cache_siz
   a.NHB = NHB;
   const int Rmax = a.R1 > a.R2 ? a.R1 : a.R2;
   P->RP = Rmax <= 16 ? 16 : (Rmax <= 32 ? 32 : 64);
-  P->lds_fwd = fwd_lds_bytes(P->RP);
-  int CHI = 64;
-  while (CHI > 1 && bwd_lds_bytes(P->RP, CHI, a.D, a.q3) > LDS_LIMIT) CHI >>= 1;
-  if (bwd_lds_bytes(P->RP, CHI, a.D, a.q3) > LDS_LIMIT || P->lds_fwd > LDS_LIMIT) return TT_ESHAPE;
+  P->lds_fwd = fwd_lds_bytes(P->RP, a.q3);
+  // work items of P positions: small for small ranks (many workgroups in flight), larger
+  // for rank 64 (fewer dG2 partials of 16x the size)
+  a.P = P->RP <= 32 ? 32 : 64;
+  // backward chunk: items <= P; reduction slots and items shrink until two workgroups
+  // fit one CU's LDS (or, failing that, one)
+  int CHI = a.P, nred = NW;
+  const size_t lds_two = LDS_LIMIT / 2 - 1024;
+  while (bwd_lds_bytes(P->RP, CHI, a.D, a.q3, nred) > lds_two && nred > 2) nred >>= 1;
+  while (bwd_lds_bytes(P->RP, CHI, a.D, a.q3, nred) > LDS_LIMIT) {
+    if (nred > 2) nred >>= 1;
+    else if (CHI > 8) CHI >>= 1;
+    else if (nred > 1) nred >>= 1;
+    else break;
+  }
+  if (bwd_lds_bytes(P->RP, CHI, a.D, a.q3, nred) > LDS_LIMIT || P->lds_fwd > LDS_LIMIT)
+    return TT_ESHAPE;
   a.CHI = CHI;
+  a.NRED = nred;
   {
     const int rows = NW * 16 * bwd_mbw(P->RP);
     const int pairs = rows / a.q1;
     a.CHPb = pairs < CHP ? pairs : CHP;
   }
-  P->lds_bwd = bwd_lds_bytes(P->RP, CHI, a.D, a.q3);
+  P->lds_bwd = bwd_lds_bytes(P->RP, CHI, a.D, a.q3, nred);
 
   const size_t n = (size_t)nnz, nb = (size_t)a.nblk, G = (size_t)T * a.p2;
   size_t cur = 0;
@@ -117,15 +132,20 @@ int make_plan(const tt_desc *d, int64_t nnz, int64_t num_bags, int64_t cache_siz
   P->o_sdB = carve(cur, n * 4);
   P->o_sdI3 = carve(cur, n * 4);
   P->o_sbag = carve(cur, n * 4);
-  P->o_pos = carve(cur, n * 4);
+  P->o_sw = carve(cur, n * 4);
+  P->o_posI3 = carve(cur, n * 4);
+  P->o_posA = carve(cur, n * 4);
+  P->o_sposI3 = carve(cur, n * 4);
+  P->o_sposA = carve(cur, n * 4);
+  P->o_fitem = carve(cur, (size_t)items_max(a) * sizeof(int4));
   P->o_grp = carve(cur, ((size_t)binsB + 1) * 4);
   P->o_chunk = carve(cur, (G + 1) * 4);
-  P->o_f1 = carve(cur, n * 4);
-  P->o_f3 = carve(cur, n * 4);
+  P->o_l1 = carve(cur, n * 4);
+  P->o_l3 = carve(cur, n * 4);
   P->o_p1 = carve(cur, n * (size_t)a.q1 * a.R1 * 4);
   P->o_p3 = carve(cur, n * (size_t)a.R2 * a.q3 * 4);
   P->o_frag = carve(cur, n * (size_t)a.D * 4);
-  P->o_gacc = carve(cur, G * (size_t)a.R1 * a.q2 * a.R2 * 4);
+  P->o_p2 = carve(cur, (size_t)items_max(a) * a.R1 * a.q2 * a.R2 * 4);
   P->ws_total = cur;
   return TT_OK;
 }
@@ -146,15 +166,20 @@ void bind_ws(Plan *P, void *ws) {
   a.s_dB = (int *)(b + P->o_sdB);
   a.s_dI3 = (int *)(b + P->o_sdI3);
   a.s_bag = (int *)(b + P->o_sbag);
-  a.pos_of = (int *)(b + P->o_pos);
+  a.s_w = (float *)(b + P->o_sw);
+  a.posI3_of = (int *)(b + P->o_posI3);
+  a.posA_of = (int *)(b + P->o_posA);
+  a.s_posI3 = (int *)(b + P->o_sposI3);
+  a.s_posA = (int *)(b + P->o_sposA);
+  a.fitem = (int4 *)(b + P->o_fitem);
   a.grp_off = (int *)(b + P->o_grp);
   a.chunk_pre = (int *)(b + P->o_chunk);
-  a.flag1 = (int *)(b + P->o_f1);
-  a.flag3 = (int *)(b + P->o_f3);
+  a.link1 = (int *)(b + P->o_l1);
+  a.link3 = (int *)(b + P->o_l3);
   a.part1 = (float *)(b + P->o_p1);
   a.part3 = (float *)(b + P->o_p3);
   a.frag = (float *)(b + P->o_frag);
-  a.gacc = (float *)(b + P->o_gacc);
+  a.part2 = (float *)(b + P->o_p2);
   a.epoch = g_epoch.fetch_add(1);
   if (a.epoch == 0) a.epoch = g_epoch.fetch_add(1);
 }
@@ -201,27 +226,126 @@ size_t tt_bag_workspace_size(const tt_desc *desc, int64_t nnz, int64_t num_bags,
 
 static int finish(hipError_t e) { return e == hipSuccess ? TT_OK : TT_EHIP; }
 
+// FNV-1a over the call's shape, sizes and input pointers: names the plan in a workspace.
+static unsigned plan_fingerprint(const tt_desc *d, int64_t nnz, int64_t num_bags,
+                                 int64_t cache_size, const void *idx, const void *off,
+                                 const void *psw, const void *slots) {
+  unsigned h = 2166136261u;
+  auto mix = [&h](uint64_t v) {
+    for (int i = 0; i < 8; ++i) {
+      h ^= (unsigned)(v & 0xff);
+      h *= 16777619u;
+      v >>= 8;
+    }
+  };
+  mix((uint64_t)d->num_tables);
+  mix((uint64_t)d->num_embeddings);
+  for (int k = 0; k < 3; ++k) { mix((uint64_t)d->p[k]); mix((uint64_t)d->q[k]); }
+  mix((uint64_t)d->ranks[0]);
+  mix((uint64_t)d->ranks[1]);
+  mix((uint64_t)nnz);
+  mix((uint64_t)num_bags);
+  mix((uint64_t)cache_size);
+  mix((uint64_t)(uintptr_t)idx);
+  mix((uint64_t)(uintptr_t)off);
+  mix((uint64_t)(uintptr_t)psw);
+  mix((uint64_t)(uintptr_t)slots);
+  return h;
+}
+
+// argument checks shared by every call that takes a batch; fills P and binds ws
+static int prepare(Plan *P, const tt_desc *desc, const int64_t *indices, int64_t nnz,
+                   const int64_t *offsets, int64_t num_bags, const float *psw,
+                   const tt_cache_view *cache, void *ws, size_t ws_bytes, int32_t *dev_status) {
+  const int64_t csize = cache ? cache->cache_size : 0;
+  int rc = make_plan(desc, nnz, num_bags, csize, P);
+  if (rc) return rc;
+  if (!offsets || (nnz > 0 && !indices)) return TT_EINVAL;
+  if ((rc = check_ws(*P, ws, ws_bytes))) return rc;
+  if ((rc = set_cache(P, cache, nnz))) return rc;
+  bind_ws(P, ws);
+  DevArgs &a = P->a;
+  a.idx = indices;
+  a.off = offsets;
+  a.psw = psw;
+  a.status = dev_status;
+  a.plan_fp = plan_fingerprint(desc, nnz, num_bags, csize, indices, offsets, psw,
+                               cache ? (const void *)cache->slots : nullptr);
+  return TT_OK;
+}
+
+static int check_cores(const float *const cores[3]) {
+  return (!cores || !cores[0] || !cores[1] || !cores[2]) ? TT_EINVAL : TT_OK;
+}
+
+int tt_bag_plan(const tt_desc *desc, const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                int64_t num_bags, const float *per_sample_weights, const tt_cache_view *cache,
+                void *ws, size_t ws_bytes, int32_t *dev_status, void *stream) {
+  Plan P;
+  int rc = prepare(&P, desc, indices, nnz, offsets, num_bags, per_sample_weights, cache, ws,
+                   ws_bytes, dev_status);
+  if (rc) return rc;
+  return finish(launch_route(P.a, (hipStream_t)stream));
+}
+
+int tt_bag_forward_planned(const tt_desc *desc, const float *const cores[3],
+                           const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                           int64_t num_bags, const float *per_sample_weights,
+                           const tt_cache_view *cache, float *out, void *ws, size_t ws_bytes,
+                           int32_t *dev_status, void *stream) {
+  Plan P;
+  int rc = prepare(&P, desc, indices, nnz, offsets, num_bags, per_sample_weights, cache, ws,
+                   ws_bytes, dev_status);
+  if (rc) return rc;
+  if ((rc = check_cores(cores)) || !out) return rc ? rc : TT_EINVAL;
+  DevArgs &a = P.a;
+  a.psw = per_sample_weights;
+  a.G1 = (float *)cores[0]; a.G2 = (float *)cores[1]; a.G3 = (float *)cores[2];
+  a.Y = out;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_yinit(a, s);
+  if (e == hipSuccess && a.nnz > 0) e = launch_fwd(a, P.RP, P.lds_fwd, s);
+  return finish(e);
+}
+
+int tt_bag_backward_sgd_planned(const tt_desc *desc, float *const cores[3],
+                                const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                                int64_t num_bags, const float *per_sample_weights,
+                                const tt_cache_view *cache, const float *grad_out, float lr,
+                                void *ws, size_t ws_bytes, int32_t *dev_status, void *stream) {
+  Plan P;
+  int rc = prepare(&P, desc, indices, nnz, offsets, num_bags, per_sample_weights, cache, ws,
+                   ws_bytes, dev_status);
+  if (rc) return rc;
+  if ((rc = check_cores(cores)) || !grad_out) return rc ? rc : TT_EINVAL;
+  if (!std::isfinite(lr)) return TT_EINVAL;
+  if (nnz == 0) return TT_OK;
+  DevArgs &a = P.a;
+  a.psw = per_sample_weights;
+  a.G1 = cores[0]; a.G2 = cores[1]; a.G3 = cores[2];
+  a.dY = grad_out;
+  a.lr = lr;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_runsum(a, s);
+  if (e == hipSuccess) e = launch_bwd(a, P.RP, P.lds_bwd, s);
+  if (e == hipSuccess) e = launch_seg(a, s);
+  return finish(e);
+}
+
 int tt_bag_forward(const tt_desc *desc, const float *const cores[3], const int64_t *indices,
                    int64_t nnz, const int64_t *offsets, int64_t num_bags,
                    const float *per_sample_weights, const tt_cache_view *cache, float *out,
                    void *ws, size_t ws_bytes, int32_t *dev_status, void *stream) {
   Plan P;
-  const int64_t csize = cache ? cache->cache_size : 0;
-  int rc = make_plan(desc, nnz, num_bags, csize, &P);
+  int rc = prepare(&P, desc, indices, nnz, offsets, num_bags, per_sample_weights, cache, ws,
+                   ws_bytes, dev_status);
   if (rc) return rc;
-  if (!cores || !cores[0] || !cores[1] || !cores[2] || !offsets || !out) return TT_EINVAL;
-  if (nnz > 0 && !indices) return TT_EINVAL;
-  if ((rc = check_ws(P, ws, ws_bytes))) return rc;
-  if ((rc = set_cache(&P, cache, nnz))) return rc;
-  bind_ws(&P, ws);
-  DevArgs &a = P.a;
-  a.idx = indices; a.off = offsets; a.psw = per_sample_weights;
-  a.G1 = (float *)cores[0]; a.G2 = (float *)cores[1]; a.G3 = (float *)cores[2];
-  a.Y = out; a.status = dev_status; a.fwd_mode = 1;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_route(a, s);
-  if (e == hipSuccess && a.nnz > 0) e = launch_fwd(a, P.RP, P.lds_fwd, s);
-  return finish(e);
+  if ((rc = check_cores(cores)) || !out) return rc ? rc : TT_EINVAL;
+  rc = tt_bag_plan(desc, indices, nnz, offsets, num_bags, per_sample_weights, cache, ws, ws_bytes,
+                   dev_status, stream);
+  if (rc) return rc;
+  return tt_bag_forward_planned(desc, cores, indices, nnz, offsets, num_bags, per_sample_weights,
+                                cache, out, ws, ws_bytes, dev_status, stream);
 }
 
 int tt_bag_backward_sgd(const tt_desc *desc, float *const cores[3], const int64_t *indices,
@@ -230,26 +354,18 @@ int tt_bag_backward_sgd(const tt_desc *desc, float *const cores[3], const int64_
                         const float *grad_out, float lr, void *ws, size_t ws_bytes,
                         int32_t *dev_status, void *stream) {
   Plan P;
-  const int64_t csize = cache ? cache->cache_size : 0;
-  int rc = make_plan(desc, nnz, num_bags, csize, &P);
+  int rc = prepare(&P, desc, indices, nnz, offsets, num_bags, per_sample_weights, cache, ws,
+                   ws_bytes, dev_status);
   if (rc) return rc;
-  if (!cores || !cores[0] || !cores[1] || !cores[2] || !offsets || !grad_out) return TT_EINVAL;
-  if (nnz > 0 && !indices) return TT_EINVAL;
+  if ((rc = check_cores(cores)) || !grad_out) return rc ? rc : TT_EINVAL;
   if (!std::isfinite(lr)) return TT_EINVAL;
-  if ((rc = check_ws(P, ws, ws_bytes))) return rc;
-  if ((rc = set_cache(&P, cache, nnz))) return rc;
   if (nnz == 0) return TT_OK;
-  bind_ws(&P, ws);
-  DevArgs &a = P.a;
-  a.idx = indices; a.off = offsets; a.psw = per_sample_weights;
-  a.G1 = cores[0]; a.G2 = cores[1]; a.G3 = cores[2];
-  a.dY = grad_out; a.lr = lr; a.status = dev_status; a.fwd_mode = 0;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_route(a, s);
-  if (e == hipSuccess) e = launch_runsum(a, s);
-  if (e == hipSuccess) e = launch_bwd(a, P.RP, P.lds_bwd, s);
-  if (e == hipSuccess) e = launch_seg(a, s);
-  return finish(e);
+  rc = tt_bag_plan(desc, indices, nnz, offsets, num_bags, per_sample_weights, cache, ws, ws_bytes,
+                   dev_status, stream);
+  if (rc) return rc;
+  return tt_bag_backward_sgd_planned(desc, cores, indices, nnz, offsets, num_bags,
+                                     per_sample_weights, cache, grad_out, lr, ws, ws_bytes,
+                                     dev_status, stream);
 }
 
 // copies the grouping order: valid elements first (see tt_bag.h)
@@ -265,21 +381,25 @@ int tt_bag_route(const tt_desc *desc, const int64_t *indices, int64_t nnz,
                  const int64_t *offsets, int64_t num_bags, const int32_t *slots,
                  int64_t cache_size, int32_t *order_out, int32_t *group_off_out, void *ws,
                  size_t ws_bytes, int32_t *dev_status, void *stream) {
+  if (!order_out || !group_off_out) return TT_EINVAL;
+  tt_cache_view view{slots, nullptr, cache_size};
   Plan P;
-  int rc = make_plan(desc, nnz, num_bags, slots ? cache_size : 0, &P);
+  const tt_cache_view *cv = slots ? &view : nullptr;
+  if (slots && cache_size < 1) return TT_EINVAL;
+  // the rows pointer is not needed for grouping
+  const int64_t csize = cv ? cache_size : 0;
+  int rc = make_plan(desc, nnz, num_bags, csize, &P);
   if (rc) return rc;
-  if (!offsets || !order_out || !group_off_out || (nnz > 0 && !indices)) return TT_EINVAL;
+  if (!offsets || (nnz > 0 && !indices)) return TT_EINVAL;
   if ((rc = check_ws(P, ws, ws_bytes))) return rc;
   bind_ws(&P, ws);
   DevArgs &a = P.a;
-  a.idx = indices; a.off = offsets; a.slots = slots; a.status = dev_status; a.fwd_mode = 0;
+  a.idx = indices; a.off = offsets; a.slots = slots; a.status = dev_status;
+  a.plan_fp = plan_fingerprint(desc, nnz, num_bags, csize, indices, offsets, nullptr, slots);
   hipStream_t s = (hipStream_t)stream;
   const int G = a.T * a.p2;
   hipError_t e = hipSuccess;
-  if (nnz == 0) {
-    e = hipMemsetAsync(group_off_out, 0, (G + 2) * sizeof(int32_t), s);
-    return finish(e);
-  }
+  if (nnz == 0) return finish(hipMemsetAsync(group_off_out, 0, (G + 2) * sizeof(int32_t), s));
   e = launch_route(a, s);
   if (e == hipSuccess) {
     const int n = (int)nnz > G + 2 ? (int)nnz : G + 2;

@@ -4,30 +4,53 @@
 
 namespace ttb {
 
-// exclusive scan of arr[0..len) in global memory by one whole block.
+// inclusive scan across the 64 lanes of a wave
+static __device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// exclusive scan of arr[0..len) in global memory by one whole block (blockDim a
+// multiple of 64, at most 1024).  Each thread owns a contiguous run of the array;
+// the per-thread sums are scanned with wave shuffles.  s_tmp: >= 17 ints of LDS.
 static __device__ void block_exclusive_scan(int *arr, int len, int *s_tmp) {
-  const int nt = blockDim.x, tid = threadIdx.x;
+  const int nt = blockDim.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int per = (len + nt - 1) / nt;
   const int beg = min(tid * per, len), end = min(beg + per, len);
   int sum = 0;
-  for (int i = beg; i < end; ++i) sum += arr[i];
-  s_tmp[tid] = sum;
+  for (int i0 = beg; i0 < end; i0 += 8) {  // eight loads in flight
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = arr[min(i0 + u, len - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += (i0 + u < end) ? v[u] : 0;
+  }
+  const int incl = wave_incl_scan(sum);
+  if (lane == 63) s_tmp[w] = incl;
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < nt; ++i) {
-      const int v = s_tmp[i];
-      s_tmp[i] = run;
-      run += v;
-    }
-    s_tmp[nt] = run;
+  if (w == 0) {
+    const int nw = nt >> 6;
+    const int v = lane < nw ? s_tmp[lane] : 0;
+    const int vi = wave_incl_scan(v);
+    if (lane < nw) s_tmp[lane] = vi - v;
   }
   __syncthreads();
-  int run = s_tmp[tid];
-  for (int i = beg; i < end; ++i) {
-    const int v = arr[i];
-    arr[i] = run;
-    run += v;
+  int run = s_tmp[w] + incl - sum;
+  for (int i0 = beg; i0 < end; i0 += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = arr[min(i0 + u, len - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (i0 + u < end) {
+        arr[i0 + u] = run;
+        run += v[u];
+      }
   }
   __threadfence_block();
   __syncthreads();

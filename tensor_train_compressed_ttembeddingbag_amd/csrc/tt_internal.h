@@ -27,8 +27,8 @@ constexpr int RB = 1024;        // routing block: elements per block
 constexpr int RT = 256;         // routing block: threads (4 elements each)
 constexpr int HB = 512;         // cache slots per hit bin
 constexpr int MAX_BINS = 8192;  // digit range of one counting-sort pass
-constexpr int PIECE = 64;       // run-sum piece length (positions)
-constexpr int FWD_CHE = 64;     // forward chunk: elements per workgroup
+constexpr int PIECE = 64;       // run-sum: positions per wave
+constexpr int ITEM_MAX = 64;    // most positions of one contraction work item
 constexpr int WG = 512;         // contraction workgroup: 8 waves
 constexpr int NW = WG / 64;
 constexpr int MBW = 2;          // forward: M-blocks (16 rows of (pair, j1)) per wave
@@ -36,12 +36,14 @@ constexpr int CHP = 64;         // backward chunk: most (i1,i2) pairs held in LD
 // backward: M-blocks per wave (register budget: one for rank-64 tiles)
 constexpr int bwd_mbw(int RP) { return RP == 64 ? 1 : 2; }
 constexpr int MAXQ3 = 16;
+constexpr int STAGE_U = 8;      // global loads in flight per thread when staging into LDS
 
 // header words inside the workspace (after three 64-bit "last block" counters)
 enum {
   H_NFWD = 3,       // number of forward work items
   H_HIT_BEG = 4, H_HIT_END = 5,  // hit region [beg, end) of the final order
   H_VALID = 6,      // number of valid (non-skipped) elements
+  H_PLAN = 7,       // fingerprint of the call that made the grouping (tt_bag_plan)
   H_WORDS = 64
 };
 
@@ -57,7 +59,9 @@ struct DevArgs {
   int NHB;
   int CHI;          // backward chunk: max items (distinct indices)
   int CHPb;         // backward chunk: max pairs (<= CHP)
-  int fwd_mode;     // route: initialise out
+  int P;            // work item: positions per piece (32 or 64, divides PIECE)
+  int NRED;         // backward: LDS slots of the cross-wave dG2 reduction (divides NW)
+  unsigned plan_fp;  // fingerprint of (shape, sizes, input pointers) of the plan
   // inputs / outputs
   const int64_t *idx;
   const int64_t *off;
@@ -76,11 +80,16 @@ struct DevArgs {
   int4 *einfo;      // per element: dA (t,i1), dB (t,i2), dI3 (t,i3), bag
   int *histA, *histB, *histI3;
   int *orderI3, *orderA;
-  int *s_n, *s_dA, *s_dB, *s_dI3, *s_bag, *pos_of;
+  int *s_n, *s_dA, *s_dB, *s_dI3, *s_bag;
+  float *s_w;       // per-sample weight in the final order (1 without weights)
+  int *posI3_of, *posA_of;   // element -> position in orderI3 / orderA
+  int *s_posI3, *s_posA;     // final position -> position in orderI3 / orderA
+  int4 *fitem;      // work items: (group, first position, end position, 0)
   int *grp_off;     // [binsB + 1]
   int *chunk_pre;   // [T*p2 + 1]
-  int *flag1, *flag3;
-  float *part1, *part3, *frag, *gacc;
+  int *link1, *link3;  // orderA / orderI3 position -> final position of the partial, or -1
+  float *part1, *part3, *frag;
+  float *part2;     // dG2 partial per work item [items][R1][q2][R2]
 };
 
 // ---------------------------------------------------------------- helpers
@@ -88,10 +97,13 @@ __device__ __forceinline__ void set_status(int32_t *st, int bit) {
   if (st) atomicOr(st, bit);
 }
 
+// device status bit for a planned call whose workspace holds another plan
+constexpr int DEV_STALE_PLAN = 16;
+
 // kernels named by the optional per-kernel timer (tt_prof.hip)
 enum KernelId {
   K_ROUTE_FIRST, K_ROUTE_PASS1, K_ROUTE_PASS2, K_ROUTE_FINAL, K_FWD, K_RUNSUM, K_BWD, K_SEG,
-  K_CACHE_LOOKUP, K_COUNT
+  K_CACHE_LOOKUP, K_YINIT, K_COUNT
 };
 void prof_begin(int id, hipStream_t s);
 void prof_end(int id, hipStream_t s);
@@ -99,10 +111,17 @@ void prof_end(int id, hipStream_t s);
 // host launchers (each kernel is launched from the file that defines it)
 hipError_t launch_route(const DevArgs &a, hipStream_t s);   // the four grouping kernels
 hipError_t launch_runsum(const DevArgs &a, hipStream_t s);
+hipError_t launch_yinit(const DevArgs &a, hipStream_t s);
 hipError_t launch_seg(const DevArgs &a, hipStream_t s);
 hipError_t launch_fwd(const DevArgs &a, int RP, size_t lds, hipStream_t s);
 hipError_t launch_bwd(const DevArgs &a, int RP, size_t lds, hipStream_t s);
-size_t fwd_lds_bytes(int RP);
-size_t bwd_lds_bytes(int RP, int CHI, int D, int q3);
+size_t fwd_lds_bytes(int RP, int q3);
+size_t bwd_lds_bytes(int RP, int CHI, int D, int q3, int nred);
+
+// Work items of both contraction kernels: every overlap of a miss group with a
+// P-aligned piece of the final order.  Upper bound of their number:
+__host__ __device__ inline int items_max(const DevArgs &a) {
+  return a.T * a.p2 + (a.nnz + a.P - 1) / a.P;
+}
 
 }  // namespace ttb

@@ -9,46 +9,94 @@
 // (i1,i2); the page's kernel relies on cub for its device-wide primitives, here
 // each pass is a hand-written stable counting sort (LSD, three digits).
 #include "tt_device.h"
+#include "tt_mfma.h"
 
 namespace ttb {
 
-__global__ __launch_bounds__(RT) void k_route_first(DevArgs a) {
-  extern __shared__ int lds_i[];
-  __shared__ int s_scan[RT + 1];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  if ((int)blockIdx.x >= a.nblk) {
-    // forward only: out[b] = sum of the weighted cache rows of bag b (zero if none)
-    const int b = (blockIdx.x - a.nblk) * (RT / 64) + w;
-    if (b >= a.NB) return;
-    int64_t lo = a.off[b], hi = a.off[b + 1];
-    lo = lo < 0 ? 0 : (lo > a.nnz ? a.nnz : lo);
-    hi = hi < lo ? lo : (hi > a.nnz ? a.nnz : hi);
-    for (int d = lane; d < a.D; d += 64) {
-      float acc = 0.f;
-      if (a.has_cache) {
-        for (int64_t n = lo; n < hi; ++n) {
-          const int s = a.slots[n];
-          if (s >= 0 && s < a.cache_size) {
-            const float wt = a.psw ? a.psw[n] : 1.f;
-            acc += wt * a.crows[(size_t)s * a.D + d];
-          }
-        }
-      }
-      a.Y[(size_t)b * a.D + d] = acc;
-    }
-    return;
+static __device__ __forceinline__ bool a_le(const int64_t *off, int c, int n) {
+  return off[c] <= (int64_t)n;
+}
+
+// Largest b in [0, NB) with off[b] <= n, found by half of the block (128 threads,
+// `half` = 0 or 1) with a 128-ary search: one global load per thread per round.
+static __device__ int half_find_bag(const int64_t *off, int NB, int n, int half, int *s_red) {
+  const int t = threadIdx.x - half * 128, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int lo = 0;
+  // invariant: the answer lies in [lo, lo + span).  The number of rounds depends on NB
+  // only, so both halves meet every barrier.
+  for (int span = NB; span > 1;) {
+    const int step = (span + 127) / 128;
+    const int c = lo + t * step;
+    const bool ok = t * step < span && c < NB && a_le(off, c, n);
+    int best = wave_max(ok ? t : -1);
+    if (lane == 0) s_red[w] = best;
+    __syncthreads();
+    best = max(s_red[half * 2], s_red[half * 2 + 1]);
+    __syncthreads();
+    if (best > 0) lo += best * step;  // best < 0 only with invalid offsets: keep lo
+    span = step;
   }
+  return lo;
+}
+
+constexpr int ROUTE_MAX_BAGS = 2048;  // offsets of one routing block kept in LDS
+
+__global__ __launch_bounds__(RT) void k_route_first(DevArgs a) {
+  extern __shared__ int lds_i[];       // [binsI3] histogram, then the block's offsets
+  __shared__ int s_scan[RT + 1];
+  __shared__ int s_red[8];
+  __shared__ int s_b[2];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int blk = blockIdx.x;
-  for (int i = tid; i < a.binsI3; i += RT) lds_i[i] = 0;
+  const int base = blk * RB, last = min(base + RB, a.nnz) - 1;
+  int *hist = lds_i;
+  int *s_off = lds_i + a.binsI3;
+  // bags overlapping [base, last]: one 128-ary search per half of the block.  The
+  // two halves search in lockstep (same NB, same number of rounds).
+  {
+    const int half = tid >> 7;
+    const int b = half_find_bag(a.off, a.NB, half ? last : base, half, s_red);
+    if ((tid & 127) == 0) s_b[half] = b;
+  }
+  for (int i = tid; i < a.binsI3; i += RT) hist[i] = 0;
+  __syncthreads();
+  const int b_lo = s_b[0], b_hi = max(s_b[1], s_b[0]);
+  const int nbag = b_hi - b_lo + 1;
+  const bool in_lds = nbag + 1 <= ROUTE_MAX_BAGS;
+  if (in_lds)
+    for (int j = tid; j <= nbag; j += RT) {
+      int64_t o = a.off[b_lo + j];
+      s_off[j] = (int)(o < 0 ? 0 : (o > a.nnz ? a.nnz : o));
+    }
   __syncthreads();
   const int dropA = a.binsA - 1, dropB = a.binsB - 1, dropI = a.binsI3 - 1;
+  // all loads of the block's elements first (clamped addresses), then the arithmetic
+  int64_t iv[4];
+  int sv[4];
+#pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int e = blk * RB + w * 256 + r * 64 + lane;
+    const int e = min(base + w * 256 + r * 64 + lane, a.nnz - 1);
+    iv[r] = a.idx[e];
+    sv[r] = (a.has_cache && a.slots) ? a.slots[e] : -1;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int e = base + w * 256 + r * 64 + lane;
     if (e >= a.nnz) continue;
-    const int b = find_bag(a.off, a.NB, e);
+    int b;
+    if (in_lds) {
+      int lo = 0, hi = nbag;  // largest j with s_off[j] <= e
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_off[mid] <= e) lo = mid; else hi = mid;
+      }
+      b = b_lo + lo;
+    } else {
+      b = find_bag(a.off, a.NB, e);
+    }
     const int t = b / a.B;
     int dA, dB, dI;
-    const int slot = (a.has_cache && a.slots) ? a.slots[e] : -1;
+    const int slot = sv[r];
     if (slot >= 0) {
       if (slot >= a.cache_size) {
         set_status(a.status, TT_DEV_BAD_SLOT);
@@ -59,7 +107,7 @@ __global__ __launch_bounds__(RT) void k_route_first(DevArgs a) {
         dI = dropI;
       }
     } else {
-      const int64_t i = a.idx[e];
+      const int64_t i = iv[r];
       if (i < 0 || i >= a.E) {
         set_status(a.status, TT_DEV_BAD_INDEX);
         dA = dropA; dB = dropB; dI = dropI;
@@ -74,7 +122,7 @@ __global__ __launch_bounds__(RT) void k_route_first(DevArgs a) {
       }
     }
     a.einfo[e] = make_int4(dA, dB, dI, b);
-    atomicAdd(&lds_i[dI], 1);
+    atomicAdd(&hist[dI], 1);
   }
   // offsets must be a CSR over [0, nnz]
   const int gt = blk * RT + tid, gn = a.nblk * RT;
@@ -89,8 +137,38 @@ __global__ __launch_bounds__(RT) void k_route_first(DevArgs a) {
   for (int k = gt; k < a.binsA * a.nblk; k += gn) a.histA[k] = 0;
   for (int k = gt; k < a.binsB * a.nblk; k += gn) a.histB[k] = 0;
   __syncthreads();
-  for (int i = tid; i < a.binsI3; i += RT) a.histI3[(size_t)i * a.nblk + blk] = lds_i[i];
+  for (int i = tid; i < a.binsI3; i += RT) a.histI3[(size_t)i * a.nblk + blk] = hist[i];
   if (last_block(&a.ctr[0], a.nblk, a.epoch)) block_exclusive_scan(a.histI3, a.binsI3 * a.nblk, s_scan);
+}
+
+// Forward: out[b] = sum of the weighted cache rows of bag b (zero when it has none);
+// the contraction kernel then adds the misses.  One wave per bag.
+__global__ __launch_bounds__(RT) void k_yinit(DevArgs a) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int b = blockIdx.x * (RT / 64) + w;
+  if (b >= a.NB) return;
+  if (a.nnz > 0 && a.hdr[H_PLAN] != (int)a.plan_fp) {  // another call's plan: touch nothing
+    if (b == 0 && lane == 0) set_status(a.status, DEV_STALE_PLAN);
+    return;
+  }
+  int64_t lo = 0, hi = 0;
+  if (a.has_cache) {
+    lo = a.off[b];
+    hi = a.off[b + 1];
+    lo = lo < 0 ? 0 : (lo > a.nnz ? a.nnz : lo);
+    hi = hi < lo ? lo : (hi > a.nnz ? a.nnz : hi);
+  }
+  for (int d = lane; d < a.D; d += 64) {
+    float acc = 0.f;
+    for (int64_t n = lo; n < hi; ++n) {
+      const int s = a.slots[n];
+      if (s >= 0 && s < a.cache_size) {
+        const float wt = a.psw ? a.psw[n] : 1.f;
+        acc += wt * a.crows[(size_t)s * a.D + d];
+      }
+    }
+    a.Y[(size_t)b * a.D + d] = acc;
+  }
 }
 
 // pass 1: original order -> orderI3 by (t,i3); histogram (t,i1) over destination blocks.
@@ -123,6 +201,7 @@ __global__ __launch_bounds__(RT) void k_route_pass(DevArgs a, int pass) {
     if (e[r] < 0) continue;
     const int pos = offs[(size_t)d[r] * a.nblk + blk] + rk[r];
     out[pos] = e[r];
+    (pass == 1 ? a.posI3_of : a.posA_of)[e[r]] = pos;
     atomicAdd(&hnext[(size_t)dn[r] * a.nblk + pos / RB], 1);
   }
   if (!last_block(&a.ctr[pass], a.nblk, a.epoch)) return;
@@ -134,11 +213,22 @@ __global__ __launch_bounds__(RT) void k_route_pass(DevArgs a, int pass) {
     if (tid == 0) a.grp_off[a.binsB] = a.nnz;
     __threadfence_block();
     __syncthreads();
-    for (int g = tid; g <= G; g += RT)
-      a.chunk_pre[g] = g < G ? (a.grp_off[g + 1] - a.grp_off[g] + FWD_CHE - 1) / FWD_CHE : 0;
+    for (int g = tid; g <= G; g += RT) {
+      const int gb = a.grp_off[g], ge = g < G ? a.grp_off[g + 1] : gb;
+      a.chunk_pre[g] = ge > gb ? (ge - 1) / a.P - gb / a.P + 1 : 0;  // pieces overlapping g
+    }
     __threadfence_block();
     __syncthreads();
     block_exclusive_scan(a.chunk_pre, G + 1, s_scan);
+    // work items: group g meets the pieces [k*P, (k+1)*P) for k = gb/P .. (ge-1)/P
+    for (int g = tid; g < G; g += RT) {
+      const int first = a.chunk_pre[g], n = a.chunk_pre[g + 1] - first;
+      const int gb = a.grp_off[g], ge = a.grp_off[g + 1];
+      const int k0 = gb / a.P;
+      for (int c = 0; c < n; ++c)
+        a.fitem[first + c] =
+            make_int4(g, max(gb, (k0 + c) * a.P), min(ge, (k0 + c + 1) * a.P), 0);
+    }
     if (tid == 0) {
       a.hdr[H_NFWD] = a.chunk_pre[G];
       a.hdr[H_HIT_BEG] = a.grp_off[G];
@@ -151,18 +241,27 @@ __global__ __launch_bounds__(RT) void k_route_pass(DevArgs a, int pass) {
 __global__ __launch_bounds__(RT) void k_route_final(DevArgs a) {
   extern __shared__ unsigned short lds_c[];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, blk = blockIdx.x;
-  int e[4], d[4], rk[4];
+  if (blk == 0 && tid == 0) a.hdr[H_PLAN] = (int)a.plan_fp;
+  int e[4], d[4], rk[4], pI[4], pA[4];
+  float wv[4];
   int4 info[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
+    const int s = min(blk * RB + w * 256 + r * 64 + lane, a.nnz - 1);
+    e[r] = a.orderA[s];
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    info[r] = a.einfo[e[r]];
+    pI[r] = a.posI3_of[e[r]];
+    pA[r] = a.posA_of[e[r]];
+    wv[r] = a.psw ? a.psw[e[r]] : 1.f;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
     const int s = blk * RB + w * 256 + r * 64 + lane;
-    e[r] = -1; d[r] = -1;
-    info[r] = make_int4(0, 0, 0, 0);
-    if (s < a.nnz) {
-      e[r] = a.orderA[s];
-      info[r] = a.einfo[e[r]];
-      d[r] = info[r].y;
-    }
+    d[r] = s < a.nnz ? info[r].y : -1;
+    if (s >= a.nnz) e[r] = -1;
   }
   block_rank4(d, rk, lds_c, a.binsB, nbits_for(a.binsB), nullptr, a.nblk);
 #pragma unroll
@@ -174,7 +273,9 @@ __global__ __launch_bounds__(RT) void k_route_final(DevArgs a) {
     a.s_dB[pos] = info[r].y;
     a.s_dI3[pos] = info[r].z;
     a.s_bag[pos] = info[r].w;
-    a.pos_of[e[r]] = pos;
+    a.s_w[pos] = wv[r];
+    a.s_posI3[pos] = pI[r];
+    a.s_posA[pos] = pA[r];
   }
 }
 
@@ -187,44 +288,48 @@ __global__ __launch_bounds__(RT) void k_runsum(DevArgs a) {
   const int piece = blockIdx.x * (RT / 64) + w;
   const int V = a.hdr[H_VALID];
   const int beg = piece * PIECE;
+  if (a.hdr[H_PLAN] != (int)a.plan_fp) {  // the workspace holds another call's plan
+    if (piece == 0 && lane == 0) set_status(a.status, DEV_STALE_PLAN);
+    return;
+  }
   if (beg >= V) return;
   const int len = min(PIECE, V - beg);
-  int kA = -1, kB = -1, kI = -1, bag = 0;
-  float wt = 0.f;
-  if (lane < len) {
-    const int s = beg + lane;
-    kA = a.s_dA[s]; kB = a.s_dB[s]; kI = a.s_dI3[s]; bag = a.s_bag[s];
-    wt = a.psw ? a.psw[a.s_n[s]] : 1.f;
-  }
+  const int s = beg + min(lane, len - 1);
+  const int kA = a.s_dA[s], kB = a.s_dB[s], kI = a.s_dI3[s], bag = a.s_bag[s];
+  const float wt = lane < len ? a.s_w[s] : 0.f;
   const int pA = __shfl_up(kA, 1), pB = __shfl_up(kB, 1), pI = __shfl_up(kI, 1);
-  const int start = (lane == 0) || kA != pA || kB != pB || kI != pI;
+  // fragments start at run starts and at every multiple of P (work item boundaries)
+  const unsigned long long starts = __ballot(
+      lane < len && ((lane == 0) || kA != pA || kB != pB || kI != pI || (s % a.P) == 0));
   for (int d0 = 0; d0 < a.D; d0 += 64) {
-    const int d = d0 + lane;
+    const int d = min(d0 + lane, a.D - 1);
+    float v[PIECE];
+#pragma unroll
+    for (int l = 0; l < PIECE; ++l) {
+      const int b = __builtin_amdgcn_readlane(bag, l);
+      v[l] = a.dY[(size_t)b * a.D + d];
+    }
     float acc = 0.f;
     int cur = beg;
-    for (int l = 0; l < len; ++l) {
-      const int st = __shfl(start, l);
-      if (st && l > 0) {
-        if (d < a.D) a.frag[(size_t)cur * a.D + d] = acc;
+#pragma unroll
+    for (int l = 0; l < PIECE; ++l) {
+      if (((starts >> l) & 1ull) && l > 0) {
+        if (d0 + lane < a.D) a.frag[(size_t)cur * a.D + d] = acc;
         acc = 0.f;
         cur = beg + l;
       }
-      const int b = __shfl(bag, l);
-      const float wv = __shfl(wt, l);
-      if (d < a.D) acc += wv * a.dY[(size_t)b * a.D + d];
+      if (l < len) acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), l)) * v[l];
     }
-    if (d < a.D) a.frag[(size_t)cur * a.D + d] = acc;
+    if (d0 + lane < a.D) a.frag[(size_t)cur * a.D + d] = acc;
   }
 }
 
 hipError_t launch_route(const DevArgs &a, hipStream_t s) {
-  const int extra = a.fwd_mode ? (a.NB + RT / 64 - 1) / (RT / 64) : 0;
-  if (a.nblk + extra > 0) {
-    prof_begin(K_ROUTE_FIRST, s);
-    hipLaunchKernelGGL(k_route_first, dim3(a.nblk + extra), dim3(RT), (size_t)a.binsI3 * 4, s, a);
-    prof_end(K_ROUTE_FIRST, s);
-  }
   if (a.nblk == 0) return hipGetLastError();
+  prof_begin(K_ROUTE_FIRST, s);
+  hipLaunchKernelGGL(k_route_first, dim3(a.nblk), dim3(RT),
+                     (size_t)(a.binsI3 + ROUTE_MAX_BAGS) * 4, s, a);
+  prof_end(K_ROUTE_FIRST, s);
   prof_begin(K_ROUTE_PASS1, s);
   hipLaunchKernelGGL(k_route_pass, dim3(a.nblk), dim3(RT), (size_t)a.binsI3 * 8, s, a, 1);
   prof_end(K_ROUTE_PASS1, s);
@@ -234,6 +339,15 @@ hipError_t launch_route(const DevArgs &a, hipStream_t s) {
   prof_begin(K_ROUTE_FINAL, s);
   hipLaunchKernelGGL(k_route_final, dim3(a.nblk), dim3(RT), (size_t)a.binsB * 8, s, a);
   prof_end(K_ROUTE_FINAL, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_yinit(const DevArgs &a, hipStream_t s) {
+  if (a.NB > 0) {
+    prof_begin(K_YINIT, s);
+    hipLaunchKernelGGL(k_yinit, dim3((a.NB + RT / 64 - 1) / (RT / 64)), dim3(RT), 0, s, a);
+    prof_end(K_YINIT, s);
+  }
   return hipGetLastError();
 }
 

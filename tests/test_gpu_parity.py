@@ -284,3 +284,42 @@ def test_cache_path_matches_oracle():
     assert np.array_equal(rows.cpu().numpy()[untouched].view(np.uint32),
                           rows_old[untouched].view(np.uint32))
     cache.close()
+
+
+def test_planned_calls_match_stateless_and_refuse_a_stale_plan():
+    wl = SMALL[1]
+    cores = W.make_cores(wl)
+    b = W.make_batch(wl, 6)
+    d = to_dev(b)
+    B = b["num_bags"]
+    desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E)
+    g1, g2 = gpu_cores(wl, cores), gpu_cores(wl, cores)
+    Y1 = abi.tt_bag_forward(desc, g1, d["indices"], d["offsets"], B, d["per_sample_weights"])
+    abi.tt_bag_backward_sgd(desc, g1, d["indices"], d["offsets"], B, d["grad_out"], wl.lr,
+                            d["per_sample_weights"])
+    ws = abi.tt_bag_plan(desc, d["indices"], d["offsets"], B, d["per_sample_weights"])
+    Y2 = abi.tt_bag_forward(desc, g2, d["indices"], d["offsets"], B, d["per_sample_weights"],
+                            ws=ws, planned=True)
+    abi.tt_bag_backward_sgd(desc, g2, d["indices"], d["offsets"], B, d["grad_out"], wl.lr,
+                            d["per_sample_weights"], ws=ws, planned=True)
+    torch.cuda.synchronize()
+    assert rel_err(Y2.cpu().numpy(), Y1.cpu().numpy()) <= 1e-6
+    for k in range(3):
+        assert torch.equal(g1[k], g2[k])
+    # a planned call with other input buffers finds another plan: nothing happens
+    b2 = W.make_batch(wl, 7)
+    d2 = to_dev(b2)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    before = [x.clone() for x in g2]
+    out = torch.full((B, wl.D), 7.0, device="cuda")
+    ws2 = abi.workspace(desc, max(d["indices"].numel(), d2["indices"].numel()), B)
+    abi.tt_bag_plan(desc, d["indices"], d["offsets"], B, d["per_sample_weights"], ws=ws2)
+    abi.tt_bag_forward(desc, g2, d2["indices"], d2["offsets"], B, d2["per_sample_weights"],
+                       out=out, ws=ws2, dev_status=st, planned=True)
+    abi.tt_bag_backward_sgd(desc, g2, d2["indices"], d2["offsets"], B, d2["grad_out"], wl.lr,
+                            d2["per_sample_weights"], ws=ws2, dev_status=st, planned=True)
+    torch.cuda.synchronize()
+    assert int(st.item()) & abi.TT_DEV_STALE_PLAN
+    assert torch.all(out == 7.0)
+    for k in range(3):
+        assert torch.equal(before[k], g2[k])
