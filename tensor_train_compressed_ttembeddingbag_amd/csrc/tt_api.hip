@@ -91,31 +91,26 @@ int make_plan(const tt_desc *d, int64_t nnz, int64_t num_bags, int64_t cache_siz
   a.NHB = NHB;
   const int Rmax = a.R1 > a.R2 ? a.R1 : a.R2;
   P->RP = Rmax <= 16 ? 16 : (Rmax <= 32 ? 32 : 64);
-  P->lds_fwd = fwd_lds_bytes(P->RP, a.q3);
-  // work items of P positions: small for small ranks (many workgroups in flight), larger
-  // for rank 64 (fewer dG2 partials of 16x the size)
-  a.P = P->RP <= 32 ? 32 : 64;
-  // backward chunk: items <= P; reduction slots and items shrink until two workgroups
-  // fit one CU's LDS (or, failing that, one)
-  int CHI = a.P, nred = NW;
-  const size_t lds_two = LDS_LIMIT / 2 - 1024;
-  while (bwd_lds_bytes(P->RP, CHI, a.D, a.q3, nred) > lds_two && nred > 2) nred >>= 1;
-  while (bwd_lds_bytes(P->RP, CHI, a.D, a.q3, nred) > LDS_LIMIT) {
-    if (nred > 2) nred >>= 1;
-    else if (CHI > 8) CHI >>= 1;
-    else if (nred > 1) nred >>= 1;
-    else break;
-  }
-  if (bwd_lds_bytes(P->RP, CHI, a.D, a.q3, nred) > LDS_LIMIT || P->lds_fwd > LDS_LIMIT)
-    return TT_ESHAPE;
-  a.CHI = CHI;
+  // work items of P positions (P * q1 rows fill at most one M-block per wave); P shrinks
+  // only when a work item's rows of width D would not fit the backward's LDS
+  a.P = P_MAX;
+  while (a.P > 8 && bwd_lds_bytes(P->RP, 1, a.P, a.q3, a.D, 1) > LDS_LIMIT) a.P >>= 1;
+  if (bwd_lds_bytes(P->RP, 1, a.P, a.q3, a.D, 1) > LDS_LIMIT) return TT_ESHAPE;
+  // LDS plans that let two workgroups share a CU where possible: G2 staged whole (fewer
+  // column blocks only when needed), backward reduction slots 8 -> 2 first
+  const size_t half = LDS_LIMIT / 2 - 1024;
+  int nred = NW, JBb = a.q2;
+  while (bwd_lds_bytes(P->RP, JBb, a.P, a.q3, a.D, nred) > half && nred > 2) nred >>= 1;
+  while (bwd_lds_bytes(P->RP, JBb, a.P, a.q3, a.D, nred) > half && JBb > 1) --JBb;
+  while (bwd_lds_bytes(P->RP, JBb, a.P, a.q3, a.D, nred) > half && nred > 1) nred >>= 1;
   a.NRED = nred;
-  {
-    const int rows = NW * 16 * bwd_mbw(P->RP);
-    const int pairs = rows / a.q1;
-    a.CHPb = pairs < CHP ? pairs : CHP;
-  }
-  P->lds_bwd = bwd_lds_bytes(P->RP, CHI, a.D, a.q3, nred);
+  a.JBb = JBb;
+  P->lds_bwd = bwd_lds_bytes(P->RP, JBb, a.P, a.q3, a.D, nred);
+  a.fwd_sw = (size_t)a.P * a.D * 4 <= 64 * 1024;
+  a.JBf = a.q2;
+  while (a.JBf > 1 && fwd_lds_bytes(P->RP, a.JBf, a.P, a.q3, a.D, a.fwd_sw) > half) --a.JBf;
+  P->lds_fwd = fwd_lds_bytes(P->RP, a.JBf, a.P, a.q3, a.D, a.fwd_sw);
+  if (P->lds_bwd > LDS_LIMIT || P->lds_fwd > LDS_LIMIT) return TT_ESHAPE;
 
   const size_t n = (size_t)nnz, nb = (size_t)a.nblk, G = (size_t)T * a.p2;
   size_t cur = 0;

@@ -14,296 +14,328 @@
 // concern for EmbeddingBag's dense gradient: sort, then accumulate without races).
 //
 // k_bwd: one workgroup per work item (the elements of one (table, i2) group inside
-// one P-aligned piece of the grouping order), cut into chunks of at most CHPb pairs
-// and CHI items (distinct indices).  Per chunk, G_u, the items' G3 slices and the
-// pairs' G1 rows are fetched once; then per column block j2 of G2 (double-buffered
-// in LDS, prefetched into registers): recompute T (MFMA), form dT and the dG3
-// partial per item (VALU, LDS only), accumulate dG2 (MFMA, K = the rows (pair, j1))
+// one P-aligned piece of the grouping order; at most P <= 32 elements, so its
+// (pair, j1) rows fit one 16-row M-block per wave).  Three dependent rounds of
+// global loads -- the work item; its elements and G2 slice; the items' G3 slices,
+// the pairs' G1 rows and the elements' dY rows -- and everything else runs from
+// LDS and registers.  Per column block j2 of G2: recompute T (MFMA), form dT and
+// the dG3 partial per item (VALU), accumulate dG2 (MFMA, K = the rows (pair, j1))
 // and dG1 per pair (MFMA after an LDS transpose of dT).  dG2 is reduced over the 8
 // waves in a fixed order into the work item's partial.  The dG1 / dG3 partials go
-// to the workspace at the final-order position of their first element.  k_seg then
-// sums every partial per slice in a fixed order and applies SGD: dG1 / dG3 in the
-// (t,i1)- / (t,i3)-order (which the links name), dG2 in work-item order.
+// to the workspace at the final-order position of their first element, and the
+// links record where they are.  k_seg then sums every partial per slice in a fixed
+// order and applies SGD: dG1 / dG3 in the (t,i1)- / (t,i3)-order, dG2 in
+// work-item order.
 #include "tt_internal.h"
 #include "tt_mfma.h"
 
 namespace ttb {
 
+// LDS carve of one backward workgroup (float words, then int words)
 template <int RP>
 struct BwdLds {
   static constexpr int LD = RP + 4;
-  __host__ __device__ static size_t red_floats(int nred) {
-    const size_t r = (size_t)nred * RP * LD, t = (size_t)NW * 16 * LD;
-    return r > t ? r : t;  // the dG2 reduction slots alias the dT transpose tiles
+  static constexpr int INTS = 64 * 5 + 65 * 2 + 64 + 64 + 16 + 8;
+  // the dG2 reduction slots alias the dT transpose tiles and the w * dY staging
+  __host__ __device__ static size_t red_floats(int nred, int P, int D) {
+    size_t r = (size_t)nred * RP * LD;
+    const size_t t = (size_t)NW * 16 * LD, y = (size_t)P * D;
+    r = r > t ? r : t;
+    return r > y ? r : y;
   }
-  static size_t floats(int CHI, int D, int q3, int nred) {
-    return (size_t)2 * RP * LD + red_floats(nred) + (size_t)CHI * D + 2 * (size_t)CHI * RP * q3;
-  }
-  static size_t ints(int CHI) { return (size_t)(CHI + 1) + 2 * CHI + (CHP + 1) + CHP + 2 * NW + 16; }
-  static size_t bytes(int CHI, int D, int q3, int nred) {
-    return floats(CHI, D, q3, nred) * 4 + ints(CHI) * 4;
+  static size_t bytes(int JB, int P, int q3, int D, int nred) {
+    return ((size_t)JB * RP * LD + red_floats(nred, P, D) + (size_t)P * D +
+            2 * (size_t)P * q3 * RP) * 4 + INTS * 4;
   }
 };
 
-size_t bwd_lds_bytes(int RP, int CHI, int D, int q3, int nred) {
+size_t bwd_lds_bytes(int RP, int JB, int P, int q3, int D, int nred) {
   switch (RP) {
-    case 16: return BwdLds<16>::bytes(CHI, D, q3, nred);
-    case 32: return BwdLds<32>::bytes(CHI, D, q3, nred);
-    default: return BwdLds<64>::bytes(CHI, D, q3, nred);
+    case 16: return BwdLds<16>::bytes(JB, P, q3, D, nred);
+    case 32: return BwdLds<32>::bytes(JB, P, q3, D, nred);
+    default: return BwdLds<64>::bytes(JB, P, q3, D, nred);
   }
-}
-
-// block-wide exclusive prefixes of two 0/1 flags (WG threads).  Totals land in
-// tot[0], tot[1] (LDS, valid after the call).
-static __device__ __forceinline__ void block_prefix2(bool f0, bool f1, int *s_w, int *tot, int &p0,
-                                                     int &p1) {
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const unsigned long long m0 = __ballot(f0), m1 = __ballot(f1);
-  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  if (lane == 0) { s_w[w] = __popcll(m0); s_w[NW + w] = __popcll(m1); }
-  __syncthreads();
-  if (tid < 64) {
-    const int v0 = lane < NW ? s_w[lane] : 0, v1 = lane < NW ? s_w[NW + lane] : 0;
-    int x0 = v0, x1 = v1;
-#pragma unroll
-    for (int o = 1; o < NW; o <<= 1) {
-      const int y0 = __shfl_up(x0, o), y1 = __shfl_up(x1, o);
-      if (lane >= o) { x0 += y0; x1 += y1; }
-    }
-    if (lane < NW) { s_w[lane] = x0 - v0; s_w[NW + lane] = x1 - v1; }
-    if (lane == NW - 1) { tot[0] = x0; tot[1] = x1; }
-  }
-  __syncthreads();
-  p0 = s_w[w] + __popcll(m0 & lt);
-  p1 = s_w[NW + w] + __popcll(m1 & lt);
-  __syncthreads();
 }
 
 template <int RP>
 __global__ __launch_bounds__(WG) void k_bwd(DevArgs a) {
-  constexpr int KS = RP / 4, NM = RP / 16, LD = BwdLds<RP>::LD, MBW = bwd_mbw(RP);
-  constexpr int KP = (RP * RP + WG - 1) / WG;
+  constexpr int KS = RP / 4, NM = RP / 16, LD = BwdLds<RP>::LD;
+  extern __shared__ float4 smem4[];
+  float *smem = (float *)smem4;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int q1 = a.q1, q2 = a.q2, q3 = a.q3, R1 = a.R1, R2 = a.R2, D = a.D;
+  const int JB = a.JBb, P = a.P, nred = a.NRED;
+  float *sG2 = smem;                                              // [JB][r2 < RP][LD]
+  float *sRed = sG2 + (size_t)JB * RP * LD;                       // slots / dT tiles / w*dY
+  float *sT = sRed;
+  float *sYe = sRed;
+  float *sGu = sRed + BwdLds<RP>::red_floats(nred, P, D);         // [item][D]
+  float *sG3 = sGu + (size_t)P * D;                               // [item][j3][r2 < RP]
+  float *sdA3 = sG3 + (size_t)P * q3 * RP;                        // [item][j3][r2 < RP]
+  int *e_bag = (int *)(sdA3 + (size_t)P * q3 * RP);               // [64]
+  float *e_w = (float *)(e_bag + 64);                             // [64]
+  int *it_i3 = (int *)(e_w + 64);                                 // [64]
+  int *it_pair = it_i3 + 64;                                      // [64]
+  int *it_beg = it_pair + 64;                                     // [65] (offsets in the item)
+  int *pr_it = it_beg + 65;                                       // [65]
+  int *pr_i1 = pr_it + 65;                                        // [64]
+  int *gcnt = pr_i1 + 64;                                         // [64] items per lane group
+  int *mb_nk = gcnt + 64;                                         // [16]
+  int *s_cnt = mb_nk + 16;                                        // [8]
+
+  // round 1: plan check and work item
   const int wi = blockIdx.x;
   const int plan = a.hdr[H_PLAN], nitems = a.hdr[H_NFWD];
   const int4 item = a.fitem[wi];
   if (plan != (int)a.plan_fp || wi >= nitems) return;
-  const int grp = item.x, gs = item.y, ge = item.z;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
-  const int q1 = a.q1, q2 = a.q2, q3 = a.q3, R1 = a.R1, R2 = a.R2, D = a.D, CHI = a.CHI;
-  const int CHPb = a.CHPb, nred = a.NRED;
-  const int t = grp / a.p2, i2 = grp - t * a.p2;
-
-  extern __shared__ float smem[];
-  float *sG2 = smem;
-  float *sRed = sG2 + 2 * RP * LD;  // aliases sT
-  float *sT = sRed;
-  float *sGu = sRed + BwdLds<RP>::red_floats(nred);
-  float *sG3 = sGu + (size_t)CHI * D;
-  float *sdA3 = sG3 + (size_t)CHI * RP * q3;
-  int *it_beg = (int *)(sdA3 + (size_t)CHI * RP * q3);  // [CHI+1] final-order positions
-  int *it_i3 = it_beg + CHI + 1;                          // [CHI]
-  int *it_pair = it_i3 + CHI;                             // [CHI]
-  int *pr_it = it_pair + CHI;                             // [CHP+1]
-  int *pr_i1 = pr_it + CHP + 1;                           // [CHP]
-  int *s_w = pr_i1 + CHP;                                 // [2*NW]
-  int *s_misc = s_w + 2 * NW;                             // [16]
-
+  const int grp = item.x, s0 = item.y, s1 = item.z;
+  const int n_el = s1 - s0;
+  const int t = grp / a.p2;
   const size_t W1 = (size_t)q1 * R1, W3 = (size_t)R2 * q3;
   const size_t slice2 = (size_t)R1 * q2 * R2;
-  const size_t g2base = (size_t)(t * a.p2 + i2) * slice2;
+  const float *G2g = a.G2 + (size_t)grp * slice2;
   const float *G1t = a.G1 + (size_t)t * a.p1 * W1;
   const float *G3t = a.G3 + (size_t)t * a.p3 * W3;
   float *part2 = a.part2 + (size_t)wi * slice2;
 
-  float pf[KP];
-  auto fetch_g2 = [&](int j2) {
+  // G2 columns [j0, j0 + nj) -> LDS as G2^T blocks, STAGE_U loads per thread per batch
+  auto load2 = [&](int j0, int nj, int base, float *v) {
+    const int total = nj * RP * RP;
 #pragma unroll
-    for (int k = 0; k < KP; ++k) {
-      const int i = tid + k * WG;
-      const int r1 = i / RP, r2 = i - r1 * RP;
-      const bool ok = i < RP * RP && r1 < R1 && r2 < R2;
-      const float v = a.G2[g2base + ((size_t)(ok ? r1 : 0) * q2 + j2) * R2 + (ok ? r2 : 0)];
-      pf[k] = ok ? v : 0.f;
+    for (int u = 0; u < STAGE_U; ++u) {
+      const int i = min(base + u * WG, total - 1);
+      const int jj = i / (RP * RP), rem = i - jj * RP * RP;
+      const int r1 = rem / RP, r2 = rem - r1 * RP;
+      const bool ok = r1 < R1 && r2 < R2;
+      v[u] = G2g[((size_t)(ok ? r1 : 0) * q2 + j0 + jj) * R2 + (ok ? r2 : 0)];
     }
   };
-  auto store_g2 = [&](float *buf) {
+  auto store2 = [&](int nj, int base, const float *v) {
+    const int total = nj * RP * RP;
 #pragma unroll
-    for (int k = 0; k < KP; ++k) {
-      const int i = tid + k * WG;
-      if (i < RP * RP) {
-        const int r1 = i / RP, r2 = i - r1 * RP;
-        buf[r2 * LD + r1] = pf[k];
+    for (int u = 0; u < STAGE_U; ++u) {
+      const int i = base + u * WG;
+      if (i < total) {
+        const int jj = i / (RP * RP), rem = i - jj * RP * RP;
+        const int r1 = rem / RP, r2 = rem - r1 * RP;
+        sG2[(size_t)jj * RP * LD + r2 * LD + r1] = (r1 < R1 && r2 < R2) ? v[u] : 0.f;
       }
+    }
+  };
+  auto stage_g2 = [&](int j0, int nj, int first) {
+    for (int base = first; base < nj * RP * RP; base += WG * STAGE_U) {
+      float v[STAGE_U];
+      load2(j0, nj, base, v);
+      store2(nj, base, v);
     }
   };
 
-  int cur = gs, chunk = 0;
-  while (cur < ge) {
-    fetch_g2(0);
-    // ---------------- chunk formation: whole items, <= CHI items, <= CHPb pairs;
-    // the links of the chunk's positions are written on the way
-    if (tid == 0) { s_misc[0] = 0; s_misc[1] = 0; s_misc[2] = ge; }
-    __syncthreads();
-    for (int base = cur; base < ge; base += WG) {
-      const int nI0 = s_misc[0], nP0 = s_misc[1];
-      const int s = base + tid;
-      const bool v = s < ge;
-      const int sc = v ? s : ge - 1, sp = max(sc - 1, 0);
-      const int dA0 = a.s_dA[sc], dI0 = a.s_dI3[sc], pdA0 = a.s_dA[sp], pdI0 = a.s_dI3[sp];
-      const int lA = a.s_posA[sc], lI = a.s_posI3[sc];
-      const bool first = s == cur;
-      const bool ist = v && (first || dA0 != pdA0 || dI0 != pdI0);
-      const bool pst = v && (first || dA0 != pdA0);
-      int ip, pp;
-      block_prefix2(ist, pst, s_w, &s_misc[3], ip, pp);
-      const int item_idx = nI0 + ip, pair_idx = nP0 + pp;  // index of an item / pair starting at s
-      if ((ist && item_idx >= CHI) || (pst && pair_idx >= CHPb)) atomicMin(&s_misc[2], s);
-      __syncthreads();
-      const int ce = s_misc[2];
-      if (ist && s < ce) {
-        it_beg[item_idx] = s;
-        it_i3[item_idx] = dI0 - t * a.p3;
-        it_pair[item_idx] = pst ? pair_idx : pair_idx - 1;
-      }
-      if (pst && s < ce) { pr_it[pair_idx] = item_idx; pr_i1[pair_idx] = dA0 - t * a.p1; }
-      if (v && s < ce) {
-        a.link1[lA] = pst ? s : -1;
-        a.link3[lI] = ist ? s : -1;
-      }
-      if (s == ce) { s_misc[5] = ip; s_misc[6] = pp; }
-      __syncthreads();
-      if (tid == 0) {
-        if (ce < ge) { s_misc[0] = nI0 + s_misc[5]; s_misc[1] = nP0 + s_misc[6]; }
-        else { s_misc[0] = nI0 + s_misc[3]; s_misc[1] = nP0 + s_misc[4]; }
-      }
-      __syncthreads();
-      if (ce < ge) break;
+  // round 2: the elements (wave 0; items, pairs, links) and the first G2 stage
+  const int nj0 = min(JB, q2);
+  float v2[STAGE_U];
+  load2(0, nj0, tid, v2);
+  if (tid < 64) {
+    const int s = s0 + min(tid, n_el - 1);
+    const bool v = tid < n_el;
+    const int dAv = a.s_dA[s], dIv = a.s_dI3[s], bagv = a.s_bag[s];
+    const int lA = a.s_posA[s], lI = a.s_posI3[s];
+    const float wv = a.s_w[s];
+    const int dA = v ? dAv : -1, i3 = v ? dIv - t * a.p3 : -1;
+    e_bag[tid] = bagv;
+    e_w[tid] = wv;
+    const int pdA = __shfl_up(dA, 1), pi3 = __shfl_up(i3, 1);
+    const bool item_st = v && (tid == 0 || dA != pdA || i3 != pi3);
+    const bool pair_st = v && (tid == 0 || dA != pdA);
+    const unsigned long long mi = __ballot(item_st), mp = __ballot(pair_st);
+    const unsigned long long lt = (tid == 0) ? 0ull : (~0ull >> (64 - tid));
+    const int it = __popcll(mi & lt), pr = __popcll(mp & lt);
+    gcnt[tid] = 0;
+    // a partial lives at the first position of its item (dG3) / pair (dG1)
+    if (v) {
+      a.link1[lA] = pair_st ? s : -1;
+      a.link3[lI] = item_st ? s : -1;
     }
-    const int nI = s_misc[0], nP = s_misc[1], ce = s_misc[2];
-    if (tid == 0) { it_beg[nI] = ce; pr_it[nP] = nI; }
-    __syncthreads();
-    // ---------------- chunk data: G_u (run fragments), the items' G3 slices, A operands,
-    // STAGE_U loads in flight per thread
-    {
-      const int total = nI * D;
-      for (int base = tid; base < total; base += WG * STAGE_U) {
-        float v[STAGE_U];
-#pragma unroll
-        for (int u = 0; u < STAGE_U; ++u) {
-          const int i = min(base + u * WG, total - 1);
-          const int it = i / D, d = i - it * D;
-          v[u] = a.frag[(size_t)it_beg[it] * D + d];
-        }
-#pragma unroll
-        for (int u = 0; u < STAGE_U; ++u) {
-          const int i = base + u * WG;
-          if (i < total) {
-            const int it = i / D, d = i - it * D;
-            const int b0 = it_beg[it], b1 = it_beg[it + 1];
-            float acc = v[u];  // runs longer than a piece carry more fragments (rare)
-            for (int p = (b0 / a.P + 1) * a.P; p < b1; p += a.P)
-              acc += a.frag[(size_t)p * D + d];
-            sGu[i] = acc;
-          }
-        }
-      }
+    wave_lds_sync();
+    if (item_st) {
+      it_beg[it] = tid;
+      it_i3[it] = i3;
+      it_pair[it] = pair_st ? pr : pr - 1;
     }
-    {
-      const int per_item = RP * q3, total = nI * per_item;
-      for (int base = tid; base < total; base += WG * STAGE_U) {
-        float v[STAGE_U];
-#pragma unroll
-        for (int u = 0; u < STAGE_U; ++u) {
-          const int i = min(base + u * WG, total - 1);
-          const int it = i / per_item, rem = i - it * per_item;
-          const int r2 = rem / q3;
-          v[u] = G3t[(size_t)it_i3[it] * W3 + (r2 < R2 ? rem : 0)];
-        }
-#pragma unroll
-        for (int u = 0; u < STAGE_U; ++u) {
-          const int i = base + u * WG;
-          if (i < total) {
-            const int rem = i % per_item;
-            sG3[i] = (rem / q3 < R2) ? v[u] : 0.f;
-            sdA3[i] = 0.f;
-          }
-        }
-      }
+    if (pair_st) {
+      const unsigned long long above = tid == 63 ? 0ull : (mp >> (tid + 1));
+      const int nxt = above ? tid + __ffsll((long long)above) : n_el;
+      const unsigned long long span = (nxt >= 64 ? ~0ull : ((1ull << nxt) - 1)) & ~lt;
+      pr_it[pr] = it;
+      pr_i1[pr] = dA - t * a.p1;
+      // the pair's rows pr*q1 .. +q1-1 lie in lane group (pr*q1)/4 of an M-block
+      atomicAdd(&gcnt[(pr * q1) >> 2], __popcll(mi & span));
     }
-    const int nmb = (nP * q1 + 15) / 16;
-    float aT[MBW][KS];      // A1[row = 16mb + c][r1 = g*KS + ks]    (stage 1)
-    float aG[MBW][4][NM];   // A1[row = 16mb + 4g + s][r1 = 16mr + c] (dG2)
-    f4 dA1[MBW][NM];        // dG1^T[r1 = 16mr + 4g + v][row = c]
-#pragma unroll
-    for (int mbi = 0; mbi < MBW; ++mbi) {
-      const int mb = w + mbi * NW;
-      {
-        const int row = mb * 16 + c;
-        const int pr = row / q1, j1 = row - pr * q1;
-        const bool ok = mb < nmb && pr < nP;
-        const float *src = G1t + ((size_t)(ok ? pr_i1[pr] : 0) * q1 + j1) * R1;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int r1 = g * KS + ks;
-          const float v = src[min(r1, R1 - 1)];
-          aT[mbi][ks] = (ok && r1 < R1) ? v : 0.f;
-        }
-      }
-#pragma unroll
-      for (int sr = 0; sr < 4; ++sr) {
-        const int row = mb * 16 + 4 * g + sr;
-        const int pr = row / q1, j1 = row - pr * q1;
-        const bool ok = mb < nmb && pr < nP;
-        const float *src = G1t + ((size_t)(ok ? pr_i1[pr] : 0) * q1 + j1) * R1;
-#pragma unroll
-        for (int mr = 0; mr < NM; ++mr) {
-          const int r1 = 16 * mr + c;
-          const float v = src[min(r1, R1 - 1)];
-          aG[mbi][sr][mr] = (ok && r1 < R1) ? v : 0.f;
-        }
-      }
-#pragma unroll
-      for (int mr = 0; mr < NM; ++mr) dA1[mbi][mr] = zero4();
+    if (tid == 0) {
+      const int nI = __popcll(mi), nP = __popcll(mp);
+      it_beg[nI] = n_el;
+      pr_it[nP] = nI;
+      s_cnt[0] = nI;
+      s_cnt[1] = nP;
     }
-    store_g2(sG2);
-    if (q2 > 1) fetch_g2(1);
-    __syncthreads();
+    wave_lds_sync();
+    if (tid < 16)
+      mb_nk[tid] = max(max(gcnt[4 * tid], gcnt[4 * tid + 1]), max(gcnt[4 * tid + 2], gcnt[4 * tid + 3]));
+  }
+  store2(nj0, tid, v2);
+  stage_g2(0, nj0, tid + WG * STAGE_U);
+  __syncthreads();
+  const int nI = s_cnt[0], nP = s_cnt[1];
+  const int nmb = (nP * q1 + 15) >> 4;
+  const int mb = w;  // one M-block per wave (P * q1 <= 16 * NW)
 
-    for (int j2 = 0; j2 < q2; ++j2) {
-      const float *buf = sG2 + (j2 & 1) * RP * LD;
+  // round 3: G3 slices -> LDS (and the dG3 accumulators cleared), G1 rows in the two
+  // operand layouts, w * dY rows of the elements.  First batches of everything are
+  // issued before the first wait.
+  const int per_item = RP * q3, total3 = nI * per_item, totalY = n_el * D;
+  auto load3 = [&](int base, float *v) {
+#pragma unroll
+    for (int u = 0; u < STAGE_U; ++u) {
+      const int i = min(base + u * WG, total3 - 1);
+      const int it = i / per_item, rem = i - it * per_item;  // rem = r2 * q3 + j3
+      v[u] = G3t[(size_t)it_i3[it] * W3 + (rem < (int)W3 ? rem : 0)];
+    }
+  };
+  auto store3 = [&](int base, const float *v) {
+#pragma unroll
+    for (int u = 0; u < STAGE_U; ++u) {
+      const int i = base + u * WG;
+      if (i < total3) {
+        const int it = i / per_item, rem = i - it * per_item;
+        const int r2 = rem / q3, j3 = rem - r2 * q3;
+        const size_t o = (size_t)it * per_item + j3 * RP + r2;
+        sG3[o] = r2 < R2 ? v[u] : 0.f;
+        sdA3[o] = 0.f;
+      }
+    }
+  };
+  auto loadY = [&](int base, float *v) {
+#pragma unroll
+    for (int u = 0; u < STAGE_U; ++u) {
+      const int i = min(base + u * WG, totalY - 1);
+      const int e = i / D, d = i - e * D;
+      v[u] = a.dY[(size_t)e_bag[e] * D + d];
+    }
+  };
+  auto storeY = [&](int base, const float *v) {
+#pragma unroll
+    for (int u = 0; u < STAGE_U; ++u) {
+      const int i = base + u * WG;
+      if (i < totalY) sYe[i] = e_w[i / D] * v[u];
+    }
+  };
+  float v3[STAGE_U], vy[STAGE_U];
+  load3(tid, v3);
+  loadY(tid, vy);
+  float aT[KS];          // A1[row = 16mb + c][r1 = g*KS + ks]     (stage 1)
+  float aG[4][NM];       // A1[row = 16mb + 4g + sr][r1 = 16mr + c] (dG2)
+  {
+    const int row = mb * 16 + c;
+    const int pr = row / q1, j1 = row - pr * q1;
+    const float *src = G1t + ((size_t)pr_i1[min(pr, nP - 1)] * q1 + j1) * R1;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) aT[ks] = src[min(g * KS + ks, R1 - 1)];
+#pragma unroll
+    for (int sr = 0; sr < 4; ++sr) {
+      const int row2 = mb * 16 + 4 * g + sr;
+      const int pr2 = row2 / q1, j12 = row2 - pr2 * q1;
+      const float *src2 = G1t + ((size_t)pr_i1[min(pr2, nP - 1)] * q1 + j12) * R1;
+#pragma unroll
+      for (int mr = 0; mr < NM; ++mr) aG[sr][mr] = src2[min(16 * mr + c, R1 - 1)];
+    }
+  }
+  store3(tid, v3);
+  storeY(tid, vy);
+  for (int base = tid + WG * STAGE_U; base < total3; base += WG * STAGE_U) {
+    float v[STAGE_U];
+    load3(base, v);
+    store3(base, v);
+  }
+  for (int base = tid + WG * STAGE_U; base < totalY; base += WG * STAGE_U) {
+    float v[STAGE_U];
+    loadY(base, v);
+    storeY(base, v);
+  }
+  {
+    const int row = mb * 16 + c;
+    const bool ok = mb < nmb && row / q1 < nP;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const float x = keep(aT[ks]);
+      aT[ks] = (ok && g * KS + ks < R1) ? x : 0.f;
+    }
+#pragma unroll
+    for (int sr = 0; sr < 4; ++sr) {
+      const int row2 = mb * 16 + 4 * g + sr;
+      const bool ok2 = mb < nmb && row2 / q1 < nP;
+#pragma unroll
+      for (int mr = 0; mr < NM; ++mr) {
+        const float x = keep(aG[sr][mr]);
+        aG[sr][mr] = (ok2 && 16 * mr + c < R1) ? x : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  // G_u of every item: its elements' w * dY rows summed in position order
+  for (int i = tid; i < nI * D; i += WG) {
+    const int it = i / D, d = i - it * D;
+    float acc = 0.f;
+    for (int e = it_beg[it]; e < it_beg[it + 1]; ++e) acc += sYe[(size_t)e * D + d];
+    sGu[i] = acc;
+  }
+  __syncthreads();
+
+  f4 dA1[NM];  // dG1^T[r1 = 16mr + 4g + v][row = c]
+#pragma unroll
+  for (int mr = 0; mr < NM; ++mr) dA1[mr] = zero4();
+  const int rb = mb * 16 + 4 * g;  // the lane group's rows rb .. rb+3
+  const int plo = rb / q1, phi = min((rb + 3) / q1, nP - 1);
+  const int ib = (mb < nmb && plo < nP) ? pr_it[plo] : 0;
+  const int ie = (mb < nmb && plo < nP) ? pr_it[phi + 1] : 0;
+  const int nk = mb < nmb ? mb_nk[mb] : 0;
+
+  for (int j0 = 0; j0 < q2; j0 += JB) {
+    if (j0 > 0) {  // next G2 stage (only when the slice does not fit at once)
+      __syncthreads();
+      stage_g2(j0, min(JB, q2 - j0), tid);
+      __syncthreads();
+    }
+    const int jend = min(q2, j0 + JB);
+    for (int j2 = j0; j2 < jend; ++j2) {
+      const float *buf = sG2 + (size_t)(j2 - j0) * RP * LD;
       f4 gacc[NM][NM];  // dG2[r1 = 16mr + 4g + v][r2 = 16m2 + c]
 #pragma unroll
       for (int mr = 0; mr < NM; ++mr)
 #pragma unroll
         for (int m2 = 0; m2 < NM; ++m2) gacc[mr][m2] = zero4();
-#pragma unroll
-      for (int mbi = 0; mbi < MBW; ++mbi) {
-        const int mb = w + mbi * NW;
-        if (mb >= nmb) break;
+      if (mb < nmb) {
         // stage 1: T[row = 16mb + 4g + v][r2 = 16m + c]
         f4 T[NM], dT[NM];
 #pragma unroll
         for (int m = 0; m < NM; ++m) { T[m] = zero4(); dT[m] = zero4(); }
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int kq = 0; kq < KS / 4; ++kq)
 #pragma unroll
-          for (int m = 0; m < NM; ++m)
-            T[m] = mfma4(aT[mbi][ks], buf[(16 * m + c) * LD + g * KS + ks], T[m]);
-        // items whose pair owns rows 16mb + 4g .. +3
-        const int rb = mb * 16 + 4 * g;
-        const int plo = rb / q1;
-        const int phi = min((rb + 3) / q1, nP - 1);
-        const int ib = plo < nP ? pr_it[plo] : 0;
-        const int ie = plo < nP ? pr_it[phi + 1] : 0;
-        const int nk = wave_max(ie - ib);
+          for (int m = 0; m < NM; ++m) {
+            const float4 bv = *(const float4 *)&buf[(16 * m + c) * LD + g * KS + 4 * kq];
+            T[m] = mfma4(aT[4 * kq + 0], bv.x, T[m]);
+            T[m] = mfma4(aT[4 * kq + 1], bv.y, T[m]);
+            T[m] = mfma4(aT[4 * kq + 2], bv.z, T[m]);
+            T[m] = mfma4(aT[4 * kq + 3], bv.w, T[m]);
+          }
+        // the items of the pairs owning the lane group's rows
         for (int kk = 0; kk < nk; ++kk) {
           const int it = ib + kk;
           const bool act = it < ie;
           const int itc = act ? it : 0;
           const int pr = act ? it_pair[itc] : -1;
-          const float *g3 = sG3 + (size_t)itc * RP * q3;
+          const float *g3 = sG3 + (size_t)itc * per_item + c;
           const float *gu = sGu + (size_t)itc * D;
-          float *da3 = sdA3 + (size_t)itc * RP * q3;
+          float *da3 = sdA3 + (size_t)itc * per_item + c;
           for (int j3 = 0; j3 < q3; ++j3) {
             float gv[4];
 #pragma unroll
@@ -315,26 +347,25 @@ __global__ __launch_bounds__(WG) void k_bwd(DevArgs a) {
             }
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-              const int r2 = 16 * m + c;
-              const float a3v = g3[r2 * q3 + j3];
+              const float a3v = g3[j3 * RP + 16 * m];
               float sacc = 0.f;
 #pragma unroll
               for (int v = 0; v < 4; ++v) {
                 sacc += T[m][v] * gv[v];
                 dT[m][v] += gv[v] * a3v;
               }
-              if (act) da3[r2 * q3 + j3] += sacc;
+              if (act) da3[j3 * RP + 16 * m] += sacc;
             }
           }
         }
-        // dG2 += A1^T dT   (K = the 16 rows; lane group g feeds rows 4g + s)
+        // dG2 += A1^T dT   (K = the 16 rows; lane group g feeds rows 4g + sr)
 #pragma unroll
         for (int sr = 0; sr < 4; ++sr)
 #pragma unroll
           for (int mr = 0; mr < NM; ++mr)
 #pragma unroll
             for (int m2 = 0; m2 < NM; ++m2)
-              gacc[mr][m2] = mfma4(aG[mbi][sr][mr], dT[m2][sr], gacc[mr][m2]);
+              gacc[mr][m2] = mfma4(aG[sr][mr], dT[m2][sr], gacc[mr][m2]);
         // dG1^T += G2_j2 dT^T  (K = r2; dT transposed through the wave's LDS tile)
         float *tt = sT + (size_t)w * 16 * LD;
 #pragma unroll
@@ -343,16 +374,16 @@ __global__ __launch_bounds__(WG) void k_bwd(DevArgs a) {
           for (int v = 0; v < 4; ++v) tt[(4 * g + v) * LD + 16 * m + c] = dT[m][v];
         wave_lds_sync();
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
+        for (int m = 0; m < NM; ++m) {
+          const float4 bT = *(const float4 *)&tt[c * LD + 16 * m + 4 * g];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int r2 = 16 * m + 4 * g + v;
-            const float bT = tt[c * LD + r2];
-#pragma unroll
-            for (int mr = 0; mr < NM; ++mr)
-              dA1[mbi][mr] = mfma4(buf[r2 * LD + 16 * mr + c], bT, dA1[mbi][mr]);
+          for (int mr = 0; mr < NM; ++mr) {
+            dA1[mr] = mfma4(buf[(16 * m + 4 * g + 0) * LD + 16 * mr + c], bT.x, dA1[mr]);
+            dA1[mr] = mfma4(buf[(16 * m + 4 * g + 1) * LD + 16 * mr + c], bT.y, dA1[mr]);
+            dA1[mr] = mfma4(buf[(16 * m + 4 * g + 2) * LD + 16 * mr + c], bT.z, dA1[mr]);
+            dA1[mr] = mfma4(buf[(16 * m + 4 * g + 3) * LD + 16 * mr + c], bT.w, dA1[mr]);
           }
-        wave_lds_sync();
+        }
       }
       // reduce dG2 over the waves: wave w adds into slot w % nred, rounds in wave order,
       // then the slots are summed in slot order
@@ -376,42 +407,30 @@ __global__ __launch_bounds__(WG) void k_bwd(DevArgs a) {
         const int r1 = i / R2, r2 = i - r1 * R2;
         float val = 0.f;
         for (int k = 0; k < nred; ++k) val += sRed[(size_t)k * RP * LD + r1 * LD + r2];
-        const size_t off = ((size_t)r1 * q2 + j2) * R2 + r2;
-        if (chunk == 0) part2[off] = val;
-        else part2[off] += val;
-      }
-      if (j2 + 1 < q2) {
-        store_g2(sG2 + ((j2 + 1) & 1) * RP * LD);
-        if (j2 + 2 < q2) fetch_g2(j2 + 2);
+        part2[((size_t)r1 * q2 + j2) * R2 + r2] = val;
       }
       __syncthreads();
     }
-    // dG1 partial per pair, dG3 partial per item, at their first positions
+  }
+  // dG1 partial per pair, dG3 partial per item, at their first positions
+  if (mb < nmb) {
+    const int row = mb * 16 + c;
+    const int pr = row / q1, j1 = row - pr * q1;
+    if (pr < nP) {
+      float *dst = a.part1 + (size_t)(s0 + it_beg[pr_it[pr]]) * W1 + (size_t)j1 * R1;
 #pragma unroll
-    for (int mbi = 0; mbi < MBW; ++mbi) {
-      const int mb = w + mbi * NW;
-      if (mb >= nmb) break;
-      const int row = mb * 16 + c;
-      const int pr = row / q1, j1 = row - pr * q1;
-      if (pr < nP) {
-        float *dst = a.part1 + (size_t)it_beg[pr_it[pr]] * W1 + (size_t)j1 * R1;
+      for (int mr = 0; mr < NM; ++mr)
 #pragma unroll
-        for (int mr = 0; mr < NM; ++mr)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int r1 = 16 * mr + 4 * g + v;
-            if (r1 < R1) dst[r1] = dA1[mbi][mr][v];
-          }
-      }
+        for (int v = 0; v < 4; ++v) {
+          const int r1 = 16 * mr + 4 * g + v;
+          if (r1 < R1) dst[r1] = dA1[mr][v];
+        }
     }
-    for (int i = tid; i < nI * (int)W3; i += WG) {
-      const int it = i / W3, rem = i - it * W3;
-      const int r2 = rem / q3, j3 = rem - r2 * q3;
-      a.part3[(size_t)it_beg[it] * W3 + rem] = sdA3[((size_t)it * RP + r2) * q3 + j3];
-    }
-    __syncthreads();
-    cur = ce;
-    ++chunk;
+  }
+  for (int i = tid; i < nI * (int)W3; i += WG) {
+    const int it = i / W3, rem = i - it * W3;
+    const int r2 = rem / q3, j3 = rem - r2 * q3;
+    a.part3[(size_t)(s0 + it_beg[it]) * W3 + rem] = sdA3[(size_t)it * per_item + j3 * RP + r2];
   }
 }
 
@@ -452,7 +471,10 @@ __global__ __launch_bounds__(256) void k_seg(DevArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int nA = a.T * a.p1, nC = a.T * a.p3, G = a.T * a.p2;
   const int nb1 = (nA + nC + 3) / 4;
-  if (a.hdr[H_PLAN] != (int)a.plan_fp) return;
+  if (a.hdr[H_PLAN] != (int)a.plan_fp) {  // the workspace holds another call's plan
+    if (blockIdx.x == 0 && tid == 0) set_status(a.status, DEV_STALE_PLAN);
+    return;
+  }
   const int bid = blockIdx.x;
   if (bid < nb1) {
     const int task = bid * 4 + w;
@@ -466,46 +488,47 @@ __global__ __launch_bounds__(256) void k_seg(DevArgs a) {
     float *dst = one ? a.G1 + (size_t)seg * W : a.G3 + (size_t)seg * W;
     const int beg = hist[(size_t)seg * a.nblk], end = hist[(size_t)(seg + 1) * a.nblk];
     if (beg >= end) return;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};  // W <= 256
-    const int c0c = min(lane, W - 1), c1c = min(lane + 64, W - 1), c2c = min(lane + 128, W - 1),
-              c3c = min(lane + 192, W - 1);
-    for (int s0 = beg; s0 < end; s0 += 64) {
-      const int sl = min(s0 + lane, end - 1);
-      const int lk = link[sl];
-      unsigned long long m = __ballot(s0 + lane < end && lk >= 0);
-      while (m) {
-        int ps[8];
-        int cnt = 0;
+    for (int col0 = 0; col0 < W; col0 += 256) {  // W <= 1024 (R2 * q3)
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      int cc[4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          ps[k] = -1;
-          if (m) {
-            const int l = __ffsll((long long)m) - 1;
-            m &= m - 1;
-            ps[k] = __builtin_amdgcn_readlane(lk, l);
-            ++cnt;
+      for (int j = 0; j < 4; ++j) cc[j] = min(col0 + lane + 64 * j, W - 1);
+      for (int s0 = beg; s0 < end; s0 += 64) {
+        const int sl = min(s0 + lane, end - 1);
+        const int lk = link[sl];
+        unsigned long long m = __ballot(s0 + lane < end && lk >= 0);
+        while (m) {
+          int ps[8];
+          int cnt = 0;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            ps[k] = -1;
+            if (m) {
+              const int l = __ffsll((long long)m) - 1;
+              m &= m - 1;
+              ps[k] = __builtin_amdgcn_readlane(lk, l);
+              ++cnt;
+            }
           }
+          float v[8][4];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float *row = part + (size_t)max(ps[k], 0) * W;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[k][j] = row[cc[j]];
+          }
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (k < cnt)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) acc[j] += v[k][j];
         }
-        float v[8][4];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float *row = part + (size_t)max(ps[k], 0) * W;
-          v[k][0] = row[c0c];
-          v[k][1] = row[c1c];
-          v[k][2] = row[c2c];
-          v[k][3] = row[c3c];
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (k < cnt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j] += v[k][j];
       }
-    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = lane + 64 * j;
-      if (col < W) dst[col] -= a.lr * acc[j];
+      for (int j = 0; j < 4; ++j) {
+        const int col = col0 + lane + 64 * j;
+        if (col < W) dst[col] -= a.lr * acc[j];
+      }
     }
     return;
   }

@@ -6,31 +6,39 @@
 //   stage 1  T[j1][j2][r2] = sum_r1 G1[i1][j1][r1] * G2[i2][r1][j2][r2]
 //   stage 2  W[i][(j1 q2 + j2) q3 + j3] = sum_r2 T[j1][j2][r2] * G3[i3][r2][j3]
 // and EmbeddingBag pooling out[b] += w_n * W[idx_n] (tensorflow/addons #2201: the
-// gathered rows are never materialised).
+// gathered rows are never materialised in global memory).
 //
 // One workgroup takes one work item: the elements of one (table, i2) group that
-// fall in one P-aligned piece of the grouping order (at most 64; all of them share
-// one G2 slice).  Stage 1 runs once per
-// distinct (i1, i2) pair ("pair"), as a GEMM on the fp32 matrix cores:
-//     T^T[r2][(pair, j1)] = sum_r1 G2[r1][j2][r2] * G1[i1(pair)][j1][r1]
-// with the column block j2 of G2 in LDS (transposed to [r2][r1], double-buffered,
-// the next block prefetched into registers during the MFMAs) and 16 (pair, j1)
-// rows per "M-block" in the MFMA column dimension.  Stage 2 runs once per
-// distinct index ("item") in VALU from the item's G3 slice staged in LDS, reducing
-// over the four lane groups; each element of the item then adds w * row into out
-// with fp32 atomics.  Bits of out may depend on the order of the atomics.
+// fall in one P-aligned piece of the grouping order (all of them share one G2
+// slice).  The kernel is built around three dependent rounds of global loads
+//   1. the work item (group, position range),
+//   2. the item's elements and its G2 slice (the first JB column blocks),
+//   3. the G1 rows of its distinct (i1, i2) pairs and the G3 slices of its
+//      distinct indices,
+// after which everything runs out of LDS and registers.  Stage 1 runs once per
+// pair as a GEMM on the fp32 matrix cores,
+//     T^T[r2][(pair, j1)] = sum_r1 G2[r1][j2][r2] * G1[i1(pair)][j1][r1],
+// with 16 (pair, j1) rows per "M-block" in the MFMA column dimension and G2^T
+// read from LDS as 16-byte vectors.  Stage 2 runs once per distinct index in VALU
+// and leaves the item's rows W in LDS; a last pass adds w * W[item] into each
+// element's bag with row-contiguous fp32 atomics.  Bits of out may depend on the
+// order of the atomics.
 #include "tt_internal.h"
 #include "tt_mfma.h"
 
 namespace ttb {
 
+// LDS carve of one forward workgroup (float words, then int words)
 template <int RP>
 struct FwdLds {
-  static constexpr int LD = RP + 4;
-  static constexpr int G2F = 2 * RP * LD;  // floats: double-buffered G2 column block
-  __host__ __device__ static size_t g3_floats(int q3) { return (size_t)ITEM_MAX * RP * q3; }
-  static constexpr int INTS = 64 * 2 + 65 + 64 + 65 + 64 + 8;
-  static size_t bytes(int q3) { return (G2F + g3_floats(q3)) * 4 + INTS * 4; }
+  static constexpr int LD = RP + 4;  // row pitch of G2^T [r2][r1]: conflict-free 16-byte reads
+  static constexpr int INTS = 64 * 4 + 65 * 2 + 64 + 16 + 8;
+  __host__ __device__ static size_t g2_floats(int JB) { return (size_t)JB * RP * LD; }
+  __host__ __device__ static size_t g3_floats(int P, int q3) { return (size_t)P * q3 * RP; }
+  __host__ __device__ static size_t w_floats(int P, int D, int sw) { return sw ? (size_t)P * D : 0; }
+  static size_t bytes(int JB, int P, int q3, int D, int sw) {
+    return (g2_floats(JB) + g3_floats(P, q3) + w_floats(P, D, sw)) * 4 + INTS * 4;
+  }
 };
 
 template <int RP>
@@ -38,68 +46,100 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
   constexpr int KS = RP / 4;   // k-steps: lane group g covers r1 = g*KS + ks
   constexpr int NM = RP / 16;  // 16-row blocks of r2
   constexpr int LD = FwdLds<RP>::LD;
-  constexpr int KP = (RP * RP + WG - 1) / WG;  // G2 column-block floats per thread
-  extern __shared__ float smem[];
+  extern __shared__ float4 smem4[];
+  float *smem = (float *)smem4;
   const int q1 = a.q1, q2 = a.q2, q3 = a.q3, R1 = a.R1, R2 = a.R2, D = a.D;
-  float *sG2 = smem;
-  float *sG3 = smem + FwdLds<RP>::G2F;                     // [item][RP][q3]
-  int *e_bag = (int *)(sG3 + FwdLds<RP>::g3_floats(q3));  // [64]
-  float *e_w = (float *)(e_bag + 64);                      // [64]
-  int *it_beg = (int *)(e_w + 64);                         // [65]
-  int *it_i3 = it_beg + 65;                                // [64]
-  int *pr_it = it_i3 + 64;                                 // [65]
-  int *pr_i1 = pr_it + 65;                                 // [64]
-  int *s_cnt = pr_i1 + 64;                                 // [8]
+  const int JB = a.JBf, P = a.P, SW = a.fwd_sw;
+  float *sG2 = smem;                                            // [JB][r2 < RP][LD]
+  float *sG3 = sG2 + FwdLds<RP>::g2_floats(JB);                 // [item][j3][r2 < RP]
+  float *sW = sG3 + FwdLds<RP>::g3_floats(P, q3);               // [item][D]
+  int *e_bag = (int *)(sW + FwdLds<RP>::w_floats(P, D, SW));  // [64]
+  float *e_w = (float *)(e_bag + 64);                           // [64]
+  int *e_it = (int *)(e_w + 64);                                // [64]
+  int *it_i3 = e_it + 64;                                       // [64]
+  int *it_beg = it_i3 + 64;                                     // [65]
+  int *pr_it = it_beg + 65;                                     // [65]
+  int *pr_i1 = pr_it + 65;                                      // [64]
+  int *mb_nk = pr_i1 + 64;                                      // [16]
+  int *s_cnt = mb_nk + 16;                                      // [8]
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int wi = blockIdx.x;
+  // round 1: plan check and work item
   const int plan = a.hdr[H_PLAN], nitems = a.hdr[H_NFWD];
   const int4 item = a.fitem[wi];
   if (plan != (int)a.plan_fp || wi >= nitems) return;
   const int grp = item.x, s0 = item.y, s1 = item.z;
   const int n_el = s1 - s0;
-  const int t = grp / a.p2, i2 = grp - t * a.p2;
-  const size_t g2base = (size_t)(t * a.p2 + i2) * R1 * q2 * R2;
+  const int t = grp / a.p2;
+  const float *G2g = a.G2 + (size_t)grp * R1 * q2 * R2;  // slice [r1][j2][r2]
   const float *G3t = a.G3 + (size_t)t * a.p3 * R2 * q3;
 
-  // G2 column block j2 -> registers (clamped addresses, zero padding)
-  float pf[KP];
-  auto fetch_g2 = [&](int j2) {
+  // G2 columns [j0, j0 + nj) -> LDS as G2^T blocks (zero padding to RP x RP), in
+  // batches of STAGE_U loads per thread
+  auto load2 = [&](int j0, int nj, int base, float *v) {
+    const int total = nj * RP * RP;
 #pragma unroll
-    for (int k = 0; k < KP; ++k) {
-      const int i = tid + k * WG;
-      const int r1 = i / RP, r2 = i - r1 * RP;
-      const bool ok = i < RP * RP && r1 < R1 && r2 < R2;
-      const float v = a.G2[g2base + ((size_t)(ok ? r1 : 0) * q2 + j2) * R2 + (ok ? r2 : 0)];
-      pf[k] = ok ? v : 0.f;
+    for (int u = 0; u < STAGE_U; ++u) {
+      const int i = min(base + u * WG, total - 1);
+      const int jj = i / (RP * RP), rem = i - jj * RP * RP;
+      const int r1 = rem / RP, r2 = rem - r1 * RP;
+      const bool ok = r1 < R1 && r2 < R2;
+      v[u] = G2g[((size_t)(ok ? r1 : 0) * q2 + j0 + jj) * R2 + (ok ? r2 : 0)];
     }
   };
-  auto store_g2 = [&](float *buf) {
+  auto store2 = [&](int nj, int base, const float *v) {
+    const int total = nj * RP * RP;
 #pragma unroll
-    for (int k = 0; k < KP; ++k) {
-      const int i = tid + k * WG;
-      if (i < RP * RP) {
-        const int r1 = i / RP, r2 = i - r1 * RP;
-        buf[r2 * LD + r1] = pf[k];
+    for (int u = 0; u < STAGE_U; ++u) {
+      const int i = base + u * WG;
+      if (i < total) {
+        const int jj = i / (RP * RP), rem = i - jj * RP * RP;
+        const int r1 = rem / RP, r2 = rem - r1 * RP;
+        sG2[(size_t)jj * RP * LD + r2 * LD + r1] = (r1 < R1 && r2 < R2) ? v[u] : 0.f;
       }
     }
   };
-  fetch_g2(0);
+  auto stage_g2 = [&](int j0, int nj, int first) {
+    for (int base = first; base < nj * RP * RP; base += WG * STAGE_U) {
+      float v[STAGE_U];
+      load2(j0, nj, base, v);
+      store2(nj, base, v);
+    }
+  };
+
+  // round 2: the elements (wave 0) and the first G2 stage (all waves; the first batch
+  // is in flight while wave 0 sorts out the elements)
+  const int nj0 = min(JB, q2);
+  float v2[STAGE_U];
+  load2(0, nj0, tid, v2);
   if (tid < 64) {
     const int s = s0 + min(tid, n_el - 1);
     const bool v = tid < n_el;
     const int dAv = a.s_dA[s], dIv = a.s_dI3[s], bagv = a.s_bag[s];
     const float wv = a.s_w[s];
     const int dA = v ? dAv : -1, i3 = v ? dIv - t * a.p3 : -1;
-    if (v) { e_bag[tid] = bagv; e_w[tid] = wv; }
+    e_bag[tid] = bagv;
+    e_w[tid] = wv;
     const int pdA = __shfl_up(dA, 1), pi3 = __shfl_up(i3, 1);
     const bool item_st = v && (tid == 0 || dA != pdA || i3 != pi3);
     const bool pair_st = v && (tid == 0 || dA != pdA);
     const unsigned long long mi = __ballot(item_st), mp = __ballot(pair_st);
     const unsigned long long lt = (tid == 0) ? 0ull : (~0ull >> (64 - tid));
     const int it = __popcll(mi & lt), pr = __popcll(mp & lt);
+    e_it[tid] = __popcll(mi & (lt | (1ull << tid))) - 1;
+    if (tid < 16) mb_nk[tid] = 0;
+    wave_lds_sync();
     if (item_st) { it_beg[it] = tid; it_i3[it] = i3; }
-    if (pair_st) { pr_it[pr] = it; pr_i1[pr] = dA - t * a.p1; }
+    if (pair_st) {
+      // items of this pair: item starts in [tid, next pair start)
+      const unsigned long long above = tid == 63 ? 0ull : (mp >> (tid + 1));
+      const int nxt = above ? tid + __ffsll((long long)above) : n_el;
+      const unsigned long long span = (nxt >= 64 ? ~0ull : ((1ull << nxt) - 1)) & ~lt;
+      pr_it[pr] = it;
+      pr_i1[pr] = dA - t * a.p1;
+      atomicMax(&mb_nk[(pr * q1) >> 4], __popcll(mi & span));
+    }
     if (tid == 0) {
       const int nI = __popcll(mi), nP = __popcll(mp);
       it_beg[nI] = n_el;
@@ -108,117 +148,141 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
       s_cnt[1] = nP;
     }
   }
-  store_g2(sG2);
+  store2(nj0, tid, v2);
+  stage_g2(0, nj0, tid + WG * STAGE_U);
   __syncthreads();
   const int nI = s_cnt[0], nP = s_cnt[1];
-  const int nmb = (nP * q1 + 15) / 16;
+  const int nmb = (nP * q1 + 15) >> 4;
 
-  // B operand of stage 1 (G1 rows of the wave's M-blocks), kept for all j2
+  // round 3: the G3 slices of the item's indices -> LDS [item][j3][r2 < RP], and the B
+  // operand of stage 1 (G1 rows of the wave's M-blocks, kept for all j2).  The first
+  // G3 batch and all G1 loads are issued before the first wait; rows past the pairs
+  // read a valid row and are zeroed afterwards.
+  const int per_item = RP * q3, total3 = nI * per_item;
+  auto load3 = [&](int base, float *v) {
+#pragma unroll
+    for (int u = 0; u < STAGE_U; ++u) {
+      const int i = min(base + u * WG, total3 - 1);
+      const int it = i / per_item, rem = i - it * per_item;  // rem = r2 * q3 + j3
+      v[u] = G3t[(size_t)it_i3[it] * R2 * q3 + (rem < R2 * q3 ? rem : 0)];
+    }
+  };
+  auto store3 = [&](int base, const float *v) {
+#pragma unroll
+    for (int u = 0; u < STAGE_U; ++u) {
+      const int i = base + u * WG;
+      if (i < total3) {
+        const int it = i / per_item, rem = i - it * per_item;
+        const int r2 = rem / q3, j3 = rem - r2 * q3;
+        sG3[(size_t)it * per_item + j3 * RP + r2] = r2 < R2 ? v[u] : 0.f;
+      }
+    }
+  };
+  float v3[STAGE_U];
+  load3(tid, v3);
   float bv[MBW][KS];
 #pragma unroll
   for (int mbi = 0; mbi < MBW; ++mbi) {
     const int row = (w + mbi * NW) * 16 + c;
     const int pr = row / q1, j1 = row - pr * q1;
-    const bool ok = (w + mbi * NW) < nmb && pr < nP;
-    const float *src = a.G1 + ((size_t)(t * a.p1 + (ok ? pr_i1[pr] : 0)) * q1 + j1) * R1;
+    const float *src = a.G1 + ((size_t)(t * a.p1 + pr_i1[min(pr, nP - 1)]) * q1 + j1) * R1;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bv[mbi][ks] = src[min(g * KS + ks, R1 - 1)];
+  }
+  store3(tid, v3);
+  for (int base = tid + WG * STAGE_U; base < total3; base += WG * STAGE_U) {
+    float v[STAGE_U];
+    load3(base, v);
+    store3(base, v);
+  }
+#pragma unroll
+  for (int mbi = 0; mbi < MBW; ++mbi) {
+    const int row = (w + mbi * NW) * 16 + c;
+    const bool ok = (w + mbi * NW) < nmb && row / q1 < nP;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int r1 = g * KS + ks;
-      const float v = src[min(r1, R1 - 1)];
-      bv[mbi][ks] = (ok && r1 < R1) ? v : 0.f;
+      const float v = keep(bv[mbi][ks]);
+      bv[mbi][ks] = (ok && g * KS + ks < R1) ? v : 0.f;
     }
   }
-  // the G3 slices of the chunk's items -> LDS [item][r2 < RP][j3] (zero padding),
-  // STAGE_U loads in flight per thread
-  {
-    const int per_item = RP * q3, total = nI * per_item;
-    for (int base = tid; base < total; base += WG * STAGE_U) {
-      float v[STAGE_U];
-#pragma unroll
-      for (int u = 0; u < STAGE_U; ++u) {
-        const int i = min(base + u * WG, total - 1);
-        const int it = i / per_item, rem = i - it * per_item;
-        const int r2 = rem / q3;
-        v[u] = G3t[(size_t)it_i3[it] * R2 * q3 + (r2 < R2 ? rem : 0)];
-      }
-#pragma unroll
-      for (int u = 0; u < STAGE_U; ++u) {
-        const int i = base + u * WG;
-        if (i < total) {
-          const int rem = i % per_item;
-          sG3[i] = (rem / q3 < R2) ? v[u] : 0.f;
-        }
-      }
-    }
-  }
-  if (q2 > 1) fetch_g2(1);
   __syncthreads();
 
-  for (int j2 = 0; j2 < q2; ++j2) {
-    const float *buf = sG2 + (j2 & 1) * RP * LD;
-#pragma unroll
-    for (int mbi = 0; mbi < MBW; ++mbi) {
-      const int mb = w + mbi * NW;
-      if (mb >= nmb) break;
-      f4 acc[NM];
-#pragma unroll
-      for (int m = 0; m < NM; ++m) acc[m] = zero4();
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-          acc[m] = mfma4(buf[(16 * m + c) * LD + g * KS + ks], bv[mbi][ks], acc[m]);
-      }
-      // stage 2: lane (g, c) holds T^T[r2 = 16m + 4g + v][row c] of this j2
-      const int row = mb * 16 + c;
-      const int pr = row / q1, j1 = row - pr * q1;
-      const bool okp = pr < nP;
-      const int ib = okp ? pr_it[pr] : 0, ie = okp ? pr_it[pr + 1] : 0;
-      const int nk = wave_max(ie - ib);
-      for (int kk = 0; kk < nk; ++kk) {
-        const int it = ib + kk;
-        const bool act = it < ie;
-        const float *g3 = sG3 + (size_t)(act ? it : 0) * RP * q3;
-        float part[MAXQ3];
-#pragma unroll
-        for (int j3 = 0; j3 < MAXQ3; ++j3) {
-          part[j3] = 0.f;
-          if (j3 < q3) {
-            float sacc = 0.f;
-#pragma unroll
-            for (int m = 0; m < NM; ++m)
-#pragma unroll
-              for (int v = 0; v < 4; ++v) sacc += acc[m][v] * g3[(16 * m + 4 * g + v) * q3 + j3];
-            sacc += __shfl_xor(sacc, 16);
-            sacc += __shfl_xor(sacc, 32);
-            part[j3] = sacc;
-          }
-        }
-        if (act) {
-          const int colbase = (j1 * q2 + j2) * q3;
-          for (int e = it_beg[it]; e < it_beg[it + 1]; ++e) {
-            float *yrow = a.Y + (size_t)e_bag[e] * D + colbase;
-            const float we = e_w[e];
-#pragma unroll
-            for (int j3 = 0; j3 < MAXQ3; ++j3)
-              if (j3 < q3 && (j3 & 3) == g) unsafeAtomicAdd(yrow + j3, we * part[j3]);
-          }
-        }
-      }
-    }
-    if (j2 + 1 < q2) {
-      store_g2(sG2 + ((j2 + 1) & 1) * RP * LD);
-      if (j2 + 2 < q2) fetch_g2(j2 + 2);
+  for (int j0 = 0; j0 < q2; j0 += JB) {
+    if (j0 > 0) {  // next G2 stage (only when the slice does not fit at once)
+      __syncthreads();
+      stage_g2(j0, min(JB, q2 - j0), tid);
       __syncthreads();
     }
+    const int jend = min(q2, j0 + JB);
+    for (int j2 = j0; j2 < jend; ++j2) {
+      const float *buf = sG2 + (size_t)(j2 - j0) * RP * LD;
+#pragma unroll
+      for (int mbi = 0; mbi < MBW; ++mbi) {
+        const int mb = w + mbi * NW;
+        if (mb >= nmb) break;
+        f4 acc[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) acc[m] = zero4();
+#pragma unroll
+        for (int kq = 0; kq < KS / 4; ++kq) {
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            const float4 av = *(const float4 *)&buf[(16 * m + c) * LD + g * KS + 4 * kq];
+            acc[m] = mfma4(av.x, bv[mbi][4 * kq + 0], acc[m]);
+            acc[m] = mfma4(av.y, bv[mbi][4 * kq + 1], acc[m]);
+            acc[m] = mfma4(av.z, bv[mbi][4 * kq + 2], acc[m]);
+            acc[m] = mfma4(av.w, bv[mbi][4 * kq + 3], acc[m]);
+          }
+        }
+        // stage 2: lane (g, c) holds T^T[r2 = 16m + 4g + v][row c] of this j2
+        const int row = mb * 16 + c;
+        const int pr = row / q1, j1 = row - pr * q1;
+        const bool okp = pr < nP;
+        const int ib = okp ? pr_it[pr] : 0, ie = okp ? pr_it[pr + 1] : 0;
+        const int nk = mb_nk[mb];
+        const int col0 = (j1 * q2 + j2) * q3;
+        for (int kk = 0; kk < nk; ++kk) {
+          const int it = ib + kk;
+          const bool act = it < ie;
+          const float *g3 = sG3 + (size_t)(act ? it : 0) * RP * q3 + 4 * g;
+          for (int j3 = 0; j3 < q3; ++j3) {
+            float sacc = 0.f;
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+              const float4 gv = *(const float4 *)&g3[j3 * RP + 16 * m];
+              sacc += acc[m][0] * gv.x + acc[m][1] * gv.y + acc[m][2] * gv.z + acc[m][3] * gv.w;
+            }
+            sacc += __shfl_xor(sacc, 16);
+            sacc += __shfl_xor(sacc, 32);
+            if (act && g == (j3 & 3)) {
+              if (SW) {
+                sW[(size_t)it * D + col0 + j3] = sacc;
+              } else {
+                for (int e = it_beg[it]; e < it_beg[it + 1]; ++e)
+                  unsafeAtomicAdd(a.Y + (size_t)e_bag[e] * D + col0 + j3, e_w[e] * sacc);
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+  if (!SW) return;
+  // pooling: out[bag] += w * W[item], one row-contiguous pass per element
+  __syncthreads();
+  for (int e = w; e < n_el; e += NW) {
+    const int it = e_it[e];
+    float *yrow = a.Y + (size_t)e_bag[e] * D;
+    const float we = e_w[e];
+    for (int d = lane; d < D; d += 64) unsafeAtomicAdd(yrow + d, we * sW[(size_t)it * D + d]);
   }
 }
 
-size_t fwd_lds_bytes(int RP, int q3) {
+size_t fwd_lds_bytes(int RP, int JB, int P, int q3, int D, int sw) {
   switch (RP) {
-    case 16: return FwdLds<16>::bytes(q3);
-    case 32: return FwdLds<32>::bytes(q3);
-    default: return FwdLds<64>::bytes(q3);
+    case 16: return FwdLds<16>::bytes(JB, P, q3, D, sw);
+    case 32: return FwdLds<32>::bytes(JB, P, q3, D, sw);
+    default: return FwdLds<64>::bytes(JB, P, q3, D, sw);
   }
 }
 

@@ -11,9 +11,9 @@
 //           k_route_final   stable scatter by (table,i2) -> final order
 //                           (table, i2, i1, i3, position); hits after misses by
 //                           (slot, position); skipped elements last.
-//   forward: k_fwd          one workgroup per 64-element chunk of an i2 group.
-//   backward: k_runsum      w * dY summed over runs of equal index (fixed pieces).
-//             k_bwd         one workgroup per i2 group.
+//   forward: k_fwd          one workgroup per work item (piece of an i2 group).
+//   backward: k_runsum      cache hits: w * dY summed over runs of one slot.
+//             k_bwd         one workgroup per work item.
 //             k_seg         core-1 / core-3 segment sums + SGD; cache-row SGD.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -31,10 +31,8 @@ constexpr int PIECE = 64;       // run-sum: positions per wave
 constexpr int ITEM_MAX = 64;    // most positions of one contraction work item
 constexpr int WG = 512;         // contraction workgroup: 8 waves
 constexpr int NW = WG / 64;
-constexpr int MBW = 2;          // forward: M-blocks (16 rows of (pair, j1)) per wave
-constexpr int CHP = 64;         // backward chunk: most (i1,i2) pairs held in LDS
-// backward: M-blocks per wave (register budget: one for rank-64 tiles)
-constexpr int bwd_mbw(int RP) { return RP == 64 ? 1 : 2; }
+constexpr int MBW = 1;          // forward: M-blocks (16 rows of (pair, j1)) per wave
+constexpr int P_MAX = 32;       // positions per work item: P * q1 <= 16 * NW rows
 constexpr int MAXQ3 = 16;
 constexpr int STAGE_U = 8;      // global loads in flight per thread when staging into LDS
 
@@ -57,10 +55,10 @@ struct DevArgs {
   int has_cache;
   int64_t cache_size;
   int NHB;
-  int CHI;          // backward chunk: max items (distinct indices)
-  int CHPb;         // backward chunk: max pairs (<= CHP)
-  int P;            // work item: positions per piece (32 or 64, divides PIECE)
+  int P;            // work item: positions per piece (8, 16 or 32; divides PIECE)
   int NRED;         // backward: LDS slots of the cross-wave dG2 reduction (divides NW)
+  int JBf, JBb;     // forward / backward: G2 column blocks (j2) staged in LDS at once
+  int fwd_sw;       // forward: 1 = rows of a work item kept in LDS and pooled at the end
   unsigned plan_fp;  // fingerprint of (shape, sizes, input pointers) of the plan
   // inputs / outputs
   const int64_t *idx;
@@ -115,8 +113,8 @@ hipError_t launch_yinit(const DevArgs &a, hipStream_t s);
 hipError_t launch_seg(const DevArgs &a, hipStream_t s);
 hipError_t launch_fwd(const DevArgs &a, int RP, size_t lds, hipStream_t s);
 hipError_t launch_bwd(const DevArgs &a, int RP, size_t lds, hipStream_t s);
-size_t fwd_lds_bytes(int RP, int q3);
-size_t bwd_lds_bytes(int RP, int CHI, int D, int q3, int nred);
+size_t fwd_lds_bytes(int RP, int JB, int P, int q3, int D, int sw);
+size_t bwd_lds_bytes(int RP, int JB, int P, int q3, int D, int nred);
 
 // Work items of both contraction kernels: every overlap of a miss group with a
 // P-aligned piece of the final order.  Upper bound of their number:

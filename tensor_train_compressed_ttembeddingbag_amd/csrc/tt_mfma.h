@@ -32,6 +32,14 @@ __device__ __forceinline__ int wave_max(int v) {
   return v;
 }
 
+// Pins a loaded value on every lane of the wave.  Without it the compiler may sink a
+// load whose result is used only under a per-lane condition into a divergent
+// branch, where it gets a full wait of its own instead of overlapping the others.
+__device__ __forceinline__ float keep(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // LDS ordering between lanes of one wave (write by one lane, read by another).
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");

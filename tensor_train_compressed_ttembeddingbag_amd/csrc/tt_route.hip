@@ -279,10 +279,11 @@ __global__ __launch_bounds__(RT) void k_route_final(DevArgs a) {
   }
 }
 
-// Backward: frag[s] = sum over positions of one run fragment of w_n * dY[bag n], where a
-// run is a maximal range of equal (dB, dA, dI3) in the final order (one index of one
-// table, or one cache slot) and fragments are the pieces of a run inside fixed
-// 64-position pieces.  One wave per piece; the summation order is the position order.
+// Backward, cache hits: frag[s] = sum over positions of one run fragment of
+// w_n * dY[bag n], where a run is a maximal range of equal (dB, dA, dI3) in the final
+// order (one cache slot) and fragments are the pieces of a run inside P-position
+// pieces.  One wave per 64 positions; the summation order is the position order.
+// (Misses sum their runs inside the backward contraction kernel.)
 __global__ __launch_bounds__(RT) void k_runsum(DevArgs a) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int piece = blockIdx.x * (RT / 64) + w;
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(RT) void k_runsum(DevArgs a) {
     if (piece == 0 && lane == 0) set_status(a.status, DEV_STALE_PLAN);
     return;
   }
-  if (beg >= V) return;
+  if (beg >= V || beg + PIECE <= a.hdr[H_HIT_BEG]) return;
   const int len = min(PIECE, V - beg);
   const int s = beg + min(lane, len - 1);
   const int kA = a.s_dA[s], kB = a.s_dB[s], kI = a.s_dI3[s], bag = a.s_bag[s];
@@ -353,7 +354,7 @@ hipError_t launch_yinit(const DevArgs &a, hipStream_t s) {
 
 hipError_t launch_runsum(const DevArgs &a, hipStream_t s) {
   const int pieces = (a.nnz + PIECE - 1) / PIECE;
-  if (pieces > 0) {
+  if (pieces > 0 && a.has_cache) {
     prof_begin(K_RUNSUM, s);
     hipLaunchKernelGGL(k_runsum, dim3((pieces + 3) / 4), dim3(RT), 0, s, a);
     prof_end(K_RUNSUM, s);

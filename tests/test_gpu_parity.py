@@ -86,6 +86,9 @@ SMALL = [
              lengths=("uniform", 0, 5), lr=0.1),
     W.custom("dup-heavy", p=(3, 2, 2), q=(4, 4, 2), ranks=(16, 16), bags_per_table=300,
              lengths=("uniform", 1, 30), init_std=0.3, lr=0.01, weighted=True),
+    # D = 1024: rows too wide to keep a work item's rows in LDS (pooled directly)
+    W.custom("wide D=1024", p=(5, 6, 7), q=(4, 16, 16), ranks=(24, 20), bags_per_table=16,
+             lengths=("uniform", 1, 6), init_std=0.3, lr=0.02, weighted=True),
 ]
 
 
