@@ -89,6 +89,11 @@ int make_plan(const tt_desc *d, int64_t nnz, int64_t num_bags, int64_t cache_siz
   a.has_cache = has_cache;
   a.cache_size = cache_size;
   a.NHB = NHB;
+  a.lq1 = a.q1 == 4 ? 2 : (a.q1 == 2 ? 1 : 0);
+  a.mq3 = fdiv_magic((unsigned)a.q3);
+  a.mD = fdiv_magic((unsigned)a.D);
+  a.rp23 = 1.0 / ((double)a.p2 * a.p3);
+  a.rp3 = 1.0 / (double)a.p3;
   const int Rmax = a.R1 > a.R2 ? a.R1 : a.R2;
   P->RP = Rmax <= 16 ? 16 : (Rmax <= 32 ? 32 : 64);
   // work items of P positions (P * q1 rows fill at most one M-block per wave); P shrinks

@@ -57,9 +57,12 @@ size_t bwd_lds_bytes(int RP, int JB, int P, int q3, int D, int nred) {
   }
 }
 
+// two workgroups per CU need <= 128 VGPRs (rank-64 tiles take one CU each)
 template <int RP>
-__global__ __launch_bounds__(WG) void k_bwd(DevArgs a) {
-  constexpr int KS = RP / 4, NM = RP / 16, LD = BwdLds<RP>::LD;
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(RP == 64 ? 2 : 4)))
+void k_bwd(DevArgs a) {
+  constexpr int KS = RP / 4, NM = RP / 16, LD = BwdLds<RP>::LD, LRP = log2_rp<RP>();
+  constexpr int JU = 2;  // j3 per batch of the item loop (register budget)
   extern __shared__ float4 smem4[];
   float *smem = (float *)smem4;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
@@ -104,8 +107,7 @@ __global__ __launch_bounds__(WG) void k_bwd(DevArgs a) {
 #pragma unroll
     for (int u = 0; u < STAGE_U; ++u) {
       const int i = min(base + u * WG, total - 1);
-      const int jj = i / (RP * RP), rem = i - jj * RP * RP;
-      const int r1 = rem / RP, r2 = rem - r1 * RP;
+      const int jj = i >> (2 * LRP), r1 = (i >> LRP) & (RP - 1), r2 = i & (RP - 1);
       const bool ok = r1 < R1 && r2 < R2;
       v[u] = G2g[((size_t)(ok ? r1 : 0) * q2 + j0 + jj) * R2 + (ok ? r2 : 0)];
     }
@@ -116,8 +118,7 @@ __global__ __launch_bounds__(WG) void k_bwd(DevArgs a) {
     for (int u = 0; u < STAGE_U; ++u) {
       const int i = base + u * WG;
       if (i < total) {
-        const int jj = i / (RP * RP), rem = i - jj * RP * RP;
-        const int r1 = rem / RP, r2 = rem - r1 * RP;
+        const int jj = i >> (2 * LRP), r1 = (i >> LRP) & (RP - 1), r2 = i & (RP - 1);
         sG2[(size_t)jj * RP * LD + r2 * LD + r1] = (r1 < R1 && r2 < R2) ? v[u] : 0.f;
       }
     }
@@ -192,12 +193,12 @@ __global__ __launch_bounds__(WG) void k_bwd(DevArgs a) {
   // operand layouts, w * dY rows of the elements.  First batches of everything are
   // issued before the first wait.
   const int per_item = RP * q3, total3 = nI * per_item, totalY = n_el * D;
-  auto load3 = [&](int base, float *v) {
+  auto load3 = [&](int base, float *v) {  // i = (item * q3 + j3) * RP + r2
 #pragma unroll
     for (int u = 0; u < STAGE_U; ++u) {
       const int i = min(base + u * WG, total3 - 1);
-      const int it = i / per_item, rem = i - it * per_item;  // rem = r2 * q3 + j3
-      v[u] = G3t[(size_t)it_i3[it] * W3 + (rem < (int)W3 ? rem : 0)];
+      const int jr = i >> LRP, it = fdiv(jr, a.mq3), j3 = jr - it * q3, r2 = i & (RP - 1);
+      v[u] = G3t[it_i3[it] * (int)W3 + (r2 < R2 ? r2 : 0) * q3 + j3];
     }
   };
   auto store3 = [&](int base, const float *v) {
@@ -205,11 +206,8 @@ __global__ __launch_bounds__(WG) void k_bwd(DevArgs a) {
     for (int u = 0; u < STAGE_U; ++u) {
       const int i = base + u * WG;
       if (i < total3) {
-        const int it = i / per_item, rem = i - it * per_item;
-        const int r2 = rem / q3, j3 = rem - r2 * q3;
-        const size_t o = (size_t)it * per_item + j3 * RP + r2;
-        sG3[o] = r2 < R2 ? v[u] : 0.f;
-        sdA3[o] = 0.f;
+        sG3[i] = (i & (RP - 1)) < R2 ? v[u] : 0.f;
+        sdA3[i] = 0.f;
       }
     }
   };
@@ -217,7 +215,7 @@ __global__ __launch_bounds__(WG) void k_bwd(DevArgs a) {
 #pragma unroll
     for (int u = 0; u < STAGE_U; ++u) {
       const int i = min(base + u * WG, totalY - 1);
-      const int e = i / D, d = i - e * D;
+      const int e = fdiv(i, a.mD), d = i - e * D;
       v[u] = a.dY[(size_t)e_bag[e] * D + d];
     }
   };
@@ -225,7 +223,7 @@ __global__ __launch_bounds__(WG) void k_bwd(DevArgs a) {
 #pragma unroll
     for (int u = 0; u < STAGE_U; ++u) {
       const int i = base + u * WG;
-      if (i < totalY) sYe[i] = e_w[i / D] * v[u];
+      if (i < totalY) sYe[i] = e_w[fdiv(i, a.mD)] * v[u];
     }
   };
   float v3[STAGE_U], vy[STAGE_U];
@@ -235,14 +233,14 @@ __global__ __launch_bounds__(WG) void k_bwd(DevArgs a) {
   float aG[4][NM];       // A1[row = 16mb + 4g + sr][r1 = 16mr + c] (dG2)
   {
     const int row = mb * 16 + c;
-    const int pr = row / q1, j1 = row - pr * q1;
+    const int pr = row >> a.lq1, j1 = row & (q1 - 1);
     const float *src = G1t + ((size_t)pr_i1[min(pr, nP - 1)] * q1 + j1) * R1;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) aT[ks] = src[min(g * KS + ks, R1 - 1)];
 #pragma unroll
     for (int sr = 0; sr < 4; ++sr) {
       const int row2 = mb * 16 + 4 * g + sr;
-      const int pr2 = row2 / q1, j12 = row2 - pr2 * q1;
+      const int pr2 = row2 >> a.lq1, j12 = row2 & (q1 - 1);
       const float *src2 = G1t + ((size_t)pr_i1[min(pr2, nP - 1)] * q1 + j12) * R1;
 #pragma unroll
       for (int mr = 0; mr < NM; ++mr) aG[sr][mr] = src2[min(16 * mr + c, R1 - 1)];
@@ -262,7 +260,7 @@ __global__ __launch_bounds__(WG) void k_bwd(DevArgs a) {
   }
   {
     const int row = mb * 16 + c;
-    const bool ok = mb < nmb && row / q1 < nP;
+    const bool ok = mb < nmb && (row >> a.lq1) < nP;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const float x = keep(aT[ks]);
@@ -271,7 +269,7 @@ __global__ __launch_bounds__(WG) void k_bwd(DevArgs a) {
 #pragma unroll
     for (int sr = 0; sr < 4; ++sr) {
       const int row2 = mb * 16 + 4 * g + sr;
-      const bool ok2 = mb < nmb && row2 / q1 < nP;
+      const bool ok2 = mb < nmb && (row2 >> a.lq1) < nP;
 #pragma unroll
       for (int mr = 0; mr < NM; ++mr) {
         const float x = keep(aG[sr][mr]);
@@ -282,7 +280,7 @@ __global__ __launch_bounds__(WG) void k_bwd(DevArgs a) {
   __syncthreads();
   // G_u of every item: its elements' w * dY rows summed in position order
   for (int i = tid; i < nI * D; i += WG) {
-    const int it = i / D, d = i - it * D;
+    const int it = fdiv(i, a.mD), d = i - it * D;
     float acc = 0.f;
     for (int e = it_beg[it]; e < it_beg[it + 1]; ++e) acc += sYe[(size_t)e * D + d];
     sGu[i] = acc;
@@ -293,7 +291,10 @@ __global__ __launch_bounds__(WG) void k_bwd(DevArgs a) {
 #pragma unroll
   for (int mr = 0; mr < NM; ++mr) dA1[mr] = zero4();
   const int rb = mb * 16 + 4 * g;  // the lane group's rows rb .. rb+3
-  const int plo = rb / q1, phi = min((rb + 3) / q1, nP - 1);
+  int j1v[4], prv[4];              // their j1 and pair
+#pragma unroll
+  for (int v = 0; v < 4; ++v) { j1v[v] = (rb + v) & (q1 - 1); prv[v] = (rb + v) >> a.lq1; }
+  const int plo = rb >> a.lq1, phi = min((rb + 3) >> a.lq1, nP - 1);
   const int ib = (mb < nmb && plo < nP) ? pr_it[plo] : 0;
   const int ie = (mb < nmb && plo < nP) ? pr_it[phi + 1] : 0;
   const int nk = mb < nmb ? mb_nk[mb] : 0;
@@ -336,26 +337,43 @@ __global__ __launch_bounds__(WG) void k_bwd(DevArgs a) {
           const float *g3 = sG3 + (size_t)itc * per_item + c;
           const float *gu = sGu + (size_t)itc * D;
           float *da3 = sdA3 + (size_t)itc * per_item + c;
-          for (int j3 = 0; j3 < q3; ++j3) {
-            float gv[4];
+          // JU j3 at a time: all LDS reads of the block first, then the arithmetic,
+          // then the updated dG3 partials (one writer lane per element)
+          for (int j30 = 0; j30 < q3; j30 += JU) {
+            float gx[JU][4], a3[JU][NM], d3[JU][NM];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int row = rb + v;
-              const int j1 = row - (row / q1) * q1;
-              const float x = gu[(j1 * q2 + j2) * q3 + j3];
-              gv[v] = (act && row / q1 == pr) ? x : 0.f;
-            }
+            for (int u = 0; u < JU; ++u) {
+              const int j3 = min(j30 + u, q3 - 1);
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-              const float a3v = g3[j3 * RP + 16 * m];
-              float sacc = 0.f;
+              for (int v = 0; v < 4; ++v) gx[u][v] = gu[((j1v[v]) * q2 + j2) * q3 + j3];
 #pragma unroll
-              for (int v = 0; v < 4; ++v) {
-                sacc += T[m][v] * gv[v];
-                dT[m][v] += gv[v] * a3v;
+              for (int m = 0; m < NM; ++m) {
+                a3[u][m] = g3[j3 * RP + 16 * m];
+                d3[u][m] = da3[j3 * RP + 16 * m];
               }
-              if (act) da3[j3 * RP + 16 * m] += sacc;
             }
+#pragma unroll
+            for (int u = 0; u < JU; ++u) {
+              const bool ok3 = act && j30 + u < q3;
+              float gv[4];
+#pragma unroll
+              for (int v = 0; v < 4; ++v) gv[v] = (ok3 && prv[v] == pr) ? gx[u][v] : 0.f;
+#pragma unroll
+              for (int m = 0; m < NM; ++m) {
+                float sacc = 0.f;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                  sacc += T[m][v] * gv[v];
+                  dT[m][v] += gv[v] * a3[u][m];
+                }
+                d3[u][m] += sacc;
+              }
+            }
+#pragma unroll
+            for (int u = 0; u < JU; ++u)
+              if (act && j30 + u < q3)
+#pragma unroll
+                for (int m = 0; m < NM; ++m) da3[(j30 + u) * RP + 16 * m] = d3[u][m];
           }
         }
         // dG2 += A1^T dT   (K = the 16 rows; lane group g feeds rows 4g + sr)
@@ -403,11 +421,11 @@ __global__ __launch_bounds__(WG) void k_bwd(DevArgs a) {
         }
         __syncthreads();
       }
-      for (int i = tid; i < R1 * R2; i += WG) {
-        const int r1 = i / R2, r2 = i - r1 * R2;
+      for (int i = tid; i < RP * RP; i += WG) {
+        const int r1 = i >> LRP, r2 = i & (RP - 1);
         float val = 0.f;
-        for (int k = 0; k < nred; ++k) val += sRed[(size_t)k * RP * LD + r1 * LD + r2];
-        part2[((size_t)r1 * q2 + j2) * R2 + r2] = val;
+        for (int k = 0; k < nred; ++k) val += sRed[k * RP * LD + r1 * LD + r2];
+        if (r1 < R1 && r2 < R2) part2[(r1 * q2 + j2) * R2 + r2] = val;
       }
       __syncthreads();
     }
@@ -415,7 +433,7 @@ __global__ __launch_bounds__(WG) void k_bwd(DevArgs a) {
   // dG1 partial per pair, dG3 partial per item, at their first positions
   if (mb < nmb) {
     const int row = mb * 16 + c;
-    const int pr = row / q1, j1 = row - pr * q1;
+    const int pr = row >> a.lq1, j1 = row & (q1 - 1);
     if (pr < nP) {
       float *dst = a.part1 + (size_t)(s0 + it_beg[pr_it[pr]]) * W1 + (size_t)j1 * R1;
 #pragma unroll
@@ -427,10 +445,9 @@ __global__ __launch_bounds__(WG) void k_bwd(DevArgs a) {
         }
     }
   }
-  for (int i = tid; i < nI * (int)W3; i += WG) {
-    const int it = i / W3, rem = i - it * W3;
-    const int r2 = rem / q3, j3 = rem - r2 * q3;
-    a.part3[(size_t)(s0 + it_beg[it]) * W3 + rem] = sdA3[(size_t)it * per_item + j3 * RP + r2];
+  for (int i = tid; i < total3; i += WG) {  // i = (item * q3 + j3) * RP + r2
+    const int jr = i >> LRP, it = fdiv(jr, a.mq3), j3 = jr - it * q3, r2 = i & (RP - 1);
+    if (r2 < R2) a.part3[(size_t)(s0 + it_beg[it]) * W3 + r2 * q3 + j3] = sdA3[i];
   }
 }
 

@@ -4,6 +4,22 @@
 
 namespace ttb {
 
+// Row split i -> (i1, i2, i3) of a valid row i (0 <= i < p1*p2*p3 < 2^40), with
+// i = (i1*p2 + i2)*p3 + i3.  The quotients come from double reciprocals (rp23 = 1/(p2*p3),
+// rp3 = 1/p3): their products are within a few ulps of the exact quotients, so the
+// truncation is exact or one too small, which one remainder check corrects.
+static __device__ __forceinline__ void split_index(int64_t i, int p3, int64_t p23, double rp23,
+                                                   double rp3, int &i1, int &i2, int &i3) {
+  int q1 = (int)((double)i * rp23);
+  int64_t r = i - (int64_t)q1 * p23;
+  if (r >= p23) { ++q1; r -= p23; } else if (r < 0) { --q1; r += p23; }
+  const int rr = (int)r;
+  int q2 = (int)((double)rr * rp3);
+  int r3 = rr - q2 * p3;
+  if (r3 >= p3) { ++q2; r3 -= p3; } else if (r3 < 0) { --q2; r3 += p3; }
+  i1 = q1; i2 = q2; i3 = r3;
+}
+
 // inclusive scan across the 64 lanes of a wave
 static __device__ __forceinline__ int wave_incl_scan(int x) {
   const int lane = threadIdx.x & 63;

@@ -45,7 +45,7 @@ template <int RP>
 __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
   constexpr int KS = RP / 4;   // k-steps: lane group g covers r1 = g*KS + ks
   constexpr int NM = RP / 16;  // 16-row blocks of r2
-  constexpr int LD = FwdLds<RP>::LD;
+  constexpr int LD = FwdLds<RP>::LD, LRP = log2_rp<RP>();
   extern __shared__ float4 smem4[];
   float *smem = (float *)smem4;
   const int q1 = a.q1, q2 = a.q2, q3 = a.q3, R1 = a.R1, R2 = a.R2, D = a.D;
@@ -73,7 +73,8 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
   const int n_el = s1 - s0;
   const int t = grp / a.p2;
   const float *G2g = a.G2 + (size_t)grp * R1 * q2 * R2;  // slice [r1][j2][r2]
-  const float *G3t = a.G3 + (size_t)t * a.p3 * R2 * q3;
+  const size_t W3 = (size_t)R2 * q3;
+  const float *G3t = a.G3 + (size_t)t * a.p3 * W3;
 
   // G2 columns [j0, j0 + nj) -> LDS as G2^T blocks (zero padding to RP x RP), in
   // batches of STAGE_U loads per thread
@@ -82,8 +83,7 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
 #pragma unroll
     for (int u = 0; u < STAGE_U; ++u) {
       const int i = min(base + u * WG, total - 1);
-      const int jj = i / (RP * RP), rem = i - jj * RP * RP;
-      const int r1 = rem / RP, r2 = rem - r1 * RP;
+      const int jj = i >> (2 * LRP), r1 = (i >> LRP) & (RP - 1), r2 = i & (RP - 1);
       const bool ok = r1 < R1 && r2 < R2;
       v[u] = G2g[((size_t)(ok ? r1 : 0) * q2 + j0 + jj) * R2 + (ok ? r2 : 0)];
     }
@@ -94,8 +94,7 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
     for (int u = 0; u < STAGE_U; ++u) {
       const int i = base + u * WG;
       if (i < total) {
-        const int jj = i / (RP * RP), rem = i - jj * RP * RP;
-        const int r1 = rem / RP, r2 = rem - r1 * RP;
+        const int jj = i >> (2 * LRP), r1 = (i >> LRP) & (RP - 1), r2 = i & (RP - 1);
         sG2[(size_t)jj * RP * LD + r2 * LD + r1] = (r1 < R1 && r2 < R2) ? v[u] : 0.f;
       }
     }
@@ -159,23 +158,19 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
   // G3 batch and all G1 loads are issued before the first wait; rows past the pairs
   // read a valid row and are zeroed afterwards.
   const int per_item = RP * q3, total3 = nI * per_item;
-  auto load3 = [&](int base, float *v) {
+  auto load3 = [&](int base, float *v) {  // i = (item * q3 + j3) * RP + r2
 #pragma unroll
     for (int u = 0; u < STAGE_U; ++u) {
       const int i = min(base + u * WG, total3 - 1);
-      const int it = i / per_item, rem = i - it * per_item;  // rem = r2 * q3 + j3
-      v[u] = G3t[(size_t)it_i3[it] * R2 * q3 + (rem < R2 * q3 ? rem : 0)];
+      const int jr = i >> LRP, it = fdiv(jr, a.mq3), j3 = jr - it * q3, r2 = i & (RP - 1);
+      v[u] = G3t[it_i3[it] * (int)W3 + (r2 < R2 ? r2 : 0) * q3 + j3];
     }
   };
   auto store3 = [&](int base, const float *v) {
 #pragma unroll
     for (int u = 0; u < STAGE_U; ++u) {
       const int i = base + u * WG;
-      if (i < total3) {
-        const int it = i / per_item, rem = i - it * per_item;
-        const int r2 = rem / q3, j3 = rem - r2 * q3;
-        sG3[(size_t)it * per_item + j3 * RP + r2] = r2 < R2 ? v[u] : 0.f;
-      }
+      if (i < total3) sG3[i] = (i & (RP - 1)) < R2 ? v[u] : 0.f;
     }
   };
   float v3[STAGE_U];
@@ -184,7 +179,7 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
 #pragma unroll
   for (int mbi = 0; mbi < MBW; ++mbi) {
     const int row = (w + mbi * NW) * 16 + c;
-    const int pr = row / q1, j1 = row - pr * q1;
+    const int pr = row >> a.lq1, j1 = row & (q1 - 1);
     const float *src = a.G1 + ((size_t)(t * a.p1 + pr_i1[min(pr, nP - 1)]) * q1 + j1) * R1;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) bv[mbi][ks] = src[min(g * KS + ks, R1 - 1)];
@@ -198,7 +193,7 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
 #pragma unroll
   for (int mbi = 0; mbi < MBW; ++mbi) {
     const int row = (w + mbi * NW) * 16 + c;
-    const bool ok = (w + mbi * NW) < nmb && row / q1 < nP;
+    const bool ok = (w + mbi * NW) < nmb && (row >> a.lq1) < nP;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const float v = keep(bv[mbi][ks]);
@@ -236,7 +231,7 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
         }
         // stage 2: lane (g, c) holds T^T[r2 = 16m + 4g + v][row c] of this j2
         const int row = mb * 16 + c;
-        const int pr = row / q1, j1 = row - pr * q1;
+        const int pr = row >> a.lq1, j1 = row & (q1 - 1);
         const bool okp = pr < nP;
         const int ib = okp ? pr_it[pr] : 0, ie = okp ? pr_it[pr + 1] : 0;
         const int nk = mb_nk[mb];
@@ -245,21 +240,30 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
           const int it = ib + kk;
           const bool act = it < ie;
           const float *g3 = sG3 + (size_t)(act ? it : 0) * RP * q3 + 4 * g;
-          for (int j3 = 0; j3 < q3; ++j3) {
-            float sacc = 0.f;
+          // four j3 at a time: independent sums, then lane group g keeps j3 = j30 + g
+          for (int j30 = 0; j30 < q3; j30 += 4) {
+            float sacc[4];
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-              const float4 gv = *(const float4 *)&g3[j3 * RP + 16 * m];
-              sacc += acc[m][0] * gv.x + acc[m][1] * gv.y + acc[m][2] * gv.z + acc[m][3] * gv.w;
+            for (int u = 0; u < 4; ++u) {
+              const int j3 = min(j30 + u, q3 - 1);
+              float x = 0.f;
+#pragma unroll
+              for (int m = 0; m < NM; ++m) {
+                const float4 gv = *(const float4 *)&g3[j3 * RP + 16 * m];
+                x += acc[m][0] * gv.x + acc[m][1] * gv.y + acc[m][2] * gv.z + acc[m][3] * gv.w;
+              }
+              sacc[u] = x;
             }
-            sacc += __shfl_xor(sacc, 16);
-            sacc += __shfl_xor(sacc, 32);
-            if (act && g == (j3 & 3)) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sacc[u] = sum_lane_groups(sacc[u]);
+            const float val = g == 0 ? sacc[0] : (g == 1 ? sacc[1] : (g == 2 ? sacc[2] : sacc[3]));
+            const int j3 = j30 + g;
+            if (act && j3 < q3) {
               if (SW) {
-                sW[(size_t)it * D + col0 + j3] = sacc;
+                sW[(size_t)it * D + col0 + j3] = val;
               } else {
                 for (int e = it_beg[it]; e < it_beg[it + 1]; ++e)
-                  unsafeAtomicAdd(a.Y + (size_t)e_bag[e] * D + col0 + j3, e_w[e] * sacc);
+                  unsafeAtomicAdd(a.Y + (size_t)e_bag[e] * D + col0 + j3, e_w[e] * val);
               }
             }
           }

@@ -58,6 +58,9 @@ struct DevArgs {
   int P;            // work item: positions per piece (8, 16 or 32; divides PIECE)
   int NRED;         // backward: LDS slots of the cross-wave dG2 reduction (divides NW)
   int JBf, JBb;     // forward / backward: G2 column blocks (j2) staged in LDS at once
+  int lq1;          // log2(q1)
+  unsigned mq3, mD; // fdiv multipliers of q3 and D
+  double rp23, rp3; // 1 / (p2 * p3), 1 / p3 (row split)
   int fwd_sw;       // forward: 1 = rows of a work item kept in LDS and pooled at the end
   unsigned plan_fp;  // fingerprint of (shape, sizes, input pointers) of the plan
   // inputs / outputs
@@ -91,6 +94,18 @@ struct DevArgs {
 };
 
 // ---------------------------------------------------------------- helpers
+// floor(k / d) for 0 <= k < 2^16 and 1 <= d <= 2^16 with one high multiply by
+// m = ceil(2^32 / d) (m = 0 stands for d = 1).  Exact: k * m / 2^32 exceeds k / d by
+// less than k / 2^32 < 2^-16 <= 1 / d, which cannot carry it past the next integer.
+inline unsigned fdiv_magic(unsigned d) {
+  return d == 1 ? 0u : (unsigned)(((1ull << 32) + d - 1) / d);
+}
+__device__ __forceinline__ int fdiv(int k, unsigned m) {
+  return m ? (int)__umulhi((unsigned)k, m) : k;
+}
+template <int RP>
+constexpr int log2_rp() { return RP == 16 ? 4 : (RP == 32 ? 5 : 6); }
+
 __device__ __forceinline__ void set_status(int32_t *st, int bit) {
   if (st) atomicOr(st, bit);
 }
@@ -101,13 +116,13 @@ constexpr int DEV_STALE_PLAN = 16;
 // kernels named by the optional per-kernel timer (tt_prof.hip)
 enum KernelId {
   K_ROUTE_FIRST, K_ROUTE_PASS1, K_ROUTE_PASS2, K_ROUTE_FINAL, K_FWD, K_RUNSUM, K_BWD, K_SEG,
-  K_CACHE_LOOKUP, K_YINIT, K_COUNT
+  K_CACHE_LOOKUP, K_YINIT, K_ROUTE_SMALL, K_COUNT
 };
 void prof_begin(int id, hipStream_t s);
 void prof_end(int id, hipStream_t s);
 
 // host launchers (each kernel is launched from the file that defines it)
-hipError_t launch_route(const DevArgs &a, hipStream_t s);   // the four grouping kernels
+hipError_t launch_route(const DevArgs &a, hipStream_t s);   // the grouping kernels
 hipError_t launch_runsum(const DevArgs &a, hipStream_t s);
 hipError_t launch_yinit(const DevArgs &a, hipStream_t s);
 hipError_t launch_seg(const DevArgs &a, hipStream_t s);

@@ -32,6 +32,18 @@ __device__ __forceinline__ int wave_max(int v) {
   return v;
 }
 
+// Sum of x over the four lane groups (lanes l, l^16, l^32, l^48), returned to all
+// four.  gfx950's permlane swaps exchange row halves of two registers in VALU:
+// swapping x with itself and adding gives x + x[l^32], then x + x[l^16].
+__device__ __forceinline__ float sum_lane_groups(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const unsigned uy = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane16_swap(uy, uy, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Pins a loaded value on every lane of the wave.  Without it the compiler may sink a
 // load whose result is used only under a per-lane condition into a divergent
 // branch, where it gets a full wait of its own instead of overlapping the others.

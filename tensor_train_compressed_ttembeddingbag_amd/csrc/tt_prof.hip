@@ -24,7 +24,7 @@ hipEvent_t g_open[K_COUNT] = {nullptr};
 
 const char *g_names[K_COUNT] = {"k_route_first", "k_route_pass1", "k_route_pass2",
                                 "k_route_final", "k_fwd", "k_runsum", "k_bwd", "k_seg",
-                                "k_cache_lookup", "k_yinit"};
+                                "k_cache_lookup", "k_yinit", "k_route_small"};
 
 hipEvent_t take() {
   if (!g_pool.empty()) {

@@ -41,6 +41,34 @@ static __device__ int half_find_bag(const int64_t *off, int NB, int n, int half,
 
 constexpr int ROUTE_MAX_BAGS = 2048;  // offsets of one routing block kept in LDS
 
+// Work items from the group table grp_off[0..binsB] (starts of the (table, i2) bins
+// in the final order): a miss group of n elements becomes ceil(n / P) items of
+// near-equal size (at most P positions each), numbered group by group.  Also the
+// header words of the grouping.  Run by one whole block.
+static __device__ void build_items(const DevArgs &a, int *s_scan) {
+  const int G = a.T * a.p2, tid = threadIdx.x, nt = blockDim.x;
+  for (int g = tid; g <= G; g += nt) {
+    const int gb = a.grp_off[g], ge = g < G ? a.grp_off[g + 1] : gb;
+    a.chunk_pre[g] = (ge - gb + a.P - 1) / a.P;
+  }
+  __threadfence_block();
+  __syncthreads();
+  block_exclusive_scan(a.chunk_pre, G + 1, s_scan);
+  for (int g = tid; g < G; g += nt) {
+    const int first = a.chunk_pre[g], nc = a.chunk_pre[g + 1] - first;
+    const int gb = a.grp_off[g], n = a.grp_off[g + 1] - gb;
+    for (int c = 0; c < nc; ++c)
+      a.fitem[first + c] = make_int4(g, gb + (int)((int64_t)n * c / nc),
+                                     gb + (int)((int64_t)n * (c + 1) / nc), 0);
+  }
+  if (tid == 0) {
+    a.hdr[H_NFWD] = a.chunk_pre[G];
+    a.hdr[H_HIT_BEG] = a.grp_off[G];
+    a.hdr[H_HIT_END] = a.grp_off[a.binsB - 1];
+    a.hdr[H_VALID] = a.grp_off[a.binsB - 1];
+  }
+}
+
 __global__ __launch_bounds__(RT) void k_route_first(DevArgs a) {
   extern __shared__ int lds_i[];       // [binsI3] histogram, then the block's offsets
   __shared__ int s_scan[RT + 1];
@@ -112,10 +140,8 @@ __global__ __launch_bounds__(RT) void k_route_first(DevArgs a) {
         set_status(a.status, TT_DEV_BAD_INDEX);
         dA = dropA; dB = dropB; dI = dropI;
       } else {
-        const int64_t p23 = (int64_t)a.p2 * a.p3;
-        const int i1 = (int)(i / p23);
-        const int i2 = (int)((i / a.p3) % a.p2);
-        const int i3 = (int)(i % a.p3);
+        int i1, i2, i3;
+        split_index(i, a.p3, (int64_t)a.p2 * a.p3, a.rp23, a.rp3, i1, i2, i3);
         dA = t * a.p1 + i1;
         dB = t * a.p2 + i2;
         dI = t * a.p3 + i3;
@@ -208,33 +234,11 @@ __global__ __launch_bounds__(RT) void k_route_pass(DevArgs a, int pass) {
   const int binsN = pass == 1 ? a.binsA : a.binsB;
   block_exclusive_scan(hnext, binsN * a.nblk, s_scan);
   if (pass == 2) {
-    const int G = a.T * a.p2;
     for (int b = tid; b < a.binsB; b += RT) a.grp_off[b] = a.histB[(size_t)b * a.nblk];
     if (tid == 0) a.grp_off[a.binsB] = a.nnz;
     __threadfence_block();
     __syncthreads();
-    for (int g = tid; g <= G; g += RT) {
-      const int gb = a.grp_off[g], ge = g < G ? a.grp_off[g + 1] : gb;
-      a.chunk_pre[g] = ge > gb ? (ge - 1) / a.P - gb / a.P + 1 : 0;  // pieces overlapping g
-    }
-    __threadfence_block();
-    __syncthreads();
-    block_exclusive_scan(a.chunk_pre, G + 1, s_scan);
-    // work items: group g meets the pieces [k*P, (k+1)*P) for k = gb/P .. (ge-1)/P
-    for (int g = tid; g < G; g += RT) {
-      const int first = a.chunk_pre[g], n = a.chunk_pre[g + 1] - first;
-      const int gb = a.grp_off[g], ge = a.grp_off[g + 1];
-      const int k0 = gb / a.P;
-      for (int c = 0; c < n; ++c)
-        a.fitem[first + c] =
-            make_int4(g, max(gb, (k0 + c) * a.P), min(ge, (k0 + c + 1) * a.P), 0);
-    }
-    if (tid == 0) {
-      a.hdr[H_NFWD] = a.chunk_pre[G];
-      a.hdr[H_HIT_BEG] = a.grp_off[G];
-      a.hdr[H_HIT_END] = a.grp_off[a.binsB - 1];
-      a.hdr[H_VALID] = a.grp_off[a.binsB - 1];
-    }
+    build_items(a, s_scan);
   }
 }
 
@@ -325,8 +329,285 @@ __global__ __launch_bounds__(RT) void k_runsum(DevArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- one-block route
+// Batches of at most SR_MAX elements with at most SR_BINS bins per digit and at most
+// SR_OFF - 1 bags are grouped by a single 1024-thread workgroup with everything in
+// LDS: the same three stable counting passes (by (t,i3), (t,i1), (t,i2)) and the
+// same outputs as the multi-block kernels, without their grid-wide scans.
+constexpr int SR_T = 1024, SR_W = SR_T / 64;
+constexpr int SR_MAX = 12288;               // elements (u16 positions)
+constexpr int SR_K = SR_MAX / SR_T;         // positions per lane and pass
+constexpr int SR_BINS = 1024;
+constexpr int SR_OFF = 8192;                // offsets kept in LDS (in the count area)
+constexpr size_t SR_LDS = (size_t)5 * SR_MAX * 2 + (size_t)SR_W * SR_BINS * 2 + (SR_BINS + 1) * 4;
+
+static bool small_route_ok(const DevArgs &a) {
+  return a.nnz <= SR_MAX && a.binsA <= SR_BINS && a.binsB <= SR_BINS && a.binsI3 <= SR_BINS &&
+         a.NB + 1 <= SR_OFF;
+}
+
+// Loads here are written unconditionally (clamped addresses, selects afterwards): a
+// load under a per-lane condition becomes a branch with a wait of its own, which
+// serialises the unrolled loops.
+__global__ __launch_bounds__(SR_T) void k_route_small(DevArgs a) {
+  extern __shared__ int4 lds4[];
+  unsigned short *dig = (unsigned short *)lds4;   // [3][SR_MAX] digits by element; the
+                                                  // first two later hold posI3 / posA
+  unsigned short *ord = dig + 3 * SR_MAX;         // [2][SR_MAX] order ping-pong
+  unsigned short *cnt = ord + 2 * SR_MAX;         // [SR_W][SR_BINS] per-wave bin counts
+  int *base = (int *)(cnt + SR_W * SR_BINS);      // [SR_BINS + 1]
+  int *s_off = (int *)cnt;                        // phase 0: offsets [NB + 1]
+  __shared__ int s_scan[SR_W + 1];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int n = a.nnz, NB = a.NB;
+
+  // offsets (clamped copy in LDS) and their validation: a CSR over [0, n]
+  for (int b = tid; b <= NB; b += SR_T) {
+    const int64_t o = a.off[b];
+    const int64_t o1 = a.off[min(b + 1, NB)];
+    s_off[b] = (int)(o < 0 ? 0 : (o > n ? n : o));
+    if ((b == 0 && o != 0) || (b == NB && o != (int64_t)n) || (b < NB && o1 < o))
+      set_status(a.status, TT_DEV_BAD_OFFSETS);
+  }
+  __syncthreads();
+  // elements: split, bag, digits (three parts: register budget)
+  bool bad_slot = false, bad_index = false;
+  for (int h = 0; h < 3; ++h) {
+    constexpr int KH = SR_K / 3;
+    int64_t iv[KH];
+    int sv[KH], lo[KH];
+#pragma unroll
+    for (int k = 0; k < KH; ++k) iv[k] = a.idx[min(tid + (h * KH + k) * SR_T, n - 1)];
+    if (a.has_cache && a.slots) {
+#pragma unroll
+      for (int k = 0; k < KH; ++k) sv[k] = a.slots[min(tid + (h * KH + k) * SR_T, n - 1)];
+    } else {
+#pragma unroll
+      for (int k = 0; k < KH; ++k) sv[k] = -1;
+    }
+    // bag = last b < NB with off[b] <= e: binary lifting, all elements in lockstep
+#pragma unroll
+    for (int k = 0; k < KH; ++k) lo[k] = 0;
+    int top = 1;
+    while (top < NB) top <<= 1;
+    for (int span = top >> 1; span > 0; span >>= 1) {
+      int ov[KH];
+#pragma unroll
+      for (int k = 0; k < KH; ++k) ov[k] = s_off[min(lo[k] + span, NB - 1)];
+#pragma unroll
+      for (int k = 0; k < KH; ++k)
+        lo[k] = (lo[k] + span < NB && ov[k] <= tid + (h * KH + k) * SR_T) ? lo[k] + span : lo[k];
+    }
+    const int dropA = a.binsA - 1, dropB = a.binsB - 1, dropI = a.binsI3 - 1;
+    const int64_t p23 = (int64_t)a.p2 * a.p3;
+#pragma unroll
+    for (int k = 0; k < KH; ++k) {
+      const int e = tid + (h * KH + k) * SR_T;
+      const int b = lo[k], t = a.T == 1 ? 0 : b / a.B;
+      const int slot = sv[k];
+      const int64_t i = iv[k];
+      const bool hit = slot >= 0, slot_ok = hit && slot < a.cache_size;
+      const bool idx_ok = !hit && i >= 0 && i < a.E;
+      const int64_t ic = idx_ok ? i : 0;
+      const int sc = slot_ok ? slot : 0;
+      int i1, i2, i3;
+      split_index(ic, a.p3, p23, a.rp23, a.rp3, i1, i2, i3);
+      int dA = t * a.p1 + i1;
+      int dB = t * a.p2 + i2;
+      int dI = t * a.p3 + i3;
+      if (slot_ok) { dA = a.T * a.p1 + sc % HB; dB = a.T * a.p2 + sc / HB; dI = dropI; }
+      if (!slot_ok && !idx_ok) { dA = dropA; dB = dropB; dI = dropI; }
+      if (e < n) {
+        bad_slot |= hit && !slot_ok;
+        bad_index |= !hit && !idx_ok;
+        a.einfo[e] = make_int4(dA, dB, dI, b);
+        dig[e] = (unsigned short)dI;
+        dig[SR_MAX + e] = (unsigned short)dA;
+        dig[2 * SR_MAX + e] = (unsigned short)dB;
+        ord[e] = (unsigned short)e;
+      }
+    }
+  }
+  if (bad_slot) set_status(a.status, TT_DEV_BAD_SLOT);
+  if (bad_index) set_status(a.status, TT_DEV_BAD_INDEX);
+  __syncthreads();
+
+  // three stable counting passes; wave w ranks the positions [w*per, (w+1)*per) of the
+  // current order, 64 at a time, by ballot matching
+  const int per = (n + SR_W * 64 - 1) / (SR_W * 64) * 64;
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int pass = 0; pass < 3; ++pass) {
+    const unsigned short *in = ord + (pass & 1) * SR_MAX;
+    unsigned short *out = ord + ((pass + 1) & 1) * SR_MAX;
+    const unsigned short *dg = dig + pass * SR_MAX;
+    const int nb = pass == 0 ? a.binsI3 : (pass == 1 ? a.binsA : a.binsB);
+    const int nbits = nbits_for(nb);
+    for (int i = tid; i < SR_W * SR_BINS / 2; i += SR_T) ((unsigned *)cnt)[i] = 0u;
+    // xd[k] = element | (digit + 1) << 14 (digit -1: no position); rk[k] = rank in wave
+    int xd[SR_K], rk[SR_K];
+#pragma unroll
+    for (int k = 0; k < SR_K; ++k) xd[k] = in[min(w * per + k * 64 + lane, n - 1)];
+#pragma unroll
+    for (int k = 0; k < SR_K; ++k) {
+      const int p = w * per + k * 64 + lane;
+      const bool act = k * 64 < per && p < n;
+      const int d = dg[xd[k]];
+      xd[k] |= (act ? d + 1 : 0) << 14;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < SR_K; ++k) {
+      const int dk = (xd[k] >> 14) - 1;
+      const bool act = dk >= 0;
+      unsigned long long m = __ballot(act);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = act && ((dk >> b) & 1);
+        const unsigned long long bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+      }
+      const int before = __popcll(m & lt);
+      const int ci = w * SR_BINS + (act ? dk : 0);
+      const int c0 = cnt[ci];
+      rk[k] = c0 + before;
+      // every lane of the group has read the count before its leader writes it back
+      __builtin_amdgcn_wave_barrier();
+      if (act && before == 0) cnt[ci] = (unsigned short)(c0 + __popcll(m));
+      __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();
+    // per bin: exclusive prefix over the waves, then the bin starts (block scan)
+    int tot = 0;
+    {
+      int cv[SR_W];
+      const int bi = min(tid, SR_BINS - 1);
+#pragma unroll
+      for (int v = 0; v < SR_W; ++v) cv[v] = cnt[v * SR_BINS + bi];
+      if (tid < nb) {
+#pragma unroll
+        for (int v = 0; v < SR_W; ++v) {
+          cnt[v * SR_BINS + bi] = (unsigned short)tot;
+          tot += cv[v];
+        }
+      }
+    }
+    const int incl = wave_incl_scan(tot);
+    if (lane == 63) s_scan[w] = incl;
+    __syncthreads();
+    if (w == 0) {
+      const int v = lane < SR_W ? s_scan[lane] : 0;
+      const int vi = wave_incl_scan(v);
+      if (lane < SR_W) s_scan[lane] = vi - v;
+    }
+    __syncthreads();
+    if (tid < nb) {
+      const int start = s_scan[w] + incl - tot;
+      base[tid] = start;
+      if (pass == 0) a.histI3[(size_t)tid * a.nblk] = start;
+      else if (pass == 1) a.histA[(size_t)tid * a.nblk] = start;
+      else a.grp_off[tid] = start;
+    }
+    if (tid == 0 && pass == 2) base[nb] = n;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < SR_K; ++k) {
+      const int dk = (xd[k] >> 14) - 1, d = dk >= 0 ? dk : 0;
+      rk[k] += base[d] + cnt[w * SR_BINS + d];
+    }
+#pragma unroll
+    for (int k = 0; k < SR_K; ++k) {
+      if ((xd[k] >> 14) > 0) {
+        const int x = xd[k] & 0x3fff;
+        out[rk[k]] = (unsigned short)x;
+        if (pass < 2) dig[pass * SR_MAX + x] = (unsigned short)rk[k];  // posI3 / posA
+      }
+    }
+    __syncthreads();
+  }
+
+  // final order (ord[1]) -> the per-position arrays (two halves: register budget)
+  for (int h = 0; h < 2; ++h) {
+    constexpr int KH = SR_K / 2;
+    const unsigned short *fin = ord + SR_MAX;
+    int ek[KH], pI[KH], pA[KH];
+    int4 info[KH];
+    float wv[KH];
+#pragma unroll
+    for (int k = 0; k < KH; ++k) ek[k] = fin[min(tid + (h * KH + k) * SR_T, n - 1)];
+#pragma unroll
+    for (int k = 0; k < KH; ++k) {
+      info[k] = a.einfo[ek[k]];
+      pI[k] = dig[ek[k]];
+      pA[k] = dig[SR_MAX + ek[k]];
+    }
+    if (a.psw) {
+#pragma unroll
+      for (int k = 0; k < KH; ++k) wv[k] = a.psw[ek[k]];
+    } else {
+#pragma unroll
+      for (int k = 0; k < KH; ++k) wv[k] = 1.f;
+    }
+#pragma unroll
+    for (int k = 0; k < KH; ++k) {
+      const int s = tid + (h * KH + k) * SR_T;
+      if (s < n) {
+        a.s_n[s] = ek[k];
+        a.s_dA[s] = info[k].x;
+        a.s_dB[s] = info[k].y;
+        a.s_dI3[s] = info[k].z;
+        a.s_bag[s] = info[k].w;
+        a.s_w[s] = wv[k];
+        a.s_posI3[s] = pI[k];
+        a.s_posA[s] = pA[k];
+      }
+    }
+  }
+  // work items from the group starts in LDS (base[0..binsB], base[binsB] = n): a
+  // group of m elements gives ceil(m / P) items of near-equal size
+  {
+    const int G = a.T * a.p2;  // G < binsB <= SR_T
+    const int gb = base[min(tid, G)], ge = base[min(tid + 1, a.binsB)];
+    const int m = tid < G ? ge - gb : 0;
+    const int nc = (m + a.P - 1) / a.P;
+    const int incl = wave_incl_scan(nc);
+    if (lane == 63) s_scan[w] = incl;
+    __syncthreads();
+    if (w == 0) {
+      const int v = lane < SR_W ? s_scan[lane] : 0;
+      const int vi = wave_incl_scan(v);
+      if (lane < SR_W) s_scan[lane] = vi - v;
+      if (lane == SR_W - 1) s_scan[SR_W] = vi;
+    }
+    __syncthreads();
+    const int first = s_scan[w] + incl - nc;
+    if (tid <= G) a.chunk_pre[tid] = first;
+    for (int c = 0; c < nc; ++c)
+      a.fitem[first + c] = make_int4(tid, gb + (int)((int64_t)m * c / nc),
+                                     gb + (int)((int64_t)m * (c + 1) / nc), 0);
+    if (tid == 0) {
+      a.grp_off[a.binsB] = n;
+      a.hdr[H_NFWD] = s_scan[SR_W];
+      a.hdr[H_HIT_BEG] = base[G];
+      a.hdr[H_HIT_END] = base[a.binsB - 1];
+      a.hdr[H_VALID] = base[a.binsB - 1];
+      a.hdr[H_PLAN] = (int)a.plan_fp;
+    }
+  }
+}
+
 hipError_t launch_route(const DevArgs &a, hipStream_t s) {
   if (a.nblk == 0) return hipGetLastError();
+  if (small_route_ok(a)) {
+    static bool attr_set = false;  // dynamic LDS above 64 KiB is opt-in per kernel
+    if (!attr_set) {
+      (void)hipFuncSetAttribute((const void *)k_route_small,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)SR_LDS);
+      attr_set = true;
+    }
+    prof_begin(K_ROUTE_SMALL, s);
+    hipLaunchKernelGGL(k_route_small, dim3(1), dim3(SR_T), SR_LDS, s, a);
+    prof_end(K_ROUTE_SMALL, s);
+    return hipGetLastError();
+  }
   prof_begin(K_ROUTE_FIRST, s);
   hipLaunchKernelGGL(k_route_first, dim3(a.nblk), dim3(RT),
                      (size_t)(a.binsI3 + ROUTE_MAX_BAGS) * 4, s, a);

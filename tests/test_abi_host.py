@@ -96,3 +96,43 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(abi, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError):
         abi.lib()
+
+
+def test_multiply_high_division_is_exact_on_its_range():
+    """The kernels divide small indices (k < 2^16) by runtime extents (q3, D) with one
+    high multiply by ceil(2^32 / d); check floor(k * m / 2^32) == k // d exhaustively
+    in k for every divisor the shape envelope allows (d <= 1024)."""
+    import numpy as np
+    k = np.arange(1 << 16, dtype=np.uint64)
+    for d in range(2, 1025):
+        m = np.uint64(((1 << 32) + d - 1) // d)
+        assert np.array_equal((k * m) >> np.uint64(32), k // np.uint64(d)), d
+
+
+def test_row_split_through_double_reciprocals():
+    """The routing kernels split a row index with double reciprocals and one correction
+    step; emulate that arithmetic (IEEE double, as on the GPU) on edge rows -- multiples
+    of p3 and p2*p3, their neighbours, the last row -- and random rows for a range of
+    shapes up to p_k = 8191 and E < 2^40."""
+    import numpy as np
+    rng = np.random.Generator(np.random.PCG64(11))
+    shapes = [(200, 220, 250), (8191, 8191, 8191), (1, 1, 1), (3, 8191, 1), (8191, 1, 7),
+              (97, 89, 83)] + [tuple(int(x) for x in rng.integers(1, 8192, 3)) for _ in range(40)]
+    for p1, p2, p3 in shapes:
+        p23 = p2 * p3
+        E = p1 * p23
+        rows = [0, E - 1] + [k * p23 + d for k in rng.integers(0, p1, 50) for d in (-1, 0, 1)]
+        rows += [k * p3 + d for k in rng.integers(0, p1 * p2, 50) for d in (-1, 0, 1)]
+        rows += list(rng.integers(0, E, 500))
+        i = np.array([r for r in rows if 0 <= r < E], dtype=np.int64)
+        rp23, rp3 = np.float64(1.0) / np.float64(p23), np.float64(1.0) / np.float64(p3)
+        q1 = (i.astype(np.float64) * rp23).astype(np.int64)  # truncation toward zero
+        r = i - q1 * p23
+        q1 = np.where(r >= p23, q1 + 1, np.where(r < 0, q1 - 1, q1))
+        r = np.where(r >= p23, r - p23, np.where(r < 0, r + p23, r))
+        q2 = (r.astype(np.float64) * rp3).astype(np.int64)
+        r3 = r - q2 * p3
+        q2 = np.where(r3 >= p3, q2 + 1, np.where(r3 < 0, q2 - 1, q2))
+        r3 = np.where(r3 >= p3, r3 - p3, np.where(r3 < 0, r3 + p3, r3))
+        assert np.array_equal(q1, i // p23) and np.array_equal(q2, (i % p23) // p3)
+        assert np.array_equal(r3, i % p3)

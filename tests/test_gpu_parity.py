@@ -161,9 +161,13 @@ def test_route_order_bit_exact():
         assert np.array_equal(np.diff(g[:wl.num_tables * wl.p[1] + 1]), counts)
 
 
-def test_route_with_cache_slots_bit_exact():
+@pytest.mark.parametrize("bags", [None, 4000], ids=["one-block", "multi-block"])
+def test_route_with_cache_slots_bit_exact(bags):
+    """Cache slots, skipped invalid indices; small batches are grouped by one
+    workgroup, larger ones by the multi-block passes: both must give the same order."""
     wl = SMALL[1]
-    b = W.make_batch(wl, 3)
+    _say("case route+cache", bags)
+    b = W.make_batch(wl, 3, bags_per_table=bags)
     rng = np.random.Generator(np.random.PCG64(5))
     n = len(b["indices"])
     slots = np.where(rng.random(n) < 0.4, rng.integers(0, 700, n), -1).astype(np.int32)
@@ -235,10 +239,13 @@ def test_empty_batch_and_empty_bags():
         assert np.array_equal(new[0][k], cores[0][k])
 
 
-def test_cache_path_matches_oracle():
+@pytest.mark.parametrize("bags", [256, 1024])
+def test_cache_path_matches_oracle(bags):
     """Warm-up lookups count frequencies; populate picks the top-K (bit-exact against
-    the oracle); then forward/backward with hits read and update cache rows."""
-    wl = W.custom("cache", p=(20, 22, 25), q=(4, 4, 4), ranks=(32, 32), bags_per_table=256,
+    the oracle); then forward/backward with hits read and update cache rows (256 bags:
+    one-block grouping; 1024 bags: multi-block grouping)."""
+    _say("case cache path", bags)
+    wl = W.custom("cache", p=(20, 22, 25), q=(4, 4, 4), ranks=(32, 32), bags_per_table=bags,
                   lengths=("fixed", 20), dist=("zipf", 1.2), init_std=1 / 32 ** 0.5, lr=0.01,
                   weighted=True)
     K = 900
@@ -260,24 +267,25 @@ def test_cache_path_matches_oracle():
     ref_rows = oracle.populate_rows(wl.p, wl.q, wl.ranks, cores[0], sel)
     assert rel_err(rows.cpu().numpy()[:nf], ref_rows) <= TOL
     b = W.make_batch(wl, 0)
+    B = b["num_bags"]
     d = to_dev(b)
     slots = cache.lookup(d["indices"], count_freq=False)
     ref_slots = oracle.lookup_slots(sel, b["indices"])
     assert np.array_equal(slots.cpu().numpy(), ref_slots)
     assert (ref_slots >= 0).any() and (ref_slots < 0).any()
     rows_old = rows.cpu().numpy().copy()
-    ws = abi.workspace(desc, d["indices"].numel(), 256, K)
-    Y = abi.tt_bag_forward(desc, g, d["indices"], d["offsets"], 256, d["per_sample_weights"],
+    ws = abi.workspace(desc, d["indices"].numel(), B, K)
+    Y = abi.tt_bag_forward(desc, g, d["indices"], d["offsets"], B, d["per_sample_weights"],
                            cache=(slots, rows), ws=ws).cpu().numpy()
-    Yo = oracle.forward(wl.p, wl.q, wl.ranks, wl.E, cores, b["indices"], b["offsets"], 256,
+    Yo = oracle.forward(wl.p, wl.q, wl.ranks, wl.E, cores, b["indices"], b["offsets"], B,
                         per_sample_weights=b["per_sample_weights"], slots=ref_slots,
                         cache_rows=rows_old)
     assert rel_err(Y, Yo) <= TOL
-    abi.tt_bag_backward_sgd(desc, g, d["indices"], d["offsets"], 256, d["grad_out"], wl.lr,
+    abi.tt_bag_backward_sgd(desc, g, d["indices"], d["offsets"], B, d["grad_out"], wl.lr,
                             d["per_sample_weights"], cache=(slots, rows), ws=ws)
     torch.cuda.synchronize()
     grads, touched, gc, tc = oracle.backward(wl.p, wl.q, wl.ranks, wl.E, cores, b["indices"],
-                                             b["offsets"], 256, b["grad_out"],
+                                             b["offsets"], B, b["grad_out"],
                                              per_sample_weights=b["per_sample_weights"],
                                              slots=ref_slots, cache_size=K)
     _check_update(wl, cores, host_cores(wl, g), grads, touched, wl.lr)
