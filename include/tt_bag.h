@@ -66,6 +66,8 @@ extern "C" {
 #define TT_DEV_BAD_SLOT    4  /* cache slot >= cache_size (element skipped)       */
 #define TT_DEV_HASH_FULL   8  /* frequency table full: new keys were not counted  */
 #define TT_DEV_STALE_PLAN 16  /* a planned call found another call's plan in ws  */
+#define TT_DEV_SYNC_TIMEOUT 32 /* grouping: a grid-wide barrier of the cooperative
+                                  launch was not reached in time (no plan made)  */
 
 /* Shape of one TT table ("Parameters": num_embeddings, embedding_dim = prod(q),
  * tt_p_shapes, tt_q_shapes, tt_ranks) and the number of tables batched
@@ -162,7 +164,7 @@ int tt_bag_backward_sgd_planned(const tt_desc *desc, float *const cores[3],
 /*
  * The grouping step of both passes, exposed for inspection and tests: splits
  * every index, finds its bag, and sorts the elements stably so that misses come
- * first ordered by (table, i2, i1, i3) and then by position, followed by cache hits
+ * first ordered by (table, i2, i1) and then by position, followed by cache hits
  * ordered by (slot, position), followed by the skipped elements by position.
  *   order_out     [nnz] int32: element positions in that order
  *   group_off_out [T*p2 + 2] int32: misses of group g = table*p2 + i2 occupy

@@ -201,7 +201,7 @@ def bag_ids(offsets, nnz):
 def route_order(p, E, num_tables, num_bags, indices, offsets, slots=None):
     """The grouping order of the elements, as a plain stable sort.
 
-    Misses (no cache slot) first, ordered by (table, i2, i1, i3) and, for equal
+    Misses (no cache slot) first, ordered by (table, i2, i1) and, for equal
     keys, by position n; then cache hits ordered by (slot, n).  Elements with an index
     outside [0, E) are left out.  Returns (order, group_counts) where
     group_counts[t*p2 + i2] counts the misses of each (table, i2) group."""
@@ -216,7 +216,7 @@ def route_order(p, E, num_tables, num_bags, indices, offsets, slots=None):
         if hit:
             keys_hit.append((int(slots[n]), n))
         elif 0 <= idx[n] < E:
-            keys_miss.append((int(t[n]), int(i2[n]), int(i1[n]), int(i3[n]), n))
+            keys_miss.append((int(t[n]), int(i2[n]), int(i1[n]), n))
     keys_miss.sort()
     keys_hit.sort()
     order = [k[-1] for k in keys_miss] + [k[-1] for k in keys_hit]

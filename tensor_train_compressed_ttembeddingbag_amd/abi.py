@@ -23,6 +23,7 @@ TT_DEV_BAD_OFFSETS = 2
 TT_DEV_BAD_SLOT = 4
 TT_DEV_HASH_FULL = 8
 TT_DEV_STALE_PLAN = 16
+TT_DEV_SYNC_TIMEOUT = 32
 
 
 class TTError(RuntimeError):

@@ -37,8 +37,8 @@ struct Plan {
   size_t lds_fwd = 0, lds_bwd = 0;
   size_t ws_total = 0;
   // byte offsets inside the workspace
-  size_t o_ctr, o_hdr, o_einfo, o_histA, o_histB, o_histI3, o_orderI3, o_orderA, o_sn, o_sdA,
-      o_sdB, o_sdI3, o_sbag, o_sw, o_posI3, o_posA, o_sposI3, o_sposA, o_fitem, o_grp, o_chunk,
+  size_t o_ctr, o_hdr, o_einfo, o_histA, o_histB, o_histI3, o_orderA, o_segI3, o_segA, o_sn,
+      o_sdA, o_sdB, o_sdI3, o_sbag, o_sw, o_posI3, o_sposI3, o_sposA, o_fitem, o_grp, o_chunk,
       o_l1, o_l3, o_p1, o_p3, o_frag, o_p2;
 };
 
@@ -125,8 +125,9 @@ int make_plan(const tt_desc *d, int64_t nnz, int64_t num_bags, int64_t cache_siz
   P->o_histA = carve(cur, (size_t)binsA * nb * 4);
   P->o_histB = carve(cur, (size_t)binsB * nb * 4);
   P->o_histI3 = carve(cur, (size_t)binsI3 * nb * 4);
-  P->o_orderI3 = carve(cur, n * 4);
   P->o_orderA = carve(cur, n * 4);
+  P->o_segI3 = carve(cur, ((size_t)binsI3 + 1) * 4);
+  P->o_segA = carve(cur, ((size_t)binsA + 1) * 4);
   P->o_sn = carve(cur, n * 4);
   P->o_sdA = carve(cur, n * 4);
   P->o_sdB = carve(cur, n * 4);
@@ -134,7 +135,6 @@ int make_plan(const tt_desc *d, int64_t nnz, int64_t num_bags, int64_t cache_siz
   P->o_sbag = carve(cur, n * 4);
   P->o_sw = carve(cur, n * 4);
   P->o_posI3 = carve(cur, n * 4);
-  P->o_posA = carve(cur, n * 4);
   P->o_sposI3 = carve(cur, n * 4);
   P->o_sposA = carve(cur, n * 4);
   P->o_fitem = carve(cur, (size_t)items_max(a) * sizeof(int4));
@@ -159,8 +159,9 @@ void bind_ws(Plan *P, void *ws) {
   a.histA = (int *)(b + P->o_histA);
   a.histB = (int *)(b + P->o_histB);
   a.histI3 = (int *)(b + P->o_histI3);
-  a.orderI3 = (int *)(b + P->o_orderI3);
   a.orderA = (int *)(b + P->o_orderA);
+  a.segI3 = (int *)(b + P->o_segI3);
+  a.segA = (int *)(b + P->o_segA);
   a.s_n = (int *)(b + P->o_sn);
   a.s_dA = (int *)(b + P->o_sdA);
   a.s_dB = (int *)(b + P->o_sdB);
@@ -168,7 +169,6 @@ void bind_ws(Plan *P, void *ws) {
   a.s_bag = (int *)(b + P->o_sbag);
   a.s_w = (float *)(b + P->o_sw);
   a.posI3_of = (int *)(b + P->o_posI3);
-  a.posA_of = (int *)(b + P->o_posA);
   a.s_posI3 = (int *)(b + P->o_sposI3);
   a.s_posA = (int *)(b + P->o_sposA);
   a.fitem = (int4 *)(b + P->o_fitem);

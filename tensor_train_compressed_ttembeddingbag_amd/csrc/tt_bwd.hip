@@ -26,7 +26,7 @@
 // links record where they are.  k_seg then sums every partial per slice in a fixed
 // order and applies SGD: dG1 / dG3 in the (t,i1)- / (t,i3)-order, dG2 in
 // work-item order.
-#include "tt_internal.h"
+#include "tt_device.h"
 #include "tt_mfma.h"
 
 namespace ttb {
@@ -35,7 +35,7 @@ namespace ttb {
 template <int RP>
 struct BwdLds {
   static constexpr int LD = RP + 4;
-  static constexpr int INTS = 64 * 5 + 65 * 2 + 64 + 64 + 16 + 8;
+  static constexpr int INTS = 64 * 7 + 65 * 2 + 64 + 64 + 16 + 8;
   // the dG2 reduction slots alias the dT transpose tiles and the w * dY staging
   __host__ __device__ static size_t red_floats(int nred, int P, int D) {
     size_t r = (size_t)nred * RP * LD;
@@ -79,12 +79,14 @@ void k_bwd(DevArgs a) {
   float *e_w = (float *)(e_bag + 64);                             // [64]
   int *it_i3 = (int *)(e_w + 64);                                 // [64]
   int *it_pair = it_i3 + 64;                                      // [64]
-  int *it_beg = it_pair + 64;                                     // [65] (offsets in the item)
+  int *it_beg = it_pair + 64;                                     // [65] item-major slots
   int *pr_it = it_beg + 65;                                       // [65]
   int *pr_i1 = pr_it + 65;                                        // [64]
   int *gcnt = pr_i1 + 64;                                         // [64] items per lane group
   int *mb_nk = gcnt + 64;                                         // [16]
   int *s_cnt = mb_nk + 16;                                        // [8]
+  int *e_perm = s_cnt + 8;                                        // [64] item-major elements
+  int *it_first = e_perm + 64;                                    // [64] leader offsets
 
   // round 1: plan check and work item
   const int wi = blockIdx.x;
@@ -141,38 +143,32 @@ void k_bwd(DevArgs a) {
     const int dAv = a.s_dA[s], dIv = a.s_dI3[s], bagv = a.s_bag[s];
     const int lA = a.s_posA[s], lI = a.s_posI3[s];
     const float wv = a.s_w[s];
-    const int dA = v ? dAv : -1, i3 = v ? dIv - t * a.p3 : -1;
+    const int dA = v ? dAv : -1, i3 = v ? dIv - t * a.p3 : 0;
     e_bag[tid] = bagv;
     e_w[tid] = wv;
-    const int pdA = __shfl_up(dA, 1), pi3 = __shfl_up(i3, 1);
-    const bool item_st = v && (tid == 0 || dA != pdA || i3 != pi3);
-    const bool pair_st = v && (tid == 0 || dA != pdA);
-    const unsigned long long mi = __ballot(item_st), mp = __ballot(pair_st);
-    const unsigned long long lt = (tid == 0) ? 0ull : (~0ull >> (64 - tid));
-    const int it = __popcll(mi & lt), pr = __popcll(mp & lt);
+    const WaveItems r = wave_items(v, dA, i3, nbits_for(a.p3));
     gcnt[tid] = 0;
     // a partial lives at the first position of its item (dG3) / pair (dG1)
     if (v) {
-      a.link1[lA] = pair_st ? s : -1;
-      a.link3[lI] = item_st ? s : -1;
+      a.link1[lA] = r.pair_st ? s : -1;
+      a.link3[lI] = r.item_st ? s : -1;
+      e_perm[r.item_pos] = tid;
     }
     wave_lds_sync();
-    if (item_st) {
-      it_beg[it] = tid;
-      it_i3[it] = i3;
-      it_pair[it] = pair_st ? pr : pr - 1;
+    if (r.item_st) {
+      it_beg[r.it] = r.it_beg;
+      it_first[r.it] = tid;
+      it_i3[r.it] = i3;
+      it_pair[r.it] = r.pair_of;
     }
-    if (pair_st) {
-      const unsigned long long above = tid == 63 ? 0ull : (mp >> (tid + 1));
-      const int nxt = above ? tid + __ffsll((long long)above) : n_el;
-      const unsigned long long span = (nxt >= 64 ? ~0ull : ((1ull << nxt) - 1)) & ~lt;
-      pr_it[pr] = it;
-      pr_i1[pr] = dA - t * a.p1;
+    if (r.pair_st) {
+      pr_it[r.pr] = r.it;
+      pr_i1[r.pr] = dA - t * a.p1;
       // the pair's rows pr*q1 .. +q1-1 lie in lane group (pr*q1)/4 of an M-block
-      atomicAdd(&gcnt[(pr * q1) >> 2], __popcll(mi & span));
+      atomicAdd(&gcnt[(r.pr * q1) >> 2], r.pair_items);
     }
     if (tid == 0) {
-      const int nI = __popcll(mi), nP = __popcll(mp);
+      const int nI = __popcll(r.mi), nP = __popcll(r.mp);
       it_beg[nI] = n_el;
       pr_it[nP] = nI;
       s_cnt[0] = nI;
@@ -282,7 +278,7 @@ void k_bwd(DevArgs a) {
   for (int i = tid; i < nI * D; i += WG) {
     const int it = fdiv(i, a.mD), d = i - it * D;
     float acc = 0.f;
-    for (int e = it_beg[it]; e < it_beg[it + 1]; ++e) acc += sYe[(size_t)e * D + d];
+    for (int k = it_beg[it]; k < it_beg[it + 1]; ++k) acc += sYe[(size_t)e_perm[k] * D + d];
     sGu[i] = acc;
   }
   __syncthreads();
@@ -435,7 +431,7 @@ void k_bwd(DevArgs a) {
     const int row = mb * 16 + c;
     const int pr = row >> a.lq1, j1 = row & (q1 - 1);
     if (pr < nP) {
-      float *dst = a.part1 + (size_t)(s0 + it_beg[pr_it[pr]]) * W1 + (size_t)j1 * R1;
+      float *dst = a.part1 + (size_t)(s0 + it_first[pr_it[pr]]) * W1 + (size_t)j1 * R1;
 #pragma unroll
       for (int mr = 0; mr < NM; ++mr)
 #pragma unroll
@@ -447,7 +443,7 @@ void k_bwd(DevArgs a) {
   }
   for (int i = tid; i < total3; i += WG) {  // i = (item * q3 + j3) * RP + r2
     const int jr = i >> LRP, it = fdiv(jr, a.mq3), j3 = jr - it * q3, r2 = i & (RP - 1);
-    if (r2 < R2) a.part3[(size_t)(s0 + it_beg[it]) * W3 + r2 * q3 + j3] = sdA3[i];
+    if (r2 < R2) a.part3[(size_t)(s0 + it_first[it]) * W3 + r2 * q3 + j3] = sdA3[i];
   }
 }
 
@@ -498,12 +494,12 @@ __global__ __launch_bounds__(256) void k_seg(DevArgs a) {
     if (task >= nA + nC) return;
     const bool one = task < nA;
     const int seg = one ? task : task - nA;
-    const int *hist = one ? a.histA : a.histI3;
+    const int *seg_start = one ? a.segA : a.segI3;
     const int *link = one ? a.link1 : a.link3;
     const float *part = one ? a.part1 : a.part3;
     const int W = one ? a.q1 * a.R1 : a.R2 * a.q3;
     float *dst = one ? a.G1 + (size_t)seg * W : a.G3 + (size_t)seg * W;
-    const int beg = hist[(size_t)seg * a.nblk], end = hist[(size_t)(seg + 1) * a.nblk];
+    const int beg = seg_start[seg], end = seg_start[seg + 1];
     if (beg >= end) return;
     for (int col0 = 0; col0 < W; col0 += 256) {  // W <= 1024 (R2 * q3)
       float acc[4] = {0.f, 0.f, 0.f, 0.f};

@@ -72,6 +72,55 @@ static __device__ void block_exclusive_scan(int *arr, int len, int *s_tmp) {
   __syncthreads();
 }
 
+// Items and pairs of one work item, worked out by one wave (lane = element offset in
+// the work item, v = a real element).  Pairs are the runs of equal dA (the grouping
+// order sorts by (t,i2,i1)); items are the distinct i3 inside a pair, numbered in the
+// order of their first element (the "leader").  item_pos is the lane's slot in the
+// item-major element list (items in order, an item's elements in position order).
+struct WaveItems {
+  unsigned long long mi, mp;  // leaders, pair starts
+  bool item_st, pair_st;
+  int e_it;        // item of this lane
+  int it, pr;      // item index (leaders), pair index (pair starts)
+  int pair_of;     // pair of this lane
+  int it_beg;      // leaders: first slot of the item in the item-major list
+  int item_pos;    // this lane's slot in the item-major list
+  int pair_items;  // pair starts: number of items of the pair
+};
+
+static __device__ WaveItems wave_items(bool v, int dA, int i3, int nbits3) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long self = 1ull << lane;
+  const unsigned long long lt = self - 1ull;
+  WaveItems r;
+  const int pdA = __shfl_up(dA, 1);
+  r.pair_st = v && (lane == 0 || dA != pdA);
+  r.mp = __ballot(r.pair_st);
+  const unsigned long long vm = __ballot(v);
+  const unsigned long long upto = r.mp & (lt | self), above = r.mp & ~(lt | self);
+  const int ps = upto ? 63 - __clzll(upto) : 0;
+  const int pe = above ? __ffsll((long long)above) - 1 : 64;
+  const unsigned long long pmask = (pe >= 64 ? ~0ull : ((1ull << pe) - 1ull)) & ~((1ull << ps) - 1ull);
+  unsigned long long m = vm & pmask;  // lanes of the same pair with the same i3
+  for (int b = 0; b < nbits3; ++b) {
+    const bool bit = (i3 >> b) & 1;
+    const unsigned long long bb = __ballot(v && bit);
+    m &= bit ? bb : ~bb;
+  }
+  const int lead = (v && m) ? __ffsll((long long)m) - 1 : lane;
+  r.item_st = v && lead == lane;
+  r.mi = __ballot(r.item_st);
+  r.e_it = __popcll(r.mi & ((1ull << lead) - 1ull));
+  r.it = __popcll(r.mi & lt);
+  r.pr = __popcll(r.mp & lt);
+  r.pair_of = __popcll(upto) - 1;
+  const int sz = r.item_st ? __popcll(m) : 0;
+  r.it_beg = wave_incl_scan(sz) - sz;
+  r.item_pos = __shfl(r.it_beg, lead) + __popcll(m & lt);
+  r.pair_items = __popcll(r.mi & pmask);
+  return r;
+}
+
 static __device__ void block_rank4(const int d[4], int rank[4], unsigned short *cnt, int nbins,
                             int nbits, int *hist_out, int nblk) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;

@@ -23,7 +23,7 @@
 // and leaves the item's rows W in LDS; a last pass adds w * W[item] into each
 // element's bag with row-contiguous fp32 atomics.  Bits of out may depend on the
 // order of the atomics.
-#include "tt_internal.h"
+#include "tt_device.h"
 #include "tt_mfma.h"
 
 namespace ttb {
@@ -32,7 +32,7 @@ namespace ttb {
 template <int RP>
 struct FwdLds {
   static constexpr int LD = RP + 4;  // row pitch of G2^T [r2][r1]: conflict-free 16-byte reads
-  static constexpr int INTS = 64 * 4 + 65 * 2 + 64 + 16 + 8;
+  static constexpr int INTS = 64 * 5 + 65 * 2 + 64 + 16 + 8;
   __host__ __device__ static size_t g2_floats(int JB) { return (size_t)JB * RP * LD; }
   __host__ __device__ static size_t g3_floats(int P, int q3) { return (size_t)P * q3 * RP; }
   __host__ __device__ static size_t w_floats(int P, int D, int sw) { return sw ? (size_t)P * D : 0; }
@@ -62,6 +62,7 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
   int *pr_i1 = pr_it + 65;                                      // [64]
   int *mb_nk = pr_i1 + 64;                                      // [16]
   int *s_cnt = mb_nk + 16;                                      // [8]
+  int *e_perm = s_cnt + 8;                                      // [64] item-major elements
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int wi = blockIdx.x;
@@ -117,30 +118,22 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
     const bool v = tid < n_el;
     const int dAv = a.s_dA[s], dIv = a.s_dI3[s], bagv = a.s_bag[s];
     const float wv = a.s_w[s];
-    const int dA = v ? dAv : -1, i3 = v ? dIv - t * a.p3 : -1;
+    const int dA = v ? dAv : -1, i3 = v ? dIv - t * a.p3 : 0;
     e_bag[tid] = bagv;
     e_w[tid] = wv;
-    const int pdA = __shfl_up(dA, 1), pi3 = __shfl_up(i3, 1);
-    const bool item_st = v && (tid == 0 || dA != pdA || i3 != pi3);
-    const bool pair_st = v && (tid == 0 || dA != pdA);
-    const unsigned long long mi = __ballot(item_st), mp = __ballot(pair_st);
-    const unsigned long long lt = (tid == 0) ? 0ull : (~0ull >> (64 - tid));
-    const int it = __popcll(mi & lt), pr = __popcll(mp & lt);
-    e_it[tid] = __popcll(mi & (lt | (1ull << tid))) - 1;
+    const WaveItems r = wave_items(v, dA, i3, nbits_for(a.p3));
+    e_it[tid] = r.e_it;
+    if (v) e_perm[r.item_pos] = tid;
     if (tid < 16) mb_nk[tid] = 0;
     wave_lds_sync();
-    if (item_st) { it_beg[it] = tid; it_i3[it] = i3; }
-    if (pair_st) {
-      // items of this pair: item starts in [tid, next pair start)
-      const unsigned long long above = tid == 63 ? 0ull : (mp >> (tid + 1));
-      const int nxt = above ? tid + __ffsll((long long)above) : n_el;
-      const unsigned long long span = (nxt >= 64 ? ~0ull : ((1ull << nxt) - 1)) & ~lt;
-      pr_it[pr] = it;
-      pr_i1[pr] = dA - t * a.p1;
-      atomicMax(&mb_nk[(pr * q1) >> 4], __popcll(mi & span));
+    if (r.item_st) { it_beg[r.it] = r.it_beg; it_i3[r.it] = i3; }
+    if (r.pair_st) {
+      pr_it[r.pr] = r.it;
+      pr_i1[r.pr] = dA - t * a.p1;
+      atomicMax(&mb_nk[(r.pr * q1) >> 4], r.pair_items);
     }
     if (tid == 0) {
-      const int nI = __popcll(mi), nP = __popcll(mp);
+      const int nI = __popcll(r.mi), nP = __popcll(r.mp);
       it_beg[nI] = n_el;
       pr_it[nP] = nI;
       s_cnt[0] = nI;
@@ -262,8 +255,10 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
               if (SW) {
                 sW[(size_t)it * D + col0 + j3] = val;
               } else {
-                for (int e = it_beg[it]; e < it_beg[it + 1]; ++e)
+                for (int k = it_beg[it]; k < it_beg[it + 1]; ++k) {
+                  const int e = e_perm[k];
                   unsafeAtomicAdd(a.Y + (size_t)e_bag[e] * D + col0 + j3, e_w[e] * val);
+                }
               }
             }
           }

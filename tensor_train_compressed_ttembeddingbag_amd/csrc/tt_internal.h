@@ -1,16 +1,12 @@
 // tt_internal.h -- shared declarations of the libttbag HIP sources (not installed).
 //
 // Pipeline of one call (all kernels on the caller's stream):
-//   route:  k_route_first   split indices, find bags, validate, histogram of the
-//                           (table,i3) digit; forward mode also initialises out
-//                           (zeros, or the pooled cache hits); last block scans.
-//           k_route_pass x2 stable scatter by (table,i3) then by (table,i1), each
-//                           histogramming the next digit over destination blocks;
-//                           last block scans (and, after the second, builds the
-//                           group table).
-//           k_route_final   stable scatter by (table,i2) -> final order
-//                           (table, i2, i1, i3, position); hits after misses by
-//                           (slot, position); skipped elements last.
+//   route:  k_route_coop    (or k_route_a, _b, _c) split indices, find bags, validate;
+//                           stable orders by (table,i3) and (table,i1); final order
+//                           (table, i2, i1, position), hits after misses by
+//                           (slot, position), skipped elements last; group table and
+//                           work items.
+//   yinit:  k_yinit         out = zeros, or the pooled cache hits.
 //   forward: k_fwd          one workgroup per work item (piece of an i2 group).
 //   backward: k_runsum      cache hits: w * dY summed over runs of one slot.
 //             k_bwd         one workgroup per work item.
@@ -80,10 +76,11 @@ struct DevArgs {
   int *hdr;
   int4 *einfo;      // per element: dA (t,i1), dB (t,i2), dI3 (t,i3), bag
   int *histA, *histB, *histI3;
-  int *orderI3, *orderA;
+  int *orderA;      // elements by (t,i1) (stable)
+  int *segI3, *segA;  // first position of each (t,i3) / (t,i1) bin in orderI3 / orderA
   int *s_n, *s_dA, *s_dB, *s_dI3, *s_bag;
   float *s_w;       // per-sample weight in the final order (1 without weights)
-  int *posI3_of, *posA_of;   // element -> position in orderI3 / orderA
+  int *posI3_of;    // element -> position in orderI3 (elements by (t,i3), stable)
   int *s_posI3, *s_posA;     // final position -> position in orderI3 / orderA
   int4 *fitem;      // work items: (group, first position, end position, 0)
   int *grp_off;     // [binsB + 1]
@@ -113,10 +110,11 @@ __device__ __forceinline__ void set_status(int32_t *st, int bit) {
 // device status bit for a planned call whose workspace holds another plan
 constexpr int DEV_STALE_PLAN = 16;
 
+
 // kernels named by the optional per-kernel timer (tt_prof.hip)
 enum KernelId {
-  K_ROUTE_FIRST, K_ROUTE_PASS1, K_ROUTE_PASS2, K_ROUTE_FINAL, K_FWD, K_RUNSUM, K_BWD, K_SEG,
-  K_CACHE_LOOKUP, K_YINIT, K_ROUTE_SMALL, K_COUNT
+  K_ROUTE_COOP, K_ROUTE_A, K_ROUTE_B, K_ROUTE_C, K_FWD, K_RUNSUM, K_BWD, K_SEG,
+  K_CACHE_LOOKUP, K_YINIT, K_COUNT
 };
 void prof_begin(int id, hipStream_t s);
 void prof_end(int id, hipStream_t s);

@@ -22,9 +22,9 @@ double g_ms[K_COUNT] = {0};
 long long g_n[K_COUNT] = {0};
 hipEvent_t g_open[K_COUNT] = {nullptr};
 
-const char *g_names[K_COUNT] = {"k_route_first", "k_route_pass1", "k_route_pass2",
-                                "k_route_final", "k_fwd", "k_runsum", "k_bwd", "k_seg",
-                                "k_cache_lookup", "k_yinit", "k_route_small"};
+const char *g_names[K_COUNT] = {"k_route_coop", "k_route_a", "k_route_b", "k_route_c",
+                                "k_fwd", "k_runsum", "k_bwd", "k_seg", "k_cache_lookup",
+                                "k_yinit"};
 
 hipEvent_t take() {
   if (!g_pool.empty()) {

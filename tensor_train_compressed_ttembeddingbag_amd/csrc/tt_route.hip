@@ -41,130 +41,424 @@ static __device__ int half_find_bag(const int64_t *off, int NB, int n, int half,
 
 constexpr int ROUTE_MAX_BAGS = 2048;  // offsets of one routing block kept in LDS
 
-// Work items from the group table grp_off[0..binsB] (starts of the (table, i2) bins
-// in the final order): a miss group of n elements becomes ceil(n / P) items of
-// near-equal size (at most P positions each), numbered group by group.  Also the
-// header words of the grouping.  Run by one whole block.
-static __device__ void build_items(const DevArgs &a, int *s_scan) {
-  const int G = a.T * a.p2, tid = threadIdx.x, nt = blockDim.x;
-  for (int g = tid; g <= G; g += nt) {
-    const int gb = a.grp_off[g], ge = g < G ? a.grp_off[g + 1] : gb;
-    a.chunk_pre[g] = (ge - gb + a.P - 1) / a.P;
-  }
-  __threadfence_block();
-  __syncthreads();
-  block_exclusive_scan(a.chunk_pre, G + 1, s_scan);
-  for (int g = tid; g < G; g += nt) {
-    const int first = a.chunk_pre[g], nc = a.chunk_pre[g + 1] - first;
-    const int gb = a.grp_off[g], n = a.grp_off[g + 1] - gb;
-    for (int c = 0; c < nc; ++c)
-      a.fitem[first + c] = make_int4(g, gb + (int)((int64_t)n * c / nc),
-                                     gb + (int)((int64_t)n * (c + 1) / nc), 0);
-  }
-  if (tid == 0) {
-    a.hdr[H_NFWD] = a.chunk_pre[G];
-    a.hdr[H_HIT_BEG] = a.grp_off[G];
-    a.hdr[H_HIT_END] = a.grp_off[a.binsB - 1];
-    a.hdr[H_VALID] = a.grp_off[a.binsB - 1];
-  }
+// ---------------------------------------------------------------- shared pieces
+// Positions of the 4 elements of thread tid in tile blk (RB = 1024 per tile).
+static __device__ __forceinline__ int tile_pos(int blk, int r) {
+  return blk * RB + (threadIdx.x >> 6) * 256 + r * 64 + (threadIdx.x & 63);
 }
 
-__global__ __launch_bounds__(RT) void k_route_first(DevArgs a) {
-  extern __shared__ int lds_i[];       // [binsI3] histogram, then the block's offsets
-  __shared__ int s_scan[RT + 1];
-  __shared__ int s_red[8];
-  __shared__ int s_b[2];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int blk = blockIdx.x;
+// Tile decode: bag, digits dA (t,i1), dB (t,i2), dI (t,i3) of the tile's elements (-1 past
+// the end), einfo written, bad indices / slots reported.  Needs LDS s_off
+// [ROUTE_MAX_BAGS], s_red [8], s_b [2].  Whole block.
+static __device__ void tile_decode(const DevArgs &a, int blk, int *s_off, int *s_red, int *s_b,
+                                   int dA[4], int dB[4], int dI[4]) {
+  const int tid = threadIdx.x;
   const int base = blk * RB, last = min(base + RB, a.nnz) - 1;
-  int *hist = lds_i;
-  int *s_off = lds_i + a.binsI3;
-  // bags overlapping [base, last]: one 128-ary search per half of the block.  The
-  // two halves search in lockstep (same NB, same number of rounds).
+  // bags overlapping [base, last]: one 128-ary search per half of the block (lockstep)
   {
     const int half = tid >> 7;
     const int b = half_find_bag(a.off, a.NB, half ? last : base, half, s_red);
     if ((tid & 127) == 0) s_b[half] = b;
   }
-  for (int i = tid; i < a.binsI3; i += RT) hist[i] = 0;
   __syncthreads();
   const int b_lo = s_b[0], b_hi = max(s_b[1], s_b[0]);
   const int nbag = b_hi - b_lo + 1;
   const bool in_lds = nbag + 1 <= ROUTE_MAX_BAGS;
   if (in_lds)
     for (int j = tid; j <= nbag; j += RT) {
-      int64_t o = a.off[b_lo + j];
+      const int64_t o = a.off[b_lo + j];
       s_off[j] = (int)(o < 0 ? 0 : (o > a.nnz ? a.nnz : o));
     }
   __syncthreads();
-  const int dropA = a.binsA - 1, dropB = a.binsB - 1, dropI = a.binsI3 - 1;
-  // all loads of the block's elements first (clamped addresses), then the arithmetic
   int64_t iv[4];
   int sv[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int e = min(base + w * 256 + r * 64 + lane, a.nnz - 1);
-    iv[r] = a.idx[e];
-    sv[r] = (a.has_cache && a.slots) ? a.slots[e] : -1;
+  for (int r = 0; r < 4; ++r) iv[r] = a.idx[min(tile_pos(blk, r), a.nnz - 1)];
+  if (a.has_cache && a.slots) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = a.slots[min(tile_pos(blk, r), a.nnz - 1)];
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = -1;
   }
+  // bag = last b with off[b] <= e: binary lifting over the tile's offsets, the four
+  // elements in lockstep (or a search in global memory for tiles of very many bags)
+  int bag[4];
+  if (in_lds) {
+    int lo[4] = {0, 0, 0, 0};
+    int top = 1;
+    while (top < nbag + 1) top <<= 1;
+    for (int span = top >> 1; span > 0; span >>= 1) {
+      int ov[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ov[r] = s_off[min(lo[r] + span, nbag)];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        lo[r] = (lo[r] + span <= nbag && ov[r] <= tile_pos(blk, r)) ? lo[r] + span : lo[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bag[r] = b_lo + min(lo[r], nbag - 1);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bag[r] = find_bag(a.off, a.NB, min(tile_pos(blk, r), a.nnz - 1));
+  }
+  const int dropA = a.binsA - 1, dropB = a.binsB - 1, dropI = a.binsI3 - 1;
+  const int64_t p23 = (int64_t)a.p2 * a.p3;
+  bool bad_slot = false, bad_index = false;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int e = base + w * 256 + r * 64 + lane;
+    const int e = tile_pos(blk, r);
+    dA[r] = dB[r] = dI[r] = -1;
     if (e >= a.nnz) continue;
-    int b;
-    if (in_lds) {
-      int lo = 0, hi = nbag;  // largest j with s_off[j] <= e
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_off[mid] <= e) lo = mid; else hi = mid;
-      }
-      b = b_lo + lo;
-    } else {
-      b = find_bag(a.off, a.NB, e);
-    }
-    const int t = b / a.B;
-    int dA, dB, dI;
+    const int b = bag[r];
+    const int t = a.T == 1 ? 0 : b / a.B;
     const int slot = sv[r];
+    const int64_t i = iv[r];
     if (slot >= 0) {
       if (slot >= a.cache_size) {
-        set_status(a.status, TT_DEV_BAD_SLOT);
-        dA = dropA; dB = dropB; dI = dropI;
+        bad_slot = true;
+        dA[r] = dropA; dB[r] = dropB; dI[r] = dropI;
       } else {
-        dA = a.T * a.p1 + slot % HB;
-        dB = a.T * a.p2 + slot / HB;
-        dI = dropI;
+        dA[r] = a.T * a.p1 + slot % HB;
+        dB[r] = a.T * a.p2 + slot / HB;
+        dI[r] = dropI;
       }
+    } else if (i < 0 || i >= a.E) {
+      bad_index = true;
+      dA[r] = dropA; dB[r] = dropB; dI[r] = dropI;
     } else {
-      const int64_t i = iv[r];
-      if (i < 0 || i >= a.E) {
-        set_status(a.status, TT_DEV_BAD_INDEX);
-        dA = dropA; dB = dropB; dI = dropI;
-      } else {
-        int i1, i2, i3;
-        split_index(i, a.p3, (int64_t)a.p2 * a.p3, a.rp23, a.rp3, i1, i2, i3);
-        dA = t * a.p1 + i1;
-        dB = t * a.p2 + i2;
-        dI = t * a.p3 + i3;
+      int i1, i2, i3;
+      split_index(i, a.p3, p23, a.rp23, a.rp3, i1, i2, i3);
+      dA[r] = t * a.p1 + i1;
+      dB[r] = t * a.p2 + i2;
+      dI[r] = t * a.p3 + i3;
+    }
+    a.einfo[e] = make_int4(dA[r], dB[r], dI[r], b);
+  }
+  if (bad_slot) set_status(a.status, TT_DEV_BAD_SLOT);
+  if (bad_index) set_status(a.status, TT_DEV_BAD_INDEX);
+}
+
+// Offsets must be a CSR over [0, nnz]; checked grid-strided by the nblk blocks.
+static __device__ void check_offsets(const DevArgs &a, int blk) {
+  const int gt = blk * RT + threadIdx.x, gn = a.nblk * RT;
+  for (int k = gt; k <= a.NB; k += gn) {
+    const int64_t o = a.off[k], o1 = a.off[min(k + 1, a.NB)];
+    if ((k == 0 && o != 0) || (k == a.NB && o != (int64_t)a.nnz) || (k < a.NB && o1 < o))
+      set_status(a.status, TT_DEV_BAD_OFFSETS);
+  }
+}
+
+// Tile histogram of digit d into column blk of the [bin][tile] matrix hist.
+static __device__ void tile_hist(const int d[4], int *lds_h, int nb, int *hist, int blk) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < nb; i += RT) lds_h[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (d[r] >= 0) atomicAdd(&lds_h[d[r]], 1);
+  __syncthreads();
+  for (int i = tid; i < nb; i += RT) hist[(size_t)i * gridDim.x + blk] = lds_h[i];
+}
+
+// Stable ranks of the tile's elements by digit d (order: position) and their output
+// positions start[d * ss + so] + rank.
+static __device__ void tile_place(const int d[4], int pos[4], unsigned short *lds_c, int nb,
+                                  const int *start, int ss, int so) {
+  int rk[4];
+  block_rank4(d, rk, lds_c, nb, nbits_for(nb), nullptr, 0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) pos[r] = d[r] >= 0 ? start[(size_t)d[r] * ss + so] + rk[r] : -1;
+}
+
+// Work items from the group table gs[0..binsB] (starts of the (t,i2) bins in the final
+// order, gs[binsB] = nnz; LDS or global): a miss group of m elements becomes ceil(m / P)
+// items of near-equal size (at most P positions each), numbered group by group; also
+// grp_off and the header words.  Whole block; cnt: G + 1 ints of scratch (LDS or global).
+static __device__ void build_items(const DevArgs &a, const int *gs, int *cnt, int *s_scan) {
+  const int G = a.T * a.p2, tid = threadIdx.x, nt = blockDim.x;
+  for (int g = tid; g <= G; g += nt) {
+    const int m = g < G ? gs[g + 1] - gs[g] : 0;
+    cnt[g] = (m + a.P - 1) / a.P;
+  }
+  for (int b = tid; b <= a.binsB; b += nt) a.grp_off[b] = gs[b];
+  __threadfence_block();
+  __syncthreads();
+  block_exclusive_scan(cnt, G + 1, s_scan);
+  for (int g = tid; g <= G; g += nt) a.chunk_pre[g] = cnt[g];
+  for (int g = tid; g < G; g += nt) {
+    const int first = cnt[g], nc = cnt[g + 1] - first;
+    const int gb = gs[g], m = gs[g + 1] - gb;
+    for (int c = 0; c < nc; ++c)
+      a.fitem[first + c] = make_int4(g, gb + (int)((int64_t)m * c / nc),
+                                     gb + (int)((int64_t)m * (c + 1) / nc), 0);
+  }
+  if (tid == 0) {
+    a.hdr[H_NFWD] = cnt[G];
+    a.hdr[H_HIT_BEG] = gs[G];
+    a.hdr[H_HIT_END] = gs[a.binsB - 1];
+    a.hdr[H_VALID] = gs[a.binsB - 1];
+  }
+}
+
+// Final pass of a tile of orderA: the elements' data gathered, placed by (t,i2).
+static __device__ void tile_final(const DevArgs &a, int blk, unsigned short *lds_c,
+                                  const int *start, int ss, int so) {
+  int e[4], d[4], pos[4], pI[4];
+  int4 info[4];
+  float wv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) e[r] = a.orderA[min(tile_pos(blk, r), a.nnz - 1)];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    info[r] = a.einfo[e[r]];
+    pI[r] = a.posI3_of[e[r]];
+  }
+  if (a.psw) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wv[r] = a.psw[e[r]];
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wv[r] = 1.f;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) d[r] = tile_pos(blk, r) < a.nnz ? info[r].y : -1;
+  tile_place(d, pos, lds_c, a.binsB, start, ss, so);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (pos[r] < 0) continue;
+    const int p = pos[r];
+    a.s_n[p] = e[r];
+    a.s_dA[p] = info[r].x;
+    a.s_dB[p] = info[r].y;
+    a.s_dI3[p] = info[r].z;
+    a.s_bag[p] = info[r].w;
+    a.s_w[p] = wv[r];
+    a.s_posI3[p] = pI[r];
+    a.s_posA[p] = tile_pos(blk, r);
+  }
+}
+
+// ---------------------------------------------------------------- cooperative path
+constexpr int COOP_TILES = 256;        // blocks of one barrier launch (and at most one per CU)
+constexpr int COOP_BINS = 2048;        // bins per digit
+constexpr int COOP_CELLS = 12288;      // bins x tiles per digit (each block reads them all)
+constexpr unsigned SYNC_POLLS = 1u << 22;  // bounded wait of a grid barrier
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!cus[dev] && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) !=
+                       hipSuccess)
+    cus[dev] = 0;
+  return cus[dev];
+}
+
+static bool coop_route_ok(const DevArgs &a) {
+  return a.nblk <= COOP_TILES && a.nblk <= device_cus() && a.binsA <= COOP_BINS && a.binsB <= COOP_BINS &&
+         a.binsI3 <= COOP_BINS && (int64_t)a.binsA * a.nblk <= COOP_CELLS &&
+         (int64_t)a.binsB * a.nblk <= COOP_CELLS && (int64_t)a.binsI3 * a.nblk <= COOP_CELLS;
+}
+
+// All blocks of the cooperative launch meet here (k-th barrier: target k * nblk).  The
+// counter holds (epoch << 32 | arrivals); a word of another call counts as zero.  The
+// wait is bounded: a block that gives up reports TT_DEV_SYNC_TIMEOUT and returns false
+// (its caller then leaves the kernel; nothing of the plan is marked valid).
+static __device__ bool grid_sync(const DevArgs &a, unsigned target) {
+  __shared__ int s_ok;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long *ctr = &a.ctr[0];
+    unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while (true) {
+      const unsigned long long nw = ((unsigned)(old >> 32) == a.epoch)
+                                        ? old + 1ull
+                                        : (((unsigned long long)a.epoch << 32) | 1ull);
+      const unsigned long long prev = atomicCAS(ctr, old, nw);
+      if (prev == old) break;
+      old = prev;
+    }
+    int ok = 1;
+    for (unsigned polls = 0;; ++polls) {
+      const unsigned long long v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((unsigned)(v >> 32) == a.epoch && (unsigned)v >= target) break;
+      if (polls >= SYNC_POLLS) {
+        ok = 0;
+        set_status(a.status, TT_DEV_SYNC_TIMEOUT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    s_ok = ok;
+  }
+  __syncthreads();
+  __threadfence();
+  return s_ok != 0;
+}
+
+// Per-tile bin starts from the [bin][tile] count matrix hist (read whole by every
+// block): start[d] = (elements in smaller bins) + (elements of bin d in tiles < blk);
+// gsum[d] = the global bin starts.  LDS arrays of nb (+1) ints.
+static __device__ void tile_starts(const int *hist, int nb, int blk, int *start, int *gsum,
+                                   int *s_scan) {
+  const int nblk = gridDim.x;
+  for (int d = threadIdx.x; d < nb; d += RT) {
+    const int *row = hist + (size_t)d * nblk;
+    int tot = 0, pre = 0;
+    for (int t0 = 0; t0 < nblk; t0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = row[min(t0 + u, nblk - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int t = t0 + u;
+        tot += t < nblk ? v[u] : 0;
+        pre += t < blk ? v[u] : 0;
       }
     }
-    a.einfo[e] = make_int4(dA, dB, dI, b);
-    atomicAdd(&hist[dI], 1);
+    start[d] = pre;
+    gsum[d] = tot;
   }
-  // offsets must be a CSR over [0, nnz]
-  const int gt = blk * RT + tid, gn = a.nblk * RT;
-  for (int k = gt; k <= a.NB; k += gn) {
-    bool bad = false;
-    if (k == 0 && a.off[0] != 0) bad = true;
-    if (k == a.NB && a.off[a.NB] != (int64_t)a.nnz) bad = true;
-    if (k < a.NB && a.off[k + 1] < a.off[k]) bad = true;
-    if (bad) set_status(a.status, TT_DEV_BAD_OFFSETS);
-  }
-  // the two later digits are histogrammed with atomics: clear them here
-  for (int k = gt; k < a.binsA * a.nblk; k += gn) a.histA[k] = 0;
-  for (int k = gt; k < a.binsB * a.nblk; k += gn) a.histB[k] = 0;
   __syncthreads();
-  for (int i = tid; i < a.binsI3; i += RT) a.histI3[(size_t)i * a.nblk + blk] = hist[i];
-  if (last_block(&a.ctr[0], a.nblk, a.epoch)) block_exclusive_scan(a.histI3, a.binsI3 * a.nblk, s_scan);
+  block_exclusive_scan(gsum, nb, s_scan);
+  for (int d = threadIdx.x; d < nb; d += RT) start[d] += gsum[d];
+  __syncthreads();
+}
+
+// LDS of the cooperative kernel (ints), phases overlap:
+//   decode:  s_off [ROUTE_MAX_BAGS] | hist [max bins]
+//   passes:  lds_c (u16 4 x bins) [2 * COOP_BINS] | startI, gsI, startA, gsA [COOP_BINS + 1]
+//            each | (t,i2) cells [COOP_CELLS]
+constexpr int COOP_LDS_INTS = 2 * COOP_BINS + 4 * (COOP_BINS + 1) + COOP_CELLS;
+
+__global__ __launch_bounds__(RT) void k_route_coop(DevArgs a) {
+  extern __shared__ int lds_i[];
+  __shared__ int s_scan[RT / 64 + 1];
+  __shared__ int s_red[8];
+  __shared__ int s_b[2];
+  const int tid = threadIdx.x, blk = blockIdx.x, nblk = gridDim.x;
+  unsigned short *lds_c = (unsigned short *)lds_i;   // [4][bins] rank counts
+  int *startI = lds_i + 2 * COOP_BINS, *gsI = startI + COOP_BINS + 1;
+  int *startA = gsI + COOP_BINS + 1, *gsA = startA + COOP_BINS + 1;
+  int *cellB = gsA + COOP_BINS + 1;  // [binsB][nblk] (t,i2) counts of the orderA tiles
+  int dA[4], dB[4], dI[4];
+
+  // ---- decode; (t,i3) and (t,i1) histograms of the tile; histB cleared for the atomics
+  tile_decode(a, blk, lds_i, s_red, s_b, dA, dB, dI);
+  check_offsets(a, blk);
+  for (int k = blk * RT + tid; k < a.binsB * nblk; k += nblk * RT) a.histB[k] = 0;
+  tile_hist(dI, lds_i + ROUTE_MAX_BAGS, a.binsI3, a.histI3, blk);
+  __syncthreads();
+  tile_hist(dA, lds_i + ROUTE_MAX_BAGS, a.binsA, a.histA, blk);
+  if (!grid_sync(a, nblk)) return;
+
+  // ---- orderI3 and orderA: stable places by (t,i3) and (t,i1); the (t,i2) counts of
+  //      the orderA tiles gathered per block in LDS, then added to histB
+  tile_starts(a.histI3, a.binsI3, blk, startI, gsI, s_scan);
+  tile_starts(a.histA, a.binsA, blk, startA, gsA, s_scan);
+  if (blk == 0) {
+    for (int d = tid; d < a.binsI3; d += RT) a.segI3[d] = gsI[d];
+    for (int d = tid; d < a.binsA; d += RT) a.segA[d] = gsA[d];
+  }
+  for (int i = tid; i < a.binsB * nblk; i += RT) cellB[i] = 0;
+  int pI[4], pA[4];
+  tile_place(dI, pI, lds_c, a.binsI3, startI, 1, 0);
+  __syncthreads();
+  tile_place(dA, pA, lds_c, a.binsA, startA, 1, 0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (pA[r] < 0) continue;
+    const int e = tile_pos(blk, r);
+    a.posI3_of[e] = pI[r];
+    a.orderA[pA[r]] = e;
+    atomicAdd(&cellB[dB[r] * nblk + pA[r] / RB], 1);
+  }
+  __syncthreads();
+  for (int i = tid; i < a.binsB * nblk; i += RT)
+    if (cellB[i]) atomicAdd(&a.histB[i], cellB[i]);
+  if (!grid_sync(a, 2 * nblk)) return;
+
+  // ---- final order: the orderA tiles placed by (t,i2); block 0 builds the work items
+  tile_starts(a.histB, a.binsB, blk, startI, gsI, s_scan);
+  tile_final(a, blk, lds_c, startI, 1, 0);
+  if (blk == 0) {
+    if (tid == 0) gsI[a.binsB] = a.nnz;
+    __syncthreads();
+    build_items(a, gsI, startA, s_scan);
+    __syncthreads();
+    if (tid == 0) a.hdr[H_PLAN] = (int)a.plan_fp;
+  }
+}
+
+// ---------------------------------------------------------------- three-kernel path
+// k_route_a: decode, (t,i3) and (t,i1) tile histograms; the last block scans both
+// [bin][tile] matrices (bin-major: entry (d, t) becomes the first position of bin d's
+// elements of tile t) and records the bin starts.
+__global__ __launch_bounds__(RT) void k_route_a(DevArgs a) {
+  extern __shared__ int lds_i[];  // s_off [ROUTE_MAX_BAGS] | hist [max(binsI3, binsA)]
+  __shared__ int s_scan[RT / 64 + 1];
+  __shared__ int s_red[8];
+  __shared__ int s_b[2];
+  const int blk = blockIdx.x, tid = threadIdx.x;
+  int dA[4], dB[4], dI[4];
+  tile_decode(a, blk, lds_i, s_red, s_b, dA, dB, dI);
+  check_offsets(a, blk);
+  for (int k = blk * RT + tid; k < a.binsB * a.nblk; k += a.nblk * RT) a.histB[k] = 0;
+  tile_hist(dI, lds_i + ROUTE_MAX_BAGS, a.binsI3, a.histI3, blk);
+  __syncthreads();
+  tile_hist(dA, lds_i + ROUTE_MAX_BAGS, a.binsA, a.histA, blk);
+  if (!last_block(&a.ctr[0], a.nblk, a.epoch)) return;
+  block_exclusive_scan(a.histI3, a.binsI3 * a.nblk, s_scan);
+  block_exclusive_scan(a.histA, a.binsA * a.nblk, s_scan);
+  for (int d = tid; d < a.binsI3; d += RT) a.segI3[d] = a.histI3[(size_t)d * a.nblk];
+  for (int d = tid; d < a.binsA; d += RT) a.segA[d] = a.histA[(size_t)d * a.nblk];
+}
+
+// k_route_b: orderI3 / orderA places of the tile; (t,i2) counts over the orderA tiles;
+// the last block scans them and builds the group table and the work items.
+__global__ __launch_bounds__(RT) void k_route_b(DevArgs a) {
+  extern __shared__ unsigned short lds_c[];  // [4][max(binsI3, binsA)]
+  __shared__ int s_scan[RT / 64 + 1];
+  const int blk = blockIdx.x;
+  int dA[4], dB[4], dI[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int e = tile_pos(blk, r);
+    const int4 info = a.einfo[min(e, a.nnz - 1)];
+    const bool v = e < a.nnz;
+    dA[r] = v ? info.x : -1;
+    dB[r] = v ? info.y : -1;
+    dI[r] = v ? info.z : -1;
+  }
+  int pI[4], pA[4];
+  tile_place(dI, pI, lds_c, a.binsI3, a.histI3, a.nblk, blk);
+  __syncthreads();
+  tile_place(dA, pA, lds_c, a.binsA, a.histA, a.nblk, blk);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (pA[r] < 0) continue;
+    const int e = tile_pos(blk, r);
+    a.posI3_of[e] = pI[r];
+    a.orderA[pA[r]] = e;
+    atomicAdd(&a.histB[(size_t)dB[r] * a.nblk + pA[r] / RB], 1);
+  }
+  if (!last_block(&a.ctr[1], a.nblk, a.epoch)) return;
+  block_exclusive_scan(a.histB, a.binsB * a.nblk, s_scan);
+  for (int d = threadIdx.x; d < a.binsB; d += RT) a.grp_off[d] = a.histB[(size_t)d * a.nblk];
+  if (threadIdx.x == 0) a.grp_off[a.binsB] = a.nnz;
+  __threadfence_block();
+  __syncthreads();
+  build_items(a, a.grp_off, a.chunk_pre, s_scan);
+}
+
+// k_route_c: the orderA tiles placed by (t,i2) into the final order.
+__global__ __launch_bounds__(RT) void k_route_c(DevArgs a) {
+  extern __shared__ unsigned short lds_c[];  // [4][binsB]
+  tile_final(a, blockIdx.x, lds_c, a.histB, a.nblk, blockIdx.x);
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr[H_PLAN] = (int)a.plan_fp;
 }
 
 // Forward: out[b] = sum of the weighted cache rows of bag b (zero when it has none);
@@ -194,92 +488,6 @@ __global__ __launch_bounds__(RT) void k_yinit(DevArgs a) {
       }
     }
     a.Y[(size_t)b * a.D + d] = acc;
-  }
-}
-
-// pass 1: original order -> orderI3 by (t,i3); histogram (t,i1) over destination blocks.
-// pass 2: orderI3 -> orderA by (t,i1); histogram (t,i2) over destination blocks, then
-//         the group table.
-__global__ __launch_bounds__(RT) void k_route_pass(DevArgs a, int pass) {
-  extern __shared__ unsigned short lds_c[];
-  __shared__ int s_scan[RT + 1];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, blk = blockIdx.x;
-  const int *in = pass == 1 ? nullptr : a.orderI3;
-  int *out = pass == 1 ? a.orderI3 : a.orderA;
-  const int *offs = pass == 1 ? a.histI3 : a.histA;
-  int *hnext = pass == 1 ? a.histA : a.histB;
-  const int nbins = pass == 1 ? a.binsI3 : a.binsA;
-  int e[4], d[4], dn[4], rk[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int s = blk * RB + w * 256 + r * 64 + lane;
-    e[r] = -1; d[r] = -1; dn[r] = 0;
-    if (s < a.nnz) {
-      e[r] = in ? in[s] : s;
-      const int4 info = a.einfo[e[r]];
-      d[r] = pass == 1 ? info.z : info.x;
-      dn[r] = pass == 1 ? info.x : info.y;
-    }
-  }
-  block_rank4(d, rk, lds_c, nbins, nbits_for(nbins), nullptr, a.nblk);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if (e[r] < 0) continue;
-    const int pos = offs[(size_t)d[r] * a.nblk + blk] + rk[r];
-    out[pos] = e[r];
-    (pass == 1 ? a.posI3_of : a.posA_of)[e[r]] = pos;
-    atomicAdd(&hnext[(size_t)dn[r] * a.nblk + pos / RB], 1);
-  }
-  if (!last_block(&a.ctr[pass], a.nblk, a.epoch)) return;
-  const int binsN = pass == 1 ? a.binsA : a.binsB;
-  block_exclusive_scan(hnext, binsN * a.nblk, s_scan);
-  if (pass == 2) {
-    for (int b = tid; b < a.binsB; b += RT) a.grp_off[b] = a.histB[(size_t)b * a.nblk];
-    if (tid == 0) a.grp_off[a.binsB] = a.nnz;
-    __threadfence_block();
-    __syncthreads();
-    build_items(a, s_scan);
-  }
-}
-
-__global__ __launch_bounds__(RT) void k_route_final(DevArgs a) {
-  extern __shared__ unsigned short lds_c[];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, blk = blockIdx.x;
-  if (blk == 0 && tid == 0) a.hdr[H_PLAN] = (int)a.plan_fp;
-  int e[4], d[4], rk[4], pI[4], pA[4];
-  float wv[4];
-  int4 info[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int s = min(blk * RB + w * 256 + r * 64 + lane, a.nnz - 1);
-    e[r] = a.orderA[s];
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    info[r] = a.einfo[e[r]];
-    pI[r] = a.posI3_of[e[r]];
-    pA[r] = a.posA_of[e[r]];
-    wv[r] = a.psw ? a.psw[e[r]] : 1.f;
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int s = blk * RB + w * 256 + r * 64 + lane;
-    d[r] = s < a.nnz ? info[r].y : -1;
-    if (s >= a.nnz) e[r] = -1;
-  }
-  block_rank4(d, rk, lds_c, a.binsB, nbits_for(a.binsB), nullptr, a.nblk);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if (e[r] < 0) continue;
-    const int pos = a.histB[(size_t)d[r] * a.nblk + blk] + rk[r];
-    a.s_n[pos] = e[r];
-    a.s_dA[pos] = info[r].x;
-    a.s_dB[pos] = info[r].y;
-    a.s_dI3[pos] = info[r].z;
-    a.s_bag[pos] = info[r].w;
-    a.s_w[pos] = wv[r];
-    a.s_posI3[pos] = pI[r];
-    a.s_posA[pos] = pA[r];
   }
 }
 
@@ -329,298 +537,33 @@ __global__ __launch_bounds__(RT) void k_runsum(DevArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- one-block route
-// Batches of at most SR_MAX elements with at most SR_BINS bins per digit and at most
-// SR_OFF - 1 bags are grouped by a single 1024-thread workgroup with everything in
-// LDS: the same three stable counting passes (by (t,i3), (t,i1), (t,i2)) and the
-// same outputs as the multi-block kernels, without their grid-wide scans.
-constexpr int SR_T = 1024, SR_W = SR_T / 64;
-constexpr int SR_MAX = 12288;               // elements (u16 positions)
-constexpr int SR_K = SR_MAX / SR_T;         // positions per lane and pass
-constexpr int SR_BINS = 1024;
-constexpr int SR_OFF = 8192;                // offsets kept in LDS (in the count area)
-constexpr size_t SR_LDS = (size_t)5 * SR_MAX * 2 + (size_t)SR_W * SR_BINS * 2 + (SR_BINS + 1) * 4;
-
-static bool small_route_ok(const DevArgs &a) {
-  return a.nnz <= SR_MAX && a.binsA <= SR_BINS && a.binsB <= SR_BINS && a.binsI3 <= SR_BINS &&
-         a.NB + 1 <= SR_OFF;
-}
-
-// Loads here are written unconditionally (clamped addresses, selects afterwards): a
-// load under a per-lane condition becomes a branch with a wait of its own, which
-// serialises the unrolled loops.
-__global__ __launch_bounds__(SR_T) void k_route_small(DevArgs a) {
-  extern __shared__ int4 lds4[];
-  unsigned short *dig = (unsigned short *)lds4;   // [3][SR_MAX] digits by element; the
-                                                  // first two later hold posI3 / posA
-  unsigned short *ord = dig + 3 * SR_MAX;         // [2][SR_MAX] order ping-pong
-  unsigned short *cnt = ord + 2 * SR_MAX;         // [SR_W][SR_BINS] per-wave bin counts
-  int *base = (int *)(cnt + SR_W * SR_BINS);      // [SR_BINS + 1]
-  int *s_off = (int *)cnt;                        // phase 0: offsets [NB + 1]
-  __shared__ int s_scan[SR_W + 1];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int n = a.nnz, NB = a.NB;
-
-  // offsets (clamped copy in LDS) and their validation: a CSR over [0, n]
-  for (int b = tid; b <= NB; b += SR_T) {
-    const int64_t o = a.off[b];
-    const int64_t o1 = a.off[min(b + 1, NB)];
-    s_off[b] = (int)(o < 0 ? 0 : (o > n ? n : o));
-    if ((b == 0 && o != 0) || (b == NB && o != (int64_t)n) || (b < NB && o1 < o))
-      set_status(a.status, TT_DEV_BAD_OFFSETS);
-  }
-  __syncthreads();
-  // elements: split, bag, digits (three parts: register budget)
-  bool bad_slot = false, bad_index = false;
-  for (int h = 0; h < 3; ++h) {
-    constexpr int KH = SR_K / 3;
-    int64_t iv[KH];
-    int sv[KH], lo[KH];
-#pragma unroll
-    for (int k = 0; k < KH; ++k) iv[k] = a.idx[min(tid + (h * KH + k) * SR_T, n - 1)];
-    if (a.has_cache && a.slots) {
-#pragma unroll
-      for (int k = 0; k < KH; ++k) sv[k] = a.slots[min(tid + (h * KH + k) * SR_T, n - 1)];
-    } else {
-#pragma unroll
-      for (int k = 0; k < KH; ++k) sv[k] = -1;
-    }
-    // bag = last b < NB with off[b] <= e: binary lifting, all elements in lockstep
-#pragma unroll
-    for (int k = 0; k < KH; ++k) lo[k] = 0;
-    int top = 1;
-    while (top < NB) top <<= 1;
-    for (int span = top >> 1; span > 0; span >>= 1) {
-      int ov[KH];
-#pragma unroll
-      for (int k = 0; k < KH; ++k) ov[k] = s_off[min(lo[k] + span, NB - 1)];
-#pragma unroll
-      for (int k = 0; k < KH; ++k)
-        lo[k] = (lo[k] + span < NB && ov[k] <= tid + (h * KH + k) * SR_T) ? lo[k] + span : lo[k];
-    }
-    const int dropA = a.binsA - 1, dropB = a.binsB - 1, dropI = a.binsI3 - 1;
-    const int64_t p23 = (int64_t)a.p2 * a.p3;
-#pragma unroll
-    for (int k = 0; k < KH; ++k) {
-      const int e = tid + (h * KH + k) * SR_T;
-      const int b = lo[k], t = a.T == 1 ? 0 : b / a.B;
-      const int slot = sv[k];
-      const int64_t i = iv[k];
-      const bool hit = slot >= 0, slot_ok = hit && slot < a.cache_size;
-      const bool idx_ok = !hit && i >= 0 && i < a.E;
-      const int64_t ic = idx_ok ? i : 0;
-      const int sc = slot_ok ? slot : 0;
-      int i1, i2, i3;
-      split_index(ic, a.p3, p23, a.rp23, a.rp3, i1, i2, i3);
-      int dA = t * a.p1 + i1;
-      int dB = t * a.p2 + i2;
-      int dI = t * a.p3 + i3;
-      if (slot_ok) { dA = a.T * a.p1 + sc % HB; dB = a.T * a.p2 + sc / HB; dI = dropI; }
-      if (!slot_ok && !idx_ok) { dA = dropA; dB = dropB; dI = dropI; }
-      if (e < n) {
-        bad_slot |= hit && !slot_ok;
-        bad_index |= !hit && !idx_ok;
-        a.einfo[e] = make_int4(dA, dB, dI, b);
-        dig[e] = (unsigned short)dI;
-        dig[SR_MAX + e] = (unsigned short)dA;
-        dig[2 * SR_MAX + e] = (unsigned short)dB;
-        ord[e] = (unsigned short)e;
-      }
-    }
-  }
-  if (bad_slot) set_status(a.status, TT_DEV_BAD_SLOT);
-  if (bad_index) set_status(a.status, TT_DEV_BAD_INDEX);
-  __syncthreads();
-
-  // three stable counting passes; wave w ranks the positions [w*per, (w+1)*per) of the
-  // current order, 64 at a time, by ballot matching
-  const int per = (n + SR_W * 64 - 1) / (SR_W * 64) * 64;
-  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int pass = 0; pass < 3; ++pass) {
-    const unsigned short *in = ord + (pass & 1) * SR_MAX;
-    unsigned short *out = ord + ((pass + 1) & 1) * SR_MAX;
-    const unsigned short *dg = dig + pass * SR_MAX;
-    const int nb = pass == 0 ? a.binsI3 : (pass == 1 ? a.binsA : a.binsB);
-    const int nbits = nbits_for(nb);
-    for (int i = tid; i < SR_W * SR_BINS / 2; i += SR_T) ((unsigned *)cnt)[i] = 0u;
-    // xd[k] = element | (digit + 1) << 14 (digit -1: no position); rk[k] = rank in wave
-    int xd[SR_K], rk[SR_K];
-#pragma unroll
-    for (int k = 0; k < SR_K; ++k) xd[k] = in[min(w * per + k * 64 + lane, n - 1)];
-#pragma unroll
-    for (int k = 0; k < SR_K; ++k) {
-      const int p = w * per + k * 64 + lane;
-      const bool act = k * 64 < per && p < n;
-      const int d = dg[xd[k]];
-      xd[k] |= (act ? d + 1 : 0) << 14;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < SR_K; ++k) {
-      const int dk = (xd[k] >> 14) - 1;
-      const bool act = dk >= 0;
-      unsigned long long m = __ballot(act);
-      for (int b = 0; b < nbits; ++b) {
-        const bool bit = act && ((dk >> b) & 1);
-        const unsigned long long bb = __ballot(bit);
-        m &= bit ? bb : ~bb;
-      }
-      const int before = __popcll(m & lt);
-      const int ci = w * SR_BINS + (act ? dk : 0);
-      const int c0 = cnt[ci];
-      rk[k] = c0 + before;
-      // every lane of the group has read the count before its leader writes it back
-      __builtin_amdgcn_wave_barrier();
-      if (act && before == 0) cnt[ci] = (unsigned short)(c0 + __popcll(m));
-      __builtin_amdgcn_wave_barrier();
-    }
-    __syncthreads();
-    // per bin: exclusive prefix over the waves, then the bin starts (block scan)
-    int tot = 0;
-    {
-      int cv[SR_W];
-      const int bi = min(tid, SR_BINS - 1);
-#pragma unroll
-      for (int v = 0; v < SR_W; ++v) cv[v] = cnt[v * SR_BINS + bi];
-      if (tid < nb) {
-#pragma unroll
-        for (int v = 0; v < SR_W; ++v) {
-          cnt[v * SR_BINS + bi] = (unsigned short)tot;
-          tot += cv[v];
-        }
-      }
-    }
-    const int incl = wave_incl_scan(tot);
-    if (lane == 63) s_scan[w] = incl;
-    __syncthreads();
-    if (w == 0) {
-      const int v = lane < SR_W ? s_scan[lane] : 0;
-      const int vi = wave_incl_scan(v);
-      if (lane < SR_W) s_scan[lane] = vi - v;
-    }
-    __syncthreads();
-    if (tid < nb) {
-      const int start = s_scan[w] + incl - tot;
-      base[tid] = start;
-      if (pass == 0) a.histI3[(size_t)tid * a.nblk] = start;
-      else if (pass == 1) a.histA[(size_t)tid * a.nblk] = start;
-      else a.grp_off[tid] = start;
-    }
-    if (tid == 0 && pass == 2) base[nb] = n;
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < SR_K; ++k) {
-      const int dk = (xd[k] >> 14) - 1, d = dk >= 0 ? dk : 0;
-      rk[k] += base[d] + cnt[w * SR_BINS + d];
-    }
-#pragma unroll
-    for (int k = 0; k < SR_K; ++k) {
-      if ((xd[k] >> 14) > 0) {
-        const int x = xd[k] & 0x3fff;
-        out[rk[k]] = (unsigned short)x;
-        if (pass < 2) dig[pass * SR_MAX + x] = (unsigned short)rk[k];  // posI3 / posA
-      }
-    }
-    __syncthreads();
-  }
-
-  // final order (ord[1]) -> the per-position arrays (two halves: register budget)
-  for (int h = 0; h < 2; ++h) {
-    constexpr int KH = SR_K / 2;
-    const unsigned short *fin = ord + SR_MAX;
-    int ek[KH], pI[KH], pA[KH];
-    int4 info[KH];
-    float wv[KH];
-#pragma unroll
-    for (int k = 0; k < KH; ++k) ek[k] = fin[min(tid + (h * KH + k) * SR_T, n - 1)];
-#pragma unroll
-    for (int k = 0; k < KH; ++k) {
-      info[k] = a.einfo[ek[k]];
-      pI[k] = dig[ek[k]];
-      pA[k] = dig[SR_MAX + ek[k]];
-    }
-    if (a.psw) {
-#pragma unroll
-      for (int k = 0; k < KH; ++k) wv[k] = a.psw[ek[k]];
-    } else {
-#pragma unroll
-      for (int k = 0; k < KH; ++k) wv[k] = 1.f;
-    }
-#pragma unroll
-    for (int k = 0; k < KH; ++k) {
-      const int s = tid + (h * KH + k) * SR_T;
-      if (s < n) {
-        a.s_n[s] = ek[k];
-        a.s_dA[s] = info[k].x;
-        a.s_dB[s] = info[k].y;
-        a.s_dI3[s] = info[k].z;
-        a.s_bag[s] = info[k].w;
-        a.s_w[s] = wv[k];
-        a.s_posI3[s] = pI[k];
-        a.s_posA[s] = pA[k];
-      }
-    }
-  }
-  // work items from the group starts in LDS (base[0..binsB], base[binsB] = n): a
-  // group of m elements gives ceil(m / P) items of near-equal size
-  {
-    const int G = a.T * a.p2;  // G < binsB <= SR_T
-    const int gb = base[min(tid, G)], ge = base[min(tid + 1, a.binsB)];
-    const int m = tid < G ? ge - gb : 0;
-    const int nc = (m + a.P - 1) / a.P;
-    const int incl = wave_incl_scan(nc);
-    if (lane == 63) s_scan[w] = incl;
-    __syncthreads();
-    if (w == 0) {
-      const int v = lane < SR_W ? s_scan[lane] : 0;
-      const int vi = wave_incl_scan(v);
-      if (lane < SR_W) s_scan[lane] = vi - v;
-      if (lane == SR_W - 1) s_scan[SR_W] = vi;
-    }
-    __syncthreads();
-    const int first = s_scan[w] + incl - nc;
-    if (tid <= G) a.chunk_pre[tid] = first;
-    for (int c = 0; c < nc; ++c)
-      a.fitem[first + c] = make_int4(tid, gb + (int)((int64_t)m * c / nc),
-                                     gb + (int)((int64_t)m * (c + 1) / nc), 0);
-    if (tid == 0) {
-      a.grp_off[a.binsB] = n;
-      a.hdr[H_NFWD] = s_scan[SR_W];
-      a.hdr[H_HIT_BEG] = base[G];
-      a.hdr[H_HIT_END] = base[a.binsB - 1];
-      a.hdr[H_VALID] = base[a.binsB - 1];
-      a.hdr[H_PLAN] = (int)a.plan_fp;
-    }
-  }
-}
-
 hipError_t launch_route(const DevArgs &a, hipStream_t s) {
   if (a.nblk == 0) return hipGetLastError();
-  if (small_route_ok(a)) {
+  if (coop_route_ok(a)) {
     static bool attr_set = false;  // dynamic LDS above 64 KiB is opt-in per kernel
+    const size_t lds = (size_t)COOP_LDS_INTS * 4;
     if (!attr_set) {
-      (void)hipFuncSetAttribute((const void *)k_route_small,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)SR_LDS);
+      (void)hipFuncSetAttribute((const void *)k_route_coop,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       attr_set = true;
     }
-    prof_begin(K_ROUTE_SMALL, s);
-    hipLaunchKernelGGL(k_route_small, dim3(1), dim3(SR_T), SR_LDS, s, a);
-    prof_end(K_ROUTE_SMALL, s);
+    // One block per CU at most (LDS), launched on an otherwise idle stream position:
+    // every block is resident at once.  The barriers are bounded waits in any case.
+    prof_begin(K_ROUTE_COOP, s);
+    hipLaunchKernelGGL(k_route_coop, dim3(a.nblk), dim3(RT), lds, s, a);
+    prof_end(K_ROUTE_COOP, s);
     return hipGetLastError();
   }
-  prof_begin(K_ROUTE_FIRST, s);
-  hipLaunchKernelGGL(k_route_first, dim3(a.nblk), dim3(RT),
-                     (size_t)(a.binsI3 + ROUTE_MAX_BAGS) * 4, s, a);
-  prof_end(K_ROUTE_FIRST, s);
-  prof_begin(K_ROUTE_PASS1, s);
-  hipLaunchKernelGGL(k_route_pass, dim3(a.nblk), dim3(RT), (size_t)a.binsI3 * 8, s, a, 1);
-  prof_end(K_ROUTE_PASS1, s);
-  prof_begin(K_ROUTE_PASS2, s);
-  hipLaunchKernelGGL(k_route_pass, dim3(a.nblk), dim3(RT), (size_t)a.binsA * 8, s, a, 2);
-  prof_end(K_ROUTE_PASS2, s);
-  prof_begin(K_ROUTE_FINAL, s);
-  hipLaunchKernelGGL(k_route_final, dim3(a.nblk), dim3(RT), (size_t)a.binsB * 8, s, a);
-  prof_end(K_ROUTE_FINAL, s);
+  const size_t bins_ia = (size_t)(a.binsI3 > a.binsA ? a.binsI3 : a.binsA);
+  prof_begin(K_ROUTE_A, s);
+  hipLaunchKernelGGL(k_route_a, dim3(a.nblk), dim3(RT), (ROUTE_MAX_BAGS + bins_ia) * 4, s, a);
+  prof_end(K_ROUTE_A, s);
+  prof_begin(K_ROUTE_B, s);
+  hipLaunchKernelGGL(k_route_b, dim3(a.nblk), dim3(RT), bins_ia * 8, s, a);
+  prof_end(K_ROUTE_B, s);
+  prof_begin(K_ROUTE_C, s);
+  hipLaunchKernelGGL(k_route_c, dim3(a.nblk), dim3(RT), (size_t)a.binsB * 8, s, a);
+  prof_end(K_ROUTE_C, s);
   return hipGetLastError();
 }
 

@@ -339,8 +339,7 @@ def test_bag_ids_and_route_order_brute_force():
         t = bag[n] // B
         if slots[n] >= 0:
             return (1, int(slots[n]), 0, 0, n)
-        return (0, int(t * p[1] + (idx[n] // p[2]) % p[1]), int(idx[n] // (p[1] * p[2])),
-                int(idx[n] % p[2]), n)
+        return (0, int(t * p[1] + (idx[n] // p[2]) % p[1]), int(idx[n] // (p[1] * p[2])), 0, n)
     ks = [key(n) for n in order]
     assert all(a < b for a, b in zip(ks, ks[1:]))
     assert counts.sum() == sum(1 for n in valid if slots[n] < 0)
