@@ -37,8 +37,8 @@ struct Plan {
   size_t lds_fwd = 0, lds_bwd = 0;
   size_t ws_total = 0;
   // byte offsets inside the workspace
-  size_t o_ctr, o_hdr, o_einfo, o_histA, o_histB, o_histI3, o_orderA, o_segI3, o_segA, o_sn,
-      o_sdA, o_sdB, o_sdI3, o_sbag, o_sw, o_posI3, o_sposI3, o_sposA, o_fitem, o_grp, o_chunk,
+  size_t o_ctr, o_hdr, o_einfo, o_histA, o_histB, o_histI3, o_rec, o_segI3, o_segA, o_srec,
+      o_fitem, o_grp, o_chunk,
       o_l1, o_l3, o_p1, o_p3, o_frag, o_p2;
 };
 
@@ -125,18 +125,10 @@ int make_plan(const tt_desc *d, int64_t nnz, int64_t num_bags, int64_t cache_siz
   P->o_histA = carve(cur, (size_t)binsA * nb * 4);
   P->o_histB = carve(cur, (size_t)binsB * nb * 4);
   P->o_histI3 = carve(cur, (size_t)binsI3 * nb * 4);
-  P->o_orderA = carve(cur, n * 4);
+  P->o_rec = carve(cur, n * 32);
   P->o_segI3 = carve(cur, ((size_t)binsI3 + 1) * 4);
   P->o_segA = carve(cur, ((size_t)binsA + 1) * 4);
-  P->o_sn = carve(cur, n * 4);
-  P->o_sdA = carve(cur, n * 4);
-  P->o_sdB = carve(cur, n * 4);
-  P->o_sdI3 = carve(cur, n * 4);
-  P->o_sbag = carve(cur, n * 4);
-  P->o_sw = carve(cur, n * 4);
-  P->o_posI3 = carve(cur, n * 4);
-  P->o_sposI3 = carve(cur, n * 4);
-  P->o_sposA = carve(cur, n * 4);
+  P->o_srec = carve(cur, n * 32);
   P->o_fitem = carve(cur, (size_t)items_max(a) * sizeof(int4));
   P->o_grp = carve(cur, ((size_t)binsB + 1) * 4);
   P->o_chunk = carve(cur, (G + 1) * 4);
@@ -159,18 +151,10 @@ void bind_ws(Plan *P, void *ws) {
   a.histA = (int *)(b + P->o_histA);
   a.histB = (int *)(b + P->o_histB);
   a.histI3 = (int *)(b + P->o_histI3);
-  a.orderA = (int *)(b + P->o_orderA);
+  a.rec = (int *)(b + P->o_rec);
   a.segI3 = (int *)(b + P->o_segI3);
   a.segA = (int *)(b + P->o_segA);
-  a.s_n = (int *)(b + P->o_sn);
-  a.s_dA = (int *)(b + P->o_sdA);
-  a.s_dB = (int *)(b + P->o_sdB);
-  a.s_dI3 = (int *)(b + P->o_sdI3);
-  a.s_bag = (int *)(b + P->o_sbag);
-  a.s_w = (float *)(b + P->o_sw);
-  a.posI3_of = (int *)(b + P->o_posI3);
-  a.s_posI3 = (int *)(b + P->o_sposI3);
-  a.s_posA = (int *)(b + P->o_sposA);
+  a.srec = (int4 *)(b + P->o_srec);
   a.fitem = (int4 *)(b + P->o_fitem);
   a.grp_off = (int *)(b + P->o_grp);
   a.chunk_pre = (int *)(b + P->o_chunk);
@@ -369,10 +353,10 @@ int tt_bag_backward_sgd(const tt_desc *desc, float *const cores[3], const int64_
 }
 
 // copies the grouping order: valid elements first (see tt_bag.h)
-__global__ void k_copy_route(const int *s_n, int nnz, const int *grp_off, int G, int binsB,
+__global__ void k_copy_route(const int4 *srec, int nnz, const int *grp_off, int G, int binsB,
                              int *order_out, int *group_off_out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < nnz) order_out[i] = s_n[i];
+  if (i < nnz) order_out[i] = srec[2 * (size_t)i].x;
   if (i <= G) group_off_out[i] = grp_off[i];
   if (i == G + 1) group_off_out[G + 1] = grp_off[binsB - 1];
 }
@@ -403,7 +387,7 @@ int tt_bag_route(const tt_desc *desc, const int64_t *indices, int64_t nnz,
   e = launch_route(a, s);
   if (e == hipSuccess) {
     const int n = (int)nnz > G + 2 ? (int)nnz : G + 2;
-    hipLaunchKernelGGL(k_copy_route, dim3((n + 255) / 256), dim3(256), 0, s, a.s_n, a.nnz,
+    hipLaunchKernelGGL(k_copy_route, dim3((n + 255) / 256), dim3(256), 0, s, a.srec, a.nnz,
                        a.grp_off, G, a.binsB, order_out, group_off_out);
     e = hipGetLastError();
   }

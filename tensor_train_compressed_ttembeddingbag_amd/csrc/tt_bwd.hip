@@ -140,9 +140,10 @@ void k_bwd(DevArgs a) {
   if (tid < 64) {
     const int s = s0 + min(tid, n_el - 1);
     const bool v = tid < n_el;
-    const int dAv = a.s_dA[s], dIv = a.s_dI3[s], bagv = a.s_bag[s];
-    const int lA = a.s_posA[s], lI = a.s_posI3[s];
-    const float wv = a.s_w[s];
+    const SPos sp = load_spos(a.srec, s);
+    const int dAv = sp.dA, dIv = sp.dI3, bagv = sp.bag;
+    const int lA = sp.posA, lI = sp.posI3;
+    const float wv = sp.w;
     const int dA = v ? dAv : -1, i3 = v ? dIv - t * a.p3 : 0;
     e_bag[tid] = bagv;
     e_w[tid] = wv;
@@ -471,116 +472,152 @@ hipError_t launch_bwd(const DevArgs &a, int RP, size_t lds, hipStream_t s) {
 
 // ---------------------------------------------------------------- k_seg
 // Blocks of 256 threads, three kinds of task:
-//  * four waves = four core-1 slices (t, i1) or core-3 slices (t, i3): a slice walks
-//    its segment of the (t,i1)- or (t,i3)-ordered element list; the link of each
-//    position names the final-order position of a partial (or -1); the partials are
-//    summed in segment order, eight loads in flight at a time, then SGD is applied;
-//  * one block = one core-2 slice (t, i2): the dG2 partials of the group's work
-//    items are summed in item order, then SGD;
+//  * one block = one core-1 slice (t, i1) or core-3 slice (t, i3): the slice's segment
+//    of the (t,i1)- / (t,i3)-ordered element list names, through the links, the final-
+//    order positions of its partials; they are listed in segment order, then summed by
+//    8 row groups (row group k takes rows k, k+8, ...; a fixed assignment), the group
+//    sums added in group order, and SGD applied;
+//  * one block = one core-2 slice (t, i2): the dG2 partials of the group's work items
+//    are summed in item order, then SGD;
 //  * four waves = four 64-position pieces of the cache-hit region: a cache run (one
 //    slot) is finished by the piece that holds its first position, which sums the
 //    run's fragments (its first position, then every multiple of P inside the run).
-__global__ __launch_bounds__(256) void k_seg(DevArgs a) {
+constexpr int SEG_T = 256;
+constexpr int SEG_ROWS = 8;   // partial rows in flight per thread
+
+__global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
+  __shared__ int s_rows[SEG_T];
+  __shared__ int s_wc[SEG_T / 64 + 1];
+  __shared__ float s_red[SEG_T * 4];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int nA = a.T * a.p1, nC = a.T * a.p3, G = a.T * a.p2;
-  const int nb1 = (nA + nC + 3) / 4;
-  if (a.hdr[H_PLAN] != (int)a.plan_fp) {  // the workspace holds another call's plan
-    if (blockIdx.x == 0 && tid == 0) set_status(a.status, DEV_STALE_PLAN);
+  const int bid = blockIdx.x;
+  // the plan check and the task's first loads go out together
+  const bool one = bid < nA;
+  const int seg = one ? bid : bid - nA;
+  const int *seg_start = one ? a.segA : a.segI3;
+  const int gi = min(max(bid - nA - nC, 0), G - 1);
+  const int plan = a.hdr[H_PLAN];
+  const int beg = seg_start[min(seg, one ? nA : nC)], end = seg_start[min(seg + 1, one ? nA : nC)];
+  const int i0 = a.chunk_pre[gi], i1 = a.chunk_pre[gi + 1];
+  if (plan != (int)a.plan_fp) {  // the workspace holds another call's plan
+    if (bid == 0 && tid == 0) set_status(a.status, DEV_STALE_PLAN);
     return;
   }
-  const int bid = blockIdx.x;
-  if (bid < nb1) {
-    const int task = bid * 4 + w;
-    if (task >= nA + nC) return;
-    const bool one = task < nA;
-    const int seg = one ? task : task - nA;
-    const int *seg_start = one ? a.segA : a.segI3;
+  if (bid < nA + nC) {
     const int *link = one ? a.link1 : a.link3;
     const float *part = one ? a.part1 : a.part3;
     const int W = one ? a.q1 * a.R1 : a.R2 * a.q3;
     float *dst = one ? a.G1 + (size_t)seg * W : a.G3 + (size_t)seg * W;
-    const int beg = seg_start[seg], end = seg_start[seg + 1];
     if (beg >= end) return;
-    for (int col0 = 0; col0 < W; col0 += 256) {  // W <= 1024 (R2 * q3)
+    // columns: 4 per lane when W allows 16-byte rows, lanes per row LPR, row groups NRG
+    const int VEC = (W & 3) == 0 ? 4 : 1;
+    const int LPR = min(SEG_T, (W + VEC - 1) / VEC), NRG = SEG_T / LPR;
+    const int rg = tid / LPR, cl = tid - rg * LPR;
+    for (int c0 = 0; c0 < W; c0 += LPR * VEC) {  // column blocks (one unless W > 1024)
+      const int col = c0 + cl * VEC;
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      int cc[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) cc[j] = min(col0 + lane + 64 * j, W - 1);
-      for (int s0 = beg; s0 < end; s0 += 64) {
-        const int sl = min(s0 + lane, end - 1);
-        const int lk = link[sl];
-        unsigned long long m = __ballot(s0 + lane < end && lk >= 0);
-        while (m) {
-          int ps[8];
-          int cnt = 0;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            ps[k] = -1;
-            if (m) {
-              const int l = __ffsll((long long)m) - 1;
-              m &= m - 1;
-              ps[k] = __builtin_amdgcn_readlane(lk, l);
-              ++cnt;
-            }
-          }
-          float v[8][4];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const float *row = part + (size_t)max(ps[k], 0) * W;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[k][j] = row[cc[j]];
-          }
-#pragma unroll
-          for (int k = 0; k < 8; ++k)
-            if (k < cnt)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) acc[j] += v[k][j];
+      for (int p0 = beg; p0 < end; p0 += SEG_T) {
+        // the chunk's partial rows, in segment order
+        const int lk = p0 + tid < end ? link[p0 + tid] : -1;
+        const unsigned long long m = __ballot(lk >= 0);
+        const unsigned long long lt = (1ull << lane) - 1ull;
+        if (lane == 0) s_wc[w] = __popcll(m);
+        __syncthreads();
+        int before = 0, n = 0;
+        for (int v = 0; v < SEG_T / 64; ++v) {
+          before += v < w ? s_wc[v] : 0;
+          n += s_wc[v];
         }
-      }
+        if (lk >= 0) s_rows[before + __popcll(m & lt)] = lk;
+        __syncthreads();
+        if (rg < NRG && col < W) {
+          for (int k0 = rg; k0 < n; k0 += NRG * SEG_ROWS) {
+            float4 v[SEG_ROWS];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = col0 + lane + 64 * j;
-        if (col < W) dst[col] -= a.lr * acc[j];
+            for (int u = 0; u < SEG_ROWS; ++u) {
+              const int k = min(k0 + u * NRG, n - 1);
+              const float *row = part + (size_t)s_rows[k] * W + col;
+              if (VEC == 4) {
+                v[u] = *(const float4 *)row;
+              } else {
+                v[u].x = row[0];
+                v[u].y = v[u].z = v[u].w = 0.f;
+              }
+            }
+#pragma unroll
+            for (int u = 0; u < SEG_ROWS; ++u)
+              if (k0 + u * NRG < n) {
+                acc[0] += v[u].x; acc[1] += v[u].y; acc[2] += v[u].z; acc[3] += v[u].w;
+              }
+          }
+        }
+        __syncthreads();
       }
+      // row groups summed in group order, then SGD
+      if (rg < NRG)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s_red[(rg * LPR + cl) * 4 + j] = acc[j];
+      __syncthreads();
+      for (int t2 = tid; t2 < LPR * VEC; t2 += SEG_T) {
+        const int c = c0 + t2;
+        float sum = 0.f;
+        for (int r = 0; r < NRG; ++r) sum += s_red[(r * LPR + t2 / VEC) * 4 + t2 % VEC];
+        if (c < W) dst[c] -= a.lr * sum;
+      }
+      __syncthreads();
     }
     return;
   }
-  if (bid < nb1 + G) {
-    const int g = bid - nb1;
-    const int i0 = a.chunk_pre[g], i1 = a.chunk_pre[g + 1];
+  if (bid < nA + nC + G) {
+    const int g = gi;
     if (i0 >= i1) return;
-    const size_t slice2 = (size_t)a.R1 * a.q2 * a.R2;
+    const int slice2 = a.R1 * a.q2 * a.R2;  // <= 64 * 64 * 64
     float *dst = a.G2 + (size_t)g * slice2;
-    for (size_t e0 = tid; e0 < slice2; e0 += 256 * 4) {
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int it = i0; it < i1; ++it) {
-        const float *src = a.part2 + (size_t)it * slice2;
-        float v[4];
+    // per thread: up to 16 columns at once (the whole slice for ranks <= 32), their old
+    // values and 2 items' partials in flight; items summed in item order
+    constexpr int CU = 16;
+    for (int e0 = tid; e0 < slice2; e0 += SEG_T * CU) {
+      float acc[CU], old[CU];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = src[min(e0 + (size_t)u * 256, slice2 - 1)];
+      for (int u = 0; u < CU; ++u) {
+        acc[u] = 0.f;
+        old[u] = dst[min(e0 + u * SEG_T, slice2 - 1)];
+      }
+      for (int it0 = i0; it0 < i1; it0 += 2) {
+        float v[2][CU];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[u] += v[u];
+        for (int k = 0; k < 2; ++k) {
+          const float *src = a.part2 + (size_t)min(it0 + k, i1 - 1) * slice2;
+#pragma unroll
+          for (int u = 0; u < CU; ++u) v[k][u] = src[min(e0 + u * SEG_T, slice2 - 1)];
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+          if (it0 + k < i1)
+#pragma unroll
+            for (int u = 0; u < CU; ++u) acc[u] += v[k][u];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const size_t e = e0 + (size_t)u * 256;
-        if (e < slice2) dst[e] -= a.lr * acc[u];
-      }
+      for (int u = 0; u < CU; ++u)
+        if (e0 + u * SEG_T < slice2) dst[e0 + u * SEG_T] = old[u] - a.lr * acc[u];
     }
     return;
   }
   if (!a.has_cache) return;
-  const int k = (bid - nb1 - G) * 4 + w;
+  const int k = (bid - nA - nC - G) * 4 + w;
   const int hb = a.hdr[H_HIT_BEG], he = a.hdr[H_HIT_END];
   const int lo = max(k * PIECE, hb), hi = min((k + 1) * PIECE, he);
   for (int s = lo; s < hi; ++s) {
-    const int kA = a.s_dA[s], kB = a.s_dB[s];
-    if (s > hb && a.s_dA[s - 1] == kA && a.s_dB[s - 1] == kB) continue;  // not a run start
+    const int4 cur = a.srec[2 * (size_t)s], prev = a.srec[2 * (size_t)max(s - 1, 0)];
+    const int kA = cur.y, kB = cur.z;
+    if (s > hb && prev.y == kA && prev.z == kB) continue;  // not a run start
     const int slot = (kB - a.T * a.p2) * HB + (kA - a.T * a.p1);
     for (int d = lane; d < a.D; d += 64) {
       float acc = a.frag[(size_t)s * a.D + d];
       for (int p = (s / a.P + 1) * a.P; p < he; p += a.P) {
-        if (a.s_dA[p] != kA || a.s_dB[p] != kB) break;
+        const int4 q = a.srec[2 * (size_t)p];
+        if (q.y != kA || q.z != kB) break;
         acc += a.frag[(size_t)p * a.D + d];
       }
       a.crows[(size_t)slot * a.D + d] -= a.lr * acc;
@@ -589,10 +626,10 @@ __global__ __launch_bounds__(256) void k_seg(DevArgs a) {
 }
 
 hipError_t launch_seg(const DevArgs &a, hipStream_t s) {
-  const int nb1 = (a.T * a.p1 + a.T * a.p3 + 3) / 4;
+  const int nseg = a.T * a.p1 + a.T * a.p3;
   const int nbh = a.has_cache ? ((a.nnz + PIECE - 1) / PIECE + 3) / 4 : 0;
   prof_begin(K_SEG, s);
-  hipLaunchKernelGGL(k_seg, dim3(nb1 + a.T * a.p2 + nbh), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_seg, dim3(nseg + a.T * a.p2 + nbh), dim3(SEG_T), 0, s, a);
   prof_end(K_SEG, s);
   return hipGetLastError();
 }

@@ -116,8 +116,9 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
   if (tid < 64) {
     const int s = s0 + min(tid, n_el - 1);
     const bool v = tid < n_el;
-    const int dAv = a.s_dA[s], dIv = a.s_dI3[s], bagv = a.s_bag[s];
-    const float wv = a.s_w[s];
+    const SPos sp = load_spos(a.srec, s);
+    const int dAv = sp.dA, dIv = sp.dI3, bagv = sp.bag;
+    const float wv = sp.w;
     const int dA = v ? dAv : -1, i3 = v ? dIv - t * a.p3 : 0;
     e_bag[tid] = bagv;
     e_w[tid] = wv;

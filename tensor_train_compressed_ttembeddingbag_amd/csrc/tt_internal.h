@@ -76,12 +76,10 @@ struct DevArgs {
   int *hdr;
   int4 *einfo;      // per element: dA (t,i1), dB (t,i2), dI3 (t,i3), bag
   int *histA, *histB, *histI3;
-  int *orderA;      // elements by (t,i1) (stable)
+  int *rec;         // [nnz][8] element records in the (t,i1) order (grouping only)
   int *segI3, *segA;  // first position of each (t,i3) / (t,i1) bin in orderI3 / orderA
-  int *s_n, *s_dA, *s_dB, *s_dI3, *s_bag;
-  float *s_w;       // per-sample weight in the final order (1 without weights)
-  int *posI3_of;    // element -> position in orderI3 (elements by (t,i3), stable)
-  int *s_posI3, *s_posA;     // final position -> position in orderI3 / orderA
+  int4 *srec;       // final order, 2 int4 per position: (element n, dA, dB, dI3),
+                    // (bag, position in orderI3, weight bits, position in orderA)
   int4 *fitem;      // work items: (group, first position, end position, 0)
   int *grp_off;     // [binsB + 1]
   int *chunk_pre;   // [T*p2 + 1]
@@ -91,6 +89,18 @@ struct DevArgs {
 };
 
 // ---------------------------------------------------------------- helpers
+// one position of the final order
+struct SPos {
+  int n, dA, dB, dI3, bag, posI3, posA;
+  float w;
+};
+__device__ __forceinline__ SPos load_spos(const int4 *srec, int s) {
+  const int4 u = srec[2 * (size_t)s], v = srec[2 * (size_t)s + 1];
+  SPos p;
+  p.n = u.x; p.dA = u.y; p.dB = u.z; p.dI3 = u.w;
+  p.bag = v.x; p.posI3 = v.y; p.w = __int_as_float(v.z); p.posA = v.w;
+  return p;
+}
 // floor(k / d) for 0 <= k < 2^16 and 1 <= d <= 2^16 with one high multiply by
 // m = ceil(2^32 / d) (m = 0 stands for d = 1).  Exact: k * m / 2^32 exceeds k / d by
 // less than k / 2^32 < 2^-16 <= 1 / d, which cannot carry it past the next integer.

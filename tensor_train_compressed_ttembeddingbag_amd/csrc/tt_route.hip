@@ -47,29 +47,49 @@ static __device__ __forceinline__ int tile_pos(int blk, int r) {
   return blk * RB + (threadIdx.x >> 6) * 256 + r * 64 + (threadIdx.x & 63);
 }
 
-// Tile decode: bag, digits dA (t,i1), dB (t,i2), dI (t,i3) of the tile's elements (-1 past
-// the end), einfo written, bad indices / slots reported.  Needs LDS s_off
+// Word accesses for data that other blocks of the same launch read after a grid
+// barrier (DEV = true): device-coherent (L2-bypassing) stores and loads, so that the
+// barrier needs no cache write-back.  Plain accesses otherwise (kernel boundaries
+// order them).
+template <bool DEV>
+static __device__ __forceinline__ void st_w(int *p, int v) {
+  if (DEV) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+template <bool DEV>
+static __device__ __forceinline__ int ld_w(const int *p) {
+  if (DEV) return __hip_atomic_load((int *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return *p;
+}
+
+// One element on its way through the passes (a "record": 8 words in the workspace).
+struct Rec {
+  int e, dA, dB, dI, bag, posI3;
+  float w;
+};
+constexpr int REC_WORDS = 8;
+
+static __device__ __forceinline__ void store_rec(int *rec, int pos, const Rec &r) {
+  int4 *q = (int4 *)(rec + (size_t)pos * REC_WORDS);
+  q[0] = make_int4(r.e, r.dA, r.dB, r.dI);
+  q[1] = make_int4(r.bag, r.posI3, __float_as_int(r.w), 0);
+}
+static __device__ __forceinline__ Rec load_rec(const int *rec, int pos) {
+  const int4 *q = (const int4 *)(rec + (size_t)pos * REC_WORDS);
+  const int4 u = q[0], v = q[1];
+  Rec r;
+  r.e = u.x; r.dA = u.y; r.dB = u.z; r.dI = u.w;
+  r.bag = v.x; r.posI3 = v.y; r.w = __int_as_float(v.z);
+  return r;
+}
+
+// Tile decode: bag, digits dA (t,i1), dB (t,i2), dI (t,i3) and weight of the tile's
+// elements (digits -1 past the end); bad indices / slots reported.  Needs LDS s_off
 // [ROUTE_MAX_BAGS], s_red [8], s_b [2].  Whole block.
 static __device__ void tile_decode(const DevArgs &a, int blk, int *s_off, int *s_red, int *s_b,
-                                   int dA[4], int dB[4], int dI[4]) {
+                                   Rec el[4]) {
   const int tid = threadIdx.x;
-  const int base = blk * RB, last = min(base + RB, a.nnz) - 1;
-  // bags overlapping [base, last]: one 128-ary search per half of the block (lockstep)
-  {
-    const int half = tid >> 7;
-    const int b = half_find_bag(a.off, a.NB, half ? last : base, half, s_red);
-    if ((tid & 127) == 0) s_b[half] = b;
-  }
-  __syncthreads();
-  const int b_lo = s_b[0], b_hi = max(s_b[1], s_b[0]);
-  const int nbag = b_hi - b_lo + 1;
-  const bool in_lds = nbag + 1 <= ROUTE_MAX_BAGS;
-  if (in_lds)
-    for (int j = tid; j <= nbag; j += RT) {
-      const int64_t o = a.off[b_lo + j];
-      s_off[j] = (int)(o < 0 ? 0 : (o > a.nnz ? a.nnz : o));
-    }
-  __syncthreads();
+  // the element loads first: they do not depend on the bags
   int64_t iv[4];
   int sv[4];
 #pragma unroll
@@ -81,7 +101,36 @@ static __device__ void tile_decode(const DevArgs &a, int blk, int *s_off, int *s
 #pragma unroll
     for (int r = 0; r < 4; ++r) sv[r] = -1;
   }
-  // bag = last b with off[b] <= e: binary lifting over the tile's offsets, the four
+  if (a.psw) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) el[r].w = a.psw[min(tile_pos(blk, r), a.nnz - 1)];
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) el[r].w = 1.f;
+  }
+  // the bags that may hold the tile's positions: all of them when their offsets fit in
+  // LDS, else the ones overlapping the tile (one 128-ary search per half of the block)
+  int b_lo = 0, nbag = a.NB;
+  if (a.NB + 1 > ROUTE_MAX_BAGS) {
+    const int base = blk * RB, last = min(base + RB, a.nnz) - 1;
+    const int half = tid >> 7;
+    const int b = half_find_bag(a.off, a.NB, half ? last : base, half, s_red);
+    if ((tid & 127) == 0) s_b[half] = b;
+    __syncthreads();
+    b_lo = s_b[0];
+    nbag = max(s_b[1], s_b[0]) - b_lo + 1;
+  }
+  const bool in_lds = nbag + 1 <= ROUTE_MAX_BAGS;
+  if (in_lds) {  // ROUTE_MAX_BAGS / RT = 8 loads per thread, all in flight
+    int64_t o[ROUTE_MAX_BAGS / RT];
+#pragma unroll
+    for (int u = 0; u < ROUTE_MAX_BAGS / RT; ++u) o[u] = a.off[b_lo + min(tid + u * RT, nbag)];
+#pragma unroll
+    for (int u = 0; u < ROUTE_MAX_BAGS / RT; ++u)
+      if (tid + u * RT <= nbag) s_off[tid + u * RT] = (int)(o[u] < 0 ? 0 : (o[u] > a.nnz ? a.nnz : o[u]));
+  }
+  __syncthreads();
+  // bag = last b with off[b] <= e: binary lifting over the offsets in LDS, the four
   // elements in lockstep (or a search in global memory for tiles of very many bags)
   int bag[4];
   if (in_lds) {
@@ -108,32 +157,34 @@ static __device__ void tile_decode(const DevArgs &a, int blk, int *s_off, int *s
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int e = tile_pos(blk, r);
-    dA[r] = dB[r] = dI[r] = -1;
+    Rec &x = el[r];
+    x.e = e;
+    x.bag = bag[r];
+    x.posI3 = -1;
+    x.dA = x.dB = x.dI = -1;
     if (e >= a.nnz) continue;
-    const int b = bag[r];
-    const int t = a.T == 1 ? 0 : b / a.B;
+    const int t = a.T == 1 ? 0 : bag[r] / a.B;
     const int slot = sv[r];
     const int64_t i = iv[r];
     if (slot >= 0) {
       if (slot >= a.cache_size) {
         bad_slot = true;
-        dA[r] = dropA; dB[r] = dropB; dI[r] = dropI;
+        x.dA = dropA; x.dB = dropB; x.dI = dropI;
       } else {
-        dA[r] = a.T * a.p1 + slot % HB;
-        dB[r] = a.T * a.p2 + slot / HB;
-        dI[r] = dropI;
+        x.dA = a.T * a.p1 + slot % HB;
+        x.dB = a.T * a.p2 + slot / HB;
+        x.dI = dropI;
       }
     } else if (i < 0 || i >= a.E) {
       bad_index = true;
-      dA[r] = dropA; dB[r] = dropB; dI[r] = dropI;
+      x.dA = dropA; x.dB = dropB; x.dI = dropI;
     } else {
       int i1, i2, i3;
       split_index(i, a.p3, p23, a.rp23, a.rp3, i1, i2, i3);
-      dA[r] = t * a.p1 + i1;
-      dB[r] = t * a.p2 + i2;
-      dI[r] = t * a.p3 + i3;
+      x.dA = t * a.p1 + i1;
+      x.dB = t * a.p2 + i2;
+      x.dI = t * a.p3 + i3;
     }
-    a.einfo[e] = make_int4(dA[r], dB[r], dI[r], b);
   }
   if (bad_slot) set_status(a.status, TT_DEV_BAD_SLOT);
   if (bad_index) set_status(a.status, TT_DEV_BAD_INDEX);
@@ -149,7 +200,9 @@ static __device__ void check_offsets(const DevArgs &a, int blk) {
   }
 }
 
-// Tile histogram of digit d into column blk of the [bin][tile] matrix hist.
+// Tile histogram of digit d; column blk of the [bin][tile] matrix (TILE_MAJOR false)
+// or row blk of the [tile][bin] matrix (true).
+template <bool DEV, bool TILE_MAJOR>
 static __device__ void tile_hist(const int d[4], int *lds_h, int nb, int *hist, int blk) {
   const int tid = threadIdx.x;
   for (int i = tid; i < nb; i += RT) lds_h[i] = 0;
@@ -158,7 +211,9 @@ static __device__ void tile_hist(const int d[4], int *lds_h, int nb, int *hist, 
   for (int r = 0; r < 4; ++r)
     if (d[r] >= 0) atomicAdd(&lds_h[d[r]], 1);
   __syncthreads();
-  for (int i = tid; i < nb; i += RT) hist[(size_t)i * gridDim.x + blk] = lds_h[i];
+  for (int i = tid; i < nb; i += RT)
+    st_w<DEV>(TILE_MAJOR ? hist + (size_t)blk * nb + i : hist + (size_t)i * gridDim.x + blk,
+              lds_h[i]);
 }
 
 // Stable ranks of the tile's elements by digit d (order: position) and their output
@@ -201,45 +256,47 @@ static __device__ void build_items(const DevArgs &a, const int *gs, int *cnt, in
   }
 }
 
-// Final pass of a tile of orderA: the elements' data gathered, placed by (t,i2).
-static __device__ void tile_final(const DevArgs &a, int blk, unsigned short *lds_c,
-                                  const int *start, int ss, int so) {
-  int e[4], d[4], pos[4], pI[4];
-  int4 info[4];
-  float wv[4];
+// orderI3 / orderA places of the tile's elements (from their bin starts); the records
+// go to their orderA positions.  Returns the orderA positions (-1: none).
+static __device__ void tile_place_ia(const DevArgs &a, Rec el[4], int pA[4], unsigned short *lds_c,
+                                     const int *startI, const int *startA, int ss, int so) {
+  int d[4], pI[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) e[r] = a.orderA[min(tile_pos(blk, r), a.nnz - 1)];
+  for (int r = 0; r < 4; ++r) d[r] = el[r].dI;
+  tile_place(d, pI, lds_c, a.binsI3, startI, ss, so);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) d[r] = el[r].dA;
+  tile_place(d, pA, lds_c, a.binsA, startA, ss, so);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    info[r] = a.einfo[e[r]];
-    pI[r] = a.posI3_of[e[r]];
+    if (pA[r] < 0) continue;
+    el[r].posI3 = pI[r];
+    store_rec(a.rec, pA[r], el[r]);
   }
-  if (a.psw) {
+}
+
+// Final pass of a tile of orderA: its records placed by (t,i2) into the final order.
+static __device__ void tile_final(const DevArgs &a, int blk, unsigned short *lds_c,
+                                  const int *start, int ss, int so) {
+  Rec x[4];
+  int d[4], pos[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) wv[r] = a.psw[e[r]];
-  } else {
+  for (int r = 0; r < 4; ++r) x[r] = load_rec(a.rec, min(tile_pos(blk, r), a.nnz - 1));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) wv[r] = 1.f;
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) d[r] = tile_pos(blk, r) < a.nnz ? info[r].y : -1;
+  for (int r = 0; r < 4; ++r) d[r] = tile_pos(blk, r) < a.nnz ? x[r].dB : -1;
   tile_place(d, pos, lds_c, a.binsB, start, ss, so);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     if (pos[r] < 0) continue;
     const int p = pos[r];
-    a.s_n[p] = e[r];
-    a.s_dA[p] = info[r].x;
-    a.s_dB[p] = info[r].y;
-    a.s_dI3[p] = info[r].z;
-    a.s_bag[p] = info[r].w;
-    a.s_w[p] = wv[r];
-    a.s_posI3[p] = pI[r];
-    a.s_posA[p] = tile_pos(blk, r);
+    a.srec[2 * (size_t)p] = make_int4(x[r].e, x[r].dA, x[r].dB, x[r].dI);
+    a.srec[2 * (size_t)p + 1] = make_int4(x[r].bag, x[r].posI3, __float_as_int(x[r].w),
+                                          tile_pos(blk, r));
   }
 }
 
-// ---------------------------------------------------------------- cooperative path
+// ---------------------------------------------------------------- one-launch path
 constexpr int COOP_TILES = 256;        // blocks of one barrier launch (and at most one per CU)
 constexpr int COOP_BINS = 2048;        // bins per digit
 constexpr int COOP_CELLS = 12288;      // bins x tiles per digit (each block reads them all)
@@ -257,18 +314,25 @@ static int device_cus() {
 }
 
 static bool coop_route_ok(const DevArgs &a) {
-  return a.nblk <= COOP_TILES && a.nblk <= device_cus() && a.binsA <= COOP_BINS && a.binsB <= COOP_BINS &&
-         a.binsI3 <= COOP_BINS && (int64_t)a.binsA * a.nblk <= COOP_CELLS &&
-         (int64_t)a.binsB * a.nblk <= COOP_CELLS && (int64_t)a.binsI3 * a.nblk <= COOP_CELLS;
+  return a.nblk <= COOP_TILES && a.nblk <= device_cus() && a.binsA <= COOP_BINS &&
+         a.binsB <= COOP_BINS && a.binsI3 <= COOP_BINS &&
+         (int64_t)a.binsA * a.nblk <= COOP_CELLS && (int64_t)a.binsB * a.nblk <= COOP_CELLS &&
+         (int64_t)a.binsI3 * a.nblk <= COOP_CELLS;
 }
 
-// All blocks of the cooperative launch meet here (k-th barrier: target k * nblk).  The
-// counter holds (epoch << 32 | arrivals); a word of another call counts as zero.  The
-// wait is bounded: a block that gives up reports TT_DEV_SYNC_TIMEOUT and returns false
-// (its caller then leaves the kernel; nothing of the plan is marked valid).
+// All blocks of the launch meet here (k-th barrier: target k * nblk).  Data crossing
+// the barrier is either written with device-coherent stores or atomics, complete
+// before the block arrives (FENCE = false), or made visible by device-scope fences
+// around the barrier (FENCE = true: plain stores and loads, at the price of an L2
+// write-back).  The counter holds (epoch << 32 | arrivals); a word of another call
+// counts as zero.  The wait is bounded: a block that gives up reports
+// TT_DEV_SYNC_TIMEOUT and returns false (its caller leaves the kernel; no plan is
+// marked valid).
+template <bool FENCE>
 static __device__ bool grid_sync(const DevArgs &a, unsigned target) {
   __shared__ int s_ok;
-  __threadfence();
+  if (FENCE) __threadfence();
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
     unsigned long long *ctr = &a.ctr[0];
@@ -290,99 +354,160 @@ static __device__ bool grid_sync(const DevArgs &a, unsigned target) {
         set_status(a.status, TT_DEV_SYNC_TIMEOUT);
         break;
       }
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(1);
     }
     s_ok = ok;
   }
   __syncthreads();
-  __threadfence();
+  if (FENCE) __threadfence();
   return s_ok != 0;
 }
 
-// Per-tile bin starts from the [bin][tile] count matrix hist (read whole by every
-// block): start[d] = (elements in smaller bins) + (elements of bin d in tiles < blk);
-// gsum[d] = the global bin starts.  LDS arrays of nb (+1) ints.
-static __device__ void tile_starts(const int *hist, int nb, int blk, int *start, int *gsum,
-                                   int *s_scan) {
-  const int nblk = gridDim.x;
-  for (int d = threadIdx.x; d < nb; d += RT) {
-    const int *row = hist + (size_t)d * nblk;
-    int tot = 0, pre = 0;
-    for (int t0 = 0; t0 < nblk; t0 += 8) {
-      int v[8];
+// Per-tile bin starts of two digits from their [tile][bin] count matrices (read whole
+// by every block): start[d] = (elements in smaller bins) + (elements of bin d in tiles
+// < blk); gsum[d] = the global bin starts.  LDS arrays of nb (+1) ints.  Thread t sums
+// the columns of bins t, t + RT, ... over 16 tiles per round of loads (all in flight);
+// the exclusive scan over bins then runs on contiguous runs of the LDS totals.
+constexpr int SCAN_TCH = 16;
+constexpr int SCAN_H = 2 * 2048 / RT;  // bins of both digits per thread (<= 16)
+static __device__ void tile_starts2(const int *h0, int nb0, int *start0, int *gs0, const int *h1,
+                                   int nb1, int *start1, int *gs1, int blk, int *s_scan) {
+  const int nblk = gridDim.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nbt = nb0 + nb1, nh = (nbt + RT - 1) / RT;
+  for (int h0i = 0; h0i < nh; h0i += 2) {  // two bins per thread per round
+    int tot[2] = {0, 0}, pre[2] = {0, 0};
+    for (int t0 = 0; t0 < nblk; t0 += SCAN_TCH) {
+      int v[2][SCAN_TCH];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = row[min(t0 + u, nblk - 1)];
+      for (int h = 0; h < 2; ++h) {
+        const int j = min(tid + (h0i + h) * RT, nbt - 1);
+        const bool first = j < nb0;
+        const int *col = first ? h0 + j : h1 + (j - nb0);
+        const int nb = first ? nb0 : nb1;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int t = t0 + u;
-        tot += t < nblk ? v[u] : 0;
-        pre += t < blk ? v[u] : 0;
+        for (int u = 0; u < SCAN_TCH; ++u)
+          v[h][u] = ld_w<true>(col + (size_t)min(t0 + u, nblk - 1) * nb);
       }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int u = 0; u < SCAN_TCH; ++u) {
+          const int t = t0 + u;
+          tot[h] += t < nblk ? v[h][u] : 0;
+          pre[h] += t < blk ? v[h][u] : 0;
+        }
     }
-    start[d] = pre;
-    gsum[d] = tot;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = tid + (h0i + h) * RT;
+      if (j < nb0) { gs0[j] = tot[h]; start0[j] = pre[h]; }
+      else if (j < nbt) { gs1[j - nb0] = tot[h]; start1[j - nb0] = pre[h]; }
+    }
   }
   __syncthreads();
-  block_exclusive_scan(gsum, nb, s_scan);
-  for (int d = threadIdx.x; d < nb; d += RT) start[d] += gsum[d];
+  // exclusive scans over the bins of each digit, on contiguous runs per thread
+  const int per = (nbt + RT - 1) / RT;
+  int run0 = 0, run1 = 0;
+  for (int k = 0; k < per; ++k) {
+    const int j = tid * per + k;
+    if (j < nb0) run0 += gs0[j];
+    else if (j < nbt) run1 += gs1[j - nb0];
+  }
+  int x0 = run0, x1 = run1;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y0 = __shfl_up(x0, o), y1 = __shfl_up(x1, o);
+    if (lane >= o) { x0 += y0; x1 += y1; }
+  }
+  if (lane == 63) { s_scan[w] = x0; s_scan[RT / 64 + w] = x1; }
+  __syncthreads();
+  int b0 = x0 - run0, b1 = x1 - run1;
+  for (int v = 0; v < w; ++v) { b0 += s_scan[v]; b1 += s_scan[RT / 64 + v]; }
+  for (int k = 0; k < per; ++k) {
+    const int j = tid * per + k;
+    if (j < nb0) {
+      const int c = gs0[j];
+      gs0[j] = b0;
+      start0[j] += b0;
+      b0 += c;
+    } else if (j < nbt) {
+      const int c = gs1[j - nb0];
+      gs1[j - nb0] = b1;
+      start1[j - nb0] += b1;
+      b1 += c;
+    }
+  }
   __syncthreads();
 }
 
-// LDS of the cooperative kernel (ints), phases overlap:
-//   decode:  s_off [ROUTE_MAX_BAGS] | hist [max bins]
-//   passes:  lds_c (u16 4 x bins) [2 * COOP_BINS] | startI, gsI, startA, gsA [COOP_BINS + 1]
-//            each | (t,i2) cells [COOP_CELLS]
-constexpr int COOP_LDS_INTS = 2 * COOP_BINS + 4 * (COOP_BINS + 1) + COOP_CELLS;
+// LDS of the one-launch kernel (ints, sized by the call's bins and tiles), phases overlap:
+//   decode:  s_off [ROUTE_MAX_BAGS] | hist [max(binsI3, binsA)]
+//   passes:  rank counts (u16 4 x bins) | startI, gsI | startA, gsA | (t,i2) cells
+struct CoopLds {
+  int c, sI, gI, sA, gA, cell, total;
+};
+__host__ __device__ inline CoopLds coop_lds(const DevArgs &a) {
+  const int mb = max(a.binsI3, max(a.binsA, a.binsB));
+  const int nX = max(a.binsI3, a.binsB) + 1, nY = max(a.binsA, a.binsB) + 1;
+  CoopLds L;
+  L.c = 0;
+  L.sI = 2 * mb;
+  L.gI = L.sI + nX;
+  L.sA = L.gI + nX;
+  L.gA = L.sA + nY;
+  L.cell = L.gA + nY;
+  L.total = max(L.cell + a.binsB * a.nblk, ROUTE_MAX_BAGS + max(a.binsI3, a.binsA));
+  return L;
+}
 
 __global__ __launch_bounds__(RT) void k_route_coop(DevArgs a) {
   extern __shared__ int lds_i[];
-  __shared__ int s_scan[RT / 64 + 1];
+  __shared__ int s_scan[2 * (RT / 64) + 1];
   __shared__ int s_red[8];
   __shared__ int s_b[2];
   const int tid = threadIdx.x, blk = blockIdx.x, nblk = gridDim.x;
-  unsigned short *lds_c = (unsigned short *)lds_i;   // [4][bins] rank counts
-  int *startI = lds_i + 2 * COOP_BINS, *gsI = startI + COOP_BINS + 1;
-  int *startA = gsI + COOP_BINS + 1, *gsA = startA + COOP_BINS + 1;
-  int *cellB = gsA + COOP_BINS + 1;  // [binsB][nblk] (t,i2) counts of the orderA tiles
-  int dA[4], dB[4], dI[4];
+  const CoopLds L = coop_lds(a);
+  unsigned short *lds_c = (unsigned short *)(lds_i + L.c);  // [4][bins] rank counts
+  int *startI = lds_i + L.sI, *gsI = lds_i + L.gI, *startA = lds_i + L.sA, *gsA = lds_i + L.gA;
+  int *cellB = lds_i + L.cell;  // [binsB][nblk] (t,i2) counts of the orderA tiles
+  Rec el[4];
 
   // ---- decode; (t,i3) and (t,i1) histograms of the tile; histB cleared for the atomics
-  tile_decode(a, blk, lds_i, s_red, s_b, dA, dB, dI);
+  tile_decode(a, blk, lds_i, s_red, s_b, el);
   check_offsets(a, blk);
-  for (int k = blk * RT + tid; k < a.binsB * nblk; k += nblk * RT) a.histB[k] = 0;
-  tile_hist(dI, lds_i + ROUTE_MAX_BAGS, a.binsI3, a.histI3, blk);
-  __syncthreads();
-  tile_hist(dA, lds_i + ROUTE_MAX_BAGS, a.binsA, a.histA, blk);
-  if (!grid_sync(a, nblk)) return;
+  for (int k = blk * RT + tid; k < a.binsB * nblk; k += nblk * RT) st_w<true>(a.histB + k, 0);
+  {
+    int d[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) d[r] = el[r].dI;
+    tile_hist<true, true>(d, lds_i + ROUTE_MAX_BAGS, a.binsI3, a.histI3, blk);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) d[r] = el[r].dA;
+    tile_hist<true, true>(d, lds_i + ROUTE_MAX_BAGS, a.binsA, a.histA, blk);
+  }
+  if (!grid_sync<false>(a, nblk)) return;
 
-  // ---- orderI3 and orderA: stable places by (t,i3) and (t,i1); the (t,i2) counts of
-  //      the orderA tiles gathered per block in LDS, then added to histB
-  tile_starts(a.histI3, a.binsI3, blk, startI, gsI, s_scan);
-  tile_starts(a.histA, a.binsA, blk, startA, gsA, s_scan);
+  // ---- orderI3 / orderA places; the (t,i2) counts of the orderA tiles gathered per
+  //      block in LDS, then added to histB
+  tile_starts2(a.histI3, a.binsI3, startI, gsI, a.histA, a.binsA, startA, gsA, blk, s_scan);
   if (blk == 0) {
     for (int d = tid; d < a.binsI3; d += RT) a.segI3[d] = gsI[d];
     for (int d = tid; d < a.binsA; d += RT) a.segA[d] = gsA[d];
   }
   for (int i = tid; i < a.binsB * nblk; i += RT) cellB[i] = 0;
-  int pI[4], pA[4];
-  tile_place(dI, pI, lds_c, a.binsI3, startI, 1, 0);
-  __syncthreads();
-  tile_place(dA, pA, lds_c, a.binsA, startA, 1, 0);
+  int pA[4];
+  tile_place_ia(a, el, pA, lds_c, startI, startA, 1, 0);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if (pA[r] < 0) continue;
-    const int e = tile_pos(blk, r);
-    a.posI3_of[e] = pI[r];
-    a.orderA[pA[r]] = e;
-    atomicAdd(&cellB[dB[r] * nblk + pA[r] / RB], 1);
-  }
+  for (int r = 0; r < 4; ++r)
+    if (pA[r] >= 0) atomicAdd(&cellB[el[r].dB * nblk + pA[r] / RB], 1);
   __syncthreads();
   for (int i = tid; i < a.binsB * nblk; i += RT)
-    if (cellB[i]) atomicAdd(&a.histB[i], cellB[i]);
-  if (!grid_sync(a, 2 * nblk)) return;
+    if (cellB[i]) atomicAdd(&a.histB[(i % nblk) * a.binsB + i / nblk], cellB[i]);
+  if (!grid_sync<true>(a, 2 * nblk)) return;
 
   // ---- final order: the orderA tiles placed by (t,i2); block 0 builds the work items
-  tile_starts(a.histB, a.binsB, blk, startI, gsI, s_scan);
+  tile_starts2(a.histB, a.binsB, startI, gsI, nullptr, 0, nullptr, nullptr, blk, s_scan);
   tile_final(a, blk, lds_c, startI, 1, 0);
   if (blk == 0) {
     if (tid == 0) gsI[a.binsB] = a.nnz;
@@ -403,48 +528,53 @@ __global__ __launch_bounds__(RT) void k_route_a(DevArgs a) {
   __shared__ int s_red[8];
   __shared__ int s_b[2];
   const int blk = blockIdx.x, tid = threadIdx.x;
-  int dA[4], dB[4], dI[4];
-  tile_decode(a, blk, lds_i, s_red, s_b, dA, dB, dI);
+  Rec el[4];
+  tile_decode(a, blk, lds_i, s_red, s_b, el);
   check_offsets(a, blk);
   for (int k = blk * RT + tid; k < a.binsB * a.nblk; k += a.nblk * RT) a.histB[k] = 0;
-  tile_hist(dI, lds_i + ROUTE_MAX_BAGS, a.binsI3, a.histI3, blk);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (el[r].e < a.nnz) a.einfo[el[r].e] = make_int4(el[r].dA, el[r].dB, el[r].dI, el[r].bag);
+  int d[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) d[r] = el[r].dI;
+  tile_hist<false, false>(d, lds_i + ROUTE_MAX_BAGS, a.binsI3, a.histI3, blk);
   __syncthreads();
-  tile_hist(dA, lds_i + ROUTE_MAX_BAGS, a.binsA, a.histA, blk);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) d[r] = el[r].dA;
+  tile_hist<false, false>(d, lds_i + ROUTE_MAX_BAGS, a.binsA, a.histA, blk);
   if (!last_block(&a.ctr[0], a.nblk, a.epoch)) return;
   block_exclusive_scan(a.histI3, a.binsI3 * a.nblk, s_scan);
   block_exclusive_scan(a.histA, a.binsA * a.nblk, s_scan);
-  for (int d = tid; d < a.binsI3; d += RT) a.segI3[d] = a.histI3[(size_t)d * a.nblk];
-  for (int d = tid; d < a.binsA; d += RT) a.segA[d] = a.histA[(size_t)d * a.nblk];
+  for (int k = tid; k < a.binsI3; k += RT) a.segI3[k] = a.histI3[(size_t)k * a.nblk];
+  for (int k = tid; k < a.binsA; k += RT) a.segA[k] = a.histA[(size_t)k * a.nblk];
 }
 
-// k_route_b: orderI3 / orderA places of the tile; (t,i2) counts over the orderA tiles;
-// the last block scans them and builds the group table and the work items.
+// k_route_b: orderI3 / orderA places of the tile (records to orderA); (t,i2) counts
+// over the orderA tiles; the last block scans them and builds the group table and the
+// work items.
 __global__ __launch_bounds__(RT) void k_route_b(DevArgs a) {
   extern __shared__ unsigned short lds_c[];  // [4][max(binsI3, binsA)]
   __shared__ int s_scan[RT / 64 + 1];
   const int blk = blockIdx.x;
-  int dA[4], dB[4], dI[4];
+  Rec el[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int e = tile_pos(blk, r);
-    const int4 info = a.einfo[min(e, a.nnz - 1)];
+    const int e = tile_pos(blk, r), ec = min(e, a.nnz - 1);
+    const int4 info = a.einfo[ec];
     const bool v = e < a.nnz;
-    dA[r] = v ? info.x : -1;
-    dB[r] = v ? info.y : -1;
-    dI[r] = v ? info.z : -1;
+    el[r].e = e;
+    el[r].dA = v ? info.x : -1;
+    el[r].dB = v ? info.y : -1;
+    el[r].dI = v ? info.z : -1;
+    el[r].bag = info.w;
+    el[r].w = a.psw ? a.psw[ec] : 1.f;
   }
-  int pI[4], pA[4];
-  tile_place(dI, pI, lds_c, a.binsI3, a.histI3, a.nblk, blk);
-  __syncthreads();
-  tile_place(dA, pA, lds_c, a.binsA, a.histA, a.nblk, blk);
+  int pA[4];
+  tile_place_ia(a, el, pA, lds_c, a.histI3, a.histA, a.nblk, blk);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if (pA[r] < 0) continue;
-    const int e = tile_pos(blk, r);
-    a.posI3_of[e] = pI[r];
-    a.orderA[pA[r]] = e;
-    atomicAdd(&a.histB[(size_t)dB[r] * a.nblk + pA[r] / RB], 1);
-  }
+  for (int r = 0; r < 4; ++r)
+    if (pA[r] >= 0) atomicAdd(&a.histB[(size_t)el[r].dB * a.nblk + pA[r] / RB], 1);
   if (!last_block(&a.ctr[1], a.nblk, a.epoch)) return;
   block_exclusive_scan(a.histB, a.binsB * a.nblk, s_scan);
   for (int d = threadIdx.x; d < a.binsB; d += RT) a.grp_off[d] = a.histB[(size_t)d * a.nblk];
@@ -508,8 +638,9 @@ __global__ __launch_bounds__(RT) void k_runsum(DevArgs a) {
   if (beg >= V || beg + PIECE <= a.hdr[H_HIT_BEG]) return;
   const int len = min(PIECE, V - beg);
   const int s = beg + min(lane, len - 1);
-  const int kA = a.s_dA[s], kB = a.s_dB[s], kI = a.s_dI3[s], bag = a.s_bag[s];
-  const float wt = lane < len ? a.s_w[s] : 0.f;
+  const SPos sp = load_spos(a.srec, s);
+  const int kA = sp.dA, kB = sp.dB, kI = sp.dI3, bag = sp.bag;
+  const float wt = lane < len ? sp.w : 0.f;
   const int pA = __shfl_up(kA, 1), pB = __shfl_up(kB, 1), pI = __shfl_up(kI, 1);
   // fragments start at run starts and at every multiple of P (work item boundaries)
   const unsigned long long starts = __ballot(
@@ -540,12 +671,13 @@ __global__ __launch_bounds__(RT) void k_runsum(DevArgs a) {
 hipError_t launch_route(const DevArgs &a, hipStream_t s) {
   if (a.nblk == 0) return hipGetLastError();
   if (coop_route_ok(a)) {
-    static bool attr_set = false;  // dynamic LDS above 64 KiB is opt-in per kernel
-    const size_t lds = (size_t)COOP_LDS_INTS * 4;
-    if (!attr_set) {
-      (void)hipFuncSetAttribute((const void *)k_route_coop,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      attr_set = true;
+    static size_t attr_lds = 64 * 1024;  // dynamic LDS above 64 KiB is opt-in per kernel
+    const size_t lds = (size_t)coop_lds(a).total * 4;
+    if (lds > attr_lds) {
+      const hipError_t e = hipFuncSetAttribute((const void *)k_route_coop,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      attr_lds = lds;
     }
     // One block per CU at most (LDS), launched on an otherwise idle stream position:
     // every block is resident at once.  The barriers are bounded waits in any case.
