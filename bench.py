@@ -43,7 +43,21 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle baseline (0 = skip)")
     ap.add_argument("--no-roofline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run device copies of BYTES (counter calibration) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes, torch):
+    """Plain device-to-device copies of a known size: what FETCH_SIZE / WRITE_SIZE read
+    for them turns the counters of the library's kernels into HBM bytes."""
+    n = nbytes // 4
+    src = torch.rand(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4, "copies": 5}), flush=True)
 
 
 def _dev(batch, torch):
@@ -69,6 +83,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, torch)
+        return
     abi.lib()
     wl = W.WORKLOADS[args.workload]
     cores = W.make_cores(wl)
@@ -185,18 +202,29 @@ def roofline(args, wl, batches, step, torch, abi, metrics, slots):
     work = {"k_bwd": metrics.bwd_kernel_flops(wl.q, wl.ranks, N, U),
             "k_fwd": metrics.fwd_kernel_flops(wl.q, wl.ranks, N, U)}
     avg_s = kernels[dom]["avg_us"] * 1e-6
+    from tensor_train_compressed_ttembeddingbag_amd import profiling
+    traffic = profiling.read_traffic(
+        os.path.join(ROOT, "profiles", "%s_%s_traffic.txt" % (dom, args.workload)), dom)
     if dom in work:
         ach = work[dom] / avg_s / 1e12
         rf = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 3),
               "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-              "frac": round(ach / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": None,
+              "frac": round(ach / PEAK_FP32_MFMA_TFLOPS, 4),
+              "traffic": None if traffic is None else round(traffic),
               "work_per_launch": "%.4g flop (2*F1 per distinct (i1,i2) pair x %.1f pairs + "
                                  "2*F2 per element x %.1f elements)" % (work[dom], U, N)
               if dom == "k_bwd" else "%.4g flop (F1 x %.1f pairs + F2 x %.1f elements)"
                                      % (work[dom], U, N)}
     else:
-        rf = {"bound": "hbm", "kernel": dom, "achieved": None, "peak": PEAK_HBM_GBS,
-              "unit": "GB/s", "frac": None, "traffic": None}
+        # grouping / pooling kernels: algorithmic bytes of the whole grouping step
+        NZ = float(np.mean([batches[i % len(batches)]["indices"].numel() for i in range(nsteps)]))
+        nbytes = metrics.route_bytes(NZ, wl.num_tables * wl.bags_per_table, wl.weighted,
+                                     slots is not None)
+        ach = nbytes / avg_s / 1e9
+        rf = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 3), "peak": PEAK_HBM_GBS,
+              "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 6),
+              "traffic": None if traffic is None else round(traffic),
+              "work_per_launch": "%.4g bytes (grouping of %.0f elements)" % (nbytes, NZ)}
     for k in ("k_fwd", "k_bwd"):
         if k in kernels:
             kernels[k]["tflops"] = round(work[k] / (kernels[k]["avg_us"] * 1e-6) / 1e12, 3)

@@ -456,9 +456,7 @@ static hipError_t launch_bwd_t(const DevArgs &a, size_t lds, hipStream_t s) {
                               160 * 1024);
     attr_set = true;
   }
-  prof_begin(K_BWD, s);
-  hipLaunchKernelGGL(k_bwd<RP>, dim3(items_max(a)), dim3(WG), lds, s, a);
-  prof_end(K_BWD, s);
+  tt_launch(K_BWD, k_bwd<RP>, dim3(items_max(a)), dim3(WG), lds, s, a);
   return hipGetLastError();
 }
 
@@ -628,9 +626,7 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
 hipError_t launch_seg(const DevArgs &a, hipStream_t s) {
   const int nseg = a.T * a.p1 + a.T * a.p3;
   const int nbh = a.has_cache ? ((a.nnz + PIECE - 1) / PIECE + 3) / 4 : 0;
-  prof_begin(K_SEG, s);
-  hipLaunchKernelGGL(k_seg, dim3(nseg + a.T * a.p2 + nbh), dim3(SEG_T), 0, s, a);
-  prof_end(K_SEG, s);
+  tt_launch(K_SEG, k_seg, dim3(nseg + a.T * a.p2 + nbh), dim3(SEG_T), 0, s, a);
   return hipGetLastError();
 }
 

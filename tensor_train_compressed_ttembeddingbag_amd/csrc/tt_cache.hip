@@ -178,10 +178,8 @@ hipError_t cache_lookup_launch(const int64_t *idx, int nnz, int64_t E, long long
                                long long M, int32_t *slot_out, int count_freq, int32_t *status,
                                hipStream_t s) {
   if (nnz > 0) {
-    prof_begin(K_CACHE_LOOKUP, s);
-    hipLaunchKernelGGL(k_cache_lookup, dim3((nnz + 255) / 256), dim3(256), 0, s, idx, nnz, E,
+    tt_launch(K_CACHE_LOOKUP, k_cache_lookup, dim3((nnz + 255) / 256), dim3(256), 0, s, idx, nnz, E,
                        hkeys, hcnt, H, mkeys, mslot, M, slot_out, count_freq, status);
-    prof_end(K_CACHE_LOOKUP, s);
   }
   return hipGetLastError();
 }

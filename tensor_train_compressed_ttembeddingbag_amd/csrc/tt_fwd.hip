@@ -295,9 +295,7 @@ static hipError_t launch_fwd_t(const DevArgs &a, size_t lds, hipStream_t s) {
     attr_set = true;
   }
   const int grid = items_max(a);
-  prof_begin(K_FWD, s);
-  hipLaunchKernelGGL(k_fwd<RP>, dim3(grid), dim3(WG), lds, s, a);
-  prof_end(K_FWD, s);
+  tt_launch(K_FWD, k_fwd<RP>, dim3(grid), dim3(WG), lds, s, a);
   return hipGetLastError();
 }
 

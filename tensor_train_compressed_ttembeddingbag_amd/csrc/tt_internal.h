@@ -12,6 +12,7 @@
 //             k_bwd         one workgroup per work item.
 //             k_seg         core-1 / core-3 segment sums + SGD; cache-row SGD.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -126,8 +127,17 @@ enum KernelId {
   K_ROUTE_COOP, K_ROUTE_A, K_ROUTE_B, K_ROUTE_C, K_FWD, K_RUNSUM, K_BWD, K_SEG,
   K_CACHE_LOOKUP, K_YINIT, K_COUNT
 };
-void prof_begin(int id, hipStream_t s);
-void prof_end(int id, hipStream_t s);
+// Start / stop events for one launch of kernel `id`, recorded by the kernel's own
+// dispatch (so they time the kernel alone), or null events while timing is off.
+void prof_events(int id, hipEvent_t *start, hipEvent_t *stop);
+
+template <typename... KArgs, typename... Args>
+inline void tt_launch(int id, void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds,
+                      hipStream_t s, Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  prof_events(id, &e0, &e1);
+  hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, e0, e1, 0u, args...);
+}
 
 // host launchers (each kernel is launched from the file that defines it)
 hipError_t launch_route(const DevArgs &a, hipStream_t s);   // the grouping kernels

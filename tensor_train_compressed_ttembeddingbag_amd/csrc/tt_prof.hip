@@ -1,6 +1,7 @@
 // tt_prof.hip -- optional per-kernel timing: while enabled, every kernel the
-// library enqueues is bracketed by a pair of HIP events recorded on the stream it
-// is launched on; tt_profile_read waits for the events and sums the elapsed times.
+// library enqueues is launched with a pair of HIP events that its own dispatch
+// records at the kernel's start and end (hipExtLaunchKernelGGL); tt_profile_read
+// waits for the events and sums the elapsed times.
 #include <mutex>
 #include <vector>
 
@@ -20,7 +21,6 @@ std::vector<Rec> g_pending;
 std::vector<hipEvent_t> g_pool;
 double g_ms[K_COUNT] = {0};
 long long g_n[K_COUNT] = {0};
-hipEvent_t g_open[K_COUNT] = {nullptr};
 
 const char *g_names[K_COUNT] = {"k_route_coop", "k_route_a", "k_route_b", "k_route_c",
                                 "k_fwd", "k_runsum", "k_bwd", "k_seg", "k_cache_lookup",
@@ -52,21 +52,15 @@ void drain() {
 
 }  // namespace
 
-void prof_begin(int id, hipStream_t s) {
+void prof_events(int id, hipEvent_t *start, hipEvent_t *stop) {
+  *start = *stop = nullptr;
   if (!g_on) return;
   std::lock_guard<std::mutex> lk(g_mu);
-  hipEvent_t e = take();
-  if (e && hipEventRecord(e, s) == hipSuccess) g_open[id] = e;
-}
-
-void prof_end(int id, hipStream_t s) {
-  if (!g_on) return;
-  std::lock_guard<std::mutex> lk(g_mu);
-  hipEvent_t a = g_open[id];
-  g_open[id] = nullptr;
-  if (!a) return;
-  hipEvent_t b = take();
-  if (b && hipEventRecord(b, s) == hipSuccess) g_pending.push_back({id, a, b});
+  hipEvent_t a = take(), b = take();
+  if (!a || !b) return;
+  *start = a;
+  *stop = b;
+  g_pending.push_back({id, a, b});
   if (g_pending.size() > 4096) drain();
 }
 

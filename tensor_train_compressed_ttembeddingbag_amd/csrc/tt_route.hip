@@ -681,29 +681,19 @@ hipError_t launch_route(const DevArgs &a, hipStream_t s) {
     }
     // One block per CU at most (LDS), launched on an otherwise idle stream position:
     // every block is resident at once.  The barriers are bounded waits in any case.
-    prof_begin(K_ROUTE_COOP, s);
-    hipLaunchKernelGGL(k_route_coop, dim3(a.nblk), dim3(RT), lds, s, a);
-    prof_end(K_ROUTE_COOP, s);
+    tt_launch(K_ROUTE_COOP, k_route_coop, dim3(a.nblk), dim3(RT), lds, s, a);
     return hipGetLastError();
   }
   const size_t bins_ia = (size_t)(a.binsI3 > a.binsA ? a.binsI3 : a.binsA);
-  prof_begin(K_ROUTE_A, s);
-  hipLaunchKernelGGL(k_route_a, dim3(a.nblk), dim3(RT), (ROUTE_MAX_BAGS + bins_ia) * 4, s, a);
-  prof_end(K_ROUTE_A, s);
-  prof_begin(K_ROUTE_B, s);
-  hipLaunchKernelGGL(k_route_b, dim3(a.nblk), dim3(RT), bins_ia * 8, s, a);
-  prof_end(K_ROUTE_B, s);
-  prof_begin(K_ROUTE_C, s);
-  hipLaunchKernelGGL(k_route_c, dim3(a.nblk), dim3(RT), (size_t)a.binsB * 8, s, a);
-  prof_end(K_ROUTE_C, s);
+  tt_launch(K_ROUTE_A, k_route_a, dim3(a.nblk), dim3(RT), (ROUTE_MAX_BAGS + bins_ia) * 4, s, a);
+  tt_launch(K_ROUTE_B, k_route_b, dim3(a.nblk), dim3(RT), bins_ia * 8, s, a);
+  tt_launch(K_ROUTE_C, k_route_c, dim3(a.nblk), dim3(RT), (size_t)a.binsB * 8, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_yinit(const DevArgs &a, hipStream_t s) {
   if (a.NB > 0) {
-    prof_begin(K_YINIT, s);
-    hipLaunchKernelGGL(k_yinit, dim3((a.NB + RT / 64 - 1) / (RT / 64)), dim3(RT), 0, s, a);
-    prof_end(K_YINIT, s);
+    tt_launch(K_YINIT, k_yinit, dim3((a.NB + RT / 64 - 1) / (RT / 64)), dim3(RT), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -711,9 +701,7 @@ hipError_t launch_yinit(const DevArgs &a, hipStream_t s) {
 hipError_t launch_runsum(const DevArgs &a, hipStream_t s) {
   const int pieces = (a.nnz + PIECE - 1) / PIECE;
   if (pieces > 0 && a.has_cache) {
-    prof_begin(K_RUNSUM, s);
-    hipLaunchKernelGGL(k_runsum, dim3((pieces + 3) / 4), dim3(RT), 0, s, a);
-    prof_end(K_RUNSUM, s);
+    tt_launch(K_RUNSUM, k_runsum, dim3((pieces + 3) / 4), dim3(RT), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -62,3 +62,12 @@ def fwd_kernel_flops(q, ranks, n_miss: int, n_pairs: int) -> int:
     product + F2 per element."""
     f1, f2 = stage_flops(q, ranks)
     return f1 * n_pairs + f2 * n_miss
+
+
+def route_bytes(nnz: float, num_bags: int, weighted: bool, has_cache: bool) -> float:
+    """Algorithmic bytes of one grouping call: every input read once (int64 index,
+    int64 offset per bag, fp32 weight, int32 cache slot) and the grouped order written
+    once (32 bytes per position: element, three digits, bag, two segment positions,
+    weight)."""
+    per = 8 + (4 if weighted else 0) + (4 if has_cache else 0) + 32
+    return nnz * per + 8.0 * (num_bags + 1)
