@@ -141,7 +141,7 @@ __global__ __launch_bounds__(RT) void k_sort_scatter(const unsigned long long *i
     d[r] = -1;
     if (i < n) { k[r] = in[i]; d[r] = (int)((k[r] >> shift) & 255ull); }
   }
-  block_rank4(d, rk, cnt, 256, 8, nullptr, nblk);
+  block_rank<RT, 4>(d, rk, cnt, 256, 8);
   for (int r = 0; r < 4; ++r)
     if (d[r] >= 0) out[off[d[r] * nblk + blockIdx.x] + rk[r]] = k[r];
 }

@@ -121,15 +121,21 @@ static __device__ WaveItems wave_items(bool v, int dA, int i3, int nbits3) {
   return r;
 }
 
-static __device__ void block_rank4(const int d[4], int rank[4], unsigned short *cnt, int nbins,
-                            int nbits, int *hist_out, int nblk) {
+// Stable ranks of the block's elements by digit (d < 0: no element).  Thread tid of
+// wave w holds EPT elements, element r at position w*64*EPT + r*64 + lane of the block's
+// order; rank = number of earlier elements with the same digit.  cnt: NW*nbins u16 of LDS
+// (per-wave counts).  Whole block of NT threads.
+template <int NT, int EPT>
+static __device__ void block_rank(const int *d, int *rank, unsigned short *cnt, int nbins,
+                                  int nbits) {
+  constexpr int NW = NT / 64;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int i = threadIdx.x; i < 4 * nbins; i += blockDim.x) cnt[i] = 0;
+  for (int i = threadIdx.x; i < NW * nbins; i += NT) cnt[i] = 0;
   __syncthreads();
-  int rw[4];
+  int rw[EPT];
   const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < EPT; ++r) {
     const bool act = d[r] >= 0;
     unsigned long long m = __ballot(act);
     for (int b = 0; b < nbits; ++b) {
@@ -138,27 +144,29 @@ static __device__ void block_rank4(const int d[4], int rank[4], unsigned short *
       m &= bit ? bb : ~bb;
     }
     const int before = __popcll(m & lt);
-    int base = 0;
-    if (act) base = cnt[w * nbins + d[r]];
+    const int ci = w * nbins + (act ? d[r] : 0);
+    const int base = cnt[ci];
     rw[r] = base + before;
     // every lane of the group has read `base` before the leader writes it back
     __builtin_amdgcn_wave_barrier();
-    if (act && before == 0) cnt[w * nbins + d[r]] = (unsigned short)(base + __popcll(m));
+    if (act && before == 0) cnt[ci] = (unsigned short)(base + __popcll(m));
     __builtin_amdgcn_wave_barrier();
   }
   __syncthreads();
-  for (int bin = threadIdx.x; bin < nbins; bin += blockDim.x) {
-    const int a0 = cnt[bin], a1 = cnt[nbins + bin], a2 = cnt[2 * nbins + bin],
-              a3 = cnt[3 * nbins + bin];
-    cnt[bin] = 0;
-    cnt[nbins + bin] = (unsigned short)a0;
-    cnt[2 * nbins + bin] = (unsigned short)(a0 + a1);
-    cnt[3 * nbins + bin] = (unsigned short)(a0 + a1 + a2);
-    if (hist_out) hist_out[(size_t)bin * nblk + blockIdx.x] = a0 + a1 + a2 + a3;
+  for (int bin = threadIdx.x; bin < nbins; bin += NT) {
+    int c[NW];
+#pragma unroll
+    for (int v = 0; v < NW; ++v) c[v] = cnt[v * nbins + bin];
+    int run = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      cnt[v * nbins + bin] = (unsigned short)run;
+      run += c[v];
+    }
   }
   __syncthreads();
 #pragma unroll
-  for (int r = 0; r < 4; ++r) rank[r] = d[r] >= 0 ? (int)cnt[w * nbins + d[r]] + rw[r] : 0;
+  for (int r = 0; r < EPT; ++r) rank[r] = d[r] >= 0 ? (int)cnt[w * nbins + d[r]] + rw[r] : 0;
 }
 
 static __device__ __forceinline__ int nbits_for(int nbins) {

@@ -42,9 +42,12 @@ static __device__ int half_find_bag(const int64_t *off, int NB, int n, int half,
 constexpr int ROUTE_MAX_BAGS = 2048;  // offsets of one routing block kept in LDS
 
 // ---------------------------------------------------------------- shared pieces
-// Positions of the 4 elements of thread tid in tile blk (RB = 1024 per tile).
+// A tile is RB = 1024 consecutive positions, held by a block of NT threads with
+// EPT = RB / NT elements each: element r of thread tid of wave w sits at position
+// w*64*EPT + r*64 + lane of the tile (the order the block ranks keep).
+template <int NT>
 static __device__ __forceinline__ int tile_pos(int blk, int r) {
-  return blk * RB + (threadIdx.x >> 6) * 256 + r * 64 + (threadIdx.x & 63);
+  return blk * RB + (threadIdx.x >> 6) * (64 * (RB / NT)) + r * 64 + (threadIdx.x & 63);
 }
 
 // Word accesses for data that other blocks of the same launch read after a grid
@@ -86,32 +89,33 @@ static __device__ __forceinline__ Rec load_rec(const int *rec, int pos) {
 // Tile decode: bag, digits dA (t,i1), dB (t,i2), dI (t,i3) and weight of the tile's
 // elements (digits -1 past the end); bad indices / slots reported.  Needs LDS s_off
 // [ROUTE_MAX_BAGS], s_red [8], s_b [2].  Whole block.
+template <int NT>
 static __device__ void tile_decode(const DevArgs &a, int blk, int *s_off, int *s_red, int *s_b,
-                                   Rec el[4]) {
+                                   Rec el[RB / NT]) {
   const int tid = threadIdx.x;
   // the element loads first: they do not depend on the bags
-  int64_t iv[4];
-  int sv[4];
+  int64_t iv[RB / NT];
+  int sv[RB / NT];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) iv[r] = a.idx[min(tile_pos(blk, r), a.nnz - 1)];
+  for (int r = 0; r < RB / NT; ++r) iv[r] = a.idx[min(tile_pos<NT>(blk, r), a.nnz - 1)];
   if (a.has_cache && a.slots) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = a.slots[min(tile_pos(blk, r), a.nnz - 1)];
+    for (int r = 0; r < RB / NT; ++r) sv[r] = a.slots[min(tile_pos<NT>(blk, r), a.nnz - 1)];
   } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = -1;
+    for (int r = 0; r < RB / NT; ++r) sv[r] = -1;
   }
   if (a.psw) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) el[r].w = a.psw[min(tile_pos(blk, r), a.nnz - 1)];
+    for (int r = 0; r < RB / NT; ++r) el[r].w = a.psw[min(tile_pos<NT>(blk, r), a.nnz - 1)];
   } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) el[r].w = 1.f;
+    for (int r = 0; r < RB / NT; ++r) el[r].w = 1.f;
   }
   // the bags that may hold the tile's positions: all of them when their offsets fit in
   // LDS, else the ones overlapping the tile (one 128-ary search per half of the block)
   int b_lo = 0, nbag = a.NB;
-  if (a.NB + 1 > ROUTE_MAX_BAGS) {
+  if (NT == 256 && a.NB + 1 > ROUTE_MAX_BAGS) {
     const int base = blk * RB, last = min(base + RB, a.nnz) - 1;
     const int half = tid >> 7;
     const int b = half_find_bag(a.off, a.NB, half ? last : base, half, s_red);
@@ -121,42 +125,44 @@ static __device__ void tile_decode(const DevArgs &a, int blk, int *s_off, int *s
     nbag = max(s_b[1], s_b[0]) - b_lo + 1;
   }
   const bool in_lds = nbag + 1 <= ROUTE_MAX_BAGS;
-  if (in_lds) {  // ROUTE_MAX_BAGS / RT = 8 loads per thread, all in flight
-    int64_t o[ROUTE_MAX_BAGS / RT];
+  if (in_lds) {  // ROUTE_MAX_BAGS / NT = 8 loads per thread, all in flight
+    int64_t o[ROUTE_MAX_BAGS / NT];
 #pragma unroll
-    for (int u = 0; u < ROUTE_MAX_BAGS / RT; ++u) o[u] = a.off[b_lo + min(tid + u * RT, nbag)];
+    for (int u = 0; u < ROUTE_MAX_BAGS / NT; ++u) o[u] = a.off[b_lo + min(tid + u * NT, nbag)];
 #pragma unroll
-    for (int u = 0; u < ROUTE_MAX_BAGS / RT; ++u)
-      if (tid + u * RT <= nbag) s_off[tid + u * RT] = (int)(o[u] < 0 ? 0 : (o[u] > a.nnz ? a.nnz : o[u]));
+    for (int u = 0; u < ROUTE_MAX_BAGS / NT; ++u)
+      if (tid + u * NT <= nbag) s_off[tid + u * NT] = (int)(o[u] < 0 ? 0 : (o[u] > a.nnz ? a.nnz : o[u]));
   }
   __syncthreads();
   // bag = last b with off[b] <= e: binary lifting over the offsets in LDS, the four
   // elements in lockstep (or a search in global memory for tiles of very many bags)
-  int bag[4];
+  int bag[RB / NT];
   if (in_lds) {
-    int lo[4] = {0, 0, 0, 0};
+    int lo[RB / NT];
+#pragma unroll
+    for (int r = 0; r < RB / NT; ++r) lo[r] = 0;
     int top = 1;
     while (top < nbag + 1) top <<= 1;
     for (int span = top >> 1; span > 0; span >>= 1) {
-      int ov[4];
+      int ov[RB / NT];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ov[r] = s_off[min(lo[r] + span, nbag)];
+      for (int r = 0; r < RB / NT; ++r) ov[r] = s_off[min(lo[r] + span, nbag)];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        lo[r] = (lo[r] + span <= nbag && ov[r] <= tile_pos(blk, r)) ? lo[r] + span : lo[r];
+      for (int r = 0; r < RB / NT; ++r)
+        lo[r] = (lo[r] + span <= nbag && ov[r] <= tile_pos<NT>(blk, r)) ? lo[r] + span : lo[r];
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) bag[r] = b_lo + min(lo[r], nbag - 1);
+    for (int r = 0; r < RB / NT; ++r) bag[r] = b_lo + min(lo[r], nbag - 1);
   } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) bag[r] = find_bag(a.off, a.NB, min(tile_pos(blk, r), a.nnz - 1));
+    for (int r = 0; r < RB / NT; ++r) bag[r] = find_bag(a.off, a.NB, min(tile_pos<NT>(blk, r), a.nnz - 1));
   }
   const int dropA = a.binsA - 1, dropB = a.binsB - 1, dropI = a.binsI3 - 1;
   const int64_t p23 = (int64_t)a.p2 * a.p3;
   bool bad_slot = false, bad_index = false;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int e = tile_pos(blk, r);
+  for (int r = 0; r < RB / NT; ++r) {
+    const int e = tile_pos<NT>(blk, r);
     Rec &x = el[r];
     x.e = e;
     x.bag = bag[r];
@@ -191,8 +197,9 @@ static __device__ void tile_decode(const DevArgs &a, int blk, int *s_off, int *s
 }
 
 // Offsets must be a CSR over [0, nnz]; checked grid-strided by the nblk blocks.
+template <int NT>
 static __device__ void check_offsets(const DevArgs &a, int blk) {
-  const int gt = blk * RT + threadIdx.x, gn = a.nblk * RT;
+  const int gt = blk * NT + threadIdx.x, gn = a.nblk * NT;
   for (int k = gt; k <= a.NB; k += gn) {
     const int64_t o = a.off[k], o1 = a.off[min(k + 1, a.NB)];
     if ((k == 0 && o != 0) || (k == a.NB && o != (int64_t)a.nnz) || (k < a.NB && o1 < o))
@@ -202,28 +209,29 @@ static __device__ void check_offsets(const DevArgs &a, int blk) {
 
 // Tile histogram of digit d; column blk of the [bin][tile] matrix (TILE_MAJOR false)
 // or row blk of the [tile][bin] matrix (true).
-template <bool DEV, bool TILE_MAJOR>
-static __device__ void tile_hist(const int d[4], int *lds_h, int nb, int *hist, int blk) {
+template <int NT, bool DEV, bool TILE_MAJOR>
+static __device__ void tile_hist(const int d[RB / NT], int *lds_h, int nb, int *hist, int blk) {
   const int tid = threadIdx.x;
-  for (int i = tid; i < nb; i += RT) lds_h[i] = 0;
+  for (int i = tid; i < nb; i += NT) lds_h[i] = 0;
   __syncthreads();
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < RB / NT; ++r)
     if (d[r] >= 0) atomicAdd(&lds_h[d[r]], 1);
   __syncthreads();
-  for (int i = tid; i < nb; i += RT)
+  for (int i = tid; i < nb; i += NT)
     st_w<DEV>(TILE_MAJOR ? hist + (size_t)blk * nb + i : hist + (size_t)i * gridDim.x + blk,
               lds_h[i]);
 }
 
 // Stable ranks of the tile's elements by digit d (order: position) and their output
 // positions start[d * ss + so] + rank.
-static __device__ void tile_place(const int d[4], int pos[4], unsigned short *lds_c, int nb,
+template <int NT>
+static __device__ void tile_place(const int d[RB / NT], int pos[RB / NT], unsigned short *lds_c, int nb,
                                   const int *start, int ss, int so) {
-  int rk[4];
-  block_rank4(d, rk, lds_c, nb, nbits_for(nb), nullptr, 0);
+  int rk[RB / NT];
+  block_rank<NT, RB / NT>(d, rk, lds_c, nb, nbits_for(nb));
 #pragma unroll
-  for (int r = 0; r < 4; ++r) pos[r] = d[r] >= 0 ? start[(size_t)d[r] * ss + so] + rk[r] : -1;
+  for (int r = 0; r < RB / NT; ++r) pos[r] = d[r] >= 0 ? start[(size_t)d[r] * ss + so] + rk[r] : -1;
 }
 
 // Work items from the group table gs[0..binsB] (starts of the (t,i2) bins in the final
@@ -258,18 +266,19 @@ static __device__ void build_items(const DevArgs &a, const int *gs, int *cnt, in
 
 // orderI3 / orderA places of the tile's elements (from their bin starts); the records
 // go to their orderA positions.  Returns the orderA positions (-1: none).
-static __device__ void tile_place_ia(const DevArgs &a, Rec el[4], int pA[4], unsigned short *lds_c,
+template <int NT>
+static __device__ void tile_place_ia(const DevArgs &a, Rec el[RB / NT], int pA[RB / NT], unsigned short *lds_c,
                                      const int *startI, const int *startA, int ss, int so) {
-  int d[4], pI[4];
+  int d[RB / NT], pI[RB / NT];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) d[r] = el[r].dI;
-  tile_place(d, pI, lds_c, a.binsI3, startI, ss, so);
+  for (int r = 0; r < RB / NT; ++r) d[r] = el[r].dI;
+  tile_place<NT>(d, pI, lds_c, a.binsI3, startI, ss, so);
   __syncthreads();
 #pragma unroll
-  for (int r = 0; r < 4; ++r) d[r] = el[r].dA;
-  tile_place(d, pA, lds_c, a.binsA, startA, ss, so);
+  for (int r = 0; r < RB / NT; ++r) d[r] = el[r].dA;
+  tile_place<NT>(d, pA, lds_c, a.binsA, startA, ss, so);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < RB / NT; ++r) {
     if (pA[r] < 0) continue;
     el[r].posI3 = pI[r];
     store_rec(a.rec, pA[r], el[r]);
@@ -277,27 +286,29 @@ static __device__ void tile_place_ia(const DevArgs &a, Rec el[4], int pA[4], uns
 }
 
 // Final pass of a tile of orderA: its records placed by (t,i2) into the final order.
+template <int NT>
 static __device__ void tile_final(const DevArgs &a, int blk, unsigned short *lds_c,
                                   const int *start, int ss, int so) {
-  Rec x[4];
-  int d[4], pos[4];
+  Rec x[RB / NT];
+  int d[RB / NT], pos[RB / NT];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) x[r] = load_rec(a.rec, min(tile_pos(blk, r), a.nnz - 1));
+  for (int r = 0; r < RB / NT; ++r) x[r] = load_rec(a.rec, min(tile_pos<NT>(blk, r), a.nnz - 1));
 #pragma unroll
-  for (int r = 0; r < 4; ++r) d[r] = tile_pos(blk, r) < a.nnz ? x[r].dB : -1;
-  tile_place(d, pos, lds_c, a.binsB, start, ss, so);
+  for (int r = 0; r < RB / NT; ++r) d[r] = tile_pos<NT>(blk, r) < a.nnz ? x[r].dB : -1;
+  tile_place<NT>(d, pos, lds_c, a.binsB, start, ss, so);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < RB / NT; ++r) {
     if (pos[r] < 0) continue;
     const int p = pos[r];
     a.srec[2 * (size_t)p] = make_int4(x[r].e, x[r].dA, x[r].dB, x[r].dI);
     a.srec[2 * (size_t)p + 1] = make_int4(x[r].bag, x[r].posI3, __float_as_int(x[r].w),
-                                          tile_pos(blk, r));
+                                          tile_pos<NT>(blk, r));
   }
 }
 
 // ---------------------------------------------------------------- one-launch path
 constexpr int COOP_TILES = 256;        // blocks of one barrier launch (and at most one per CU)
+constexpr int CT = 1024;               // threads of a block of that launch (one element each)
 constexpr int COOP_BINS = 2048;        // bins per digit
 constexpr int COOP_CELLS = 12288;      // bins x tiles per digit (each block reads them all)
 constexpr unsigned SYNC_POLLS = 1u << 22;  // bounded wait of a grid barrier
@@ -314,7 +325,8 @@ static int device_cus() {
 }
 
 static bool coop_route_ok(const DevArgs &a) {
-  return a.nblk <= COOP_TILES && a.nblk <= device_cus() && a.binsA <= COOP_BINS &&
+  return a.nblk <= COOP_TILES && a.nblk <= device_cus() && a.NB + 1 <= ROUTE_MAX_BAGS &&
+         a.binsA <= COOP_BINS &&
          a.binsB <= COOP_BINS && a.binsI3 <= COOP_BINS &&
          (int64_t)a.binsA * a.nblk <= COOP_CELLS && (int64_t)a.binsB * a.nblk <= COOP_CELLS &&
          (int64_t)a.binsI3 * a.nblk <= COOP_CELLS;
@@ -331,10 +343,12 @@ static bool coop_route_ok(const DevArgs &a) {
 template <bool FENCE>
 static __device__ bool grid_sync(const DevArgs &a, unsigned target) {
   __shared__ int s_ok;
-  if (FENCE) __threadfence();
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // every wave's stores are complete; one thread then fences for the whole block (the
+  // L2 write-back / invalidate act on the caches the block's waves share)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
+    if (FENCE) __threadfence();
     unsigned long long *ctr = &a.ctr[0];
     unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     while (true) {
@@ -356,31 +370,31 @@ static __device__ bool grid_sync(const DevArgs &a, unsigned target) {
       }
       __builtin_amdgcn_s_sleep(1);
     }
+    if (FENCE) __threadfence();
     s_ok = ok;
   }
   __syncthreads();
-  if (FENCE) __threadfence();
   return s_ok != 0;
 }
 
 // Per-tile bin starts of two digits from their [tile][bin] count matrices (read whole
 // by every block): start[d] = (elements in smaller bins) + (elements of bin d in tiles
 // < blk); gsum[d] = the global bin starts.  LDS arrays of nb (+1) ints.  Thread t sums
-// the columns of bins t, t + RT, ... over 16 tiles per round of loads (all in flight);
+// the columns of bins t, t + CT, ... over 16 tiles per round of loads (all in flight);
 // the exclusive scan over bins then runs on contiguous runs of the LDS totals.
 constexpr int SCAN_TCH = 16;
-constexpr int SCAN_H = 2 * 2048 / RT;  // bins of both digits per thread (<= 16)
+constexpr int SCAN_H = 2 * 2048 / CT;  // bins of both digits per thread (<= 16)
 static __device__ void tile_starts2(const int *h0, int nb0, int *start0, int *gs0, const int *h1,
                                    int nb1, int *start1, int *gs1, int blk, int *s_scan) {
   const int nblk = gridDim.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int nbt = nb0 + nb1, nh = (nbt + RT - 1) / RT;
+  const int nbt = nb0 + nb1, nh = (nbt + CT - 1) / CT;
   for (int h0i = 0; h0i < nh; h0i += 2) {  // two bins per thread per round
     int tot[2] = {0, 0}, pre[2] = {0, 0};
     for (int t0 = 0; t0 < nblk; t0 += SCAN_TCH) {
       int v[2][SCAN_TCH];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int j = min(tid + (h0i + h) * RT, nbt - 1);
+        const int j = min(tid + (h0i + h) * CT, nbt - 1);
         const bool first = j < nb0;
         const int *col = first ? h0 + j : h1 + (j - nb0);
         const int nb = first ? nb0 : nb1;
@@ -399,14 +413,14 @@ static __device__ void tile_starts2(const int *h0, int nb0, int *start0, int *gs
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int j = tid + (h0i + h) * RT;
+      const int j = tid + (h0i + h) * CT;
       if (j < nb0) { gs0[j] = tot[h]; start0[j] = pre[h]; }
       else if (j < nbt) { gs1[j - nb0] = tot[h]; start1[j - nb0] = pre[h]; }
     }
   }
   __syncthreads();
   // exclusive scans over the bins of each digit, on contiguous runs per thread
-  const int per = (nbt + RT - 1) / RT;
+  const int per = (nbt + CT - 1) / CT;
   int run0 = 0, run1 = 0;
   for (int k = 0; k < per; ++k) {
     const int j = tid * per + k;
@@ -419,10 +433,10 @@ static __device__ void tile_starts2(const int *h0, int nb0, int *start0, int *gs
     const int y0 = __shfl_up(x0, o), y1 = __shfl_up(x1, o);
     if (lane >= o) { x0 += y0; x1 += y1; }
   }
-  if (lane == 63) { s_scan[w] = x0; s_scan[RT / 64 + w] = x1; }
+  if (lane == 63) { s_scan[w] = x0; s_scan[CT / 64 + w] = x1; }
   __syncthreads();
   int b0 = x0 - run0, b1 = x1 - run1;
-  for (int v = 0; v < w; ++v) { b0 += s_scan[v]; b1 += s_scan[RT / 64 + v]; }
+  for (int v = 0; v < w; ++v) { b0 += s_scan[v]; b1 += s_scan[CT / 64 + v]; }
   for (int k = 0; k < per; ++k) {
     const int j = tid * per + k;
     if (j < nb0) {
@@ -442,7 +456,7 @@ static __device__ void tile_starts2(const int *h0, int nb0, int *start0, int *gs
 
 // LDS of the one-launch kernel (ints, sized by the call's bins and tiles), phases overlap:
 //   decode:  s_off [ROUTE_MAX_BAGS] | hist [max(binsI3, binsA)]
-//   passes:  rank counts (u16 4 x bins) | startI, gsI | startA, gsA | (t,i2) cells
+//   passes:  rank counts (u16, waves x bins) | startI, gsI | startA, gsA | (t,i2) cells
 struct CoopLds {
   int c, sI, gI, sA, gA, cell, total;
 };
@@ -451,7 +465,7 @@ __host__ __device__ inline CoopLds coop_lds(const DevArgs &a) {
   const int nX = max(a.binsI3, a.binsB) + 1, nY = max(a.binsA, a.binsB) + 1;
   CoopLds L;
   L.c = 0;
-  L.sI = 2 * mb;
+  L.sI = (CT / 64) * mb / 2 + 1;  // u16 counts per wave and bin
   L.gI = L.sI + nX;
   L.sA = L.gI + nX;
   L.gA = L.sA + nY;
@@ -460,31 +474,31 @@ __host__ __device__ inline CoopLds coop_lds(const DevArgs &a) {
   return L;
 }
 
-__global__ __launch_bounds__(RT) void k_route_coop(DevArgs a) {
+__global__ __launch_bounds__(CT) void k_route_coop(DevArgs a) {
   extern __shared__ int lds_i[];
-  __shared__ int s_scan[2 * (RT / 64) + 1];
+  __shared__ int s_scan[2 * (CT / 64) + 1];
   __shared__ int s_red[8];
   __shared__ int s_b[2];
   const int tid = threadIdx.x, blk = blockIdx.x, nblk = gridDim.x;
   const CoopLds L = coop_lds(a);
-  unsigned short *lds_c = (unsigned short *)(lds_i + L.c);  // [4][bins] rank counts
+  unsigned short *lds_c = (unsigned short *)(lds_i + L.c);  // [waves][bins] rank counts
   int *startI = lds_i + L.sI, *gsI = lds_i + L.gI, *startA = lds_i + L.sA, *gsA = lds_i + L.gA;
   int *cellB = lds_i + L.cell;  // [binsB][nblk] (t,i2) counts of the orderA tiles
-  Rec el[4];
+  Rec el[RB / CT];
 
   // ---- decode; (t,i3) and (t,i1) histograms of the tile; histB cleared for the atomics
-  tile_decode(a, blk, lds_i, s_red, s_b, el);
-  check_offsets(a, blk);
-  for (int k = blk * RT + tid; k < a.binsB * nblk; k += nblk * RT) st_w<true>(a.histB + k, 0);
+  tile_decode<CT>(a, blk, lds_i, s_red, s_b, el);
+  check_offsets<CT>(a, blk);
+  for (int k = blk * CT + tid; k < a.binsB * nblk; k += nblk * CT) st_w<true>(a.histB + k, 0);
   {
-    int d[4];
+    int d[RB / CT];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) d[r] = el[r].dI;
-    tile_hist<true, true>(d, lds_i + ROUTE_MAX_BAGS, a.binsI3, a.histI3, blk);
+    for (int r = 0; r < RB / CT; ++r) d[r] = el[r].dI;
+    tile_hist<CT, true, true>(d, lds_i + ROUTE_MAX_BAGS, a.binsI3, a.histI3, blk);
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < 4; ++r) d[r] = el[r].dA;
-    tile_hist<true, true>(d, lds_i + ROUTE_MAX_BAGS, a.binsA, a.histA, blk);
+    for (int r = 0; r < RB / CT; ++r) d[r] = el[r].dA;
+    tile_hist<CT, true, true>(d, lds_i + ROUTE_MAX_BAGS, a.binsA, a.histA, blk);
   }
   if (!grid_sync<false>(a, nblk)) return;
 
@@ -492,23 +506,23 @@ __global__ __launch_bounds__(RT) void k_route_coop(DevArgs a) {
   //      block in LDS, then added to histB
   tile_starts2(a.histI3, a.binsI3, startI, gsI, a.histA, a.binsA, startA, gsA, blk, s_scan);
   if (blk == 0) {
-    for (int d = tid; d < a.binsI3; d += RT) a.segI3[d] = gsI[d];
-    for (int d = tid; d < a.binsA; d += RT) a.segA[d] = gsA[d];
+    for (int d = tid; d < a.binsI3; d += CT) a.segI3[d] = gsI[d];
+    for (int d = tid; d < a.binsA; d += CT) a.segA[d] = gsA[d];
   }
-  for (int i = tid; i < a.binsB * nblk; i += RT) cellB[i] = 0;
-  int pA[4];
-  tile_place_ia(a, el, pA, lds_c, startI, startA, 1, 0);
+  for (int i = tid; i < a.binsB * nblk; i += CT) cellB[i] = 0;
+  int pA[RB / CT];
+  tile_place_ia<CT>(a, el, pA, lds_c, startI, startA, 1, 0);
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < RB / CT; ++r)
     if (pA[r] >= 0) atomicAdd(&cellB[el[r].dB * nblk + pA[r] / RB], 1);
   __syncthreads();
-  for (int i = tid; i < a.binsB * nblk; i += RT)
+  for (int i = tid; i < a.binsB * nblk; i += CT)
     if (cellB[i]) atomicAdd(&a.histB[(i % nblk) * a.binsB + i / nblk], cellB[i]);
   if (!grid_sync<true>(a, 2 * nblk)) return;
 
   // ---- final order: the orderA tiles placed by (t,i2); block 0 builds the work items
   tile_starts2(a.histB, a.binsB, startI, gsI, nullptr, 0, nullptr, nullptr, blk, s_scan);
-  tile_final(a, blk, lds_c, startI, 1, 0);
+  tile_final<CT>(a, blk, lds_c, startI, 1, 0);
   if (blk == 0) {
     if (tid == 0) gsI[a.binsB] = a.nnz;
     __syncthreads();
@@ -529,8 +543,8 @@ __global__ __launch_bounds__(RT) void k_route_a(DevArgs a) {
   __shared__ int s_b[2];
   const int blk = blockIdx.x, tid = threadIdx.x;
   Rec el[4];
-  tile_decode(a, blk, lds_i, s_red, s_b, el);
-  check_offsets(a, blk);
+  tile_decode<RT>(a, blk, lds_i, s_red, s_b, el);
+  check_offsets<RT>(a, blk);
   for (int k = blk * RT + tid; k < a.binsB * a.nblk; k += a.nblk * RT) a.histB[k] = 0;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
@@ -538,11 +552,11 @@ __global__ __launch_bounds__(RT) void k_route_a(DevArgs a) {
   int d[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) d[r] = el[r].dI;
-  tile_hist<false, false>(d, lds_i + ROUTE_MAX_BAGS, a.binsI3, a.histI3, blk);
+  tile_hist<RT, false, false>(d, lds_i + ROUTE_MAX_BAGS, a.binsI3, a.histI3, blk);
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < 4; ++r) d[r] = el[r].dA;
-  tile_hist<false, false>(d, lds_i + ROUTE_MAX_BAGS, a.binsA, a.histA, blk);
+  tile_hist<RT, false, false>(d, lds_i + ROUTE_MAX_BAGS, a.binsA, a.histA, blk);
   if (!last_block(&a.ctr[0], a.nblk, a.epoch)) return;
   block_exclusive_scan(a.histI3, a.binsI3 * a.nblk, s_scan);
   block_exclusive_scan(a.histA, a.binsA * a.nblk, s_scan);
@@ -560,7 +574,7 @@ __global__ __launch_bounds__(RT) void k_route_b(DevArgs a) {
   Rec el[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int e = tile_pos(blk, r), ec = min(e, a.nnz - 1);
+    const int e = tile_pos<RT>(blk, r), ec = min(e, a.nnz - 1);
     const int4 info = a.einfo[ec];
     const bool v = e < a.nnz;
     el[r].e = e;
@@ -571,7 +585,7 @@ __global__ __launch_bounds__(RT) void k_route_b(DevArgs a) {
     el[r].w = a.psw ? a.psw[ec] : 1.f;
   }
   int pA[4];
-  tile_place_ia(a, el, pA, lds_c, a.histI3, a.histA, a.nblk, blk);
+  tile_place_ia<RT>(a, el, pA, lds_c, a.histI3, a.histA, a.nblk, blk);
 #pragma unroll
   for (int r = 0; r < 4; ++r)
     if (pA[r] >= 0) atomicAdd(&a.histB[(size_t)el[r].dB * a.nblk + pA[r] / RB], 1);
@@ -587,7 +601,7 @@ __global__ __launch_bounds__(RT) void k_route_b(DevArgs a) {
 // k_route_c: the orderA tiles placed by (t,i2) into the final order.
 __global__ __launch_bounds__(RT) void k_route_c(DevArgs a) {
   extern __shared__ unsigned short lds_c[];  // [4][binsB]
-  tile_final(a, blockIdx.x, lds_c, a.histB, a.nblk, blockIdx.x);
+  tile_final<RT>(a, blockIdx.x, lds_c, a.histB, a.nblk, blockIdx.x);
   if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr[H_PLAN] = (int)a.plan_fp;
 }
 
@@ -681,7 +695,7 @@ hipError_t launch_route(const DevArgs &a, hipStream_t s) {
     }
     // One block per CU at most (LDS), launched on an otherwise idle stream position:
     // every block is resident at once.  The barriers are bounded waits in any case.
-    tt_launch(K_ROUTE_COOP, k_route_coop, dim3(a.nblk), dim3(RT), lds, s, a);
+    tt_launch(K_ROUTE_COOP, k_route_coop, dim3(a.nblk), dim3(CT), lds, s, a);
     return hipGetLastError();
   }
   const size_t bins_ia = (size_t)(a.binsI3 > a.binsA ? a.binsI3 : a.binsA);
