@@ -37,7 +37,7 @@ struct Plan {
   size_t lds_fwd = 0, lds_bwd = 0;
   size_t ws_total = 0;
   // byte offsets inside the workspace
-  size_t o_ctr, o_hdr, o_einfo, o_histA, o_histB, o_histI3, o_rec, o_segI3, o_segA, o_srec,
+  size_t o_ctr, o_flag, o_hdr, o_einfo, o_histA, o_histB, o_histI3, o_rec, o_segI3, o_segA, o_srec,
       o_fitem, o_grp, o_chunk,
       o_l1, o_l3, o_p1, o_p3, o_frag, o_p2;
 };
@@ -120,6 +120,7 @@ int make_plan(const tt_desc *d, int64_t nnz, int64_t num_bags, int64_t cache_siz
   const size_t n = (size_t)nnz, nb = (size_t)a.nblk, G = (size_t)T * a.p2;
   size_t cur = 0;
   P->o_ctr = carve(cur, 3 * sizeof(unsigned long long));
+  P->o_flag = carve(cur, COOP_TILES * sizeof(unsigned long long));
   P->o_hdr = carve(cur, H_WORDS * sizeof(int));
   P->o_einfo = carve(cur, n * sizeof(int4));
   P->o_histA = carve(cur, (size_t)binsA * nb * 4);
@@ -146,6 +147,7 @@ void bind_ws(Plan *P, void *ws) {
   char *b = (char *)ws;
   DevArgs &a = P->a;
   a.ctr = (unsigned long long *)(b + P->o_ctr);
+  a.flag = (unsigned long long *)(b + P->o_flag);
   a.hdr = (int *)(b + P->o_hdr);
   a.einfo = (int4 *)(b + P->o_einfo);
   a.histA = (int *)(b + P->o_histA);

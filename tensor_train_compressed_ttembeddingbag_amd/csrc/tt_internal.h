@@ -32,6 +32,7 @@ constexpr int MBW = 1;          // forward: M-blocks (16 rows of (pair, j1)) per
 constexpr int P_MAX = 32;       // positions per work item: P * q1 <= 16 * NW rows
 constexpr int MAXQ3 = 16;
 constexpr int STAGE_U = 8;      // global loads in flight per thread when staging into LDS
+constexpr int COOP_TILES = 256; // blocks of the one-launch grouping kernel (one per CU)
 
 // header words inside the workspace (after three 64-bit "last block" counters)
 enum {
@@ -73,6 +74,7 @@ struct DevArgs {
   int32_t *status;
   // workspace
   unsigned long long *ctr;  // [3] epoch-tagged completion counters (no zeroing needed)
+  unsigned long long *flag;  // [COOP_TILES] grid-barrier arrival words (epoch << 32 | k)
   unsigned epoch;           // unique per call
   int *hdr;
   int4 *einfo;      // per element: dA (t,i1), dB (t,i2), dI3 (t,i3), bag

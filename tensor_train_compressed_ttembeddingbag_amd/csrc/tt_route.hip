@@ -307,7 +307,6 @@ static __device__ void tile_final(const DevArgs &a, int blk, unsigned short *lds
 }
 
 // ---------------------------------------------------------------- one-launch path
-constexpr int COOP_TILES = 256;        // blocks of one barrier launch (and at most one per CU)
 constexpr int CT = 1024;               // threads of a block of that launch (one element each)
 constexpr int COOP_BINS = 2048;        // bins per digit
 constexpr int COOP_CELLS = 12288;      // bins x tiles per digit (each block reads them all)
@@ -332,46 +331,50 @@ static bool coop_route_ok(const DevArgs &a) {
          (int64_t)a.binsI3 * a.nblk <= COOP_CELLS;
 }
 
-// All blocks of the launch meet here (k-th barrier: target k * nblk).  Data crossing
-// the barrier is either written with device-coherent stores or atomics, complete
-// before the block arrives (FENCE = false), or made visible by device-scope fences
-// around the barrier (FENCE = true: plain stores and loads, at the price of an L2
-// write-back).  The counter holds (epoch << 32 | arrivals); a word of another call
-// counts as zero.  The wait is bounded: a block that gives up reports
-// TT_DEV_SYNC_TIMEOUT and returns false (its caller leaves the kernel; no plan is
-// marked valid).
+// All blocks of the launch meet here (k-th barrier).  Data crossing the barrier is
+// either written with device-coherent stores or atomics, complete before the block
+// arrives (FENCE = false), or made visible by device-scope fences around the barrier
+// (FENCE = true: plain stores and loads, at the price of an L2 write-back).  Arrival
+// is one device-coherent store of (epoch << 32 | k) into the block's own flag word (no
+// read-modify-write, so arrivals never contend); the first wave then reads all flags
+// until each holds this call's epoch and a count >= k.  Words left by another call
+// carry another epoch, so the flags never need clearing.  The wait is bounded: a block
+// that gives up reports TT_DEV_SYNC_TIMEOUT and returns false (its caller leaves the
+// kernel; no plan is marked valid).
 template <bool FENCE>
-static __device__ bool grid_sync(const DevArgs &a, unsigned target) {
+static __device__ bool grid_sync(const DevArgs &a, unsigned k) {
   __shared__ int s_ok;
+  const int tid = threadIdx.x, nblk = gridDim.x;
   // every wave's stores are complete; one thread then fences for the whole block (the
   // L2 write-back / invalidate act on the caches the block's waves share)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     if (FENCE) __threadfence();
-    unsigned long long *ctr = &a.ctr[0];
-    unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    while (true) {
-      const unsigned long long nw = ((unsigned)(old >> 32) == a.epoch)
-                                        ? old + 1ull
-                                        : (((unsigned long long)a.epoch << 32) | 1ull);
-      const unsigned long long prev = atomicCAS(ctr, old, nw);
-      if (prev == old) break;
-      old = prev;
-    }
+    __hip_atomic_store(&a.flag[blockIdx.x], ((unsigned long long)a.epoch << 32) | k,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (tid < 64) {
     int ok = 1;
     for (unsigned polls = 0;; ++polls) {
-      const unsigned long long v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if ((unsigned)(v >> 32) == a.epoch && (unsigned)v >= target) break;
+      bool mine = true;  // this lane's flags (blocks tid, tid + 64, ...) have arrived
+      for (int b = tid; b < nblk; b += 64) {
+        const unsigned long long v =
+            __hip_atomic_load(&a.flag[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        mine = mine && (unsigned)(v >> 32) == a.epoch && (unsigned)v >= k;
+      }
+      if (__ballot(!mine) == 0ull) break;
       if (polls >= SYNC_POLLS) {
         ok = 0;
-        set_status(a.status, TT_DEV_SYNC_TIMEOUT);
+        if (tid == 0) set_status(a.status, TT_DEV_SYNC_TIMEOUT);
         break;
       }
       __builtin_amdgcn_s_sleep(1);
     }
-    if (FENCE) __threadfence();
-    s_ok = ok;
+    if (tid == 0) {
+      if (FENCE) __threadfence();
+      s_ok = ok;
+    }
   }
   __syncthreads();
   return s_ok != 0;
@@ -500,7 +503,7 @@ __global__ __launch_bounds__(CT) void k_route_coop(DevArgs a) {
     for (int r = 0; r < RB / CT; ++r) d[r] = el[r].dA;
     tile_hist<CT, true, true>(d, lds_i + ROUTE_MAX_BAGS, a.binsA, a.histA, blk);
   }
-  if (!grid_sync<false>(a, nblk)) return;
+  if (!grid_sync<false>(a, 1)) return;
 
   // ---- orderI3 / orderA places; the (t,i2) counts of the orderA tiles gathered per
   //      block in LDS, then added to histB
@@ -518,7 +521,7 @@ __global__ __launch_bounds__(CT) void k_route_coop(DevArgs a) {
   __syncthreads();
   for (int i = tid; i < a.binsB * nblk; i += CT)
     if (cellB[i]) atomicAdd(&a.histB[(i % nblk) * a.binsB + i / nblk], cellB[i]);
-  if (!grid_sync<true>(a, 2 * nblk)) return;
+  if (!grid_sync<true>(a, 2)) return;
 
   // ---- final order: the orderA tiles placed by (t,i2); block 0 builds the work items
   tile_starts2(a.histB, a.binsB, startI, gsI, nullptr, 0, nullptr, nullptr, blk, s_scan);
