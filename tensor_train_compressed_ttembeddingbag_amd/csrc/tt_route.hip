@@ -237,26 +237,48 @@ static __device__ void tile_place(const int d[RB / NT], int pos[RB / NT], unsign
 // Work items from the group table gs[0..binsB] (starts of the (t,i2) bins in the final
 // order, gs[binsB] = nnz; LDS or global): a miss group of m elements becomes ceil(m / P)
 // items of near-equal size (at most P positions each), numbered group by group; also
-// grp_off and the header words.  Whole block; cnt: G + 1 ints of scratch (LDS or global).
-static __device__ void build_items(const DevArgs &a, const int *gs, int *cnt, int *s_scan) {
-  const int G = a.T * a.p2, tid = threadIdx.x, nt = blockDim.x;
-  for (int g = tid; g <= G; g += nt) {
-    const int m = g < G ? gs[g + 1] - gs[g] : 0;
-    cnt[g] = (m + a.P - 1) / a.P;
+// grp_off, chunk_pre and the header words.  Every block of a launch may call it with
+// its own part: all compute the item numbering (cnt: G + 1 ints of scratch, LDS or
+// global), part k of nparts writes the entries of the groups g = k (mod nparts).
+static __device__ void build_items(const DevArgs &a, const int *gs, int *cnt, int *s_scan,
+                                   int part, int nparts) {
+  const int G = a.T * a.p2, tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, w = tid >> 6;
+  const int lP = 31 - __clz(a.P), P1 = a.P - 1;  // P is a power of two
+  // exclusive scan of the item counts on contiguous runs per thread
+  const int per = (G + nt) / nt, beg = min(tid * per, G + 1), end = min(beg + per, G + 1);
+  int sum = 0;
+  for (int g = beg; g < end; ++g) sum += g < G ? (gs[g + 1] - gs[g] + P1) >> lP : 0;
+  const int incl = wave_incl_scan(sum);
+  if (lane == 63) s_scan[w] = incl;
+  __syncthreads();
+  int run = incl - sum;
+  for (int v = 0; v < w; ++v) run += s_scan[v];
+  for (int g = beg; g < end; ++g) {
+    cnt[g] = run;
+    run += g < G ? (gs[g + 1] - gs[g] + P1) >> lP : 0;
   }
-  for (int b = tid; b <= a.binsB; b += nt) a.grp_off[b] = gs[b];
   __threadfence_block();
   __syncthreads();
-  block_exclusive_scan(cnt, G + 1, s_scan);
-  for (int g = tid; g <= G; g += nt) a.chunk_pre[g] = cnt[g];
-  for (int g = tid; g < G; g += nt) {
+  for (int b = part + tid * nparts; b <= a.binsB; b += nt * nparts) a.grp_off[b] = gs[b];
+  for (int g = part + tid * nparts; g <= G; g += nt * nparts) a.chunk_pre[g] = cnt[g];
+  for (int g = part + tid * nparts; g < G; g += nt * nparts) {
     const int first = cnt[g], nc = cnt[g + 1] - first;
     const int gb = gs[g], m = gs[g + 1] - gb;
-    for (int c = 0; c < nc; ++c)
-      a.fitem[first + c] = make_int4(g, gb + (int)((int64_t)m * c / nc),
-                                     gb + (int)((int64_t)m * (c + 1) / nc), 0);
+    if (nc == 0) continue;
+    // item c spans [m c / nc, m (c + 1) / nc) of the group; m c / nc = q c + r c / nc
+    const int q = m / nc, r = m - q * nc;
+    auto cut = [&](int c) {
+      return gb + q * c + (nc < 65536 ? (int)((unsigned)r * (unsigned)c / (unsigned)nc)
+                                      : (int)((long long)r * c / nc));
+    };
+    int lo = gb;
+    for (int c = 0; c < nc; ++c) {
+      const int hi = c + 1 < nc ? cut(c + 1) : gb + m;
+      a.fitem[first + c] = make_int4(g, lo, hi, 0);
+      lo = hi;
+    }
   }
-  if (tid == 0) {
+  if (part == 0 && tid == 0) {
     a.hdr[H_NFWD] = cnt[G];
     a.hdr[H_HIT_BEG] = gs[G];
     a.hdr[H_HIT_END] = gs[a.binsB - 1];
@@ -309,7 +331,6 @@ static __device__ void tile_final(const DevArgs &a, int blk, unsigned short *lds
 // ---------------------------------------------------------------- one-launch path
 constexpr int CT = 1024;               // threads of a block of that launch (one element each)
 constexpr int COOP_BINS = 2048;        // bins per digit
-constexpr int COOP_CELLS = 12288;      // bins x tiles per digit (each block reads them all)
 constexpr unsigned SYNC_POLLS = 1u << 22;  // bounded wait of a grid barrier
 
 // Compute units of the current device (cached per device).
@@ -383,43 +404,33 @@ static __device__ bool grid_sync(const DevArgs &a, unsigned k) {
 // Per-tile bin starts of two digits from their [tile][bin] count matrices (read whole
 // by every block): start[d] = (elements in smaller bins) + (elements of bin d in tiles
 // < blk); gsum[d] = the global bin starts.  LDS arrays of nb (+1) ints.  Thread t sums
-// the columns of bins t, t + CT, ... over 16 tiles per round of loads (all in flight);
-// the exclusive scan over bins then runs on contiguous runs of the LDS totals.
+// the column of bin t (then t + CT, ...) over 16 tiles per round of loads (all in
+// flight); threads without a bin issue no loads.  The exclusive scan over bins then
+// runs on contiguous runs of the LDS totals.
 constexpr int SCAN_TCH = 16;
-constexpr int SCAN_H = 2 * 2048 / CT;  // bins of both digits per thread (<= 16)
 static __device__ void tile_starts2(const int *h0, int nb0, int *start0, int *gs0, const int *h1,
                                    int nb1, int *start1, int *gs1, int blk, int *s_scan) {
   const int nblk = gridDim.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int nbt = nb0 + nb1, nh = (nbt + CT - 1) / CT;
-  for (int h0i = 0; h0i < nh; h0i += 2) {  // two bins per thread per round
-    int tot[2] = {0, 0}, pre[2] = {0, 0};
+  const int nbt = nb0 + nb1;
+  for (int j = tid; j < nbt; j += CT) {
+    const bool first = j < nb0;
+    const int *col = first ? h0 + j : h1 + (j - nb0);
+    const int nb = first ? nb0 : nb1;
+    int tot = 0, pre = 0;
     for (int t0 = 0; t0 < nblk; t0 += SCAN_TCH) {
-      int v[2][SCAN_TCH];
+      int v[SCAN_TCH];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int j = min(tid + (h0i + h) * CT, nbt - 1);
-        const bool first = j < nb0;
-        const int *col = first ? h0 + j : h1 + (j - nb0);
-        const int nb = first ? nb0 : nb1;
+      for (int u = 0; u < SCAN_TCH; ++u)
+        v[u] = ld_w<true>(col + (size_t)min(t0 + u, nblk - 1) * nb);
 #pragma unroll
-        for (int u = 0; u < SCAN_TCH; ++u)
-          v[h][u] = ld_w<true>(col + (size_t)min(t0 + u, nblk - 1) * nb);
+      for (int u = 0; u < SCAN_TCH; ++u) {
+        const int t = t0 + u;
+        tot += t < nblk ? v[u] : 0;
+        pre += t < blk ? v[u] : 0;
       }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int u = 0; u < SCAN_TCH; ++u) {
-          const int t = t0 + u;
-          tot[h] += t < nblk ? v[h][u] : 0;
-          pre[h] += t < blk ? v[h][u] : 0;
-        }
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int j = tid + (h0i + h) * CT;
-      if (j < nb0) { gs0[j] = tot[h]; start0[j] = pre[h]; }
-      else if (j < nbt) { gs1[j - nb0] = tot[h]; start1[j - nb0] = pre[h]; }
-    }
+    if (first) { gs0[j] = tot; start0[j] = pre; }
+    else { gs1[j - nb0] = tot; start1[j - nb0] = pre; }
   }
   __syncthreads();
   // exclusive scans over the bins of each digit, on contiguous runs per thread
@@ -489,10 +500,10 @@ __global__ __launch_bounds__(CT) void k_route_coop(DevArgs a) {
   int *cellB = lds_i + L.cell;  // [binsB][nblk] (t,i2) counts of the orderA tiles
   Rec el[RB / CT];
 
-  // ---- decode; (t,i3) and (t,i1) histograms of the tile; histB cleared for the atomics
+  // ---- histB cleared for the atomics; decode; (t,i3) and (t,i1) histograms of the tile
+  for (int k = blk * CT + tid; k < a.binsB * nblk; k += nblk * CT) st_w<true>(a.histB + k, 0);
   tile_decode<CT>(a, blk, lds_i, s_red, s_b, el);
   check_offsets<CT>(a, blk);
-  for (int k = blk * CT + tid; k < a.binsB * nblk; k += nblk * CT) st_w<true>(a.histB + k, 0);
   {
     int d[RB / CT];
 #pragma unroll
@@ -523,16 +534,14 @@ __global__ __launch_bounds__(CT) void k_route_coop(DevArgs a) {
     if (cellB[i]) atomicAdd(&a.histB[(i % nblk) * a.binsB + i / nblk], cellB[i]);
   if (!grid_sync<true>(a, 2)) return;
 
-  // ---- final order: the orderA tiles placed by (t,i2); block 0 builds the work items
+  // ---- work items (each block writes its share); final order: the orderA tiles placed
+  //      by (t,i2)
   tile_starts2(a.histB, a.binsB, startI, gsI, nullptr, 0, nullptr, nullptr, blk, s_scan);
+  if (tid == 0) gsI[a.binsB] = a.nnz;
+  __syncthreads();
+  build_items(a, gsI, startA, s_scan, blk, nblk);
   tile_final<CT>(a, blk, lds_c, startI, 1, 0);
-  if (blk == 0) {
-    if (tid == 0) gsI[a.binsB] = a.nnz;
-    __syncthreads();
-    build_items(a, gsI, startA, s_scan);
-    __syncthreads();
-    if (tid == 0) a.hdr[H_PLAN] = (int)a.plan_fp;
-  }
+  if (blk == 0 && tid == 0) a.hdr[H_PLAN] = (int)a.plan_fp;
 }
 
 // ---------------------------------------------------------------- three-kernel path
@@ -598,7 +607,7 @@ __global__ __launch_bounds__(RT) void k_route_b(DevArgs a) {
   if (threadIdx.x == 0) a.grp_off[a.binsB] = a.nnz;
   __threadfence_block();
   __syncthreads();
-  build_items(a, a.grp_off, a.chunk_pre, s_scan);
+  build_items(a, a.grp_off, a.chunk_pre, s_scan, 0, 1);
 }
 
 // k_route_c: the orderA tiles placed by (t,i2) into the final order.
