@@ -43,11 +43,17 @@
  *    weights are updated in the backward pass instead of returning gradients.
  *    Reading taken: identical to one plain SGD step G <- G - lr * dG at the
  *    pre-update cores; slices that received no contribution are left untouched.
+ *    Without the fused update (`sparse` False) the gradients above are the result.
+ *
+ *  - Fused Adagrad ("Parameters": `optimizer`, `eps` for Adagrad only): the
+ *    diagonal Adagrad step of Duchi, Hazan and Singer (2011) on the touched slices,
+ *    one running sum of squared gradients per parameter, eps added to its root.
  *
  * Error behaviour: returns 0 on success, -1 if an index is outside [0, E), an
  * offsets array is not a valid CSR over [0, nnz], or a cache slot is outside
  * [0, cache_size).  Nothing is written on error.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -251,5 +257,46 @@ void oracle_sgd_rows(float *rows, const double *grad, const uint8_t *touched,
         if (!touched[sl]) continue;
         for (int64_t j = 0; j < D; ++j)
             rows[sl * D + j] = (float)((double)rows[sl * D + j] - lr * grad[sl * D + j]);
+    }
+}
+
+/*
+ * Adagrad, the other optimizer of the fused update ("Parameters": `optimizer`, and
+ * `eps` added to the denominator): the diagonal method of Duchi, Hazan and Singer
+ * (2011).  Each parameter x keeps a running sum S of its squared gradients:
+ *     S <- fp32( double(S) + g^2 );   x <- fp32( double(x) - lr * g / (sqrt(S) + eps) )
+ * with the S just stored.  `state` has the layout of `core`; untouched slices keep
+ * the bits of both.
+ */
+void oracle_adagrad_core(const oracle_shape *s, int k, float *core, float *state,
+                         const double *grad, const uint8_t *touched, double lr, double eps)
+{
+    const int64_t ra = (k == 0) ? 1 : s->r[k - 1];
+    const int64_t rb = (k == 2) ? 1 : s->r[k];
+    for (int64_t a = 0; a < ra; ++a)
+        for (int64_t ik = 0; ik < s->p[k]; ++ik) {
+            if (!touched[ik]) continue;
+            for (int64_t jk = 0; jk < s->q[k]; ++jk)
+                for (int64_t c = 0; c < rb; ++c) {
+                    const int64_t e = core_index(s, k, a, ik, jk, c);
+                    const double g = grad[e];
+                    state[e] = (float)((double)state[e] + g * g);
+                    core[e] = (float)((double)core[e] - lr * g / (sqrt((double)state[e]) + eps));
+                }
+        }
+}
+
+/* the same step for cache rows, state [nrows][D] */
+void oracle_adagrad_rows(float *rows, float *state, const double *grad, const uint8_t *touched,
+                         int64_t nrows, int64_t D, double lr, double eps)
+{
+    for (int64_t sl = 0; sl < nrows; ++sl) {
+        if (!touched[sl]) continue;
+        for (int64_t j = 0; j < D; ++j) {
+            const int64_t e = sl * D + j;
+            const double g = grad[e];
+            state[e] = (float)((double)state[e] + g * g);
+            rows[e] = (float)((double)rows[e] - lr * g / (sqrt((double)state[e]) + eps));
+        }
     }
 }

@@ -1,7 +1,8 @@
 """CPU oracle for TT-EmbeddingBag -- TEST INFRASTRUCTURE ONLY.
 
 Floating-point side: ``tt_oracle.c`` (plain double loops over the definition of
-the TT table, EmbeddingBag pooling, the product-rule backward and plain SGD),
+the TT table, EmbeddingBag pooling, the product-rule backward, plain SGD and
+Adagrad),
 loaded here through ctypes.  Integer side (index split, bag ids, the grouping
 order, cache frequency counts, top-K selection, slot lookup): plain numpy / dict
 code in this file.
@@ -34,7 +35,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "tt_oracle.c")
 _SO = os.path.join(_HERE, "libtt_oracle.so")
 
-__all__ = ["build", "forward", "backward", "sgd", "tt_row", "split_index", "bag_ids",
+__all__ = ["build", "forward", "backward", "sgd", "adagrad", "tt_row", "split_index", "bag_ids",
            "route_order", "group_counts", "count_frequencies", "select_cache",
            "lookup_slots", "populate_rows"]
 
@@ -44,7 +45,7 @@ def build(force: bool = False) -> str:
     if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
         tmp = _SO + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared",
-                               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp])
+                               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _SO)
     return _SO
 
@@ -71,6 +72,10 @@ def _L():
         lib.oracle_backward.restype = ctypes.c_int
         lib.oracle_sgd_core.argtypes = [P, ctypes.c_int, P, P, P, ctypes.c_double]
         lib.oracle_sgd_rows.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_double]
+        lib.oracle_adagrad_core.argtypes = [P, ctypes.c_int, P, P, P, P, ctypes.c_double,
+                                            ctypes.c_double]
+        lib.oracle_adagrad_rows.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_double, ctypes.c_double]
         lib.oracle_tt_row.argtypes = [P, P, P, P, ctypes.c_int64, P]
         _lib = lib
     return _lib
@@ -183,6 +188,31 @@ def sgd(p, q, ranks, E, cores, grads, touched, lr, cache_rows=None, grad_cache=N
                              _ptr(np.ascontiguousarray(touched_cache)), rows.shape[0],
                              rows.shape[1], float(lr))
     return new, rows
+
+
+def adagrad(p, q, ranks, E, cores, states, grads, touched, lr, eps, cache_rows=None,
+            cache_state=None, grad_cache=None, touched_cache=None):
+    """Diagonal Adagrad on touched slices (copies): per parameter, S += g^2 and
+    x -= lr * g / (sqrt(S) + eps).  states: T lists of fp32 arrays shaped like the
+    cores.  Returns (new_cores, new_states, new_cache_rows, new_cache_state)."""
+    T = len(cores)
+    s = _shape(p, q, ranks, E, T)
+    new = [[_f32(c).copy() for c in tbl] for tbl in cores]
+    st = [[_f32(c).copy() for c in tbl] for tbl in states]
+    for t in range(T):
+        for k in range(3):
+            _L().oracle_adagrad_core(ctypes.byref(s), k, _ptr(new[t][k]), _ptr(st[t][k]),
+                                     _ptr(np.ascontiguousarray(grads[t][k])),
+                                     _ptr(np.ascontiguousarray(touched[t][k])), float(lr),
+                                     float(eps))
+    rows = rst = None
+    if cache_rows is not None:
+        rows = _f32(cache_rows).copy()
+        rst = _f32(cache_state).copy()
+        _L().oracle_adagrad_rows(_ptr(rows), _ptr(rst), _ptr(np.ascontiguousarray(grad_cache)),
+                                 _ptr(np.ascontiguousarray(touched_cache)), rows.shape[0],
+                                 rows.shape[1], float(lr), float(eps))
+    return new, st, rows, rst
 
 
 # ---------------------------------------------------------------- integer side

@@ -271,6 +271,81 @@ def test_sgd_step_invariants():
     assert abs((l0 - l1) - eps * gnorm) < 0.05 * eps * gnorm
 
 
+def _torch_adagrad(params, grads, states, lr, eps):
+    """One step of torch.optim.Adagrad (float64, no decay) from the given running sums."""
+    P = [torch.tensor(x.astype(np.float64)) for x in params]
+    opt = torch.optim.Adagrad(P, lr=lr, eps=eps, lr_decay=0.0, weight_decay=0.0,
+                              initial_accumulator_value=0.0)
+    for x, g, s0 in zip(P, grads, states):
+        x.grad = torch.tensor(np.asarray(g, dtype=np.float64))
+        opt.state[x]["sum"].copy_(torch.tensor(s0.astype(np.float64)))
+    opt.step()
+    return [x.numpy() for x in P], [opt.state[x]["sum"].numpy() for x in P]
+
+
+def test_adagrad_matches_torch_optim_adagrad():
+    """Library routine: torch.optim.Adagrad (float64) fed the oracle's dense gradients
+    (zero outside the touched slices) and the same running sums.  eps is large enough
+    that its place (after the root) shows.  Pins the core and the cache-row update and
+    that untouched slices and their sums keep their bits."""
+    rng = _rng(23)
+    wl = W.WORKLOADS["tiny"]
+    cores = W.make_cores(wl)
+    b = W.make_batch(wl, 0)
+    idx, off = b["indices"], b["offsets"]
+    other = W.make_batch(wl, 3)["indices"]
+    cached = oracle.select_cache(oracle.count_frequencies([idx[:6], other]), 8)
+    rows = oracle.populate_rows(wl.p, wl.q, wl.ranks, cores[0], cached).astype(np.float32)
+    slots = oracle.lookup_slots(cached, idx)
+    args = (wl.p, wl.q, wl.ranks, wl.E)
+    grads, touched, gc, tc = oracle.backward(*args, cores, idx, off, 8, b["grad_out"],
+                                             slots=slots, cache_size=8)
+    states = [[rng.uniform(0.2, 2.0, c.shape).astype(np.float32) for c in cores[0]]]
+    rstate = rng.uniform(0.2, 2.0, rows.shape).astype(np.float32)
+    lr, eps = 0.05, 0.3
+    new, st, nrows, nrst = oracle.adagrad(*args, cores, states, grads, touched, lr, eps,
+                                          cache_rows=rows, cache_state=rstate, grad_cache=gc,
+                                          touched_cache=tc)
+    ref_x, ref_s = _torch_adagrad(list(cores[0]) + [rows], list(grads[0]) + [gc],
+                                  list(states[0]) + [rstate], lr, eps)
+    got_x, got_s = list(new[0]) + [nrows], list(st[0]) + [nrst]
+    for k in range(4):
+        np.testing.assert_allclose(got_x[k], ref_x[k], rtol=1e-6, atol=1e-7)
+        np.testing.assert_allclose(got_s[k], ref_s[k], rtol=1e-6, atol=1e-7)
+    for k in range(3):
+        for ik in np.flatnonzero(touched[0][k] == 0):
+            sl = (slice(None), ik)
+            assert np.array_equal(new[0][k][sl].view(np.uint32), cores[0][k][sl].view(np.uint32))
+            assert np.array_equal(st[0][k][sl].view(np.uint32), states[0][k][sl].view(np.uint32))
+    assert any(np.any(touched[0][k] == 0) for k in range(3)) and np.any(tc == 0) and np.any(tc == 1)
+    for sl in np.flatnonzero(tc == 0):
+        assert np.array_equal(nrows[sl].view(np.uint32), rows[sl].view(np.uint32))
+
+
+def test_adagrad_first_step_closed_form():
+    """Closed form: from zero running sums with eps = 0 the first Adagrad step moves
+    every parameter with a nonzero gradient by lr against its sign, and leaves
+    S = g^2."""
+    wl = W.WORKLOADS["tiny"]
+    cores = W.make_cores(wl)
+    b = W.make_batch(wl, 1)
+    args = (wl.p, wl.q, wl.ranks, wl.E)
+    grads, touched, _, _ = oracle.backward(*args, cores, b["indices"], b["offsets"], 8,
+                                           b["grad_out"])
+    zeros = [[np.zeros_like(c) for c in cores[0]]]
+    lr = 0.125
+    new, st, _, _ = oracle.adagrad(*args, cores, zeros, grads, touched, lr, 0.0)
+    for k in range(3):
+        g = grads[0][k]
+        nz = g != 0
+        assert nz.sum() > 0
+        exp = (cores[0][k].astype(np.float64) - lr * np.sign(g)).astype(np.float32)
+        # S holds g^2 rounded to fp32, so g / sqrt(S) is +-1 to within 2^-24
+        np.testing.assert_allclose(new[0][k][nz], exp[nz], rtol=2e-7, atol=1e-7)
+        np.testing.assert_allclose(st[0][k][nz], (g * g)[nz], rtol=1e-7)
+        assert np.array_equal(new[0][k][~nz], cores[0][k][~nz])
+
+
 def test_cache_semantics():
     """Right after populate, a hit reads exactly the TT row; its gradient goes to
     the cache row (sum of w * dY) and not to the cores."""
@@ -428,6 +503,15 @@ _MUTANTS = [
     # off-by-one bag: table of a bag
     ("const int64_t t = b / B;\n        for (int64_t n = off[b]; n < off[b + 1]; ++n) {\n            const double w = psw ? (double)psw[n] : 1.0;\n            if (slot && slot[n] >= 0) {\n                for (int64_t j = 0; j < D; ++j) row[j]",
      "const int64_t t = (b + 1) / B % s->num_tables;\n        for (int64_t n = off[b]; n < off[b + 1]; ++n) {\n            const double w = psw ? (double)psw[n] : 1.0;\n            if (slot && slot[n] >= 0) {\n                for (int64_t j = 0; j < D; ++j) row[j]"),
+    # Adagrad: eps under the root
+    ("core[e] = (float)((double)core[e] - lr * g / (sqrt((double)state[e]) + eps));",
+     "core[e] = (float)((double)core[e] - lr * g / sqrt((double)state[e] + eps));"),
+    # Adagrad: the step taken with the sum before this gradient
+    ("state[e] = (float)((double)state[e] + g * g);\n                    core[e] = (float)((double)core[e] - lr * g / (sqrt((double)state[e]) + eps));",
+     "core[e] = (float)((double)core[e] - lr * g / (sqrt((double)state[e]) + eps));\n                    state[e] = (float)((double)state[e] + g * g);"),
+    # Adagrad on cache rows: the squared gradient not added
+    ("state[e] = (float)((double)state[e] + g * g);\n            rows[e]",
+     "state[e] = (float)((double)state[e] + g);\n            rows[e]"),
 ]
 
 
@@ -456,7 +540,8 @@ def test_pins_catch_planted_mistakes(mi, tmp_path, monkeypatch):
             test_degenerate_tt_is_plain_embedding_bag,
             test_pooling_matches_torch_embedding_bag_on_decompressed_table,
             test_pooling_invariants, test_backward_equals_exact_finite_differences,
-            test_backward_matches_torch_autograd, test_sgd_step_invariants]
+            test_backward_matches_torch_autograd, test_sgd_step_invariants,
+            test_adagrad_matches_torch_optim_adagrad, test_adagrad_first_step_closed_form]
     try:
         for f in pins:
             try:
