@@ -142,7 +142,8 @@ int tt_bag_backward_sgd(const tt_desc *desc, float *const cores[3],
  * match it does nothing but set TT_DEV_STALE_PLAN in *dev_status.  The caller
  * must re-plan after changing the CONTENTS of those buffers (the fingerprint
  * cannot see that).  tt_bag_forward = plan + forward_planned, and
- * tt_bag_backward_sgd = plan + backward_sgd_planned.
+ * tt_bag_backward_sgd = plan + backward_sgd_planned (the same for the Adagrad and
+ * gradient variants below).
  */
 int tt_bag_plan(const tt_desc *desc, const int64_t *indices, int64_t nnz,
                 const int64_t *offsets, int64_t num_bags, const float *per_sample_weights,
@@ -160,6 +161,61 @@ int tt_bag_backward_sgd_planned(const tt_desc *desc, float *const cores[3],
                                 int64_t num_bags, const float *per_sample_weights,
                                 const tt_cache_view *cache, const float *grad_out, float lr,
                                 void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
+
+/*
+ * Backward with fused Adagrad ("Parameters": `sparse`=True with the Adagrad
+ * optimizer type, whose `eps` is added to the denominator; the update itself is the
+ * diagonal Adagrad of Duchi, Hazan and Singer 2011).  Same gradient as
+ * tt_bag_backward_sgd; then, for every element x of a touched core slice or cache
+ * row, with its gradient g and its running sum of squared gradients S:
+ *     S <- S + g*g;   x <- x - lr * g / (sqrt(S) + eps)
+ * Untouched slices/rows keep x and S.
+ *   state      [3] device pointers, state[k] in the layout of cores[k] (fp32; start
+ *              at zero or any non-negative value); updated in place
+ *   state_rows [cache_size][D] fp32 running sums of the cache rows (required with a
+ *              cache, ignored without)
+ *   eps        finite and >= 0; lr finite
+ * Bit-reproducible run to run like tt_bag_backward_sgd.
+ */
+int tt_bag_backward_adagrad(const tt_desc *desc, float *const cores[3],
+                            const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                            int64_t num_bags, const float *per_sample_weights,
+                            const tt_cache_view *cache, const float *grad_out, float lr, float eps,
+                            float *const state[3], float *state_rows,
+                            void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
+
+int tt_bag_backward_adagrad_planned(const tt_desc *desc, float *const cores[3],
+                                    const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                                    int64_t num_bags, const float *per_sample_weights,
+                                    const tt_cache_view *cache, const float *grad_out, float lr,
+                                    float eps, float *const state[3], float *state_rows,
+                                    void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
+
+/*
+ * Backward without an update ("Parameters": `sparse`=False, the gradient with
+ * respect to the TT cores or the cache is returned to an external optimizer).  The
+ * cores and cache rows are only read.
+ *   grad_cores [3] device pointers, grad_cores[k] in the layout of cores[k] (T
+ *              tables, slice-major), fully overwritten: dL/dG on the slices this
+ *              batch touches, zero elsewhere
+ *   grad_rows  [cache_size][D] fp32, fully overwritten: dL/d(row) for rows with
+ *              hits (the sum of w * grad_out over them), zero elsewhere (required
+ *              with a cache, ignored without)
+ * An empty batch (nnz = 0) writes all-zero gradients.  Bit-reproducible run to run.
+ */
+int tt_bag_backward_grad(const tt_desc *desc, const float *const cores[3],
+                         const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                         int64_t num_bags, const float *per_sample_weights,
+                         const tt_cache_view *cache, const float *grad_out,
+                         float *const grad_cores[3], float *grad_rows,
+                         void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
+
+int tt_bag_backward_grad_planned(const tt_desc *desc, const float *const cores[3],
+                                 const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                                 int64_t num_bags, const float *per_sample_weights,
+                                 const tt_cache_view *cache, const float *grad_out,
+                                 float *const grad_cores[3], float *grad_rows,
+                                 void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
 
 /*
  * The grouping step of both passes, exposed for inspection and tests: splits

@@ -56,6 +56,16 @@ _SIG = {
                                               ctypes.c_size_t, _P, _P]),
     "tt_bag_backward_sgd_planned": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P,
                                                    ctypes.c_float, _P, ctypes.c_size_t, _P, _P]),
+    "tt_bag_backward_adagrad": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P,
+                                               ctypes.c_float, ctypes.c_float, _P, _P, _P,
+                                               ctypes.c_size_t, _P, _P]),
+    "tt_bag_backward_adagrad_planned": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P,
+                                                       ctypes.c_float, ctypes.c_float, _P, _P,
+                                                       _P, ctypes.c_size_t, _P, _P]),
+    "tt_bag_backward_grad": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P, _P, _P, _P,
+                                            ctypes.c_size_t, _P, _P]),
+    "tt_bag_backward_grad_planned": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P, _P,
+                                                    _P, _P, ctypes.c_size_t, _P, _P]),
     "tt_bag_route": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _I64, _P, _P, _P, ctypes.c_size_t,
                                     _P, _P]),
     "tt_cache_create": (ctypes.c_int, [_P, _P, _I64, _I64]),
@@ -237,6 +247,72 @@ def tt_bag_backward_sgd(desc: TTDesc, cores, indices, offsets, num_bags: int, gr
                                    float(lr), _ptr(ws), ws.numel(), _ptr(dev_status),
                                    _stream(stream))
     _check("tt_bag_backward_sgd_planned" if planned else "tt_bag_backward_sgd", rc)
+
+
+def _batch_args(desc, indices, offsets, num_bags, grad_out, per_sample_weights, cache, ws,
+                dev_status):
+    _need(indices, torch.int64, "indices")
+    _need(offsets, torch.int64, "offsets")
+    _need(grad_out, torch.float32, "grad_out")
+    if per_sample_weights is not None:
+        _need(per_sample_weights, torch.float32, "per_sample_weights")
+    view, csize = _cache_view(cache)
+    if ws is None:
+        ws = workspace(desc, indices.numel(), num_bags, csize or 0, indices.device)
+    _need(ws, torch.uint8, "ws")
+    if dev_status is not None:
+        _need(dev_status, torch.int32, "dev_status")
+    return view, csize, ws
+
+
+def _rows_arg(t, csize, name):
+    if not csize:
+        return None
+    if t is None:
+        raise ValueError("%s is required with a cache" % name)
+    _need(t, torch.float32, name)
+    return t
+
+
+def tt_bag_backward_adagrad(desc: TTDesc, cores, indices, offsets, num_bags: int, grad_out,
+                            lr: float, eps: float, state, state_rows=None,
+                            per_sample_weights=None, cache=None, ws=None, dev_status=None,
+                            stream=None, planned: bool = False) -> None:
+    """In-place fused Adagrad on the touched cores / cache rows; state = three running-sum
+    tensors shaped like the cores (and state_rows for the cache rows), updated in place."""
+    view, csize, ws = _batch_args(desc, indices, offsets, num_bags, grad_out, per_sample_weights,
+                                  cache, ws, dev_status)
+    st = _cores(state)
+    sr = _rows_arg(state_rows, csize, "state_rows")
+    name = "tt_bag_backward_adagrad_planned" if planned else "tt_bag_backward_adagrad"
+    rc = getattr(lib(), name)(ctypes.byref(desc), _cores(cores), _ptr(indices), indices.numel(),
+                              _ptr(offsets), int(num_bags), _ptr(per_sample_weights),
+                              None if view is None else ctypes.byref(view), _ptr(grad_out),
+                              float(lr), float(eps), st, _ptr(sr), _ptr(ws), ws.numel(),
+                              _ptr(dev_status), _stream(stream))
+    _check(name, rc)
+
+
+def tt_bag_backward_grad(desc: TTDesc, cores, indices, offsets, num_bags: int, grad_out,
+                         grad_cores=None, grad_rows=None, per_sample_weights=None, cache=None,
+                         ws=None, dev_status=None, stream=None, planned: bool = False):
+    """Gradients with respect to the cores (and cache rows), fully overwritten; the
+    cores are not changed.  Returns (grad_cores, grad_rows)."""
+    view, csize, ws = _batch_args(desc, indices, offsets, num_bags, grad_out, per_sample_weights,
+                                  cache, ws, dev_status)
+    if grad_cores is None:
+        grad_cores = [torch.empty_like(c) for c in cores]
+    if csize and grad_rows is None:
+        grad_rows = torch.empty_like(cache[1])
+    gr = _rows_arg(grad_rows, csize, "grad_rows")
+    name = "tt_bag_backward_grad_planned" if planned else "tt_bag_backward_grad"
+    rc = getattr(lib(), name)(ctypes.byref(desc), _cores(cores), _ptr(indices), indices.numel(),
+                              _ptr(offsets), int(num_bags), _ptr(per_sample_weights),
+                              None if view is None else ctypes.byref(view), _ptr(grad_out),
+                              _cores(grad_cores), _ptr(gr), _ptr(ws), ws.numel(),
+                              _ptr(dev_status), _stream(stream))
+    _check(name, rc)
+    return grad_cores, gr
 
 
 def tt_bag_route(desc: TTDesc, indices, offsets, num_bags: int, slots=None, cache_size: int = 0,

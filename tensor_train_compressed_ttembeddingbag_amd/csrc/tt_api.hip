@@ -294,28 +294,102 @@ int tt_bag_forward_planned(const tt_desc *desc, const float *const cores[3],
   return finish(e);
 }
 
+}  // extern "C"
+
+namespace {
+
+// what the backward does with the gradients (see apply_update)
+struct Update {
+  int mode;
+  float lr, eps;
+  float *const *aux;  // [3] per core: Adagrad running sums or gradient outputs
+  float *aux_rows;    // the same for the cache rows
+};
+
+// Every backward entry point: argument checks, then (plan_first) the grouping, then
+// the run sums of cache hits, the contraction and the segment sums with the update.
+int backward_call(const tt_desc *desc, float *const cores[3], const int64_t *indices, int64_t nnz,
+                  const int64_t *offsets, int64_t num_bags, const float *psw,
+                  const tt_cache_view *cache, const float *grad_out, const Update &u, void *ws,
+                  size_t ws_bytes, int32_t *dev_status, void *stream, bool plan_first) {
+  Plan P;
+  int rc = prepare(&P, desc, indices, nnz, offsets, num_bags, psw, cache, ws, ws_bytes,
+                   dev_status);
+  if (rc) return rc;
+  if ((rc = check_cores(cores)) || !grad_out) return rc ? rc : TT_EINVAL;
+  DevArgs &a = P.a;
+  if (u.mode != UPD_GRAD && !std::isfinite(u.lr)) return TT_EINVAL;
+  if (u.mode == UPD_ADAGRAD && !(std::isfinite(u.eps) && u.eps >= 0.f)) return TT_EINVAL;
+  if (u.mode != UPD_SGD) {
+    if (!u.aux || !u.aux[0] || !u.aux[1] || !u.aux[2]) return TT_EINVAL;
+    if (a.cache_size > 0 && !u.aux_rows) return TT_EINVAL;
+    a.X1 = u.aux[0]; a.X2 = u.aux[1]; a.X3 = u.aux[2];
+    a.Xc = u.aux_rows;
+  }
+  a.upd = u.mode;
+  a.lr = u.lr;
+  a.eps = u.eps;
+  a.psw = psw;
+  a.G1 = cores[0]; a.G2 = cores[1]; a.G3 = cores[2];
+  a.dY = grad_out;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (u.mode == UPD_GRAD) {
+    // gradient outputs are overwritten whole: rows without hits are cleared here, core
+    // slices without contributions by the segment sums (or here for an empty batch)
+    if (a.cache_size > 0) e = launch_zero(a.Xc, (size_t)a.cache_size * a.D, s);
+    if (nnz == 0) {
+      const size_t T = (size_t)a.T;
+      if (e == hipSuccess) e = launch_zero(a.X1, T * a.p1 * a.q1 * a.R1, s);
+      if (e == hipSuccess) e = launch_zero(a.X2, T * a.p2 * a.R1 * a.q2 * a.R2, s);
+      if (e == hipSuccess) e = launch_zero(a.X3, T * a.p3 * a.R2 * a.q3, s);
+      return finish(e);
+    }
+  } else if (nnz == 0) {
+    return TT_OK;
+  }
+  if (e == hipSuccess && plan_first) e = launch_route(a, s);
+  if (e == hipSuccess) e = launch_runsum(a, s);
+  if (e == hipSuccess) e = launch_bwd(a, P.RP, P.lds_bwd, s);
+  if (e == hipSuccess) e = launch_seg(a, s);
+  return finish(e);
+}
+
+}  // namespace
+
+extern "C" {
+
 int tt_bag_backward_sgd_planned(const tt_desc *desc, float *const cores[3],
                                 const int64_t *indices, int64_t nnz, const int64_t *offsets,
                                 int64_t num_bags, const float *per_sample_weights,
                                 const tt_cache_view *cache, const float *grad_out, float lr,
                                 void *ws, size_t ws_bytes, int32_t *dev_status, void *stream) {
-  Plan P;
-  int rc = prepare(&P, desc, indices, nnz, offsets, num_bags, per_sample_weights, cache, ws,
-                   ws_bytes, dev_status);
-  if (rc) return rc;
-  if ((rc = check_cores(cores)) || !grad_out) return rc ? rc : TT_EINVAL;
-  if (!std::isfinite(lr)) return TT_EINVAL;
-  if (nnz == 0) return TT_OK;
-  DevArgs &a = P.a;
-  a.psw = per_sample_weights;
-  a.G1 = cores[0]; a.G2 = cores[1]; a.G3 = cores[2];
-  a.dY = grad_out;
-  a.lr = lr;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_runsum(a, s);
-  if (e == hipSuccess) e = launch_bwd(a, P.RP, P.lds_bwd, s);
-  if (e == hipSuccess) e = launch_seg(a, s);
-  return finish(e);
+  const Update u{UPD_SGD, lr, 0.f, nullptr, nullptr};
+  return backward_call(desc, cores, indices, nnz, offsets, num_bags, per_sample_weights, cache,
+                       grad_out, u, ws, ws_bytes, dev_status, stream, false);
+}
+
+int tt_bag_backward_adagrad_planned(const tt_desc *desc, float *const cores[3],
+                                    const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                                    int64_t num_bags, const float *per_sample_weights,
+                                    const tt_cache_view *cache, const float *grad_out, float lr,
+                                    float eps, float *const state[3], float *state_rows, void *ws,
+                                    size_t ws_bytes, int32_t *dev_status, void *stream) {
+  const Update u{UPD_ADAGRAD, lr, eps, state, state_rows};
+  return backward_call(desc, cores, indices, nnz, offsets, num_bags, per_sample_weights, cache,
+                       grad_out, u, ws, ws_bytes, dev_status, stream, false);
+}
+
+int tt_bag_backward_grad_planned(const tt_desc *desc, const float *const cores[3],
+                                 const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                                 int64_t num_bags, const float *per_sample_weights,
+                                 const tt_cache_view *cache, const float *grad_out,
+                                 float *const grad_cores[3], float *grad_rows, void *ws,
+                                 size_t ws_bytes, int32_t *dev_status, void *stream) {
+  const Update u{UPD_GRAD, 0.f, 0.f, grad_cores, grad_rows};
+  return backward_call(desc, (float *const *)cores, indices, nnz, offsets, num_bags,
+                       per_sample_weights, cache, grad_out, u, ws, ws_bytes, dev_status, stream,
+                       false);
 }
 
 int tt_bag_forward(const tt_desc *desc, const float *const cores[3], const int64_t *indices,
@@ -339,19 +413,32 @@ int tt_bag_backward_sgd(const tt_desc *desc, float *const cores[3], const int64_
                         const float *per_sample_weights, const tt_cache_view *cache,
                         const float *grad_out, float lr, void *ws, size_t ws_bytes,
                         int32_t *dev_status, void *stream) {
-  Plan P;
-  int rc = prepare(&P, desc, indices, nnz, offsets, num_bags, per_sample_weights, cache, ws,
-                   ws_bytes, dev_status);
-  if (rc) return rc;
-  if ((rc = check_cores(cores)) || !grad_out) return rc ? rc : TT_EINVAL;
-  if (!std::isfinite(lr)) return TT_EINVAL;
-  if (nnz == 0) return TT_OK;
-  rc = tt_bag_plan(desc, indices, nnz, offsets, num_bags, per_sample_weights, cache, ws, ws_bytes,
-                   dev_status, stream);
-  if (rc) return rc;
-  return tt_bag_backward_sgd_planned(desc, cores, indices, nnz, offsets, num_bags,
-                                     per_sample_weights, cache, grad_out, lr, ws, ws_bytes,
-                                     dev_status, stream);
+  const Update u{UPD_SGD, lr, 0.f, nullptr, nullptr};
+  return backward_call(desc, cores, indices, nnz, offsets, num_bags, per_sample_weights, cache,
+                       grad_out, u, ws, ws_bytes, dev_status, stream, true);
+}
+
+int tt_bag_backward_adagrad(const tt_desc *desc, float *const cores[3], const int64_t *indices,
+                            int64_t nnz, const int64_t *offsets, int64_t num_bags,
+                            const float *per_sample_weights, const tt_cache_view *cache,
+                            const float *grad_out, float lr, float eps, float *const state[3],
+                            float *state_rows, void *ws, size_t ws_bytes, int32_t *dev_status,
+                            void *stream) {
+  const Update u{UPD_ADAGRAD, lr, eps, state, state_rows};
+  return backward_call(desc, cores, indices, nnz, offsets, num_bags, per_sample_weights, cache,
+                       grad_out, u, ws, ws_bytes, dev_status, stream, true);
+}
+
+int tt_bag_backward_grad(const tt_desc *desc, const float *const cores[3],
+                         const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                         int64_t num_bags, const float *per_sample_weights,
+                         const tt_cache_view *cache, const float *grad_out,
+                         float *const grad_cores[3], float *grad_rows, void *ws, size_t ws_bytes,
+                         int32_t *dev_status, void *stream) {
+  const Update u{UPD_GRAD, 0.f, 0.f, grad_cores, grad_rows};
+  return backward_call(desc, (float *const *)cores, indices, nnz, offsets, num_bags,
+                       per_sample_weights, cache, grad_out, u, ws, ws_bytes, dev_status, stream,
+                       true);
 }
 
 // copies the grouping order: valid elements first (see tt_bag.h)

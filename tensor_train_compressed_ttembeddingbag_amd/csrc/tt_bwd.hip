@@ -26,6 +26,8 @@
 // links record where they are.  k_seg then sums every partial per slice in a fixed
 // order and applies SGD: dG1 / dG3 in the (t,i1)- / (t,i3)-order, dG2 in
 // work-item order.
+#include <algorithm>
+
 #include "tt_device.h"
 #include "tt_mfma.h"
 
@@ -507,7 +509,12 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
     const float *part = one ? a.part1 : a.part3;
     const int W = one ? a.q1 * a.R1 : a.R2 * a.q3;
     float *dst = one ? a.G1 + (size_t)seg * W : a.G3 + (size_t)seg * W;
-    if (beg >= end) return;
+    float *aux = one ? a.X1 + (size_t)seg * W : a.X3 + (size_t)seg * W;
+    if (beg >= end) {  // an untouched slice: a zero gradient, no update
+      if (a.upd == UPD_GRAD)
+        for (int c = tid; c < W; c += SEG_T) aux[c] = 0.f;
+      return;
+    }
     // columns: 4 per lane when W allows 16-byte rows, lanes per row LPR, row groups NRG
     const int VEC = (W & 3) == 0 ? 4 : 1;
     const int LPR = min(SEG_T, (W + VEC - 1) / VEC), NRG = SEG_T / LPR;
@@ -552,7 +559,7 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
         }
         __syncthreads();
       }
-      // row groups summed in group order, then SGD
+      // row groups summed in group order, then the update
       if (rg < NRG)
 #pragma unroll
         for (int j = 0; j < 4; ++j) s_red[(rg * LPR + cl) * 4 + j] = acc[j];
@@ -561,7 +568,7 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
         const int c = c0 + t2;
         float sum = 0.f;
         for (int r = 0; r < NRG; ++r) sum += s_red[(r * LPR + t2 / VEC) * 4 + t2 % VEC];
-        if (c < W) dst[c] -= a.lr * sum;
+        if (c < W) apply_update(a, dst, aux, c, sum);
       }
       __syncthreads();
     }
@@ -569,18 +576,25 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
   }
   if (bid < nA + nC + G) {
     const int g = gi;
-    if (i0 >= i1) return;
     const int slice2 = a.R1 * a.q2 * a.R2;  // <= 64 * 64 * 64
-    float *dst = a.G2 + (size_t)g * slice2;
-    // per thread: up to 16 columns at once (the whole slice for ranks <= 32), their old
-    // values and 2 items' partials in flight; items summed in item order
+    float *dst = a.G2 + (size_t)g * slice2, *aux = a.X2 + (size_t)g * slice2;
+    if (i0 >= i1) {  // an untouched slice: a zero gradient, no update
+      if (a.upd == UPD_GRAD)
+        for (int e = tid; e < slice2; e += SEG_T) aux[e] = 0.f;
+      return;
+    }
+    // per thread: up to 16 columns at once (the whole slice for ranks <= 32), the
+    // values the update reads and 2 items' partials in flight; items summed in item order
     constexpr int CU = 16;
+    const bool rd_x = a.upd != UPD_GRAD, rd_aux = a.upd == UPD_ADAGRAD;
     for (int e0 = tid; e0 < slice2; e0 += SEG_T * CU) {
-      float acc[CU], old[CU];
+      float acc[CU], old[CU], oaux[CU];
 #pragma unroll
       for (int u = 0; u < CU; ++u) {
         acc[u] = 0.f;
-        old[u] = dst[min(e0 + u * SEG_T, slice2 - 1)];
+        const int e = min(e0 + u * SEG_T, slice2 - 1);
+        old[u] = rd_x ? dst[e] : 0.f;
+        oaux[u] = rd_aux ? aux[e] : 0.f;
       }
       for (int it0 = i0; it0 < i1; it0 += 2) {
         float v[2][CU];
@@ -597,8 +611,19 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
             for (int u = 0; u < CU; ++u) acc[u] += v[k][u];
       }
 #pragma unroll
-      for (int u = 0; u < CU; ++u)
-        if (e0 + u * SEG_T < slice2) dst[e0 + u * SEG_T] = old[u] - a.lr * acc[u];
+      for (int u = 0; u < CU; ++u) {
+        const int e = e0 + u * SEG_T;
+        if (e >= slice2) continue;
+        if (a.upd == UPD_GRAD) {
+          aux[e] = acc[u];
+        } else if (a.upd == UPD_ADAGRAD) {
+          const float S = oaux[u] + acc[u] * acc[u];
+          aux[e] = S;
+          dst[e] = old[u] - a.lr * acc[u] / (sqrtf(S) + a.eps);
+        } else {
+          dst[e] = old[u] - a.lr * acc[u];
+        }
+      }
     }
     return;
   }
@@ -618,9 +643,22 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
         if (q.y != kA || q.z != kB) break;
         acc += a.frag[(size_t)p * a.D + d];
       }
-      a.crows[(size_t)slot * a.D + d] -= a.lr * acc;
+      apply_update(a, a.crows, a.Xc, (size_t)slot * a.D + d, acc);
     }
   }
+}
+
+// x[0 .. n) = 0 (gradient outputs of rows that get no contribution)
+__global__ __launch_bounds__(256) void k_zero(float *x, size_t n) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) x[i] = 0.f;
+}
+
+hipError_t launch_zero(float *x, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const unsigned nb = (unsigned)std::min<size_t>((n + 1023) / 1024, 16384);
+  tt_launch(K_ZERO, k_zero, dim3(nb), dim3(256), 0, s, x, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_seg(const DevArgs &a, hipStream_t s) {

@@ -72,6 +72,10 @@ struct DevArgs {
   float *Y;
   const float *dY;
   float lr;
+  int upd;          // UPD_SGD, UPD_ADAGRAD or UPD_GRAD: what the backward does with a gradient
+  float eps;        // Adagrad: added to the root of the running sum
+  float *X1, *X2, *X3, *Xc;  // per core / cache rows, in their layout: Adagrad running
+                             // sums (UPD_ADAGRAD) or the gradient outputs (UPD_GRAD)
   int32_t *status;
   // workspace
   unsigned long long *ctr;  // [3] epoch-tagged completion counters (no zeroing needed)
@@ -121,6 +125,26 @@ __device__ __forceinline__ void set_status(int32_t *st, int bit) {
   if (st) atomicOr(st, bit);
 }
 
+// update modes of the backward
+enum { UPD_SGD = 0, UPD_ADAGRAD = 1, UPD_GRAD = 2 };
+
+// The update of parameter x[i] (aux[i] in the same layout) with gradient g:
+//   SGD      x -= lr g
+//   Adagrad  S = aux + g^2 -> aux;  x -= lr g / (sqrt(S) + eps)
+//   gradient aux = g (x unchanged)
+__device__ __forceinline__ void apply_update(const DevArgs &a, float *x, float *aux, size_t i,
+                                             float g) {
+  if (a.upd == UPD_GRAD) {
+    aux[i] = g;
+  } else if (a.upd == UPD_ADAGRAD) {
+    const float S = aux[i] + g * g;
+    aux[i] = S;
+    x[i] -= a.lr * g / (sqrtf(S) + a.eps);
+  } else {
+    x[i] -= a.lr * g;
+  }
+}
+
 // device status bit for a planned call whose workspace holds another plan
 constexpr int DEV_STALE_PLAN = 16;
 
@@ -128,7 +152,7 @@ constexpr int DEV_STALE_PLAN = 16;
 // kernels named by the optional per-kernel timer (tt_prof.hip)
 enum KernelId {
   K_ROUTE_COOP, K_ROUTE_A, K_ROUTE_B, K_ROUTE_C, K_FWD, K_RUNSUM, K_BWD, K_SEG,
-  K_CACHE_LOOKUP, K_YINIT, K_COUNT
+  K_CACHE_LOOKUP, K_YINIT, K_ZERO, K_COUNT
 };
 // Start / stop events for one launch of kernel `id`, recorded by the kernel's own
 // dispatch (so they time the kernel alone), or null events while timing is off.
@@ -147,6 +171,7 @@ hipError_t launch_route(const DevArgs &a, hipStream_t s);   // the grouping kern
 hipError_t launch_runsum(const DevArgs &a, hipStream_t s);
 hipError_t launch_yinit(const DevArgs &a, hipStream_t s);
 hipError_t launch_seg(const DevArgs &a, hipStream_t s);
+hipError_t launch_zero(float *x, size_t n, hipStream_t s);  // x[0 .. n) = 0
 hipError_t launch_fwd(const DevArgs &a, int RP, size_t lds, hipStream_t s);
 hipError_t launch_bwd(const DevArgs &a, int RP, size_t lds, hipStream_t s);
 size_t fwd_lds_bytes(int RP, int JB, int P, int q3, int D, int sw);

@@ -1,0 +1,261 @@
+"""GPU parity of the backward variants: gradients returned instead of an update, and
+the fused Adagrad update, against the CPU oracle (through the C ABI).
+
+Gradients are compared per tensor within 1e-4 of the oracle's fp64 gradients
+(max|x - x*| / max|x*|); every element of the gradient outputs is written (the
+buffers start as NaN) and untouched slices read exactly zero.  Adagrad is compared
+as deltas: the parameter deltas new - old and the running-sum deltas against the
+oracle's, per tensor within 1e-4; untouched slices keep the bits of both.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tensor_train_compressed_ttembeddingbag_amd import abi, workloads as W
+from helpers import TOL, gpu_cores, host_cores, rel_err, to_dev
+from test_gpu_parity import SMALL
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _desc(wl):
+    return abi.make_desc(wl.p, wl.q, wl.ranks, wl.E, wl.num_tables)
+
+
+def _nan_like(ts):
+    return [torch.full_like(t, float("nan")) for t in ts]
+
+
+def _oracle_grads(wl, cores, b, slots=None, cache_size=0):
+    return oracle.backward(wl.p, wl.q, wl.ranks, wl.E, cores, b["indices"], b["offsets"],
+                           b["num_bags"], b["grad_out"],
+                           per_sample_weights=b["per_sample_weights"], slots=slots,
+                           cache_size=cache_size)
+
+
+def _check_grads(wl, gk_dev, grads, touched):
+    got = host_cores(wl, gk_dev)
+    for t in range(wl.num_tables):
+        for k in range(3):
+            x = got[t][k]
+            assert not np.isnan(x).any(), (t, k)
+            e = rel_err(x, grads[t][k])
+            assert e <= TOL, "table %d core %d: gradient rel err %.3g" % (t, k, e)
+            sl = np.moveaxis(x, 1, 0)
+            for ik in np.flatnonzero(touched[t][k] == 0):
+                assert np.all(sl[ik] == 0.0), (t, k, ik)
+
+
+def _grad_parity(wl, seed=0):
+    cores = W.make_cores(wl)
+    b = W.make_batch(wl, seed)
+    g = gpu_cores(wl, cores)
+    bits = [x.clone() for x in g]
+    d = to_dev(b)
+    out = _nan_like(g)
+    abi.tt_bag_backward_grad(_desc(wl), g, d["indices"], d["offsets"], b["num_bags"],
+                             d["grad_out"], grad_cores=out,
+                             per_sample_weights=d["per_sample_weights"])
+    torch.cuda.synchronize()
+    for x, y in zip(g, bits):  # the cores are only read
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+    grads, touched, _, _ = _oracle_grads(wl, cores, b)
+    _check_grads(wl, out, grads, touched)
+    return out
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_gradients_small_shapes(wl):
+    _say("case grad", wl.name)
+    _grad_parity(wl)
+
+
+def test_gradients_readme_shape_full():
+    _say("case grad readme full")
+    _grad_parity(W.WORKLOADS["readme"])
+
+
+def test_gradients_are_bit_reproducible_and_planned_equals_stateless():
+    _say("case grad reproducible / planned")
+    wl = W.WORKLOADS["readme"]
+    cores = W.make_cores(wl)
+    b = W.make_batch(wl, 1)
+    g = gpu_cores(wl, cores)
+    d = to_dev(b)
+    desc = _desc(wl)
+    B = b["num_bags"]
+    a1, _ = abi.tt_bag_backward_grad(desc, g, d["indices"], d["offsets"], B, d["grad_out"])
+    ws = abi.tt_bag_plan(desc, d["indices"], d["offsets"], B)
+    a2, _ = abi.tt_bag_backward_grad(desc, g, d["indices"], d["offsets"], B, d["grad_out"],
+                                     grad_cores=_nan_like(g), ws=ws, planned=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a1, a2):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+
+
+def test_gradients_of_an_empty_batch_are_zero():
+    _say("case grad empty")
+    wl = W.WORKLOADS["tiny"]
+    g = gpu_cores(wl, W.make_cores(wl))
+    B = 8
+    idx = torch.zeros(0, dtype=torch.int64, device="cuda")
+    off = torch.zeros(B + 1, dtype=torch.int64, device="cuda")
+    dY = torch.randn(B, wl.D, device="cuda")
+    out, _ = abi.tt_bag_backward_grad(_desc(wl), g, idx, off, B, dY, grad_cores=_nan_like(g))
+    torch.cuda.synchronize()
+    for x in out:
+        assert torch.count_nonzero(x).item() == 0 and not torch.isnan(x).any()
+
+
+def _adagrad_steps(wl, batches, lr, eps, state0):
+    """Consecutive fused Adagrad steps on the GPU and in the oracle; checks each."""
+    cores = W.make_cores(wl)
+    g = gpu_cores(wl, cores)
+    st = gpu_cores(wl, state0)
+    desc = _desc(wl)
+    for b in batches:
+        d = to_dev(b)
+        old_c = host_cores(wl, g)
+        old_s = host_cores(wl, st)
+        abi.tt_bag_backward_adagrad(desc, g, d["indices"], d["offsets"], b["num_bags"],
+                                    d["grad_out"], lr, eps, st,
+                                    per_sample_weights=d["per_sample_weights"])
+        torch.cuda.synchronize()
+        new_c, new_s = host_cores(wl, g), host_cores(wl, st)
+        grads, touched, _, _ = _oracle_grads(wl, old_c, b)
+        ref_c, ref_s, _, _ = oracle.adagrad(wl.p, wl.q, wl.ranks, wl.E, old_c, old_s, grads,
+                                            touched, lr, eps)
+        for t in range(wl.num_tables):
+            for k in range(3):
+                for nw, old, ref, what in ((new_c, old_c, ref_c, "core"),
+                                           (new_s, old_s, ref_s, "sum")):
+                    dx = nw[t][k].astype(np.float64) - old[t][k]
+                    dr = ref[t][k].astype(np.float64) - old[t][k]
+                    e = rel_err(dx, dr)
+                    assert e <= TOL, "%s: table %d core %d delta rel err %.3g" % (what, t, k, e)
+                    o_sl, n_sl = np.moveaxis(old[t][k], 1, 0), np.moveaxis(nw[t][k], 1, 0)
+                    for ik in np.flatnonzero(touched[t][k] == 0):
+                        assert np.array_equal(o_sl[ik].view(np.uint32), n_sl[ik].view(np.uint32))
+
+
+def _states(wl, lo=0.2, hi=2.0, seed=5):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return [[rng.uniform(lo, hi, c.shape).astype(np.float32) for c in tbl]
+            for tbl in W.make_cores(wl)]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_adagrad_small_shapes_two_steps(wl):
+    _say("case adagrad", wl.name)
+    _adagrad_steps(wl, [W.make_batch(wl, 0), W.make_batch(wl, 1)], 0.05, 1e-10, _states(wl))
+
+
+def test_adagrad_readme_shape_full():
+    _say("case adagrad readme full")
+    wl = W.WORKLOADS["readme"]
+    _adagrad_steps(wl, [W.make_batch(wl, 0)], 0.01, 1e-10, _states(wl))
+
+
+def test_adagrad_from_zero_sums():
+    """From zero running sums the first step is about lr against the gradient's sign
+    for every parameter: compared where the oracle's gradient is not tiny (a sign
+    decided by rounding is not comparable), bounded by lr everywhere."""
+    _say("case adagrad zero sums")
+    wl = W.WORKLOADS["tiny"]
+    cores = W.make_cores(wl)
+    b = W.make_batch(wl, 2)
+    g = gpu_cores(wl, cores)
+    zero = [torch.zeros_like(x) for x in g]
+    d = to_dev(b)
+    lr, eps = 0.1, 1e-10
+    abi.tt_bag_backward_adagrad(_desc(wl), g, d["indices"], d["offsets"], b["num_bags"],
+                                d["grad_out"], lr, eps, zero)
+    torch.cuda.synchronize()
+    new_c, new_s = host_cores(wl, g), host_cores(wl, zero)
+    grads, touched, _, _ = _oracle_grads(wl, cores, b)
+    zs = [[np.zeros_like(c) for c in cores[0]]]
+    ref_c, ref_s, _, _ = oracle.adagrad(wl.p, wl.q, wl.ranks, wl.E, cores, zs, grads, touched,
+                                        lr, eps)
+    for k in range(3):
+        gk = grads[0][k]
+        big = np.abs(gk) > 1e-3 * np.max(np.abs(gk))
+        dx = new_c[0][k].astype(np.float64) - cores[0][k]
+        dr = ref_c[0][k].astype(np.float64) - cores[0][k]
+        assert np.all(np.abs(dx) <= lr * (1 + 1e-5))
+        assert rel_err(dx[big], dr[big]) <= TOL
+        assert rel_err(new_s[0][k], ref_s[0][k]) <= TOL
+
+
+@pytest.mark.parametrize("mode", ["grad", "adagrad"])
+def test_cache_rows_gradient_and_adagrad(mode):
+    """With the software cache: the hit rows' gradient (grad mode, rows without hits
+    zero) or their Adagrad update with row running sums; the cores as above."""
+    _say("case cache", mode)
+    wl = W.custom("cache", p=(20, 22, 25), q=(4, 4, 4), ranks=(32, 32), bags_per_table=512,
+                  lengths=("fixed", 20), dist=("zipf", 1.2), init_std=1 / 32 ** 0.5, lr=0.01,
+                  weighted=True)
+    K = 900
+    cores = W.make_cores(wl)
+    desc = _desc(wl)
+    cache = abi.Cache(desc, K, 1 << 14)
+    for i in range(3):
+        cache.lookup(torch.from_numpy(W.make_batch(wl, 100 + i)["indices"]).cuda(),
+                     count_freq=True)
+    g = gpu_cores(wl, cores)
+    rows = torch.zeros(K, wl.D, device="cuda")
+    nf = cache.populate(g, rows)
+    assert nf == K
+    b = W.make_batch(wl, 0)
+    d = to_dev(b)
+    slots = cache.lookup(d["indices"], count_freq=False)
+    sl = slots.cpu().numpy()
+    rows_old = rows.cpu().numpy().copy()
+    grads, touched, gc, tc = _oracle_grads(wl, cores, b, slots=sl, cache_size=K)
+    assert (tc == 0).any() and (tc == 1).any()
+    if mode == "grad":
+        gk, gr = _nan_like(g), torch.full_like(rows, float("nan"))
+        abi.tt_bag_backward_grad(desc, g, d["indices"], d["offsets"], b["num_bags"],
+                                 d["grad_out"], grad_cores=gk, grad_rows=gr,
+                                 per_sample_weights=d["per_sample_weights"], cache=(slots, rows))
+        torch.cuda.synchronize()
+        _check_grads(wl, gk, grads, touched)
+        x = gr.cpu().numpy()
+        assert not np.isnan(x).any()
+        assert rel_err(x, gc) <= TOL
+        assert np.all(x[tc == 0] == 0.0)
+        assert np.array_equal(rows.cpu().numpy().view(np.uint32), rows_old.view(np.uint32))
+    else:
+        rng = np.random.Generator(np.random.PCG64(9))
+        rs0 = rng.uniform(0.2, 2.0, rows_old.shape).astype(np.float32)
+        rs = torch.from_numpy(rs0).cuda()
+        st0 = _states(wl)
+        st = gpu_cores(wl, st0)
+        lr, eps = 0.02, 1e-8
+        abi.tt_bag_backward_adagrad(desc, g, d["indices"], d["offsets"], b["num_bags"],
+                                    d["grad_out"], lr, eps, st, state_rows=rs,
+                                    per_sample_weights=d["per_sample_weights"],
+                                    cache=(slots, rows))
+        torch.cuda.synchronize()
+        ref_c, ref_s, ref_r, ref_rs = oracle.adagrad(
+            wl.p, wl.q, wl.ranks, wl.E, cores, st0, grads, touched, lr, eps,
+            cache_rows=rows_old, cache_state=rs0, grad_cache=gc, touched_cache=tc)
+        new_c = host_cores(wl, g)
+        for k in range(3):
+            e = rel_err(new_c[0][k].astype(np.float64) - cores[0][k],
+                        ref_c[0][k].astype(np.float64) - cores[0][k])
+            assert e <= TOL, (k, e)
+        nr, nrs = rows.cpu().numpy(), rs.cpu().numpy()
+        assert rel_err(nr.astype(np.float64) - rows_old, ref_r.astype(np.float64) - rows_old) <= TOL
+        assert rel_err(nrs.astype(np.float64) - rs0, ref_rs.astype(np.float64) - rs0) <= TOL
+        un = tc == 0
+        assert np.array_equal(nr[un].view(np.uint32), rows_old[un].view(np.uint32))
+        assert np.array_equal(nrs[un].view(np.uint32), rs0[un].view(np.uint32))
+    cache.close()
