@@ -485,6 +485,7 @@ hipError_t launch_bwd(const DevArgs &a, int RP, size_t lds, hipStream_t s) {
 constexpr int SEG_T = 256;
 constexpr int SEG_ROWS = 8;   // partial rows in flight per thread
 
+template <int UPD>
 __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
   __shared__ int s_rows[SEG_T];
   __shared__ int s_wc[SEG_T / 64 + 1];
@@ -511,7 +512,7 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
     float *dst = one ? a.G1 + (size_t)seg * W : a.G3 + (size_t)seg * W;
     float *aux = one ? a.X1 + (size_t)seg * W : a.X3 + (size_t)seg * W;
     if (beg >= end) {  // an untouched slice: a zero gradient, no update
-      if (a.upd == UPD_GRAD)
+      if (UPD == UPD_GRAD)
         for (int c = tid; c < W; c += SEG_T) aux[c] = 0.f;
       return;
     }
@@ -568,7 +569,9 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
         const int c = c0 + t2;
         float sum = 0.f;
         for (int r = 0; r < NRG; ++r) sum += s_red[(r * LPR + t2 / VEC) * 4 + t2 % VEC];
-        if (c < W) apply_update(a, dst, aux, c, sum);
+        if (c < W)
+          apply_update<UPD>(a, dst, aux, c, sum, UPD == UPD_GRAD ? 0.f : dst[c],
+                            UPD == UPD_ADAGRAD ? aux[c] : 0.f);
       }
       __syncthreads();
     }
@@ -579,22 +582,21 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
     const int slice2 = a.R1 * a.q2 * a.R2;  // <= 64 * 64 * 64
     float *dst = a.G2 + (size_t)g * slice2, *aux = a.X2 + (size_t)g * slice2;
     if (i0 >= i1) {  // an untouched slice: a zero gradient, no update
-      if (a.upd == UPD_GRAD)
+      if (UPD == UPD_GRAD)
         for (int e = tid; e < slice2; e += SEG_T) aux[e] = 0.f;
       return;
     }
     // per thread: up to 16 columns at once (the whole slice for ranks <= 32), the
     // values the update reads and 2 items' partials in flight; items summed in item order
     constexpr int CU = 16;
-    const bool rd_x = a.upd != UPD_GRAD, rd_aux = a.upd == UPD_ADAGRAD;
     for (int e0 = tid; e0 < slice2; e0 += SEG_T * CU) {
       float acc[CU], old[CU], oaux[CU];
 #pragma unroll
       for (int u = 0; u < CU; ++u) {
         acc[u] = 0.f;
         const int e = min(e0 + u * SEG_T, slice2 - 1);
-        old[u] = rd_x ? dst[e] : 0.f;
-        oaux[u] = rd_aux ? aux[e] : 0.f;
+        old[u] = UPD != UPD_GRAD ? dst[e] : 0.f;
+        oaux[u] = UPD == UPD_ADAGRAD ? aux[e] : 0.f;
       }
       for (int it0 = i0; it0 < i1; it0 += 2) {
         float v[2][CU];
@@ -611,19 +613,9 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
             for (int u = 0; u < CU; ++u) acc[u] += v[k][u];
       }
 #pragma unroll
-      for (int u = 0; u < CU; ++u) {
-        const int e = e0 + u * SEG_T;
-        if (e >= slice2) continue;
-        if (a.upd == UPD_GRAD) {
-          aux[e] = acc[u];
-        } else if (a.upd == UPD_ADAGRAD) {
-          const float S = oaux[u] + acc[u] * acc[u];
-          aux[e] = S;
-          dst[e] = old[u] - a.lr * acc[u] / (sqrtf(S) + a.eps);
-        } else {
-          dst[e] = old[u] - a.lr * acc[u];
-        }
-      }
+      for (int u = 0; u < CU; ++u)
+        if (e0 + u * SEG_T < slice2)
+          apply_update<UPD>(a, dst, aux, e0 + u * SEG_T, acc[u], old[u], oaux[u]);
     }
     return;
   }
@@ -643,7 +635,9 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
         if (q.y != kA || q.z != kB) break;
         acc += a.frag[(size_t)p * a.D + d];
       }
-      apply_update(a, a.crows, a.Xc, (size_t)slot * a.D + d, acc);
+      const size_t e = (size_t)slot * a.D + d;
+      apply_update<UPD>(a, a.crows, a.Xc, e, acc, UPD == UPD_GRAD ? 0.f : a.crows[e],
+                        UPD == UPD_ADAGRAD ? a.Xc[e] : 0.f);
     }
   }
 }
@@ -664,7 +658,10 @@ hipError_t launch_zero(float *x, size_t n, hipStream_t s) {
 hipError_t launch_seg(const DevArgs &a, hipStream_t s) {
   const int nseg = a.T * a.p1 + a.T * a.p3;
   const int nbh = a.has_cache ? ((a.nnz + PIECE - 1) / PIECE + 3) / 4 : 0;
-  tt_launch(K_SEG, k_seg, dim3(nseg + a.T * a.p2 + nbh), dim3(SEG_T), 0, s, a);
+  const dim3 grid(nseg + a.T * a.p2 + nbh);
+  if (a.upd == UPD_GRAD) tt_launch(K_SEG, k_seg<UPD_GRAD>, grid, dim3(SEG_T), 0, s, a);
+  else if (a.upd == UPD_ADAGRAD) tt_launch(K_SEG, k_seg<UPD_ADAGRAD>, grid, dim3(SEG_T), 0, s, a);
+  else tt_launch(K_SEG, k_seg<UPD_SGD>, grid, dim3(SEG_T), 0, s, a);
   return hipGetLastError();
 }
 

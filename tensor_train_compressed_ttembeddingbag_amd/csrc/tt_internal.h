@@ -132,16 +132,18 @@ enum { UPD_SGD = 0, UPD_ADAGRAD = 1, UPD_GRAD = 2 };
 //   SGD      x -= lr g
 //   Adagrad  S = aux + g^2 -> aux;  x -= lr g / (sqrt(S) + eps)
 //   gradient aux = g (x unchanged)
+// x_old / aux_old: the values of x[i] / aux[i] (already loaded by the caller).
+template <int UPD>
 __device__ __forceinline__ void apply_update(const DevArgs &a, float *x, float *aux, size_t i,
-                                             float g) {
-  if (a.upd == UPD_GRAD) {
+                                             float g, float x_old, float aux_old) {
+  if constexpr (UPD == UPD_GRAD) {
     aux[i] = g;
-  } else if (a.upd == UPD_ADAGRAD) {
-    const float S = aux[i] + g * g;
+  } else if constexpr (UPD == UPD_ADAGRAD) {
+    const float S = aux_old + g * g;
     aux[i] = S;
-    x[i] -= a.lr * g / (sqrtf(S) + a.eps);
+    x[i] = x_old - a.lr * g / (sqrtf(S) + a.eps);
   } else {
-    x[i] -= a.lr * g;
+    x[i] = x_old - a.lr * g;
   }
 }
 
