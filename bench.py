@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--workload", default="readme",
                     choices=["tiny", "readme", "skewed", "multitable", "cached"])
     ap.add_argument("--batches", type=int, default=8, help="distinct batches cycled through")
+    ap.add_argument("--update", default="sgd", choices=["sgd", "adagrad", "grad"],
+                    help="backward: fused SGD, fused Adagrad (eps 1e-10), or gradients returned")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle baseline (0 = skip)")
     ap.add_argument("--no-roofline", action="store_true")
@@ -105,6 +107,12 @@ def main():
         rows = torch.zeros(wl.cache_size, wl.D, device="cuda")
         n_filled = cache.populate(g, rows)
         slots = [torch.empty(b["indices"].numel(), dtype=torch.int32, device="cuda") for b in batches]
+    if args.update == "adagrad":  # running sums of squared gradients, from zero
+        aux = [torch.zeros_like(x) for x in g]
+        aux_rows = torch.zeros_like(rows) if cache is not None else None
+    elif args.update == "grad":  # gradient outputs
+        aux = [torch.empty_like(x) for x in g]
+        aux_rows = torch.empty_like(rows) if cache is not None else None
     ws = abi.workspace(desc, max_nnz, B, wl.cache_size)
     out = torch.empty(wl.num_tables * B, wl.D, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -120,9 +128,20 @@ def main():
                         ws=ws, dev_status=status)
         abi.tt_bag_forward(desc, g, b["indices"], b["offsets"], B, b["per_sample_weights"],
                            cache=cv, out=out, ws=ws, dev_status=status, planned=True)
-        abi.tt_bag_backward_sgd(desc, g, b["indices"], b["offsets"], B, b["grad_out"], wl.lr,
-                                b["per_sample_weights"], cache=cv, ws=ws, dev_status=status,
-                                planned=True)
+        if args.update == "sgd":
+            abi.tt_bag_backward_sgd(desc, g, b["indices"], b["offsets"], B, b["grad_out"], wl.lr,
+                                    b["per_sample_weights"], cache=cv, ws=ws, dev_status=status,
+                                    planned=True)
+        elif args.update == "adagrad":
+            abi.tt_bag_backward_adagrad(desc, g, b["indices"], b["offsets"], B, b["grad_out"],
+                                        wl.lr, 1e-10, aux, state_rows=aux_rows,
+                                        per_sample_weights=b["per_sample_weights"], cache=cv,
+                                        ws=ws, dev_status=status, planned=True)
+        else:
+            abi.tt_bag_backward_grad(desc, g, b["indices"], b["offsets"], B, b["grad_out"],
+                                     grad_cores=aux, grad_rows=aux_rows,
+                                     per_sample_weights=b["per_sample_weights"], cache=cv,
+                                     ws=ws, dev_status=status, planned=True)
 
     for i in range(args.warmup):
         step(i)
@@ -163,7 +182,8 @@ def main():
                                % (wl.name, list(wl.p), list(wl.q), list(wl.ranks), wl.E, wl.D,
                                   wl.num_tables, B, nnz_mean, list(wl.lengths), list(wl.dist),
                                   wl.weighted, wl.lr, wl.cache_size),
-                   "nnz": nnz_mean, "global_batch": wl.num_tables * B},
+                   "nnz": nnz_mean, "global_batch": wl.num_tables * B,
+                   "update": args.update},
     }
     if cache is not None:
         res["config"]["cache_rows_filled"] = n_filled

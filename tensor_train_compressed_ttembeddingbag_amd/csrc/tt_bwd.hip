@@ -481,7 +481,8 @@ hipError_t launch_bwd(const DevArgs &a, int RP, size_t lds, hipStream_t s) {
 //    are summed in item order, then SGD;
 //  * four waves = four 64-position pieces of the cache-hit region: a cache run (one
 //    slot) is finished by the piece that holds its first position, which sums the
-//    run's fragments (its first position, then every multiple of P inside the run).
+//    run's fragments (its first position, then every piece start inside the run) in
+//    position order.
 constexpr int SEG_T = 256;
 constexpr int SEG_ROWS = 8;   // partial rows in flight per thread
 
@@ -620,20 +621,46 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
     return;
   }
   if (!a.has_cache) return;
+  // cache hits: the wave's piece of the hit region; run starts from one load per lane
   const int k = (bid - nA - nC - G) * 4 + w;
   const int hb = a.hdr[H_HIT_BEG], he = a.hdr[H_HIT_END];
   const int lo = max(k * PIECE, hb), hi = min((k + 1) * PIECE, he);
-  for (int s = lo; s < hi; ++s) {
-    const int4 cur = a.srec[2 * (size_t)s], prev = a.srec[2 * (size_t)max(s - 1, 0)];
-    const int kA = cur.y, kB = cur.z;
-    if (s > hb && prev.y == kA && prev.z == kB) continue;  // not a run start
+  if (lo >= hi) return;
+  const int sl = min(lo + lane, hi - 1);
+  const int4 cur = a.srec[2 * (size_t)sl], prev = a.srec[2 * (size_t)max(sl - 1, 0)];
+  const bool st = lo + lane < hi && (sl == hb || prev.y != cur.y || prev.z != cur.z);
+  unsigned long long starts = __ballot(st);
+  while (starts) {
+    const int l = __ffsll((long long)starts) - 1;
+    starts &= starts - 1ull;
+    const int s0 = lo + l;
+    const int kA = __shfl(cur.y, l), kB = __shfl(cur.z, l);
     const int slot = (kB - a.T * a.p2) * HB + (kA - a.T * a.p1);
+    // the run's fragments: s0, then every piece start inside the run (k_runsum);
+    // their number, 64 piece starts per round
+    const int pb = (s0 / PIECE + 1) * PIECE;
+    int nfr = 0;
+    for (;;) {
+      const int pj = pb + (nfr + lane) * PIECE;
+      bool in = pj < he;
+      if (in) {
+        const int4 q = a.srec[2 * (size_t)pj];
+        in = q.y == kA && q.z == kB;
+      }
+      const unsigned long long out = __ballot(!in);
+      if (out) { nfr += __ffsll((long long)out) - 1; break; }
+      nfr += 64;
+    }
     for (int d = lane; d < a.D; d += 64) {
-      float acc = a.frag[(size_t)s * a.D + d];
-      for (int p = (s / a.P + 1) * a.P; p < he; p += a.P) {
-        const int4 q = a.srec[2 * (size_t)p];
-        if (q.y != kA || q.z != kB) break;
-        acc += a.frag[(size_t)p * a.D + d];
+      float acc = a.frag[(size_t)s0 * a.D + d];
+      for (int j0 = 0; j0 < nfr; j0 += 16) {  // 16 fragments in flight, summed in order
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          v[u] = a.frag[(size_t)(pb + min(j0 + u, nfr - 1) * PIECE) * a.D + d];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (j0 + u < nfr) acc += v[u];
       }
       const size_t e = (size_t)slot * a.D + d;
       apply_update<UPD>(a, a.crows, a.Xc, e, acc, UPD == UPD_GRAD ? 0.f : a.crows[e],

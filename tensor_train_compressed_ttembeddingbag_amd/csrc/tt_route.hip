@@ -649,8 +649,8 @@ __global__ __launch_bounds__(RT) void k_yinit(DevArgs a) {
 
 // Backward, cache hits: frag[s] = sum over positions of one run fragment of
 // w_n * dY[bag n], where a run is a maximal range of equal (dB, dA, dI3) in the final
-// order (one cache slot) and fragments are the pieces of a run inside P-position
-// pieces.  One wave per 64 positions; the summation order is the position order.
+// order (one cache slot) and fragments are the parts of a run inside the 64-position
+// pieces.  One wave per piece; the summation order is the position order.
 // (Misses sum their runs inside the backward contraction kernel.)
 __global__ __launch_bounds__(RT) void k_runsum(DevArgs a) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -668,9 +668,9 @@ __global__ __launch_bounds__(RT) void k_runsum(DevArgs a) {
   const int kA = sp.dA, kB = sp.dB, kI = sp.dI3, bag = sp.bag;
   const float wt = lane < len ? sp.w : 0.f;
   const int pA = __shfl_up(kA, 1), pB = __shfl_up(kB, 1), pI = __shfl_up(kI, 1);
-  // fragments start at run starts and at every multiple of P (work item boundaries)
-  const unsigned long long starts = __ballot(
-      lane < len && ((lane == 0) || kA != pA || kB != pB || kI != pI || (s % a.P) == 0));
+  // fragments start at run starts and at the piece start
+  const unsigned long long starts =
+      __ballot(lane < len && ((lane == 0) || kA != pA || kB != pB || kI != pI));
   for (int d0 = 0; d0 < a.D; d0 += 64) {
     const int d = min(d0 + lane, a.D - 1);
     float v[PIECE];
