@@ -477,14 +477,20 @@ hipError_t launch_bwd(const DevArgs &a, int RP, size_t lds, hipStream_t s) {
 //    order positions of its partials; they are listed in segment order, then summed by
 //    8 row groups (row group k takes rows k, k+8, ...; a fixed assignment), the group
 //    sums added in group order, and SGD applied;
-//  * one block = one core-2 slice (t, i2): the dG2 partials of the group's work items
-//    are summed in item order, then SGD;
+//  * one block = one column chunk of a core-2 slice (t, i2): the dG2 partials of the
+//    group's work items are summed in item order, then the update;
 //  * four waves = four 64-position pieces of the cache-hit region: a cache run (one
 //    slot) is finished by the piece that holds its first position, which sums the
 //    run's fragments (its first position, then every piece start inside the run) in
 //    position order.
 constexpr int SEG_T = 256;
 constexpr int SEG_ROWS = 8;   // partial rows in flight per thread
+constexpr int SEG_CW = 4;     // core-2 slices: columns per thread,
+constexpr int SEG_IB = 8;     // work items in flight,
+constexpr int SEG_COLS = SEG_T * SEG_CW;  // and columns per block
+__host__ __device__ inline int seg_chunks(const DevArgs &a) {
+  return (a.R1 * a.q2 * a.R2 + SEG_COLS - 1) / SEG_COLS;
+}
 
 template <int UPD>
 __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
@@ -498,7 +504,8 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
   const bool one = bid < nA;
   const int seg = one ? bid : bid - nA;
   const int *seg_start = one ? a.segA : a.segI3;
-  const int gi = min(max(bid - nA - nC, 0), G - 1);
+  const int nch = seg_chunks(a);
+  const int gi = min(max(bid - nA - nC, 0) / nch, G - 1);
   const int plan = a.hdr[H_PLAN];
   const int beg = seg_start[min(seg, one ? nA : nC)], end = seg_start[min(seg + 1, one ? nA : nC)];
   const int i0 = a.chunk_pre[gi], i1 = a.chunk_pre[gi + 1];
@@ -578,51 +585,51 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
     }
     return;
   }
-  if (bid < nA + nC + G) {
-    const int g = gi;
+  if (bid < nA + nC + G * nch) {
+    // one column chunk of one core-2 slice: SEG_COLS columns, SEG_CW per thread, the
+    // values the update reads and SEG_IB items' partials in flight; items summed in
+    // item order
+    const int g = gi, c0 = (bid - nA - nC - g * nch) * SEG_COLS + tid;
     const int slice2 = a.R1 * a.q2 * a.R2;  // <= 64 * 64 * 64
     float *dst = a.G2 + (size_t)g * slice2, *aux = a.X2 + (size_t)g * slice2;
     if (i0 >= i1) {  // an untouched slice: a zero gradient, no update
       if (UPD == UPD_GRAD)
-        for (int e = tid; e < slice2; e += SEG_T) aux[e] = 0.f;
+#pragma unroll
+        for (int u = 0; u < SEG_CW; ++u)
+          if (c0 + u * SEG_T < slice2) aux[c0 + u * SEG_T] = 0.f;
       return;
     }
-    // per thread: up to 16 columns at once (the whole slice for ranks <= 32), the
-    // values the update reads and 2 items' partials in flight; items summed in item order
-    constexpr int CU = 16;
-    for (int e0 = tid; e0 < slice2; e0 += SEG_T * CU) {
-      float acc[CU], old[CU], oaux[CU];
+    float acc[SEG_CW], old[SEG_CW], oaux[SEG_CW];
 #pragma unroll
-      for (int u = 0; u < CU; ++u) {
-        acc[u] = 0.f;
-        const int e = min(e0 + u * SEG_T, slice2 - 1);
-        old[u] = UPD != UPD_GRAD ? dst[e] : 0.f;
-        oaux[u] = UPD == UPD_ADAGRAD ? aux[e] : 0.f;
-      }
-      for (int it0 = i0; it0 < i1; it0 += 2) {
-        float v[2][CU];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const float *src = a.part2 + (size_t)min(it0 + k, i1 - 1) * slice2;
-#pragma unroll
-          for (int u = 0; u < CU; ++u) v[k][u] = src[min(e0 + u * SEG_T, slice2 - 1)];
-        }
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-          if (it0 + k < i1)
-#pragma unroll
-            for (int u = 0; u < CU; ++u) acc[u] += v[k][u];
-      }
-#pragma unroll
-      for (int u = 0; u < CU; ++u)
-        if (e0 + u * SEG_T < slice2)
-          apply_update<UPD>(a, dst, aux, e0 + u * SEG_T, acc[u], old[u], oaux[u]);
+    for (int u = 0; u < SEG_CW; ++u) {
+      acc[u] = 0.f;
+      const int e = min(c0 + u * SEG_T, slice2 - 1);
+      old[u] = UPD != UPD_GRAD ? dst[e] : 0.f;
+      oaux[u] = UPD == UPD_ADAGRAD ? aux[e] : 0.f;
     }
+    for (int it0 = i0; it0 < i1; it0 += SEG_IB) {
+      float v[SEG_IB][SEG_CW];
+#pragma unroll
+      for (int k = 0; k < SEG_IB; ++k) {
+        const float *src = a.part2 + (size_t)min(it0 + k, i1 - 1) * slice2;
+#pragma unroll
+        for (int u = 0; u < SEG_CW; ++u) v[k][u] = src[min(c0 + u * SEG_T, slice2 - 1)];
+      }
+#pragma unroll
+      for (int k = 0; k < SEG_IB; ++k)
+        if (it0 + k < i1)
+#pragma unroll
+          for (int u = 0; u < SEG_CW; ++u) acc[u] += v[k][u];
+    }
+#pragma unroll
+    for (int u = 0; u < SEG_CW; ++u)
+      if (c0 + u * SEG_T < slice2)
+        apply_update<UPD>(a, dst, aux, c0 + u * SEG_T, acc[u], old[u], oaux[u]);
     return;
   }
   if (!a.has_cache) return;
   // cache hits: the wave's piece of the hit region; run starts from one load per lane
-  const int k = (bid - nA - nC - G) * 4 + w;
+  const int k = (bid - nA - nC - G * nch) * 4 + w;
   const int hb = a.hdr[H_HIT_BEG], he = a.hdr[H_HIT_END];
   const int lo = max(k * PIECE, hb), hi = min((k + 1) * PIECE, he);
   if (lo >= hi) return;
@@ -685,7 +692,7 @@ hipError_t launch_zero(float *x, size_t n, hipStream_t s) {
 hipError_t launch_seg(const DevArgs &a, hipStream_t s) {
   const int nseg = a.T * a.p1 + a.T * a.p3;
   const int nbh = a.has_cache ? ((a.nnz + PIECE - 1) / PIECE + 3) / 4 : 0;
-  const dim3 grid(nseg + a.T * a.p2 + nbh);
+  const dim3 grid(nseg + a.T * a.p2 * seg_chunks(a) + nbh);
   if (a.upd == UPD_GRAD) tt_launch(K_SEG, k_seg<UPD_GRAD>, grid, dim3(SEG_T), 0, s, a);
   else if (a.upd == UPD_ADAGRAD) tt_launch(K_SEG, k_seg<UPD_ADAGRAD>, grid, dim3(SEG_T), 0, s, a);
   else tt_launch(K_SEG, k_seg<UPD_SGD>, grid, dim3(SEG_T), 0, s, a);
