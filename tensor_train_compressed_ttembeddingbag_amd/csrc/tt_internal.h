@@ -33,7 +33,8 @@ constexpr int P_MAX = 32;       // positions per work item: P * q1 <= 16 * NW ro
 constexpr int MAXQ3 = 16;
 constexpr int STAGE_U = 8;      // global loads in flight per thread when staging into LDS
 constexpr int COOP_TILES = 256; // blocks of the one-launch grouping kernel (one per CU)
-constexpr int COOP_CELLS = 12288;  // its bins x tiles per digit (each block reads them all)
+constexpr int COOP_CELLS = 65536;  // its bins x tiles per digit (each block reads them all)
+constexpr int COOP_LDS_CELLS = 12288;  // (t,i2) x tile counts gathered in LDS up to this size
 
 // header words inside the workspace (after three 64-bit "last block" counters)
 enum {

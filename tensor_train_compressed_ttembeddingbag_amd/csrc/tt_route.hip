@@ -17,19 +17,22 @@ static __device__ __forceinline__ bool a_le(const int64_t *off, int c, int n) {
   return off[c] <= (int64_t)n;
 }
 
-// Largest b in [0, NB) with off[b] <= n, found by half of the block (128 threads,
-// `half` = 0 or 1) with a 128-ary search: one global load per thread per round.
+// Largest b in [0, NB) with off[b] <= n, found by 128 threads (`half` = 0: threads
+// 0..127, 1: threads 128..255) with a 128-ary search: one global load per thread per
+// round.  Every thread of the block calls it (barriers); threads from 256 on only
+// take part in the barriers.
 static __device__ int half_find_bag(const int64_t *off, int NB, int n, int half, int *s_red) {
   const int t = threadIdx.x - half * 128, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const bool searcher = threadIdx.x < 256;
   int lo = 0;
   // invariant: the answer lies in [lo, lo + span).  The number of rounds depends on NB
   // only, so both halves meet every barrier.
   for (int span = NB; span > 1;) {
     const int step = (span + 127) / 128;
     const int c = lo + t * step;
-    const bool ok = t * step < span && c < NB && a_le(off, c, n);
+    const bool ok = searcher && t * step < span && c < NB && a_le(off, c, n);
     int best = wave_max(ok ? t : -1);
-    if (lane == 0) s_red[w] = best;
+    if (lane == 0 && searcher) s_red[w] = best;
     __syncthreads();
     best = max(s_red[half * 2], s_red[half * 2 + 1]);
     __syncthreads();
@@ -115,11 +118,11 @@ static __device__ void tile_decode(const DevArgs &a, int blk, int *s_off, int *s
   // the bags that may hold the tile's positions: all of them when their offsets fit in
   // LDS, else the ones overlapping the tile (one 128-ary search per half of the block)
   int b_lo = 0, nbag = a.NB;
-  if (NT == 256 && a.NB + 1 > ROUTE_MAX_BAGS) {
+  if (a.NB + 1 > ROUTE_MAX_BAGS) {
     const int base = blk * RB, last = min(base + RB, a.nnz) - 1;
-    const int half = tid >> 7;
+    const int half = min(tid >> 7, 1);
     const int b = half_find_bag(a.off, a.NB, half ? last : base, half, s_red);
-    if ((tid & 127) == 0) s_b[half] = b;
+    if (tid == 0 || tid == 128) s_b[half] = b;
     __syncthreads();
     b_lo = s_b[0];
     nbag = max(s_b[1], s_b[0]) - b_lo + 1;
@@ -345,8 +348,7 @@ static int device_cus() {
 }
 
 static bool coop_route_ok(const DevArgs &a) {
-  return a.nblk <= COOP_TILES && a.nblk <= device_cus() && a.NB + 1 <= ROUTE_MAX_BAGS &&
-         a.binsA <= COOP_BINS &&
+  return a.nblk <= COOP_TILES && a.nblk <= device_cus() && a.binsA <= COOP_BINS &&
          a.binsB <= COOP_BINS && a.binsI3 <= COOP_BINS &&
          (int64_t)a.binsA * a.nblk <= COOP_CELLS && (int64_t)a.binsB * a.nblk <= COOP_CELLS &&
          (int64_t)a.binsI3 * a.nblk <= COOP_CELLS;
@@ -484,7 +486,8 @@ __host__ __device__ inline CoopLds coop_lds(const DevArgs &a) {
   L.sA = L.gI + nX;
   L.gA = L.sA + nY;
   L.cell = L.gA + nY;
-  L.total = max(L.cell + a.binsB * a.nblk, ROUTE_MAX_BAGS + max(a.binsI3, a.binsA));
+  const int cells = a.binsB * a.nblk <= COOP_LDS_CELLS ? a.binsB * a.nblk : 0;
+  L.total = max(L.cell + cells, ROUTE_MAX_BAGS + max(a.binsI3, a.binsA));
   return L;
 }
 
@@ -523,15 +526,23 @@ __global__ __launch_bounds__(CT) void k_route_coop(DevArgs a) {
     for (int d = tid; d < a.binsI3; d += CT) a.segI3[d] = gsI[d];
     for (int d = tid; d < a.binsA; d += CT) a.segA[d] = gsA[d];
   }
-  for (int i = tid; i < a.binsB * nblk; i += CT) cellB[i] = 0;
+  // (t,i2) counts per orderA tile: gathered in LDS when the matrix fits, else added to
+  // histB directly
+  const bool in_lds = a.binsB * nblk <= COOP_LDS_CELLS;
+  if (in_lds)
+    for (int i = tid; i < a.binsB * nblk; i += CT) cellB[i] = 0;
   int pA[RB / CT];
   tile_place_ia<CT>(a, el, pA, lds_c, startI, startA, 1, 0);
 #pragma unroll
   for (int r = 0; r < RB / CT; ++r)
-    if (pA[r] >= 0) atomicAdd(&cellB[el[r].dB * nblk + pA[r] / RB], 1);
+    if (pA[r] >= 0) {
+      if (in_lds) atomicAdd(&cellB[el[r].dB * nblk + pA[r] / RB], 1);
+      else atomicAdd(&a.histB[(pA[r] / RB) * a.binsB + el[r].dB], 1);
+    }
   __syncthreads();
-  for (int i = tid; i < a.binsB * nblk; i += CT)
-    if (cellB[i]) atomicAdd(&a.histB[(i % nblk) * a.binsB + i / nblk], cellB[i]);
+  if (in_lds)
+    for (int i = tid; i < a.binsB * nblk; i += CT)
+      if (cellB[i]) atomicAdd(&a.histB[(i % nblk) * a.binsB + i / nblk], cellB[i]);
   if (!grid_sync<true>(a, 2)) return;
 
   // ---- work items (each block writes its share); final order: the orderA tiles placed

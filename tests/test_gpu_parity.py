@@ -161,6 +161,29 @@ def test_route_order_bit_exact():
         assert np.array_equal(np.diff(g[:wl.num_tables * wl.p[1] + 1]), counts)
 
 
+def test_many_tiles_use_the_three_kernel_grouping():
+    """More than 256 tiles of 1024 elements: the grouping runs as three kernels
+    without a grid-wide barrier.  Order bit-exact, then one fwd+bwd step against the
+    oracle."""
+    wl = W.custom("many tiles", p=(4, 5, 6), q=(2, 2, 2), ranks=(4, 4), bags_per_table=120000,
+                  lengths=("uniform", 1, 4), lr=0.1)
+    _say("case many tiles")
+    b = W.make_batch(wl, 0)
+    assert len(b["indices"]) > 256 * 1024
+    d = to_dev(b)
+    desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E, wl.num_tables)
+    abi.tt_profile_enable(True)
+    order, goff = abi.tt_bag_route(desc, d["indices"], d["offsets"], b["num_bags"])
+    torch.cuda.synchronize()
+    prof = abi.tt_profile_read()
+    abi.tt_profile_enable(False)
+    assert prof["k_route_a"][1] == 1 and prof["k_route_coop"][1] == 0
+    ref, counts = oracle.route_order(wl.p, wl.E, 1, b["num_bags"], b["indices"], b["offsets"])
+    assert np.array_equal(order.cpu().numpy()[:len(ref)], ref)
+    assert np.array_equal(np.diff(goff.cpu().numpy()[:wl.p[1] + 1]), counts)
+    _full_parity(wl, b)
+
+
 @pytest.mark.parametrize("bags", [None, 4000], ids=["one-block", "multi-block"])
 def test_route_with_cache_slots_bit_exact(bags):
     """Cache slots, skipped invalid indices; small batches are grouped by one
