@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--workload", default="readme",
                     choices=["tiny", "readme", "skewed", "multitable", "cached"])
     ap.add_argument("--batches", type=int, default=8, help="distinct batches cycled through")
+    ap.add_argument("--no-pipeline", action="store_true",
+                    help="group each batch right before its forward (no overlap with the "
+                         "previous backward)")
     ap.add_argument("--update", default="sgd", choices=["sgd", "adagrad", "grad"],
                     help="backward: fused SGD, fused Adagrad (eps 1e-10), or gradients returned")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -113,21 +116,58 @@ def main():
     elif args.update == "grad":  # gradient outputs
         aux = [torch.empty_like(x) for x in g]
         aux_rows = torch.empty_like(rows) if cache is not None else None
-    ws = abi.workspace(desc, max_nnz, B, wl.cache_size)
+    # Training loop.  Every batch is grouped (tt_bag_plan), then runs forward and backward
+    # with the plan.  Pipelined (default): the grouping of batch i+1 is enqueued on a second
+    # stream right after the forward of batch i, so it overlaps the backward of batch i;
+    # two workspaces alternate, and events order (a) the forward of a batch after its
+    # grouping and (b) a grouping after the last use of its workspace (two batches back).
+    pipeline = not args.no_pipeline
+    wss = [abi.workspace(desc, max_nnz, B, wl.cache_size) for _ in range(2 if pipeline else 1)]
     out = torch.empty(wl.num_tables * B, wl.D, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream() if pipeline else main  # default priority
+    ev_plan = [torch.cuda.Event() for _ in range(2)]
+    ev_done = [torch.cuda.Event() for _ in range(2)]
+    for e in ev_done:
+        e.record(main)
+    seq = {"next": 0}
 
-    def step(i):
+    def plan(i):
         b = batches[i % len(batches)]
+        ws = wss[i % len(wss)]
         cv = None
+        if pipeline:
+            side.wait_event(ev_done[i % 2])
         if cache is not None:
             s = slots[i % len(batches)]
-            cache.lookup(b["indices"], slot_out=s, count_freq=True, dev_status=status)
+            cache.lookup(b["indices"], slot_out=s, count_freq=True, dev_status=status,
+                         stream=side)
             cv = (s, rows)
         abi.tt_bag_plan(desc, b["indices"], b["offsets"], B, b["per_sample_weights"], cache=cv,
-                        ws=ws, dev_status=status)
+                        ws=ws, dev_status=status, stream=side)
+        if pipeline:
+            ev_plan[i % 2].record(side)
+        return cv
+
+    cvs = {}
+    if pipeline:
+        cvs[0] = plan(0)
+
+    def step(_):
+        i = seq["next"]
+        seq["next"] += 1
+        b = batches[i % len(batches)]
+        ws = wss[i % len(wss)]
+        if pipeline:
+            main.wait_event(ev_plan[i % 2])
+            cv = cvs.pop(i)
+        else:
+            cv = plan(i)
         abi.tt_bag_forward(desc, g, b["indices"], b["offsets"], B, b["per_sample_weights"],
                            cache=cv, out=out, ws=ws, dev_status=status, planned=True)
+        if pipeline:
+            cvs[i + 1] = plan(i + 1)
         if args.update == "sgd":
             abi.tt_bag_backward_sgd(desc, g, b["indices"], b["offsets"], B, b["grad_out"], wl.lr,
                                     b["per_sample_weights"], cache=cv, ws=ws, dev_status=status,
@@ -142,21 +182,22 @@ def main():
                                      grad_cores=aux, grad_rows=aux_rows,
                                      per_sample_weights=b["per_sample_weights"], cache=cv,
                                      ws=ws, dev_status=status, planned=True)
+        if pipeline:
+            ev_done[i % 2].record(main)
+        return i
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
+    done = [step(i) for i in range(args.steps)]
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if int(status.item()) != 0:
         print("device status %d during the benchmark" % int(status.item()), file=sys.stderr)
         sys.exit(1)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    nnz_mean = float(np.mean([batches[i % len(batches)]["indices"].numel()
-                              for i in range(args.steps)]))
+    nnz_mean = float(np.mean([batches[i % len(batches)]["indices"].numel() for i in done]))
     us_per_nnz = ms_per_step * 1e3 / nnz_mean
     f1, f2 = metrics.stage_flops(wl.q, wl.ranks)
     step_flops = metrics.step_flops_per_nnz(wl.q, wl.ranks) * nnz_mean
@@ -183,7 +224,9 @@ def main():
                                   wl.num_tables, B, nnz_mean, list(wl.lengths), list(wl.dist),
                                   wl.weighted, wl.lr, wl.cache_size),
                    "nnz": nnz_mean, "global_batch": wl.num_tables * B,
-                   "update": args.update},
+                   "update": args.update,
+                   "pipeline": "grouping of batch i+1 overlapped with the backward of batch i"
+                               if pipeline else "none"},
     }
     if cache is not None:
         res["config"]["cache_rows_filled"] = n_filled
@@ -200,8 +243,7 @@ def roofline(args, wl, batches, step, torch, abi, metrics, slots):
     """Dominant kernel's achieved rate from HIP events around each launch."""
     nsteps = min(args.steps, 400)
     abi.tt_profile_enable(True)
-    for i in range(nsteps):
-        step(i)
+    done = [step(i) for i in range(nsteps)]
     torch.cuda.synchronize()
     prof = abi.tt_profile_read()
     abi.tt_profile_enable(False)
@@ -217,8 +259,8 @@ def roofline(args, wl, batches, step, torch, abi, metrics, slots):
         per_batch.append((metrics.unique_pairs(wl.p, wl.num_tables, wl.bags_per_table,
                                                nb["indices"], nb["offsets"], sl, wl.E),
                           int(np.sum(sl < 0)) if sl is not None else len(nb["indices"])))
-    U = float(np.mean([per_batch[i % len(batches)][0] for i in range(nsteps)]))
-    N = float(np.mean([per_batch[i % len(batches)][1] for i in range(nsteps)]))
+    U = float(np.mean([per_batch[i % len(batches)][0] for i in done]))
+    N = float(np.mean([per_batch[i % len(batches)][1] for i in done]))
     work = {"k_bwd": metrics.bwd_kernel_flops(wl.q, wl.ranks, N, U),
             "k_fwd": metrics.fwd_kernel_flops(wl.q, wl.ranks, N, U)}
     avg_s = kernels[dom]["avg_us"] * 1e-6
@@ -237,7 +279,7 @@ def roofline(args, wl, batches, step, torch, abi, metrics, slots):
                                      % (work[dom], U, N)}
     else:
         # grouping / pooling kernels: algorithmic bytes of the whole grouping step
-        NZ = float(np.mean([batches[i % len(batches)]["indices"].numel() for i in range(nsteps)]))
+        NZ = float(np.mean([batches[i % len(batches)]["indices"].numel() for i in done]))
         nbytes = metrics.route_bytes(NZ, wl.num_tables * wl.bags_per_table, wl.weighted,
                                      slots is not None)
         ach = nbytes / avg_s / 1e9
