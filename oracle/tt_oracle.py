@@ -4,8 +4,8 @@ Floating-point side: ``tt_oracle.c`` (plain double loops over the definition of
 the TT table, EmbeddingBag pooling, the product-rule backward, plain SGD and
 Adagrad),
 loaded here through ctypes.  Integer side (index split, bag ids, the grouping
-order, cache frequency counts, top-K selection, slot lookup): plain numpy / dict
-code in this file.
+order, cache frequency counts, top-K selection, the set-associative LFU populate,
+slot lookup): plain numpy / dict code in this file.
 
 Pages followed ("FBTT-Embedding" README unless stated):
   * "Initialization": core shapes R_{k-1} x p_k x q_k x R_k, ranks [1]+tt_ranks+[1].
@@ -37,7 +37,7 @@ _SO = os.path.join(_HERE, "libtt_oracle.so")
 
 __all__ = ["build", "forward", "backward", "sgd", "adagrad", "tt_row", "split_index", "bag_ids",
            "route_order", "group_counts", "count_frequencies", "select_cache",
-           "lookup_slots", "populate_rows"]
+           "lookup_slots", "populate_rows", "splitmix64", "lfu_set", "lfu_populate", "LFU_WAYS"]
 
 
 def build(force: bool = False) -> str:
@@ -291,3 +291,58 @@ def populate_rows(p, q, ranks, cores3, cached):
     for s, i in enumerate(np.asarray(cached).tolist()):
         out[s] = tt_row(p, q, ranks, cores3, i)
     return out
+
+
+# ---------------------------------------------------------------- set-associative LFU
+# "Software Cache" names a 32-way set-associative least-frequently-used cache whose
+# frequencies are counted in an open-addressing hash table, refreshed on populate.  The
+# pages fix no hash, no replacement detail and no row handling; the reading taken:
+#   * slot = set * 32 + way; set of index i = (splitmix64(i) >> 32) mod (cache_size / 32),
+#     with the splitmix64 finalizer of Steele, Lea and Flood (2014);
+#   * on populate each set holds the (at most) 32 counted indices of that set with the
+#     highest counts, ties to the smaller index;
+#   * an index that stays keeps its way (and its row, with whatever updates it received);
+#     the newcomers, in (count desc, index asc) order, take the freed ways in ascending
+#     order; ways left over are empty (-1); only the newcomers' rows are rebuilt from the
+#     TT cores.
+
+LFU_WAYS = 32
+_M64 = (1 << 64) - 1
+
+
+def splitmix64(x: int) -> int:
+    """The splitmix64 output finalizer (Steele, Lea, Flood 2014) on a 64-bit word."""
+    x &= _M64
+    x = ((x ^ (x >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+    x = ((x ^ (x >> 27)) * 0x94D049BB133111EB) & _M64
+    return x ^ (x >> 31)
+
+
+def lfu_set(index: int, nsets: int) -> int:
+    return (splitmix64(index) >> 32) % nsets
+
+
+def lfu_populate(counts: dict, cached, cache_size: int):
+    """One populate of the set-associative LFU cache.  cached: current index per slot
+    (-1 = empty).  Returns (new cached array, fresh mask: slots whose row is rebuilt)."""
+    assert cache_size % LFU_WAYS == 0
+    nsets = cache_size // LFU_WAYS
+    old = [int(v) for v in np.asarray(cached, dtype=np.int64).tolist()]
+    assert len(old) == cache_size
+    by_set = {}
+    for k, c in counts.items():
+        by_set.setdefault(lfu_set(k, nsets), []).append((-c, k))
+    new = [-1] * cache_size
+    fresh = np.zeros(cache_size, dtype=bool)
+    for s in range(nsets):
+        members = [k for _, k in sorted(by_set.get(s, []))[:LFU_WAYS]]
+        ways = old[s * LFU_WAYS:(s + 1) * LFU_WAYS]
+        kept = [w for w in range(LFU_WAYS) if ways[w] >= 0 and ways[w] in members]
+        free = [w for w in range(LFU_WAYS) if w not in kept]
+        newcomers = [k for k in members if k not in ways]
+        for w in kept:
+            new[s * LFU_WAYS + w] = ways[w]
+        for w, k in zip(free, newcomers):
+            new[s * LFU_WAYS + w] = k
+            fresh[s * LFU_WAYS + w] = True
+    return np.asarray(new, dtype=np.int64), fresh

@@ -551,3 +551,57 @@ def test_pins_catch_planted_mistakes(mi, tmp_path, monkeypatch):
     finally:
         O._lib = saved
     assert failures > 0, "planted mistake %d went unnoticed" % mi
+
+
+# --------------------------------------------------------------- set-associative LFU
+
+def test_splitmix64_published_sequence():
+    """The splitmix64 generator from seed 0 (state += 0x9E3779B97F4A7C15, then the
+    finalizer) starts 0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F."""
+    g = 0x9E3779B97F4A7C15
+    got = [oracle.tt_oracle.splitmix64((g * k) & ((1 << 64) - 1)) for k in (1, 2, 3)]
+    assert got == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+def test_lfu_single_set_is_exact_top_k():
+    """With one set (32 slots) the set-associative LFU filled from empty is the exact
+    top-32 in priority order (the brute-force-pinned select_cache)."""
+    rng = _rng(31)
+    counts = {int(k): int(c) for k, c in zip(rng.choice(5000, 300, replace=False),
+                                              rng.integers(1, 40, 300))}
+    new, fresh = oracle.tt_oracle.lfu_populate(counts, [-1] * 32, 32)
+    assert np.array_equal(new, oracle.select_cache(counts, 32))
+    assert fresh.all()
+
+
+def test_lfu_repeated_populates_brute_force():
+    """Brute-force invariants over repeated populates with changing counts: every set
+    holds exactly the candidates of that set that fewer than 32 others of the set beat;
+    an index that stays keeps its slot; fresh slots are exactly the changed, non-empty
+    ones; every cached index sits in its own set."""
+    rng = _rng(32)
+    K = 32 * 5
+    cached = np.full(K, -1, dtype=np.int64)
+    counts = {}
+    for rnd in range(6):
+        for k in rng.integers(0, 3000, 900).tolist():
+            counts[k] = counts.get(k, 0) + 1
+        new, fresh = oracle.tt_oracle.lfu_populate(counts, cached, K)
+        cand = list(counts.items())
+        sets = {k: oracle.tt_oracle.lfu_set(k, K // 32) for k, _ in cand}
+        want = set()
+        for k, c in cand:
+            beaten_by = sum(1 for k2, c2 in cand
+                            if sets[k2] == sets[k] and (c2 > c or (c2 == c and k2 < k)))
+            if beaten_by < 32:
+                want.add(k)
+        got = [int(v) for v in new if v >= 0]
+        assert len(got) == len(set(got)) and set(got) == want
+        for s, v in enumerate(new.tolist()):
+            if v >= 0:
+                assert sets[v] == s // 32
+        for s in range(K):
+            if cached[s] >= 0 and cached[s] in want:
+                assert new[s] == cached[s]
+            assert fresh[s] == (new[s] >= 0 and new[s] != cached[s])
+        cached = new
