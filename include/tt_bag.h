@@ -243,25 +243,59 @@ int tt_bag_route(const tt_desc *desc, const int64_t *indices, int64_t nnz,
  */
 typedef struct tt_cache tt_cache;
 
+/* Replacement policies of tt_cache_populate:
+ *  TT_CACHE_TOPK   fully associative: the cache_size most frequent indices, slot = rank;
+ *                  every populate rebuilds every row from the cores.
+ *  TT_CACHE_LFU32  the pages' 32-way set-associative LFU ("Software Cache"; hash, ways
+ *                  and row handling are this library's reading): slot = set * 32 + way,
+ *                  set = (splitmix64(index) >> 32) mod (cache_size / 32), splitmix64 being
+ *                  the output finalizer of Steele, Lea and Flood (2014).  Each populate
+ *                  keeps in every set the 32 counted indices of that set with the highest
+ *                  counts (ties: smaller index).  An index that stays keeps its slot and
+ *                  its row (with the updates the backward applied to it); newcomers take
+ *                  the freed ways in ascending order, in (count desc, index asc) order,
+ *                  and only their rows are rebuilt from the cores.  Evicted rows are
+ *                  dropped (their updates are not written back to the cores).
+ *                  cache_size must be a multiple of 32. */
+#define TT_CACHE_TOPK  0
+#define TT_CACHE_LFU32 1
+
 /* Allocates the count table, the index->slot map and populate's scratch for a
- * table of shape *desc (num_tables must be 1).  *out receives a host handle. */
+ * table of shape *desc (num_tables must be 1).  *out receives a host handle.
+ * tt_cache_create is tt_cache_create_policy with TT_CACHE_TOPK. */
 int tt_cache_create(tt_cache **out, const tt_desc *desc, int64_t cache_size,
                     int64_t hashtbl_size);
+int tt_cache_create_policy(tt_cache **out, const tt_desc *desc, int64_t cache_size,
+                           int64_t hashtbl_size, int policy);
 
 /* slot_out[n] = slot of indices[n] in the cache, or -1.  With count_freq != 0 every
  * element with an index in [0, E) also adds one to its index's count. */
 int tt_cache_lookup(tt_cache *c, const int64_t *indices, int64_t nnz, int32_t *slot_out,
                     int count_freq, int32_t *dev_status, void *stream);
 
-/* Re-selects the cached indices from the counts and writes their decompressed
- * rows into rows[0 .. n_filled) ([cache_size][D] fp32).  *n_filled is a HOST
- * pointer; this call synchronises `stream`. */
+/* Re-selects the cached indices from the counts (policy above) and writes the rows
+ * it rebuilds into rows ([cache_size][D] fp32): TT_CACHE_TOPK fills slots
+ * 0 .. n_filled-1; TT_CACHE_LFU32 rebuilds the newcomers' slots and n_filled is the
+ * number of occupied slots.  *n_filled is a HOST pointer; this call synchronises
+ * `stream`. */
 int tt_cache_populate(tt_cache *c, const float *const cores[3], float *rows,
                       int64_t *n_filled, void *stream);
 
 /* cached_out[s] = index held in slot s for s < n_filled (int64 device buffer of
  * cache_size entries; entries past n_filled are -1). */
 int tt_cache_cached_indices(tt_cache *c, int64_t *cached_out, void *stream);
+
+/* The cache state (the rows are the caller's): the index of every slot
+ * (cached [cache_size] int64, -1 = empty) and the raw frequency table (keys
+ * [hashtbl_size] int64, -1 = unused entry; counts [hashtbl_size] int32).  Device
+ * buffers, asynchronous on `stream`.  tt_cache_import restores a state exported from a
+ * cache created with the same descriptor, sizes and policy (its content is not
+ * checked) and rebuilds the index->slot map; lookups and populates then behave as in
+ * the exporting cache. */
+int tt_cache_export(tt_cache *c, int64_t *cached_out, int64_t *keys_out, int32_t *counts_out,
+                    void *stream);
+int tt_cache_import(tt_cache *c, const int64_t *cached, const int64_t *keys,
+                    const int32_t *counts, void *stream);
 
 int tt_cache_destroy(tt_cache *c);
 

@@ -24,6 +24,8 @@ TT_DEV_BAD_SLOT = 4
 TT_DEV_HASH_FULL = 8
 TT_DEV_STALE_PLAN = 16
 TT_DEV_SYNC_TIMEOUT = 32
+TT_CACHE_TOPK = 0
+TT_CACHE_LFU32 = 1
 
 
 class TTError(RuntimeError):
@@ -69,6 +71,9 @@ _SIG = {
     "tt_bag_route": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _I64, _P, _P, _P, ctypes.c_size_t,
                                     _P, _P]),
     "tt_cache_create": (ctypes.c_int, [_P, _P, _I64, _I64]),
+    "tt_cache_create_policy": (ctypes.c_int, [_P, _P, _I64, _I64, ctypes.c_int]),
+    "tt_cache_export": (ctypes.c_int, [_P, _P, _P, _P, _P]),
+    "tt_cache_import": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "tt_cache_lookup": (ctypes.c_int, [_P, _P, _I64, _P, ctypes.c_int, _P, _P]),
     "tt_cache_populate": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "tt_cache_cached_indices": (ctypes.c_int, [_P, _P, _P]),
@@ -354,12 +359,15 @@ def tt_profile_read() -> dict:
 class Cache:
     """Owner of a tt_cache handle (frequency table + index->slot map)."""
 
-    def __init__(self, desc: TTDesc, cache_size: int, hashtbl_size: int):
+    def __init__(self, desc: TTDesc, cache_size: int, hashtbl_size: int,
+                 policy: int = TT_CACHE_TOPK):
         self.desc = desc
         self.cache_size = int(cache_size)
+        self.hashtbl_size = int(hashtbl_size)
         self._h = ctypes.c_void_p()
-        _check("tt_cache_create", lib().tt_cache_create(ctypes.byref(self._h), ctypes.byref(desc),
-                                                        int(cache_size), int(hashtbl_size)))
+        _check("tt_cache_create_policy",
+               lib().tt_cache_create_policy(ctypes.byref(self._h), ctypes.byref(desc),
+                                            int(cache_size), int(hashtbl_size), int(policy)))
 
     def lookup(self, indices, slot_out=None, count_freq: bool = True, dev_status=None,
                stream=None) -> torch.Tensor:
@@ -384,6 +392,25 @@ class Cache:
         _check("tt_cache_cached_indices",
                lib().tt_cache_cached_indices(self._h, _ptr(out), _stream(stream)))
         return out
+
+    def export_state(self, stream=None):
+        """(cached [cache_size] int64, keys [hashtbl_size] int64, counts [hashtbl_size] int32)."""
+        cached = torch.empty(self.cache_size, dtype=torch.int64, device="cuda")
+        keys = torch.empty(self.hashtbl_size, dtype=torch.int64, device="cuda")
+        counts = torch.empty(self.hashtbl_size, dtype=torch.int32, device="cuda")
+        _check("tt_cache_export", lib().tt_cache_export(self._h, _ptr(cached), _ptr(keys),
+                                                        _ptr(counts), _stream(stream)))
+        return cached, keys, counts
+
+    def import_state(self, cached, keys, counts, stream=None) -> None:
+        _need(cached, torch.int64, "cached")
+        _need(keys, torch.int64, "keys")
+        _need(counts, torch.int32, "counts")
+        if (cached.numel() != self.cache_size or keys.numel() != self.hashtbl_size
+                or counts.numel() != self.hashtbl_size):
+            raise ValueError("state sizes do not match this cache")
+        _check("tt_cache_import", lib().tt_cache_import(self._h, _ptr(cached), _ptr(keys),
+                                                        _ptr(counts), _stream(stream)))
 
     def close(self):
         if self._h:

@@ -21,6 +21,16 @@ hipError_t cache_assign_launch(const unsigned long long *sorted, int nf, int kbi
                                int64_t cache_size, int64_t *cached, long long *mkeys, int *mslot,
                                long long M, hipStream_t s);
 hipError_t iota64_launch(int64_t *a, long long n, hipStream_t s);
+hipError_t lfu_setkey_launch(const unsigned long long *prio, int n, int kbits, long long nsets,
+                             unsigned long long *out, hipStream_t s);
+hipError_t lfu_first_launch(const unsigned long long *sk, int n, int *set_first, hipStream_t s);
+hipError_t lfu_assign_launch(const unsigned long long *prio, const unsigned long long *sk, int n,
+                             int kbits, const int *set_first, long long nsets, int64_t *cached,
+                             int *fresh_slot, int64_t *fresh_idx, int *counters, hipStream_t s);
+hipError_t map_insert_launch(const int64_t *cached, long long K, long long *mkeys, int *mslot,
+                             long long M, hipStream_t s);
+hipError_t scatter_rows_launch(const float *tmp, const int *slot, int nf, int D, float *rows,
+                               hipStream_t s);
 }  // namespace ttb
 
 using namespace ttb;
@@ -486,6 +496,7 @@ int tt_bag_route(const tt_desc *desc, const int64_t *indices, int64_t nnz,
 // ---------------------------------------------------------------- cache
 struct tt_cache {
   tt_desc desc;
+  int policy = TT_CACHE_TOPK;
   int64_t cache_size = 0, H = 0, M = 0;
   int kbits = 1;
   long long *hkeys = nullptr;
@@ -500,12 +511,18 @@ struct tt_cache {
   void *fws = nullptr;
   size_t fws_bytes = 0;
   int device = 0;
+  // set-associative LFU only: set-major sort keys, set starts, newcomers, their rows
+  unsigned long long *lk0 = nullptr, *lk1 = nullptr;
+  int *set_first = nullptr, *fresh_slot = nullptr, *lcnt = nullptr;
+  int64_t *fresh_idx = nullptr;
+  float *rows_tmp = nullptr;
 };
 
 static void cache_free(tt_cache *c) {
   if (!c) return;
   void *ptrs[] = {c->hkeys, c->hcnt, c->mkeys, c->mslot, c->cached, c->sk0, c->sk1,
-                  c->shist, c->nent, c->bag_off, c->fws};
+                  c->shist, c->nent, c->bag_off, c->fws, c->lk0, c->lk1, c->set_first,
+                  c->fresh_slot, c->lcnt, c->fresh_idx, c->rows_tmp};
   for (void *p : ptrs)
     if (p) (void)hipFree(p);
   delete c;
@@ -513,7 +530,14 @@ static void cache_free(tt_cache *c) {
 
 int tt_cache_create(tt_cache **out, const tt_desc *desc, int64_t cache_size,
                     int64_t hashtbl_size) {
+  return tt_cache_create_policy(out, desc, cache_size, hashtbl_size, TT_CACHE_TOPK);
+}
+
+int tt_cache_create_policy(tt_cache **out, const tt_desc *desc, int64_t cache_size,
+                           int64_t hashtbl_size, int policy) {
   if (!out || !desc || cache_size < 1 || hashtbl_size < 1) return TT_EINVAL;
+  if (policy != TT_CACHE_TOPK && policy != TT_CACHE_LFU32) return TT_EINVAL;
+  if (policy == TT_CACHE_LFU32 && cache_size % 32 != 0) return TT_EINVAL;
   if (desc->num_tables != 1) return TT_ESHAPE;
   if (cache_size >= (int64_t)1 << 29 || hashtbl_size >= (int64_t)1 << 31) return TT_EFULL;
   Plan P;
@@ -522,6 +546,7 @@ int tt_cache_create(tt_cache **out, const tt_desc *desc, int64_t cache_size,
   tt_cache *c = new (std::nothrow) tt_cache();
   if (!c) return TT_EINVAL;
   c->desc = *desc;
+  c->policy = policy;
   c->cache_size = cache_size;
   c->H = hashtbl_size;
   int64_t M = 1;
@@ -545,6 +570,16 @@ int tt_cache_create(tt_cache **out, const tt_desc *desc, int64_t cache_size,
   ok = ok && hipMalloc(&c->nent, 4) == hipSuccess;
   ok = ok && hipMalloc(&c->bag_off, (size_t)(cache_size + 1) * 8) == hipSuccess;
   ok = ok && hipMalloc(&c->fws, c->fws_bytes) == hipSuccess;
+  if (policy == TT_CACHE_LFU32) {
+    const size_t D = (size_t)desc->q[0] * desc->q[1] * desc->q[2];
+    ok = ok && hipMalloc(&c->lk0, nsort * 8) == hipSuccess;
+    ok = ok && hipMalloc(&c->lk1, nsort * 8) == hipSuccess;
+    ok = ok && hipMalloc(&c->set_first, (size_t)(cache_size / 32) * 4) == hipSuccess;
+    ok = ok && hipMalloc(&c->fresh_slot, (size_t)cache_size * 4) == hipSuccess;
+    ok = ok && hipMalloc(&c->fresh_idx, (size_t)cache_size * 8) == hipSuccess;
+    ok = ok && hipMalloc(&c->lcnt, 8) == hipSuccess;
+    ok = ok && hipMalloc(&c->rows_tmp, (size_t)cache_size * D * 4) == hipSuccess;
+  }
   ok = ok && hipMemset(c->hkeys, 0xff, (size_t)c->H * 8) == hipSuccess;
   ok = ok && hipMemset(c->hcnt, 0, (size_t)c->H * 4) == hipSuccess;
   ok = ok && hipMemset(c->mkeys, 0xff, (size_t)M * 8) == hipSuccess;
@@ -568,6 +603,41 @@ int tt_cache_lookup(tt_cache *c, const int64_t *indices, int64_t nnz, int32_t *s
                                     dev_status, (hipStream_t)stream));
 }
 
+// Set-associative LFU populate: counts -> priority order -> set-major order -> one wave
+// per set keeps / replaces ways -> map rebuilt -> newcomers' rows rebuilt and scattered.
+static int populate_lfu(tt_cache *c, const float *const cores[3], float *rows, int64_t *n_filled,
+                        int n, hipStream_t s) {
+  const long long nsets = c->cache_size / 32;
+  hipError_t e = hipSuccess;
+  if (n > 0) e = radix_sort64(c->sk0, c->sk1, n, c->shist, s);
+  if (e == hipSuccess) e = lfu_setkey_launch(c->sk0, n, c->kbits, nsets, c->lk0, s);
+  if (e == hipSuccess && n > 0) e = radix_sort64(c->lk0, c->lk1, n, c->shist, s);
+  if (e == hipSuccess) e = hipMemsetAsync(c->set_first, 0xff, (size_t)nsets * 4, s);
+  if (e == hipSuccess) e = lfu_first_launch(c->lk0, n, c->set_first, s);
+  if (e == hipSuccess) e = hipMemsetAsync(c->lcnt, 0, 8, s);
+  if (e == hipSuccess)
+    e = lfu_assign_launch(c->sk0, c->lk0, n, c->kbits, c->set_first, nsets, c->cached,
+                          c->fresh_slot, c->fresh_idx, c->lcnt, s);
+  if (e == hipSuccess) e = hipMemsetAsync(c->mkeys, 0xff, (size_t)c->M * 8, s);
+  if (e == hipSuccess) e = map_insert_launch(c->cached, c->cache_size, c->mkeys, c->mslot, c->M, s);
+  int cnt[2] = {0, 0};
+  if (e == hipSuccess) e = hipMemcpyAsync(cnt, c->lcnt, 8, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return TT_EHIP;
+  const int nfresh = cnt[0];
+  if (nfresh > 0) {
+    int rc = tt_bag_forward(&c->desc, cores, c->fresh_idx, nfresh, c->bag_off, nfresh, nullptr,
+                            nullptr, c->rows_tmp, c->fws, c->fws_bytes, nullptr, s);
+    if (rc) return rc;
+    const int D = c->desc.q[0] * c->desc.q[1] * c->desc.q[2];
+    e = scatter_rows_launch(c->rows_tmp, c->fresh_slot, nfresh, D, rows, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return TT_EHIP;
+  }
+  *n_filled = cnt[1];
+  return TT_OK;
+}
+
 int tt_cache_populate(tt_cache *c, const float *const cores[3], float *rows, int64_t *n_filled,
                       void *stream) {
   if (!c || !cores || !cores[0] || !cores[1] || !cores[2] || !rows || !n_filled) return TT_EINVAL;
@@ -578,6 +648,7 @@ int tt_cache_populate(tt_cache *c, const float *const cores[3], float *rows, int
   if (e == hipSuccess) e = hipMemcpyAsync(&n, c->nent, 4, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return TT_EHIP;
+  if (c->policy == TT_CACHE_LFU32) return populate_lfu(c, cores, rows, n_filled, n, s);
   e = radix_sort64(c->sk0, c->sk1, n, c->shist, s);
   const int nf = (int)(n < c->cache_size ? n : c->cache_size);
   if (e == hipSuccess) e = hipMemsetAsync(c->mkeys, 0xff, (size_t)c->M * 8, s);
@@ -594,6 +665,34 @@ int tt_cache_populate(tt_cache *c, const float *const cores[3], float *rows, int
   if (e != hipSuccess) return TT_EHIP;
   *n_filled = nf;
   return TT_OK;
+}
+
+int tt_cache_export(tt_cache *c, int64_t *cached_out, int64_t *keys_out, int32_t *counts_out,
+                    void *stream) {
+  if (!c || !cached_out || !keys_out || !counts_out) return TT_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(cached_out, c->cached, (size_t)c->cache_size * 8,
+                                hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(keys_out, c->hkeys, (size_t)c->H * 8, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(counts_out, c->hcnt, (size_t)c->H * 4, hipMemcpyDeviceToDevice, s);
+  return finish(e);
+}
+
+int tt_cache_import(tt_cache *c, const int64_t *cached, const int64_t *keys,
+                    const int32_t *counts, void *stream) {
+  if (!c || !cached || !keys || !counts) return TT_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(c->cached, cached, (size_t)c->cache_size * 8,
+                                hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(c->hkeys, keys, (size_t)c->H * 8, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(c->hcnt, counts, (size_t)c->H * 4, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipMemsetAsync(c->mkeys, 0xff, (size_t)c->M * 8, s);
+  if (e == hipSuccess) e = map_insert_launch(c->cached, c->cache_size, c->mkeys, c->mslot, c->M, s);
+  return finish(e);
 }
 
 int tt_cache_cached_indices(tt_cache *c, int64_t *cached_out, void *stream) {

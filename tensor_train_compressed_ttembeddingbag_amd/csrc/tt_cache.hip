@@ -167,6 +167,120 @@ __global__ __launch_bounds__(256) void k_cache_assign(const unsigned long long *
   }
 }
 
+// ---------------------------------------------------------------- set-associative LFU
+// "Software Cache" names a 32-way set-associative LFU cache.  slot = set * 32 + way; the
+// set of index i is (splitmix64(i) >> 32) mod nsets.  A populate keeps in every set the
+// 32 counted indices of the set with the highest counts (ties: smaller index); indices
+// that stay keep their way (and their row); newcomers take the freed ways in ascending
+// order, in (count desc, index asc) order, and only their rows are rebuilt.
+constexpr int LFU_WAYS = 32;
+
+__device__ __forceinline__ long long lfu_set(long long key, long long nsets) {
+  return (long long)((mix64((unsigned long long)key) >> 32) % (unsigned long long)nsets);
+}
+
+// key[r] = (set << 32) | r for the r-th entry of the priority order (sorting these keys
+// orders the entries by set, then priority)
+__global__ __launch_bounds__(256) void k_lfu_setkey(const unsigned long long *prio, int n,
+                                                     int kbits, long long nsets,
+                                                     unsigned long long *out) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= n) return;
+  const unsigned long long mask = (kbits >= 64) ? ~0ull : ((1ull << kbits) - 1ull);
+  const long long key = (long long)(prio[r] & mask);
+  out[r] = ((unsigned long long)lfu_set(key, nsets) << 32) | (unsigned)r;
+}
+
+// first position of every set in the set-major order (-1: no candidate)
+__global__ __launch_bounds__(256) void k_lfu_first(const unsigned long long *sk, int n,
+                                                    int *set_first) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= n) return;
+  const unsigned s = (unsigned)(sk[p] >> 32);
+  if (p == 0 || (unsigned)(sk[p - 1] >> 32) != s) set_first[s] = p;
+}
+
+// one wave per set: lanes 0..31 are the ways (old occupants) and the new members
+__global__ __launch_bounds__(256) void k_lfu_assign(const unsigned long long *prio,
+                                                     const unsigned long long *sk, int n,
+                                                     int kbits, const int *set_first,
+                                                     long long nsets, int64_t *cached,
+                                                     int *fresh_slot, int64_t *fresh_idx,
+                                                     int *counters) {
+  const int lane = threadIdx.x & 63;
+  const long long s = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (s >= nsets) return;
+  const unsigned long long mask = (kbits >= 64) ? ~0ull : ((1ull << kbits) - 1ull);
+  const int first = set_first[s];
+  long long m = -1;  // member `lane` of the set (priority order), or -1
+  if (first >= 0 && lane < LFU_WAYS && first + lane < n) {
+    const unsigned long long k = sk[first + lane];
+    if ((long long)(k >> 32) == s) m = (long long)(prio[(unsigned)k] & mask);
+  }
+  const long long o = lane < LFU_WAYS ? (long long)cached[s * LFU_WAYS + lane] : -1;
+  bool kept = false, is_new = m >= 0;
+  for (int j = 0; j < LFU_WAYS; ++j) {
+    const long long mj = __shfl(m, j), oj = __shfl(o, j);
+    kept = kept || (o >= 0 && o == mj);
+    is_new = is_new && m != oj;
+  }
+  const unsigned long long keep_m = __ballot(lane < LFU_WAYS && kept);
+  const unsigned long long new_m = __ballot(lane < LFU_WAYS && is_new);
+  const unsigned long long free_m = ~keep_m & 0xffffffffull;
+  // way `lane`: kept, or the r-th free way takes the r-th newcomer, or empty
+  long long v = kept ? o : -1;
+  bool fresh = false;
+  if (lane < LFU_WAYS && !kept) {
+    const int r = __popcll(free_m & ((1ull << lane) - 1ull));
+    unsigned long long nm = new_m;
+    for (int t = 0; t < r && nm; ++t) nm &= nm - 1ull;  // drop the first r newcomers
+    if (nm) {
+      const int j = __ffsll((long long)nm) - 1;
+      v = j;  // lane of the newcomer; its index is read below
+      fresh = true;
+    }
+  }
+  const long long mv = __shfl(m, fresh ? (int)v : 0);
+  if (fresh) v = mv;
+  if (lane < LFU_WAYS) {
+    const long long slot = s * LFU_WAYS + lane;
+    cached[slot] = v;
+    if (fresh) {
+      const int f = atomicAdd(&counters[0], 1);
+      fresh_slot[f] = (int)slot;
+      fresh_idx[f] = v;
+    }
+  }
+  const unsigned long long valid = __ballot(lane < LFU_WAYS && v >= 0);
+  if (lane == 0 && valid) atomicAdd(&counters[1], __popcll(valid));
+}
+
+// the index -> slot map from the slot table
+__global__ __launch_bounds__(256) void k_map_insert(const int64_t *cached, long long K,
+                                                     long long *mkeys, int *mslot, long long M) {
+  const long long s = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= K) return;
+  const long long key = (long long)cached[s];
+  if (key < 0) return;
+  long long h = (long long)(mix64((unsigned long long)key) & (unsigned long long)(M - 1));
+  for (long long probe = 0; probe < M; ++probe) {
+    const long long prev = (long long)atomicCAS((unsigned long long *)&mkeys[h],
+                                                (unsigned long long)EMPTY_KEY,
+                                                (unsigned long long)key);
+    if (prev == EMPTY_KEY) { mslot[h] = (int)s; return; }
+    h = (h + 1) & (M - 1);
+  }
+}
+
+// rows[slot[f]] = tmp[f]
+__global__ __launch_bounds__(256) void k_scatter_rows(const float *tmp, const int *slot, int nf,
+                                                       int D, float *rows) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)nf * D) return;
+  const long long f = i / D, d = i - f * D;
+  rows[(size_t)slot[f] * D + d] = tmp[i];
+}
+
 __global__ void k_iota64(int64_t *a, long long n) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) a[i] = i;
@@ -211,6 +325,41 @@ hipError_t cache_assign_launch(const unsigned long long *sorted, int nf, int kbi
   if (cache_size > 0)
     hipLaunchKernelGGL(k_cache_assign, dim3((unsigned)((cache_size + 255) / 256)), dim3(256), 0,
                        s, sorted, nf, kbits, cache_size, cached, mkeys, mslot, M);
+  return hipGetLastError();
+}
+
+hipError_t lfu_setkey_launch(const unsigned long long *prio, int n, int kbits, long long nsets,
+                             unsigned long long *out, hipStream_t s) {
+  if (n > 0) hipLaunchKernelGGL(k_lfu_setkey, dim3((n + 255) / 256), dim3(256), 0, s, prio, n, kbits,
+                                nsets, out);
+  return hipGetLastError();
+}
+
+hipError_t lfu_first_launch(const unsigned long long *sk, int n, int *set_first, hipStream_t s) {
+  if (n > 0) hipLaunchKernelGGL(k_lfu_first, dim3((n + 255) / 256), dim3(256), 0, s, sk, n, set_first);
+  return hipGetLastError();
+}
+
+hipError_t lfu_assign_launch(const unsigned long long *prio, const unsigned long long *sk, int n,
+                             int kbits, const int *set_first, long long nsets, int64_t *cached,
+                             int *fresh_slot, int64_t *fresh_idx, int *counters, hipStream_t s) {
+  hipLaunchKernelGGL(k_lfu_assign, dim3((unsigned)((nsets + 3) / 4)), dim3(256), 0, s, prio, sk, n,
+                     kbits, set_first, nsets, cached, fresh_slot, fresh_idx, counters);
+  return hipGetLastError();
+}
+
+hipError_t map_insert_launch(const int64_t *cached, long long K, long long *mkeys, int *mslot,
+                             long long M, hipStream_t s) {
+  if (K > 0) hipLaunchKernelGGL(k_map_insert, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s,
+                                cached, K, mkeys, mslot, M);
+  return hipGetLastError();
+}
+
+hipError_t scatter_rows_launch(const float *tmp, const int *slot, int nf, int D, float *rows,
+                               hipStream_t s) {
+  const long long n = (long long)nf * D;
+  if (n > 0) hipLaunchKernelGGL(k_scatter_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                                tmp, slot, nf, D, rows);
   return hipGetLastError();
 }
 
