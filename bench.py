@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-pipeline", action="store_true",
                     help="group each batch right before its forward (no overlap with the "
                          "previous backward)")
+    ap.add_argument("--cache-policy", default="topk", choices=["topk", "lfu32"],
+                    help="cached workload: exact top-K or 32-way set-associative LFU")
     ap.add_argument("--update", default="sgd", choices=["sgd", "adagrad", "grad"],
                     help="backward: fused SGD, fused Adagrad (eps 1e-10), or gradients returned")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -102,13 +104,19 @@ def main():
     max_nnz = max(b["indices"].numel() for b in batches)
     B = wl.bags_per_table
     cache = None
+    csize = 0
     if wl.cache_size:
-        cache = abi.Cache(desc, wl.cache_size, wl.hashtbl_size)
+        policy = abi.TT_CACHE_LFU32 if args.cache_policy == "lfu32" else abi.TT_CACHE_TOPK
+        csize = wl.cache_size // 32 * 32 if policy == abi.TT_CACHE_LFU32 else wl.cache_size
+        cache = abi.Cache(desc, csize, wl.hashtbl_size, policy=policy)
         for k in range(wl.warmup_batches):
             wb = W.make_batch(wl, 500 + k)
             cache.lookup(torch.from_numpy(wb["indices"]).cuda(), count_freq=True)
-        rows = torch.zeros(wl.cache_size, wl.D, device="cuda")
+        rows = torch.zeros(csize, wl.D, device="cuda")
+        torch.cuda.synchronize()
+        tp = time.perf_counter()
         n_filled = cache.populate(g, rows)
+        populate_ms = (time.perf_counter() - tp) * 1e3
         slots = [torch.empty(b["indices"].numel(), dtype=torch.int32, device="cuda") for b in batches]
     if args.update == "adagrad":  # running sums of squared gradients, from zero
         aux = [torch.zeros_like(x) for x in g]
@@ -122,7 +130,7 @@ def main():
     # two workspaces alternate, and events order (a) the forward of a batch after its
     # grouping and (b) a grouping after the last use of its workspace (two batches back).
     pipeline = not args.no_pipeline
-    wss = [abi.workspace(desc, max_nnz, B, wl.cache_size) for _ in range(2 if pipeline else 1)]
+    wss = [abi.workspace(desc, max_nnz, B, csize) for _ in range(2 if pipeline else 1)]
     out = torch.empty(wl.num_tables * B, wl.D, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     main = torch.cuda.current_stream()
@@ -222,7 +230,7 @@ def main():
                                "nnz/step=%.0f lengths=%s indices=%s weighted=%s lr=%g cache=%d"
                                % (wl.name, list(wl.p), list(wl.q), list(wl.ranks), wl.E, wl.D,
                                   wl.num_tables, B, nnz_mean, list(wl.lengths), list(wl.dist),
-                                  wl.weighted, wl.lr, wl.cache_size),
+                                  wl.weighted, wl.lr, csize),
                    "nnz": nnz_mean, "global_batch": wl.num_tables * B,
                    "update": args.update,
                    "pipeline": "grouping of batch i+1 overlapped with the backward of batch i"
@@ -230,6 +238,8 @@ def main():
     }
     if cache is not None:
         res["config"]["cache_rows_filled"] = n_filled
+        res["config"]["cache_policy"] = args.cache_policy
+        res["config"]["populate_ms"] = round(populate_ms, 3)
 
     if not args.no_roofline:
         res["roofline"], res["kernels"] = roofline(args, wl, batches, step, torch, abi, metrics,
