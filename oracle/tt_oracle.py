@@ -37,7 +37,8 @@ _SO = os.path.join(_HERE, "libtt_oracle.so")
 
 __all__ = ["build", "forward", "backward", "sgd", "adagrad", "tt_row", "split_index", "bag_ids",
            "route_order", "group_counts", "count_frequencies", "select_cache",
-           "lookup_slots", "populate_rows", "splitmix64", "lfu_set", "lfu_populate", "LFU_WAYS"]
+           "lookup_slots", "populate_rows", "splitmix64", "lfu_set", "lfu_populate", "LFU_WAYS",
+           "philox4x32_10", "init_param", "init_core", "factorize"]
 
 
 def build(force: bool = False) -> str:
@@ -346,3 +347,81 @@ def lfu_populate(counts: dict, cached, cache_size: int):
             new[s * LFU_WAYS + w] = k
             fresh[s * LFU_WAYS + w] = True
     return np.asarray(new, dtype=np.int64), fresh
+
+
+# ---------------------------------------------------------------- initialisation
+# "Parameters" (`weight_dist`) and the TT-Rec abstract: i.i.d. cores, or cores drawn so
+# that the full table's entries follow the target; readings in the C ABI's header.
+
+_PHILOX_M = (0xD2511F53, 0xCD9E8D57)
+_PHILOX_W = (0x9E3779B9, 0xBB67AE85)
+
+
+def philox4x32_10(c0, c1, c2, c3, k0, k1):
+    """Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011) on uint32 numpy arrays (or
+    ints): ten rounds of two 32x32->64 multiplications, the Weyl-sequence key bumps."""
+    u = np.uint64
+    c0, c1, c2, c3 = (np.asarray(x, dtype=np.uint64) for x in (c0, c1, c2, c3))
+    k0, k1 = np.asarray(k0, dtype=np.uint64), np.asarray(k1, dtype=np.uint64)
+    m32 = u(0xFFFFFFFF)
+    for _ in range(10):
+        p0 = u(_PHILOX_M[0]) * c0
+        p1 = u(_PHILOX_M[1]) * c2
+        c0, c1, c2, c3 = ((p1 >> u(32)) ^ c1 ^ k0) & m32, p1 & m32, \
+            ((p0 >> u(32)) ^ c3 ^ k1) & m32, p0 & m32
+        k0 = (k0 + u(_PHILOX_W[0])) & m32
+        k1 = (k1 + u(_PHILOX_W[1])) & m32
+    return c0, c1, c2, c3
+
+
+def init_param(dist: int, scale: float, R1: int, R2: int) -> float:
+    """Parameter of the core distribution: 0 uniform U(-s,s), 1 normal N(0,s^2),
+    2 approx-uniform, 3 approx-normal (table entries with the target's variance)."""
+    rr = float(R1) * float(R2)
+    if dist == 3:
+        return (scale * scale / rr) ** (1.0 / 6.0)
+    if dist == 2:
+        return (3.0 * (scale * scale / (3.0 * rr)) ** (1.0 / 3.0)) ** 0.5
+    return float(scale)
+
+
+def init_core(n: int, k: int, dist: int, a: float, seed: int):
+    """The n values (fp64) of core k's stored array for the given seed."""
+    i = np.arange(n, dtype=np.uint64)
+    x0, x1, _, _ = philox4x32_10(i & np.uint64(0xFFFFFFFF), i >> np.uint64(32),
+                                 np.full(n, k, dtype=np.uint64), np.zeros(n, dtype=np.uint64),
+                                 seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
+    u0 = ((x0 >> np.uint64(9)).astype(np.float64) + 0.5) * 2.0 ** -23
+    if dist in (1, 3):
+        u1 = ((x1 >> np.uint64(9)).astype(np.float64) + 0.5) * 2.0 ** -23
+        return a * np.sqrt(-2.0 * np.log(u0)) * np.cos(2.0 * np.pi * u1)
+    return a * (2.0 * u0 - 1.0)
+
+
+def factorize(n: int, exact: bool):
+    """Brute force of the automatic-shape rule: exact (q1 q2 q3 == n, q1 in {1,2,4},
+    q3 <= 16): the smallest largest factor, then the largest smallest, then the
+    smallest q1, then the largest q2; not exact (p1 <= p2 <= p3, product >= n): the
+    smallest largest factor, then the smallest product, then the smallest p1."""
+    best = None
+    if exact:
+        for a in (1, 2, 4):
+            for b in range(1, n + 1):
+                for c in range(1, 17):
+                    if a * b * c != n:
+                        continue
+                    key = (max(a, b, c), -min(a, b, c), a, -b)
+                    if best is None or key < best[0]:
+                        best = (key, (a, b, c))
+        return None if best is None else best[1]
+    for p3 in range(1, n + 1):
+        for p2 in range(1, p3 + 1):
+            for p1 in range(1, p2 + 1):
+                if p1 * p2 * p3 < n:
+                    continue
+                key = (p3, p1 * p2 * p3, p1)
+                if best is None or key < best[0]:
+                    best = (key, (p1, p2, p3))
+        if best is not None and best[0][0] <= p3:
+            break
+    return best[1]

@@ -605,3 +605,57 @@ def test_lfu_repeated_populates_brute_force():
                 assert new[s] == cached[s]
             assert fresh[s] == (new[s] >= 0 and new[s] != cached[s])
         cached = new
+
+
+# --------------------------------------------------------------- initialisation / shapes
+
+def test_philox_known_answers():
+    """Philox4x32-10 known-answer vectors published with the generator (Random123)."""
+    P = oracle.tt_oracle.philox4x32_10
+    M = 0xFFFFFFFF
+    cases = [((0, 0, 0, 0), (0, 0), (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+             ((M, M, M, M), (M, M), (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+             ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+              (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1))]
+    for ctr, key, want in cases:
+        assert tuple(int(x) for x in P(*ctr, *key)) == want
+
+
+def test_init_distributions_moments():
+    """Moments of the oracle's initialisers: uniform cores have variance a^2/3, normal
+    cores a^2; for the approx- variants the dense table built from the cores has
+    (close to) the target's mean 0 and variance (scale^2 or scale^2/3)."""
+    O = oracle.tt_oracle
+    u = O.init_core(200000, 0, 0, 0.5, 7)
+    assert abs(u.mean()) < 0.01 and abs(u.var() - 0.25 / 3) < 0.003 and np.abs(u).max() < 0.5
+    z = O.init_core(200000, 1, 1, 2.0, 8)
+    assert abs(z.mean()) < 0.03 and abs(z.var() - 4.0) < 0.1
+    assert abs(np.mean(z ** 4) / np.mean(z ** 2) ** 2 - 3.0) < 0.1  # normal kurtosis
+    p, q, ranks = (9, 8, 7), (2, 2, 2), (6, 5)
+    full = (1,) + ranks + (1,)
+    for dist, scale, var in ((3, 0.3, 0.09), (2, 0.6, 0.12)):
+        a = O.init_param(dist, scale, *ranks)
+        cores = []
+        for k in range(3):
+            shp = (p[k], full[k], q[k], full[k + 1])  # slice-major, as stored
+            x = O.init_core(int(np.prod(shp)), k, dist, a, 100 + dist)
+            cores.append(np.moveaxis(x.reshape(shp), 0, 1).astype(np.float32))
+        Wd = _dense_rows(p, q, ranks, cores)
+        assert abs(Wd.mean()) < 0.05 * scale
+        assert abs(Wd.var() / var - 1.0) < 0.15, (dist, Wd.var(), var)
+
+
+def test_factorize_rule_by_hand():
+    """Values worked out by hand from the rule (exact: min max, max min, min q1, max q2
+    among q1 in {1,2,4}, q3 <= 16; not exact: p3 = ceil(cbrt n), min product, min p1)."""
+    F = oracle.tt_oracle.factorize
+    assert F(64, True) == (4, 4, 4)
+    assert F(128, True) == (4, 8, 4)
+    assert F(3, True) == (1, 3, 1)
+    assert F(1024, True) == (4, 16, 16)
+    assert F(12, True) == (2, 3, 2)
+    assert F(10, False) == (2, 2, 3)
+    assert F(11, False) == (2, 2, 3)
+    assert F(120, False) == (5, 5, 5)
+    assert F(1000, False) == (10, 10, 10)
+    assert F(1001, False) == (9, 11, 11)  # p3 = 11, p1 p2 >= 91: 9 * 11 = 99 < 10 * 10
