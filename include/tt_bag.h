@@ -299,6 +299,41 @@ int tt_cache_import(tt_cache *c, const int64_t *cached, const int64_t *keys,
 
 int tt_cache_destroy(tt_cache *c);
 
+/* ---------------------------------------------------------------- initialisation
+ * "Parameters" (`weight_dist`): the cores are drawn i.i.d. from the named distribution,
+ * or ("approx-" variants) so that the entries of the full table follow it; the TT-Rec
+ * abstract recommends sampled-Gaussian cores (= TT_INIT_APPROX_NORMAL here).  A table
+ * entry sums R1*R2 products of one entry per core, so zero-mean i.i.d. cores of
+ * variance v give Var(W) = R1 R2 v^3; the approx- variants pick v to match the target's
+ * mean (0) and variance:
+ *   TT_INIT_UNIFORM         cores U(-scale, scale)
+ *   TT_INIT_NORMAL          cores N(0, scale^2)
+ *   TT_INIT_APPROX_UNIFORM  W with the variance of U(-scale, scale): cores U(-c, c),
+ *                           c^2 / 3 = (scale^2 / (3 R1 R2))^(1/3)
+ *   TT_INIT_APPROX_NORMAL   W with the variance of N(0, scale^2): cores N(0, v),
+ *                           v = (scale^2 / (R1 R2))^(1/3)
+ * Random numbers: Philox4x32-10 (Salmon et al., SC 2011), key = seed (low word first),
+ * counter = (n mod 2^32, n >> 32, k, 0) for element n of core k in its stored array
+ * (all tables, slice-major); u = ((x >> 9) + 1/2) 2^-23 from the counter's words x0, x1;
+ * uniform a (2 u0 - 1); normal by Box-Muller, a sqrt(-2 ln u0) cos(2 pi u1).
+ * Fills cores[0..2] (device, the layout of the forward) on `stream`; scale finite, >= 0. */
+#define TT_INIT_UNIFORM        0
+#define TT_INIT_NORMAL         1
+#define TT_INIT_APPROX_UNIFORM 2
+#define TT_INIT_APPROX_NORMAL  3
+int tt_init_cores(const tt_desc *desc, float *const cores[3], int dist, float scale,
+                  uint64_t seed, void *stream);
+
+/* Automatic shapes ("Initialization": without p / q shapes the sizes are factored
+ * automatically; the pages state no rule).  Host function, 1 <= n < 2^31.
+ *   exact != 0 (q: q1 q2 q3 == n, q1 in {1, 2, 4}, q3 <= 16 as the kernels require;
+ *              TT_ESHAPE if there is none): the triple with the smallest largest
+ *              factor, then the largest smallest factor, then the smallest q1, then the
+ *              largest q2;
+ *   exact == 0 (p: p1 p2 p3 >= n): p3 = the smallest m with m^3 >= n, p1 <= p2 <= p3
+ *              with the smallest product, then the smallest p1. */
+int tt_factorize(int64_t n, int exact, int32_t out[3]);
+
 /* ---------------------------------------------------------------- timing
  * Optional per-kernel timing for benchmarks: while enabled, every kernel the
  * library enqueues is bracketed by two HIP events recorded on the stream it is

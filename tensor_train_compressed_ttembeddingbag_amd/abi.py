@@ -26,6 +26,10 @@ TT_DEV_STALE_PLAN = 16
 TT_DEV_SYNC_TIMEOUT = 32
 TT_CACHE_TOPK = 0
 TT_CACHE_LFU32 = 1
+TT_INIT_UNIFORM = 0
+TT_INIT_NORMAL = 1
+TT_INIT_APPROX_UNIFORM = 2
+TT_INIT_APPROX_NORMAL = 3
 
 
 class TTError(RuntimeError):
@@ -70,6 +74,8 @@ _SIG = {
                                                     _P, _P, ctypes.c_size_t, _P, _P]),
     "tt_bag_route": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _I64, _P, _P, _P, ctypes.c_size_t,
                                     _P, _P]),
+    "tt_init_cores": (ctypes.c_int, [_P, _P, ctypes.c_int, ctypes.c_float, ctypes.c_uint64, _P]),
+    "tt_factorize": (ctypes.c_int, [_I64, ctypes.c_int, _P]),
     "tt_cache_create": (ctypes.c_int, [_P, _P, _I64, _I64]),
     "tt_cache_create_policy": (ctypes.c_int, [_P, _P, _I64, _I64, ctypes.c_int]),
     "tt_cache_export": (ctypes.c_int, [_P, _P, _P, _P, _P]),
@@ -318,6 +324,20 @@ def tt_bag_backward_grad(desc: TTDesc, cores, indices, offsets, num_bags: int, g
                               _ptr(dev_status), _stream(stream))
     _check(name, rc)
     return grad_cores, gr
+
+
+def tt_init_cores(desc: TTDesc, cores, dist: int, scale: float, seed: int, stream=None) -> None:
+    """Fill the three core tensors (slice-major, all tables) on the device (see tt_bag.h)."""
+    _check("tt_init_cores", lib().tt_init_cores(ctypes.byref(desc), _cores(cores), int(dist),
+                                                float(scale), int(seed) & ((1 << 64) - 1),
+                                                _stream(stream)))
+
+
+def tt_factorize(n: int, exact: bool):
+    """Automatic factorisation of a table size (exact: product == n, else >= n)."""
+    out = (ctypes.c_int32 * 3)()
+    _check("tt_factorize", lib().tt_factorize(int(n), 1 if exact else 0, out))
+    return tuple(int(x) for x in out)
 
 
 def tt_bag_route(desc: TTDesc, indices, offsets, num_bags: int, slots=None, cache_size: int = 0,

@@ -136,3 +136,17 @@ def test_row_split_through_double_reciprocals():
         r3 = np.where(r3 >= p3, r3 - p3, np.where(r3 < 0, r3 + p3, r3))
         assert np.array_equal(q1, i // p23) and np.array_equal(q2, (i % p23) // p3)
         assert np.array_equal(r3, i % p3)
+
+
+def test_factorize_host_function_matches_the_oracle_rule():
+    """tt_factorize (host code of the library, no GPU) against the oracle's brute force."""
+    import oracle.tt_oracle as O
+    for n in range(1, 160):
+        assert abi.tt_factorize(n, False) == O.factorize(n, False), n
+        want = O.factorize(n, True)
+        if want is None:
+            with pytest.raises(abi.TTError):
+                abi.tt_factorize(n, True)
+        else:
+            assert abi.tt_factorize(n, True) == want, n
+    assert abi.tt_factorize(11000000, False) == (222, 223, 223)
