@@ -236,6 +236,19 @@ def main():
                    "pipeline": "grouping of batch i+1 overlapped with the backward of batch i"
                                if pipeline else "none"},
     }
+    # initialisation of the workload's cores (approx-normal), off the training path
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    scratch = [torch.empty_like(x) for x in g]
+    abi.tt_init_cores(desc, scratch, abi.TT_INIT_APPROX_NORMAL, 1.0, 1)
+    ev0.record()
+    for r in range(20):
+        abi.tt_init_cores(desc, scratch, abi.TT_INIT_APPROX_NORMAL, 1.0, r)
+    ev1.record()
+    torch.cuda.synchronize()
+    init_us = ev0.elapsed_time(ev1) * 1e3 / 20
+    nel = sum(x.numel() for x in g)
+    res["config"]["init_cores_us"] = round(init_us, 2)
+    res["config"]["init_cores_gbs"] = round(nel * 4 / (init_us * 1e-6) / 1e9, 1)
     if cache is not None:
         res["config"]["cache_rows_filled"] = n_filled
         res["config"]["cache_policy"] = args.cache_policy
