@@ -24,6 +24,10 @@
  *    the offsets array carries the terminal entry off[nbags] = nnz.  Sum pooling,
  *    optional per-sample weights, an empty bag gives a zero row.
  *
+ *  - Mean pooling (PyTorch EmbeddingBag's mode "mean", named as a variant in the survey
+ *    of the pages): the bag's (weighted) sum divided by its number of elements; an
+ *    empty bag gives a zero row.
+ *
  *  - TableBatched layout ("TableBatchedTTEmbeddingBag" section: T tables of one
  *    shape).  Bags are numbered table-major, bag b belongs to table b / B.
  *
@@ -64,6 +68,7 @@ typedef struct {
     int32_t p[3];
     int32_t q[3];
     int32_t r[2];            /* tt_ranks; full ranks are {1, r[0], r[1], 1} */
+    int32_t pooling;         /* 0: sum, 1: mean (sum divided by the bag's length) */
 } oracle_shape;
 
 static int64_t prod3(const int32_t *v) { return (int64_t)v[0] * v[1] * v[2]; }
@@ -164,6 +169,8 @@ int oracle_forward(const oracle_shape *s, const float *const *cores,
             }
             for (int64_t j = 0; j < D; ++j) Y[b * D + j] += w * row[j];
         }
+        if (s->pooling == 1 && off[b + 1] > off[b])
+            for (int64_t j = 0; j < D; ++j) Y[b * D + j] /= (double)(off[b + 1] - off[b]);
     }
     free(row);
     return 0;
@@ -197,8 +204,10 @@ int oracle_backward(const oracle_shape *s, const float *const *cores,
         const int64_t t = b / B;
         const float *G1 = cores[3 * t], *G2 = cores[3 * t + 1], *G3 = cores[3 * t + 2];
         double *d1 = grad[3 * t], *d2 = grad[3 * t + 1], *d3 = grad[3 * t + 2];
+        /* mean pooling: out[b] = (sum) / len, so each element's gradient carries 1 / len */
+        const double inv = (s->pooling == 1) ? 1.0 / (double)(off[b + 1] - off[b]) : 1.0;
         for (int64_t n = off[b]; n < off[b + 1]; ++n) {
-            const double w = psw ? (double)psw[n] : 1.0;
+            const double w = (psw ? (double)psw[n] : 1.0) * inv;
             if (slot && slot[n] >= 0) {
                 for (int64_t j = 0; j < D; ++j)
                     grad_cache[slot[n] * D + j] += w * (double)dY[b * D + j];

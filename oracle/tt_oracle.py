@@ -54,7 +54,7 @@ def build(force: bool = False) -> str:
 class _Shape(ctypes.Structure):
     _fields_ = [("num_tables", ctypes.c_int32), ("num_embeddings", ctypes.c_int64),
                 ("p", ctypes.c_int32 * 3), ("q", ctypes.c_int32 * 3),
-                ("r", ctypes.c_int32 * 2)]
+                ("r", ctypes.c_int32 * 2), ("pooling", ctypes.c_int32)]
 
 
 _lib = None
@@ -82,8 +82,9 @@ def _L():
     return _lib
 
 
-def _shape(p, q, ranks, E, T):
+def _shape(p, q, ranks, E, T, pooling=0):
     s = _Shape()
+    s.pooling = int(pooling)
     s.num_tables = int(T)
     s.num_embeddings = int(E)
     for k in range(3):
@@ -118,14 +119,14 @@ def tt_row(p, q, ranks, cores3, i: int) -> np.ndarray:
 
 
 def forward(p, q, ranks, E, cores, indices, offsets, num_bags, per_sample_weights=None,
-            slots=None, cache_rows=None):
+            slots=None, cache_rows=None, pooling=0):
     """EmbeddingBag forward over the implicit TT table(s).
 
-    cores: list of T lists [G1, G2, G3] in the logical layout.  Returns Y as
-    float64 [T*num_bags, D]."""
+    cores: list of T lists [G1, G2, G3] in the logical layout; pooling 0 = sum,
+    1 = mean.  Returns Y as float64 [T*num_bags, D]."""
     T = len(cores)
     flat = [_f32(c) for tbl in cores for c in tbl]
-    s = _shape(p, q, ranks, E, T)
+    s = _shape(p, q, ranks, E, T, pooling)
     idx = np.ascontiguousarray(indices, dtype=np.int64)
     off = np.ascontiguousarray(offsets, dtype=np.int64)
     psw = None if per_sample_weights is None else _f32(per_sample_weights)
@@ -142,7 +143,7 @@ def forward(p, q, ranks, E, cores, indices, offsets, num_bags, per_sample_weight
 
 
 def backward(p, q, ranks, E, cores, indices, offsets, num_bags, grad_out,
-             per_sample_weights=None, slots=None, cache_size=0):
+             per_sample_weights=None, slots=None, cache_size=0, pooling=0):
     """Gradients of L = sum_b <dY[b], Y[b]>.
 
     Returns (grads, touched, grad_cache, touched_cache): grads is a list of T lists
@@ -150,7 +151,7 @@ def backward(p, q, ranks, E, cores, indices, offsets, num_bags, grad_out,
     uint8 masks over the slices p_k."""
     T = len(cores)
     flat = [_f32(c) for tbl in cores for c in tbl]
-    s = _shape(p, q, ranks, E, T)
+    s = _shape(p, q, ranks, E, T, pooling)
     idx = np.ascontiguousarray(indices, dtype=np.int64)
     off = np.ascontiguousarray(offsets, dtype=np.int64)
     psw = None if per_sample_weights is None else _f32(per_sample_weights)

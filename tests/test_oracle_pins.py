@@ -509,6 +509,9 @@ _MUTANTS = [
     # Adagrad: the step taken with the sum before this gradient
     ("state[e] = (float)((double)state[e] + g * g);\n                    core[e] = (float)((double)core[e] - lr * g / (sqrt((double)state[e]) + eps));",
      "core[e] = (float)((double)core[e] - lr * g / (sqrt((double)state[e]) + eps));\n                    state[e] = (float)((double)state[e] + g * g);"),
+    # mean pooling: the backward without the 1 / length
+    ("const double w = (psw ? (double)psw[n] : 1.0) * inv;",
+     "const double w = (psw ? (double)psw[n] : 1.0);"),
     # Adagrad on cache rows: the squared gradient not added
     ("state[e] = (float)((double)state[e] + g * g);\n            rows[e]",
      "state[e] = (float)((double)state[e] + g);\n            rows[e]"),
@@ -541,7 +544,8 @@ def test_pins_catch_planted_mistakes(mi, tmp_path, monkeypatch):
             test_pooling_matches_torch_embedding_bag_on_decompressed_table,
             test_pooling_invariants, test_backward_equals_exact_finite_differences,
             test_backward_matches_torch_autograd, test_sgd_step_invariants,
-            test_adagrad_matches_torch_optim_adagrad, test_adagrad_first_step_closed_form]
+            test_adagrad_matches_torch_optim_adagrad, test_adagrad_first_step_closed_form,
+            test_mean_pooling_matches_torch_embedding_bag]
     try:
         for f in pins:
             try:
@@ -659,3 +663,38 @@ def test_factorize_rule_by_hand():
     assert F(120, False) == (5, 5, 5)
     assert F(1000, False) == (10, 10, 10)
     assert F(1001, False) == (9, 11, 11)  # p3 = 11, p1 p2 >= 91: 9 * 11 = 99 < 10 * 10
+
+
+# --------------------------------------------------------------- mean pooling
+
+def test_mean_pooling_matches_torch_embedding_bag():
+    """Library routine: torch's EmbeddingBag in mode "mean" (float64) over the dense
+    rebuild of the table, forward and autograd backward, two tables, empty bags.  With
+    per-sample weights (which torch takes in sum mode only) the mean is the weighted sum
+    over the bag's length."""
+    rng = _rng(41)
+    p, q, ranks, E, B, T = (4, 3, 2), (2, 2, 3), (3, 4), 23, 4, 2
+    cores = [_rand_cores(rng, p, q, ranks) for _ in range(T)]
+    lens = np.array([2, 5, 0, 4, 3, 1, 6, 2])
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    idx = rng.integers(0, E, off[-1]).astype(np.int64)
+    dY = rng.standard_normal((T * B, 12)).astype(np.float32)
+    Y = oracle.forward(p, q, ranks, E, cores, idx, off, B, pooling=1)
+    grads, _, _, _ = oracle.backward(p, q, ranks, E, cores, idx, off, B, dY, pooling=1)
+    for t in range(T):
+        G = [torch.tensor(c.astype(np.float64), requires_grad=True) for c in cores[t]]
+        Wt = torch.einsum("aipr,rjqs,skvb->ijkpqv", *G).reshape(int(np.prod(p)), 12)[:E]
+        lo = off[t * B]
+        Yt = torch.nn.functional.embedding_bag(
+            torch.from_numpy(idx[lo:off[(t + 1) * B]]), Wt,
+            torch.from_numpy(off[t * B:(t + 1) * B] - lo), mode="mean")
+        np.testing.assert_allclose(Y[t * B:(t + 1) * B], Yt.detach().numpy(), rtol=1e-12,
+                                   atol=1e-13)
+        (Yt * torch.from_numpy(dY[t * B:(t + 1) * B].astype(np.float64))).sum().backward()
+        for k in range(3):
+            np.testing.assert_allclose(grads[t][k], G[k].grad.numpy(), rtol=1e-11, atol=1e-12)
+    w = rng.random(off[-1]).astype(np.float32)
+    Ys = oracle.forward(p, q, ranks, E, cores, idx, off, B, per_sample_weights=w)
+    Ym = oracle.forward(p, q, ranks, E, cores, idx, off, B, per_sample_weights=w, pooling=1)
+    L = np.maximum(lens, 1)[:, None]
+    np.testing.assert_allclose(Ym * L, Ys, rtol=1e-13, atol=1e-14)
