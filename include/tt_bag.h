@@ -78,7 +78,13 @@ typedef struct tt_desc {
     int32_t p[3];            /* tt_p_shapes                                    */
     int32_t q[3];            /* tt_q_shapes; embedding_dim D = q[0]*q[1]*q[2]  */
     int32_t ranks[2];        /* tt_ranks (R1, R2); full ranks {1, R1, R2, 1}   */
+    int32_t pooling;         /* TT_POOL_SUM (0) or TT_POOL_MEAN (1)            */
 } tt_desc;
+/* Pooling of a bag (PyTorch EmbeddingBag's modes "sum" and "mean"): the mean is the
+ * (weighted) sum divided by the bag's number of elements; an empty bag gives zeros.
+ * The backward scales each element's gradient by the same 1 / length. */
+#define TT_POOL_SUM  0
+#define TT_POOL_MEAN 1
 
 /* A view of the software cache for one forward/backward call ("Software Cache").
  * slots[n] >= 0 makes element n a hit: the forward reads rows[slots[n]] instead

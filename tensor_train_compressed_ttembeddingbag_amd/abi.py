@@ -24,6 +24,8 @@ TT_DEV_BAD_SLOT = 4
 TT_DEV_HASH_FULL = 8
 TT_DEV_STALE_PLAN = 16
 TT_DEV_SYNC_TIMEOUT = 32
+TT_POOL_SUM = 0
+TT_POOL_MEAN = 1
 TT_CACHE_TOPK = 0
 TT_CACHE_LFU32 = 1
 TT_INIT_UNIFORM = 0
@@ -41,7 +43,7 @@ class TTError(RuntimeError):
 class TTDesc(ctypes.Structure):
     _fields_ = [("num_tables", ctypes.c_int32), ("num_embeddings", ctypes.c_int64),
                 ("p", ctypes.c_int32 * 3), ("q", ctypes.c_int32 * 3),
-                ("ranks", ctypes.c_int32 * 2)]
+                ("ranks", ctypes.c_int32 * 2), ("pooling", ctypes.c_int32)]
 
 
 class TTCacheView(ctypes.Structure):
@@ -115,8 +117,10 @@ def status_string(code: int) -> str:
     return lib().tt_status_string(int(code)).decode()
 
 
-def make_desc(p, q, ranks, num_embeddings: Optional[int] = None, num_tables: int = 1) -> TTDesc:
+def make_desc(p, q, ranks, num_embeddings: Optional[int] = None, num_tables: int = 1,
+              pooling: int = 0) -> TTDesc:
     d = TTDesc()
+    d.pooling = int(pooling)
     d.num_tables = int(num_tables)
     d.num_embeddings = int(num_embeddings if num_embeddings is not None else p[0] * p[1] * p[2])
     for k in range(3):

@@ -66,6 +66,7 @@ int make_plan(const tt_desc *d, int64_t nnz, int64_t num_bags, int64_t cache_siz
   for (int k = 0; k < 3; ++k)
     if (d->p[k] < 1 || d->q[k] < 1) return TT_ESHAPE;
   if (d->ranks[0] < 1 || d->ranks[1] < 1 || d->ranks[0] > 64 || d->ranks[1] > 64) return TT_ESHAPE;
+  if (d->pooling != TT_POOL_SUM && d->pooling != TT_POOL_MEAN) return TT_EINVAL;
   if (!(d->q[0] == 1 || d->q[0] == 2 || d->q[0] == 4)) return TT_ESHAPE;
   if (d->q[2] > MAXQ3) return TT_ESHAPE;
   const int64_t D = (int64_t)d->q[0] * d->q[1] * d->q[2];
@@ -86,6 +87,7 @@ int make_plan(const tt_desc *d, int64_t nnz, int64_t num_bags, int64_t cache_siz
   DevArgs &a = P->a;
   memset(&a, 0, sizeof(a));
   a.T = T;
+  a.mean = d->pooling == TT_POOL_MEAN;
   a.p1 = d->p[0]; a.p2 = d->p[1]; a.p3 = d->p[2];
   a.q1 = d->q[0]; a.q2 = d->q[1]; a.q3 = d->q[2];
   a.R1 = d->ranks[0]; a.R2 = d->ranks[1];
@@ -239,6 +241,7 @@ static unsigned plan_fingerprint(const tt_desc *d, int64_t nnz, int64_t num_bags
   for (int k = 0; k < 3; ++k) { mix((uint64_t)d->p[k]); mix((uint64_t)d->q[k]); }
   mix((uint64_t)d->ranks[0]);
   mix((uint64_t)d->ranks[1]);
+  mix((uint64_t)d->pooling);
   mix((uint64_t)nnz);
   mix((uint64_t)num_bags);
   mix((uint64_t)cache_size);

@@ -53,6 +53,7 @@ struct DevArgs {
   int nnz, nblk;
   int binsA, binsB, binsI3;
   int has_cache;
+  int mean;         // mean pooling: element weights carry 1 / (bag length)
   int64_t cache_size;
   int NHB;
   int P;            // work item: positions per piece (8, 16 or 32; divides PIECE)

@@ -160,6 +160,19 @@ static __device__ void tile_decode(const DevArgs &a, int blk, int *s_off, int *s
 #pragma unroll
     for (int r = 0; r < RB / NT; ++r) bag[r] = find_bag(a.off, a.NB, min(tile_pos<NT>(blk, r), a.nnz - 1));
   }
+  if (a.mean) {  // mean pooling: the weight carries 1 / (bag length)
+#pragma unroll
+    for (int r = 0; r < RB / NT; ++r) {
+      int64_t len;
+      if (in_lds) {
+        const int k = min(bag[r] - b_lo, nbag - 1);
+        len = s_off[k + 1] - s_off[k];
+      } else {
+        len = a.off[bag[r] + 1] - a.off[bag[r]];
+      }
+      el[r].w = el[r].w / (float)(len > 0 ? len : 1);
+    }
+  }
   const int dropA = a.binsA - 1, dropB = a.binsB - 1, dropI = a.binsI3 - 1;
   const int64_t p23 = (int64_t)a.p2 * a.p3;
   bool bad_slot = false, bad_index = false;
@@ -606,6 +619,10 @@ __global__ __launch_bounds__(RT) void k_route_b(DevArgs a) {
     el[r].dI = v ? info.z : -1;
     el[r].bag = info.w;
     el[r].w = a.psw ? a.psw[ec] : 1.f;
+    if (a.mean && v) {  // mean pooling: the weight carries 1 / (bag length)
+      const int64_t len = a.off[info.w + 1] - a.off[info.w];
+      el[r].w = el[r].w / (float)(len > 0 ? len : 1);
+    }
   }
   int pA[4];
   tile_place_ia<RT>(a, el, pA, lds_c, a.histI3, a.histA, a.nblk, blk);
@@ -650,7 +667,8 @@ __global__ __launch_bounds__(RT) void k_yinit(DevArgs a) {
     for (int64_t n = lo; n < hi; ++n) {
       const int s = a.slots[n];
       if (s >= 0 && s < a.cache_size) {
-        const float wt = a.psw ? a.psw[n] : 1.f;
+        const float wt = a.mean ? (a.psw ? a.psw[n] : 1.f) / (float)(hi - lo)
+                                : (a.psw ? a.psw[n] : 1.f);
         acc += wt * a.crows[(size_t)s * a.D + d];
       }
     }
