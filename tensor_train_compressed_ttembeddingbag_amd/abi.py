@@ -78,6 +78,7 @@ _SIG = {
                                     _P, _P]),
     "tt_init_cores": (ctypes.c_int, [_P, _P, ctypes.c_int, ctypes.c_float, ctypes.c_uint64, _P]),
     "tt_factorize": (ctypes.c_int, [_I64, ctypes.c_int, _P]),
+    "tt_full_weight": (ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _I64, _P, _P]),
     "tt_cache_create": (ctypes.c_int, [_P, _P, _I64, _I64]),
     "tt_cache_create_policy": (ctypes.c_int, [_P, _P, _I64, _I64, ctypes.c_int]),
     "tt_cache_export": (ctypes.c_int, [_P, _P, _P, _P, _P]),
@@ -335,6 +336,19 @@ def tt_init_cores(desc: TTDesc, cores, dist: int, scale: float, seed: int, strea
     _check("tt_init_cores", lib().tt_init_cores(ctypes.byref(desc), _cores(cores), int(dist),
                                                 float(scale), int(seed) & ((1 << 64) - 1),
                                                 _stream(stream)))
+
+
+def tt_full_weight(desc: TTDesc, cores, first: int, count: int, table: int = 0, out=None,
+                   stream=None) -> torch.Tensor:
+    """Rows [first, first + count) of one table as a dense [count, D] tensor."""
+    D = desc.q[0] * desc.q[1] * desc.q[2]
+    if out is None:
+        out = torch.empty(int(count), D, dtype=torch.float32, device=cores[0].device)
+    _need(out, torch.float32, "out")
+    _check("tt_full_weight", lib().tt_full_weight(ctypes.byref(desc), _cores(cores), int(table),
+                                                  int(first), int(count), _ptr(out),
+                                                  _stream(stream)))
+    return out
 
 
 def tt_factorize(n: int, exact: bool):

@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libttbag.so")
-SOURCES = ["tt_route.hip", "tt_fwd.hip", "tt_bwd.hip", "tt_cache.hip", "tt_init.hip", "tt_prof.hip",
+SOURCES = ["tt_route.hip", "tt_fwd.hip", "tt_bwd.hip", "tt_cache.hip", "tt_init.hip", "tt_full.hip",
+           "tt_prof.hip",
            "tt_api.hip"]
 ARCH = "gfx950"
 
