@@ -248,6 +248,20 @@ def main():
     init_us = ev0.elapsed_time(ev1) * 1e3 / 20
     nel = sum(x.numel() for x in g)
     res["config"]["init_cores_us"] = round(init_us, 2)
+    # full-weight expansion of (up to) 1,000,000 rows of table 0, off the training path
+    nrow = min(1_000_000, wl.E)
+    dense = torch.empty(nrow, wl.D, device="cuda")
+    abi.tt_full_weight(desc, g, 0, nrow, out=dense)
+    ev0.record()
+    for r in range(5):
+        abi.tt_full_weight(desc, g, 0, nrow, out=dense)
+    ev1.record()
+    torch.cuda.synchronize()
+    full_us = ev0.elapsed_time(ev1) * 1e3 / 5
+    res["config"]["full_weight_rows"] = nrow
+    res["config"]["full_weight_us"] = round(full_us, 1)
+    res["config"]["full_weight_gbs"] = round(nrow * wl.D * 4 / (full_us * 1e-6) / 1e9, 1)
+    del dense
     res["config"]["init_cores_gbs"] = round(nel * 4 / (init_us * 1e-6) / 1e9, 1)
     if cache is not None:
         res["config"]["cache_rows_filled"] = n_filled

@@ -343,8 +343,9 @@ int tt_factorize(int64_t n, int exact, int32_t out[3]);
 /* ---------------------------------------------------------------- full weight
  * Rows first .. first+count-1 of table `table` decompressed ("Initialization": a row is
  * the chain G1[i1] G2[i2] G3[i3]) into out [count][D] fp32 (device, fully overwritten),
- * on `stream`.  first + count <= num_embeddings.  TT_ESHAPE when T = G1[i1] G2[i2], a G2
- * slice, a G1 slice and one G3 slice do not fit the 160 KiB of LDS together. */
+ * on `stream`.  first + count <= num_embeddings.  TT_ESHAPE when q3 > 16 or when
+ * T = G1[i1] G2[i2], a G2 slice, a G1 slice and one G3 slice do not fit the 160 KiB of
+ * LDS together. */
 int tt_full_weight(const tt_desc *desc, const float *const cores[3], int table, int64_t first,
                    int64_t count, float *out, void *stream);
 
