@@ -47,7 +47,7 @@ struct Plan {
   size_t lds_fwd = 0, lds_bwd = 0;
   size_t ws_total = 0;
   // byte offsets inside the workspace
-  size_t o_ctr, o_flag, o_hdr, o_einfo, o_histA, o_histB, o_histI3, o_rec, o_segI3, o_segA, o_srec,
+  size_t o_ctr, o_flag, o_fflag, o_hdr, o_einfo, o_histA, o_histB, o_histI3, o_rec, o_segI3, o_segA, o_srec,
       o_fitem, o_grp, o_chunk,
       o_l1, o_l3, o_p1, o_p3, o_frag, o_p2;
 };
@@ -133,6 +133,7 @@ int make_plan(const tt_desc *d, int64_t nnz, int64_t num_bags, int64_t cache_siz
   size_t cur = 0;
   P->o_ctr = carve(cur, 3 * sizeof(unsigned long long));
   P->o_flag = carve(cur, COOP_TILES * sizeof(unsigned long long));
+  P->o_fflag = carve(cur, FWD_ZERO_BLOCKS * sizeof(unsigned long long));
   P->o_hdr = carve(cur, H_WORDS * sizeof(int));
   P->o_einfo = carve(cur, n * sizeof(int4));
   P->o_histA = carve(cur, (size_t)binsA * nb * 4);
@@ -160,6 +161,7 @@ void bind_ws(Plan *P, void *ws) {
   DevArgs &a = P->a;
   a.ctr = (unsigned long long *)(b + P->o_ctr);
   a.flag = (unsigned long long *)(b + P->o_flag);
+  a.fflag = (unsigned long long *)(b + P->o_fflag);
   a.hdr = (int *)(b + P->o_hdr);
   a.einfo = (int4 *)(b + P->o_einfo);
   a.histA = (int *)(b + P->o_histA);
@@ -302,7 +304,9 @@ int tt_bag_forward_planned(const tt_desc *desc, const float *const cores[3],
   a.G1 = (float *)cores[0]; a.G2 = (float *)cores[1]; a.G3 = (float *)cores[2];
   a.Y = out;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_yinit(a, s);
+  // without a cache the forward kernel clears out itself; with one, k_yinit pools the hits
+  a.fzero = !a.has_cache && a.nnz > 0;
+  hipError_t e = a.fzero ? hipSuccess : launch_yinit(a, s);
   if (e == hipSuccess && a.nnz > 0) e = launch_fwd(a, P.RP, P.lds_fwd, s);
   return finish(e);
 }

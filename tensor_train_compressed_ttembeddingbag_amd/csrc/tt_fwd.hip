@@ -15,8 +15,9 @@
 //   2. the item's elements and its G2 slice (the first JB column blocks),
 //   3. the G1 rows of its distinct (i1, i2) pairs and the G3 slices of its
 //      distinct indices,
-// after which everything runs out of LDS and registers.  Stage 1 runs once per
-// pair as a GEMM on the fp32 matrix cores,
+// after which everything runs out of LDS and registers.  Without a cache the first
+// workgroups also clear out (fwd_clear_out), so no separate kernel runs before.
+// Stage 1 runs once per pair as a GEMM on the fp32 matrix cores,
 //     T^T[r2][(pair, j1)] = sum_r1 G2[r1][j2][r2] * G1[i1(pair)][j1][r1],
 // with 16 (pair, j1) rows per "M-block" in the MFMA column dimension and G2^T
 // read from LDS as 16-byte vectors.  Stage 2 runs once per distinct index in VALU
@@ -40,6 +41,49 @@ struct FwdLds {
     return (g2_floats(JB) + g3_floats(P, q3) + w_floats(P, D, sw)) * 4 + INTS * 4;
   }
 };
+
+// Clearing of out by the forward itself (no cache): blocks 0 .. nz-1 clear a slice each
+// with device-coherent stores and then raise their flag (this call's epoch); every block
+// checks all flags before its first atomic into out.  The clearing blocks are dispatched
+// before any block that waits and never wait themselves before raising the flag.
+__device__ __forceinline__ int fwd_zero_blocks(const DevArgs &a) {
+  return min(FWD_ZERO_BLOCKS, (int)gridDim.x);
+}
+static __device__ void fwd_clear_out(const DevArgs &a) {
+  const long long n = (long long)a.NB * a.D, nz = fwd_zero_blocks(a);
+  const long long chunk = (n + nz - 1) / nz, lo = blockIdx.x * chunk, hi = min(n, lo + chunk);
+  for (long long i = lo + threadIdx.x; i < hi; i += WG)
+    __hip_atomic_store(a.Y + i, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+static __device__ void fwd_raise_flag(const DevArgs &a) {  // whole block
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's clearing stores are done
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&a.fflag[blockIdx.x], (unsigned long long)a.epoch, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+static __device__ void fwd_wait_out(const DevArgs &a) {  // whole block
+  __shared__ int s_ok;
+  if (threadIdx.x < 64) {
+    const int nz = fwd_zero_blocks(a), lane = threadIdx.x;
+    int ok = 1;
+    for (unsigned polls = 0;; ++polls) {
+      const unsigned long long v = lane < nz
+          ? __hip_atomic_load(&a.fflag[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+          : (unsigned long long)a.epoch;
+      if (__ballot(v != (unsigned long long)a.epoch) == 0ull) break;
+      if (polls >= (1u << 22)) {
+        ok = 0;
+        if (lane == 0) set_status(a.status, TT_DEV_SYNC_TIMEOUT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (lane == 0) s_ok = ok;
+  }
+  __syncthreads();
+  (void)s_ok;
+}
 
 template <int RP>
 __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
@@ -66,10 +110,16 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int wi = blockIdx.x;
-  // round 1: plan check and work item
+  const bool clearer = a.fzero && wi < fwd_zero_blocks(a);
+  // round 1: plan check and work item (a stale plan leaves out untouched)
   const int plan = a.hdr[H_PLAN], nitems = a.hdr[H_NFWD];
   const int4 item = a.fitem[wi];
-  if (plan != (int)a.plan_fp || wi >= nitems) return;
+  const bool stale = plan != (int)a.plan_fp;
+  if (clearer && !stale) fwd_clear_out(a);
+  if (stale || wi >= nitems) {
+    if (clearer) fwd_raise_flag(a);
+    return;
+  }
   const int grp = item.x, s0 = item.y, s1 = item.z;
   const int n_el = s1 - s0;
   const int t = grp / a.p2;
@@ -143,7 +193,8 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
   }
   store2(nj0, tid, v2);
   stage_g2(0, nj0, tid + WG * STAGE_U);
-  __syncthreads();
+  if (clearer) fwd_raise_flag(a);  // (includes the barrier)
+  else __syncthreads();
   const int nI = s_cnt[0], nP = s_cnt[1];
   const int nmb = (nP * q1 + 15) >> 4;
 
@@ -196,6 +247,7 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
   }
   __syncthreads();
 
+  if (a.fzero && !SW) fwd_wait_out(a);  // stage 2 adds into out directly
   for (int j0 = 0; j0 < q2; j0 += JB) {
     if (j0 > 0) {  // next G2 stage (only when the slice does not fit at once)
       __syncthreads();
@@ -269,7 +321,8 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
   }
   if (!SW) return;
   // pooling: out[bag] += w * W[item], one row-contiguous pass per element
-  __syncthreads();
+  if (a.fzero) fwd_wait_out(a);  // (includes the barrier)
+  else __syncthreads();
   for (int e = w; e < n_el; e += NW) {
     const int it = e_it[e];
     float *yrow = a.Y + (size_t)e_bag[e] * D;

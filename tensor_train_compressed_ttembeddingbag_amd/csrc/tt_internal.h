@@ -33,6 +33,7 @@ constexpr int P_MAX = 32;       // positions per work item: P * q1 <= 16 * NW ro
 constexpr int MAXQ3 = 16;
 constexpr int STAGE_U = 8;      // global loads in flight per thread when staging into LDS
 constexpr int COOP_TILES = 256; // blocks of the one-launch grouping kernel (one per CU)
+constexpr int FWD_ZERO_BLOCKS = 64;  // forward blocks that clear out when it does
 constexpr int COOP_CELLS = 65536;  // its bins x tiles per digit (each block reads them all)
 constexpr int COOP_LDS_CELLS = 12288;  // (t,i2) x tile counts gathered in LDS up to this size
 
@@ -82,6 +83,8 @@ struct DevArgs {
   // workspace
   unsigned long long *ctr;  // [3] epoch-tagged completion counters (no zeroing needed)
   unsigned long long *flag;  // [COOP_TILES] grid-barrier arrival words (epoch << 32 | k)
+  unsigned long long *fflag; // [FWD_ZERO_BLOCKS] forward: "my slice of out is cleared" words
+  int fzero;                 // forward: its first blocks clear out (no separate kernel)
   unsigned epoch;           // unique per call
   int *hdr;
   int4 *einfo;      // per element: dA (t,i1), dB (t,i2), dI3 (t,i3), bag
