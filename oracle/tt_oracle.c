@@ -177,7 +177,9 @@ int oracle_forward(const oracle_shape *s, const float *const *cores,
 }
 
 /*
- * Backward.  dY is [T*B][D] fp32.  grad[3t+k] are double buffers in the logical
+ * Backward.  dY is [T*B][D] fp32.  grad_w (may be NULL) receives dL/dw_n for every
+ * element, the gradient with respect to its per-sample weight: <dY[bag], row_n>, times
+ * 1/len with mean pooling (row_n from cache_rows for a hit).  grad[3t+k] are double buffers in the logical
  * layout of core k of table t, fully overwritten.  touched[3t+k] (may be NULL)
  * are byte arrays of length p_k set to 1 for every slice i_k that received a
  * contribution.  grad_cache ([cache_size][D], may be NULL when slot is NULL) and
@@ -187,7 +189,8 @@ int oracle_backward(const oracle_shape *s, const float *const *cores,
                     const int64_t *idx, int64_t nnz, const int64_t *off, int64_t B,
                     const float *psw, const int32_t *slot, int64_t cache_size,
                     const float *dY, double *const *grad, uint8_t *const *touched,
-                    double *grad_cache, uint8_t *touched_cache)
+                    double *grad_cache, uint8_t *touched_cache, double *grad_w,
+                    const float *cache_rows)
 {
     const int64_t T = s->num_tables, D = prod3(s->q), NB = T * B;
     if (check_inputs(s, idx, nnz, off, NB, slot, cache_size)) return -1;
@@ -212,10 +215,25 @@ int oracle_backward(const oracle_shape *s, const float *const *cores,
                 for (int64_t j = 0; j < D; ++j)
                     grad_cache[slot[n] * D + j] += w * (double)dY[b * D + j];
                 if (touched_cache) touched_cache[slot[n]] = 1;
+                if (grad_w) {
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < D; ++j)
+                        acc += (double)dY[b * D + j] * (double)cache_rows[slot[n] * D + j];
+                    grad_w[n] = acc * inv;
+                }
                 continue;
             }
             int64_t ii[3];
             oracle_split_index(s->p, idx[n], ii);
+            if (grad_w) {
+                /* dL/dw_n = <dY[b], W[idx_n]> (times 1/len with mean pooling) */
+                double *row = (double *)malloc(sizeof(double) * D);
+                oracle_tt_row(s, G1, G2, G3, idx[n], row);
+                double acc = 0.0;
+                for (int64_t j = 0; j < D; ++j) acc += (double)dY[b * D + j] * row[j];
+                grad_w[n] = acc * inv;
+                free(row);
+            }
             if (touched)
                 for (int k = 0; k < 3; ++k) touched[3 * t + k][ii[k]] = 1;
             for (int64_t j1 = 0; j1 < q[0]; ++j1)

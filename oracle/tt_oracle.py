@@ -69,7 +69,7 @@ def _L():
                                        ctypes.c_int64, P]
         lib.oracle_forward.restype = ctypes.c_int
         lib.oracle_backward.argtypes = [P, P, P, ctypes.c_int64, P, ctypes.c_int64, P, P,
-                                        ctypes.c_int64, P, P, P, P, P]
+                                        ctypes.c_int64, P, P, P, P, P, P, P]
         lib.oracle_backward.restype = ctypes.c_int
         lib.oracle_sgd_core.argtypes = [P, ctypes.c_int, P, P, P, ctypes.c_double]
         lib.oracle_sgd_rows.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_double]
@@ -143,12 +143,13 @@ def forward(p, q, ranks, E, cores, indices, offsets, num_bags, per_sample_weight
 
 
 def backward(p, q, ranks, E, cores, indices, offsets, num_bags, grad_out,
-             per_sample_weights=None, slots=None, cache_size=0, pooling=0):
+             per_sample_weights=None, slots=None, cache_size=0, pooling=0, cache_rows=None,
+             weight_grad=False):
     """Gradients of L = sum_b <dY[b], Y[b]>.
 
     Returns (grads, touched, grad_cache, touched_cache): grads is a list of T lists
     of float64 arrays in the logical core layout, touched a list of T lists of
-    uint8 masks over the slices p_k."""
+    uint8 masks over the slices p_k.  weight_grad=True appends dL/dw per element."""
     T = len(cores)
     flat = [_f32(c) for tbl in cores for c in tbl]
     s = _shape(p, q, ranks, E, T, pooling)
@@ -162,13 +163,19 @@ def backward(p, q, ranks, E, cores, indices, offsets, num_bags, grad_out,
     D = int(np.prod(q))
     gc = np.zeros((cache_size, D), dtype=np.float64) if sl is not None else None
     tc = np.zeros(cache_size, dtype=np.uint8) if sl is not None else None
+    gw = np.zeros(len(idx), dtype=np.float64) if weight_grad else None
+    cr = None if cache_rows is None else _f32(cache_rows)
+    if weight_grad and sl is not None and cr is None:
+        raise ValueError("the weight gradient of cache hits needs the cache rows")
     rc = _L().oracle_backward(ctypes.byref(s), _ptr_array(flat), _ptr(idx), len(idx), _ptr(off),
                               int(num_bags), _ptr(psw), _ptr(sl), int(cache_size), _ptr(dY),
                               _ptr_array([g for tbl in grads for g in tbl]),
                               _ptr_array([m for tbl in touched for m in tbl]),
-                              _ptr(gc), _ptr(tc))
+                              _ptr(gc), _ptr(tc), _ptr(gw), _ptr(cr))
     if rc != 0:
         raise ValueError("oracle_backward: invalid input")
+    if weight_grad:
+        return grads, touched, gc, tc, gw
     return grads, touched, gc, tc
 
 

@@ -512,6 +512,8 @@ _MUTANTS = [
     # mean pooling: the backward without the 1 / length
     ("const double w = (psw ? (double)psw[n] : 1.0) * inv;",
      "const double w = (psw ? (double)psw[n] : 1.0);"),
+    # weight gradient: the mean pooling's 1 / length dropped
+    ("grad_w[n] = acc * inv;\n                free(row);", "grad_w[n] = acc;\n                free(row);"),
     # Adagrad on cache rows: the squared gradient not added
     ("state[e] = (float)((double)state[e] + g * g);\n            rows[e]",
      "state[e] = (float)((double)state[e] + g);\n            rows[e]"),
@@ -545,7 +547,8 @@ def test_pins_catch_planted_mistakes(mi, tmp_path, monkeypatch):
             test_pooling_invariants, test_backward_equals_exact_finite_differences,
             test_backward_matches_torch_autograd, test_sgd_step_invariants,
             test_adagrad_matches_torch_optim_adagrad, test_adagrad_first_step_closed_form,
-            test_mean_pooling_matches_torch_embedding_bag]
+            test_mean_pooling_matches_torch_embedding_bag,
+            test_weight_gradient_matches_torch_and_exact_differences]
     try:
         for f in pins:
             try:
@@ -698,3 +701,48 @@ def test_mean_pooling_matches_torch_embedding_bag():
     Ym = oracle.forward(p, q, ranks, E, cores, idx, off, B, per_sample_weights=w, pooling=1)
     L = np.maximum(lens, 1)[:, None]
     np.testing.assert_allclose(Ym * L, Ys, rtol=1e-13, atol=1e-14)
+
+
+# --------------------------------------------------------------- per-sample-weight gradients
+
+def test_weight_gradient_matches_torch_and_exact_differences():
+    """dL/dw per element: against torch's autograd of EmbeddingBag (sum mode, weights
+    with requires_grad) on the dense rebuild, and against exact secant differences
+    (L is affine in each weight), in sum and mean pooling and for cache hits."""
+    rng = _rng(51)
+    p, q, ranks, E, B = (4, 3, 2), (2, 2, 3), (3, 4), 23, 5
+    cores = [_rand_cores(rng, p, q, ranks)]
+    lens = np.array([2, 5, 0, 4, 3])
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    idx = rng.integers(0, E, off[-1]).astype(np.int64)
+    w = rng.random(off[-1]).astype(np.float32)
+    dY = rng.standard_normal((B, 12)).astype(np.float32)
+    gw = oracle.backward(p, q, ranks, E, cores, idx, off, B, dY, per_sample_weights=w,
+                         weight_grad=True)[4]
+    G = [torch.tensor(c.astype(np.float64)) for c in cores[0]]
+    Wt = torch.einsum("aipr,rjqs,skvb->ijkpqv", *G).reshape(int(np.prod(p)), 12)[:E]
+    wt = torch.tensor(w.astype(np.float64), requires_grad=True)
+    Y = torch.nn.functional.embedding_bag(torch.from_numpy(idx), Wt, torch.from_numpy(off[:-1]),
+                                          mode="sum", per_sample_weights=wt)
+    (Y * torch.from_numpy(dY.astype(np.float64))).sum().backward()
+    np.testing.assert_allclose(gw, wt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    # secant differences, mean pooling, with two elements served by a cache
+    slots = np.full(len(idx), -1, dtype=np.int32)
+    slots[[1, 6]] = [0, 1]
+    rows = np.stack([oracle.tt_row(p, q, ranks, cores[0], int(idx[1])),
+                     oracle.tt_row(p, q, ranks, cores[0], int(idx[6])) + 0.25]).astype(np.float32)
+    for pooling in (0, 1):
+        gw = oracle.backward(p, q, ranks, E, cores, idx, off, B, dY, per_sample_weights=w,
+                             slots=slots, cache_size=2, pooling=pooling, cache_rows=rows,
+                             weight_grad=True)[4]
+        L0 = float(np.sum(dY.astype(np.float64) * oracle.forward(
+            p, q, ranks, E, cores, idx, off, B, per_sample_weights=w, slots=slots,
+            cache_rows=rows, pooling=pooling)))
+        for n in range(len(idx)):
+            w2 = w.copy()
+            w2[n] += 0.5
+            L1 = float(np.sum(dY.astype(np.float64) * oracle.forward(
+                p, q, ranks, E, cores, idx, off, B, per_sample_weights=w2, slots=slots,
+                cache_rows=rows, pooling=pooling)))
+            h = float(w2[n]) - float(w[n])  # the fp32 weights' actual step
+            assert abs((L1 - L0) / h - gw[n]) < 1e-9 * (1 + abs(gw[n])), (pooling, n)
