@@ -224,6 +224,29 @@ int tt_bag_backward_grad_planned(const tt_desc *desc, const float *const cores[3
                                  void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
 
 /*
+ * Gradient with respect to the per-sample weights (the survey's N4 variant; PyTorch's
+ * EmbeddingBag returns it when the weights require a gradient): for every element n,
+ *     grad_weights[n] = <grad_out[bag n], W[indices[n]]>   (times 1 / bag length with
+ *                                                         mean pooling),
+ * the row being the cache row for a hit; skipped elements get 0.  Cores and rows are
+ * only read.  grad_weights [nnz] fp32, fully overwritten.  TT_ESHAPE when a work
+ * item's rows (32 x D floats) do not fit the forward kernel's LDS (D > 512).  Bit-
+ * reproducible run to run.
+ */
+int tt_bag_weight_grad(const tt_desc *desc, const float *const cores[3],
+                       const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                       int64_t num_bags, const float *per_sample_weights,
+                       const tt_cache_view *cache, const float *grad_out, float *grad_weights,
+                       void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
+
+int tt_bag_weight_grad_planned(const tt_desc *desc, const float *const cores[3],
+                               const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                               int64_t num_bags, const float *per_sample_weights,
+                               const tt_cache_view *cache, const float *grad_out,
+                               float *grad_weights, void *ws, size_t ws_bytes,
+                               int32_t *dev_status, void *stream);
+
+/*
  * The grouping step of both passes, exposed for inspection and tests: splits
  * every index, finds its bag, and sorts the elements stably so that misses come
  * first ordered by (table, i2, i1) and then by position, followed by cache hits

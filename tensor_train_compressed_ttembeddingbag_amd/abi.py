@@ -74,6 +74,10 @@ _SIG = {
                                             ctypes.c_size_t, _P, _P]),
     "tt_bag_backward_grad_planned": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P, _P,
                                                     _P, _P, ctypes.c_size_t, _P, _P]),
+    "tt_bag_weight_grad": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P, _P, _P,
+                                          ctypes.c_size_t, _P, _P]),
+    "tt_bag_weight_grad_planned": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P, _P,
+                                                  _P, ctypes.c_size_t, _P, _P]),
     "tt_bag_route": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _I64, _P, _P, _P, ctypes.c_size_t,
                                     _P, _P]),
     "tt_init_cores": (ctypes.c_int, [_P, _P, ctypes.c_int, ctypes.c_float, ctypes.c_uint64, _P]),
@@ -329,6 +333,24 @@ def tt_bag_backward_grad(desc: TTDesc, cores, indices, offsets, num_bags: int, g
                               _ptr(dev_status), _stream(stream))
     _check(name, rc)
     return grad_cores, gr
+
+
+def tt_bag_weight_grad(desc: TTDesc, cores, indices, offsets, num_bags: int, grad_out,
+                       per_sample_weights=None, cache=None, out=None, ws=None, dev_status=None,
+                       stream=None, planned: bool = False) -> torch.Tensor:
+    """dL/dw per element (see tt_bag.h); returns out [nnz] fp32."""
+    view, csize, ws = _batch_args(desc, indices, offsets, num_bags, grad_out, per_sample_weights,
+                                  cache, ws, dev_status)
+    if out is None:
+        out = torch.empty(indices.numel(), dtype=torch.float32, device=indices.device)
+    _need(out, torch.float32, "out")
+    name = "tt_bag_weight_grad_planned" if planned else "tt_bag_weight_grad"
+    rc = getattr(lib(), name)(ctypes.byref(desc), _cores(cores), _ptr(indices), indices.numel(),
+                              _ptr(offsets), int(num_bags), _ptr(per_sample_weights),
+                              None if view is None else ctypes.byref(view), _ptr(grad_out),
+                              _ptr(out), _ptr(ws), ws.numel(), _ptr(dev_status), _stream(stream))
+    _check(name, rc)
+    return out
 
 
 def tt_init_cores(desc: TTDesc, cores, dist: int, scale: float, seed: int, stream=None) -> None:

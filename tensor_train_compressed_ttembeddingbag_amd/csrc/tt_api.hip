@@ -458,6 +458,50 @@ int tt_bag_backward_grad(const tt_desc *desc, const float *const cores[3],
                        true);
 }
 
+static int weight_grad_call(const tt_desc *desc, const float *const cores[3],
+                            const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                            int64_t num_bags, const float *psw, const tt_cache_view *cache,
+                            const float *grad_out, float *grad_w, void *ws, size_t ws_bytes,
+                            int32_t *dev_status, void *stream, bool plan_first) {
+  Plan P;
+  int rc = prepare(&P, desc, indices, nnz, offsets, num_bags, psw, cache, ws, ws_bytes,
+                   dev_status);
+  if (rc) return rc;
+  if ((rc = check_cores(cores)) || !grad_out || (nnz > 0 && !grad_w)) return rc ? rc : TT_EINVAL;
+  DevArgs &a = P.a;
+  if (!a.fwd_sw) return TT_ESHAPE;  // the rows of a work item must fit the forward's LDS
+  if (nnz == 0) return TT_OK;
+  a.psw = psw;
+  a.G1 = (float *)cores[0]; a.G2 = (float *)cores[1]; a.G3 = (float *)cores[2];
+  a.dY = grad_out;
+  a.gw = grad_w;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_zero(grad_w, (size_t)nnz, s);  // skipped elements keep 0
+  if (e == hipSuccess && plan_first) e = launch_route(a, s);
+  if (e == hipSuccess) e = launch_wgrad(a, P.RP, P.lds_fwd, s);
+  if (e == hipSuccess) e = launch_wgrad_hits(a, s);
+  return finish(e);
+}
+
+int tt_bag_weight_grad(const tt_desc *desc, const float *const cores[3], const int64_t *indices,
+                       int64_t nnz, const int64_t *offsets, int64_t num_bags,
+                       const float *per_sample_weights, const tt_cache_view *cache,
+                       const float *grad_out, float *grad_weights, void *ws, size_t ws_bytes,
+                       int32_t *dev_status, void *stream) {
+  return weight_grad_call(desc, cores, indices, nnz, offsets, num_bags, per_sample_weights, cache,
+                          grad_out, grad_weights, ws, ws_bytes, dev_status, stream, true);
+}
+
+int tt_bag_weight_grad_planned(const tt_desc *desc, const float *const cores[3],
+                               const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                               int64_t num_bags, const float *per_sample_weights,
+                               const tt_cache_view *cache, const float *grad_out,
+                               float *grad_weights, void *ws, size_t ws_bytes,
+                               int32_t *dev_status, void *stream) {
+  return weight_grad_call(desc, cores, indices, nnz, offsets, num_bags, per_sample_weights, cache,
+                          grad_out, grad_weights, ws, ws_bytes, dev_status, stream, false);
+}
+
 // copies the grouping order: valid elements first (see tt_bag.h)
 __global__ void k_copy_route(const int4 *srec, int nnz, const int *grp_off, int G, int binsB,
                              int *order_out, int *group_off_out) {

@@ -33,7 +33,7 @@ namespace ttb {
 template <int RP>
 struct FwdLds {
   static constexpr int LD = RP + 4;  // row pitch of G2^T [r2][r1]: conflict-free 16-byte reads
-  static constexpr int INTS = 64 * 5 + 65 * 2 + 64 + 16 + 8;
+  static constexpr int INTS = 64 * 6 + 65 * 2 + 64 + 16 + 8;
   __host__ __device__ static size_t g2_floats(int JB) { return (size_t)JB * RP * LD; }
   __host__ __device__ static size_t g3_floats(int P, int q3) { return (size_t)P * q3 * RP; }
   __host__ __device__ static size_t w_floats(int P, int D, int sw) { return sw ? (size_t)P * D : 0; }
@@ -85,7 +85,9 @@ static __device__ void fwd_wait_out(const DevArgs &a) {  // whole block
   (void)s_ok;
 }
 
-template <int RP>
+// DOT: instead of pooling, the gradient with respect to each element's per-sample weight,
+// dL/dw_n = <grad_out[bag n], row n> (times 1 / bag length with mean pooling); rows in LDS.
+template <int RP, bool DOT>
 __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
   constexpr int KS = RP / 4;   // k-steps: lane group g covers r1 = g*KS + ks
   constexpr int NM = RP / 16;  // 16-row blocks of r2
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
   extern __shared__ float4 smem4[];
   float *smem = (float *)smem4;
   const int q1 = a.q1, q2 = a.q2, q3 = a.q3, R1 = a.R1, R2 = a.R2, D = a.D;
-  const int JB = a.JBf, P = a.P, SW = a.fwd_sw;
+  const int JB = a.JBf, P = a.P, SW = DOT ? 1 : a.fwd_sw;
   float *sG2 = smem;                                            // [JB][r2 < RP][LD]
   float *sG3 = sG2 + FwdLds<RP>::g2_floats(JB);                 // [item][j3][r2 < RP]
   float *sW = sG3 + FwdLds<RP>::g3_floats(P, q3);               // [item][D]
@@ -107,6 +109,7 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
   int *mb_nk = pr_i1 + 64;                                      // [16]
   int *s_cnt = mb_nk + 16;                                      // [8]
   int *e_perm = s_cnt + 8;                                      // [64] item-major elements
+  int *e_n = e_perm + 64;                                       // [64] element positions
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int wi = blockIdx.x;
@@ -172,6 +175,7 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
     const int dA = v ? dAv : -1, i3 = v ? dIv - t * a.p3 : 0;
     e_bag[tid] = bagv;
     e_w[tid] = wv;
+    e_n[tid] = sp.n;
     const WaveItems r = wave_items(v, dA, i3, nbits_for(a.p3));
     e_it[tid] = r.e_it;
     if (v) e_perm[r.item_pos] = tid;
@@ -319,6 +323,25 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
       }
     }
   }
+  if (DOT) {  // dL/dw per element: one wave per element, row . grad_out[bag]
+    __syncthreads();
+    for (int e = w; e < n_el; e += NW) {
+      const int it = e_it[e], b = e_bag[e];
+      float acc = 0.f;
+      for (int d = lane; d < D; d += 64) acc += sW[(size_t)it * D + d] * a.dY[(size_t)b * D + d];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+      if (lane == 0) {
+        float scale = 1.f;
+        if (a.mean) {
+          const long long len = a.off[b + 1] - a.off[b];
+          scale = 1.f / (float)(len > 0 ? len : 1);
+        }
+        a.gw[e_n[e]] = acc * scale;
+      }
+    }
+    return;
+  }
   if (!SW) return;
   // pooling: out[bag] += w * W[item], one row-contiguous pass per element
   if (a.fzero) fwd_wait_out(a);  // (includes the barrier)
@@ -343,13 +366,33 @@ template <int RP>
 static hipError_t launch_fwd_t(const DevArgs &a, size_t lds, hipStream_t s) {
   static bool attr_set = false;  // dynamic LDS above 64 KiB is opt-in per kernel
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void *)k_fwd<RP>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              160 * 1024);
+    (void)hipFuncSetAttribute((const void *)k_fwd<RP, false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr_set = true;
   }
   const int grid = items_max(a);
-  tt_launch(K_FWD, k_fwd<RP>, dim3(grid), dim3(WG), lds, s, a);
+  tt_launch(K_FWD, k_fwd<RP, false>, dim3(grid), dim3(WG), lds, s, a);
   return hipGetLastError();
+}
+
+template <int RP>
+static hipError_t launch_wgrad_t(const DevArgs &a, size_t lds, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute((const void *)k_fwd<RP, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    attr_set = true;
+  }
+  tt_launch(K_FWD, k_fwd<RP, true>, dim3(items_max(a)), dim3(WG), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad(const DevArgs &a, int RP, size_t lds, hipStream_t s) {
+  switch (RP) {
+    case 16: return launch_wgrad_t<16>(a, lds, s);
+    case 32: return launch_wgrad_t<32>(a, lds, s);
+    default: return launch_wgrad_t<64>(a, lds, s);
+  }
 }
 
 hipError_t launch_fwd(const DevArgs &a, int RP, size_t lds, hipStream_t s) {

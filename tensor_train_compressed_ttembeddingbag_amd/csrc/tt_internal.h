@@ -77,6 +77,7 @@ struct DevArgs {
   float lr;
   int upd;          // UPD_SGD, UPD_ADAGRAD or UPD_GRAD: what the backward does with a gradient
   float eps;        // Adagrad: added to the root of the running sum
+  float *gw;        // gradient with respect to the per-sample weights [nnz] (or null)
   float *X1, *X2, *X3, *Xc;  // per core / cache rows, in their layout: Adagrad running
                              // sums (UPD_ADAGRAD) or the gradient outputs (UPD_GRAD)
   int32_t *status;
@@ -180,6 +181,9 @@ hipError_t launch_yinit(const DevArgs &a, hipStream_t s);
 hipError_t launch_seg(const DevArgs &a, hipStream_t s);
 hipError_t launch_zero(float *x, size_t n, hipStream_t s);  // x[0 .. n) = 0
 hipError_t launch_fwd(const DevArgs &a, int RP, size_t lds, hipStream_t s);
+// dL/dw of the misses (the forward's rows dotted with grad_out, needs fwd_sw) / of the hits
+hipError_t launch_wgrad(const DevArgs &a, int RP, size_t lds, hipStream_t s);
+hipError_t launch_wgrad_hits(const DevArgs &a, hipStream_t s);
 hipError_t launch_bwd(const DevArgs &a, int RP, size_t lds, hipStream_t s);
 size_t fwd_lds_bytes(int RP, int JB, int P, int q3, int D, int sw);
 size_t bwd_lds_bytes(int RP, int JB, int P, int q3, int D, int nred);

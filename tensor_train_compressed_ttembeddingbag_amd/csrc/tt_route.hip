@@ -723,6 +723,43 @@ __global__ __launch_bounds__(RT) void k_runsum(DevArgs a) {
   }
 }
 
+// dL/dw of the cache hits: one thread per position of the hit region,
+// <cache row, grad_out[bag]> (times 1 / bag length with mean pooling), 8 loads in flight.
+__global__ __launch_bounds__(256) void k_wgrad_hits(DevArgs a) {
+  const int hb = a.hdr[H_HIT_BEG], he = a.hdr[H_HIT_END];
+  if (a.hdr[H_PLAN] != (int)a.plan_fp) return;  // stale plan: the caller's status shows it
+  const int s = hb + blockIdx.x * 256 + threadIdx.x;
+  if (s >= he) return;
+  const SPos sp = load_spos(a.srec, s);
+  const int slot = (sp.dB - a.T * a.p2) * HB + (sp.dA - a.T * a.p1);
+  const float *row = a.crows + (size_t)slot * a.D, *dy = a.dY + (size_t)sp.bag * a.D;
+  float acc = 0.f;
+  for (int d0 = 0; d0 < a.D; d0 += 8) {
+    float x[8], y[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int d = min(d0 + u, a.D - 1);
+      x[u] = row[d];
+      y[u] = dy[d];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (d0 + u < a.D) acc += x[u] * y[u];
+  }
+  float scale = 1.f;
+  if (a.mean) {
+    const long long len = a.off[sp.bag + 1] - a.off[sp.bag];
+    scale = 1.f / (float)(len > 0 ? len : 1);
+  }
+  a.gw[sp.n] = acc * scale;
+}
+
+hipError_t launch_wgrad_hits(const DevArgs &a, hipStream_t s) {
+  if (a.has_cache && a.nnz > 0)
+    hipLaunchKernelGGL(k_wgrad_hits, dim3((a.nnz + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const DevArgs &a, hipStream_t s) {
   if (a.nblk == 0) return hipGetLastError();
   if (coop_route_ok(a)) {
