@@ -236,6 +236,28 @@ def main():
                    "pipeline": "grouping of batch i+1 overlapped with the backward of batch i"
                                if pipeline else "none"},
     }
+    # gradient with respect to the per-sample weights of one planned batch (off the
+    # default training step)
+    b0 = batches[0]
+    wsw = abi.workspace(desc, max_nnz, B, csize)
+    cv0 = None
+    if cache is not None:
+        cv0 = (slots[0], rows)
+    if not (wl.D > 512):
+        abi.tt_bag_plan(desc, b0["indices"], b0["offsets"], B, b0["per_sample_weights"], cache=cv0,
+                        ws=wsw)
+        gw = abi.tt_bag_weight_grad(desc, g, b0["indices"], b0["offsets"], B, b0["grad_out"],
+                                    b0["per_sample_weights"], cache=cv0, ws=wsw, planned=True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(20):
+            abi.tt_bag_weight_grad(desc, g, b0["indices"], b0["offsets"], B, b0["grad_out"],
+                                   b0["per_sample_weights"], cache=cv0, ws=wsw, out=gw,
+                                   planned=True)
+        e1.record()
+        torch.cuda.synchronize()
+        res["config"]["weight_grad_us"] = round(e0.elapsed_time(e1) * 1e3 / 20, 2)
+    del wsw
     # initialisation of the workload's cores (approx-normal), off the training path
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     scratch = [torch.empty_like(x) for x in g]
