@@ -637,7 +637,44 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
   const int4 cur = a.srec[2 * (size_t)sl], prev = a.srec[2 * (size_t)max(sl - 1, 0)];
   const bool st = lo + lane < hi && (sl == hb || prev.y != cur.y || prev.z != cur.z);
   unsigned long long starts = __ballot(st);
-  while (starts) {
+  // every run but the piece's last one ends inside the piece (one fragment): four of them
+  // at a time, lane group q = lane / 16 takes run q and its 16 lanes the columns
+  if (starts) {
+    const int lastl = 63 - __clzll((long long)starts);
+    unsigned long long early = starts & ~(1ull << lastl);
+    starts = 1ull << lastl;
+    const int q = lane >> 4, cq = lane & 15;
+    while (early) {
+      int lq = -1;
+      for (int k = 0; k < 4 && early; ++k) {
+        const int l = __ffsll((long long)early) - 1;
+        early &= early - 1ull;
+        if (k == q) lq = l;
+      }
+      const int l = lq >= 0 ? lq : 0;
+      const int kA = __shfl(cur.y, l), kB = __shfl(cur.z, l);
+      if (lq < 0) continue;
+      const int s0 = lo + l;
+      const int slot = (kB - a.T * a.p2) * HB + (kA - a.T * a.p1);
+      for (int c0 = cq; c0 < a.D; c0 += 64) {  // 4 columns of 16 lanes in flight
+        float fv[4], xv[4], av[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int c = min(c0 + 16 * k, a.D - 1);
+          const size_t e = (size_t)slot * a.D + c;
+          fv[k] = a.frag[(size_t)s0 * a.D + c];
+          xv[k] = UPD == UPD_GRAD ? 0.f : a.crows[e];
+          av[k] = UPD == UPD_ADAGRAD ? a.Xc[e] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (c0 + 16 * k < a.D)
+            apply_update<UPD>(a, a.crows, a.Xc, (size_t)slot * a.D + c0 + 16 * k, fv[k], xv[k],
+                              av[k]);
+      }
+    }
+  }
+  while (starts) {  // the last run: it may continue into the next pieces
     const int l = __ffsll((long long)starts) - 1;
     starts &= starts - 1ull;
     const int s0 = lo + l;
