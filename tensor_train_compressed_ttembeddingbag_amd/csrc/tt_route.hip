@@ -646,7 +646,9 @@ __global__ __launch_bounds__(RT) void k_route_c(DevArgs a) {
 }
 
 // Forward: out[b] = sum of the weighted cache rows of bag b (zero when it has none);
-// the contraction kernel then adds the misses.  One wave per bag.
+// the contraction kernel then adds the misses.  One wave per bag: the slots and
+// weights of 64 elements per load, then the hit rows eight at a time (summed in
+// position order).
 __global__ __launch_bounds__(RT) void k_yinit(DevArgs a) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int b = blockIdx.x * (RT / 64) + w;
@@ -662,17 +664,51 @@ __global__ __launch_bounds__(RT) void k_yinit(DevArgs a) {
     lo = lo < 0 ? 0 : (lo > a.nnz ? a.nnz : lo);
     hi = hi < lo ? lo : (hi > a.nnz ? a.nnz : hi);
   }
-  for (int d = lane; d < a.D; d += 64) {
-    float acc = 0.f;
-    for (int64_t n = lo; n < hi; ++n) {
-      const int s = a.slots[n];
-      if (s >= 0 && s < a.cache_size) {
-        const float wt = a.mean ? (a.psw ? a.psw[n] : 1.f) / (float)(hi - lo)
-                                : (a.psw ? a.psw[n] : 1.f);
-        acc += wt * a.crows[(size_t)s * a.D + d];
+  const float inv = (a.mean && hi > lo) ? 1.f / (float)(hi - lo) : 1.f;
+  constexpr int MAXC = 16;  // columns per lane (D <= 1024)
+  float acc[MAXC];
+#pragma unroll
+  for (int k = 0; k < MAXC; ++k) acc[k] = 0.f;
+  for (int64_t n0 = lo; n0 < hi; n0 += 64) {
+    const int64_t n = n0 + lane;
+    const int sl = n < hi ? a.slots[n] : -1;
+    const bool hit = sl >= 0 && sl < a.cache_size;
+    const float wt = hit ? (a.psw ? a.psw[n] : 1.f) * inv : 0.f;
+    unsigned long long m = __ballot(hit);
+    while (m) {
+      int li[8];
+      int cnt = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        li[k] = m ? __ffsll((long long)m) - 1 : -1;
+        if (m) { m &= m - 1ull; ++cnt; }
+      }
+      int rs[8];
+      float rw[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int l = li[k] >= 0 ? li[k] : 0;
+        rs[k] = __shfl(sl, l);
+        rw[k] = li[k] >= 0 ? __shfl(wt, l) : 0.f;
+        if (rs[k] < 0) rs[k] = 0;
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < MAXC; ++k2) {
+        const int d = lane + 64 * k2;
+        if (d >= a.D) break;
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = a.crows[(size_t)rs[k] * a.D + d];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (k < cnt) acc[k2] += rw[k] * v[k];
       }
     }
-    a.Y[(size_t)b * a.D + d] = acc;
+  }
+#pragma unroll
+  for (int k2 = 0; k2 < MAXC; ++k2) {
+    const int d = lane + 64 * k2;
+    if (d < a.D) a.Y[(size_t)b * a.D + d] = acc[k2];
   }
 }
 
