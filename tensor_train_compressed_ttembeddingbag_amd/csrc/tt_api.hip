@@ -114,12 +114,14 @@ int make_plan(const tt_desc *d, int64_t nnz, int64_t num_bags, int64_t cache_siz
   while (a.P > 8 && bwd_lds_bytes(P->RP, 1, a.P, a.q3, a.D, 1) > LDS_LIMIT) a.P >>= 1;
   if (bwd_lds_bytes(P->RP, 1, a.P, a.q3, a.D, 1) > LDS_LIMIT) return TT_ESHAPE;
   // LDS plans that let two workgroups share a CU where possible: G2 staged whole (fewer
-  // column blocks only when needed), backward reduction slots 8 -> 2 first
+  // column blocks only when needed), backward reduction slots 8 -> 2 first.  The rank-64
+  // backward holds a whole CU by its register count, so its plan may take all of the LDS.
   const size_t half = LDS_LIMIT / 2 - 1024;
+  const size_t bwd_budget = P->RP == 64 ? LDS_LIMIT : half;
   int nred = NW, JBb = a.q2;
-  while (bwd_lds_bytes(P->RP, JBb, a.P, a.q3, a.D, nred) > half && nred > 2) nred >>= 1;
-  while (bwd_lds_bytes(P->RP, JBb, a.P, a.q3, a.D, nred) > half && JBb > 1) --JBb;
-  while (bwd_lds_bytes(P->RP, JBb, a.P, a.q3, a.D, nred) > half && nred > 1) nred >>= 1;
+  while (bwd_lds_bytes(P->RP, JBb, a.P, a.q3, a.D, nred) > bwd_budget && nred > 2) nred >>= 1;
+  while (bwd_lds_bytes(P->RP, JBb, a.P, a.q3, a.D, nred) > bwd_budget && JBb > 1) --JBb;
+  while (bwd_lds_bytes(P->RP, JBb, a.P, a.q3, a.D, nred) > bwd_budget && nred > 1) nred >>= 1;
   a.NRED = nred;
   a.JBb = JBb;
   P->lds_bwd = bwd_lds_bytes(P->RP, JBb, a.P, a.q3, a.D, nred);
