@@ -199,6 +199,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     done = [step(i) for i in range(args.steps)]
+    t_enq = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if int(status.item()) != 0:
@@ -233,6 +234,7 @@ def main():
                                   wl.weighted, wl.lr, csize),
                    "nnz": nnz_mean, "global_batch": wl.num_tables * B,
                    "update": args.update,
+                   "host_enqueue_us_per_step": round((t_enq - t0) * 1e6 / args.steps, 2),
                    "pipeline": "grouping of batch i+1 overlapped with the backward of batch i"
                                if pipeline else "none"},
     }

@@ -135,14 +135,16 @@ def make_desc(p, q, ranks, num_embeddings: Optional[int] = None, num_tables: int
     return d
 
 
+# Marshalling is kept cheap: a training step makes a few of these calls, and their host
+# cost adds to every step's latency when the kernels are short.
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()  # argtypes convert the int to void*
 
 
 def _need(t: torch.Tensor, dtype, name: str):
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError("%s must be on the GPU" % name)
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
@@ -150,10 +152,17 @@ def _need(t: torch.Tensor, dtype, name: str):
         raise ValueError("%s must be contiguous" % name)
 
 
-def _stream(stream) -> ctypes.c_void_p:
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, like: Optional[torch.Tensor] = None):
+    """The HIP stream handle: the given torch stream, else the current stream of the
+    device that holds `like` (of the current device without it)."""
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(like.get_device() if like is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _check(fn: str, rc: int):
@@ -174,12 +183,21 @@ def workspace(desc: TTDesc, nnz: int, num_bags: int, cache_size: int = 0, device
     return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
 
 
+_core_arrays = {}
+
+
 def _cores(cores: Sequence[torch.Tensor]):
     if len(cores) != 3:
         raise ValueError("three cores expected")
-    for k, c in enumerate(cores):
-        _need(c, torch.float32, "cores[%d]" % k)
-    return (ctypes.c_void_p * 3)(*[c.data_ptr() for c in cores])
+    for c in cores:
+        _need(c, torch.float32, "cores")
+    key = (cores[0].data_ptr(), cores[1].data_ptr(), cores[2].data_ptr())
+    arr = _core_arrays.get(key)
+    if arr is None:  # pointer triples are reused across calls: keep their ctypes arrays
+        if len(_core_arrays) >= 64:
+            _core_arrays.clear()
+        arr = _core_arrays[key] = (ctypes.c_void_p * 3)(*key)
+    return arr
 
 
 def _cache_view(cache):
@@ -211,7 +229,7 @@ def tt_bag_plan(desc: TTDesc, indices, offsets, num_bags: int, per_sample_weight
     rc = lib().tt_bag_plan(ctypes.byref(desc), _ptr(indices), indices.numel(), _ptr(offsets),
                            int(num_bags), _ptr(per_sample_weights),
                            None if view is None else ctypes.byref(view), _ptr(ws),
-                           ws.numel(), _ptr(dev_status), _stream(stream))
+                           ws.numel(), _ptr(dev_status), _stream(stream, indices))
     _check("tt_bag_plan", rc)
     return ws
 
@@ -239,7 +257,7 @@ def tt_bag_forward(desc: TTDesc, cores, indices, offsets, num_bags: int,
     rc = fn(ctypes.byref(desc), _cores(cores), _ptr(indices), indices.numel(),
                               _ptr(offsets), int(num_bags), _ptr(per_sample_weights),
                               None if view is None else ctypes.byref(view), _ptr(out), _ptr(ws),
-                              ws.numel(), _ptr(dev_status), _stream(stream))
+                              ws.numel(), _ptr(dev_status), _stream(stream, indices))
     _check("tt_bag_forward_planned" if planned else "tt_bag_forward", rc)
     return out
 
@@ -265,7 +283,7 @@ def tt_bag_backward_sgd(desc: TTDesc, cores, indices, offsets, num_bags: int, gr
                                    _ptr(offsets), int(num_bags), _ptr(per_sample_weights),
                                    None if view is None else ctypes.byref(view), _ptr(grad_out),
                                    float(lr), _ptr(ws), ws.numel(), _ptr(dev_status),
-                                   _stream(stream))
+                                   _stream(stream, indices))
     _check("tt_bag_backward_sgd_planned" if planned else "tt_bag_backward_sgd", rc)
 
 
@@ -309,7 +327,7 @@ def tt_bag_backward_adagrad(desc: TTDesc, cores, indices, offsets, num_bags: int
                               _ptr(offsets), int(num_bags), _ptr(per_sample_weights),
                               None if view is None else ctypes.byref(view), _ptr(grad_out),
                               float(lr), float(eps), st, _ptr(sr), _ptr(ws), ws.numel(),
-                              _ptr(dev_status), _stream(stream))
+                              _ptr(dev_status), _stream(stream, indices))
     _check(name, rc)
 
 
@@ -330,7 +348,7 @@ def tt_bag_backward_grad(desc: TTDesc, cores, indices, offsets, num_bags: int, g
                               _ptr(offsets), int(num_bags), _ptr(per_sample_weights),
                               None if view is None else ctypes.byref(view), _ptr(grad_out),
                               _cores(grad_cores), _ptr(gr), _ptr(ws), ws.numel(),
-                              _ptr(dev_status), _stream(stream))
+                              _ptr(dev_status), _stream(stream, indices))
     _check(name, rc)
     return grad_cores, gr
 
@@ -348,7 +366,7 @@ def tt_bag_weight_grad(desc: TTDesc, cores, indices, offsets, num_bags: int, gra
     rc = getattr(lib(), name)(ctypes.byref(desc), _cores(cores), _ptr(indices), indices.numel(),
                               _ptr(offsets), int(num_bags), _ptr(per_sample_weights),
                               None if view is None else ctypes.byref(view), _ptr(grad_out),
-                              _ptr(out), _ptr(ws), ws.numel(), _ptr(dev_status), _stream(stream))
+                              _ptr(out), _ptr(ws), ws.numel(), _ptr(dev_status), _stream(stream, indices))
     _check(name, rc)
     return out
 
@@ -394,7 +412,7 @@ def tt_bag_route(desc: TTDesc, indices, offsets, num_bags: int, slots=None, cach
         ws = workspace(desc, indices.numel(), num_bags, cache_size if slots is not None else 0, dev)
     rc = lib().tt_bag_route(ctypes.byref(desc), _ptr(indices), indices.numel(), _ptr(offsets),
                             int(num_bags), _ptr(slots), int(cache_size), _ptr(order), _ptr(goff),
-                            _ptr(ws), ws.numel(), _ptr(dev_status), _stream(stream))
+                            _ptr(ws), ws.numel(), _ptr(dev_status), _stream(stream, indices))
     _check("tt_bag_route", rc)
     return order, goff
 
@@ -437,7 +455,7 @@ class Cache:
         _need(slot_out, torch.int32, "slot_out")
         _check("tt_cache_lookup", lib().tt_cache_lookup(self._h, _ptr(indices), indices.numel(),
                                                         _ptr(slot_out), 1 if count_freq else 0,
-                                                        _ptr(dev_status), _stream(stream)))
+                                                        _ptr(dev_status), _stream(stream, indices)))
         return slot_out
 
     def populate(self, cores, rows, stream=None) -> int:

@@ -171,7 +171,10 @@ inline void tt_launch(int id, void (*kernel)(KArgs...), dim3 grid, dim3 block, s
                       hipStream_t s, Args... args) {
   hipEvent_t e0 = nullptr, e1 = nullptr;
   prof_events(id, &e0, &e1);
-  hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, e0, e1, 0u, args...);
+  if (e0)
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, e0, e1, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
 }
 
 // host launchers (each kernel is launched from the file that defines it)
