@@ -327,3 +327,198 @@ void oracle_adagrad_rows(float *rows, float *state, const double *grad, const ui
         }
     }
 }
+
+/* ------------------------------------------------------------------------------------
+ * General number of cores d ("FBTT-Embedding" README, "Parameters": tt_p_shapes,
+ * tt_q_shapes and tt_ranks are lists of one length d, ranks padded to {1, ..., 1}).
+ * Core k (k = 0 .. d-1) has shape R(k) x p_k x q_k x R(k+1) in the logical layout,
+ * with R(0) = R(d) = 1 and R(k) = r[k-1] otherwise.  The row index i and the column
+ * index j are split over p and q row-major, as above, and W[i][j] is the product of
+ * the d slice matrices G_k[:, i_k, j_k, :] (a 1 x 1 result), evaluated left to right.
+ * The gradient of core k at (a, i_k, j_k, b) is g[j] times the product of the slices
+ * before k (entry a of that row vector) times the product of the slices after k
+ * (entry b of that column vector).
+ * ------------------------------------------------------------------------------------ */
+#define ORACLE_MAX_D 8
+
+typedef struct {
+    int32_t num_tables;      /* T >= 1 */
+    int32_t d;               /* 1 <= d <= ORACLE_MAX_D */
+    int64_t num_embeddings;  /* E */
+    int32_t p[ORACLE_MAX_D];
+    int32_t q[ORACLE_MAX_D];
+    int32_t r[ORACLE_MAX_D - 1];
+    int32_t pooling;         /* 0: sum, 1: mean */
+} oracle_shape_d;
+
+static int64_t rank_d(const oracle_shape_d *s, int k)
+{
+    return (k == 0 || k == s->d) ? 1 : s->r[k - 1];
+}
+
+int64_t oracle_core_numel_d(const oracle_shape_d *s, int k)
+{
+    return rank_d(s, k) * s->p[k] * s->q[k] * rank_d(s, k + 1);
+}
+
+static int64_t core_index_d(const oracle_shape_d *s, int k, int64_t a, int64_t ik, int64_t jk,
+                            int64_t b)
+{
+    return ((a * s->p[k] + ik) * s->q[k] + jk) * rank_d(s, k + 1) + b;
+}
+
+/* row-major mixed-radix split of v over the d extents e */
+static void split_d(const int32_t *e, int d, int64_t v, int64_t *out)
+{
+    for (int k = d - 1; k >= 0; --k) {
+        out[k] = v % e[k];
+        v /= e[k];
+    }
+}
+
+static int check_inputs_d(const oracle_shape_d *s, const int64_t *idx, int64_t nnz,
+                          const int64_t *off, int64_t nbags_total)
+{
+    if (s->d < 1 || s->d > ORACLE_MAX_D) return -1;
+    double prodp = 1.0;
+    for (int k = 0; k < s->d; ++k) prodp *= s->p[k];
+    if (prodp < (double)s->num_embeddings) return -1;
+    if (off[0] != 0 || off[nbags_total] != nnz) return -1;
+    for (int64_t b = 0; b < nbags_total; ++b)
+        if (off[b + 1] < off[b]) return -1;
+    for (int64_t n = 0; n < nnz; ++n)
+        if (idx[n] < 0 || idx[n] >= s->num_embeddings) return -1;
+    return 0;
+}
+
+static int64_t dim_d(const oracle_shape_d *s)
+{
+    int64_t D = 1;
+    for (int k = 0; k < s->d; ++k) D *= s->q[k];
+    return D;
+}
+
+static int64_t max_rank_d(const oracle_shape_d *s)
+{
+    int64_t m = 1;
+    for (int k = 1; k < s->d; ++k)
+        if (rank_d(s, k) > m) m = rank_d(s, k);
+    return m;
+}
+
+/* prefix vectors L[k] (length R(k)) of one (i, j): L[0] = 1, L[k+1] = L[k] * G_k slice */
+static void prefix_d(const oracle_shape_d *s, const float *const *G, const int64_t *ii,
+                     const int64_t *jj, int64_t M, double *L)
+{
+    L[0] = 1.0;
+    for (int k = 0; k < s->d; ++k) {
+        const int64_t ra = rank_d(s, k), rb = rank_d(s, k + 1);
+        for (int64_t b = 0; b < rb; ++b) {
+            double acc = 0.0;
+            for (int64_t a = 0; a < ra; ++a)
+                acc += L[k * M + a] * (double)G[k][core_index_d(s, k, a, ii[k], jj[k], b)];
+            L[(k + 1) * M + b] = acc;
+        }
+    }
+}
+
+/* suffix vectors S[k] (length R(k)): S[d] = 1, S[k] = G_k slice * S[k+1] */
+static void suffix_d(const oracle_shape_d *s, const float *const *G, const int64_t *ii,
+                     const int64_t *jj, int64_t M, double *S)
+{
+    S[s->d * M] = 1.0;
+    for (int k = s->d - 1; k >= 0; --k) {
+        const int64_t ra = rank_d(s, k), rb = rank_d(s, k + 1);
+        for (int64_t a = 0; a < ra; ++a) {
+            double acc = 0.0;
+            for (int64_t b = 0; b < rb; ++b)
+                acc += (double)G[k][core_index_d(s, k, a, ii[k], jj[k], b)] * S[(k + 1) * M + b];
+            S[k * M + a] = acc;
+        }
+    }
+}
+
+/* W[i][:] of one table (G: its d cores) */
+void oracle_tt_row_d(const oracle_shape_d *s, const float *const *G, int64_t i, double *row)
+{
+    const int64_t D = dim_d(s), M = max_rank_d(s);
+    int64_t ii[ORACLE_MAX_D], jj[ORACLE_MAX_D];
+    double *L = (double *)malloc(sizeof(double) * (s->d + 1) * M);
+    split_d(s->p, s->d, i, ii);
+    for (int64_t j = 0; j < D; ++j) {
+        split_d(s->q, s->d, j, jj);
+        prefix_d(s, G, ii, jj, M, L);
+        row[j] = L[s->d * M];
+    }
+    free(L);
+}
+
+/* Forward over d-core tables: cores holds d*T pointers, table t's at [d*t .. d*t+d). */
+int oracle_forward_d(const oracle_shape_d *s, const float *const *cores, const int64_t *idx,
+                     int64_t nnz, const int64_t *off, int64_t B, const float *psw, double *Y)
+{
+    const int64_t T = s->num_tables, NB = T * B;
+    if (check_inputs_d(s, idx, nnz, off, NB)) return -1;
+    const int64_t D = dim_d(s);
+    double *row = (double *)malloc(sizeof(double) * D);
+    memset(Y, 0, sizeof(double) * NB * D);
+    for (int64_t b = 0; b < NB; ++b) {
+        const int64_t t = b / B;
+        for (int64_t n = off[b]; n < off[b + 1]; ++n) {
+            const double w = psw ? (double)psw[n] : 1.0;
+            oracle_tt_row_d(s, cores + s->d * t, idx[n], row);
+            for (int64_t j = 0; j < D; ++j) Y[b * D + j] += w * row[j];
+        }
+        if (s->pooling == 1 && off[b + 1] > off[b])
+            for (int64_t j = 0; j < D; ++j) Y[b * D + j] /= (double)(off[b + 1] - off[b]);
+    }
+    free(row);
+    return 0;
+}
+
+/* Backward over d-core tables: grad[d*t + k] (double, logical layout) fully overwritten;
+ * touched[d*t + k] (may be NULL) marks the slices that received a contribution. */
+int oracle_backward_d(const oracle_shape_d *s, const float *const *cores, const int64_t *idx,
+                      int64_t nnz, const int64_t *off, int64_t B, const float *psw,
+                      const float *dY, double *const *grad, uint8_t *const *touched)
+{
+    const int64_t T = s->num_tables, NB = T * B;
+    if (check_inputs_d(s, idx, nnz, off, NB)) return -1;
+    const int d = s->d;
+    const int64_t D = dim_d(s), M = max_rank_d(s);
+    for (int64_t t = 0; t < T; ++t)
+        for (int k = 0; k < d; ++k) {
+            memset(grad[d * t + k], 0, sizeof(double) * oracle_core_numel_d(s, k));
+            if (touched) memset(touched[d * t + k], 0, (size_t)s->p[k]);
+        }
+    double *L = (double *)malloc(sizeof(double) * (d + 1) * M);
+    double *S = (double *)malloc(sizeof(double) * (d + 1) * M);
+    int64_t ii[ORACLE_MAX_D], jj[ORACLE_MAX_D];
+    for (int64_t b = 0; b < NB; ++b) {
+        const int64_t t = b / B;
+        const float *const *G = cores + d * t;
+        const double inv = (s->pooling == 1) ? 1.0 / (double)(off[b + 1] - off[b]) : 1.0;
+        for (int64_t n = off[b]; n < off[b + 1]; ++n) {
+            const double w = (psw ? (double)psw[n] : 1.0) * inv;
+            split_d(s->p, d, idx[n], ii);
+            if (touched)
+                for (int k = 0; k < d; ++k) touched[d * t + k][ii[k]] = 1;
+            for (int64_t j = 0; j < D; ++j) {
+                const double g = w * (double)dY[b * D + j];
+                split_d(s->q, d, j, jj);
+                prefix_d(s, G, ii, jj, M, L);
+                suffix_d(s, G, ii, jj, M, S);
+                for (int k = 0; k < d; ++k) {
+                    const int64_t ra = rank_d(s, k), rb = rank_d(s, k + 1);
+                    for (int64_t a = 0; a < ra; ++a)
+                        for (int64_t c = 0; c < rb; ++c)
+                            grad[d * t + k][core_index_d(s, k, a, ii[k], jj[k], c)] +=
+                                g * L[k * M + a] * S[(k + 1) * M + c];
+                }
+            }
+        }
+    }
+    free(L);
+    free(S);
+    return 0;
+}

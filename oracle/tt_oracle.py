@@ -17,6 +17,8 @@ Pages followed ("FBTT-Embedding" README unless stated):
     is counted and the cache is (re)filled from the most frequent rows on
     `cache_populate()`, each row initialised from the TT cores.
   * "TableBatchedTTEmbeddingBag": T tables of one shape in one call.
+  * "Parameters": the shape lists have one length d (any number of cores); the
+    d-core functions (``*_d``) take the row as the product of the d slice matrices.
 
 Readings where the pages are silent: row-major mixed radix for the index split;
 offsets carry a terminal entry; duplicates sum; the cache is filled with the K
@@ -38,7 +40,8 @@ _SO = os.path.join(_HERE, "libtt_oracle.so")
 __all__ = ["build", "forward", "backward", "sgd", "adagrad", "tt_row", "split_index", "bag_ids",
            "route_order", "group_counts", "count_frequencies", "select_cache",
            "lookup_slots", "populate_rows", "splitmix64", "lfu_set", "lfu_populate", "LFU_WAYS",
-           "philox4x32_10", "init_param", "init_core", "factorize"]
+           "philox4x32_10", "init_param", "init_core", "factorize", "tt_row_d", "forward_d",
+           "backward_d", "sgd_d", "MAX_D"]
 
 
 def build(force: bool = False) -> str:
@@ -78,8 +81,102 @@ def _L():
         lib.oracle_adagrad_rows.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_int64,
                                             ctypes.c_double, ctypes.c_double]
         lib.oracle_tt_row.argtypes = [P, P, P, P, ctypes.c_int64, P]
+        lib.oracle_forward_d.argtypes = [P, P, P, ctypes.c_int64, P, ctypes.c_int64, P, P]
+        lib.oracle_forward_d.restype = ctypes.c_int
+        lib.oracle_backward_d.argtypes = [P, P, P, ctypes.c_int64, P, ctypes.c_int64, P, P, P,
+                                          P]
+        lib.oracle_backward_d.restype = ctypes.c_int
+        lib.oracle_tt_row_d.argtypes = [P, P, ctypes.c_int64, P]
         _lib = lib
     return _lib
+
+
+MAX_D = 8
+
+
+class _ShapeD(ctypes.Structure):
+    _fields_ = [("num_tables", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("num_embeddings", ctypes.c_int64), ("p", ctypes.c_int32 * MAX_D),
+                ("q", ctypes.c_int32 * MAX_D), ("r", ctypes.c_int32 * (MAX_D - 1)),
+                ("pooling", ctypes.c_int32)]
+
+
+def _shape_d(p, q, ranks, E, T, pooling=0):
+    d = len(p)
+    if not (1 <= d <= MAX_D and len(q) == d and len(ranks) == d - 1):
+        raise ValueError("d-core shape: len(p) == len(q) == len(ranks) + 1 <= %d" % MAX_D)
+    s = _ShapeD()
+    s.num_tables, s.d, s.num_embeddings, s.pooling = int(T), d, int(E), int(pooling)
+    for k in range(d):
+        s.p[k], s.q[k] = int(p[k]), int(q[k])
+    for k in range(d - 1):
+        s.r[k] = int(ranks[k])
+    return s
+
+
+def tt_row_d(p, q, ranks, cores, i: int) -> np.ndarray:
+    """One row W[i, :] (float64) of a single d-core table (cores in the logical layout)."""
+    c = [_f32(x) for x in cores]
+    s = _shape_d(p, q, ranks, int(np.prod(p)), 1)
+    out = np.zeros(int(np.prod(q)), dtype=np.float64)
+    _L().oracle_tt_row_d(ctypes.byref(s), _ptr_array(c), int(i), _ptr(out))
+    return out
+
+
+def forward_d(p, q, ranks, E, cores, indices, offsets, num_bags, per_sample_weights=None,
+              pooling=0):
+    """EmbeddingBag forward over d-core TT tables (d = len(p)); cores: T lists of d
+    arrays in the logical layout [R_{k-1}][p_k][q_k][R_k].  Returns Y float64."""
+    T = len(cores)
+    flat = [_f32(c) for tbl in cores for c in tbl]
+    s = _shape_d(p, q, ranks, E, T, pooling)
+    idx = np.ascontiguousarray(indices, dtype=np.int64)
+    off = np.ascontiguousarray(offsets, dtype=np.int64)
+    psw = None if per_sample_weights is None else _f32(per_sample_weights)
+    Y = np.zeros((T * num_bags, int(np.prod(q))), dtype=np.float64)
+    rc = _L().oracle_forward_d(ctypes.byref(s), _ptr_array(flat), _ptr(idx), len(idx),
+                               _ptr(off), int(num_bags), _ptr(psw), _ptr(Y))
+    if rc != 0:
+        raise ValueError("oracle_forward_d: invalid input")
+    return Y
+
+
+def backward_d(p, q, ranks, E, cores, indices, offsets, num_bags, grad_out,
+               per_sample_weights=None, pooling=0):
+    """Core gradients of L = sum_b <dY[b], Y[b]> for d-core tables: (grads, touched),
+    T lists of d float64 arrays (logical layout) and of d uint8 slice masks."""
+    T, d = len(cores), len(p)
+    flat = [_f32(c) for tbl in cores for c in tbl]
+    s = _shape_d(p, q, ranks, E, T, pooling)
+    idx = np.ascontiguousarray(indices, dtype=np.int64)
+    off = np.ascontiguousarray(offsets, dtype=np.int64)
+    psw = None if per_sample_weights is None else _f32(per_sample_weights)
+    dY = _f32(grad_out)
+    grads = [[np.zeros(c.shape, dtype=np.float64) for c in tbl] for tbl in cores]
+    touched = [[np.zeros(p[k], dtype=np.uint8) for k in range(d)] for _ in cores]
+    rc = _L().oracle_backward_d(ctypes.byref(s), _ptr_array(flat), _ptr(idx), len(idx),
+                                _ptr(off), int(num_bags), _ptr(psw), _ptr(dY),
+                                _ptr_array([g for tbl in grads for g in tbl]),
+                                _ptr_array([m for tbl in touched for m in tbl]))
+    if rc != 0:
+        raise ValueError("oracle_backward_d: invalid input")
+    return grads, touched
+
+
+def sgd_d(cores, grads, touched, lr):
+    """Plain SGD on the touched slices of d-core tables, in fp64, rounded to fp32:
+    G <- fp32(double(G) - lr * dG); untouched slices keep their bits."""
+    out = []
+    for tbl, gt, mt in zip(cores, grads, touched):
+        row = []
+        for c, g, m in zip(tbl, gt, mt):
+            new = np.array(c, dtype=np.float32, copy=True)
+            upd = (c.astype(np.float64) - float(lr) * g).astype(np.float32)
+            sel = m.astype(bool)
+            new[:, sel] = upd[:, sel]
+            row.append(new)
+        out.append(row)
+    return out
 
 
 def _shape(p, q, ranks, E, T, pooling=0):
