@@ -372,6 +372,53 @@ int tt_factorize(int64_t n, int exact, int32_t out[3]);
 int tt_full_weight(const tt_desc *desc, const float *const cores[3], int table, int64_t first,
                    int64_t count, float *out, void *stream);
 
+/* ---------------------------------------------------------------- d-core tables
+ * Tables of any number d of cores ("FBTT-Embedding" README, "Parameters": tt_p_shapes,
+ * tt_q_shapes and tt_ranks are lists of one length; "Initialization": core k has shape
+ * R_{k-1} x p_k x q_k x R_k with R_0 = R_d = 1).  The row index is split over p and the
+ * column index over q row-major; the row is the product of the d slice matrices.
+ * Cores are stored slice-major [p_k][R_{k-1}][q_k][R_k], T tables one after the other in
+ * each core's buffer, as for three cores.
+ *
+ * The d cores are cut into three groups of consecutive cores; each group is multiplied
+ * out into one (dense) core in the workspace, the three-core kernels run on those, and
+ * their gradients are split back onto the d cores by the product rule.  The cut is the
+ * one with the least dense work among those the three-core path accepts (q of the first
+ * group in {1, 2, 4}, of the last <= 16, at most 8191 / T slices per group, ranks <= 64);
+ * TT_ESHAPE when there is none.  No cache.  Semantics as tt_bag_forward /
+ * tt_bag_backward_sgd / tt_bag_backward_grad, with d core pointers (host arrays of
+ * device pointers).  Gradients (grad_d) are dense and fully overwritten: zero on slices
+ * no index touched.  SGD (sgd_d) changes only entries with a nonzero gradient.
+ * The workspace (tt_bag_workspace_size_d bytes, 256-byte aligned) holds the three-core
+ * workspace, the multiplied-out cores with their gradients and d gradient buffers. */
+#define TT_MAX_CORES 8
+typedef struct tt_desc_d {
+    int32_t num_tables;              /* T >= 1                                       */
+    int32_t d;                       /* 3 <= d <= TT_MAX_CORES                       */
+    int64_t num_embeddings;          /* E, 1 <= E <= prod(p)                         */
+    int32_t p[TT_MAX_CORES];         /* p[0 .. d)                                    */
+    int32_t q[TT_MAX_CORES];         /* q[0 .. d); D = prod(q)                       */
+    int32_t ranks[TT_MAX_CORES - 1]; /* ranks[0 .. d-1), each in [1, 64]             */
+    int32_t pooling;                 /* TT_POOL_SUM or TT_POOL_MEAN                  */
+} tt_desc_d;
+
+size_t tt_bag_workspace_size_d(const tt_desc_d *desc, int64_t nnz, int64_t num_bags);
+/* the chosen cut: groups [0, cut[0]), [cut[0], cut[1]), [cut[1], d) */
+int tt_bag_groups_d(const tt_desc_d *desc, int32_t cut[2]);
+int tt_bag_forward_d(const tt_desc_d *desc, const float *const *cores, const int64_t *indices,
+                     int64_t nnz, const int64_t *offsets, int64_t num_bags,
+                     const float *per_sample_weights, float *out, void *ws, size_t ws_bytes,
+                     int32_t *dev_status, void *stream);
+int tt_bag_backward_sgd_d(const tt_desc_d *desc, float *const *cores, const int64_t *indices,
+                          int64_t nnz, const int64_t *offsets, int64_t num_bags,
+                          const float *per_sample_weights, const float *grad_out, float lr,
+                          void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
+int tt_bag_backward_grad_d(const tt_desc_d *desc, const float *const *cores,
+                           const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                           int64_t num_bags, const float *per_sample_weights,
+                           const float *grad_out, float *const *grad_cores, void *ws,
+                           size_t ws_bytes, int32_t *dev_status, void *stream);
+
 /* ---------------------------------------------------------------- timing
  * Optional per-kernel timing for benchmarks: while enabled, every kernel the
  * library enqueues is bracketed by two HIP events recorded on the stream it is

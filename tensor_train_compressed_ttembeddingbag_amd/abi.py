@@ -9,6 +9,7 @@ loudly (``RuntimeError``) when the library has not been built.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from typing import Optional, Sequence
 
@@ -44,6 +45,16 @@ class TTDesc(ctypes.Structure):
     _fields_ = [("num_tables", ctypes.c_int32), ("num_embeddings", ctypes.c_int64),
                 ("p", ctypes.c_int32 * 3), ("q", ctypes.c_int32 * 3),
                 ("ranks", ctypes.c_int32 * 2), ("pooling", ctypes.c_int32)]
+
+
+TT_MAX_CORES = 8
+
+
+class TTDescD(ctypes.Structure):
+    _fields_ = [("num_tables", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("num_embeddings", ctypes.c_int64), ("p", ctypes.c_int32 * TT_MAX_CORES),
+                ("q", ctypes.c_int32 * TT_MAX_CORES),
+                ("ranks", ctypes.c_int32 * (TT_MAX_CORES - 1)), ("pooling", ctypes.c_int32)]
 
 
 class TTCacheView(ctypes.Structure):
@@ -83,6 +94,14 @@ _SIG = {
     "tt_init_cores": (ctypes.c_int, [_P, _P, ctypes.c_int, ctypes.c_float, ctypes.c_uint64, _P]),
     "tt_factorize": (ctypes.c_int, [_I64, ctypes.c_int, _P]),
     "tt_full_weight": (ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _I64, _P, _P]),
+    "tt_bag_workspace_size_d": (ctypes.c_size_t, [_P, _I64, _I64]),
+    "tt_bag_groups_d": (ctypes.c_int, [_P, _P]),
+    "tt_bag_forward_d": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P, ctypes.c_size_t,
+                                        _P, _P]),
+    "tt_bag_backward_sgd_d": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, ctypes.c_float,
+                                             _P, ctypes.c_size_t, _P, _P]),
+    "tt_bag_backward_grad_d": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P, _P,
+                                              ctypes.c_size_t, _P, _P]),
     "tt_cache_create": (ctypes.c_int, [_P, _P, _I64, _I64]),
     "tt_cache_create_policy": (ctypes.c_int, [_P, _P, _I64, _I64, ctypes.c_int]),
     "tt_cache_export": (ctypes.c_int, [_P, _P, _P, _P, _P]),
@@ -500,3 +519,111 @@ class Cache:
             self.close()
         except Exception:
             pass
+
+
+# ------------------------------------------------------------------ d-core tables
+
+def make_desc_d(p, q, ranks, num_embeddings: Optional[int] = None, num_tables: int = 1,
+                pooling: int = 0) -> TTDescD:
+    """Descriptor of d-core tables, d = len(p) = len(q) = len(ranks) + 1."""
+    d = len(p)
+    if not (3 <= d <= TT_MAX_CORES and len(q) == d and len(ranks) == d - 1):
+        raise ValueError("d-core shape: 3 <= len(p) == len(q) == len(ranks) + 1 <= %d"
+                         % TT_MAX_CORES)
+    x = TTDescD()
+    x.num_tables, x.d, x.pooling = int(num_tables), d, int(pooling)
+    x.num_embeddings = int(num_embeddings if num_embeddings is not None else math.prod(p))
+    for k in range(d):
+        x.p[k], x.q[k] = int(p[k]), int(q[k])
+    for k in range(d - 1):
+        x.ranks[k] = int(ranks[k])
+    return x
+
+
+def _cores_d(desc: TTDescD, cores):
+    if len(cores) != desc.d:
+        raise ValueError("%d cores expected" % desc.d)
+    for c in cores:
+        _need(c, torch.float32, "cores")
+    return (ctypes.c_void_p * desc.d)(*[c.data_ptr() for c in cores])
+
+
+def tt_bag_workspace_size_d(desc: TTDescD, nnz: int, num_bags: int) -> int:
+    n = lib().tt_bag_workspace_size_d(ctypes.byref(desc), int(nnz), int(num_bags))
+    if n == 0:
+        raise TTError("tt_bag_workspace_size_d", -2)
+    return int(n)
+
+
+def workspace_d(desc: TTDescD, nnz: int, num_bags: int, device=None) -> torch.Tensor:
+    return torch.empty(tt_bag_workspace_size_d(desc, nnz, num_bags), dtype=torch.uint8,
+                       device=device or "cuda")
+
+
+def tt_bag_groups_d(desc: TTDescD):
+    """The cut of the d cores into three groups: (a, b) for [0, a), [a, b), [b, d)."""
+    cut = (ctypes.c_int32 * 2)()
+    _check("tt_bag_groups_d", lib().tt_bag_groups_d(ctypes.byref(desc), cut))
+    return int(cut[0]), int(cut[1])
+
+
+def _args_d(desc, indices, offsets, num_bags, per_sample_weights, ws, dev_status):
+    _need(indices, torch.int64, "indices")
+    _need(offsets, torch.int64, "offsets")
+    if per_sample_weights is not None:
+        _need(per_sample_weights, torch.float32, "per_sample_weights")
+    if ws is None:
+        ws = workspace_d(desc, indices.numel(), num_bags, indices.device)
+    _need(ws, torch.uint8, "ws")
+    if dev_status is not None:
+        _need(dev_status, torch.int32, "dev_status")
+    return ws
+
+
+def tt_bag_forward_d(desc: TTDescD, cores, indices, offsets, num_bags: int,
+                     per_sample_weights=None, out=None, ws=None, dev_status=None,
+                     stream=None) -> torch.Tensor:
+    """out[T*num_bags, D] = pooled rows of d-core tables (see tt_bag.h)."""
+    ws = _args_d(desc, indices, offsets, num_bags, per_sample_weights, ws, dev_status)
+    D = math.prod(desc.q[k] for k in range(desc.d))
+    if out is None:
+        out = torch.empty(desc.num_tables * num_bags, D, dtype=torch.float32,
+                          device=indices.device)
+    _need(out, torch.float32, "out")
+    rc = lib().tt_bag_forward_d(ctypes.byref(desc), _cores_d(desc, cores), _ptr(indices),
+                                indices.numel(), _ptr(offsets), int(num_bags),
+                                _ptr(per_sample_weights), _ptr(out), _ptr(ws), ws.numel(),
+                                _ptr(dev_status), _stream(stream, indices))
+    _check("tt_bag_forward_d", rc)
+    return out
+
+
+def tt_bag_backward_sgd_d(desc: TTDescD, cores, indices, offsets, num_bags: int, grad_out,
+                          lr: float, per_sample_weights=None, ws=None, dev_status=None,
+                          stream=None) -> None:
+    """In-place SGD on the d cores."""
+    ws = _args_d(desc, indices, offsets, num_bags, per_sample_weights, ws, dev_status)
+    _need(grad_out, torch.float32, "grad_out")
+    rc = lib().tt_bag_backward_sgd_d(ctypes.byref(desc), _cores_d(desc, cores), _ptr(indices),
+                                     indices.numel(), _ptr(offsets), int(num_bags),
+                                     _ptr(per_sample_weights), _ptr(grad_out), float(lr),
+                                     _ptr(ws), ws.numel(), _ptr(dev_status),
+                                     _stream(stream, indices))
+    _check("tt_bag_backward_sgd_d", rc)
+
+
+def tt_bag_backward_grad_d(desc: TTDescD, cores, indices, offsets, num_bags: int, grad_out,
+                           grad_cores=None, per_sample_weights=None, ws=None, dev_status=None,
+                           stream=None):
+    """Dense gradients with respect to the d cores (fully overwritten); returns them."""
+    ws = _args_d(desc, indices, offsets, num_bags, per_sample_weights, ws, dev_status)
+    _need(grad_out, torch.float32, "grad_out")
+    if grad_cores is None:
+        grad_cores = [torch.empty_like(c) for c in cores]
+    rc = lib().tt_bag_backward_grad_d(ctypes.byref(desc), _cores_d(desc, cores), _ptr(indices),
+                                      indices.numel(), _ptr(offsets), int(num_bags),
+                                      _ptr(per_sample_weights), _ptr(grad_out),
+                                      _cores_d(desc, grad_cores), _ptr(ws), ws.numel(),
+                                      _ptr(dev_status), _stream(stream, indices))
+    _check("tt_bag_backward_grad_d", rc)
+    return grad_cores
