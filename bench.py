@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="readme",
-                    choices=["tiny", "readme", "skewed", "multitable", "cached"])
+                    choices=["tiny", "readme", "skewed", "multitable", "cached", "readme4"])
     ap.add_argument("--batches", type=int, default=8, help="distinct batches cycled through")
     ap.add_argument("--no-pipeline", action="store_true",
                     help="group each batch right before its forward (no overlap with the "
@@ -96,6 +96,9 @@ def main():
     abi.lib()
     wl = W.WORKLOADS[args.workload]
     cores = W.make_cores(wl)
+    if len(wl.p) != 3:
+        run_dcore(args, wl, cores, torch, abi, metrics, W)
+        return
     g = [torch.from_numpy(np.concatenate([W.slice_major(cores[t][k]).ravel()
                                           for t in range(wl.num_tables)])).cuda()
          for k in range(3)]
@@ -354,6 +357,86 @@ def roofline(args, wl, batches, step, torch, abi, metrics, slots):
     return rf, kernels
 
 
+def run_dcore(args, wl, cores, torch, abi, metrics, W):
+    """d-core workload: a step is tt_bag_plan_d (grouping) + tt_bag_forward_d_planned +
+    tt_bag_backward_sgd_d_planned on one stream (both multiply out the groups of cores; the
+    backward splits the gradients back and applies SGD to the d cores)."""
+    d = len(wl.p)
+    g = [torch.from_numpy(np.concatenate([W.slice_major(cores[t][k]).ravel()
+                                          for t in range(wl.num_tables)])).cuda()
+         for k in range(d)]
+    desc = abi.make_desc_d(wl.p, wl.q, wl.ranks, wl.E, wl.num_tables)
+    a, b = abi.tt_bag_groups_d(desc)
+    q3 = (int(np.prod(wl.q[:a])), int(np.prod(wl.q[a:b])), int(np.prod(wl.q[b:])))
+    r3 = (wl.ranks[a - 1], wl.ranks[b - 1])
+    batches = [_dev(W.make_batch(wl, k), torch) for k in range(args.batches)]
+    B = wl.bags_per_table
+    ws = abi.workspace_d(desc, max(x["indices"].numel() for x in batches), B)
+    out = torch.empty(wl.num_tables * B, wl.D, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    main = torch.cuda.current_stream()
+
+    def step(i):
+        x = batches[i % len(batches)]
+        abi.tt_bag_plan_d(desc, x["indices"], x["offsets"], B, x["per_sample_weights"], ws=ws,
+                          dev_status=status, stream=main)
+        abi.tt_bag_forward_d(desc, g, x["indices"], x["offsets"], B, x["per_sample_weights"],
+                             out=out, ws=ws, dev_status=status, stream=main, planned=True)
+        abi.tt_bag_backward_sgd_d(desc, g, x["indices"], x["offsets"], B, x["grad_out"], wl.lr,
+                                  x["per_sample_weights"], ws=ws, dev_status=status,
+                                  stream=main, planned=True)
+        return i
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    done = [step(i) for i in range(args.steps)]
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if int(status.item()) != 0:
+        print("device status %d during the benchmark" % int(status.item()), file=sys.stderr)
+        sys.exit(1)
+    ms = (t1 - t0) * 1e3 / args.steps
+    nnz = float(np.mean([batches[i % len(batches)]["indices"].numel() for i in done]))
+    res = {"metric": "TT-EmbeddingBag fwd+bwd µs/nnz and GFLOPS (E=11M, D=64, R=32, B=512)",
+           "value": round(ms * 1e3 / nnz, 6), "unit": "us/nnz", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic (seeded numpy PCG64; random-normal cores)",
+           "config": {"workload": "%s: d=%d p=%s q=%s ranks=%s E=%d D=%d tables=%d bags/table=%d "
+                                  "cut=[0,%d)[%d,%d)[%d,%d) (as three cores q=%s ranks=%s)"
+                      % (wl.name, d, list(wl.p), list(wl.q), list(wl.ranks), wl.E, wl.D,
+                         wl.num_tables, B, a, a, b, b, d, list(q3), list(r3)),
+                      "nnz": nnz, "global_batch": B, "update": "sgd"}}
+    if not args.no_roofline:
+        abi.tt_profile_enable(True)
+        done = [step(i) for i in range(min(args.steps, 200))]
+        torch.cuda.synchronize()
+        prof = abi.tt_profile_read()
+        abi.tt_profile_enable(False)
+        kernels = {k: {"total_ms": round(v[0], 4), "launches": v[1],
+                       "avg_us": round(1e3 * v[0] / v[1], 3)} for k, v in prof.items() if v[1]}
+        dom = max(kernels, key=lambda k: kernels[k]["total_ms"])
+        # the contraction kernels run the three-core shape of the cut
+        p3 = (int(np.prod(wl.p[:a])), int(np.prod(wl.p[a:b])), int(np.prod(wl.p[b:])))
+        U = float(np.mean([metrics.unique_pairs(p3, wl.num_tables, B, batches[i % len(batches)]["np"]["indices"],
+                                                batches[i % len(batches)]["np"]["offsets"], None, wl.E)
+                           for i in range(len(batches))]))
+        work = {"k_bwd": metrics.bwd_kernel_flops(q3, r3, nnz, U),
+                "k_fwd": metrics.fwd_kernel_flops(q3, r3, nnz, U)}
+        if dom in work:
+            ach = work[dom] / (kernels[dom]["avg_us"] * 1e-6) / 1e12
+            res["roofline"] = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 3),
+                               "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(ach / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": None,
+                               "work_per_launch": "%.4g flop" % work[dom]}
+        res["kernels"] = kernels
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(wl, cores, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 def cpu_baseline(wl, cores, budget_s):
     """The oracle, as it stands, on a prefix of the bags of batch 0 of the same
     workload: the prefix doubles until one fwd+bwd run takes >= budget/8 (or covers
@@ -369,10 +452,11 @@ def cpu_baseline(wl, cores, budget_s):
         n = int(off[bags])
         psw = None if b["per_sample_weights"] is None else b["per_sample_weights"][:n]
         t0 = time.perf_counter()
-        oracle.forward(wl.p, wl.q, wl.ranks, wl.E, cores, b["indices"][:n], off[:bags + 1], bags,
-                       psw)
-        oracle.backward(wl.p, wl.q, wl.ranks, wl.E, cores, b["indices"][:n], off[:bags + 1], bags,
-                        b["grad_out"][:bags], psw)
+        fwd, bwd = ((oracle.forward, oracle.backward) if len(wl.p) == 3
+                    else (oracle.forward_d, oracle.backward_d))
+        fwd(wl.p, wl.q, wl.ranks, wl.E, cores, b["indices"][:n], off[:bags + 1], bags, psw)
+        bwd(wl.p, wl.q, wl.ranks, wl.E, cores, b["indices"][:n], off[:bags + 1], bags,
+            b["grad_out"][:bags], psw)
         dt = time.perf_counter() - t0
         t_used += dt
         nnz_done += n

@@ -418,6 +418,27 @@ int tt_bag_backward_grad_d(const tt_desc_d *desc, const float *const *cores,
                            int64_t num_bags, const float *per_sample_weights,
                            const float *grad_out, float *const *grad_cores, void *ws,
                            size_t ws_bytes, int32_t *dev_status, void *stream);
+/* The grouping of a batch done once (as tt_bag_plan, into the three-core part of the
+ * d-core workspace) and reused by the _planned calls below, which otherwise behave as
+ * the calls above (same arguments; a plan made for other inputs sets
+ * TT_DEV_STALE_PLAN and leaves the outputs unspecified). */
+int tt_bag_plan_d(const tt_desc_d *desc, const int64_t *indices, int64_t nnz,
+                  const int64_t *offsets, int64_t num_bags, const float *per_sample_weights,
+                  void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
+int tt_bag_forward_d_planned(const tt_desc_d *desc, const float *const *cores,
+                             const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                             int64_t num_bags, const float *per_sample_weights, float *out,
+                             void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
+int tt_bag_backward_sgd_d_planned(const tt_desc_d *desc, float *const *cores,
+                                  const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                                  int64_t num_bags, const float *per_sample_weights,
+                                  const float *grad_out, float lr, void *ws, size_t ws_bytes,
+                                  int32_t *dev_status, void *stream);
+int tt_bag_backward_grad_d_planned(const tt_desc_d *desc, const float *const *cores,
+                                   const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                                   int64_t num_bags, const float *per_sample_weights,
+                                   const float *grad_out, float *const *grad_cores, void *ws,
+                                   size_t ws_bytes, int32_t *dev_status, void *stream);
 
 /* ---------------------------------------------------------------- timing
  * Optional per-kernel timing for benchmarks: while enabled, every kernel the

@@ -102,6 +102,14 @@ _SIG = {
                                              _P, ctypes.c_size_t, _P, _P]),
     "tt_bag_backward_grad_d": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P, _P,
                                               ctypes.c_size_t, _P, _P]),
+    "tt_bag_plan_d": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _P, ctypes.c_size_t, _P, _P]),
+    "tt_bag_forward_d_planned": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P,
+                                                ctypes.c_size_t, _P, _P]),
+    "tt_bag_backward_sgd_d_planned": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P,
+                                                     ctypes.c_float, _P, ctypes.c_size_t, _P,
+                                                     _P]),
+    "tt_bag_backward_grad_d_planned": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P,
+                                                      _P, ctypes.c_size_t, _P, _P]),
     "tt_cache_create": (ctypes.c_int, [_P, _P, _I64, _I64]),
     "tt_cache_create_policy": (ctypes.c_int, [_P, _P, _I64, _I64, ctypes.c_int]),
     "tt_cache_export": (ctypes.c_int, [_P, _P, _P, _P, _P]),
@@ -580,9 +588,20 @@ def _args_d(desc, indices, offsets, num_bags, per_sample_weights, ws, dev_status
     return ws
 
 
+def tt_bag_plan_d(desc: TTDescD, indices, offsets, num_bags: int, per_sample_weights=None,
+                  ws=None, dev_status=None, stream=None) -> torch.Tensor:
+    """Group the batch into ws (allocated if None) for the _planned d-core calls."""
+    ws = _args_d(desc, indices, offsets, num_bags, per_sample_weights, ws, dev_status)
+    rc = lib().tt_bag_plan_d(ctypes.byref(desc), _ptr(indices), indices.numel(), _ptr(offsets),
+                             int(num_bags), _ptr(per_sample_weights), _ptr(ws), ws.numel(),
+                             _ptr(dev_status), _stream(stream, indices))
+    _check("tt_bag_plan_d", rc)
+    return ws
+
+
 def tt_bag_forward_d(desc: TTDescD, cores, indices, offsets, num_bags: int,
                      per_sample_weights=None, out=None, ws=None, dev_status=None,
-                     stream=None) -> torch.Tensor:
+                     stream=None, planned: bool = False) -> torch.Tensor:
     """out[T*num_bags, D] = pooled rows of d-core tables (see tt_bag.h)."""
     ws = _args_d(desc, indices, offsets, num_bags, per_sample_weights, ws, dev_status)
     D = math.prod(desc.q[k] for k in range(desc.d))
@@ -590,7 +609,8 @@ def tt_bag_forward_d(desc: TTDescD, cores, indices, offsets, num_bags: int,
         out = torch.empty(desc.num_tables * num_bags, D, dtype=torch.float32,
                           device=indices.device)
     _need(out, torch.float32, "out")
-    rc = lib().tt_bag_forward_d(ctypes.byref(desc), _cores_d(desc, cores), _ptr(indices),
+    fn = lib().tt_bag_forward_d_planned if planned else lib().tt_bag_forward_d
+    rc = fn(ctypes.byref(desc), _cores_d(desc, cores), _ptr(indices),
                                 indices.numel(), _ptr(offsets), int(num_bags),
                                 _ptr(per_sample_weights), _ptr(out), _ptr(ws), ws.numel(),
                                 _ptr(dev_status), _stream(stream, indices))
@@ -600,11 +620,12 @@ def tt_bag_forward_d(desc: TTDescD, cores, indices, offsets, num_bags: int,
 
 def tt_bag_backward_sgd_d(desc: TTDescD, cores, indices, offsets, num_bags: int, grad_out,
                           lr: float, per_sample_weights=None, ws=None, dev_status=None,
-                          stream=None) -> None:
+                          stream=None, planned: bool = False) -> None:
     """In-place SGD on the d cores."""
     ws = _args_d(desc, indices, offsets, num_bags, per_sample_weights, ws, dev_status)
     _need(grad_out, torch.float32, "grad_out")
-    rc = lib().tt_bag_backward_sgd_d(ctypes.byref(desc), _cores_d(desc, cores), _ptr(indices),
+    fn = lib().tt_bag_backward_sgd_d_planned if planned else lib().tt_bag_backward_sgd_d
+    rc = fn(ctypes.byref(desc), _cores_d(desc, cores), _ptr(indices),
                                      indices.numel(), _ptr(offsets), int(num_bags),
                                      _ptr(per_sample_weights), _ptr(grad_out), float(lr),
                                      _ptr(ws), ws.numel(), _ptr(dev_status),
@@ -614,13 +635,14 @@ def tt_bag_backward_sgd_d(desc: TTDescD, cores, indices, offsets, num_bags: int,
 
 def tt_bag_backward_grad_d(desc: TTDescD, cores, indices, offsets, num_bags: int, grad_out,
                            grad_cores=None, per_sample_weights=None, ws=None, dev_status=None,
-                           stream=None):
+                           stream=None, planned: bool = False):
     """Dense gradients with respect to the d cores (fully overwritten); returns them."""
     ws = _args_d(desc, indices, offsets, num_bags, per_sample_weights, ws, dev_status)
     _need(grad_out, torch.float32, "grad_out")
     if grad_cores is None:
         grad_cores = [torch.empty_like(c) for c in cores]
-    rc = lib().tt_bag_backward_grad_d(ctypes.byref(desc), _cores_d(desc, cores), _ptr(indices),
+    fn = lib().tt_bag_backward_grad_d_planned if planned else lib().tt_bag_backward_grad_d
+    rc = fn(ctypes.byref(desc), _cores_d(desc, cores), _ptr(indices),
                                       indices.numel(), _ptr(offsets), int(num_bags),
                                       _ptr(per_sample_weights), _ptr(grad_out),
                                       _cores_d(desc, grad_cores), _ptr(ws), ws.numel(),

@@ -99,15 +99,95 @@ __global__ __launch_bounds__(GBLK) void k_dsplit_x(const float *__restrict__ dY,
   }
 }
 
-// SGD on a whole core: entries with a zero gradient (every entry of an untouched
-// slice) keep their bits
-__global__ __launch_bounds__(GBLK) void k_dapply(float *__restrict__ x,
-                                                 const float *__restrict__ g, long long n,
-                                                 float lr) {
+// The same two sums with one wavefront per output when they are long: lane l adds the
+// terms l, l + 64, ... in order, then the 64 partials are added by a fixed butterfly,
+// so the result does not depend on timing.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__global__ __launch_bounds__(GBLK) void k_dsplit_g_wave(const float *__restrict__ X,
+                                                        const float *__restrict__ dY,
+                                                        float *__restrict__ dG, long long n,
+                                                        int PX, int pk, int Rl, int QX, int qk,
+                                                        int Rm, int Rr) {
+  const long long PY = (long long)PX * pk, QY = (long long)QX * qk;
+  const long long L = (long long)PX * Rl * QX;  // terms (iX, a, jX), jX fastest
+  const int lane = threadIdx.x & 63;
+  for (long long e = (blockIdx.x * (long long)GBLK + threadIdx.x) >> 6; e < n;
+       e += ((long long)gridDim.x * GBLK) >> 6) {
+    long long v = e;
+    const int r = (int)(v % Rr); v /= Rr;
+    const int jk = (int)(v % qk); v /= qk;
+    const int s = (int)(v % Rm); v /= Rm;
+    const long long ik = v % pk;
+    const long long t = v / pk;
+    float acc = 0.f;
+    for (long long m = lane; m < L; m += 64) {
+      const int jX = (int)(m % QX);
+      const long long ia = m / QX;  // iX * Rl + a
+      const long long iX = ia / Rl, a = ia % Rl;
+      const float x = X[((t * PX + iX) * Rl + a) * QX * (long long)Rm + (long long)jX * Rm + s];
+      const float y = dY[(((t * PY + iX * pk + ik) * Rl + a) * QY + (long long)jX * qk + jk) * Rr + r];
+      acc = fmaf(x, y, acc);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) dG[e] = acc;
+  }
+}
+
+__global__ __launch_bounds__(GBLK) void k_dsplit_x_wave(const float *__restrict__ dY,
+                                                        const float *__restrict__ G,
+                                                        float *__restrict__ dX, long long n,
+                                                        int PX, int pk, int Rl, int QX, int qk,
+                                                        int Rm, int Rr) {
+  const long long PY = (long long)PX * pk, QY = (long long)QX * qk;
+  const long long L = (long long)pk * qk * Rr;  // terms (ik, jk, r), r fastest
+  const int lane = threadIdx.x & 63;
+  for (long long e = (blockIdx.x * (long long)GBLK + threadIdx.x) >> 6; e < n;
+       e += ((long long)gridDim.x * GBLK) >> 6) {
+    long long v = e;
+    const int s = (int)(v % Rm); v /= Rm;
+    const int jX = (int)(v % QX); v /= QX;
+    const int a = (int)(v % Rl); v /= Rl;
+    const long long iX = v % PX;
+    const long long t = v / PX;
+    float acc = 0.f;
+    for (long long m = lane; m < L; m += 64) {
+      const int r = (int)(m % Rr);
+      const long long u = m / Rr;
+      const int jk = (int)(u % qk);
+      const long long ik = u / qk;
+      const float y = dY[(((t * PY + iX * pk + ik) * Rl + a) * QY + (long long)jX * qk + jk) * Rr + r];
+      const float g = G[(((t * pk + ik) * Rm + s) * (long long)qk + jk) * Rr + r];
+      acc = fmaf(y, g, acc);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) dX[e] = acc;
+  }
+}
+
+// SGD on every core in one launch: entries with a zero gradient (every entry of an
+// untouched slice) keep their bits
+struct ApplyArgs {
+  float *x[TT_MAX_CORES];
+  const float *g[TT_MAX_CORES];
+  long long end[TT_MAX_CORES];  // running sum of the cores' sizes
+  int ncores;
+  float lr;
+};
+
+__global__ __launch_bounds__(GBLK) void k_dapply(ApplyArgs A) {
+  const long long n = A.end[A.ncores - 1];
   for (long long e = blockIdx.x * (long long)GBLK + threadIdx.x; e < n;
        e += (long long)gridDim.x * GBLK) {
-    const float ge = g[e];
-    if (ge != 0.f) x[e] = x[e] - lr * ge;
+    int k = 0;
+    while (k < A.ncores - 1 && e >= A.end[k]) ++k;
+    const long long i = e - (k > 0 ? A.end[k - 1] : 0);
+    const float ge = A.g[k][i];
+    if (ge != 0.f) A.x[k][i] = A.x[k][i] - A.lr * ge;
   }
 }
 
@@ -115,6 +195,8 @@ int grid_for(long long n) {
   const long long b = (n + GBLK - 1) / GBLK;
   return (int)(b < 8192 ? (b > 0 ? b : 1) : 8192);
 }
+
+constexpr long long WAVE_SUM_MIN = 64;  // sums at least this long take a wavefront each
 
 struct DPlan {
   int d, T;
@@ -283,15 +365,16 @@ int check_call(const tt_desc_d *d, const void *cores, const int64_t *indices, in
 int backward_d(const tt_desc_d *d, const DPlan &P, const float *const *cores,
                const int64_t *indices, int64_t nnz, const int64_t *offsets, int64_t num_bags,
                const float *psw, const float *grad_out, float *const *dG, void *ws,
-               int32_t *dev_status, hipStream_t s) {
+               int32_t *dev_status, hipStream_t s, bool planned) {
   const float *S[3];
   hipError_t e = merge_all(d, P, cores, ws, S, s);
   if (e != hipSuccess) return TT_EHIP;
   float *dS[3];
   for (int g = 0; g < 3; ++g)
     dS[g] = P.hi[g] - P.lo[g] == 1 ? dG[P.lo[g]] : wsf(ws, P.offdP[P.hi[g] - 1]);
-  int rc = tt_bag_backward_grad(&P.d3, S, indices, nnz, offsets, num_bags, psw, nullptr,
-                                grad_out, dS, nullptr, ws, P.ws3, dev_status, s);
+  int rc = (planned ? tt_bag_backward_grad_planned : tt_bag_backward_grad)(
+      &P.d3, S, indices, nnz, offsets, num_bags, psw, nullptr, grad_out, dS, nullptr, ws, P.ws3,
+      dev_status, s);
   if (rc != TT_OK) return rc;
   for (int g = 0; g < 3; ++g)
     for (int k = P.hi[g] - 1; k > P.lo[g]; --k) {
@@ -299,12 +382,20 @@ int backward_d(const tt_desc_d *d, const DPlan &P, const float *const *cores,
       const float *X = k - 1 == P.lo[g] ? cores[P.lo[g]] : wsf(ws, P.offP[k - 1]);
       const float *dY = wsf(ws, P.offdP[k]);
       const long long nG = P.numelG[k];
-      tt_launch(K_DSPLIT, k_dsplit_g, dim3(grid_for(nG)), dim3(GBLK), 0, s, X, dY, dG[k], nG,
-                st.PX, st.pk, st.Rl, st.QX, st.qk, st.Rm, st.Rr);
+      if ((long long)st.PX * st.Rl * st.QX >= WAVE_SUM_MIN)
+        tt_launch(K_DSPLIT, k_dsplit_g_wave, dim3(grid_for(nG * 64)), dim3(GBLK), 0, s, X, dY,
+                  dG[k], nG, st.PX, st.pk, st.Rl, st.QX, st.qk, st.Rm, st.Rr);
+      else
+        tt_launch(K_DSPLIT, k_dsplit_g, dim3(grid_for(nG)), dim3(GBLK), 0, s, X, dY, dG[k], nG,
+                  st.PX, st.pk, st.Rl, st.QX, st.qk, st.Rm, st.Rr);
       float *dX = k - 1 == P.lo[g] ? dG[P.lo[g]] : wsf(ws, P.offdP[k - 1]);
       const long long nX = k - 1 == P.lo[g] ? P.numelG[P.lo[g]] : P.numelP[k - 1];
-      tt_launch(K_DSPLIT, k_dsplit_x, dim3(grid_for(nX)), dim3(GBLK), 0, s, dY, cores[k], dX, nX,
-                st.PX, st.pk, st.Rl, st.QX, st.qk, st.Rm, st.Rr);
+      if ((long long)st.pk * st.qk * st.Rr >= WAVE_SUM_MIN)
+        tt_launch(K_DSPLIT, k_dsplit_x_wave, dim3(grid_for(nX * 64)), dim3(GBLK), 0, s, dY,
+                  cores[k], dX, nX, st.PX, st.pk, st.Rl, st.QX, st.qk, st.Rm, st.Rr);
+      else
+        tt_launch(K_DSPLIT, k_dsplit_x, dim3(grid_for(nX)), dim3(GBLK), 0, s, dY, cores[k], dX,
+                  nX, st.PX, st.pk, st.Rl, st.QX, st.qk, st.Rm, st.Rr);
     }
   return hipGetLastError() == hipSuccess ? TT_OK : TT_EHIP;
 }
@@ -313,6 +404,75 @@ int backward_d(const tt_desc_d *d, const DPlan &P, const float *const *cores,
 }  // namespace ttb
 
 using namespace ttb;
+
+namespace ttb {
+namespace {
+
+int forward_d(const tt_desc_d *desc, const float *const *cores, const int64_t *indices,
+              int64_t nnz, const int64_t *offsets, int64_t num_bags,
+              const float *per_sample_weights, float *out, void *ws, size_t ws_bytes,
+              int32_t *dev_status, void *stream, bool planned) {
+  DPlan P;
+  int rc = check_call(desc, cores, indices, nnz, offsets, ws, ws_bytes, &P, num_bags);
+  if (rc != TT_OK) return rc;
+  if (!out) return TT_EINVAL;
+  for (int k = 0; k < desc->d; ++k)
+    if (!cores[k]) return TT_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  const float *S[3];
+  if (merge_all(desc, P, cores, ws, S, s) != hipSuccess) return TT_EHIP;
+  return (planned ? tt_bag_forward_planned : tt_bag_forward)(
+      &P.d3, S, indices, nnz, offsets, num_bags, per_sample_weights, nullptr, out, ws, P.ws3,
+      dev_status, stream);
+}
+
+int grad_d(const tt_desc_d *desc, const float *const *cores, const int64_t *indices,
+           int64_t nnz, const int64_t *offsets, int64_t num_bags,
+           const float *per_sample_weights, const float *grad_out, float *const *grad_cores,
+           void *ws, size_t ws_bytes, int32_t *dev_status, void *stream, bool planned) {
+  DPlan P;
+  int rc = check_call(desc, cores, indices, nnz, offsets, ws, ws_bytes, &P, num_bags);
+  if (rc != TT_OK) return rc;
+  if (!grad_out || !grad_cores) return TT_EINVAL;
+  for (int k = 0; k < desc->d; ++k)
+    if (!cores[k] || !grad_cores[k]) return TT_EINVAL;
+  return backward_d(desc, P, cores, indices, nnz, offsets, num_bags, per_sample_weights,
+                    grad_out, grad_cores, ws, dev_status, (hipStream_t)stream, planned);
+}
+
+int sgd_d(const tt_desc_d *desc, float *const *cores, const int64_t *indices, int64_t nnz,
+          const int64_t *offsets, int64_t num_bags, const float *per_sample_weights,
+          const float *grad_out, float lr, void *ws, size_t ws_bytes, int32_t *dev_status,
+          void *stream, bool planned) {
+  DPlan P;
+  int rc = check_call(desc, cores, indices, nnz, offsets, ws, ws_bytes, &P, num_bags);
+  if (rc != TT_OK) return rc;
+  if (!grad_out) return TT_EINVAL;
+  for (int k = 0; k < desc->d; ++k)
+    if (!cores[k]) return TT_EINVAL;
+  float *dG[TT_MAX_CORES];
+  for (int k = 0; k < desc->d; ++k) dG[k] = wsf(ws, P.offdG[k]);
+  hipStream_t s = (hipStream_t)stream;
+  rc = backward_d(desc, P, cores, indices, nnz, offsets, num_bags, per_sample_weights, grad_out,
+                  dG, ws, dev_status, s, planned);
+  if (rc != TT_OK) return rc;
+  ApplyArgs A;
+  memset(&A, 0, sizeof(A));
+  A.ncores = desc->d;
+  A.lr = lr;
+  long long run = 0;
+  for (int k = 0; k < desc->d; ++k) {
+    A.x[k] = cores[k];
+    A.g[k] = dG[k];
+    run += P.numelG[k];
+    A.end[k] = run;
+  }
+  tt_launch(K_DAPPLY, k_dapply, dim3(grid_for(run)), dim3(GBLK), 0, s, A);
+  return hipGetLastError() == hipSuccess ? TT_OK : TT_EHIP;
+}
+
+}  // namespace
+}  // namespace ttb
 
 extern "C" {
 
@@ -332,21 +492,32 @@ int tt_bag_groups_d(const tt_desc_d *desc, int32_t cut[2]) {
   return TT_OK;
 }
 
+int tt_bag_plan_d(const tt_desc_d *desc, const int64_t *indices, int64_t nnz,
+                  const int64_t *offsets, int64_t num_bags, const float *per_sample_weights,
+                  void *ws, size_t ws_bytes, int32_t *dev_status, void *stream) {
+  DPlan P;
+  if (!offsets || !ws || (nnz > 0 && !indices)) return TT_EINVAL;
+  const int rc = make_dplan(desc, nnz, num_bags, &P);
+  if (rc != TT_OK) return rc;
+  if (ws_bytes < P.total || ((uintptr_t)ws & 255)) return TT_EWORKSPACE;
+  return tt_bag_plan(&P.d3, indices, nnz, offsets, num_bags, per_sample_weights, nullptr, ws,
+                     P.ws3, dev_status, stream);
+}
+
 int tt_bag_forward_d(const tt_desc_d *desc, const float *const *cores, const int64_t *indices,
                      int64_t nnz, const int64_t *offsets, int64_t num_bags,
                      const float *per_sample_weights, float *out, void *ws, size_t ws_bytes,
                      int32_t *dev_status, void *stream) {
-  DPlan P;
-  int rc = check_call(desc, cores, indices, nnz, offsets, ws, ws_bytes, &P, num_bags);
-  if (rc != TT_OK) return rc;
-  if (!out) return TT_EINVAL;
-  for (int k = 0; k < desc->d; ++k)
-    if (!cores[k]) return TT_EINVAL;
-  hipStream_t s = (hipStream_t)stream;
-  const float *S[3];
-  if (merge_all(desc, P, cores, ws, S, s) != hipSuccess) return TT_EHIP;
-  return tt_bag_forward(&P.d3, S, indices, nnz, offsets, num_bags, per_sample_weights, nullptr,
-                        out, ws, P.ws3, dev_status, stream);
+  return forward_d(desc, cores, indices, nnz, offsets, num_bags, per_sample_weights, out, ws,
+                   ws_bytes, dev_status, stream, false);
+}
+
+int tt_bag_forward_d_planned(const tt_desc_d *desc, const float *const *cores,
+                             const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                             int64_t num_bags, const float *per_sample_weights, float *out,
+                             void *ws, size_t ws_bytes, int32_t *dev_status, void *stream) {
+  return forward_d(desc, cores, indices, nnz, offsets, num_bags, per_sample_weights, out, ws,
+                   ws_bytes, dev_status, stream, true);
 }
 
 int tt_bag_backward_grad_d(const tt_desc_d *desc, const float *const *cores,
@@ -354,36 +525,34 @@ int tt_bag_backward_grad_d(const tt_desc_d *desc, const float *const *cores,
                            int64_t num_bags, const float *per_sample_weights,
                            const float *grad_out, float *const *grad_cores, void *ws,
                            size_t ws_bytes, int32_t *dev_status, void *stream) {
-  DPlan P;
-  int rc = check_call(desc, cores, indices, nnz, offsets, ws, ws_bytes, &P, num_bags);
-  if (rc != TT_OK) return rc;
-  if (!grad_out || !grad_cores) return TT_EINVAL;
-  for (int k = 0; k < desc->d; ++k)
-    if (!cores[k] || !grad_cores[k]) return TT_EINVAL;
-  return backward_d(desc, P, cores, indices, nnz, offsets, num_bags, per_sample_weights,
-                    grad_out, grad_cores, ws, dev_status, (hipStream_t)stream);
+  return grad_d(desc, cores, indices, nnz, offsets, num_bags, per_sample_weights, grad_out,
+                grad_cores, ws, ws_bytes, dev_status, stream, false);
+}
+
+int tt_bag_backward_grad_d_planned(const tt_desc_d *desc, const float *const *cores,
+                                   const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                                   int64_t num_bags, const float *per_sample_weights,
+                                   const float *grad_out, float *const *grad_cores, void *ws,
+                                   size_t ws_bytes, int32_t *dev_status, void *stream) {
+  return grad_d(desc, cores, indices, nnz, offsets, num_bags, per_sample_weights, grad_out,
+                grad_cores, ws, ws_bytes, dev_status, stream, true);
 }
 
 int tt_bag_backward_sgd_d(const tt_desc_d *desc, float *const *cores, const int64_t *indices,
                           int64_t nnz, const int64_t *offsets, int64_t num_bags,
                           const float *per_sample_weights, const float *grad_out, float lr,
                           void *ws, size_t ws_bytes, int32_t *dev_status, void *stream) {
-  DPlan P;
-  int rc = check_call(desc, cores, indices, nnz, offsets, ws, ws_bytes, &P, num_bags);
-  if (rc != TT_OK) return rc;
-  if (!grad_out) return TT_EINVAL;
-  for (int k = 0; k < desc->d; ++k)
-    if (!cores[k]) return TT_EINVAL;
-  float *dG[TT_MAX_CORES];
-  for (int k = 0; k < desc->d; ++k) dG[k] = wsf(ws, P.offdG[k]);
-  hipStream_t s = (hipStream_t)stream;
-  rc = backward_d(desc, P, cores, indices, nnz, offsets, num_bags, per_sample_weights, grad_out,
-                  dG, ws, dev_status, s);
-  if (rc != TT_OK) return rc;
-  for (int k = 0; k < desc->d; ++k)
-    tt_launch(K_DAPPLY, k_dapply, dim3(grid_for(P.numelG[k])), dim3(GBLK), 0, s, cores[k],
-              (const float *)dG[k], (long long)P.numelG[k], lr);
-  return hipGetLastError() == hipSuccess ? TT_OK : TT_EHIP;
+  return sgd_d(desc, cores, indices, nnz, offsets, num_bags, per_sample_weights, grad_out, lr,
+               ws, ws_bytes, dev_status, stream, false);
+}
+
+int tt_bag_backward_sgd_d_planned(const tt_desc_d *desc, float *const *cores,
+                                  const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                                  int64_t num_bags, const float *per_sample_weights,
+                                  const float *grad_out, float lr, void *ws, size_t ws_bytes,
+                                  int32_t *dev_status, void *stream) {
+  return sgd_d(desc, cores, indices, nnz, offsets, num_bags, per_sample_weights, grad_out, lr,
+               ws, ws_bytes, dev_status, stream, true);
 }
 
 }  // extern "C"

@@ -121,6 +121,7 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
   if (clearer && !stale) fwd_clear_out(a);
   if (stale || wi >= nitems) {
     if (clearer) fwd_raise_flag(a);
+    if (stale && wi == 0 && tid == 0) set_status(a.status, DEV_STALE_PLAN);
     return;
   }
   const int grp = item.x, s0 = item.y, s1 = item.z;

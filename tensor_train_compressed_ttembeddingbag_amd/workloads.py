@@ -17,10 +17,12 @@ describe or imply:
 * ``cached``    the ``readme`` shape, 4096 bags of 20 Zipf(1.2) indices, with an
                 HBM cache of 110,000 rows filled from a 10-batch warm-up
                 ("Software Cache" section).
+* ``readme4``   the ``readme`` table size and batch as four cores p=(10,20,220,250),
+                q=(2,2,4,4), ranks=(32,32,32) (the shape lists may have any length).
 
 Seeds: cores come from PCG64(seed); batch k from PCG64(seed*1000 + k); the Zipf
 permutation of table t from PCG64(seed*100 + 50 + t).  ``seed`` defaults to the
-workload's number (tiny=1 ... cached=5).
+workload's number (tiny=1 ... cached=5, readme4=6).
 
 Cores are returned in the pages' logical layout ``[R_{k-1}][p_k][q_k][R_k]``
 ("Initialization" section).  ``slice_major`` reorders one to the
@@ -76,6 +78,9 @@ WORKLOADS = {
     "cached": Workload("cached", 5, (200, 220, 250), (4, 4, 4), (32, 32), 1, 4096,
                        ("fixed", 20), ("zipf", 1.2), 1.0 / math.sqrt(32), 0.01,
                        cache_size=110_000, warmup_batches=10, hashtbl_size=1 << 21),
+    # the readme table and batch with E = 11,000,000 split over four cores
+    "readme4": Workload("readme4", 6, (10, 20, 220, 250), (2, 2, 4, 4), (32, 32, 32), 1, 512,
+                        ("fixed", 20), ("uniform",), 1.0 / math.sqrt(32), 0.01),
 }
 
 
@@ -92,7 +97,7 @@ def custom(name="custom", p=(4, 5, 6), q=(2, 2, 2), ranks=(4, 4), num_tables=1,
 def core_shapes(wl: Workload):
     """Logical core shapes [R_{k-1}, p_k, q_k, R_k] with ranks [1]+ranks+[1]."""
     full = (1,) + tuple(wl.ranks) + (1,)
-    return [(full[k], wl.p[k], wl.q[k], full[k + 1]) for k in range(3)]
+    return [(full[k], wl.p[k], wl.q[k], full[k + 1]) for k in range(len(wl.p))]
 
 
 def make_cores(wl: Workload, seed: Optional[int] = None):

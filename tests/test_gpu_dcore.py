@@ -157,6 +157,47 @@ def test_dcore_readme_sized_four_cores():
         assert rel_err(delta, -lr * grads[0][k]) <= TOL, k
 
 
+def test_dcore_planned_calls_match_stateless():
+    """One tt_bag_plan_d reused by the _planned forward, gradient and SGD calls gives the
+    stateless calls' results (the backward bit for bit); a plan made for another batch
+    raises TT_DEV_STALE_PLAN."""
+    print("case d-core planned", flush=True)
+    p, q, ranks, E, T, B, pooling, weighted, _ = CASES[0]
+    rng = np.random.Generator(np.random.PCG64(712))
+    cores = _cores(rng, p, q, ranks, T, 0.6)
+    idx, off = _batch(rng, E, T, B)
+    w = rng.random(len(idx)).astype(np.float32)
+    dY = rng.standard_normal((T * B, int(np.prod(q)))).astype(np.float32)
+    desc = abi.make_desc_d(p, q, ranks, E, T, pooling)
+    g = [_dev(cores, k) for k in range(len(p))]
+    d_idx, d_off = torch.from_numpy(idx).cuda(), torch.from_numpy(off).cuda()
+    d_w, d_dY = torch.from_numpy(w).cuda(), torch.from_numpy(dY).cuda()
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = abi.tt_bag_plan_d(desc, d_idx, d_off, B, d_w, dev_status=st)
+    Yp = abi.tt_bag_forward_d(desc, g, d_idx, d_off, B, d_w, ws=ws, dev_status=st, planned=True)
+    Ys = abi.tt_bag_forward_d(desc, g, d_idx, d_off, B, d_w)
+    assert rel_err(Yp.cpu().numpy(), Ys.cpu().numpy().astype(np.float64)) <= 1e-6
+    gp = abi.tt_bag_backward_grad_d(desc, g, d_idx, d_off, B, d_dY, per_sample_weights=d_w,
+                                    ws=ws, dev_status=st, planned=True)
+    gs = abi.tt_bag_backward_grad_d(desc, g, d_idx, d_off, B, d_dY, per_sample_weights=d_w)
+    for a, b in zip(gp, gs):
+        assert torch.equal(a, b)
+    n1 = [x.clone() for x in g]
+    n2 = [x.clone() for x in g]
+    abi.tt_bag_backward_sgd_d(desc, n1, d_idx, d_off, B, d_dY, 0.05, d_w, ws=ws, dev_status=st,
+                              planned=True)
+    abi.tt_bag_backward_sgd_d(desc, n2, d_idx, d_off, B, d_dY, 0.05, d_w)
+    for a, b in zip(n1, n2):
+        assert torch.equal(a, b)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    # a plan for other indices: the planned call refuses it on the device
+    other = torch.from_numpy(rng.integers(0, E, len(idx)).astype(np.int64)).cuda()
+    abi.tt_bag_forward_d(desc, g, other, d_off, B, d_w, ws=ws, dev_status=st, planned=True)
+    torch.cuda.synchronize()
+    assert int(st.item()) & abi.TT_DEV_STALE_PLAN
+
+
 def test_dcore_rejects_bad_shapes():
     """Shapes no cut can serve, and d outside [3, 8], are refused before any launch."""
     with pytest.raises(ValueError):
