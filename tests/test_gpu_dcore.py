@@ -198,6 +198,29 @@ def test_dcore_planned_calls_match_stateless():
     assert int(st.item()) & abi.TT_DEV_STALE_PLAN
 
 
+def test_dcore_empty_batch():
+    """No indices: the forward gives zero rows, the gradients are all zero, SGD changes
+    nothing."""
+    print("case d-core empty", flush=True)
+    p, q, ranks, E, T = (4, 5, 6, 7), (2, 2, 2, 2), (4, 5, 3), 800, 2
+    rng = np.random.Generator(np.random.PCG64(713))
+    cores = _cores(rng, p, q, ranks, T, 0.6)
+    desc = abi.make_desc_d(p, q, ranks, E, T)
+    g = [_dev(cores, k) for k in range(4)]
+    B = 3
+    idx = torch.zeros(0, dtype=torch.int64, device="cuda")
+    off = torch.zeros(T * B + 1, dtype=torch.int64, device="cuda")
+    dY = torch.randn(T * B, 16, device="cuda")
+    out = torch.full((T * B, 16), 5.0, device="cuda")
+    abi.tt_bag_forward_d(desc, g, idx, off, B, out=out)
+    assert torch.all(out == 0)
+    gg = abi.tt_bag_backward_grad_d(desc, g, idx, off, B, dY)
+    assert all(torch.all(x == 0) for x in gg)
+    new = [x.clone() for x in g]
+    abi.tt_bag_backward_sgd_d(desc, new, idx, off, B, dY, 0.1)
+    assert all(torch.equal(a, b) for a, b in zip(new, g))
+
+
 def test_dcore_rejects_bad_shapes():
     """Shapes no cut can serve, and d outside [3, 8], are refused before any launch."""
     with pytest.raises(ValueError):
