@@ -44,7 +44,7 @@ def source_digest() -> str:
 
 def _short(name: str) -> str:
     """`void ttb::k_fwd<32>(ttb::DevArgs)` -> `k_fwd<32>`."""
-    n = name.split("(")[0]
+    n = name.replace("(anonymous namespace)::", "").split("(")[0]
     n = re.sub(r"^void\s+", "", n)
     return n.replace("ttb::", "")
 
