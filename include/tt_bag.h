@@ -372,6 +372,40 @@ int tt_factorize(int64_t n, int exact, int32_t out[3]);
 int tt_full_weight(const tt_desc *desc, const float *const cores[3], int table, int64_t first,
                    int64_t count, float *out, void *stream);
 
+/* ---------------------------------------------------------------- backward over distinct indices
+ * The loss is linear in the rows, so the gradient of a batch equals that of a virtual
+ * batch with one element per distinct (table, index) u, weight 1, alone in its bag, whose
+ * grad_out row is sum_{n: idx_n = u} w_n grad_out[bag n] (times 1/len with mean pooling).
+ * With repeated indices (Zipf-skewed batches) the virtual batch is smaller and a hot index
+ * costs one element.  No cache.
+ *   tt_bag_plan_dedup: the grouping of the batch (as tt_bag_plan, so tt_bag_forward_planned
+ *     on the same ws runs the forward), the sort by index, the runs of equal indices, and
+ *     the grouping of the virtual batch.  HOST-SYNCHRONOUS: it waits for the number of
+ *     distinct indices and returns info[0] = that number, info[1] = the largest per table
+ *     (host array; pass it unchanged to the backward).
+ *   tt_bag_backward_sgd_dedup / _grad_dedup: the grad_out sums of the runs (fixed order:
+ *     32-element chunks of the sorted order, then each run's pieces in order), then the
+ *     planned three-core backward (SGD, or dense gradients fully overwritten) on the
+ *     virtual batch.  Same arguments as the planned calls plus info.
+ * Workspace: tt_bag_workspace_size_dedup bytes (256-byte aligned); TT_ESHAPE when T * nnz
+ * reaches 2^30 or the sort key (bits of T*E plus bits of nnz) exceeds 64 bits. */
+size_t tt_bag_workspace_size_dedup(const tt_desc *desc, int64_t nnz, int64_t num_bags);
+int tt_bag_plan_dedup(const tt_desc *desc, const int64_t *indices, int64_t nnz,
+                      const int64_t *offsets, int64_t num_bags, const float *per_sample_weights,
+                      void *ws, size_t ws_bytes, int32_t *dev_status, int64_t info[2],
+                      void *stream);
+int tt_bag_backward_sgd_dedup(const tt_desc *desc, float *const cores[3], const int64_t *indices,
+                              int64_t nnz, const int64_t *offsets, int64_t num_bags,
+                              const float *per_sample_weights, const float *grad_out, float lr,
+                              const int64_t info[2], void *ws, size_t ws_bytes,
+                              int32_t *dev_status, void *stream);
+int tt_bag_backward_grad_dedup(const tt_desc *desc, const float *const cores[3],
+                               const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                               int64_t num_bags, const float *per_sample_weights,
+                               const float *grad_out, float *const grad_cores[3],
+                               const int64_t info[2], void *ws, size_t ws_bytes,
+                               int32_t *dev_status, void *stream);
+
 /* ---------------------------------------------------------------- d-core tables
  * Tables of any number d of cores ("FBTT-Embedding" README, "Parameters": tt_p_shapes,
  * tt_q_shapes and tt_ranks are lists of one length; "Initialization": core k has shape

@@ -94,6 +94,14 @@ _SIG = {
     "tt_init_cores": (ctypes.c_int, [_P, _P, ctypes.c_int, ctypes.c_float, ctypes.c_uint64, _P]),
     "tt_factorize": (ctypes.c_int, [_I64, ctypes.c_int, _P]),
     "tt_full_weight": (ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _I64, _P, _P]),
+    "tt_bag_workspace_size_dedup": (ctypes.c_size_t, [_P, _I64, _I64]),
+    "tt_bag_plan_dedup": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _P, ctypes.c_size_t, _P, _P,
+                                         _P]),
+    "tt_bag_backward_sgd_dedup": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P,
+                                                 ctypes.c_float, _P, _P, ctypes.c_size_t, _P,
+                                                 _P]),
+    "tt_bag_backward_grad_dedup": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P, _P, _P,
+                                                  ctypes.c_size_t, _P, _P]),
     "tt_bag_workspace_size_d": (ctypes.c_size_t, [_P, _I64, _I64]),
     "tt_bag_groups_d": (ctypes.c_int, [_P, _P]),
     "tt_bag_forward_d": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P, ctypes.c_size_t,
@@ -527,6 +535,71 @@ class Cache:
             self.close()
         except Exception:
             pass
+
+
+# ------------------------------------------------------------------ backward over distinct indices
+
+def workspace_dedup(desc: TTDesc, nnz: int, num_bags: int, device=None) -> torch.Tensor:
+    n = lib().tt_bag_workspace_size_dedup(ctypes.byref(desc), int(nnz), int(num_bags))
+    if n == 0:
+        raise TTError("tt_bag_workspace_size_dedup", -2)
+    return torch.empty(int(n), dtype=torch.uint8, device=device or "cuda")
+
+
+def tt_bag_plan_dedup(desc: TTDesc, indices, offsets, num_bags: int, per_sample_weights=None,
+                      ws=None, dev_status=None, stream=None):
+    """Group the batch and its distinct indices (host-synchronous).  Returns (ws, info):
+    pass both to tt_bag_forward(planned=True) / tt_bag_backward_*_dedup."""
+    _need(indices, torch.int64, "indices")
+    _need(offsets, torch.int64, "offsets")
+    if per_sample_weights is not None:
+        _need(per_sample_weights, torch.float32, "per_sample_weights")
+    if ws is None:
+        ws = workspace_dedup(desc, indices.numel(), num_bags, indices.device)
+    _need(ws, torch.uint8, "ws")
+    if dev_status is not None:
+        _need(dev_status, torch.int32, "dev_status")
+    info = (ctypes.c_int64 * 2)()
+    rc = lib().tt_bag_plan_dedup(ctypes.byref(desc), _ptr(indices), indices.numel(),
+                                 _ptr(offsets), int(num_bags), _ptr(per_sample_weights), _ptr(ws),
+                                 ws.numel(), _ptr(dev_status), info, _stream(stream, indices))
+    _check("tt_bag_plan_dedup", rc)
+    return ws, (int(info[0]), int(info[1]))
+
+
+def _info(info):
+    return (ctypes.c_int64 * 2)(int(info[0]), int(info[1]))
+
+
+def tt_bag_backward_sgd_dedup(desc: TTDesc, cores, indices, offsets, num_bags: int, grad_out,
+                              lr: float, info, per_sample_weights=None, ws=None, dev_status=None,
+                              stream=None) -> None:
+    """In-place SGD through the backward over distinct indices (plan: tt_bag_plan_dedup)."""
+    _need(grad_out, torch.float32, "grad_out")
+    _need(ws, torch.uint8, "ws")
+    rc = lib().tt_bag_backward_sgd_dedup(ctypes.byref(desc), _cores(cores), _ptr(indices),
+                                         indices.numel(), _ptr(offsets), int(num_bags),
+                                         _ptr(per_sample_weights), _ptr(grad_out), float(lr),
+                                         _info(info), _ptr(ws), ws.numel(), _ptr(dev_status),
+                                         _stream(stream, indices))
+    _check("tt_bag_backward_sgd_dedup", rc)
+
+
+def tt_bag_backward_grad_dedup(desc: TTDesc, cores, indices, offsets, num_bags: int, grad_out,
+                               info, grad_cores=None, per_sample_weights=None, ws=None,
+                               dev_status=None, stream=None):
+    """Dense core gradients through the backward over distinct indices; returns them."""
+    _need(grad_out, torch.float32, "grad_out")
+    _need(ws, torch.uint8, "ws")
+    if grad_cores is None:
+        grad_cores = [torch.empty_like(c) for c in cores]
+    rc = lib().tt_bag_backward_grad_dedup(ctypes.byref(desc), _cores(cores), _ptr(indices),
+                                          indices.numel(), _ptr(offsets), int(num_bags),
+                                          _ptr(per_sample_weights), _ptr(grad_out),
+                                          _cores(grad_cores), _info(info), _ptr(ws), ws.numel(),
+                                          _ptr(dev_status), _stream(stream, indices))
+    _check("tt_bag_backward_grad_dedup", rc)
+    return grad_cores
 
 
 # ------------------------------------------------------------------ d-core tables

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libttbag.so")
 SOURCES = ["tt_route.hip", "tt_fwd.hip", "tt_bwd.hip", "tt_cache.hip", "tt_init.hip", "tt_full.hip",
-           "tt_dcore.hip",
+           "tt_dcore.hip", "tt_dedup.hip",
            "tt_prof.hip",
            "tt_api.hip"]
 ARCH = "gfx950"

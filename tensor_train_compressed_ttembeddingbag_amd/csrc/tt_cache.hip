@@ -305,6 +305,21 @@ hipError_t cache_compact_launch(const long long *hkeys, const int *hcnt, long lo
   return hipGetLastError();
 }
 
+// stable sort of n keys by their bits [lo, hi) (8 per pass); returns the buffer that holds
+// the result (a after an even number of passes, else b)
+unsigned long long *radix_sort64_bits(unsigned long long *a, unsigned long long *b, int n,
+                                      int *hist, int lo, int hi, hipStream_t s) {
+  const int nblk = (n + RB - 1) / RB;
+  if (nblk == 0) return a;
+  for (int shift = lo; shift < hi; shift += 8) {
+    hipLaunchKernelGGL(k_sort_hist, dim3(nblk), dim3(RT), 0, s, a, n, shift, hist, nblk);
+    hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(RT), 0, s, hist, 256 * nblk);
+    hipLaunchKernelGGL(k_sort_scatter, dim3(nblk), dim3(RT), 0, s, a, n, shift, hist, nblk, b);
+    unsigned long long *t = a; a = b; b = t;
+  }
+  return a;
+}
+
 // sorts n keys in place (a is input and output, b scratch), 64 bits
 hipError_t radix_sort64(unsigned long long *a, unsigned long long *b, int n, int *hist,
                         hipStream_t s) {

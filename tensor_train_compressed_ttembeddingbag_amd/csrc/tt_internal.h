@@ -177,6 +177,10 @@ inline void tt_launch(int id, void (*kernel)(KArgs...), dim3 grid, dim3 block, s
     hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
 }
 
+// stable LSD radix sort of n 64-bit keys by bits [lo, hi); returns a or b (the result)
+unsigned long long *radix_sort64_bits(unsigned long long *a, unsigned long long *b, int n,
+                                      int *hist, int lo, int hi, hipStream_t s);
+
 // host launchers (each kernel is launched from the file that defines it)
 hipError_t launch_route(const DevArgs &a, hipStream_t s);   // the grouping kernels
 hipError_t launch_runsum(const DevArgs &a, hipStream_t s);
