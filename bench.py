@@ -47,6 +47,9 @@ def parse():
                     help="cached workload: exact top-K or 32-way set-associative LFU")
     ap.add_argument("--update", default="sgd", choices=["sgd", "adagrad", "grad"],
                     help="backward: fused SGD, fused Adagrad (eps 1e-10), or gradients returned")
+    ap.add_argument("--dedup", action="store_true",
+                    help="backward over distinct indices (tt_bag_plan_dedup + "
+                         "tt_bag_backward_*_dedup); no cache, update sgd or grad")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle baseline (0 = skip)")
     ap.add_argument("--no-roofline", action="store_true")
@@ -133,7 +136,12 @@ def main():
     # two workspaces alternate, and events order (a) the forward of a batch after its
     # grouping and (b) a grouping after the last use of its workspace (two batches back).
     pipeline = not args.no_pipeline
-    wss = [abi.workspace(desc, max_nnz, B, csize) for _ in range(2 if pipeline else 1)]
+    if args.dedup and (cache is not None or args.update == "adagrad"):
+        print("--dedup takes no cache and updates by sgd or grad", file=sys.stderr)
+        sys.exit(2)
+    wss = [abi.workspace_dedup(desc, max_nnz, B) if args.dedup
+           else abi.workspace(desc, max_nnz, B, csize) for _ in range(2 if pipeline else 1)]
+    infos = {}
     out = torch.empty(wl.num_tables * B, wl.D, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     main = torch.cuda.current_stream()
@@ -155,8 +163,13 @@ def main():
             cache.lookup(b["indices"], slot_out=s, count_freq=True, dev_status=status,
                          stream=side)
             cv = (s, rows)
-        abi.tt_bag_plan(desc, b["indices"], b["offsets"], B, b["per_sample_weights"], cache=cv,
-                        ws=ws, dev_status=status, stream=side)
+        if args.dedup:  # host-synchronous: returns the size of the distinct-index batch
+            _, infos[i] = abi.tt_bag_plan_dedup(desc, b["indices"], b["offsets"], B,
+                                                b["per_sample_weights"], ws=ws,
+                                                dev_status=status, stream=side)
+        else:
+            abi.tt_bag_plan(desc, b["indices"], b["offsets"], B, b["per_sample_weights"],
+                            cache=cv, ws=ws, dev_status=status, stream=side)
         if pipeline:
             ev_plan[i % 2].record(side)
         return cv
@@ -177,8 +190,25 @@ def main():
             cv = plan(i)
         abi.tt_bag_forward(desc, g, b["indices"], b["offsets"], B, b["per_sample_weights"],
                            cache=cv, out=out, ws=ws, dev_status=status, planned=True)
-        if pipeline:
+        if pipeline and not args.dedup:
             cvs[i + 1] = plan(i + 1)
+        if args.dedup:
+            # the next plan waits on the host, so it is enqueued after this backward
+            info = infos.pop(i)
+            if args.update == "sgd":
+                abi.tt_bag_backward_sgd_dedup(desc, g, b["indices"], b["offsets"], B,
+                                              b["grad_out"], wl.lr, info,
+                                              per_sample_weights=b["per_sample_weights"],
+                                              ws=ws, dev_status=status)
+            else:
+                abi.tt_bag_backward_grad_dedup(desc, g, b["indices"], b["offsets"], B,
+                                               b["grad_out"], info, grad_cores=aux,
+                                               per_sample_weights=b["per_sample_weights"],
+                                               ws=ws, dev_status=status)
+            if pipeline:
+                ev_done[i % 2].record(main)
+                cvs[i + 1] = plan(i + 1)
+            return i
         if args.update == "sgd":
             abi.tt_bag_backward_sgd(desc, g, b["indices"], b["offsets"], B, b["grad_out"], wl.lr,
                                     b["per_sample_weights"], cache=cv, ws=ws, dev_status=status,
@@ -236,7 +266,8 @@ def main():
                                   wl.num_tables, B, nnz_mean, list(wl.lengths), list(wl.dist),
                                   wl.weighted, wl.lr, csize),
                    "nnz": nnz_mean, "global_batch": wl.num_tables * B,
-                   "update": args.update,
+                   "update": args.update + (" (backward over distinct indices)"
+                                            if args.dedup else ""),
                    "host_enqueue_us_per_step": round((t_enq - t0) * 1e6 / args.steps, 2),
                    "pipeline": "grouping of batch i+1 overlapped with the backward of batch i"
                                if pipeline else "none"},
@@ -320,12 +351,19 @@ def roofline(args, wl, batches, step, torch, abi, metrics, slots):
     for j, b in enumerate(batches):
         nb = b["np"]
         sl = None if slots is None else slots[j].cpu().numpy()
+        nel = int(np.sum(sl < 0)) if sl is not None else len(nb["indices"])
+        nbw = nel
+        if args.dedup:  # the backward runs one element per distinct (table, index)
+            tb = (np.searchsorted(nb["offsets"], np.arange(len(nb["indices"])), side="right")
+                  - 1) // wl.bags_per_table
+            nbw = len(np.unique(tb.astype(np.int64) * wl.E + nb["indices"]))
         per_batch.append((metrics.unique_pairs(wl.p, wl.num_tables, wl.bags_per_table,
-                                               nb["indices"], nb["offsets"], sl, wl.E),
-                          int(np.sum(sl < 0)) if sl is not None else len(nb["indices"])))
+                                               nb["indices"], nb["offsets"], sl, wl.E), nel,
+                          nbw))
     U = float(np.mean([per_batch[i % len(batches)][0] for i in done]))
     N = float(np.mean([per_batch[i % len(batches)][1] for i in done]))
-    work = {"k_bwd": metrics.bwd_kernel_flops(wl.q, wl.ranks, N, U),
+    Nb = float(np.mean([per_batch[i % len(batches)][2] for i in done]))
+    work = {"k_bwd": metrics.bwd_kernel_flops(wl.q, wl.ranks, Nb, U),
             "k_fwd": metrics.fwd_kernel_flops(wl.q, wl.ranks, N, U)}
     avg_s = kernels[dom]["avg_us"] * 1e-6
     from tensor_train_compressed_ttembeddingbag_amd import profiling
@@ -338,7 +376,7 @@ def roofline(args, wl, batches, step, torch, abi, metrics, slots):
               "frac": round(ach / PEAK_FP32_MFMA_TFLOPS, 4),
               "traffic": None if traffic is None else round(traffic),
               "work_per_launch": "%.4g flop (2*F1 per distinct (i1,i2) pair x %.1f pairs + "
-                                 "2*F2 per element x %.1f elements)" % (work[dom], U, N)
+                                 "2*F2 per element x %.1f elements)" % (work[dom], U, Nb)
               if dom == "k_bwd" else "%.4g flop (F1 x %.1f pairs + F2 x %.1f elements)"
                                      % (work[dom], U, N)}
     else:

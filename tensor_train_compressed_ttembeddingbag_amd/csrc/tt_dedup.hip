@@ -392,12 +392,14 @@ static int backward_dedup(const tt_desc *desc, float *const cores[3], const int6
   if (U > 0) {
     unsigned long long *sk = sorted_keys(P, ws);
     float *frag = at<float>(ws, P.o_frag);
-    hipLaunchKernelGGL(k_dd_frag, dim3((P.nnz + DD_CH - 1) / DD_CH), dim3(DD_T), 0, s, sk, P.nnz,
-                       P.pbits, P.inv, at<int>(ws, P.o_bag), offsets, psw,
-                       desc->pooling == TT_POOL_MEAN ? 1 : 0, grad_out, P.D, frag);
-    hipLaunchKernelGGL(k_dd_gu, dim3((unsigned)U), dim3(DD_T), 0, s, at<int>(ws, P.o_rs),
-                       at<int>(ws, P.o_re), at<int>(ws, P.o_rtab), at<int64_t>(ws, P.o_Rt),
-                       (int)Bp, P.D, (const float *)frag, Gu);
+    tt_launch(K_DD_FRAG, k_dd_frag, dim3((P.nnz + DD_CH - 1) / DD_CH), dim3(DD_T), 0, s,
+              (const unsigned long long *)sk, P.nnz, P.pbits, P.inv,
+              (const int *)at<int>(ws, P.o_bag), offsets, psw,
+              desc->pooling == TT_POOL_MEAN ? 1 : 0, grad_out, P.D, frag);
+    tt_launch(K_DD_GU, k_dd_gu, dim3((unsigned)U), dim3(DD_T), 0, s,
+              (const int *)at<int>(ws, P.o_rs), (const int *)at<int>(ws, P.o_re),
+              (const int *)at<int>(ws, P.o_rtab), (const int64_t *)at<int64_t>(ws, P.o_Rt),
+              (int)Bp, P.D, (const float *)frag, Gu);
     if (hipGetLastError() != hipSuccess) return TT_EHIP;
   }
   const int64_t vb = Bp > 0 ? Bp : 1;
