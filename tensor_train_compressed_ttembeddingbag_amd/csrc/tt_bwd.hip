@@ -59,24 +59,26 @@ size_t bwd_lds_bytes(int RP, int JB, int P, int q3, int D, int nred) {
   }
 }
 
-// two workgroups per CU need <= 128 VGPRs (rank-64 tiles take one CU each)
-template <int RP>
+// two workgroups per CU need <= 128 VGPRs (rank-64 tiles take one CU each).  Q3 = 4
+// fixes q3 at compile time (each item's G3 / dG3 rows of four j3 move as 16-byte LDS
+// vectors); Q3 = 0 reads it from the arguments.
+template <int RP, int Q3>
 __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(RP == 64 ? 2 : 4)))
 void k_bwd(DevArgs a) {
   constexpr int KS = RP / 4, NM = RP / 16, LD = BwdLds<RP>::LD, LRP = log2_rp<RP>();
-  constexpr int JU = 2;  // j3 per batch of the item loop (register budget)
+  constexpr int JU = 2;  // j3 per batch of the item loop with a runtime q3 (register budget)
   extern __shared__ float4 smem4[];
   float *smem = (float *)smem4;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
-  const int q1 = a.q1, q2 = a.q2, q3 = a.q3, R1 = a.R1, R2 = a.R2, D = a.D;
+  const int q1 = a.q1, q2 = a.q2, q3 = Q3 ? Q3 : a.q3, R1 = a.R1, R2 = a.R2, D = a.D;
   const int JB = a.JBb, P = a.P, nred = a.NRED;
   float *sG2 = smem;                                              // [JB][r2 < RP][LD]
   float *sRed = sG2 + (size_t)JB * RP * LD;                       // slots / dT tiles / w*dY
   float *sT = sRed;
   float *sYe = sRed;
   float *sGu = sRed + BwdLds<RP>::red_floats(nred, P, D);         // [item][D]
-  float *sG3 = sGu + (size_t)P * D;                               // [item][j3][r2 < RP]
-  float *sdA3 = sG3 + (size_t)P * q3 * RP;                        // [item][j3][r2 < RP]
+  float *sG3 = sGu + (size_t)P * D;                               // [item][r2 < RP][j3]
+  float *sdA3 = sG3 + (size_t)P * q3 * RP;                        // [item][r2 < RP][j3]
   int *e_bag = (int *)(sdA3 + (size_t)P * q3 * RP);               // [64]
   float *e_w = (float *)(e_bag + 64);                             // [64]
   int *it_i3 = (int *)(e_w + 64);                                 // [64]
@@ -192,11 +194,18 @@ void k_bwd(DevArgs a) {
   // operand layouts, w * dY rows of the elements.  First batches of everything are
   // issued before the first wait.
   const int per_item = RP * q3, total3 = nI * per_item, totalY = n_el * D;
-  auto load3 = [&](int base, float *v) {  // i = (item * q3 + j3) * RP + r2
+  // i = (item * RP + r2) * q3 + j3 -> (item * RP + r2, j3)
+  auto split3 = [&](int i, int &jr, int &j3) {
+    jr = Q3 ? i / Q3 : fdiv(i, a.mq3);
+    j3 = i - jr * q3;
+  };
+  auto load3 = [&](int base, float *v) {
 #pragma unroll
     for (int u = 0; u < STAGE_U; ++u) {
       const int i = min(base + u * WG, total3 - 1);
-      const int jr = i >> LRP, it = fdiv(jr, a.mq3), j3 = jr - it * q3, r2 = i & (RP - 1);
+      int jr, j3;
+      split3(i, jr, j3);
+      const int it = jr >> LRP, r2 = jr & (RP - 1);
       v[u] = G3t[it_i3[it] * (int)W3 + (r2 < R2 ? r2 : 0) * q3 + j3];
     }
   };
@@ -205,7 +214,9 @@ void k_bwd(DevArgs a) {
     for (int u = 0; u < STAGE_U; ++u) {
       const int i = base + u * WG;
       if (i < total3) {
-        sG3[i] = (i & (RP - 1)) < R2 ? v[u] : 0.f;
+        int jr, j3;
+        split3(i, jr, j3);
+        sG3[i] = (jr & (RP - 1)) < R2 ? v[u] : 0.f;
         sdA3[i] = 0.f;
       }
     }
@@ -333,9 +344,36 @@ void k_bwd(DevArgs a) {
           const bool act = it < ie;
           const int itc = act ? it : 0;
           const int pr = act ? it_pair[itc] : -1;
-          const float *g3 = sG3 + (size_t)itc * per_item + c;
+          const float *g3 = sG3 + (size_t)itc * per_item + c * q3;  // + 16 m q3 + j3
           const float *gu = sGu + (size_t)itc * D;
-          float *da3 = sdA3 + (size_t)itc * per_item + c;
+          float *da3 = sdA3 + (size_t)itc * per_item + c * q3;
+          if (Q3 == 4) {
+            // all four j3 at once: G_u of the four rows, the item's G3 and dG3 rows as
+            // 16-byte vectors (every offset here is a multiple of four floats)
+            float4 gx[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              gx[v] = *(const float4 *)&gu[(j1v[v] * q2 + j2) * 4];
+              if (!(act && prv[v] == pr)) gx[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {  // one column block's G3 / dG3 vectors live
+              const float4 a3 = *(const float4 *)&g3[64 * m];
+              float4 d3 = *(const float4 *)&da3[64 * m];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                float sacc = 0.f;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                  sacc += T[m][v] * gx[v][u];
+                  dT[m][v] += gx[v][u] * a3[u];
+                }
+                d3[u] += sacc;
+              }
+              if (act) *(float4 *)&da3[64 * m] = d3;
+            }
+            continue;
+          }
           // JU j3 at a time: all LDS reads of the block first, then the arithmetic,
           // then the updated dG3 partials (one writer lane per element)
           for (int j30 = 0; j30 < q3; j30 += JU) {
@@ -347,8 +385,8 @@ void k_bwd(DevArgs a) {
               for (int v = 0; v < 4; ++v) gx[u][v] = gu[((j1v[v]) * q2 + j2) * q3 + j3];
 #pragma unroll
               for (int m = 0; m < NM; ++m) {
-                a3[u][m] = g3[j3 * RP + 16 * m];
-                d3[u][m] = da3[j3 * RP + 16 * m];
+                a3[u][m] = g3[16 * m * q3 + j3];
+                d3[u][m] = da3[16 * m * q3 + j3];
               }
             }
 #pragma unroll
@@ -372,7 +410,7 @@ void k_bwd(DevArgs a) {
             for (int u = 0; u < JU; ++u)
               if (act && j30 + u < q3)
 #pragma unroll
-                for (int m = 0; m < NM; ++m) da3[(j30 + u) * RP + 16 * m] = d3[u][m];
+                for (int m = 0; m < NM; ++m) da3[16 * m * q3 + j30 + u] = d3[u][m];
           }
         }
         // dG2 += A1^T dT   (K = the 16 rows; lane group g feeds rows 4g + sr)
@@ -444,30 +482,37 @@ void k_bwd(DevArgs a) {
         }
     }
   }
-  for (int i = tid; i < total3; i += WG) {  // i = (item * q3 + j3) * RP + r2
-    const int jr = i >> LRP, it = fdiv(jr, a.mq3), j3 = jr - it * q3, r2 = i & (RP - 1);
+  for (int i = tid; i < total3; i += WG) {  // i = (item * RP + r2) * q3 + j3
+    int jr, j3;
+    split3(i, jr, j3);
+    const int it = jr >> LRP, r2 = jr & (RP - 1);
     if (r2 < R2) a.part3[(size_t)(s0 + it_first[it]) * W3 + r2 * q3 + j3] = sdA3[i];
   }
 }
 
-template <int RP>
+template <int RP, int Q3>
 static hipError_t launch_bwd_t(const DevArgs &a, size_t lds, hipStream_t s) {
   static bool attr_set = false;  // dynamic LDS above 64 KiB is opt-in per kernel
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void *)k_bwd<RP>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              160 * 1024);
+    (void)hipFuncSetAttribute((const void *)k_bwd<RP, Q3>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr_set = true;
   }
-  tt_launch(K_BWD, k_bwd<RP>, dim3(items_max(a)), dim3(WG), lds, s, a);
+  tt_launch(K_BWD, k_bwd<RP, Q3>, dim3(items_max(a)), dim3(WG), lds, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const DevArgs &a, int RP, size_t lds, hipStream_t s) {
+template <int Q3>
+static hipError_t launch_bwd_q(const DevArgs &a, int RP, size_t lds, hipStream_t s) {
   switch (RP) {
-    case 16: return launch_bwd_t<16>(a, lds, s);
-    case 32: return launch_bwd_t<32>(a, lds, s);
-    default: return launch_bwd_t<64>(a, lds, s);
+    case 16: return launch_bwd_t<16, Q3>(a, lds, s);
+    case 32: return launch_bwd_t<32, Q3>(a, lds, s);
+    default: return launch_bwd_t<64, Q3>(a, lds, s);
   }
+}
+
+hipError_t launch_bwd(const DevArgs &a, int RP, size_t lds, hipStream_t s) {
+  return a.q3 == 4 ? launch_bwd_q<4>(a, RP, lds, s) : launch_bwd_q<0>(a, RP, lds, s);
 }
 
 // ---------------------------------------------------------------- k_seg

@@ -216,20 +216,54 @@ __global__ __launch_bounds__(DD_T) void k_dd_frag(const unsigned long long *__re
   }
 }
 
-// pass 2: each run's pieces in sorted order -> the grad_out row of its virtual bag
+// pass 2: each run's pieces in sorted order -> the grad_out row of its virtual bag.  A
+// run's pieces start at its first position and then at every chunk boundary inside it.
+// NG = DD_T / D groups of D threads (one group when D >= DD_T) take contiguous ranges of
+// the pieces, eight loads in flight, and the group sums are added in group order.
 __global__ __launch_bounds__(DD_T) void k_dd_gu(const int *__restrict__ rstart,
                                                 const int *__restrict__ rend,
                                                 const int *__restrict__ rtab,
                                                 const int64_t *__restrict__ Rt, int Bp, int D,
                                                 const float *__restrict__ frag,
                                                 float *__restrict__ Gu) {
+  __shared__ float s_part[DD_T];
   const int u = blockIdx.x;
   const int a = rstart[u], z = rend[u], t = rtab[u];
   const long long vb = (long long)t * Bp + (u - Rt[t]);
-  for (int d = threadIdx.x; d < D; d += DD_T) {
+  const int c0 = a / DD_CH, nf = (z - 1) / DD_CH - c0 + 1;
+  const int NG = D < DD_T ? DD_T / D : 1;
+  const int g = D < DD_T ? (int)threadIdx.x / D : 0;
+  const int per = (nf + NG - 1) / NG;
+  const int k0 = min(nf, g * per), k1 = min(nf, k0 + per);
+  for (int d0 = 0; d0 < D; d0 += DD_T) {  // more than one pass only when D > DD_T
+    const int d = D < DD_T ? (int)threadIdx.x - g * D : d0 + (int)threadIdx.x;
+    const bool act = g < NG && d < D;
     float acc = 0.f;
-    for (int f = a; f < z; f = min(z, (f / DD_CH + 1) * DD_CH)) acc += frag[(size_t)f * D + d];
-    Gu[vb * D + d] = acc;
+    if (act) {
+      int k = k0;
+      for (; k + 8 <= k1; k += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int f = (k + j == 0) ? a : (c0 + k + j) * DD_CH;
+          v[j] = frag[(size_t)f * D + d];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc += v[j];
+      }
+      for (; k < k1; ++k) acc += frag[(size_t)(k == 0 ? a : (c0 + k) * DD_CH) * D + d];
+    }
+    if (NG > 1) {
+      if (act) s_part[threadIdx.x] = acc;
+      __syncthreads();
+      if (g == 0 && act) {
+        float tot = 0.f;
+        for (int x = 0; x < NG; ++x) tot += s_part[x * D + d];
+        Gu[vb * D + d] = tot;
+      }
+    } else if (act) {
+      Gu[vb * D + d] = acc;
+    }
   }
 }
 
