@@ -326,12 +326,33 @@ def main():
         res["config"]["cache_policy"] = args.cache_policy
         res["config"]["populate_ms"] = round(populate_ms, 3)
 
+    res["config"]["step_us_percentiles"] = step_percentiles(step, min(args.steps, 400), torch)
     if not args.no_roofline:
         res["roofline"], res["kernels"] = roofline(args, wl, batches, step, torch, abi, metrics,
                                                    None if cache is None else slots)
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(wl, cores, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def step_percentiles(step, n, torch, window=10):
+    """p10 / p50 / p90 of the step time in a separate pass of n steps, each sample the mean
+    over a window of `window` consecutive steps: an event on the main stream at every
+    window boundary (one event per step would add enough host work per step to make the
+    loop wait on the host)."""
+    main = torch.cuda.current_stream()
+    nw = max(1, n // window)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nw + 1)]
+    for k in range(nw * window):
+        if k % window == 0:
+            evs[k // window].record(main)
+        step(k)
+    evs[nw].record(main)
+    torch.cuda.synchronize()
+    t = np.array([evs[k].elapsed_time(evs[k + 1]) * 1e3 / window for k in range(nw)])
+    return {"p10": round(float(np.percentile(t, 10)), 2),
+            "p50": round(float(np.percentile(t, 50)), 2),
+            "p90": round(float(np.percentile(t, 90)), 2), "windows": nw, "window_steps": window}
 
 
 def roofline(args, wl, batches, step, torch, abi, metrics, slots):

@@ -19,7 +19,10 @@
  * Conventions for every entry point
  *  - Pointers are DEVICE pointers unless the comment says host.  `stream` is a
  *    hipStream_t (NULL = the default stream).  Every call is asynchronous on
- *    `stream` and does not synchronise the host, except tt_cache_populate.
+ *    `stream` and does not synchronise the host, except tt_cache_populate and
+ *    tt_bag_plan_dedup (which read a size back).  Calls must not be captured
+ *    into a HIP graph: each launch carries a per-call tag for its grid-wide
+ *    flags and counters, and a replayed graph would repeat it.
  *  - Ownership: the caller owns every buffer it passes, including the workspace.
  *    The library allocates device memory only inside tt_cache_create and frees it
  *    only in tt_cache_destroy; it keeps no caller pointer between calls.

@@ -4,6 +4,12 @@
         --title T --command C
         per-kernel table of a `rocprofv3 --kernel-trace --stats --output-format csv` run
 
+    python -m tensor_train_compressed_ttembeddingbag_amd.profiling mfma DIR --trace TDIR \
+        --kernels k_fwd,k_bwd --out FILE.txt --command C --trace-command C
+        executed fp32 MFMA work per launch from SQ_INSTS_VALU_MFMA_F32 (16x16x4 f32:
+        2048 flop per instruction) and SQ_INSTS_VALU_MFMA_MOPS_F32 (512 flop per unit),
+        over the kernel's average duration in a separate --kernel-trace --stats run
+
     python -m tensor_train_compressed_ttembeddingbag_amd.profiling traffic \
         --kernel k_bwd --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \
         --copy-bytes N --out FILE.txt --command-fetch C --command-write C
@@ -154,6 +160,40 @@ def cmd_traffic(a):
     print("\n".join(lines))
 
 
+PEAK_FP32_MFMA_TFLOPS = 157.3
+
+
+def cmd_mfma(a):
+    m = counter_means(a.dir)
+    durs = {}
+    for n, c, t, av, p in kernel_stats(a.trace):
+        k = _short(n)
+        if k not in durs or c > durs[k][1]:
+            durs[k] = (av, c)
+    lines = ["command=%s" % a.command, "trace_command=%s" % a.trace_command]
+    for kern in a.kernels.split(","):
+        cs = _match(m, kern)
+        dk = [k for k in durs if k == kern or k.startswith(kern + "<")]
+        dk = max(dk, key=lambda k: durs[k][1])
+        us = durs[dk][0]
+        inst = cs.get("SQ_INSTS_VALU_MFMA_F32", float("nan"))
+        mops = cs.get("SQ_INSTS_VALU_MFMA_MOPS_F32", float("nan"))
+        lines += ["kernel=%s" % dk,
+                  "avg_us=%.3f" % us,
+                  "mfma_f32_insts_per_launch=%.0f" % inst,
+                  "mfma_mops_f32_per_launch=%.0f" % mops,
+                  "executed_flop_from_insts=%.4g" % (inst * 2048.0),
+                  "executed_flop_from_mops=%.4g" % (mops * 512.0),
+                  "executed_tflops=%.3f" % (inst * 2048.0 / (us * 1e-6) / 1e12),
+                  "executed_frac_of_fp32_mfma_peak=%.4f"
+                  % (inst * 2048.0 / (us * 1e-6) / 1e12 / PEAK_FP32_MFMA_TFLOPS)]
+        for c in sorted(cs):
+            lines.append("%s=%.6g" % (c, cs[c]))
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def read_traffic(path: str, kernel: str):
     """Bytes per launch of `kernel` from a traffic file, or None when the file is
     missing, names another kernel, or was measured on other sources."""
@@ -185,12 +225,18 @@ def main(argv=None):
               "command-write", "command-copy-fetch", "command-copy-write"):
         t.add_argument("--" + k, required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
+    mm = sub.add_parser("mfma")
+    mm.add_argument("dir")
+    for k in ("trace", "kernels", "out", "command", "trace-command"):
+        mm.add_argument("--" + k, required=True)
     sub.add_parser("digest")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         cmd_stats(a)
     elif a.cmd == "traffic":
         cmd_traffic(a)
+    elif a.cmd == "mfma":
+        cmd_mfma(a)
     else:
         print(source_digest())
 
