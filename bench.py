@@ -89,6 +89,7 @@ def main():
 
     import torch
     from tensor_train_compressed_ttembeddingbag_amd import abi, metrics, workloads as W
+    from tensor_train_compressed_ttembeddingbag_amd.loop import TrainLoop
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -109,7 +110,7 @@ def main():
     batches = [_dev(W.make_batch(wl, k), torch) for k in range(args.batches)]
     max_nnz = max(b["indices"].numel() for b in batches)
     B = wl.bags_per_table
-    cache = None
+    cache = rows = slots = aux = aux_rows = None
     csize = 0
     if wl.cache_size:
         policy = abi.TT_CACHE_LFU32 if args.cache_policy == "lfu32" else abi.TT_CACHE_TOPK
@@ -130,102 +131,20 @@ def main():
     elif args.update == "grad":  # gradient outputs
         aux = [torch.empty_like(x) for x in g]
         aux_rows = torch.empty_like(rows) if cache is not None else None
-    # Training loop.  Every batch is grouped (tt_bag_plan), then runs forward and backward
-    # with the plan.  Pipelined (default): the grouping of batch i+1 is enqueued on a second
-    # stream right after the forward of batch i, so it overlaps the backward of batch i;
-    # two workspaces alternate, and events order (a) the forward of a batch after its
-    # grouping and (b) a grouping after the last use of its workspace (two batches back).
+    # Training loop (loop.TrainLoop): every batch grouped, then the planned forward and
+    # backward; by default the grouping of batch i+1 overlaps the backward of batch i.
     pipeline = not args.no_pipeline
     if args.dedup and (cache is not None or args.update == "adagrad"):
         print("--dedup takes no cache and updates by sgd or grad", file=sys.stderr)
         sys.exit(2)
-    wss = [abi.workspace_dedup(desc, max_nnz, B) if args.dedup
-           else abi.workspace(desc, max_nnz, B, csize) for _ in range(2 if pipeline else 1)]
-    infos = {}
     out = torch.empty(wl.num_tables * B, wl.D, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    main = torch.cuda.current_stream()
-    side = torch.cuda.Stream() if pipeline else main  # default priority
-    ev_plan = [torch.cuda.Event() for _ in range(2)]
-    ev_done = [torch.cuda.Event() for _ in range(2)]
-    for e in ev_done:
-        e.record(main)
-    seq = {"next": 0}
-
-    def plan(i):
-        b = batches[i % len(batches)]
-        ws = wss[i % len(wss)]
-        cv = None
-        if pipeline:
-            side.wait_event(ev_done[i % 2])
-        if cache is not None:
-            s = slots[i % len(batches)]
-            cache.lookup(b["indices"], slot_out=s, count_freq=True, dev_status=status,
-                         stream=side)
-            cv = (s, rows)
-        if args.dedup:  # host-synchronous: returns the size of the distinct-index batch
-            _, infos[i] = abi.tt_bag_plan_dedup(desc, b["indices"], b["offsets"], B,
-                                                b["per_sample_weights"], ws=ws,
-                                                dev_status=status, stream=side)
-        else:
-            abi.tt_bag_plan(desc, b["indices"], b["offsets"], B, b["per_sample_weights"],
-                            cache=cv, ws=ws, dev_status=status, stream=side)
-        if pipeline:
-            ev_plan[i % 2].record(side)
-        return cv
-
-    cvs = {}
-    if pipeline:
-        cvs[0] = plan(0)
+    loop = TrainLoop(desc, g, batches, B, wl.lr, out, status, update=args.update, aux=aux,
+                     aux_rows=aux_rows, cache=cache, rows=rows, slots=slots, dedup=args.dedup,
+                     pipeline=pipeline)
 
     def step(_):
-        i = seq["next"]
-        seq["next"] += 1
-        b = batches[i % len(batches)]
-        ws = wss[i % len(wss)]
-        if pipeline:
-            main.wait_event(ev_plan[i % 2])
-            cv = cvs.pop(i)
-        else:
-            cv = plan(i)
-        abi.tt_bag_forward(desc, g, b["indices"], b["offsets"], B, b["per_sample_weights"],
-                           cache=cv, out=out, ws=ws, dev_status=status, planned=True)
-        if pipeline and not args.dedup:
-            cvs[i + 1] = plan(i + 1)
-        if args.dedup:
-            # the next plan waits on the host, so it is enqueued after this backward
-            info = infos.pop(i)
-            if args.update == "sgd":
-                abi.tt_bag_backward_sgd_dedup(desc, g, b["indices"], b["offsets"], B,
-                                              b["grad_out"], wl.lr, info,
-                                              per_sample_weights=b["per_sample_weights"],
-                                              ws=ws, dev_status=status)
-            else:
-                abi.tt_bag_backward_grad_dedup(desc, g, b["indices"], b["offsets"], B,
-                                               b["grad_out"], info, grad_cores=aux,
-                                               per_sample_weights=b["per_sample_weights"],
-                                               ws=ws, dev_status=status)
-            if pipeline:
-                ev_done[i % 2].record(main)
-                cvs[i + 1] = plan(i + 1)
-            return i
-        if args.update == "sgd":
-            abi.tt_bag_backward_sgd(desc, g, b["indices"], b["offsets"], B, b["grad_out"], wl.lr,
-                                    b["per_sample_weights"], cache=cv, ws=ws, dev_status=status,
-                                    planned=True)
-        elif args.update == "adagrad":
-            abi.tt_bag_backward_adagrad(desc, g, b["indices"], b["offsets"], B, b["grad_out"],
-                                        wl.lr, 1e-10, aux, state_rows=aux_rows,
-                                        per_sample_weights=b["per_sample_weights"], cache=cv,
-                                        ws=ws, dev_status=status, planned=True)
-        else:
-            abi.tt_bag_backward_grad(desc, g, b["indices"], b["offsets"], B, b["grad_out"],
-                                     grad_cores=aux, grad_rows=aux_rows,
-                                     per_sample_weights=b["per_sample_weights"], cache=cv,
-                                     ws=ws, dev_status=status, planned=True)
-        if pipeline:
-            ev_done[i % 2].record(main)
-        return i
+        return loop.step()
 
     for i in range(args.warmup):
         step(i)

@@ -1,0 +1,132 @@
+"""The training loop that bench.py times, as a reusable object (the parity tests run the
+same object, so the launch configuration they check is the one the benchmark measures).
+
+Every batch is grouped (tt_bag_plan, or tt_bag_plan_dedup for the backward over distinct
+indices), then runs the planned forward and the planned backward.  Pipelined (default):
+the grouping of batch i+1 is enqueued on a second stream right after the forward of batch
+i (after the backward with the distinct-index plan, which waits on the host), so it
+overlaps the backward of batch i; two workspaces alternate, and events order (a) the
+forward of a batch after its grouping and (b) a grouping after the last use of its
+workspace (two batches back).  With a cache, the lookup of a batch runs on the grouping
+stream just before its grouping.  Argument marshalling only: every step runs in libttbag.
+"""
+from __future__ import annotations
+
+from typing import List
+
+import torch
+
+from . import abi
+
+
+class TrainLoop:
+    """step() enqueues one training step of the next batch (batches are cycled) and
+    returns its index.  batches: dicts with device tensors "indices", "offsets",
+    "grad_out", "per_sample_weights" (or None).  update: "sgd" (fused SGD, lr), "adagrad"
+    (fused Adagrad with eps 1e-10; aux / aux_rows hold the running sums) or "grad"
+    (gradients written to aux / aux_rows).  cache: an abi.Cache with its rows and one
+    slot buffer per batch.  out receives the pooled forward of the step."""
+
+    def __init__(self, desc, cores: List[torch.Tensor], batches, num_bags: int, lr: float,
+                 out: torch.Tensor, status: torch.Tensor, update: str = "sgd", aux=None,
+                 aux_rows=None, cache=None, rows=None, slots=None, dedup: bool = False,
+                 pipeline: bool = True):
+        if dedup and (cache is not None or update == "adagrad"):
+            raise ValueError("the backward over distinct indices takes no cache and updates "
+                             "by sgd or grad")
+        if update not in ("sgd", "adagrad", "grad"):
+            raise ValueError("update must be sgd, adagrad or grad")
+        self.desc, self.g, self.batches, self.B, self.lr = desc, cores, batches, num_bags, lr
+        self.out, self.status, self.update = out, status, update
+        self.aux, self.aux_rows = aux, aux_rows
+        self.cache, self.rows, self.slots = cache, rows, slots
+        self.dedup, self.pipeline = dedup, pipeline
+        max_nnz = max(b["indices"].numel() for b in batches)
+        csize = cache.cache_size if cache is not None else 0
+        self.wss = [abi.workspace_dedup(desc, max_nnz, num_bags) if dedup
+                    else abi.workspace(desc, max_nnz, num_bags, csize)
+                    for _ in range(2 if pipeline else 1)]
+        self.main = torch.cuda.current_stream()
+        self.side = torch.cuda.Stream() if pipeline else self.main  # default priority
+        self.ev_plan = [torch.cuda.Event() for _ in range(2)]
+        self.ev_done = [torch.cuda.Event() for _ in range(2)]
+        for e in self.ev_done:
+            e.record(self.main)
+        self.next = 0
+        self.cvs = {}
+        self.infos = {}
+        if pipeline:
+            self.cvs[0] = self._plan(0)
+
+    def _plan(self, i: int):
+        b = self.batches[i % len(self.batches)]
+        ws = self.wss[i % len(self.wss)]
+        cv = None
+        if self.pipeline:
+            self.side.wait_event(self.ev_done[i % 2])
+        if self.cache is not None:
+            s = self.slots[i % len(self.batches)]
+            self.cache.lookup(b["indices"], slot_out=s, count_freq=True, dev_status=self.status,
+                              stream=self.side)
+            cv = (s, self.rows)
+        if self.dedup:  # host-synchronous: returns the size of the distinct-index batch
+            _, self.infos[i] = abi.tt_bag_plan_dedup(self.desc, b["indices"], b["offsets"], self.B,
+                                                     b["per_sample_weights"], ws=ws,
+                                                     dev_status=self.status, stream=self.side)
+        else:
+            abi.tt_bag_plan(self.desc, b["indices"], b["offsets"], self.B,
+                            b["per_sample_weights"], cache=cv, ws=ws, dev_status=self.status,
+                            stream=self.side)
+        if self.pipeline:
+            self.ev_plan[i % 2].record(self.side)
+        return cv
+
+    def step(self) -> int:
+        i = self.next
+        self.next += 1
+        b = self.batches[i % len(self.batches)]
+        ws = self.wss[i % len(self.wss)]
+        if self.pipeline:
+            self.main.wait_event(self.ev_plan[i % 2])
+            cv = self.cvs.pop(i)
+        else:
+            cv = self._plan(i)
+        w = b["per_sample_weights"]
+        abi.tt_bag_forward(self.desc, self.g, b["indices"], b["offsets"], self.B, w, cache=cv,
+                           out=self.out, ws=ws, dev_status=self.status, planned=True)
+        if self.dedup:
+            # the next plan waits on the host, so it is enqueued after this backward
+            info = self.infos.pop(i)
+            if self.update == "sgd":
+                abi.tt_bag_backward_sgd_dedup(self.desc, self.g, b["indices"], b["offsets"],
+                                              self.B, b["grad_out"], self.lr, info,
+                                              per_sample_weights=w, ws=ws,
+                                              dev_status=self.status)
+            else:
+                abi.tt_bag_backward_grad_dedup(self.desc, self.g, b["indices"], b["offsets"],
+                                               self.B, b["grad_out"], info, grad_cores=self.aux,
+                                               per_sample_weights=w, ws=ws,
+                                               dev_status=self.status)
+            if self.pipeline:
+                self.ev_done[i % 2].record(self.main)
+                self.cvs[i + 1] = self._plan(i + 1)
+            return i
+        if self.pipeline:
+            self.cvs[i + 1] = self._plan(i + 1)
+        if self.update == "sgd":
+            abi.tt_bag_backward_sgd(self.desc, self.g, b["indices"], b["offsets"], self.B,
+                                    b["grad_out"], self.lr, w, cache=cv, ws=ws,
+                                    dev_status=self.status, planned=True)
+        elif self.update == "adagrad":
+            abi.tt_bag_backward_adagrad(self.desc, self.g, b["indices"], b["offsets"], self.B,
+                                        b["grad_out"], self.lr, 1e-10, self.aux,
+                                        state_rows=self.aux_rows, per_sample_weights=w,
+                                        cache=cv, ws=ws, dev_status=self.status, planned=True)
+        else:
+            abi.tt_bag_backward_grad(self.desc, self.g, b["indices"], b["offsets"], self.B,
+                                     b["grad_out"], grad_cores=self.aux, grad_rows=self.aux_rows,
+                                     per_sample_weights=w, cache=cv, ws=ws,
+                                     dev_status=self.status, planned=True)
+        if self.pipeline:
+            self.ev_done[i % 2].record(self.main)
+        return i
