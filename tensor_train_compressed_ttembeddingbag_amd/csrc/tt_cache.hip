@@ -122,8 +122,9 @@ __global__ __launch_bounds__(RT) void k_sort_hist(const unsigned long long *keys
 }
 
 // ... one-block exclusive scan ...
-__global__ __launch_bounds__(RT) void k_sort_scan(int *hist, int len) {
-  __shared__ int s[RT + 1];
+constexpr int SCAN_T = 1024;  // the histogram scan: one block, a short run per thread
+__global__ __launch_bounds__(SCAN_T) void k_sort_scan(int *hist, int len) {
+  __shared__ int s[SCAN_T / 64 + 1];
   block_exclusive_scan(hist, len, s);
 }
 
@@ -313,7 +314,7 @@ unsigned long long *radix_sort64_bits(unsigned long long *a, unsigned long long 
   if (nblk == 0) return a;
   for (int shift = lo; shift < hi; shift += 8) {
     hipLaunchKernelGGL(k_sort_hist, dim3(nblk), dim3(RT), 0, s, a, n, shift, hist, nblk);
-    hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(RT), 0, s, hist, 256 * nblk);
+    hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(SCAN_T), 0, s, hist, 256 * nblk);
     hipLaunchKernelGGL(k_sort_scatter, dim3(nblk), dim3(RT), 0, s, a, n, shift, hist, nblk, b);
     unsigned long long *t = a; a = b; b = t;
   }
@@ -327,7 +328,7 @@ hipError_t radix_sort64(unsigned long long *a, unsigned long long *b, int n, int
   if (nblk == 0) return hipSuccess;
   for (int shift = 0; shift < 64; shift += 8) {
     hipLaunchKernelGGL(k_sort_hist, dim3(nblk), dim3(RT), 0, s, a, n, shift, hist, nblk);
-    hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(RT), 0, s, hist, 256 * nblk);
+    hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(SCAN_T), 0, s, hist, 256 * nblk);
     hipLaunchKernelGGL(k_sort_scatter, dim3(nblk), dim3(RT), 0, s, a, n, shift, hist, nblk, b);
     unsigned long long *t = a; a = b; b = t;
   }
