@@ -89,6 +89,12 @@ SMALL = [
     # D = 1024: rows too wide to keep a work item's rows in LDS (pooled directly)
     W.custom("wide D=1024", p=(5, 6, 7), q=(4, 16, 16), ranks=(24, 20), bags_per_table=16,
              lengths=("uniform", 1, 6), init_std=0.3, lr=0.02, weighted=True),
+    # D = 512, q3 = 8: work items of 16 positions (the backward's LDS plan shrinks them)
+    W.custom("D=512 P=16", p=(5, 6, 7), q=(4, 16, 8), ranks=(32, 32), bags_per_table=16,
+             lengths=("uniform", 0, 7), init_std=0.2, lr=0.02, weighted=True),
+    # rank 64 with D = 512: the largest ranks, work items of 8 positions
+    W.custom("r=64 D=512 P=8", p=(4, 5, 6), q=(4, 8, 16), ranks=(64, 64), bags_per_table=12,
+             lengths=("uniform", 1, 6), init_std=0.12, lr=0.02),
 ]
 
 
