@@ -208,11 +208,13 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
   // G3 batch and all G1 loads are issued before the first wait; rows past the pairs
   // read a valid row and are zeroed afterwards.
   const int per_item = RP * q3, total3 = nI * per_item;
-  auto load3 = [&](int base, float *v) {  // i = (item * q3 + j3) * RP + r2
+  // element i = (item * RP + r2) * q3 + j3: contiguous in the global slice [r2][j3],
+  // stored to LDS at (item * q3 + j3) * RP + r2
+  auto load3 = [&](int base, float *v) {
 #pragma unroll
     for (int u = 0; u < STAGE_U; ++u) {
       const int i = min(base + u * WG, total3 - 1);
-      const int jr = i >> LRP, it = fdiv(jr, a.mq3), j3 = jr - it * q3, r2 = i & (RP - 1);
+      const int jr = fdiv(i, a.mq3), j3 = i - jr * q3, it = jr >> LRP, r2 = jr & (RP - 1);
       v[u] = G3t[it_i3[it] * (int)W3 + (r2 < R2 ? r2 : 0) * q3 + j3];
     }
   };
@@ -220,7 +222,10 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
 #pragma unroll
     for (int u = 0; u < STAGE_U; ++u) {
       const int i = base + u * WG;
-      if (i < total3) sG3[i] = (i & (RP - 1)) < R2 ? v[u] : 0.f;
+      if (i < total3) {
+        const int jr = fdiv(i, a.mq3), j3 = i - jr * q3, it = jr >> LRP, r2 = jr & (RP - 1);
+        sG3[(it * q3 + j3) * RP + r2] = r2 < R2 ? v[u] : 0.f;
+      }
     }
   };
   float v3[STAGE_U];
