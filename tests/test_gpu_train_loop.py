@@ -9,31 +9,9 @@ import torch
 import oracle
 from tensor_train_compressed_ttembeddingbag_amd import abi, workloads as W
 from tensor_train_compressed_ttembeddingbag_amd.loop import TrainLoop
-from helpers import TOL, rel_err
+from helpers import TOL, gpu_cores, host_cores, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
-
-
-def _dev(batch):
-    d = {k: torch.from_numpy(batch[k]).cuda() for k in ("indices", "offsets", "grad_out")}
-    w = batch["per_sample_weights"]
-    d["per_sample_weights"] = None if w is None else torch.from_numpy(w).cuda()
-    return d
-
-
-def _tables(flat, wl):
-    """Device cores (core k of every table, slice-major, concatenated) -> T lists of three
-    logical-layout arrays."""
-    shapes = W.core_shapes(wl)
-    host = [x.cpu().numpy() for x in flat]
-    out = []
-    for t in range(wl.num_tables):
-        tbl = []
-        for k in range(3):
-            n = int(np.prod(shapes[k]))
-            tbl.append(W.logical(host[k][t * n:(t + 1) * n], shapes[k]))
-        out.append(tbl)
-    return out
 
 
 @pytest.mark.parametrize("name, steps", [("readme", 3), ("multitable", 2)])
@@ -42,13 +20,12 @@ def test_pipelined_loop_matches_oracle(name, steps):
     wl = W.WORKLOADS[name]
     T, B = wl.num_tables, wl.bags_per_table
     cores = W.make_cores(wl)
-    g = [torch.from_numpy(np.concatenate([W.slice_major(cores[t][k]).ravel() for t in range(T)]))
-         .cuda() for k in range(3)]
+    g = gpu_cores(wl, cores)
     desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E, T)
     host_batches = [W.make_batch(wl, k) for k in range(2)]  # cycled, as the benchmark does
     out = torch.empty(T * B, wl.D, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    loop = TrainLoop(desc, g, [_dev(b) for b in host_batches], B, wl.lr, out, status)
+    loop = TrainLoop(desc, g, [to_dev(b) for b in host_batches], B, wl.lr, out, status)
     snaps, ys = [[x.clone() for x in g]], []
     for _ in range(steps):
         loop.step()
@@ -59,7 +36,7 @@ def test_pipelined_loop_matches_oracle(name, steps):
     assert int(status.item()) == 0
     for i in range(steps):
         b = host_batches[i % 2]
-        start, end = _tables(snaps[i], wl), _tables(snaps[i + 1], wl)
+        start, end = host_cores(wl, snaps[i]), host_cores(wl, snaps[i + 1])
         yref = oracle.forward(wl.p, wl.q, wl.ranks, wl.E, start, b["indices"], b["offsets"], B,
                               per_sample_weights=b["per_sample_weights"])
         assert rel_err(ys[i].cpu().numpy(), yref) <= TOL, i
