@@ -188,7 +188,8 @@ def main():
                    "update": args.update + (" (backward over distinct indices)"
                                             if args.dedup else ""),
                    "host_enqueue_us_per_step": round((t_enq - t0) * 1e6 / args.steps, 2),
-                   "pipeline": "grouping of batch i+1 overlapped with the backward of batch i"
+                   "pipeline": "grouping of batch i+1 beside the backward of batch i; the "
+                               "host waits for it before the forward of batch i+1"
                                if pipeline else "none"},
     }
     # gradient with respect to the per-sample weights of one planned batch (off the

@@ -3,11 +3,10 @@ same object, so the launch configuration they check is the one the benchmark mea
 
 Every batch is grouped (tt_bag_plan, or tt_bag_plan_dedup for the backward over distinct
 indices), then runs the planned forward and the planned backward.  Pipelined (default):
-the grouping of batch i+1 is enqueued on a second stream right after the forward of batch
-i (after the backward with the distinct-index plan, which waits on the host), so it
-overlaps the backward of batch i; two workspaces alternate, and events order (a) the
-forward of a batch after its grouping and (b) a grouping after the last use of its
-workspace (two batches back).  With a cache, the lookup of a batch runs on the grouping
+the grouping of batch i+1 is enqueued on a second stream right after the backward of batch
+i and runs beside it; two workspaces alternate; the host waits for a batch's grouping
+before it enqueues the batch's forward, and an event orders a grouping after the last use
+of its workspace (two batches back).  With a cache, the lookup of a batch runs on the grouping
 stream just before its grouping.  Argument marshalling only: every step runs in libttbag.
 """
 from __future__ import annotations
@@ -87,7 +86,10 @@ class TrainLoop:
         b = self.batches[i % len(self.batches)]
         ws = self.wss[i % len(self.wss)]
         if self.pipeline:
-            self.main.wait_event(self.ev_plan[i % 2])
+            # the host waits for this batch's grouping (it ran beside the previous
+            # backward and is normally long done) instead of the device: a cross-stream
+            # wait on the device costs about 5 us per step even when the event is done
+            self.ev_plan[i % 2].synchronize()
             cv = self.cvs.pop(i)
         else:
             cv = self._plan(i)
@@ -95,7 +97,6 @@ class TrainLoop:
         abi.tt_bag_forward(self.desc, self.g, b["indices"], b["offsets"], self.B, w, cache=cv,
                            out=self.out, ws=ws, dev_status=self.status, planned=True)
         if self.dedup:
-            # the next plan waits on the host, so it is enqueued after this backward
             info = self.infos.pop(i)
             if self.update == "sgd":
                 abi.tt_bag_backward_sgd_dedup(self.desc, self.g, b["indices"], b["offsets"],
@@ -107,13 +108,7 @@ class TrainLoop:
                                                self.B, b["grad_out"], info, grad_cores=self.aux,
                                                per_sample_weights=w, ws=ws,
                                                dev_status=self.status)
-            if self.pipeline:
-                self.ev_done[i % 2].record(self.main)
-                self.cvs[i + 1] = self._plan(i + 1)
-            return i
-        if self.pipeline:
-            self.cvs[i + 1] = self._plan(i + 1)
-        if self.update == "sgd":
+        elif self.update == "sgd":
             abi.tt_bag_backward_sgd(self.desc, self.g, b["indices"], b["offsets"], self.B,
                                     b["grad_out"], self.lr, w, cache=cv, ws=ws,
                                     dev_status=self.status, planned=True)
@@ -128,5 +123,9 @@ class TrainLoop:
                                      per_sample_weights=w, cache=cv, ws=ws,
                                      dev_status=self.status, planned=True)
         if self.pipeline:
+            # the next grouping is enqueued after this backward: the device gets the
+            # backward without waiting on the host's enqueue of the grouping, and the
+            # grouping still runs beside it on the second stream
             self.ev_done[i % 2].record(self.main)
+            self.cvs[i + 1] = self._plan(i + 1)
         return i
