@@ -87,7 +87,9 @@ static __device__ void fwd_wait_out(const DevArgs &a) {  // whole block
 
 // DOT: instead of pooling, the gradient with respect to each element's per-sample weight,
 // dL/dw_n = <grad_out[bag n], row n> (times 1 / bag length with mean pooling); rows in LDS.
-template <int RP, bool DOT>
+// MF: stage 2 on the matrix cores (q1 = q3 = 4, rows kept in LDS, RP <= 32), chosen by the
+// host when the work items are expected to be resident at once (see mf_stage2).
+template <int RP, bool DOT, bool MF>
 __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
   constexpr int KS = RP / 4;   // k-steps: lane group g covers r1 = g*KS + ks
   constexpr int NM = RP / 16;  // 16-row blocks of r2
@@ -285,6 +287,40 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
             acc[m] = mfma4(av.w, bv[mbi][4 * kq + 3], acc[m]);
           }
         }
+        if (MF) {
+          // stage 2 on the matrix cores (q1 = q3 = 4, rows kept in LDS): the rows of the
+          // M-block's items times their G3 slices, four items x four j3 per 16-column
+          // block.  A = T straight from acc (instruction (m, v) takes r2 = 16m + 4g + v
+          // as the k index of lane group g); B = G3 of item s = c / 4 at j3 = c % 4.
+          // Lane (g, c) gets rows 4g .. 4g+3 of the M-block (its pair p0 + g, j1 = v) in
+          // column c and keeps the columns of its own pair's items.
+          const int p0 = mb * 4;  // mb < nmb, so p0 < nP
+          const int it0 = pr_it[p0], it1 = pr_it[min(p0 + 4, nP)];
+          const int myp = p0 + g;
+          const int mib = myp < nP ? pr_it[myp] : 0, mie = myp < nP ? pr_it[myp + 1] : 0;
+          const int s4 = c >> 2, jc = c & 3;
+          for (int nb = it0; nb < it1; nb += 4) {
+            const int it = nb + s4;
+            const bool okit = it < it1;
+            const float *g3p = sG3 + (size_t)(okit ? it : it0) * RP * 4 + jc * RP + 4 * g;
+            f4 dW = zero4();
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+              float4 bq = *(const float4 *)&g3p[16 * m];
+              if (!okit) bq = make_float4(0.f, 0.f, 0.f, 0.f);
+              dW = mfma4(acc[m][0], bq.x, dW);
+              dW = mfma4(acc[m][1], bq.y, dW);
+              dW = mfma4(acc[m][2], bq.z, dW);
+              dW = mfma4(acc[m][3], bq.w, dW);
+            }
+            if (okit && it >= mib && it < mie) {
+              float *wr = sW + (size_t)it * D + j2 * 4 + jc;
+#pragma unroll
+              for (int v = 0; v < 4; ++v) wr[v * q2 * 4] = dW[v];
+            }
+          }
+          continue;
+        }
         // stage 2: lane (g, c) holds T^T[r2 = 16m + 4g + v][row c] of this j2
         const int row = mb * 16 + c;
         const int pr = row >> a.lq1, j1 = row & (q1 - 1);
@@ -368,44 +404,51 @@ size_t fwd_lds_bytes(int RP, int JB, int P, int q3, int D, int sw) {
   }
 }
 
-template <int RP>
-static hipError_t launch_fwd_t(const DevArgs &a, size_t lds, hipStream_t s) {
+// Stage 2 on the matrix cores is chosen when the shape allows it and the work items are
+// expected to fit the device at once (two workgroups per CU; groups of the mean size
+// nnz / groups cut into P-position items).  Such a launch is bound by each item's chain
+// of dependent steps, which the matrix cores shorten; with more items it is bound by
+// throughput, where the per-item VALU path does less work (both measured).  A wrong
+// guess costs time only.
+static bool mf_stage2(const DevArgs &a, int RP, bool dot) {
+  if (RP > 32 || a.q1 != 4 || a.q3 != 4 || !(dot || a.fwd_sw) || a.nnz <= 0) return false;
+  const long long G = (long long)a.T * a.p2;
+  const long long per = (a.nnz + G - 1) / G;
+  const long long items = G * ((per + a.P - 1) / a.P);
+  return items <= 2LL * device_cus();
+}
+
+template <int RP, bool DOT, bool MF>
+static hipError_t launch_fwd_k(const DevArgs &a, size_t lds, hipStream_t s) {
   static bool attr_set = false;  // dynamic LDS above 64 KiB is opt-in per kernel
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void *)k_fwd<RP, false>,
+    (void)hipFuncSetAttribute((const void *)k_fwd<RP, DOT, MF>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr_set = true;
   }
-  const int grid = items_max(a);
-  tt_launch(K_FWD, k_fwd<RP, false>, dim3(grid), dim3(WG), lds, s, a);
+  tt_launch(K_FWD, k_fwd<RP, DOT, MF>, dim3(items_max(a)), dim3(WG), lds, s, a);
   return hipGetLastError();
 }
 
-template <int RP>
-static hipError_t launch_wgrad_t(const DevArgs &a, size_t lds, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute((const void *)k_fwd<RP, true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr_set = true;
-  }
-  tt_launch(K_FWD, k_fwd<RP, true>, dim3(items_max(a)), dim3(WG), lds, s, a);
-  return hipGetLastError();
+template <int RP, bool DOT>
+static hipError_t launch_fwd_t(const DevArgs &a, size_t lds, hipStream_t s) {
+  if (RP <= 32 && mf_stage2(a, RP, DOT)) return launch_fwd_k<RP, DOT, RP <= 32>(a, lds, s);
+  return launch_fwd_k<RP, DOT, false>(a, lds, s);
 }
 
 hipError_t launch_wgrad(const DevArgs &a, int RP, size_t lds, hipStream_t s) {
   switch (RP) {
-    case 16: return launch_wgrad_t<16>(a, lds, s);
-    case 32: return launch_wgrad_t<32>(a, lds, s);
-    default: return launch_wgrad_t<64>(a, lds, s);
+    case 16: return launch_fwd_t<16, true>(a, lds, s);
+    case 32: return launch_fwd_t<32, true>(a, lds, s);
+    default: return launch_fwd_t<64, true>(a, lds, s);
   }
 }
 
 hipError_t launch_fwd(const DevArgs &a, int RP, size_t lds, hipStream_t s) {
   switch (RP) {
-    case 16: return launch_fwd_t<16>(a, lds, s);
-    case 32: return launch_fwd_t<32>(a, lds, s);
-    default: return launch_fwd_t<64>(a, lds, s);
+    case 16: return launch_fwd_t<16, false>(a, lds, s);
+    case 32: return launch_fwd_t<32, false>(a, lds, s);
+    default: return launch_fwd_t<64, false>(a, lds, s);
   }
 }
 

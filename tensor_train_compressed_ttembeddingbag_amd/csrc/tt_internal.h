@@ -178,6 +178,9 @@ inline void tt_launch(int id, void (*kernel)(KArgs...), dim3 grid, dim3 block, s
     hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
 }
 
+// compute units of the current device (cached per device; 0 if the query fails)
+int device_cus();
+
 // stable LSD radix sort of n 64-bit keys by bits [lo, hi); returns a or b (the result)
 unsigned long long *radix_sort64_bits(unsigned long long *a, unsigned long long *b, int n,
                                       int *hist, int lo, int hi, hipStream_t s);

@@ -350,7 +350,7 @@ constexpr int COOP_BINS = 2048;        // bins per digit
 constexpr unsigned SYNC_POLLS = 1u << 22;  // bounded wait of a grid barrier
 
 // Compute units of the current device (cached per device).
-static int device_cus() {
+int device_cus() {
   static int cus[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
