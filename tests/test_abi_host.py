@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from tensor_train_compressed_ttembeddingbag_amd import abi, workloads as W
 
@@ -150,3 +151,16 @@ def test_factorize_host_function_matches_the_oracle_rule():
         else:
             assert abi.tt_factorize(n, True) == want, n
     assert abi.tt_factorize(11000000, False) == (222, 223, 223)
+
+
+def test_train_loop_rejects_invalid_options():
+    """The benchmark's training loop refuses, before any device work, an unknown update
+    and the backward over distinct indices combined with a cache or with Adagrad."""
+    from tensor_train_compressed_ttembeddingbag_amd.loop import TrainLoop
+    batch = [{"indices": torch.zeros(1, dtype=torch.int64)}]
+    with pytest.raises(ValueError):
+        TrainLoop(None, [], batch, 1, 0.1, None, None, update="adam")
+    with pytest.raises(ValueError):
+        TrainLoop(None, [], batch, 1, 0.1, None, None, cache=object(), dedup=True)
+    with pytest.raises(ValueError):
+        TrainLoop(None, [], batch, 1, 0.1, None, None, update="adagrad", dedup=True)
