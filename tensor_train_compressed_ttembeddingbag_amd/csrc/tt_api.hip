@@ -368,7 +368,6 @@ int backward_call(const tt_desc *desc, float *const cores[3], const int64_t *ind
     return TT_OK;
   }
   if (e == hipSuccess && plan_first) e = launch_route(a, s);
-  if (e == hipSuccess) e = launch_runsum(a, s);
   if (e == hipSuccess) e = launch_bwd(a, P.RP, P.lds_bwd, s);
   if (e == hipSuccess) e = launch_seg(a, s);
   return finish(e);

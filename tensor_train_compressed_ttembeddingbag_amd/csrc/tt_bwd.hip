@@ -25,7 +25,8 @@
 // to the workspace at the final-order position of their first element, and the
 // links record where they are.  k_seg then sums every partial per slice in a fixed
 // order and applies SGD: dG1 / dG3 in the (t,i1)- / (t,i3)-order, dG2 in
-// work-item order.
+// work-item order.  With a cache, workgroups after the work items sum w * dY over the
+// cache-hit runs (runsum_piece), beside the contraction.
 #include <algorithm>
 
 #include "tt_device.h"
@@ -61,8 +62,10 @@ size_t bwd_lds_bytes(int RP, int JB, int P, int q3, int D, int nred) {
 
 // two workgroups per CU need <= 128 VGPRs (rank-64 tiles take one CU each).  Q3 = 4
 // fixes q3 at compile time (each item's G3 / dG3 rows of four j3 move as 16-byte LDS
-// vectors); Q3 = 0 reads it from the arguments.
-template <int RP, int Q3>
+// vectors); Q3 = 0 reads it from the arguments.  HITS: the instance for calls with a
+// cache, whose extra workgroups sum the cache-hit runs (an instance of its own, so that
+// the register budget of the others is not shared with that path).
+template <int RP, int Q3, bool HITS>
 __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(RP == 64 ? 2 : 4)))
 void k_bwd(DevArgs a) {
   constexpr int KS = RP / 4, NM = RP / 16, LD = BwdLds<RP>::LD, LRP = log2_rp<RP>();
@@ -92,6 +95,16 @@ void k_bwd(DevArgs a) {
   int *e_perm = s_cnt + 8;                                        // [64] item-major elements
   int *it_first = e_perm + 64;                                    // [64] leader offsets
 
+  // workgroups past the work items' part of the grid: the cache-hit run sums, one wave
+  // per 64-position piece (they need only the plan and grad_out, so they run beside the
+  // contraction; the segment sums read their fragments after this launch)
+  const int nwi = items_max(a);
+  if (HITS && (int)blockIdx.x >= nwi) {
+    if (a.hdr[H_PLAN] != (int)a.plan_fp) return;  // stale plan: k_seg reports it
+    const int piece = ((int)blockIdx.x - nwi) * NW + (int)(threadIdx.x >> 6);
+    runsum_piece(a, piece, (int)(threadIdx.x & 63));
+    return;
+  }
   // round 1: plan check and work item
   const int wi = blockIdx.x;
   const int plan = a.hdr[H_PLAN], nitems = a.hdr[H_NFWD];
@@ -490,16 +503,25 @@ void k_bwd(DevArgs a) {
   }
 }
 
-template <int RP, int Q3>
-static hipError_t launch_bwd_t(const DevArgs &a, size_t lds, hipStream_t s) {
+template <int RP, int Q3, bool HITS>
+static hipError_t launch_bwd_k(const DevArgs &a, size_t lds, hipStream_t s) {
   static bool attr_set = false;  // dynamic LDS above 64 KiB is opt-in per kernel
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void *)k_bwd<RP, Q3>,
+    (void)hipFuncSetAttribute((const void *)k_bwd<RP, Q3, HITS>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr_set = true;
   }
-  tt_launch(K_BWD, k_bwd<RP, Q3>, dim3(items_max(a)), dim3(WG), lds, s, a);
+  // with a cache, extra workgroups (eight 64-position pieces each) sum the hit runs
+  const int pieces = HITS ? (a.nnz + PIECE - 1) / PIECE : 0;
+  const int grid = items_max(a) + (pieces + NW - 1) / NW;
+  tt_launch(K_BWD, k_bwd<RP, Q3, HITS>, dim3(grid), dim3(WG), lds, s, a);
   return hipGetLastError();
+}
+
+template <int RP, int Q3>
+static hipError_t launch_bwd_t(const DevArgs &a, size_t lds, hipStream_t s) {
+  return a.has_cache ? launch_bwd_k<RP, Q3, true>(a, lds, s)
+                     : launch_bwd_k<RP, Q3, false>(a, lds, s);
 }
 
 template <int Q3>
@@ -725,7 +747,7 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
     const int s0 = lo + l;
     const int kA = __shfl(cur.y, l), kB = __shfl(cur.z, l);
     const int slot = (kB - a.T * a.p2) * HB + (kA - a.T * a.p1);
-    // the run's fragments: s0, then every piece start inside the run (k_runsum);
+    // the run's fragments: s0, then every piece start inside the run (runsum_piece);
     // their number, 64 piece starts per round
     const int pb = (s0 / PIECE + 1) * PIECE;
     int nfr = 0;

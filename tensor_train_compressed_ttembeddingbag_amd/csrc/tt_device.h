@@ -206,4 +206,50 @@ static __device__ bool last_block(unsigned long long *ctr, int nblocks, unsigned
   return s_last != 0;
 }
 
+// One wave's part of the cache-hit run sums: the w_n * dY[bag n] of piece `piece` (64
+// positions of the final order) summed per fragment (run starts and the piece start) in
+// position order.  Runs of the same slot are cache hits of one row; misses sum theirs in
+// the backward contraction itself.
+static __device__ __forceinline__ void runsum_piece(const DevArgs &a, int piece, int lane) {
+  const int V = a.hdr[H_VALID];
+  const int beg = piece * PIECE;
+  if (beg >= V || beg + PIECE <= a.hdr[H_HIT_BEG]) return;
+  const int len = min(PIECE, V - beg);
+  const int s = beg + min(lane, len - 1);
+  const SPos sp = load_spos(a.srec, s);
+  const int kA = sp.dA, kB = sp.dB, kI = sp.dI3, bag = sp.bag;
+  const float wt = lane < len ? sp.w : 0.f;
+  const int pA = __shfl_up(kA, 1), pB = __shfl_up(kB, 1), pI = __shfl_up(kI, 1);
+  // fragments start at run starts and at the piece start
+  const unsigned long long starts =
+      __ballot(lane < len && ((lane == 0) || kA != pA || kB != pB || kI != pI));
+  constexpr int HALF = PIECE / 2;  // dY rows in flight (two halves keep registers low)
+  for (int d0 = 0; d0 < a.D; d0 += 64) {
+    const int d = min(d0 + lane, a.D - 1);
+    float acc = 0.f;
+    int cur = beg;
+#pragma unroll
+    for (int h = 0; h < PIECE; h += HALF) {
+      float v[HALF];
+#pragma unroll
+      for (int l = 0; l < HALF; ++l) {
+        const int b = __builtin_amdgcn_readlane(bag, h + l);
+        v[l] = a.dY[(size_t)b * a.D + d];
+      }
+#pragma unroll
+      for (int l = 0; l < HALF; ++l) {
+        const int ll = h + l;
+        if (((starts >> ll) & 1ull) && ll > 0) {
+          if (d0 + lane < a.D) a.frag[(size_t)cur * a.D + d] = acc;
+          acc = 0.f;
+          cur = beg + ll;
+        }
+        if (ll < len)
+          acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), ll)) * v[l];
+      }
+    }
+    if (d0 + lane < a.D) a.frag[(size_t)cur * a.D + d] = acc;
+  }
+}
+
 }  // namespace ttb

@@ -8,7 +8,7 @@
 //                           work items.
 //   yinit:  k_yinit         out = zeros, or the pooled cache hits.
 //   forward: k_fwd          one workgroup per work item (piece of an i2 group).
-//   backward: k_runsum      cache hits: w * dY summed over runs of one slot.
+//   backward: k_bwd         also sums w * dY over the cache-hit runs of one slot.
 //             k_bwd         one workgroup per work item.
 //             k_seg         core-1 / core-3 segment sums + SGD; cache-row SGD.
 #pragma once
@@ -187,7 +187,6 @@ unsigned long long *radix_sort64_bits(unsigned long long *a, unsigned long long 
 
 // host launchers (each kernel is launched from the file that defines it)
 hipError_t launch_route(const DevArgs &a, hipStream_t s);   // the grouping kernels
-hipError_t launch_runsum(const DevArgs &a, hipStream_t s);
 hipError_t launch_yinit(const DevArgs &a, hipStream_t s);
 hipError_t launch_seg(const DevArgs &a, hipStream_t s);
 hipError_t launch_zero(float *x, size_t n, hipStream_t s);  // x[0 .. n) = 0

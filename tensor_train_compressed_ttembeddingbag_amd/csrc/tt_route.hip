@@ -712,53 +712,6 @@ __global__ __launch_bounds__(RT) void k_yinit(DevArgs a) {
   }
 }
 
-// Backward, cache hits: frag[s] = sum over positions of one run fragment of
-// w_n * dY[bag n], where a run is a maximal range of equal (dB, dA, dI3) in the final
-// order (one cache slot) and fragments are the parts of a run inside the 64-position
-// pieces.  One wave per piece; the summation order is the position order.
-// (Misses sum their runs inside the backward contraction kernel.)
-__global__ __launch_bounds__(RT) void k_runsum(DevArgs a) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int piece = blockIdx.x * (RT / 64) + w;
-  const int V = a.hdr[H_VALID];
-  const int beg = piece * PIECE;
-  if (a.hdr[H_PLAN] != (int)a.plan_fp) {  // the workspace holds another call's plan
-    if (piece == 0 && lane == 0) set_status(a.status, DEV_STALE_PLAN);
-    return;
-  }
-  if (beg >= V || beg + PIECE <= a.hdr[H_HIT_BEG]) return;
-  const int len = min(PIECE, V - beg);
-  const int s = beg + min(lane, len - 1);
-  const SPos sp = load_spos(a.srec, s);
-  const int kA = sp.dA, kB = sp.dB, kI = sp.dI3, bag = sp.bag;
-  const float wt = lane < len ? sp.w : 0.f;
-  const int pA = __shfl_up(kA, 1), pB = __shfl_up(kB, 1), pI = __shfl_up(kI, 1);
-  // fragments start at run starts and at the piece start
-  const unsigned long long starts =
-      __ballot(lane < len && ((lane == 0) || kA != pA || kB != pB || kI != pI));
-  for (int d0 = 0; d0 < a.D; d0 += 64) {
-    const int d = min(d0 + lane, a.D - 1);
-    float v[PIECE];
-#pragma unroll
-    for (int l = 0; l < PIECE; ++l) {
-      const int b = __builtin_amdgcn_readlane(bag, l);
-      v[l] = a.dY[(size_t)b * a.D + d];
-    }
-    float acc = 0.f;
-    int cur = beg;
-#pragma unroll
-    for (int l = 0; l < PIECE; ++l) {
-      if (((starts >> l) & 1ull) && l > 0) {
-        if (d0 + lane < a.D) a.frag[(size_t)cur * a.D + d] = acc;
-        acc = 0.f;
-        cur = beg + l;
-      }
-      if (l < len) acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), l)) * v[l];
-    }
-    if (d0 + lane < a.D) a.frag[(size_t)cur * a.D + d] = acc;
-  }
-}
-
 // dL/dw of the cache hits: one thread per position of the hit region,
 // <cache row, grad_out[bag]> (times 1 / bag length with mean pooling), 8 loads in flight.
 __global__ __launch_bounds__(256) void k_wgrad_hits(DevArgs a) {
@@ -826,12 +779,5 @@ hipError_t launch_yinit(const DevArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_runsum(const DevArgs &a, hipStream_t s) {
-  const int pieces = (a.nnz + PIECE - 1) / PIECE;
-  if (pieces > 0 && a.has_cache) {
-    tt_launch(K_RUNSUM, k_runsum, dim3((pieces + 3) / 4), dim3(RT), 0, s, a);
-  }
-  return hipGetLastError();
-}
 
 }  // namespace ttb

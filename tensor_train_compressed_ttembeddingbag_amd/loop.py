@@ -3,8 +3,9 @@ same object, so the launch configuration they check is the one the benchmark mea
 
 Every batch is grouped (tt_bag_plan, or tt_bag_plan_dedup for the backward over distinct
 indices), then runs the planned forward and the planned backward.  Pipelined (default):
-the grouping of batch i+1 is enqueued on a second stream right after the backward of batch
-i and runs beside it; two workspaces alternate; the host waits for a batch's grouping
+the grouping of batch i+1 is enqueued on a second stream right after the forward of batch i
+(after the backward with the distinct-index grouping, which waits on the host) and runs
+beside the backward; two workspaces alternate; the host waits for a batch's grouping
 before it enqueues the batch's forward, and an event orders a grouping after the last use
 of its workspace (two batches back).  With a cache, the lookup of a batch runs on the grouping
 stream just before its grouping.  Argument marshalling only: every step runs in libttbag.
@@ -96,6 +97,10 @@ class TrainLoop:
         w = b["per_sample_weights"]
         abi.tt_bag_forward(self.desc, self.g, b["indices"], b["offsets"], self.B, w, cache=cv,
                            out=self.out, ws=ws, dev_status=self.status, planned=True)
+        if self.pipeline and not self.dedup:
+            # the next grouping starts now, beside this batch's backward (with a cache its
+            # lookup and grouping take longer than the backward alone)
+            self.cvs[i + 1] = self._plan(i + 1)
         if self.dedup:
             info = self.infos.pop(i)
             if self.update == "sgd":
@@ -123,9 +128,9 @@ class TrainLoop:
                                      per_sample_weights=w, cache=cv, ws=ws,
                                      dev_status=self.status, planned=True)
         if self.pipeline:
-            # the next grouping is enqueued after this backward: the device gets the
-            # backward without waiting on the host's enqueue of the grouping, and the
-            # grouping still runs beside it on the second stream
             self.ev_done[i % 2].record(self.main)
-            self.cvs[i + 1] = self._plan(i + 1)
+            if self.dedup:
+                # the distinct-index grouping waits on the host for its size, so it is
+                # enqueued after this backward, which then runs meanwhile
+                self.cvs[i + 1] = self._plan(i + 1)
         return i
