@@ -159,7 +159,7 @@ constexpr int DEV_STALE_PLAN = 16;
 
 // kernels named by the optional per-kernel timer (tt_prof.hip)
 enum KernelId {
-  K_ROUTE_COOP, K_ROUTE_A, K_ROUTE_B, K_ROUTE_C, K_FWD, K_RUNSUM, K_BWD, K_SEG,
+  K_ROUTE_COOP, K_ROUTE_A, K_ROUTE_B, K_ROUTE_C, K_FWD, K_BWD, K_SEG,
   K_CACHE_LOOKUP, K_YINIT, K_ZERO, K_DMERGE, K_DSPLIT, K_DAPPLY, K_DD_FRAG, K_DD_GU,
   K_COUNT
 };
