@@ -49,3 +49,65 @@ def test_pipelined_loop_matches_oracle(name, steps):
                 assert rel_err(delta, -wl.lr * grads[t][k]) <= TOL, (i, t, k)
                 m = ~touched[t][k].astype(bool)
                 assert np.array_equal(end[t][k][:, m], start[t][k][:, m]), (i, t, k)
+
+
+def test_pipelined_loop_with_cache_matches_oracle():
+    """The loop with a cache (each batch's lookup and grouping on the second stream,
+    started right after the previous forward): every step's forward, core update and
+    cache-row update against the oracle, whose slots come from its own top-K selection."""
+    print("case train loop cache", flush=True)
+    wl = W.custom("cache", p=(20, 22, 25), q=(4, 4, 4), ranks=(32, 32), bags_per_table=256,
+                  lengths=("fixed", 20), dist=("zipf", 1.2), init_std=1 / 32 ** 0.5, lr=0.01,
+                  weighted=True)
+    K, B, steps = 900, 256, 3
+    cores = W.make_cores(wl)
+    desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E)
+    cache = abi.Cache(desc, K, 1 << 14)
+    warm = [W.make_batch(wl, 100 + i) for i in range(4)]
+    for bt in warm:
+        cache.lookup(torch.from_numpy(bt["indices"]).cuda(), count_freq=True)
+    g = gpu_cores(wl, cores)
+    rows = torch.zeros(K, wl.D, device="cuda")
+    nf = cache.populate(g, rows)
+    sel = oracle.select_cache(oracle.count_frequencies([bt["indices"] for bt in warm]), K)
+    assert nf == len(sel)
+    host_batches = [W.make_batch(wl, k) for k in range(2)]
+    batches = [to_dev(b) for b in host_batches]
+    slots = [torch.empty(b["indices"].numel(), dtype=torch.int32, device="cuda")
+             for b in batches]
+    out = torch.empty(B, wl.D, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    loop = TrainLoop(desc, g, batches, B, wl.lr, out, status, cache=cache, rows=rows,
+                     slots=slots)
+    snaps, rsnaps, ys = [[x.clone() for x in g]], [rows.clone()], []
+    for _ in range(steps):
+        loop.step()
+        ys.append(out.clone())
+        snaps.append([x.clone() for x in g])
+        rsnaps.append(rows.clone())
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for i in range(steps):
+        b = host_batches[i % 2]
+        ref_slots = oracle.lookup_slots(sel, b["indices"])
+        assert (ref_slots >= 0).any() and (ref_slots < 0).any()
+        start, end = host_cores(wl, snaps[i]), host_cores(wl, snaps[i + 1])
+        r0 = rsnaps[i].cpu().numpy()
+        r1 = rsnaps[i + 1].cpu().numpy()
+        yref = oracle.forward(wl.p, wl.q, wl.ranks, wl.E, start, b["indices"], b["offsets"], B,
+                              per_sample_weights=b["per_sample_weights"], slots=ref_slots,
+                              cache_rows=r0)
+        assert rel_err(ys[i].cpu().numpy(), yref) <= TOL, i
+        grads, touched, gc, tc = oracle.backward(wl.p, wl.q, wl.ranks, wl.E, start,
+                                                 b["indices"], b["offsets"], B, b["grad_out"],
+                                                 per_sample_weights=b["per_sample_weights"],
+                                                 slots=ref_slots, cache_size=K)
+        for k in range(3):
+            delta = end[0][k].astype(np.float64) - start[0][k].astype(np.float64)
+            assert rel_err(delta, -wl.lr * grads[0][k]) <= TOL, (i, k)
+            m = ~touched[0][k].astype(bool)
+            assert np.array_equal(end[0][k][:, m], start[0][k][:, m]), (i, k)
+        drows = r1.astype(np.float64) - r0.astype(np.float64)
+        assert rel_err(drows, -wl.lr * gc) <= TOL, i
+        untouched = np.flatnonzero(tc == 0)
+        assert np.array_equal(r1[untouched].view(np.uint32), r0[untouched].view(np.uint32)), i
