@@ -111,3 +111,45 @@ def test_pipelined_loop_with_cache_matches_oracle():
         assert rel_err(drows, -wl.lr * gc) <= TOL, i
         untouched = np.flatnonzero(tc == 0)
         assert np.array_equal(r1[untouched].view(np.uint32), r0[untouched].view(np.uint32)), i
+
+
+def test_pipelined_loop_with_distinct_index_backward_matches_oracle():
+    """The loop with the backward over distinct indices (its grouping waits on the host
+    and is enqueued after each backward): two tables, heavy repeats, per-sample weights,
+    empty bags; every step's forward and core update against the oracle."""
+    print("case train loop dedup", flush=True)
+    wl = W.custom("dedup loop", p=(6, 5, 7), q=(2, 4, 2), ranks=(8, 6), num_tables=2,
+                  bags_per_table=40, lengths=("uniform", 0, 8), dist=("zipf", 1.3),
+                  init_std=0.5, lr=0.05, weighted=True, num_embeddings=200)
+    T, B, steps = wl.num_tables, wl.bags_per_table, 3
+    cores = W.make_cores(wl)
+    g = gpu_cores(wl, cores)
+    desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E, T)
+    host_batches = [W.make_batch(wl, k) for k in range(2)]
+    assert len(np.unique(host_batches[0]["indices"])) < len(host_batches[0]["indices"]) // 2
+    out = torch.empty(T * B, wl.D, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    loop = TrainLoop(desc, g, [to_dev(b) for b in host_batches], B, wl.lr, out, status,
+                     dedup=True)
+    snaps, ys = [[x.clone() for x in g]], []
+    for _ in range(steps):
+        loop.step()
+        ys.append(out.clone())
+        snaps.append([x.clone() for x in g])
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for i in range(steps):
+        b = host_batches[i % 2]
+        start, end = host_cores(wl, snaps[i]), host_cores(wl, snaps[i + 1])
+        yref = oracle.forward(wl.p, wl.q, wl.ranks, wl.E, start, b["indices"], b["offsets"], B,
+                              per_sample_weights=b["per_sample_weights"])
+        assert rel_err(ys[i].cpu().numpy(), yref) <= TOL, i
+        grads, touched, _, _ = oracle.backward(wl.p, wl.q, wl.ranks, wl.E, start, b["indices"],
+                                               b["offsets"], B, b["grad_out"],
+                                               per_sample_weights=b["per_sample_weights"])
+        for t in range(T):
+            for k in range(3):
+                delta = end[t][k].astype(np.float64) - start[t][k].astype(np.float64)
+                assert rel_err(delta, -wl.lr * grads[t][k]) <= TOL, (i, t, k)
+                m = ~touched[t][k].astype(bool)
+                assert np.array_equal(end[t][k][:, m], start[t][k][:, m]), (i, t, k)
