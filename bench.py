@@ -338,8 +338,10 @@ def roofline(args, wl, batches, step, torch, abi, metrics, slots):
 
 def run_dcore(args, wl, cores, torch, abi, metrics, W):
     """d-core workload: a step is tt_bag_plan_d (grouping) + tt_bag_forward_d_planned +
-    tt_bag_backward_sgd_d_planned on one stream (both multiply out the groups of cores; the
-    backward splits the gradients back and applies SGD to the d cores)."""
+    tt_bag_backward_sgd_d_planned (both multiply out the groups of cores; the backward
+    splits the gradients back and applies SGD to the d cores), in the same pipelined loop
+    as the three-core workloads (loop.TrainLoop)."""
+    from tensor_train_compressed_ttembeddingbag_amd.loop import TrainLoop
     d = len(wl.p)
     g = [torch.from_numpy(np.concatenate([W.slice_major(cores[t][k]).ravel()
                                           for t in range(wl.num_tables)])).cuda()
@@ -350,21 +352,12 @@ def run_dcore(args, wl, cores, torch, abi, metrics, W):
     r3 = (wl.ranks[a - 1], wl.ranks[b - 1])
     batches = [_dev(W.make_batch(wl, k), torch) for k in range(args.batches)]
     B = wl.bags_per_table
-    ws = abi.workspace_d(desc, max(x["indices"].numel() for x in batches), B)
     out = torch.empty(wl.num_tables * B, wl.D, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    main = torch.cuda.current_stream()
+    loop = TrainLoop(desc, g, batches, B, wl.lr, out, status, pipeline=not args.no_pipeline)
 
-    def step(i):
-        x = batches[i % len(batches)]
-        abi.tt_bag_plan_d(desc, x["indices"], x["offsets"], B, x["per_sample_weights"], ws=ws,
-                          dev_status=status, stream=main)
-        abi.tt_bag_forward_d(desc, g, x["indices"], x["offsets"], B, x["per_sample_weights"],
-                             out=out, ws=ws, dev_status=status, stream=main, planned=True)
-        abi.tt_bag_backward_sgd_d(desc, g, x["indices"], x["offsets"], B, x["grad_out"], wl.lr,
-                                  x["per_sample_weights"], ws=ws, dev_status=status,
-                                  stream=main, planned=True)
-        return i
+    def step(_):
+        return loop.step()
 
     for i in range(args.warmup):
         step(i)
@@ -387,7 +380,11 @@ def run_dcore(args, wl, cores, torch, abi, metrics, W):
                                   "cut=[0,%d)[%d,%d)[%d,%d) (as three cores q=%s ranks=%s)"
                       % (wl.name, d, list(wl.p), list(wl.q), list(wl.ranks), wl.E, wl.D,
                          wl.num_tables, B, a, a, b, b, d, list(q3), list(r3)),
-                      "nnz": nnz, "global_batch": B, "update": "sgd"}}
+                      "nnz": nnz, "global_batch": B, "update": "sgd",
+                      "pipeline": "grouping of batch i+1 beside the backward of batch i; the "
+                                  "host waits for it before the forward of batch i+1"
+                                  if not args.no_pipeline else "none"}}
+    res["config"]["step_us_percentiles"] = step_percentiles(step, min(args.steps, 400), torch)
     if not args.no_roofline:
         abi.tt_profile_enable(True)
         done = [step(i) for i in range(min(args.steps, 200))]

@@ -25,7 +25,9 @@ class TrainLoop:
     "grad_out", "per_sample_weights" (or None).  update: "sgd" (fused SGD, lr), "adagrad"
     (fused Adagrad with eps 1e-10; aux / aux_rows hold the running sums) or "grad"
     (gradients written to aux / aux_rows).  cache: an abi.Cache with its rows and one
-    slot buffer per batch.  out receives the pooled forward of the step."""
+    slot buffer per batch.  out receives the pooled forward of the step.  A d-core
+    descriptor (abi.TTDescD) runs the d-core calls (no cache, no distinct-index backward,
+    sgd or grad)."""
 
     def __init__(self, desc, cores: List[torch.Tensor], batches, num_bags: int, lr: float,
                  out: torch.Tensor, status: torch.Tensor, update: str = "sgd", aux=None,
@@ -34,6 +36,10 @@ class TrainLoop:
         if dedup and (cache is not None or update == "adagrad"):
             raise ValueError("the backward over distinct indices takes no cache and updates "
                              "by sgd or grad")
+        self.dcore = isinstance(desc, abi.TTDescD)
+        if self.dcore and (cache is not None or dedup or update == "adagrad"):
+            raise ValueError("d-core tables take no cache and no distinct-index backward, "
+                             "and update by sgd or grad")
         if update not in ("sgd", "adagrad", "grad"):
             raise ValueError("update must be sgd, adagrad or grad")
         self.desc, self.g, self.batches, self.B, self.lr = desc, cores, batches, num_bags, lr
@@ -43,9 +49,13 @@ class TrainLoop:
         self.dedup, self.pipeline = dedup, pipeline
         max_nnz = max(b["indices"].numel() for b in batches)
         csize = cache.cache_size if cache is not None else 0
-        self.wss = [abi.workspace_dedup(desc, max_nnz, num_bags) if dedup
-                    else abi.workspace(desc, max_nnz, num_bags, csize)
-                    for _ in range(2 if pipeline else 1)]
+        if self.dcore:
+            make_ws = lambda: abi.workspace_d(desc, max_nnz, num_bags)  # noqa: E731
+        elif dedup:
+            make_ws = lambda: abi.workspace_dedup(desc, max_nnz, num_bags)  # noqa: E731
+        else:
+            make_ws = lambda: abi.workspace(desc, max_nnz, num_bags, csize)  # noqa: E731
+        self.wss = [make_ws() for _ in range(2 if pipeline else 1)]
         self.main = torch.cuda.current_stream()
         self.side = torch.cuda.Stream() if pipeline else self.main  # default priority
         self.ev_plan = [torch.cuda.Event() for _ in range(2)]
@@ -69,7 +79,11 @@ class TrainLoop:
             self.cache.lookup(b["indices"], slot_out=s, count_freq=True, dev_status=self.status,
                               stream=self.side)
             cv = (s, self.rows)
-        if self.dedup:  # host-synchronous: returns the size of the distinct-index batch
+        if self.dcore:
+            abi.tt_bag_plan_d(self.desc, b["indices"], b["offsets"], self.B,
+                              b["per_sample_weights"], ws=ws, dev_status=self.status,
+                              stream=self.side)
+        elif self.dedup:  # host-synchronous: returns the size of the distinct-index batch
             _, self.infos[i] = abi.tt_bag_plan_dedup(self.desc, b["indices"], b["offsets"], self.B,
                                                      b["per_sample_weights"], ws=ws,
                                                      dev_status=self.status, stream=self.side)
@@ -95,13 +109,28 @@ class TrainLoop:
         else:
             cv = self._plan(i)
         w = b["per_sample_weights"]
-        abi.tt_bag_forward(self.desc, self.g, b["indices"], b["offsets"], self.B, w, cache=cv,
-                           out=self.out, ws=ws, dev_status=self.status, planned=True)
+        if self.dcore:
+            abi.tt_bag_forward_d(self.desc, self.g, b["indices"], b["offsets"], self.B, w,
+                                 out=self.out, ws=ws, dev_status=self.status, planned=True)
+        else:
+            abi.tt_bag_forward(self.desc, self.g, b["indices"], b["offsets"], self.B, w,
+                               cache=cv, out=self.out, ws=ws, dev_status=self.status,
+                               planned=True)
         if self.pipeline and not self.dedup:
             # the next grouping starts now, beside this batch's backward (with a cache its
             # lookup and grouping take longer than the backward alone)
             self.cvs[i + 1] = self._plan(i + 1)
-        if self.dedup:
+        if self.dcore:
+            if self.update == "sgd":
+                abi.tt_bag_backward_sgd_d(self.desc, self.g, b["indices"], b["offsets"], self.B,
+                                          b["grad_out"], self.lr, w, ws=ws,
+                                          dev_status=self.status, planned=True)
+            else:
+                abi.tt_bag_backward_grad_d(self.desc, self.g, b["indices"], b["offsets"],
+                                           self.B, b["grad_out"], grad_cores=self.aux,
+                                           per_sample_weights=w, ws=ws,
+                                           dev_status=self.status, planned=True)
+        elif self.dedup:
             info = self.infos.pop(i)
             if self.update == "sgd":
                 abi.tt_bag_backward_sgd_dedup(self.desc, self.g, b["indices"], b["offsets"],

@@ -153,3 +153,53 @@ def test_pipelined_loop_with_distinct_index_backward_matches_oracle():
                 assert rel_err(delta, -wl.lr * grads[t][k]) <= TOL, (i, t, k)
                 m = ~touched[t][k].astype(bool)
                 assert np.array_equal(end[t][k][:, m], start[t][k][:, m]), (i, t, k)
+
+
+def _host_d(wl, gcores):
+    """d device tensors (core k of every table, slice-major) -> T lists of d logical cores."""
+    shapes = W.core_shapes(wl)
+    T, d = wl.num_tables, len(wl.p)
+    res = [[None] * d for _ in range(T)]
+    for k in range(d):
+        arr = gcores[k].detach().cpu().numpy().reshape(T, -1)
+        for t in range(T):
+            res[t][k] = W.logical(arr[t], shapes[k])
+    return res
+
+
+def test_pipelined_loop_four_cores_matches_oracle():
+    """The same loop on the four-core readme-sized table (d-core calls; the grouping is
+    the three-core one of the multiplied-out cut): two steps against the d-core oracle."""
+    print("case train loop readme4", flush=True)
+    wl = W.WORKLOADS["readme4"]
+    T, B, d, steps = wl.num_tables, wl.bags_per_table, len(wl.p), 2
+    cores = W.make_cores(wl)
+    g = [torch.from_numpy(np.concatenate([W.slice_major(cores[t][k]).ravel() for t in range(T)]))
+         .cuda() for k in range(d)]
+    desc = abi.make_desc_d(wl.p, wl.q, wl.ranks, wl.E, T)
+    host_batches = [W.make_batch(wl, k) for k in range(2)]
+    out = torch.empty(T * B, wl.D, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    loop = TrainLoop(desc, g, [to_dev(b) for b in host_batches], B, wl.lr, out, status)
+    snaps, ys = [[x.clone() for x in g]], []
+    for _ in range(steps):
+        loop.step()
+        ys.append(out.clone())
+        snaps.append([x.clone() for x in g])
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for i in range(steps):
+        b = host_batches[i % 2]
+        start, end = _host_d(wl, snaps[i]), _host_d(wl, snaps[i + 1])
+        yref = oracle.forward_d(wl.p, wl.q, wl.ranks, wl.E, start, b["indices"], b["offsets"],
+                                B, b["per_sample_weights"])
+        assert rel_err(ys[i].cpu().numpy(), yref) <= TOL, i
+        grads, touched = oracle.backward_d(wl.p, wl.q, wl.ranks, wl.E, start, b["indices"],
+                                           b["offsets"], B, b["grad_out"],
+                                           b["per_sample_weights"])
+        for t in range(T):
+            for k in range(d):
+                delta = end[t][k].astype(np.float64) - start[t][k].astype(np.float64)
+                assert rel_err(delta, -wl.lr * grads[t][k]) <= TOL, (i, t, k)
+                m = ~touched[t][k].astype(bool)
+                assert np.array_equal(end[t][k][:, m], start[t][k][:, m]), (i, t, k)
