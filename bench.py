@@ -416,13 +416,16 @@ def run_dcore(args, wl, cores, torch, abi, metrics, W):
 def cpu_baseline(wl, cores, budget_s):
     """The oracle, as it stands, on a prefix of the bags of batch 0 of the same
     workload: the prefix doubles until one fwd+bwd run takes >= budget/8 (or covers
-    the batch), then runs repeat until the budget is spent.  Single-threaded C."""
+    the batch), then runs repeat until the budget is spent.  Single-threaded C.  With
+    several tables the prefix is taken from table 0 (bags are table-major), run as a
+    one-table batch with that table's cores."""
     import oracle
     from tensor_train_compressed_ttembeddingbag_amd import workloads as W
     oracle.build()
     b = W.make_batch(wl, 0)
     off = b["offsets"]
-    all_bags = wl.num_tables * wl.bags_per_table
+    all_bags = wl.bags_per_table  # table 0's bags
+    cores = cores[:1]
     bags, t_used, nnz_done, runs, sized = min(16, all_bags), 0.0, 0, 0, False
     while True:
         n = int(off[bags])
@@ -446,9 +449,11 @@ def cpu_baseline(wl, cores, budget_s):
             break
     return {"value": round(t_used * 1e6 / nnz_done, 3), "unit": "us/nnz", "cores": 1,
             "kind": "oracle",
-            "sample": "%d fwd+bwd runs over prefixes of batch 0 (final prefix %d of %d bags, "
+            "sample": "%d fwd+bwd runs over prefixes of batch 0 (final prefix %d of %d bags%s, "
                       "%d nnz in total, %.1f s), fp64 C oracle, one thread; host %s, %d CPUs"
-                      % (runs, bags, all_bags, nnz_done, t_used,
+                      % (runs, bags, all_bags,
+                         " of table 0 of %d" % wl.num_tables if wl.num_tables > 1 else "",
+                         nnz_done, t_used,
                          platform.processor() or platform.machine(), os.cpu_count() or 0)}
 
 
