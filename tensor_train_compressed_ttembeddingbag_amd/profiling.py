@@ -10,6 +10,11 @@
         2048 flop per instruction) and SQ_INSTS_VALU_MFMA_MOPS_F32 (512 flop per unit),
         over the kernel's average duration in a separate --kernel-trace --stats run
 
+    python -m tensor_train_compressed_ttembeddingbag_amd.profiling sq DIR [DIR ...] \
+        --kernels k_fwd,k_bwd --out FILE.txt --command C [--command C ...]
+        per-dispatch means of the SQ counters of several --pmc runs, with the ratios used to
+        read them (time waiting, instructions per MFMA, LDS bank conflicts per LDS access)
+
     python -m tensor_train_compressed_ttembeddingbag_amd.profiling traffic \
         --kernel k_bwd --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \
         --copy-bytes N --out FILE.txt --command-fetch C --command-write C
@@ -194,6 +199,39 @@ def cmd_mfma(a):
     print("\n".join(lines))
 
 
+def cmd_sq(a):
+    m = {}
+    for d in a.dirs:
+        for k, cs in counter_means(d).items():
+            m.setdefault(k, {}).update(cs)
+    lines = ["command=%s" % c for c in a.command]
+    for kern in a.kernels.split(","):
+        cs = _match(m, kern)
+        name = [k for k in m if k == kern or k.startswith(kern + "<")][0]
+        lines.append("kernel=%s" % name)
+        for c in sorted(cs):
+            lines.append("%s=%.6g" % (c, cs[c]))
+        g = cs.get
+        if g("SQ_WAVE_CYCLES"):
+            if g("SQ_WAIT_ANY") is not None:
+                lines.append("ratio_wait_any_per_wave_cycle=%.3f"
+                             % (g("SQ_WAIT_ANY") / g("SQ_WAVE_CYCLES")))
+            if g("SQ_ACTIVE_INST_ANY") is not None:
+                lines.append("ratio_active_inst_per_wave_cycle=%.3f"
+                             % (g("SQ_ACTIVE_INST_ANY") / g("SQ_WAVE_CYCLES")))
+        if g("SQ_INSTS_MFMA"):
+            for c in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU"):
+                if g(c) is not None:
+                    lines.append("ratio_%s_per_mfma=%.2f"
+                                 % (c[9:].lower(), g(c) / g("SQ_INSTS_MFMA")))
+        if g("SQ_INSTS_LDS") and g("SQ_LDS_BANK_CONFLICT") is not None:
+            lines.append("ratio_lds_bank_conflict_cycles_per_lds_inst=%.2f"
+                         % (g("SQ_LDS_BANK_CONFLICT") / g("SQ_INSTS_LDS")))
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def read_traffic(path: str, kernel: str):
     """Bytes per launch of `kernel` from a traffic file, or None when the file is
     missing, names another kernel, or was measured on other sources."""
@@ -225,6 +263,11 @@ def main(argv=None):
               "command-write", "command-copy-fetch", "command-copy-write"):
         t.add_argument("--" + k, required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
+    sq = sub.add_parser("sq")
+    sq.add_argument("dirs", nargs="+")
+    sq.add_argument("--kernels", required=True)
+    sq.add_argument("--out", required=True)
+    sq.add_argument("--command", action="append", required=True)
     mm = sub.add_parser("mfma")
     mm.add_argument("dir")
     for k in ("trace", "kernels", "out", "command", "trace-command"):
@@ -237,6 +280,8 @@ def main(argv=None):
         cmd_traffic(a)
     elif a.cmd == "mfma":
         cmd_mfma(a)
+    elif a.cmd == "sq":
+        cmd_sq(a)
     else:
         print(source_digest())
 
