@@ -8,8 +8,8 @@
 //                           work items.
 //   yinit:  k_yinit         out = zeros, or the pooled cache hits.
 //   forward: k_fwd          one workgroup per work item (piece of an i2 group).
-//   backward: k_bwd         also sums w * dY over the cache-hit runs of one slot.
-//             k_bwd         one workgroup per work item.
+//   backward: k_bwd         one workgroup per work item; with a cache, extra
+//                           workgroups sum w * dY over the cache-hit runs of one slot.
 //             k_seg         core-1 / core-3 segment sums + SGD; cache-row SGD.
 #pragma once
 #include <hip/hip_ext.h>

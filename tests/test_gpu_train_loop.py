@@ -203,3 +203,79 @@ def test_pipelined_loop_four_cores_matches_oracle():
                 assert rel_err(delta, -wl.lr * grads[t][k]) <= TOL, (i, t, k)
                 m = ~touched[t][k].astype(bool)
                 assert np.array_equal(end[t][k][:, m], start[t][k][:, m]), (i, t, k)
+
+
+@pytest.mark.parametrize("update, pipeline", [("adagrad", True), ("grad", True), ("sgd", False)],
+                         ids=["adagrad", "grad", "sgd-unpipelined"])
+def test_loop_update_modes_match_oracle(update, pipeline):
+    """The loop's other update modes and its unpipelined form, on two tables with
+    ranks 32, weights, empty bags and repeats (E short of p1 p2 p3, so ten core-1 slices
+    stay untouched): fused Adagrad (parameter and running-sum
+    deltas against the oracle's Adagrad of the oracle's gradients), gradients returned
+    (against the oracle's gradients; cores unchanged) and SGD without the second stream,
+    two steps each, every step's forward against the oracle."""
+    print("case train loop mode", update, pipeline, flush=True)
+    wl = W.custom("loop modes", p=(40, 44, 50), q=(4, 4, 4), ranks=(32, 32), num_tables=2,
+                  bags_per_table=96, lengths=("uniform", 0, 24), dist=("zipf", 1.1),
+                  init_std=1 / 32 ** 0.5, lr=0.02, weighted=True, num_embeddings=30 * 44 * 50)
+    T, B, steps, eps = wl.num_tables, wl.bags_per_table, 2, 1e-10
+    cores = W.make_cores(wl)
+    g = gpu_cores(wl, cores)
+    aux = None
+    if update == "adagrad":
+        rng = np.random.Generator(np.random.PCG64(3))
+        aux = gpu_cores(wl, [[rng.uniform(0.2, 2.0, c.shape).astype(np.float32) for c in tbl]
+                             for tbl in cores])
+    elif update == "grad":
+        aux = [torch.full_like(x, float("nan")) for x in g]
+    desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E, T)
+    host_batches = [W.make_batch(wl, k) for k in range(2)]
+    out = torch.empty(T * B, wl.D, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    loop = TrainLoop(desc, g, [to_dev(b) for b in host_batches], B, wl.lr, out, status,
+                     update=update, aux=aux, pipeline=pipeline)
+    snaps, asnaps, ys = [[x.clone() for x in g]], [], []
+    if aux is not None:
+        asnaps.append([x.clone() for x in aux])
+    for _ in range(steps):
+        loop.step()
+        ys.append(out.clone())
+        snaps.append([x.clone() for x in g])
+        if aux is not None:
+            asnaps.append([x.clone() for x in aux])
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for i in range(steps):
+        b = host_batches[i % 2]
+        start, end = host_cores(wl, snaps[i]), host_cores(wl, snaps[i + 1])
+        yref = oracle.forward(wl.p, wl.q, wl.ranks, wl.E, start, b["indices"], b["offsets"], B,
+                              per_sample_weights=b["per_sample_weights"])
+        assert rel_err(ys[i].cpu().numpy(), yref) <= TOL, i
+        grads, touched, _, _ = oracle.backward(wl.p, wl.q, wl.ranks, wl.E, start, b["indices"],
+                                               b["offsets"], B, b["grad_out"],
+                                               per_sample_weights=b["per_sample_weights"])
+        if update == "adagrad":
+            s0, s1 = host_cores(wl, asnaps[i]), host_cores(wl, asnaps[i + 1])
+            ref_c, ref_s, _, _ = oracle.adagrad(wl.p, wl.q, wl.ranks, wl.E, start, s0, grads,
+                                                touched, wl.lr, eps)
+        if update == "grad":
+            gk = host_cores(wl, asnaps[i + 1])
+        for t in range(T):
+            for k in range(3):
+                m = ~touched[t][k].astype(bool)
+                old = start[t][k].astype(np.float64)
+                if update == "grad":
+                    got = gk[t][k]
+                    assert rel_err(got, grads[t][k]) <= TOL, (i, t, k)
+                    assert np.all(got[:, m] == 0.0), (i, t, k)
+                    assert np.array_equal(end[t][k], start[t][k]), (i, t, k)
+                    continue
+                if update == "adagrad":
+                    ds = s1[t][k].astype(np.float64) - s0[t][k]
+                    assert rel_err(ds, ref_s[t][k] - s0[t][k]) <= TOL, (i, t, k)
+                    assert np.array_equal(s1[t][k][:, m], s0[t][k][:, m]), (i, t, k)
+                    ref = ref_c[t][k] - old
+                else:
+                    ref = -wl.lr * grads[t][k]
+                assert rel_err(end[t][k].astype(np.float64) - old, ref) <= TOL, (i, t, k)
+                assert np.array_equal(end[t][k][:, m], start[t][k][:, m]), (i, t, k)
