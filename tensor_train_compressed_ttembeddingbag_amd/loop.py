@@ -5,10 +5,14 @@ Every batch is grouped (tt_bag_plan, or tt_bag_plan_dedup for the backward over 
 indices), then runs the planned forward and the planned backward.  Pipelined (default):
 the grouping of batch i+1 is enqueued on a second stream right after the forward of batch i
 (after the backward with the distinct-index grouping, which waits on the host) and runs
-beside the backward; two workspaces alternate; the host waits for a batch's grouping
-before it enqueues the batch's forward, and an event orders a grouping after the last use
-of its workspace (two batches back).  With a cache, the lookup of a batch runs on the grouping
-stream just before its grouping.  Argument marshalling only: every step runs in libttbag.
+beside the backward; the host waits for a batch's grouping before it enqueues the batch's
+forward.  A grouping must not overwrite a workspace before the last step that used it has
+finished.  An event recorded on the main stream costs several microseconds of that stream's
+time, so it is recorded only after every DONE_EVERY-th step, DONE_EVERY + 1 workspaces
+rotate, and a grouping waits for the latest step with an event, which is at or after the last
+user of its workspace.  With a cache, the lookup of a batch runs on the grouping stream just
+before its grouping and writes that batch's slot buffer, last read two batches back, so
+there an event follows every step.  Argument marshalling only: every step runs in libttbag.
 """
 from __future__ import annotations
 
@@ -17,6 +21,8 @@ from typing import List
 import torch
 
 from . import abi
+
+DONE_EVERY = 4  # steps per main-stream "done" event in the pipelined loop (without a cache)
 
 
 class TrainLoop:
@@ -55,13 +61,15 @@ class TrainLoop:
             make_ws = lambda: abi.workspace_dedup(desc, max_nnz, num_bags)  # noqa: E731
         else:
             make_ws = lambda: abi.workspace(desc, max_nnz, num_bags, csize)  # noqa: E731
-        self.wss = [make_ws() for _ in range(2 if pipeline else 1)]
+        # done events after steps k with k % every == every - 1; workspace of step i:
+        # i % (every + 1), so the latest such k <= i - 2 is at or after i - every - 1
+        self.every = 1 if cache is not None else DONE_EVERY
+        self.wss = [make_ws() for _ in range(self.every + 1 if pipeline else 1)]
         self.main = torch.cuda.current_stream()
         self.side = torch.cuda.Stream() if pipeline else self.main  # default priority
         self.ev_plan = [torch.cuda.Event() for _ in range(2)]
-        self.ev_done = [torch.cuda.Event() for _ in range(2)]
-        for e in self.ev_done:
-            e.record(self.main)
+        self.ev_done = {-1: torch.cuda.Event()}  # step -> event after its backward
+        self.ev_done[-1].record(self.main)
         self.next = 0
         self.cvs = {}
         self.infos = {}
@@ -73,7 +81,10 @@ class TrainLoop:
         ws = self.wss[i % len(self.wss)]
         cv = None
         if self.pipeline:
-            self.side.wait_event(self.ev_done[i % 2])
+            k = self.done_step(i)
+            self.side.wait_event(self.ev_done[k])
+            for old in [k0 for k0 in self.ev_done if k0 < k]:
+                del self.ev_done[old]
         if self.cache is not None:
             s = self.slots[i % len(self.batches)]
             self.cache.lookup(b["indices"], slot_out=s, count_freq=True, dev_status=self.status,
@@ -94,6 +105,14 @@ class TrainLoop:
         if self.pipeline:
             self.ev_plan[i % 2].record(self.side)
         return cv
+
+    def done_step(self, i: int) -> int:
+        """The step whose done event the grouping of batch i waits for: the latest step
+        k <= i - 2 with an event (-1 = before the first step).  Batch i's workspace was
+        last used by step i - every - 1, and k >= i - every - 1."""
+        e = self.every
+        k = ((i - 2 + 1) // e) * e - 1
+        return max(k, -1)
 
     def step(self) -> int:
         i = self.next
@@ -157,7 +176,10 @@ class TrainLoop:
                                      per_sample_weights=w, cache=cv, ws=ws,
                                      dev_status=self.status, planned=True)
         if self.pipeline:
-            self.ev_done[i % 2].record(self.main)
+            if i % self.every == self.every - 1:
+                ev = torch.cuda.Event()
+                ev.record(self.main)
+                self.ev_done[i] = ev
             if self.dedup:
                 # the distinct-index grouping waits on the host for its size, so it is
                 # enqueued after this backward, which then runs meanwhile

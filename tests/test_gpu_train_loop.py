@@ -279,3 +279,47 @@ def test_loop_update_modes_match_oracle(update, pipeline):
                     ref = -wl.lr * grads[t][k]
                 assert rel_err(end[t][k].astype(np.float64) - old, ref) <= TOL, (i, t, k)
                 assert np.array_equal(end[t][k][:, m], start[t][k][:, m]), (i, t, k)
+
+
+@pytest.mark.parametrize("dedup", [False, True], ids=["plain", "dedup"])
+def test_loop_reuses_its_workspaces_over_many_steps(dedup):
+    """Eleven pipelined steps over three batches of different sizes, so that every one
+    of the loop's workspaces is reused (its done events follow only every few steps):
+    every step's forward and core update against the oracle."""
+    from tensor_train_compressed_ttembeddingbag_amd import loop as L
+    print("case train loop reuse", dedup, flush=True)
+    wl = W.custom("loop reuse", p=(12, 10, 14), q=(4, 4, 4), ranks=(16, 32), num_tables=2,
+                  bags_per_table=48, lengths=("uniform", 0, 30), dist=("zipf", 1.2),
+                  init_std=1 / 32 ** 0.5, lr=0.002, weighted=True)  # stays bounded 11 steps
+    T, B, steps = wl.num_tables, wl.bags_per_table, 11
+    assert steps > 2 * (L.DONE_EVERY + 1)
+    cores = W.make_cores(wl)
+    g = gpu_cores(wl, cores)
+    desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E, T)
+    host_batches = [W.make_batch(wl, k) for k in range(3)]
+    assert len({len(b["indices"]) for b in host_batches}) == 3
+    out = torch.empty(T * B, wl.D, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    loop = TrainLoop(desc, g, [to_dev(b) for b in host_batches], B, wl.lr, out, status,
+                     dedup=dedup)
+    assert len(loop.wss) == L.DONE_EVERY + 1
+    snaps, ys = [[x.clone() for x in g]], []
+    for _ in range(steps):
+        loop.step()
+        ys.append(out.clone())
+        snaps.append([x.clone() for x in g])
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for i in range(steps):
+        b = host_batches[i % 3]
+        start, end = host_cores(wl, snaps[i]), host_cores(wl, snaps[i + 1])
+        yref = oracle.forward(wl.p, wl.q, wl.ranks, wl.E, start, b["indices"], b["offsets"], B,
+                              per_sample_weights=b["per_sample_weights"])
+        assert rel_err(ys[i].cpu().numpy(), yref) <= TOL, i
+        grads, touched, _, _ = oracle.backward(wl.p, wl.q, wl.ranks, wl.E, start, b["indices"],
+                                               b["offsets"], B, b["grad_out"],
+                                               per_sample_weights=b["per_sample_weights"])
+        for t in range(T):
+            for k in range(3):
+                delta = end[t][k].astype(np.float64) - start[t][k].astype(np.float64)
+                assert rel_err(delta, -wl.lr * grads[t][k]) <= TOL, (i, t, k)
