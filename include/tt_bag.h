@@ -489,6 +489,14 @@ int tt_profile_num_kernels(void);
 const char *tt_profile_kernel_name(int kernel_id);
 int tt_profile_read(int kernel_id, double *total_ms, int64_t *launches);
 
+/* Bound of every wait a kernel of this library makes for other workgroups of its own
+ * launch (the grouping's grid-wide barriers, the forward's check that out is cleared):
+ * the number of polls after which a waiting workgroup gives up, reports
+ * TT_DEV_SYNC_TIMEOUT and leaves (every workgroup still ends normally).  polls < 0
+ * restores the default (2^22 polls).  Takes effect for calls made after it, in every
+ * thread; meant for tests that drive the give-up path from the host. */
+int tt_debug_sync_poll_limit(int64_t polls);
+
 /* Static description of a return code. */
 const char *tt_status_string(int code);
 

@@ -66,7 +66,9 @@ _lib = None
 def _L():
     global _lib
     if _lib is None:
-        lib = ctypes.CDLL(build())
+        # TT_ORACLE_LIB: a build of the same source to load instead (the sanitizer test
+        # runs the pins against an -fsanitize=address,undefined build this way)
+        lib = ctypes.CDLL(os.environ.get("TT_ORACLE_LIB") or build())
         P = ctypes.c_void_p
         lib.oracle_forward.argtypes = [P, P, P, ctypes.c_int64, P, ctypes.c_int64, P, P, P,
                                        ctypes.c_int64, P]

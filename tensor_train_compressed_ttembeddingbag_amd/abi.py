@@ -130,6 +130,7 @@ _SIG = {
     "tt_profile_num_kernels": (ctypes.c_int, []),
     "tt_profile_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
     "tt_profile_read": (ctypes.c_int, [ctypes.c_int, _P, _P]),
+    "tt_debug_sync_poll_limit": (ctypes.c_int, [_I64]),
     "tt_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 EXPORTS = tuple(_SIG)
@@ -187,6 +188,31 @@ def _need(t: torch.Tensor, dtype, name: str):
         raise ValueError("%s must be contiguous" % name)
 
 
+def _numel(t: torch.Tensor, n: int, name: str):
+    """The kernels index every buffer by the sizes the call states, so a buffer of any
+    other size would be read or written out of bounds: reject it here."""
+    if t.numel() != n:
+        raise ValueError("%s has %d elements, expected %d" % (name, t.numel(), n))
+
+
+def _dim(desc) -> int:
+    return desc.q[0] * desc.q[1] * desc.q[2]
+
+
+def _core_numels(desc):
+    """Elements of core k of all tables: T * p_k * R_{k-1} * q_k * R_k."""
+    T, r = desc.num_tables, (1, desc.ranks[0], desc.ranks[1], 1)
+    return tuple(T * desc.p[k] * r[k] * desc.q[k] * r[k + 1] for k in range(3))
+
+
+def _batch_sizes(desc, indices, offsets, num_bags: int, per_sample_weights=None):
+    """offsets must hold T*num_bags + 1 entries (the terminal one included) and the
+    per-sample weights one per index."""
+    _numel(offsets, desc.num_tables * int(num_bags) + 1, "offsets")
+    if per_sample_weights is not None:
+        _numel(per_sample_weights, indices.numel(), "per_sample_weights")
+
+
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
@@ -221,11 +247,14 @@ def workspace(desc: TTDesc, nnz: int, num_bags: int, cache_size: int = 0, device
 _core_arrays = {}
 
 
-def _cores(cores: Sequence[torch.Tensor]):
+def _cores(cores: Sequence[torch.Tensor], desc=None, name: str = "cores"):
     if len(cores) != 3:
         raise ValueError("three cores expected")
     for c in cores:
-        _need(c, torch.float32, "cores")
+        _need(c, torch.float32, name)
+    if desc is not None:
+        for k, n in enumerate(_core_numels(desc)):
+            _numel(cores[k], n, "%s[%d]" % (name, k))
     key = (cores[0].data_ptr(), cores[1].data_ptr(), cores[2].data_ptr())
     arr = _core_arrays.get(key)
     if arr is None:  # pointer triples are reused across calls: keep their ctypes arrays
@@ -235,12 +264,16 @@ def _cores(cores: Sequence[torch.Tensor]):
     return arr
 
 
-def _cache_view(cache):
+def _cache_view(cache, desc=None, nnz: Optional[int] = None):
     if cache is None:
         return None, None
     slots, rows = cache
     _need(slots, torch.int32, "cache slots")
     _need(rows, torch.float32, "cache rows")
+    if rows.dim() != 2 or (desc is not None and rows.shape[1] != _dim(desc)):
+        raise ValueError("cache rows must be [cache_size, D], got %s" % (tuple(rows.shape),))
+    if nnz is not None:
+        _numel(slots, nnz, "cache slots")
     v = TTCacheView()
     v.slots = slots.data_ptr()
     v.rows = rows.data_ptr()
@@ -255,7 +288,8 @@ def tt_bag_plan(desc: TTDesc, indices, offsets, num_bags: int, per_sample_weight
     _need(offsets, torch.int64, "offsets")
     if per_sample_weights is not None:
         _need(per_sample_weights, torch.float32, "per_sample_weights")
-    view, csize = _cache_view(cache)
+    _batch_sizes(desc, indices, offsets, num_bags, per_sample_weights)
+    view, csize = _cache_view(cache, desc, indices.numel())
     if ws is None:
         ws = workspace(desc, indices.numel(), num_bags, csize or 0, indices.device)
     _need(ws, torch.uint8, "ws")
@@ -278,18 +312,21 @@ def tt_bag_forward(desc: TTDesc, cores, indices, offsets, num_bags: int,
     _need(offsets, torch.int64, "offsets")
     if per_sample_weights is not None:
         _need(per_sample_weights, torch.float32, "per_sample_weights")
-    D = desc.q[0] * desc.q[1] * desc.q[2]
+    _batch_sizes(desc, indices, offsets, num_bags, per_sample_weights)
+    D = _dim(desc)
     if out is None:
         out = torch.empty(desc.num_tables * num_bags, D, dtype=torch.float32, device=indices.device)
     _need(out, torch.float32, "out")
-    view, csize = _cache_view(cache)
+    _numel(out, desc.num_tables * int(num_bags) * D, "out")
+    view, csize = _cache_view(cache, desc, indices.numel())
     if ws is None:
         ws = workspace(desc, indices.numel(), num_bags, csize or 0, indices.device)
     _need(ws, torch.uint8, "ws")
     if dev_status is not None:
         _need(dev_status, torch.int32, "dev_status")
+    core_ptrs = _cores(cores, desc)
     fn = lib().tt_bag_forward_planned if planned else lib().tt_bag_forward
-    rc = fn(ctypes.byref(desc), _cores(cores), _ptr(indices), indices.numel(),
+    rc = fn(ctypes.byref(desc), core_ptrs, _ptr(indices), indices.numel(),
                               _ptr(offsets), int(num_bags), _ptr(per_sample_weights),
                               None if view is None else ctypes.byref(view), _ptr(out), _ptr(ws),
                               ws.numel(), _ptr(dev_status), _stream(stream, indices))
@@ -307,14 +344,17 @@ def tt_bag_backward_sgd(desc: TTDesc, cores, indices, offsets, num_bags: int, gr
     _need(grad_out, torch.float32, "grad_out")
     if per_sample_weights is not None:
         _need(per_sample_weights, torch.float32, "per_sample_weights")
-    view, csize = _cache_view(cache)
+    _batch_sizes(desc, indices, offsets, num_bags, per_sample_weights)
+    _numel(grad_out, desc.num_tables * int(num_bags) * _dim(desc), "grad_out")
+    view, csize = _cache_view(cache, desc, indices.numel())
     if ws is None:
         ws = workspace(desc, indices.numel(), num_bags, csize or 0, indices.device)
     _need(ws, torch.uint8, "ws")
     if dev_status is not None:
         _need(dev_status, torch.int32, "dev_status")
+    core_ptrs = _cores(cores, desc)
     fn = lib().tt_bag_backward_sgd_planned if planned else lib().tt_bag_backward_sgd
-    rc = fn(ctypes.byref(desc), _cores(cores), _ptr(indices), indices.numel(),
+    rc = fn(ctypes.byref(desc), core_ptrs, _ptr(indices), indices.numel(),
                                    _ptr(offsets), int(num_bags), _ptr(per_sample_weights),
                                    None if view is None else ctypes.byref(view), _ptr(grad_out),
                                    float(lr), _ptr(ws), ws.numel(), _ptr(dev_status),
@@ -329,7 +369,9 @@ def _batch_args(desc, indices, offsets, num_bags, grad_out, per_sample_weights, 
     _need(grad_out, torch.float32, "grad_out")
     if per_sample_weights is not None:
         _need(per_sample_weights, torch.float32, "per_sample_weights")
-    view, csize = _cache_view(cache)
+    _batch_sizes(desc, indices, offsets, num_bags, per_sample_weights)
+    _numel(grad_out, desc.num_tables * int(num_bags) * _dim(desc), "grad_out")
+    view, csize = _cache_view(cache, desc, indices.numel())
     if ws is None:
         ws = workspace(desc, indices.numel(), num_bags, csize or 0, indices.device)
     _need(ws, torch.uint8, "ws")
@@ -338,12 +380,13 @@ def _batch_args(desc, indices, offsets, num_bags, grad_out, per_sample_weights, 
     return view, csize, ws
 
 
-def _rows_arg(t, csize, name):
+def _rows_arg(t, csize, name, D):
     if not csize:
         return None
     if t is None:
         raise ValueError("%s is required with a cache" % name)
     _need(t, torch.float32, name)
+    _numel(t, int(csize) * D, name)
     return t
 
 
@@ -355,11 +398,13 @@ def tt_bag_backward_adagrad(desc: TTDesc, cores, indices, offsets, num_bags: int
     tensors shaped like the cores (and state_rows for the cache rows), updated in place."""
     view, csize, ws = _batch_args(desc, indices, offsets, num_bags, grad_out, per_sample_weights,
                                   cache, ws, dev_status)
-    st = _cores(state)
-    sr = _rows_arg(state_rows, csize, "state_rows")
+    st = _cores(state, desc, "state")
+    sr = _rows_arg(state_rows, csize, "state_rows", _dim(desc))
     name = "tt_bag_backward_adagrad_planned" if planned else "tt_bag_backward_adagrad"
-    rc = getattr(lib(), name)(ctypes.byref(desc), _cores(cores), _ptr(indices), indices.numel(),
-                              _ptr(offsets), int(num_bags), _ptr(per_sample_weights),
+    core_ptrs = _cores(cores, desc)
+    rc = getattr(lib(), name)(ctypes.byref(desc), core_ptrs, _ptr(indices),
+                              indices.numel(), _ptr(offsets), int(num_bags),
+                              _ptr(per_sample_weights),
                               None if view is None else ctypes.byref(view), _ptr(grad_out),
                               float(lr), float(eps), st, _ptr(sr), _ptr(ws), ws.numel(),
                               _ptr(dev_status), _stream(stream, indices))
@@ -377,12 +422,15 @@ def tt_bag_backward_grad(desc: TTDesc, cores, indices, offsets, num_bags: int, g
         grad_cores = [torch.empty_like(c) for c in cores]
     if csize and grad_rows is None:
         grad_rows = torch.empty_like(cache[1])
-    gr = _rows_arg(grad_rows, csize, "grad_rows")
+    gr = _rows_arg(grad_rows, csize, "grad_rows", _dim(desc))
     name = "tt_bag_backward_grad_planned" if planned else "tt_bag_backward_grad"
-    rc = getattr(lib(), name)(ctypes.byref(desc), _cores(cores), _ptr(indices), indices.numel(),
-                              _ptr(offsets), int(num_bags), _ptr(per_sample_weights),
+    core_ptrs = _cores(cores, desc)
+    grad_ptrs = _cores(grad_cores, desc, "grad_cores")
+    rc = getattr(lib(), name)(ctypes.byref(desc), core_ptrs, _ptr(indices),
+                              indices.numel(), _ptr(offsets), int(num_bags),
+                              _ptr(per_sample_weights),
                               None if view is None else ctypes.byref(view), _ptr(grad_out),
-                              _cores(grad_cores), _ptr(gr), _ptr(ws), ws.numel(),
+                              grad_ptrs, _ptr(gr), _ptr(ws), ws.numel(),
                               _ptr(dev_status), _stream(stream, indices))
     _check(name, rc)
     return grad_cores, gr
@@ -397,8 +445,10 @@ def tt_bag_weight_grad(desc: TTDesc, cores, indices, offsets, num_bags: int, gra
     if out is None:
         out = torch.empty(indices.numel(), dtype=torch.float32, device=indices.device)
     _need(out, torch.float32, "out")
+    _numel(out, indices.numel(), "out")
     name = "tt_bag_weight_grad_planned" if planned else "tt_bag_weight_grad"
-    rc = getattr(lib(), name)(ctypes.byref(desc), _cores(cores), _ptr(indices), indices.numel(),
+    core_ptrs = _cores(cores, desc)
+    rc = getattr(lib(), name)(ctypes.byref(desc), core_ptrs, _ptr(indices), indices.numel(),
                               _ptr(offsets), int(num_bags), _ptr(per_sample_weights),
                               None if view is None else ctypes.byref(view), _ptr(grad_out),
                               _ptr(out), _ptr(ws), ws.numel(), _ptr(dev_status), _stream(stream, indices))
@@ -408,7 +458,8 @@ def tt_bag_weight_grad(desc: TTDesc, cores, indices, offsets, num_bags: int, gra
 
 def tt_init_cores(desc: TTDesc, cores, dist: int, scale: float, seed: int, stream=None) -> None:
     """Fill the three core tensors (slice-major, all tables) on the device (see tt_bag.h)."""
-    _check("tt_init_cores", lib().tt_init_cores(ctypes.byref(desc), _cores(cores), int(dist),
+    core_ptrs = _cores(cores, desc)
+    _check("tt_init_cores", lib().tt_init_cores(ctypes.byref(desc), core_ptrs, int(dist),
                                                 float(scale), int(seed) & ((1 << 64) - 1),
                                                 _stream(stream)))
 
@@ -416,11 +467,13 @@ def tt_init_cores(desc: TTDesc, cores, dist: int, scale: float, seed: int, strea
 def tt_full_weight(desc: TTDesc, cores, first: int, count: int, table: int = 0, out=None,
                    stream=None) -> torch.Tensor:
     """Rows [first, first + count) of one table as a dense [count, D] tensor."""
-    D = desc.q[0] * desc.q[1] * desc.q[2]
+    D = _dim(desc)
     if out is None:
         out = torch.empty(int(count), D, dtype=torch.float32, device=cores[0].device)
     _need(out, torch.float32, "out")
-    _check("tt_full_weight", lib().tt_full_weight(ctypes.byref(desc), _cores(cores), int(table),
+    _numel(out, max(int(count), 0) * D, "out")
+    core_ptrs = _cores(cores, desc)
+    _check("tt_full_weight", lib().tt_full_weight(ctypes.byref(desc), core_ptrs, int(table),
                                                   int(first), int(count), _ptr(out),
                                                   _stream(stream)))
     return out
@@ -440,6 +493,8 @@ def tt_bag_route(desc: TTDesc, indices, offsets, num_bags: int, slots=None, cach
     _need(offsets, torch.int64, "offsets")
     if slots is not None:
         _need(slots, torch.int32, "slots")
+        _numel(slots, indices.numel(), "slots")
+    _batch_sizes(desc, indices, offsets, num_bags)
     dev = indices.device
     order = torch.empty(indices.numel(), dtype=torch.int32, device=dev)
     goff = torch.empty(desc.num_tables * desc.p[1] + 2, dtype=torch.int32, device=dev)
@@ -450,6 +505,11 @@ def tt_bag_route(desc: TTDesc, indices, offsets, num_bags: int, slots=None, cach
                             _ptr(ws), ws.numel(), _ptr(dev_status), _stream(stream, indices))
     _check("tt_bag_route", rc)
     return order, goff
+
+
+def tt_debug_sync_poll_limit(polls: int) -> None:
+    """Bound the device-side waits of later calls (polls < 0: the default); see tt_bag.h."""
+    _check("tt_debug_sync_poll_limit", lib().tt_debug_sync_poll_limit(int(polls)))
 
 
 def tt_profile_enable(on: bool = True) -> None:
@@ -488,6 +548,7 @@ class Cache:
         if slot_out is None:
             slot_out = torch.empty(indices.numel(), dtype=torch.int32, device=indices.device)
         _need(slot_out, torch.int32, "slot_out")
+        _numel(slot_out, indices.numel(), "slot_out")
         _check("tt_cache_lookup", lib().tt_cache_lookup(self._h, _ptr(indices), indices.numel(),
                                                         _ptr(slot_out), 1 if count_freq else 0,
                                                         _ptr(dev_status), _stream(stream, indices)))
@@ -495,8 +556,10 @@ class Cache:
 
     def populate(self, cores, rows, stream=None) -> int:
         _need(rows, torch.float32, "rows")
+        _numel(rows, self.cache_size * _dim(self.desc), "rows")
         n = ctypes.c_int64(0)
-        _check("tt_cache_populate", lib().tt_cache_populate(self._h, _cores(cores), _ptr(rows),
+        core_ptrs = _cores(cores, self.desc)
+        _check("tt_cache_populate", lib().tt_cache_populate(self._h, core_ptrs, _ptr(rows),
                                                             ctypes.byref(n), _stream(stream)))
         return int(n.value)
 
@@ -554,6 +617,7 @@ def tt_bag_plan_dedup(desc: TTDesc, indices, offsets, num_bags: int, per_sample_
     _need(offsets, torch.int64, "offsets")
     if per_sample_weights is not None:
         _need(per_sample_weights, torch.float32, "per_sample_weights")
+    _batch_sizes(desc, indices, offsets, num_bags, per_sample_weights)
     if ws is None:
         ws = workspace_dedup(desc, indices.numel(), num_bags, indices.device)
     _need(ws, torch.uint8, "ws")
@@ -567,6 +631,19 @@ def tt_bag_plan_dedup(desc: TTDesc, indices, offsets, num_bags: int, per_sample_
     return ws, (int(info[0]), int(info[1]))
 
 
+def _dedup_args(desc, indices, offsets, num_bags, grad_out, per_sample_weights, ws, dev_status):
+    _need(indices, torch.int64, "indices")
+    _need(offsets, torch.int64, "offsets")
+    _need(grad_out, torch.float32, "grad_out")
+    if per_sample_weights is not None:
+        _need(per_sample_weights, torch.float32, "per_sample_weights")
+    _batch_sizes(desc, indices, offsets, num_bags, per_sample_weights)
+    _numel(grad_out, desc.num_tables * int(num_bags) * _dim(desc), "grad_out")
+    _need(ws, torch.uint8, "ws")
+    if dev_status is not None:
+        _need(dev_status, torch.int32, "dev_status")
+
+
 def _info(info):
     return (ctypes.c_int64 * 2)(int(info[0]), int(info[1]))
 
@@ -575,9 +652,9 @@ def tt_bag_backward_sgd_dedup(desc: TTDesc, cores, indices, offsets, num_bags: i
                               lr: float, info, per_sample_weights=None, ws=None, dev_status=None,
                               stream=None) -> None:
     """In-place SGD through the backward over distinct indices (plan: tt_bag_plan_dedup)."""
-    _need(grad_out, torch.float32, "grad_out")
-    _need(ws, torch.uint8, "ws")
-    rc = lib().tt_bag_backward_sgd_dedup(ctypes.byref(desc), _cores(cores), _ptr(indices),
+    _dedup_args(desc, indices, offsets, num_bags, grad_out, per_sample_weights, ws, dev_status)
+    core_ptrs = _cores(cores, desc)
+    rc = lib().tt_bag_backward_sgd_dedup(ctypes.byref(desc), core_ptrs, _ptr(indices),
                                          indices.numel(), _ptr(offsets), int(num_bags),
                                          _ptr(per_sample_weights), _ptr(grad_out), float(lr),
                                          _info(info), _ptr(ws), ws.numel(), _ptr(dev_status),
@@ -589,14 +666,15 @@ def tt_bag_backward_grad_dedup(desc: TTDesc, cores, indices, offsets, num_bags: 
                                info, grad_cores=None, per_sample_weights=None, ws=None,
                                dev_status=None, stream=None):
     """Dense core gradients through the backward over distinct indices; returns them."""
-    _need(grad_out, torch.float32, "grad_out")
-    _need(ws, torch.uint8, "ws")
+    _dedup_args(desc, indices, offsets, num_bags, grad_out, per_sample_weights, ws, dev_status)
     if grad_cores is None:
         grad_cores = [torch.empty_like(c) for c in cores]
-    rc = lib().tt_bag_backward_grad_dedup(ctypes.byref(desc), _cores(cores), _ptr(indices),
+    core_ptrs = _cores(cores, desc)
+    grad_ptrs = _cores(grad_cores, desc, "grad_cores")
+    rc = lib().tt_bag_backward_grad_dedup(ctypes.byref(desc), core_ptrs, _ptr(indices),
                                           indices.numel(), _ptr(offsets), int(num_bags),
                                           _ptr(per_sample_weights), _ptr(grad_out),
-                                          _cores(grad_cores), _info(info), _ptr(ws), ws.numel(),
+                                          grad_ptrs, _info(info), _ptr(ws), ws.numel(),
                                           _ptr(dev_status), _stream(stream, indices))
     _check("tt_bag_backward_grad_dedup", rc)
     return grad_cores
@@ -621,11 +699,17 @@ def make_desc_d(p, q, ranks, num_embeddings: Optional[int] = None, num_tables: i
     return x
 
 
-def _cores_d(desc: TTDescD, cores):
+def _core_numels_d(desc: TTDescD):
+    d, r = desc.d, [1] + [desc.ranks[k] for k in range(desc.d - 1)] + [1]
+    return tuple(desc.num_tables * desc.p[k] * r[k] * desc.q[k] * r[k + 1] for k in range(d))
+
+
+def _cores_d(desc: TTDescD, cores, name: str = "cores"):
     if len(cores) != desc.d:
         raise ValueError("%d cores expected" % desc.d)
-    for c in cores:
-        _need(c, torch.float32, "cores")
+    for k, (c, n) in enumerate(zip(cores, _core_numels_d(desc))):
+        _need(c, torch.float32, name)
+        _numel(c, n, "%s[%d]" % (name, k))
     return (ctypes.c_void_p * desc.d)(*[c.data_ptr() for c in cores])
 
 
@@ -653,6 +737,7 @@ def _args_d(desc, indices, offsets, num_bags, per_sample_weights, ws, dev_status
     _need(offsets, torch.int64, "offsets")
     if per_sample_weights is not None:
         _need(per_sample_weights, torch.float32, "per_sample_weights")
+    _batch_sizes(desc, indices, offsets, num_bags, per_sample_weights)
     if ws is None:
         ws = workspace_d(desc, indices.numel(), num_bags, indices.device)
     _need(ws, torch.uint8, "ws")
@@ -682,8 +767,10 @@ def tt_bag_forward_d(desc: TTDescD, cores, indices, offsets, num_bags: int,
         out = torch.empty(desc.num_tables * num_bags, D, dtype=torch.float32,
                           device=indices.device)
     _need(out, torch.float32, "out")
+    _numel(out, desc.num_tables * int(num_bags) * D, "out")
+    core_ptrs = _cores_d(desc, cores)
     fn = lib().tt_bag_forward_d_planned if planned else lib().tt_bag_forward_d
-    rc = fn(ctypes.byref(desc), _cores_d(desc, cores), _ptr(indices),
+    rc = fn(ctypes.byref(desc), core_ptrs, _ptr(indices),
                                 indices.numel(), _ptr(offsets), int(num_bags),
                                 _ptr(per_sample_weights), _ptr(out), _ptr(ws), ws.numel(),
                                 _ptr(dev_status), _stream(stream, indices))
@@ -697,8 +784,11 @@ def tt_bag_backward_sgd_d(desc: TTDescD, cores, indices, offsets, num_bags: int,
     """In-place SGD on the d cores."""
     ws = _args_d(desc, indices, offsets, num_bags, per_sample_weights, ws, dev_status)
     _need(grad_out, torch.float32, "grad_out")
+    _numel(grad_out, desc.num_tables * int(num_bags) * math.prod(desc.q[k] for k in range(desc.d)),
+           "grad_out")
+    core_ptrs = _cores_d(desc, cores)
     fn = lib().tt_bag_backward_sgd_d_planned if planned else lib().tt_bag_backward_sgd_d
-    rc = fn(ctypes.byref(desc), _cores_d(desc, cores), _ptr(indices),
+    rc = fn(ctypes.byref(desc), core_ptrs, _ptr(indices),
                                      indices.numel(), _ptr(offsets), int(num_bags),
                                      _ptr(per_sample_weights), _ptr(grad_out), float(lr),
                                      _ptr(ws), ws.numel(), _ptr(dev_status),
@@ -712,13 +802,17 @@ def tt_bag_backward_grad_d(desc: TTDescD, cores, indices, offsets, num_bags: int
     """Dense gradients with respect to the d cores (fully overwritten); returns them."""
     ws = _args_d(desc, indices, offsets, num_bags, per_sample_weights, ws, dev_status)
     _need(grad_out, torch.float32, "grad_out")
+    _numel(grad_out, desc.num_tables * int(num_bags) * math.prod(desc.q[k] for k in range(desc.d)),
+           "grad_out")
     if grad_cores is None:
         grad_cores = [torch.empty_like(c) for c in cores]
+    core_ptrs = _cores_d(desc, cores)
+    grad_ptrs = _cores_d(desc, grad_cores, "grad_cores")
     fn = lib().tt_bag_backward_grad_d_planned if planned else lib().tt_bag_backward_grad_d
-    rc = fn(ctypes.byref(desc), _cores_d(desc, cores), _ptr(indices),
+    rc = fn(ctypes.byref(desc), core_ptrs, _ptr(indices),
                                       indices.numel(), _ptr(offsets), int(num_bags),
                                       _ptr(per_sample_weights), _ptr(grad_out),
-                                      _cores_d(desc, grad_cores), _ptr(ws), ws.numel(),
+                                      grad_ptrs, _ptr(ws), ws.numel(),
                                       _ptr(dev_status), _stream(stream, indices))
     _check("tt_bag_backward_grad_d", rc)
     return grad_cores

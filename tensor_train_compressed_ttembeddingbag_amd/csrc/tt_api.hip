@@ -40,6 +40,8 @@ namespace {
 constexpr size_t ALIGN = 256;
 constexpr size_t LDS_LIMIT = 160 * 1024;
 std::atomic<unsigned> g_epoch{1};
+constexpr unsigned SYNC_POLLS = 1u << 22;  // default bound of a device-side wait
+std::atomic<unsigned> g_sync_polls{SYNC_POLLS};
 
 struct Plan {
   DevArgs a;
@@ -184,6 +186,7 @@ void bind_ws(Plan *P, void *ws) {
   a.part2 = (float *)(b + P->o_p2);
   a.epoch = g_epoch.fetch_add(1);
   if (a.epoch == 0) a.epoch = g_epoch.fetch_add(1);
+  a.sync_polls = g_sync_polls.load(std::memory_order_relaxed);
 }
 
 int check_ws(const Plan &P, void *ws, size_t ws_bytes) {
@@ -217,6 +220,12 @@ const char *tt_status_string(int code) {
     case TT_EFULL: return "cache capacity exceeded";
     default: return "unknown status";
   }
+}
+
+int tt_debug_sync_poll_limit(int64_t polls) {
+  if (polls > (int64_t)0xffffffffu) return TT_EINVAL;
+  g_sync_polls.store(polls < 0 ? SYNC_POLLS : (unsigned)polls, std::memory_order_relaxed);
+  return TT_OK;
 }
 
 size_t tt_bag_workspace_size(const tt_desc *desc, int64_t nnz, int64_t num_bags,
@@ -280,6 +289,25 @@ static int prepare(Plan *P, const tt_desc *desc, const int64_t *indices, int64_t
 static int check_cores(const float *const cores[3]) {
   return (!cores || !cores[0] || !cores[1] || !cores[2]) ? TT_EINVAL : TT_OK;
 }
+
+}  // extern "C"
+
+namespace ttb {
+// Where a three-core plan keeps its header inside ws, and the fingerprint a plan made
+// for these arguments carries (no cache).  Used by the backward over distinct indices,
+// whose kernels read the real batch's plan and must see whether it is this batch's.
+int plan_identity(const tt_desc *desc, int64_t nnz, int64_t num_bags, const void *idx,
+                  const void *off, const void *psw, void *ws, int **hdr, unsigned *fp) {
+  Plan P;
+  const int rc = make_plan(desc, nnz, num_bags, 0, &P);
+  if (rc) return rc;
+  *hdr = (int *)((char *)ws + P.o_hdr);
+  *fp = plan_fingerprint(desc, nnz, num_bags, 0, idx, off, psw, nullptr);
+  return TT_OK;
+}
+}  // namespace ttb
+
+extern "C" {
 
 int tt_bag_plan(const tt_desc *desc, const int64_t *indices, int64_t nnz, const int64_t *offsets,
                 int64_t num_bags, const float *per_sample_weights, const tt_cache_view *cache,

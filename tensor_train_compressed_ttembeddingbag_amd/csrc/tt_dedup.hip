@@ -159,17 +159,34 @@ __global__ __launch_bounds__(DD_T) void k_dd_voff(const int64_t *__restrict__ Rt
   voff[b] = Rt[t] + (j < cntt ? j : cntt);
 }
 
+// The plan both passes read (sorted keys, bags, runs) belongs to the batch of the call
+// only if the real batch's plan header holds this call's fingerprint.  Otherwise they
+// touch nothing, report DEV_STALE_PLAN and mark the virtual batch's plan invalid, so
+// that the planned backward that follows leaves the cores alone as well.
+__device__ __forceinline__ bool dd_plan_ok(const int *rhdr, unsigned rfp, int *vhdr,
+                                           unsigned vfp, int32_t *status) {
+  if (rhdr[H_PLAN] == (int)rfp) return true;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    set_status(status, DEV_STALE_PLAN);
+    vhdr[H_PLAN] = (int)~vfp;
+  }
+  return false;
+}
+
 // pass 1: per 32-element chunk of the sorted order, the sum of w_n dY[bag n] of each run's
 // piece in the chunk, stored at the piece's first sorted position
 __global__ __launch_bounds__(DD_T) void k_dd_frag(const unsigned long long *__restrict__ keys,
                                                   int nnz, int pbits, unsigned long long inv,
-                                                  const int *__restrict__ bagv,
+                                                  const int *__restrict__ bagv, int NB,
                                                   const int64_t *__restrict__ off,
                                                   const float *__restrict__ psw, int mean,
                                                   const float *__restrict__ dY, int D,
-                                                  float *__restrict__ frag) {
+                                                  float *__restrict__ frag, const int *rhdr,
+                                                  unsigned rfp, int *vhdr, unsigned vfp,
+                                                  int32_t *status) {
   __shared__ float s_w[DD_CH];
   __shared__ int s_b[DD_CH], s_cut[DD_CH];
+  if (!dd_plan_ok(rhdr, rfp, vhdr, vfp, status)) return;
   const int m0 = blockIdx.x * DD_CH;
   const unsigned long long pmask = (1ull << pbits) - 1ull;
   if (threadIdx.x < DD_CH) {
@@ -179,8 +196,8 @@ __global__ __launch_bounds__(DD_T) void k_dd_frag(const unsigned long long *__re
     if (m < nnz) {
       const unsigned long long k = keys[m];
       if (dd_valid(k, pbits, inv)) {
-        const int n = (int)(k & pmask);
-        bv = bagv[n];
+        const int n = min((int)(k & pmask), nnz - 1);
+        bv = min(max(bagv[n], 0), NB - 1);
         wv = psw ? psw[n] : 1.f;
         if (mean) {
           const long long len = off[bv + 1] - off[bv];
@@ -225,8 +242,11 @@ __global__ __launch_bounds__(DD_T) void k_dd_gu(const int *__restrict__ rstart,
                                                 const int *__restrict__ rtab,
                                                 const int64_t *__restrict__ Rt, int Bp, int D,
                                                 const float *__restrict__ frag,
-                                                float *__restrict__ Gu) {
+                                                float *__restrict__ Gu, const int *rhdr,
+                                                unsigned rfp, int *vhdr, unsigned vfp,
+                                                int32_t *status) {
   __shared__ float s_part[DD_T];
+  if (!dd_plan_ok(rhdr, rfp, vhdr, vfp, status)) return;
   const int u = blockIdx.x;
   const int a = rstart[u], z = rend[u], t = rtab[u];
   const long long vb = (long long)t * Bp + (u - Rt[t]);
@@ -423,21 +443,31 @@ static int backward_dedup(const tt_desc *desc, float *const cores[3], const int6
     return TT_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   float *Gu = at<float>(ws, P.o_gu);
+  const int64_t vb = Bp > 0 ? Bp : 1;
+  int64_t *vidx = at<int64_t>(ws, P.o_vidx), *voff = at<int64_t>(ws, P.o_voff);
   if (U > 0) {
+    // the plans the passes check: the real batch's (this call's inputs) and the virtual one's
+    int *rhdr = nullptr, *vhdr = nullptr;
+    unsigned rfp = 0, vfp = 0;
+    if ((rc = plan_identity(desc, nnz, num_bags, indices, offsets, psw, ws, &rhdr, &rfp)) ||
+        (rc = plan_identity(&P.vdesc, U, vb, vidx, voff, nullptr, at<char>(ws, P.o_ws2), &vhdr,
+                            &vfp)))
+      return rc;
     unsigned long long *sk = sorted_keys(P, ws);
     float *frag = at<float>(ws, P.o_frag);
+    const int NB = (int)((int64_t)P.T * num_bags);
     tt_launch(K_DD_FRAG, k_dd_frag, dim3((P.nnz + DD_CH - 1) / DD_CH), dim3(DD_T), 0, s,
               (const unsigned long long *)sk, P.nnz, P.pbits, P.inv,
-              (const int *)at<int>(ws, P.o_bag), offsets, psw,
-              desc->pooling == TT_POOL_MEAN ? 1 : 0, grad_out, P.D, frag);
+              (const int *)at<int>(ws, P.o_bag), NB, offsets, psw,
+              desc->pooling == TT_POOL_MEAN ? 1 : 0, grad_out, P.D, frag, (const int *)rhdr,
+              rfp, vhdr, vfp, dev_status);
     tt_launch(K_DD_GU, k_dd_gu, dim3((unsigned)U), dim3(DD_T), 0, s,
               (const int *)at<int>(ws, P.o_rs), (const int *)at<int>(ws, P.o_re),
               (const int *)at<int>(ws, P.o_rtab), (const int64_t *)at<int64_t>(ws, P.o_Rt),
-              (int)Bp, P.D, (const float *)frag, Gu);
+              (int)Bp, P.D, (const float *)frag, Gu, (const int *)rhdr, rfp, vhdr, vfp,
+              dev_status);
     if (hipGetLastError() != hipSuccess) return TT_EHIP;
   }
-  const int64_t vb = Bp > 0 ? Bp : 1;
-  int64_t *vidx = at<int64_t>(ws, P.o_vidx), *voff = at<int64_t>(ws, P.o_voff);
   if (U == 0 && fill64(voff, (long long)P.T * vb + 1, 0, s) != TT_OK)  // an empty virtual batch
     return TT_EHIP;
   if (grad_cores)

@@ -68,15 +68,15 @@ static __device__ void fwd_wait_out(const DevArgs &a) {  // whole block
     const int nz = fwd_zero_blocks(a), lane = threadIdx.x;
     int ok = 1;
     for (unsigned polls = 0;; ++polls) {
-      const unsigned long long v = lane < nz
-          ? __hip_atomic_load(&a.fflag[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-          : (unsigned long long)a.epoch;
-      if (__ballot(v != (unsigned long long)a.epoch) == 0ull) break;
-      if (polls >= (1u << 22)) {
+      if (polls >= a.sync_polls) {  // (a limit of 0 gives up before the first poll)
         ok = 0;
         if (lane == 0) set_status(a.status, TT_DEV_SYNC_TIMEOUT);
         break;
       }
+      const unsigned long long v = lane < nz
+          ? __hip_atomic_load(&a.fflag[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+          : (unsigned long long)a.epoch;
+      if (__ballot(v != (unsigned long long)a.epoch) == 0ull) break;
       __builtin_amdgcn_s_sleep(1);
     }
     if (lane == 0) s_ok = ok;

@@ -87,6 +87,7 @@ struct DevArgs {
   unsigned long long *fflag; // [FWD_ZERO_BLOCKS] forward: "my slice of out is cleared" words
   int fzero;                 // forward: its first blocks clear out (no separate kernel)
   unsigned epoch;           // unique per call
+  unsigned sync_polls;      // bound of every device-side wait (polls before giving up)
   int *hdr;
   int4 *einfo;      // per element: dA (t,i1), dB (t,i2), dI3 (t,i3), bag
   int *histA, *histB, *histI3;
@@ -177,6 +178,11 @@ inline void tt_launch(int id, void (*kernel)(KArgs...), dim3 grid, dim3 block, s
   else
     hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
 }
+
+// header pointer and fingerprint of the three-core plan of these arguments in ws (no
+// cache); TT_OK or the descriptor's rejection code
+int plan_identity(const tt_desc *desc, int64_t nnz, int64_t num_bags, const void *idx,
+                  const void *off, const void *psw, void *ws, int **hdr, unsigned *fp);
 
 // compute units of the current device (cached per device; 0 if the query fails)
 int device_cus();

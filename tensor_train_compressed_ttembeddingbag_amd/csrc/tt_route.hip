@@ -347,7 +347,6 @@ static __device__ void tile_final(const DevArgs &a, int blk, unsigned short *lds
 // ---------------------------------------------------------------- one-launch path
 constexpr int CT = 1024;               // threads of a block of that launch (one element each)
 constexpr int COOP_BINS = 2048;        // bins per digit
-constexpr unsigned SYNC_POLLS = 1u << 22;  // bounded wait of a grid barrier
 
 // Compute units of the current device (cached per device).
 int device_cus() {
@@ -393,6 +392,11 @@ static __device__ bool grid_sync(const DevArgs &a, unsigned k) {
   if (tid < 64) {
     int ok = 1;
     for (unsigned polls = 0;; ++polls) {
+      if (polls >= a.sync_polls) {  // (a limit of 0 gives up before the first poll)
+        ok = 0;
+        if (tid == 0) set_status(a.status, TT_DEV_SYNC_TIMEOUT);
+        break;
+      }
       bool mine = true;  // this lane's flags (blocks tid, tid + 64, ...) have arrived
       for (int b = tid; b < nblk; b += 64) {
         const unsigned long long v =
@@ -400,11 +404,6 @@ static __device__ bool grid_sync(const DevArgs &a, unsigned k) {
         mine = mine && (unsigned)(v >> 32) == a.epoch && (unsigned)v >= k;
       }
       if (__ballot(!mine) == 0ull) break;
-      if (polls >= SYNC_POLLS) {
-        ok = 0;
-        if (tid == 0) set_status(a.status, TT_DEV_SYNC_TIMEOUT);
-        break;
-      }
       __builtin_amdgcn_s_sleep(1);
     }
     if (tid == 0) {
@@ -515,6 +514,9 @@ __global__ __launch_bounds__(CT) void k_route_coop(DevArgs a) {
   int *startI = lds_i + L.sI, *gsI = lds_i + L.gI, *startA = lds_i + L.sA, *gsA = lds_i + L.gA;
   int *cellB = lds_i + L.cell;  // [binsB][nblk] (t,i2) counts of the orderA tiles
   Rec el[RB / CT];
+  // whatever plan ws held stops being valid before any of it is rewritten (a grouping
+  // that gives up at a barrier then leaves no plan that a later call could take for whole)
+  if (blk == 0 && tid == 0) a.hdr[H_PLAN] = (int)~a.plan_fp;
 
   // ---- histB cleared for the atomics; decode; (t,i3) and (t,i1) histograms of the tile
   for (int k = blk * CT + tid; k < a.binsB * nblk; k += nblk * CT) st_w<true>(a.histB + k, 0);
@@ -579,6 +581,7 @@ __global__ __launch_bounds__(RT) void k_route_a(DevArgs a) {
   __shared__ int s_b[2];
   const int blk = blockIdx.x, tid = threadIdx.x;
   Rec el[4];
+  if (blk == 0 && tid == 0) a.hdr[H_PLAN] = (int)~a.plan_fp;  // the old plan is void from here
   tile_decode<RT>(a, blk, lds_i, s_red, s_b, el);
   check_offsets<RT>(a, blk);
   for (int k = blk * RT + tid; k < a.binsB * a.nblk; k += a.nblk * RT) a.histB[k] = 0;

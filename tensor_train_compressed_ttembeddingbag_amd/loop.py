@@ -48,6 +48,10 @@ class TrainLoop:
                              "and update by sgd or grad")
         if update not in ("sgd", "adagrad", "grad"):
             raise ValueError("update must be sgd, adagrad or grad")
+        if cache is not None and pipeline and len(batches) < 2:
+            # the lookup of batch i+1 writes the slot buffer of batch (i+1) % len(batches),
+            # which the forward of step i may still read when that is the same buffer
+            raise ValueError("the pipelined loop with a cache needs at least two batches")
         self.desc, self.g, self.batches, self.B, self.lr = desc, cores, batches, num_bags, lr
         self.out, self.status, self.update = out, status, update
         self.aux, self.aux_rows = aux, aux_rows

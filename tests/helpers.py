@@ -53,3 +53,103 @@ def to_dev(batch, device="cuda"):
 def slice_view(arr_logical, k):
     """Logical core [ra][pk][qk][rb] -> list over slices i_k of the slice values."""
     return np.moveaxis(arr_logical, 1, 0)
+
+
+# ---------------------------------------------------------------- the oracle over bag chunks
+# The oracle is single-threaded; at full workload sizes the tests run it on disjoint chunks
+# of bags in parallel threads (its C entry points hold no state and release the GIL).  The
+# pooled rows of a chunk are those bags' rows, and the gradient of the batch is the sum of
+# the chunks' gradients (the loss is a sum over bags), so the result is the oracle's own up
+# to the fp64 rounding of that final sum.
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import oracle
+
+
+def _threads():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _chunks(wl, batch, nchunks):
+    """(table, first bag, end bag) ranges: every table's bags cut into nchunks pieces."""
+    B = batch["num_bags"]
+    out = []
+    for t in range(wl.num_tables):
+        cuts = np.linspace(0, B, nchunks + 1).astype(np.int64)
+        out += [(t, int(a), int(b)) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+    return out
+
+
+def _sub(batch, t, b0, b1, B, slots=None):
+    off = batch["offsets"]
+    lo, hi = int(off[t * B + b0]), int(off[t * B + b1])
+    sub_off = (off[t * B + b0: t * B + b1 + 1] - lo).astype(np.int64)
+    psw = batch.get("per_sample_weights")
+    return dict(indices=batch["indices"][lo:hi], offsets=sub_off,
+                per_sample_weights=None if psw is None else psw[lo:hi],
+                grad_out=batch["grad_out"][t * B + b0: t * B + b1],
+                slots=None if slots is None else slots[lo:hi])
+
+
+def par_forward(wl, cores, batch, slots=None, cache_rows=None, pooling=0):
+    """oracle.forward of the whole batch, computed over bag chunks in threads."""
+    B = batch["num_bags"]
+    parts = _chunks(wl, batch, 2 * _threads())
+
+    def run(c):
+        t, b0, b1 = c
+        s = _sub(batch, t, b0, b1, B, slots)
+        return c, oracle.forward(wl.p, wl.q, wl.ranks, wl.E, [cores[t]], s["indices"],
+                                 s["offsets"], b1 - b0, per_sample_weights=s["per_sample_weights"],
+                                 slots=s["slots"], cache_rows=cache_rows, pooling=pooling)
+
+    Y = np.zeros((wl.num_tables * B, wl.D), dtype=np.float64)
+    with ThreadPoolExecutor(_threads()) as ex:
+        for (t, b0, b1), y in ex.map(run, parts):
+            Y[t * B + b0: t * B + b1] = y
+    return Y
+
+
+def par_backward(wl, cores, batch, slots=None, cache_size=0, pooling=0):
+    """oracle.backward of the whole batch over bag chunks in threads: (grads, touched,
+    grad_cache, touched_cache) as oracle.backward returns them."""
+    B = batch["num_bags"]
+    parts = _chunks(wl, batch, 2 * _threads())
+
+    def run(c):
+        t, b0, b1 = c
+        s = _sub(batch, t, b0, b1, B, slots)
+        return c, oracle.backward(wl.p, wl.q, wl.ranks, wl.E, [cores[t]], s["indices"],
+                                  s["offsets"], b1 - b0, s["grad_out"],
+                                  per_sample_weights=s["per_sample_weights"], slots=s["slots"],
+                                  cache_size=cache_size, pooling=pooling)
+
+    grads = [[np.zeros(c.shape, dtype=np.float64) for c in tbl] for tbl in cores]
+    touched = [[np.zeros(wl.p[k], dtype=np.uint8) for k in range(3)] for _ in cores]
+    gc = np.zeros((cache_size, wl.D), dtype=np.float64) if slots is not None else None
+    tc = np.zeros(cache_size, dtype=np.uint8) if slots is not None else None
+    with ThreadPoolExecutor(_threads()) as ex:
+        for (t, _, _), (g, m, g_c, t_c) in ex.map(run, parts):
+            for k in range(3):
+                grads[t][k] += g[0][k]
+                touched[t][k] |= m[0][k]
+            if gc is not None:
+                gc += g_c
+                tc |= t_c
+    return grads, touched, gc, tc
+
+
+def par_rows(wl, cores3, cached):
+    """oracle.populate_rows over chunks of the cached indices in threads."""
+    cached = np.asarray(cached)
+    parts = np.array_split(np.arange(len(cached)), 4 * _threads())
+    out = np.zeros((len(cached), wl.D), dtype=np.float64)
+
+    def run(ix):
+        return ix, oracle.populate_rows(wl.p, wl.q, wl.ranks, cores3, cached[ix])
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        for ix, r in ex.map(run, [p for p in parts if len(p)]):
+            out[ix] = r
+    return out

@@ -164,3 +164,88 @@ def test_train_loop_rejects_invalid_options():
         TrainLoop(None, [], batch, 1, 0.1, None, None, cache=object(), dedup=True)
     with pytest.raises(ValueError):
         TrainLoop(None, [], batch, 1, 0.1, None, None, update="adagrad", dedup=True)
+    # with a cache, one batch would let a lookup rewrite the slots a forward still reads
+    with pytest.raises(ValueError):
+        TrainLoop(None, [], batch, 1, 0.1, None, None, cache=object())
+
+
+def _host_only_binding(monkeypatch):
+    """The binding with its device check relaxed to dtype/contiguity (CPU tensors stand in
+    for device ones) and a library that must never be called: a size mismatch has to be
+    rejected before any call into libttbag."""
+    def need(t, dtype, name):
+        if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_contiguous():
+            raise TypeError(name)
+
+    def no_lib():
+        raise AssertionError("the library was called with mis-sized buffers")
+
+    monkeypatch.setattr(abi, "_need", need)
+    monkeypatch.setattr(abi, "lib", no_lib)
+
+
+def test_binding_rejects_mis_sized_buffers_before_any_device_work(monkeypatch):
+    """Every size the kernels index by is checked by the binding: offsets without the
+    terminal entry (the README example's [0, 4] form), a wrong out / grad_out shape, a
+    wrong core size, per-sample weights or slots of the wrong length, and cache rows of
+    the wrong width each raise ValueError before the C entry point is reached."""
+    _host_only_binding(monkeypatch)
+    wl = W.WORKLOADS["tiny"]
+    d = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E)
+    D, B, nnz = 8, 2, 8
+    sizes = abi._core_numels(d)
+    assert sizes == (4 * 2 * 4, 5 * 4 * 2 * 4, 6 * 4 * 2)
+    cores = [torch.zeros(n) for n in sizes]
+    idx = torch.tensor([1, 2, 4, 5, 4, 3, 2, 9], dtype=torch.int64)
+    off = torch.tensor([0, 4, 8], dtype=torch.int64)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    out = torch.zeros(B, D)
+    gout = torch.zeros(B, D)
+
+    def fwd(**kw):
+        args = dict(cores=cores, indices=idx, offsets=off, num_bags=B, out=out, ws=ws)
+        args.update(kw)
+        return abi.tt_bag_forward(d, args.pop("cores"), args.pop("indices"), args.pop("offsets"),
+                                  args.pop("num_bags"), **args)
+
+    def bwd(**kw):
+        args = dict(cores=cores, offsets=off, grad_out=gout, ws=ws)
+        args.update(kw)
+        return abi.tt_bag_backward_sgd(d, args.pop("cores"), idx, args.pop("offsets"), B,
+                                       args.pop("grad_out"), 0.1, **args)
+
+    cases = [
+        lambda: fwd(offsets=torch.tensor([0, 4], dtype=torch.int64)),  # no terminal entry
+        lambda: fwd(out=torch.zeros(B, D + 1)),
+        lambda: fwd(out=torch.zeros(B + 1, D)),
+        lambda: fwd(cores=[cores[0], torch.zeros(sizes[1] - 1), cores[2]]),
+        lambda: fwd(per_sample_weights=torch.ones(nnz - 1)),
+        lambda: fwd(cache=(torch.zeros(nnz, dtype=torch.int32), torch.zeros(10, D + 1))),
+        lambda: fwd(cache=(torch.zeros(nnz - 1, dtype=torch.int32), torch.zeros(10, D))),
+        lambda: bwd(offsets=torch.tensor([0, 4], dtype=torch.int64)),
+        lambda: bwd(grad_out=torch.zeros(B, D - 1)),
+        lambda: bwd(cores=[torch.zeros(sizes[0] + 4), cores[1], cores[2]]),
+        lambda: abi.tt_bag_plan(d, idx, torch.tensor([0, 8], dtype=torch.int64), B, ws=ws),
+        lambda: abi.tt_bag_backward_grad(d, cores, idx, off, B, gout, ws=ws,
+                                         grad_cores=[c.clone() for c in cores[:2]]
+                                         + [torch.zeros(3)]),
+        lambda: abi.tt_bag_backward_adagrad(d, cores, idx, off, B, gout, 0.1, 1e-8,
+                                            [torch.zeros(1), cores[1], cores[2]], ws=ws),
+        lambda: abi.tt_bag_weight_grad(d, cores, idx, off, B, gout, ws=ws,
+                                       out=torch.zeros(nnz + 1)),
+        lambda: abi.tt_full_weight(d, cores, 0, 4, out=torch.zeros(4, D - 1)),
+        lambda: abi.tt_init_cores(d, [cores[0], cores[1], torch.zeros(1)], 0, 1.0, 0),
+        lambda: abi.tt_bag_route(d, idx, off, B, slots=torch.zeros(3, dtype=torch.int32),
+                                 cache_size=10, ws=ws),
+    ]
+    for k, case in enumerate(cases):
+        with pytest.raises(ValueError):
+            case()
+            pytest.fail("case %d was accepted" % k)
+    # the d-core binding checks its cores the same way
+    dd = abi.make_desc_d((2, 2, 5, 6), (1, 2, 2, 2), (2, 4, 4), 120)
+    nd = abi._core_numels_d(dd)
+    assert nd == (2 * 1 * 1 * 2, 2 * 2 * 2 * 4, 5 * 4 * 2 * 4, 6 * 4 * 2 * 1)
+    with pytest.raises(ValueError):
+        abi.tt_bag_forward_d(dd, [torch.zeros(n) for n in nd[:3]] + [torch.zeros(nd[3] + 1)],
+                             idx, off, B, ws=ws)

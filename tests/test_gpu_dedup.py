@@ -136,3 +136,43 @@ def test_dedup_empty_batch():
     new = [x.clone() for x in g]
     abi.tt_bag_backward_sgd_dedup(desc, new, idx, off, B, dY, 0.1, info, ws=ws)
     assert all(torch.equal(a, b) for a, b in zip(new, g))
+
+
+def test_dedup_backward_refuses_another_batchs_plan():
+    """A distinct-index backward for batch B on a workspace planned for batch A (same nnz,
+    so every size agrees) finds another batch's plan: it reports TT_DEV_STALE_PLAN and
+    leaves the cores bit-identical."""
+    print("case dedup stale plan", flush=True)
+    wl = W.custom(p=(6, 5, 7), q=(2, 4, 2), ranks=(8, 6), bags_per_table=30,
+                  lengths=("fixed", 6), dist=("zipf", 1.2), lr=0.05)
+    cores = W.make_cores(wl)
+    desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E)
+    ba, bb = W.make_batch(wl, 0), W.make_batch(wl, 1)
+    assert len(ba["indices"]) == len(bb["indices"])
+    dev = lambda x: torch.from_numpy(x).cuda()  # noqa: E731
+    g = [_dev(cores, k) for k in range(3)]
+    before = [x.clone() for x in g]
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws, info = abi.tt_bag_plan_dedup(desc, dev(ba["indices"]), dev(ba["offsets"]), 30,
+                                     dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and info[0] > 0
+    abi.tt_bag_backward_sgd_dedup(desc, g, dev(bb["indices"]), dev(bb["offsets"]), 30,
+                                  dev(bb["grad_out"]), wl.lr, info, ws=ws, dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & abi.TT_DEV_STALE_PLAN
+    for k in range(3):
+        assert torch.equal(before[k], g[k]), k
+    # the workspace still serves its own batch once it is planned again
+    st.zero_()
+    ws, info = abi.tt_bag_plan_dedup(desc, dev(bb["indices"]), dev(bb["offsets"]), 30, ws=ws,
+                                     dev_status=st)
+    abi.tt_bag_backward_sgd_dedup(desc, g, dev(bb["indices"]), dev(bb["offsets"]), 30,
+                                  dev(bb["grad_out"]), wl.lr, info, ws=ws, dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    grads, touched, _, _ = oracle.backward(wl.p, wl.q, wl.ranks, wl.E, cores, bb["indices"],
+                                           bb["offsets"], 30, bb["grad_out"])
+    for k in range(3):
+        got = _host(g[k], cores, k)[0].astype(np.float64)
+        assert rel_err(got - cores[0][k], -wl.lr * grads[0][k]) <= TOL, k

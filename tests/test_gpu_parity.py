@@ -363,3 +363,97 @@ def test_planned_calls_match_stateless_and_refuse_a_stale_plan():
     assert torch.all(out == 7.0)
     for k in range(3):
         assert torch.equal(before[k], g2[k])
+
+
+def test_device_waits_that_give_up_leave_no_plan_and_end_normally():
+    """The bounded device-side waits, driven to give up from the host (a poll limit of 0:
+    every waiting workgroup gives up at once and leaves normally).  A grouping whose grid
+    barrier gives up reports TT_DEV_SYNC_TIMEOUT and leaves no valid plan -- even where the
+    workspace held a valid plan of the same fingerprint before -- so the planned forward
+    and backward report TT_DEV_STALE_PLAN and touch nothing.  A forward whose clearing
+    check gives up reports the timeout as well.  With the default bound restored the same
+    calls are correct again."""
+    wl = W.WORKLOADS["readme"]  # ten 1024-element tiles: a multi-block grouping
+    _say("case sync give-up")
+    cores = W.make_cores(wl)
+    b = W.make_batch(wl, 3)
+    d = to_dev(b)
+    B = b["num_bags"]
+    desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E)
+    g = gpu_cores(wl, cores)
+    before = [x.clone() for x in g]
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = abi.tt_bag_plan(desc, d["indices"], d["offsets"], B, dev_status=st)  # a valid plan
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    out = torch.full((B, wl.D), 7.0, device="cuda")
+    try:
+        abi.tt_debug_sync_poll_limit(0)
+        abi.tt_bag_plan(desc, d["indices"], d["offsets"], B, ws=ws, dev_status=st)
+        abi.tt_debug_sync_poll_limit(-1)
+        torch.cuda.synchronize()
+        assert int(st.item()) & abi.TT_DEV_SYNC_TIMEOUT
+        abi.tt_bag_forward(desc, g, d["indices"], d["offsets"], B, out=out, ws=ws,
+                           dev_status=st, planned=True)
+        abi.tt_bag_backward_sgd(desc, g, d["indices"], d["offsets"], B, d["grad_out"], wl.lr,
+                                ws=ws, dev_status=st, planned=True)
+        torch.cuda.synchronize()
+        assert int(st.item()) & abi.TT_DEV_STALE_PLAN
+        assert torch.all(out == 7.0)
+        for k in range(3):
+            assert torch.equal(before[k], g[k])
+        # the forward's check that out is cleared, given up at once (valid plan)
+        st.zero_()
+        abi.tt_bag_plan(desc, d["indices"], d["offsets"], B, ws=ws, dev_status=st)
+        abi.tt_debug_sync_poll_limit(0)
+        abi.tt_bag_forward(desc, g, d["indices"], d["offsets"], B, out=out, ws=ws,
+                           dev_status=st, planned=True)
+        abi.tt_debug_sync_poll_limit(-1)
+        torch.cuda.synchronize()
+        assert int(st.item()) & abi.TT_DEV_SYNC_TIMEOUT
+    finally:
+        abi.tt_debug_sync_poll_limit(-1)
+    st.zero_()
+    Y = abi.tt_bag_forward(desc, g, d["indices"], d["offsets"], B, ws=ws, dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    Yo = oracle.forward(wl.p, wl.q, wl.ranks, wl.E, cores, b["indices"], b["offsets"], B)
+    assert rel_err(Y.cpu().numpy(), Yo) <= TOL
+
+
+@pytest.mark.parametrize("fill", ["0xff", "nan"])
+def test_poisoned_workspace_gives_the_clean_result(fill):
+    """The kernels keep flags, counters and partial sums in the caller's workspace and
+    never rely on it being cleared: a workspace filled with 0xFF bytes or with NaNs before
+    the call gives the same pooled output (up to the order of the forward's atomics) and
+    bit-identical core updates as a zeroed one, with no status bit set."""
+    for wl in (W.WORKLOADS["readme"], SMALL[6]):
+        _say("case poisoned workspace", fill, wl.name)
+        cores = W.make_cores(wl)
+        b = W.make_batch(wl, 4)
+        d = to_dev(b)
+        B = b["num_bags"]
+        desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E)
+        res = []
+        for poison in (None, fill):
+            ws = abi.workspace(desc, d["indices"].numel(), B)
+            if poison is None:
+                ws.zero_()
+            elif poison == "0xff":
+                ws.fill_(255)
+            else:
+                ws.view(torch.float32)[:] = float("nan")
+            g = gpu_cores(wl, cores)
+            st = torch.zeros(1, dtype=torch.int32, device="cuda")
+            Y = abi.tt_bag_forward(desc, g, d["indices"], d["offsets"], B,
+                                   d["per_sample_weights"], ws=ws, dev_status=st)
+            abi.tt_bag_backward_sgd(desc, g, d["indices"], d["offsets"], B, d["grad_out"], wl.lr,
+                                    d["per_sample_weights"], ws=ws, dev_status=st)
+            torch.cuda.synchronize()
+            assert int(st.item()) == 0
+            assert torch.isfinite(Y).all()
+            res.append((Y.cpu().numpy(), [x.cpu().numpy() for x in g]))
+        (Y0, g0), (Y1, g1) = res
+        assert rel_err(Y1, Y0) <= 1e-6
+        for k in range(3):
+            assert np.array_equal(g0[k].view(np.uint32), g1[k].view(np.uint32)), k

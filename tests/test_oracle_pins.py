@@ -380,6 +380,44 @@ def test_cache_semantics():
         np.testing.assert_allclose(g[0][k], g2[0][k], rtol=1e-13, atol=1e-15)
 
 
+def test_cache_row_sgd_invariants_and_exact_loss_decrease():
+    """SGD on cache rows (oracle.sgd with cache_rows): touched rows become
+    fp32(row - lr * g) exactly, untouched rows keep their bits, and -- L being linear in
+    the cache rows -- the loss with the updated rows (cores unchanged) drops by exactly
+    lr * |g|^2 up to the fp32 rounding of the rows."""
+    wl = W.WORKLOADS["tiny"]
+    cores = W.make_cores(wl)
+    b = W.make_batch(wl, 0)
+    idx, off, dY = b["indices"], b["offsets"], b["grad_out"]
+    K = 7
+    # three frequent indices outside the batch: cached rows the batch does not touch
+    extra = np.array([i for i in range(wl.E) if i not in set(idx.tolist())][:3], dtype=np.int64)
+    cached = oracle.select_cache(oracle.count_frequencies([idx, np.repeat(extra, 9)]), K)
+    rows = oracle.populate_rows(wl.p, wl.q, wl.ranks, cores[0], cached).astype(np.float32)
+    rows += (_rng(23).standard_normal(rows.shape) * 0.1).astype(np.float32)  # trained rows
+    slots = oracle.lookup_slots(cached, idx)
+    args = (wl.p, wl.q, wl.ranks, wl.E, cores, idx, off, 8)
+    g, tch, gc, tc = oracle.backward(*args, dY, slots=slots, cache_size=K)
+    assert tc.any() and not tc.all()
+    lr = 0.01
+    new_cores, new_rows = oracle.sgd(wl.p, wl.q, wl.ranks, wl.E, cores, g, tch, lr,
+                                     cache_rows=rows, grad_cache=gc, touched_cache=tc)
+    for sl in range(K):
+        if tc[sl]:
+            exp = (rows[sl].astype(np.float64) - lr * gc[sl]).astype(np.float32)
+            assert np.array_equal(new_rows[sl], exp)
+        else:
+            assert np.array_equal(new_rows[sl].view(np.uint32), rows[sl].view(np.uint32))
+
+    def loss(r):
+        Y = oracle.forward(*args, slots=slots, cache_rows=r)
+        return float(np.sum(Y * dY.astype(np.float64)))
+
+    drop = loss(rows) - loss(new_rows)
+    want = lr * float(np.sum(gc * gc))
+    assert abs(drop - want) <= 1e-4 * want
+
+
 # --------------------------------------------------------------- integer side
 
 def test_split_index_brute_force():
@@ -514,6 +552,9 @@ _MUTANTS = [
      "const double w = (psw ? (double)psw[n] : 1.0);"),
     # weight gradient: the mean pooling's 1 / length dropped
     ("grad_w[n] = acc * inv;\n                free(row);", "grad_w[n] = acc;\n                free(row);"),
+    # SGD on cache rows: the step taken up the gradient
+    ("rows[sl * D + j] = (float)((double)rows[sl * D + j] - lr * grad[sl * D + j]);",
+     "rows[sl * D + j] = (float)((double)rows[sl * D + j] + lr * grad[sl * D + j]);"),
     # Adagrad on cache rows: the squared gradient not added
     ("state[e] = (float)((double)state[e] + g * g);\n            rows[e]",
      "state[e] = (float)((double)state[e] + g);\n            rows[e]"),
@@ -548,7 +589,8 @@ def test_pins_catch_planted_mistakes(mi, tmp_path, monkeypatch):
             test_backward_matches_torch_autograd, test_sgd_step_invariants,
             test_adagrad_matches_torch_optim_adagrad, test_adagrad_first_step_closed_form,
             test_mean_pooling_matches_torch_embedding_bag,
-            test_weight_gradient_matches_torch_and_exact_differences]
+            test_weight_gradient_matches_torch_and_exact_differences,
+            test_cache_row_sgd_invariants_and_exact_loss_decrease]
     try:
         for f in pins:
             try:
