@@ -149,26 +149,26 @@ def test_dedup_backward_refuses_another_batchs_plan():
     desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E)
     ba, bb = W.make_batch(wl, 0), W.make_batch(wl, 1)
     assert len(ba["indices"]) == len(bb["indices"])
-    dev = lambda x: torch.from_numpy(x).cuda()  # noqa: E731
+    # both batches stay allocated: a freed buffer's address may be handed to the next one,
+    # and a plan cannot tell new contents at an old address (the documented contract)
+    ia, oa = torch.from_numpy(ba["indices"]).cuda(), torch.from_numpy(ba["offsets"]).cuda()
+    ib, ob = torch.from_numpy(bb["indices"]).cuda(), torch.from_numpy(bb["offsets"]).cuda()
+    gb = torch.from_numpy(bb["grad_out"]).cuda()
     g = [_dev(cores, k) for k in range(3)]
     before = [x.clone() for x in g]
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
-    ws, info = abi.tt_bag_plan_dedup(desc, dev(ba["indices"]), dev(ba["offsets"]), 30,
-                                     dev_status=st)
+    ws, info = abi.tt_bag_plan_dedup(desc, ia, oa, 30, dev_status=st)
     torch.cuda.synchronize()
     assert int(st.item()) == 0 and info[0] > 0
-    abi.tt_bag_backward_sgd_dedup(desc, g, dev(bb["indices"]), dev(bb["offsets"]), 30,
-                                  dev(bb["grad_out"]), wl.lr, info, ws=ws, dev_status=st)
+    abi.tt_bag_backward_sgd_dedup(desc, g, ib, ob, 30, gb, wl.lr, info, ws=ws, dev_status=st)
     torch.cuda.synchronize()
     assert int(st.item()) & abi.TT_DEV_STALE_PLAN
     for k in range(3):
         assert torch.equal(before[k], g[k]), k
     # the workspace still serves its own batch once it is planned again
     st.zero_()
-    ws, info = abi.tt_bag_plan_dedup(desc, dev(bb["indices"]), dev(bb["offsets"]), 30, ws=ws,
-                                     dev_status=st)
-    abi.tt_bag_backward_sgd_dedup(desc, g, dev(bb["indices"]), dev(bb["offsets"]), 30,
-                                  dev(bb["grad_out"]), wl.lr, info, ws=ws, dev_status=st)
+    ws, info = abi.tt_bag_plan_dedup(desc, ib, ob, 30, ws=ws, dev_status=st)
+    abi.tt_bag_backward_sgd_dedup(desc, g, ib, ob, 30, gb, wl.lr, info, ws=ws, dev_status=st)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     grads, touched, _, _ = oracle.backward(wl.p, wl.q, wl.ranks, wl.E, cores, bb["indices"],
