@@ -140,6 +140,26 @@ int tt_bag_backward_sgd(const tt_desc *desc, float *const cores[3],
                         void *ws, size_t ws_bytes, int32_t *dev_status, void *stream);
 
 /*
+ * Forward for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): tt_bag_forward
+ * without a workspace argument.  The grouping and the forward run in a scratch array
+ * that the library holds in static device storage, TT_STATIC_SCRATCH_BYTES per GPU
+ * (each GPU the library runs on keeps its copy until the process ends); the call
+ * allocates nothing.  The batch may use at most that much of it: the forward's share
+ * of tt_bag_workspace_size (about 80 bytes per index plus the bin tables: under 1 MiB
+ * for 10,240 indices of the README shape); a larger batch returns TT_EWORKSPACE and
+ * enqueues nothing.  Every call on one GPU shares that GPU's array, so calls that may
+ * overlap on one GPU (other streams, other host threads) race and must be ordered by
+ * the caller.  Arguments and results as tt_bag_forward.
+ */
+#define TT_STATIC_SCRATCH_BYTES 8388608
+int tt_bag_forward_static(const tt_desc *desc, const float *const cores[3],
+                          const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                          int64_t num_bags, const float *per_sample_weights,
+                          const tt_cache_view *cache, float *out, int32_t *dev_status,
+                          void *stream);
+
+/*
  * Split of one training step into its grouping and its arithmetic.  tt_bag_plan
  * runs the grouping step (index split, bag ids, validation, the stable sorts) and
  * leaves the result in `ws`.  tt_bag_forward_planned / tt_bag_backward_sgd_planned

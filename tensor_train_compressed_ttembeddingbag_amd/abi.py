@@ -70,6 +70,7 @@ _SIG = {
                                       _P, _P]),
     "tt_bag_backward_sgd": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P, ctypes.c_float,
                                            _P, ctypes.c_size_t, _P, _P]),
+    "tt_bag_forward_static": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P, _P, _P]),
     "tt_bag_plan": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _P, _P, ctypes.c_size_t, _P, _P]),
     "tt_bag_forward_planned": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P, _P,
                                               ctypes.c_size_t, _P, _P]),
@@ -331,6 +332,37 @@ def tt_bag_forward(desc: TTDesc, cores, indices, offsets, num_bags: int,
                               None if view is None else ctypes.byref(view), _ptr(out), _ptr(ws),
                               ws.numel(), _ptr(dev_status), _stream(stream, indices))
     _check("tt_bag_forward_planned" if planned else "tt_bag_forward", rc)
+    return out
+
+
+TT_STATIC_SCRATCH_BYTES = 8388608
+
+
+def tt_bag_forward_static(desc: TTDesc, cores, indices, offsets, num_bags: int,
+                          per_sample_weights=None, cache=None, out=None, dev_status=None,
+                          stream=None) -> torch.Tensor:
+    """tt_bag_forward in the library's static scratch: no workspace, no allocation in the
+    library (out is allocated here only when not given)."""
+    _need(indices, torch.int64, "indices")
+    _need(offsets, torch.int64, "offsets")
+    if per_sample_weights is not None:
+        _need(per_sample_weights, torch.float32, "per_sample_weights")
+    _batch_sizes(desc, indices, offsets, num_bags, per_sample_weights)
+    D = _dim(desc)
+    if out is None:
+        out = torch.empty(desc.num_tables * num_bags, D, dtype=torch.float32, device=indices.device)
+    _need(out, torch.float32, "out")
+    _numel(out, desc.num_tables * int(num_bags) * D, "out")
+    view, _ = _cache_view(cache, desc, indices.numel())
+    if dev_status is not None:
+        _need(dev_status, torch.int32, "dev_status")
+    core_ptrs = _cores(cores, desc)
+    rc = lib().tt_bag_forward_static(ctypes.byref(desc), core_ptrs, _ptr(indices),
+                                     indices.numel(), _ptr(offsets), int(num_bags),
+                                     _ptr(per_sample_weights),
+                                     None if view is None else ctypes.byref(view), _ptr(out),
+                                     _ptr(dev_status), _stream(stream, indices))
+    _check("tt_bag_forward_static", rc)
     return out
 
 

@@ -4,6 +4,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "tt_internal.h"
@@ -48,6 +49,7 @@ struct Plan {
   int RP = 0;
   size_t lds_fwd = 0, lds_bwd = 0;
   size_t ws_total = 0;
+  size_t ws_fwd = 0;  // the prefix the grouping and the forward use (no backward partials)
   // byte offsets inside the workspace
   size_t o_ctr, o_flag, o_fflag, o_hdr, o_einfo, o_histA, o_histB, o_histI3, o_rec, o_segI3, o_segA, o_srec,
       o_fitem, o_grp, o_chunk,
@@ -150,6 +152,7 @@ int make_plan(const tt_desc *d, int64_t nnz, int64_t num_bags, int64_t cache_siz
   P->o_fitem = carve(cur, (size_t)items_max(a) * sizeof(int4));
   P->o_grp = carve(cur, ((size_t)binsB + 1) * 4);
   P->o_chunk = carve(cur, (G + 1) * 4);
+  P->ws_fwd = cur;  // from here on: parts only the backward writes
   P->o_l1 = carve(cur, n * 4);
   P->o_l3 = carve(cur, n * 4);
   P->o_p1 = carve(cur, n * (size_t)a.q1 * a.R1 * 4);
@@ -189,10 +192,11 @@ void bind_ws(Plan *P, void *ws) {
   a.sync_polls = g_sync_polls.load(std::memory_order_relaxed);
 }
 
-int check_ws(const Plan &P, void *ws, size_t ws_bytes) {
+// fwd_only: the call runs the grouping and the forward only, which use ws_fwd bytes
+int check_ws(const Plan &P, void *ws, size_t ws_bytes, bool fwd_only = false) {
   if (!ws) return TT_EINVAL;
   if (((uintptr_t)ws) % ALIGN) return TT_EWORKSPACE;
-  if (ws_bytes < P.ws_total) return TT_EWORKSPACE;
+  if (ws_bytes < (fwd_only ? P.ws_fwd : P.ws_total)) return TT_EWORKSPACE;
   return TT_OK;
 }
 
@@ -268,12 +272,13 @@ static unsigned plan_fingerprint(const tt_desc *d, int64_t nnz, int64_t num_bags
 // argument checks shared by every call that takes a batch; fills P and binds ws
 static int prepare(Plan *P, const tt_desc *desc, const int64_t *indices, int64_t nnz,
                    const int64_t *offsets, int64_t num_bags, const float *psw,
-                   const tt_cache_view *cache, void *ws, size_t ws_bytes, int32_t *dev_status) {
+                   const tt_cache_view *cache, void *ws, size_t ws_bytes, int32_t *dev_status,
+                   bool fwd_only = false) {
   const int64_t csize = cache ? cache->cache_size : 0;
   int rc = make_plan(desc, nnz, num_bags, csize, P);
   if (rc) return rc;
   if (!offsets || (nnz > 0 && !indices)) return TT_EINVAL;
-  if ((rc = check_ws(*P, ws, ws_bytes))) return rc;
+  if ((rc = check_ws(*P, ws, ws_bytes, fwd_only))) return rc;
   if ((rc = set_cache(P, cache, nnz))) return rc;
   bind_ws(P, ws);
   DevArgs &a = P->a;
@@ -307,26 +312,27 @@ int plan_identity(const tt_desc *desc, int64_t nnz, int64_t num_bags, const void
 }
 }  // namespace ttb
 
-extern "C" {
-
-int tt_bag_plan(const tt_desc *desc, const int64_t *indices, int64_t nnz, const int64_t *offsets,
-                int64_t num_bags, const float *per_sample_weights, const tt_cache_view *cache,
-                void *ws, size_t ws_bytes, int32_t *dev_status, void *stream) {
+// the grouping / the planned forward; fwd_only: ws holds only the forward's part
+static int plan_call(const tt_desc *desc, const int64_t *indices, int64_t nnz,
+                     const int64_t *offsets, int64_t num_bags, const float *per_sample_weights,
+                     const tt_cache_view *cache, void *ws, size_t ws_bytes, int32_t *dev_status,
+                     void *stream, bool fwd_only) {
   Plan P;
   int rc = prepare(&P, desc, indices, nnz, offsets, num_bags, per_sample_weights, cache, ws,
-                   ws_bytes, dev_status);
+                   ws_bytes, dev_status, fwd_only);
   if (rc) return rc;
   return finish(launch_route(P.a, (hipStream_t)stream));
 }
 
-int tt_bag_forward_planned(const tt_desc *desc, const float *const cores[3],
-                           const int64_t *indices, int64_t nnz, const int64_t *offsets,
-                           int64_t num_bags, const float *per_sample_weights,
-                           const tt_cache_view *cache, float *out, void *ws, size_t ws_bytes,
-                           int32_t *dev_status, void *stream) {
+static int forward_planned_call(const tt_desc *desc, const float *const cores[3],
+                                const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                                int64_t num_bags, const float *per_sample_weights,
+                                const tt_cache_view *cache, float *out, void *ws,
+                                size_t ws_bytes, int32_t *dev_status, void *stream,
+                                bool fwd_only) {
   Plan P;
   int rc = prepare(&P, desc, indices, nnz, offsets, num_bags, per_sample_weights, cache, ws,
-                   ws_bytes, dev_status);
+                   ws_bytes, dev_status, fwd_only);
   if (rc) return rc;
   if ((rc = check_cores(cores)) || !out) return rc ? rc : TT_EINVAL;
   DevArgs &a = P.a;
@@ -339,6 +345,42 @@ int tt_bag_forward_planned(const tt_desc *desc, const float *const cores[3],
   hipError_t e = a.fzero ? hipSuccess : launch_yinit(a, s);
   if (e == hipSuccess && a.nnz > 0) e = launch_fwd(a, P.RP, P.lds_fwd, s);
   return finish(e);
+}
+
+// the stateless forward: argument checks, then grouping + planned forward in ws
+static int forward_call(const tt_desc *desc, const float *const cores[3], const int64_t *indices,
+                        int64_t nnz, const int64_t *offsets, int64_t num_bags,
+                        const float *per_sample_weights, const tt_cache_view *cache, float *out,
+                        void *ws, size_t ws_bytes, int32_t *dev_status, void *stream,
+                        bool fwd_only) {
+  Plan P;
+  int rc = prepare(&P, desc, indices, nnz, offsets, num_bags, per_sample_weights, cache, ws,
+                   ws_bytes, dev_status, fwd_only);
+  if (rc) return rc;
+  if ((rc = check_cores(cores)) || !out) return rc ? rc : TT_EINVAL;
+  rc = plan_call(desc, indices, nnz, offsets, num_bags, per_sample_weights, cache, ws, ws_bytes,
+                 dev_status, stream, fwd_only);
+  if (rc) return rc;
+  return forward_planned_call(desc, cores, indices, nnz, offsets, num_bags, per_sample_weights,
+                              cache, out, ws, ws_bytes, dev_status, stream, fwd_only);
+}
+
+extern "C" {
+
+int tt_bag_plan(const tt_desc *desc, const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                int64_t num_bags, const float *per_sample_weights, const tt_cache_view *cache,
+                void *ws, size_t ws_bytes, int32_t *dev_status, void *stream) {
+  return plan_call(desc, indices, nnz, offsets, num_bags, per_sample_weights, cache, ws, ws_bytes,
+                   dev_status, stream, false);
+}
+
+int tt_bag_forward_planned(const tt_desc *desc, const float *const cores[3],
+                           const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                           int64_t num_bags, const float *per_sample_weights,
+                           const tt_cache_view *cache, float *out, void *ws, size_t ws_bytes,
+                           int32_t *dev_status, void *stream) {
+  return forward_planned_call(desc, cores, indices, nnz, offsets, num_bags, per_sample_weights,
+                              cache, out, ws, ws_bytes, dev_status, stream, false);
 }
 
 }  // extern "C"
@@ -442,16 +484,8 @@ int tt_bag_forward(const tt_desc *desc, const float *const cores[3], const int64
                    int64_t nnz, const int64_t *offsets, int64_t num_bags,
                    const float *per_sample_weights, const tt_cache_view *cache, float *out,
                    void *ws, size_t ws_bytes, int32_t *dev_status, void *stream) {
-  Plan P;
-  int rc = prepare(&P, desc, indices, nnz, offsets, num_bags, per_sample_weights, cache, ws,
-                   ws_bytes, dev_status);
-  if (rc) return rc;
-  if ((rc = check_cores(cores)) || !out) return rc ? rc : TT_EINVAL;
-  rc = tt_bag_plan(desc, indices, nnz, offsets, num_bags, per_sample_weights, cache, ws, ws_bytes,
-                   dev_status, stream);
-  if (rc) return rc;
-  return tt_bag_forward_planned(desc, cores, indices, nnz, offsets, num_bags, per_sample_weights,
-                                cache, out, ws, ws_bytes, dev_status, stream);
+  return forward_call(desc, cores, indices, nnz, offsets, num_bags, per_sample_weights, cache,
+                      out, ws, ws_bytes, dev_status, stream, false);
 }
 
 int tt_bag_backward_sgd(const tt_desc *desc, float *const cores[3], const int64_t *indices,
@@ -789,3 +823,47 @@ int tt_cache_destroy(tt_cache *c) {
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- forward without allocation
+// For callers that cannot allocate device memory (code under HIP graph capture, tight
+// serving loops, harnesses that forbid it): tt_bag_forward_static runs the grouping and
+// the forward in a scratch array of the library instead of a caller workspace.  Each GPU
+// holds its own copy of `scratch` (static storage, zero at load; nothing in it needs
+// clearing: histograms are cleared by the grouping kernels themselves and the flag and
+// counter words carry each call's epoch).  Host code never takes the array's name for an
+// address: the device address comes from hipGetSymbolAddress once per device.
+static __device__ __align__(256) unsigned char scratch[TT_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[MAX_DEVICES];
+
+// the current device's copy of `scratch` (looked up on the first call on that device)
+void *scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch[dev] = ptr;
+  }
+  return g_scratch[dev];
+}
+}  // namespace
+
+extern "C" int tt_bag_forward_static(const tt_desc *desc, const float *const cores[3],
+                                     const int64_t *indices, int64_t nnz, const int64_t *offsets,
+                                     int64_t num_bags, const float *per_sample_weights,
+                                     const tt_cache_view *cache, float *out, int32_t *dev_status,
+                                     void *stream) {
+  Plan P;
+  int rc = make_plan(desc, nnz, num_bags, cache ? cache->cache_size : 0, &P);
+  if (rc) return rc;
+  if (P.ws_fwd > (size_t)TT_STATIC_SCRATCH_BYTES) return TT_EWORKSPACE;  // batch too large
+  void *ws = scratch_of_current_device();
+  if (!ws) return TT_EHIP;
+  return forward_call(desc, cores, indices, nnz, offsets, num_bags, per_sample_weights, cache,
+                      out, ws, TT_STATIC_SCRATCH_BYTES, dev_status, stream, true);
+}
