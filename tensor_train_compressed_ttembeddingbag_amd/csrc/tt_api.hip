@@ -39,7 +39,7 @@ using namespace ttb;
 namespace {
 
 constexpr size_t ALIGN = 256;
-constexpr size_t LDS_LIMIT = 160 * 1024;
+constexpr size_t LDS_LIMIT = LDS_DYN_MAX;  // dynamic LDS of one contraction workgroup
 std::atomic<unsigned> g_epoch{1};
 constexpr unsigned SYNC_POLLS = 1u << 22;  // default bound of a device-side wait
 std::atomic<unsigned> g_sync_polls{SYNC_POLLS};
@@ -52,7 +52,7 @@ struct Plan {
   size_t ws_fwd = 0;  // the prefix the grouping and the forward use (no backward partials)
   // byte offsets inside the workspace
   size_t o_ctr, o_flag, o_fflag, o_hdr, o_einfo, o_histA, o_histB, o_histI3, o_rec, o_segI3, o_segA, o_srec,
-      o_fitem, o_grp, o_chunk,
+      o_fitem, o_meta, o_grp, o_chunk,
       o_l1, o_l3, o_p1, o_p3, o_frag, o_p2;
 };
 
@@ -150,11 +150,12 @@ int make_plan(const tt_desc *d, int64_t nnz, int64_t num_bags, int64_t cache_siz
   P->o_segA = carve(cur, ((size_t)binsA + 1) * 4);
   P->o_srec = carve(cur, n * 32);
   P->o_fitem = carve(cur, (size_t)items_max(a) * sizeof(int4));
+  P->o_meta = carve(cur, (size_t)items_max(a) * META_INTS * 4);
   P->o_grp = carve(cur, ((size_t)binsB + 1) * 4);
   P->o_chunk = carve(cur, (G + 1) * 4);
-  P->ws_fwd = cur;  // from here on: parts only the backward writes
   P->o_l1 = carve(cur, n * 4);
   P->o_l3 = carve(cur, n * 4);
+  P->ws_fwd = cur;  // from here on: parts only the backward writes
   P->o_p1 = carve(cur, n * (size_t)a.q1 * a.R1 * 4);
   P->o_p3 = carve(cur, n * (size_t)a.R2 * a.q3 * 4);
   P->o_frag = carve(cur, n * (size_t)a.D * 4);
@@ -179,6 +180,7 @@ void bind_ws(Plan *P, void *ws) {
   a.segA = (int *)(b + P->o_segA);
   a.srec = (int4 *)(b + P->o_srec);
   a.fitem = (int4 *)(b + P->o_fitem);
+  a.meta = (int *)(b + P->o_meta);
   a.grp_off = (int *)(b + P->o_grp);
   a.chunk_pre = (int *)(b + P->o_chunk);
   a.link1 = (int *)(b + P->o_l1);

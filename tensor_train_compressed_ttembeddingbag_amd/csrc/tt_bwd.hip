@@ -38,7 +38,7 @@ namespace ttb {
 template <int RP>
 struct BwdLds {
   static constexpr int LD = RP + 4;
-  static constexpr int INTS = 64 * 7 + 65 * 2 + 64 + 64 + 16 + 8;
+  static constexpr int INTS = META_INTS;
   // the dG2 reduction slots alias the dT transpose tiles and the w * dY staging
   __host__ __device__ static size_t red_floats(int nred, int P, int D) {
     size_t r = (size_t)nred * RP * LD;
@@ -60,14 +60,16 @@ size_t bwd_lds_bytes(int RP, int JB, int P, int q3, int D, int nred) {
   }
 }
 
-// two workgroups per CU need <= 128 VGPRs (rank-64 tiles take one CU each).  Q3 = 4
-// fixes q3 at compile time (each item's G3 / dG3 rows of four j3 move as 16-byte LDS
-// vectors); Q3 = 0 reads it from the arguments.  HITS: the instance for calls with a
+// two workgroups per CU need <= 128 VGPRs (rank-64 tiles take one CU each).  F44: the
+// instance for q1 = q3 = 4 (a lane group's four rows are one pair; each item's G3 / dG3
+// rows of four j3 move as 16-byte LDS vectors); otherwise q1 and q3 come from the
+// arguments.  HITS: the instance for calls with a
 // cache, whose extra workgroups sum the cache-hit runs (an instance of its own, so that
 // the register budget of the others is not shared with that path).
-template <int RP, int Q3, bool HITS>
+template <int RP, bool F44, bool HITS>
 __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(RP == 64 ? 2 : 4)))
 void k_bwd(DevArgs a) {
+  constexpr int Q3 = F44 ? 4 : 0;  // q3 fixed at compile time with q1 = q3 = 4
   constexpr int KS = RP / 4, NM = RP / 16, LD = BwdLds<RP>::LD, LRP = log2_rp<RP>();
   constexpr int JU = 2;  // j3 per batch of the item loop with a runtime q3 (register budget)
   extern __shared__ float4 smem4[];
@@ -82,18 +84,8 @@ void k_bwd(DevArgs a) {
   float *sGu = sRed + BwdLds<RP>::red_floats(nred, P, D);         // [item][D]
   float *sG3 = sGu + (size_t)P * D;                               // [item][r2 < RP][j3]
   float *sdA3 = sG3 + (size_t)P * q3 * RP;                        // [item][r2 < RP][j3]
-  int *e_bag = (int *)(sdA3 + (size_t)P * q3 * RP);               // [64]
-  float *e_w = (float *)(e_bag + 64);                             // [64]
-  int *it_i3 = (int *)(e_w + 64);                                 // [64]
-  int *it_pair = it_i3 + 64;                                      // [64]
-  int *it_beg = it_pair + 64;                                     // [65] item-major slots
-  int *pr_it = it_beg + 65;                                       // [65]
-  int *pr_i1 = pr_it + 65;                                        // [64]
-  int *gcnt = pr_i1 + 64;                                         // [64] items per lane group
-  int *mb_nk = gcnt + 64;                                         // [16]
-  int *s_cnt = mb_nk + 16;                                        // [8]
-  int *e_perm = s_cnt + 8;                                        // [64] item-major elements
-  int *it_first = e_perm + 64;                                    // [64] leader offsets
+  int *s_meta = (int *)(sdA3 + (size_t)P * q3 * RP);              // [META_INTS]
+  const WorkMeta &M = *(const WorkMeta *)s_meta;
 
   // workgroups past the work items' part of the grid: the cache-hit run sums, one wave
   // per 64-position piece (they need only the plan and grad_out, so they run beside the
@@ -105,13 +97,15 @@ void k_bwd(DevArgs a) {
     runsum_piece(a, piece, (int)(threadIdx.x & 63));
     return;
   }
-  // round 1: plan check and work item
+  // round 1: plan check and the work item's metadata (built by the grouping)
   const int wi = blockIdx.x;
   const int plan = a.hdr[H_PLAN], nitems = a.hdr[H_NFWD];
-  const int4 item = a.fitem[wi];
+  __shared__ int s_pl[NW];
+  if (tid < META_INTS) s_meta[tid] = a.meta[(size_t)wi * META_INTS + tid];
+  note_placement(s_pl);
+  __syncthreads();
   if (plan != (int)a.plan_fp || wi >= nitems) return;
-  const int grp = item.x, s0 = item.y, s1 = item.z;
-  const int n_el = s1 - s0;
+  const int grp = M.grp, s0 = M.s0, n_el = M.n_el, nI = M.nI, nP = M.nP;
   const int t = grp / a.p2;
   const size_t W1 = (size_t)q1 * R1, W3 = (size_t)R2 * q3;
   const size_t slice2 = (size_t)R1 * q2 * R2;
@@ -150,62 +144,12 @@ void k_bwd(DevArgs a) {
     }
   };
 
-  // round 2: the elements (wave 0; items, pairs, links) and the first G2 stage
+  // round 2: the first G2 stage, the items' G3 slices (-> LDS, with the dG3 accumulators
+  // cleared), the pairs' G1 rows in the two operand layouts and the elements' w * dY rows,
+  // the first batch of everything in flight at once
   const int nj0 = min(JB, q2);
-  float v2[STAGE_U];
-  load2(0, nj0, tid, v2);
-  if (tid < 64) {
-    const int s = s0 + min(tid, n_el - 1);
-    const bool v = tid < n_el;
-    const SPos sp = load_spos(a.srec, s);
-    const int dAv = sp.dA, dIv = sp.dI3, bagv = sp.bag;
-    const int lA = sp.posA, lI = sp.posI3;
-    const float wv = sp.w;
-    const int dA = v ? dAv : -1, i3 = v ? dIv - t * a.p3 : 0;
-    e_bag[tid] = bagv;
-    e_w[tid] = wv;
-    const WaveItems r = wave_items(v, dA, i3, nbits_for(a.p3));
-    gcnt[tid] = 0;
-    // a partial lives at the first position of its item (dG3) / pair (dG1)
-    if (v) {
-      a.link1[lA] = r.pair_st ? s : -1;
-      a.link3[lI] = r.item_st ? s : -1;
-      e_perm[r.item_pos] = tid;
-    }
-    wave_lds_sync();
-    if (r.item_st) {
-      it_beg[r.it] = r.it_beg;
-      it_first[r.it] = tid;
-      it_i3[r.it] = i3;
-      it_pair[r.it] = r.pair_of;
-    }
-    if (r.pair_st) {
-      pr_it[r.pr] = r.it;
-      pr_i1[r.pr] = dA - t * a.p1;
-      // the pair's rows pr*q1 .. +q1-1 lie in lane group (pr*q1)/4 of an M-block
-      atomicAdd(&gcnt[(r.pr * q1) >> 2], r.pair_items);
-    }
-    if (tid == 0) {
-      const int nI = __popcll(r.mi), nP = __popcll(r.mp);
-      it_beg[nI] = n_el;
-      pr_it[nP] = nI;
-      s_cnt[0] = nI;
-      s_cnt[1] = nP;
-    }
-    wave_lds_sync();
-    if (tid < 16)
-      mb_nk[tid] = max(max(gcnt[4 * tid], gcnt[4 * tid + 1]), max(gcnt[4 * tid + 2], gcnt[4 * tid + 3]));
-  }
-  store2(nj0, tid, v2);
-  stage_g2(0, nj0, tid + WG * STAGE_U);
-  __syncthreads();
-  const int nI = s_cnt[0], nP = s_cnt[1];
   const int nmb = (nP * q1 + 15) >> 4;
-  const int mb = w;  // one M-block per wave (P * q1 <= 16 * NW)
-
-  // round 3: G3 slices -> LDS (and the dG3 accumulators cleared), G1 rows in the two
-  // operand layouts, w * dY rows of the elements.  First batches of everything are
-  // issued before the first wait.
+  const int mb = placed_mblock<NW>(s_pl);  // one M-block per wave (P * q1 <= 16 * NW)
   const int per_item = RP * q3, total3 = nI * per_item, totalY = n_el * D;
   // i = (item * RP + r2) * q3 + j3 -> (item * RP + r2, j3)
   auto split3 = [&](int i, int &jr, int &j3) {
@@ -219,7 +163,7 @@ void k_bwd(DevArgs a) {
       int jr, j3;
       split3(i, jr, j3);
       const int it = jr >> LRP, r2 = jr & (RP - 1);
-      v[u] = G3t[it_i3[it] * (int)W3 + (r2 < R2 ? r2 : 0) * q3 + j3];
+      v[u] = G3t[M.it_i3[it] * (int)W3 + (r2 < R2 ? r2 : 0) * q3 + j3];
     }
   };
   auto store3 = [&](int base, const float *v) {
@@ -239,47 +183,119 @@ void k_bwd(DevArgs a) {
     for (int u = 0; u < STAGE_U; ++u) {
       const int i = min(base + u * WG, totalY - 1);
       const int e = fdiv(i, a.mD), d = i - e * D;
-      v[u] = a.dY[(size_t)e_bag[e] * D + d];
+      v[u] = a.dY[(size_t)M.e_bag[e] * D + d];
     }
   };
   auto storeY = [&](int base, const float *v) {
 #pragma unroll
     for (int u = 0; u < STAGE_U; ++u) {
       const int i = base + u * WG;
-      if (i < totalY) sYe[i] = e_w[fdiv(i, a.mD)] * v[u];
+      if (i < totalY) sYe[i] = M.e_w[fdiv(i, a.mD)] * v[u];
     }
   };
-  float v3[STAGE_U], vy[STAGE_U];
-  load3(tid, v3);
-  loadY(tid, vy);
   float aT[KS];          // A1[row = 16mb + c][r1 = g*KS + ks]     (stage 1)
   float aG[4][NM];       // A1[row = 16mb + 4g + sr][r1 = 16mr + c] (dG2)
-  {
+  // G1 rows of the wave's M-block: aT as 16-byte vectors when the ranks fill RP
+  auto load_g1 = [&](bool vec) {
     const int row = mb * 16 + c;
     const int pr = row >> a.lq1, j1 = row & (q1 - 1);
-    const float *src = G1t + ((size_t)pr_i1[min(pr, nP - 1)] * q1 + j1) * R1;
+    const float *src = G1t + ((size_t)M.pr_i1[min(pr, nP - 1)] * q1 + j1) * R1;
+    if (vec) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) aT[ks] = src[min(g * KS + ks, R1 - 1)];
+      for (int k4 = 0; k4 < KS / 4; ++k4) {
+        const float4 x = *(const float4 *)&src[g * KS + 4 * k4];
+        aT[4 * k4] = x.x; aT[4 * k4 + 1] = x.y; aT[4 * k4 + 2] = x.z; aT[4 * k4 + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) aT[ks] = src[min(g * KS + ks, R1 - 1)];
+    }
 #pragma unroll
     for (int sr = 0; sr < 4; ++sr) {
       const int row2 = mb * 16 + 4 * g + sr;
       const int pr2 = row2 >> a.lq1, j12 = row2 & (q1 - 1);
-      const float *src2 = G1t + ((size_t)pr_i1[min(pr2, nP - 1)] * q1 + j12) * R1;
+      const float *src2 = G1t + ((size_t)M.pr_i1[min(pr2, nP - 1)] * q1 + j12) * R1;
 #pragma unroll
       for (int mr = 0; mr < NM; ++mr) aG[sr][mr] = src2[min(16 * mr + c, R1 - 1)];
     }
-  }
-  store3(tid, v3);
-  storeY(tid, vy);
-  for (int base = tid + WG * STAGE_U; base < total3; base += WG * STAGE_U) {
-    float v[STAGE_U];
-    load3(base, v);
-    store3(base, v);
-  }
-  for (int base = tid + WG * STAGE_U; base < totalY; base += WG * STAGE_U) {
-    float v[STAGE_U];
-    loadY(base, v);
-    storeY(base, v);
+  };
+  if (F44 && R1 == RP && R2 == RP) {
+    // 16-byte loads throughout (ranks fill RP, q3 = 4, D a multiple of 4): G2 along r2,
+    // an item's G3 slice as one (r2, four j3) vector per lane, w * dY along d.  The
+    // number of memory instructions, not the bytes, bounds this round.
+    constexpr int SV = 2;
+    const int n2 = nj0 * RP * RP / 4, n3 = nI * RP, D4 = D >> 2, nY = n_el * D4;
+    auto ld2 = [&](int i4) {
+      const int jj = i4 >> (2 * LRP - 2), r1 = (i4 >> (LRP - 2)) & (RP - 1);
+      const int r2 = (i4 & (RP / 4 - 1)) * 4;
+      return *(const float4 *)&G2g[((size_t)r1 * q2 + jj) * R2 + r2];
+    };
+    auto st2 = [&](int i4, float4 x) {
+      const int jj = i4 >> (2 * LRP - 2), r1 = (i4 >> (LRP - 2)) & (RP - 1);
+      const int r2 = (i4 & (RP / 4 - 1)) * 4;
+      float *d = &sG2[(size_t)jj * RP * LD + r2 * LD + r1];
+      d[0] = x.x; d[LD] = x.y; d[2 * LD] = x.z; d[3 * LD] = x.w;
+    };
+    auto ld3 = [&](int i4) {
+      return *(const float4 *)&G3t[M.it_i3[i4 >> LRP] * (int)W3 + (i4 & (RP - 1)) * 4];
+    };
+    auto ldY = [&](int i4) {
+      const int e = i4 / D4;
+      return *(const float4 *)&a.dY[(size_t)M.e_bag[e] * D + (i4 - e * D4) * 4];
+    };
+    float4 v2[SV], v3[SV], vy[SV];
+#pragma unroll
+    for (int u = 0; u < SV; ++u) {
+      v2[u] = ld2(min(tid + u * WG, n2 - 1));
+      v3[u] = ld3(min(tid + u * WG, n3 - 1));
+      vy[u] = ldY(min(tid + u * WG, nY - 1));
+    }
+    load_g1(true);
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < SV; ++u) {
+      const int i4 = tid + u * WG;
+      if (i4 < n2) st2(i4, v2[u]);
+      if (i4 < n3) {
+        *(float4 *)&sG3[4 * i4] = v3[u];
+        *(float4 *)&sdA3[4 * i4] = z4;
+      }
+      if (i4 < nY) {
+        const float we = M.e_w[i4 / D4];
+        *(float4 *)&sYe[4 * i4] = make_float4(we * vy[u].x, we * vy[u].y, we * vy[u].z,
+                                              we * vy[u].w);
+      }
+    }
+    for (int i4 = tid + SV * WG; i4 < n2; i4 += WG) st2(i4, ld2(i4));
+    for (int i4 = tid + SV * WG; i4 < n3; i4 += WG) {
+      *(float4 *)&sG3[4 * i4] = ld3(i4);
+      *(float4 *)&sdA3[4 * i4] = z4;
+    }
+    for (int i4 = tid + SV * WG; i4 < nY; i4 += WG) {
+      const float4 x = ldY(i4);
+      const float we = M.e_w[i4 / D4];
+      *(float4 *)&sYe[4 * i4] = make_float4(we * x.x, we * x.y, we * x.z, we * x.w);
+    }
+  } else {
+    float v2[STAGE_U], v3[STAGE_U], vy[STAGE_U];
+    load2(0, nj0, tid, v2);
+    load3(tid, v3);
+    loadY(tid, vy);
+    load_g1(false);
+    store2(nj0, tid, v2);
+    stage_g2(0, nj0, tid + WG * STAGE_U);
+    store3(tid, v3);
+    storeY(tid, vy);
+    for (int base = tid + WG * STAGE_U; base < total3; base += WG * STAGE_U) {
+      float v[STAGE_U];
+      load3(base, v);
+      store3(base, v);
+    }
+    for (int base = tid + WG * STAGE_U; base < totalY; base += WG * STAGE_U) {
+      float v[STAGE_U];
+      loadY(base, v);
+      storeY(base, v);
+    }
   }
   {
     const int row = mb * 16 + c;
@@ -305,7 +321,7 @@ void k_bwd(DevArgs a) {
   for (int i = tid; i < nI * D; i += WG) {
     const int it = fdiv(i, a.mD), d = i - it * D;
     float acc = 0.f;
-    for (int k = it_beg[it]; k < it_beg[it + 1]; ++k) acc += sYe[(size_t)e_perm[k] * D + d];
+    for (int k = M.it_beg[it]; k < M.it_beg[it + 1]; ++k) acc += sYe[(size_t)M.e_perm[k] * D + d];
     sGu[i] = acc;
   }
   __syncthreads();
@@ -318,9 +334,9 @@ void k_bwd(DevArgs a) {
 #pragma unroll
   for (int v = 0; v < 4; ++v) { j1v[v] = (rb + v) & (q1 - 1); prv[v] = (rb + v) >> a.lq1; }
   const int plo = rb >> a.lq1, phi = min((rb + 3) >> a.lq1, nP - 1);
-  const int ib = (mb < nmb && plo < nP) ? pr_it[plo] : 0;
-  const int ie = (mb < nmb && plo < nP) ? pr_it[phi + 1] : 0;
-  const int nk = mb < nmb ? mb_nk[mb] : 0;
+  const int ib = (mb < nmb && plo < nP) ? M.pr_it[plo] : 0;
+  const int ie = (mb < nmb && plo < nP) ? M.pr_it[phi + 1] : 0;
+  const int nk = mb < nmb ? M.mbb[mb] : 0;
 
   for (int j0 = 0; j0 < q2; j0 += JB) {
     if (j0 > 0) {  // next G2 stage (only when the slice does not fit at once)
@@ -332,98 +348,106 @@ void k_bwd(DevArgs a) {
     for (int j2 = j0; j2 < jend; ++j2) {
       const float *buf = sG2 + (size_t)(j2 - j0) * RP * LD;
       f4 gacc[NM][NM];  // dG2[r1 = 16mr + 4g + v][r2 = 16m2 + c]
-#pragma unroll
-      for (int mr = 0; mr < NM; ++mr)
-#pragma unroll
-        for (int m2 = 0; m2 < NM; ++m2) gacc[mr][m2] = zero4();
       if (mb < nmb) {
-        // stage 1: T[row = 16mb + 4g + v][r2 = 16m + c]
+        // stage 1: T[row = 16mb + 4g + v][r2 = 16m + c] (the first product starts from 0)
         f4 T[NM], dT[NM];
-#pragma unroll
-        for (int m = 0; m < NM; ++m) { T[m] = zero4(); dT[m] = zero4(); }
 #pragma unroll
         for (int kq = 0; kq < KS / 4; ++kq)
 #pragma unroll
           for (int m = 0; m < NM; ++m) {
             const float4 bv = *(const float4 *)&buf[(16 * m + c) * LD + g * KS + 4 * kq];
-            T[m] = mfma4(aT[4 * kq + 0], bv.x, T[m]);
+            T[m] = mfma4(aT[4 * kq + 0], bv.x, kq == 0 ? zero4() : T[m]);
             T[m] = mfma4(aT[4 * kq + 1], bv.y, T[m]);
             T[m] = mfma4(aT[4 * kq + 2], bv.z, T[m]);
             T[m] = mfma4(aT[4 * kq + 3], bv.w, T[m]);
           }
+#pragma unroll
+        for (int m = 0; m < NM; ++m) dT[m] = zero4();
         // the items of the pairs owning the lane group's rows
-        for (int kk = 0; kk < nk; ++kk) {
-          const int it = ib + kk;
-          const bool act = it < ie;
-          const int itc = act ? it : 0;
-          const int pr = act ? it_pair[itc] : -1;
-          const float *g3 = sG3 + (size_t)itc * per_item + c * q3;  // + 16 m q3 + j3
-          const float *gu = sGu + (size_t)itc * D;
-          float *da3 = sdA3 + (size_t)itc * per_item + c * q3;
-          if (Q3 == 4) {
-            // all four j3 at once: G_u of the four rows, the item's G3 and dG3 rows as
-            // 16-byte vectors (every offset here is a multiple of four floats)
-            float4 gx[4];
+        if (F44) {
+          // q1 = q3 = 4: a lane group's four rows are one pair (j1 = v); each lane group
+          // runs its own pair's items (inactive lanes simply sit out), all four j3 of an
+          // item's G_u, G3 and dG3 rows as 16-byte vectors
+          for (int kk = 0; kk < nk; ++kk) {
+            const int it = ib + kk;
+            if (it < ie) {
+              const float *g3 = sG3 + (size_t)it * per_item + c * 4;  // + 64 m
+              const float *gu = sGu + (size_t)it * D + j2 * 4;        // + 4 q2 j1
+              float *da3 = sdA3 + (size_t)it * per_item + c * 4;
+              float4 gx[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              gx[v] = *(const float4 *)&gu[(j1v[v] * q2 + j2) * 4];
-              if (!(act && prv[v] == pr)) gx[v] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+              for (int v = 0; v < 4; ++v) gx[v] = *(const float4 *)&gu[v * q2 * 4];
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {  // one column block's G3 / dG3 vectors live
-              const float4 a3 = *(const float4 *)&g3[64 * m];
-              float4 d3 = *(const float4 *)&da3[64 * m];
-#pragma unroll
-              for (int u = 0; u < 4; ++u) {
-                float sacc = 0.f;
+              for (int m = 0; m < NM; ++m) {
+                const float4 a3 = *(const float4 *)&g3[64 * m];
+                float4 d3 = *(const float4 *)&da3[64 * m];
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                  sacc += T[m][v] * gx[v][u];
-                  dT[m][v] += gx[v][u] * a3[u];
+                  d3.x = fmaf(T[m][v], gx[v].x, d3.x);
+                  d3.y = fmaf(T[m][v], gx[v].y, d3.y);
+                  d3.z = fmaf(T[m][v], gx[v].z, d3.z);
+                  d3.w = fmaf(T[m][v], gx[v].w, d3.w);
+                  dT[m][v] = fmaf(gx[v].x, a3.x, dT[m][v]);
+                  dT[m][v] = fmaf(gx[v].y, a3.y, dT[m][v]);
+                  dT[m][v] = fmaf(gx[v].z, a3.z, dT[m][v]);
+                  dT[m][v] = fmaf(gx[v].w, a3.w, dT[m][v]);
                 }
-                d3[u] += sacc;
+                *(float4 *)&da3[64 * m] = d3;
               }
-              if (act) *(float4 *)&da3[64 * m] = d3;
             }
-            continue;
           }
-          // JU j3 at a time: all LDS reads of the block first, then the arithmetic,
-          // then the updated dG3 partials (one writer lane per element)
-          for (int j30 = 0; j30 < q3; j30 += JU) {
-            float gx[JU][4], a3[JU][NM], d3[JU][NM];
+        } else {
+          for (int kk = 0; kk < nk; ++kk) {
+            const int it = ib + kk;
+            const bool act = it < ie;
+            const int itc = act ? it : 0;
+            const int pr = act ? M.it_pair[itc] : -1;
+            const float *g3 = sG3 + (size_t)itc * per_item + c * q3;  // + 16 m q3 + j3
+            const float *gu = sGu + (size_t)itc * D;
+            float *da3 = sdA3 + (size_t)itc * per_item + c * q3;
+            // JU j3 at a time: all LDS reads of the block first, then the arithmetic,
+            // then the updated dG3 partials (one writer lane per element); rows of
+            // another pair (q1 < 4: a lane group spans several pairs) get weight 0
+            float mk[4];
 #pragma unroll
-            for (int u = 0; u < JU; ++u) {
-              const int j3 = min(j30 + u, q3 - 1);
+            for (int v = 0; v < 4; ++v) mk[v] = (act && prv[v] == pr) ? 1.f : 0.f;
+            for (int j30 = 0; j30 < q3; j30 += JU) {
+              float gx[JU][4], a3[JU][NM], d3[JU][NM];
 #pragma unroll
-              for (int v = 0; v < 4; ++v) gx[u][v] = gu[((j1v[v]) * q2 + j2) * q3 + j3];
+              for (int u = 0; u < JU; ++u) {
+                const int j3 = min(j30 + u, q3 - 1);
 #pragma unroll
-              for (int m = 0; m < NM; ++m) {
-                a3[u][m] = g3[16 * m * q3 + j3];
-                d3[u][m] = da3[16 * m * q3 + j3];
-              }
-            }
+                for (int v = 0; v < 4; ++v)
+                  gx[u][v] = mk[v] * gu[((j1v[v]) * q2 + j2) * q3 + j3];
 #pragma unroll
-            for (int u = 0; u < JU; ++u) {
-              const bool ok3 = act && j30 + u < q3;
-              float gv[4];
-#pragma unroll
-              for (int v = 0; v < 4; ++v) gv[v] = (ok3 && prv[v] == pr) ? gx[u][v] : 0.f;
-#pragma unroll
-              for (int m = 0; m < NM; ++m) {
-                float sacc = 0.f;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                  sacc += T[m][v] * gv[v];
-                  dT[m][v] += gv[v] * a3[u][m];
+                for (int m = 0; m < NM; ++m) {
+                  a3[u][m] = g3[16 * m * q3 + j3];
+                  d3[u][m] = da3[16 * m * q3 + j3];
                 }
-                d3[u][m] += sacc;
+              }
+#pragma unroll
+              for (int u = 0; u < JU; ++u) {
+                const bool ok3 = j30 + u < q3;
+#pragma unroll
+                for (int m = 0; m < NM; ++m) {
+                  float sacc = 0.f;
+#pragma unroll
+                  for (int v = 0; v < 4; ++v) {
+                    const float gv = ok3 ? gx[u][v] : 0.f;
+                    sacc += T[m][v] * gv;
+                    dT[m][v] += gv * a3[u][m];
+                  }
+                  d3[u][m] += sacc;
+                }
+              }
+              if (act) {
+#pragma unroll
+                for (int u = 0; u < JU; ++u)
+                  if (j30 + u < q3)
+#pragma unroll
+                    for (int m = 0; m < NM; ++m) da3[16 * m * q3 + j30 + u] = d3[u][m];
               }
             }
-#pragma unroll
-            for (int u = 0; u < JU; ++u)
-              if (act && j30 + u < q3)
-#pragma unroll
-                for (int m = 0; m < NM; ++m) da3[16 * m * q3 + j30 + u] = d3[u][m];
           }
         }
         // dG2 += A1^T dT   (K = the 16 rows; lane group g feeds rows 4g + sr)
@@ -433,7 +457,7 @@ void k_bwd(DevArgs a) {
           for (int mr = 0; mr < NM; ++mr)
 #pragma unroll
             for (int m2 = 0; m2 < NM; ++m2)
-              gacc[mr][m2] = mfma4(aG[sr][mr], dT[m2][sr], gacc[mr][m2]);
+              gacc[mr][m2] = mfma4(aG[sr][mr], dT[m2][sr], sr == 0 ? zero4() : gacc[mr][m2]);
         // dG1^T += G2_j2 dT^T  (K = r2; dT transposed through the wave's LDS tile)
         float *tt = sT + (size_t)w * 16 * LD;
 #pragma unroll
@@ -452,30 +476,54 @@ void k_bwd(DevArgs a) {
             dA1[mr] = mfma4(buf[(16 * m + 4 * g + 3) * LD + 16 * mr + c], bT.w, dA1[mr]);
           }
         }
+      } else {
+#pragma unroll
+        for (int mr = 0; mr < NM; ++mr)
+#pragma unroll
+          for (int m2 = 0; m2 < NM; ++m2) gacc[mr][m2] = zero4();
       }
-      // reduce dG2 over the waves: wave w adds into slot w % nred, rounds in wave order,
-      // then the slots are summed in slot order
+      // reduce dG2 over the waves in M-block order (the order does not depend on which
+      // wave holds which M-block, so the sum is reproducible): M-block mb adds into slot
+      // mb % nred in round mb / nred, then the slots are summed in slot order.  A slot holds
+      // [r2][r1] (row pitch LD), so a lane's four r1 = 16mr + 4g .. +3 of one r2 move as
+      // one 16-byte vector.
       __syncthreads();  // the transpose tiles (aliased by the slots) are free
       for (int rr = 0; rr < NW / nred; ++rr) {
-        if (w / nred == rr) {
-          float *slot = sRed + (size_t)(w % nred) * RP * LD;
+        if (mb / nred == rr) {
+          float *slot = sRed + (size_t)(mb % nred) * RP * LD;
 #pragma unroll
           for (int mr = 0; mr < NM; ++mr)
 #pragma unroll
-            for (int m2 = 0; m2 < NM; ++m2)
-#pragma unroll
-              for (int v = 0; v < 4; ++v) {
-                const int idx = (16 * mr + 4 * g + v) * LD + 16 * m2 + c;
-                slot[idx] = (rr == 0 ? 0.f : slot[idx]) + gacc[mr][m2][v];
+            for (int m2 = 0; m2 < NM; ++m2) {
+              float4 *q = (float4 *)&slot[(16 * m2 + c) * LD + 16 * mr + 4 * g];
+              float4 x = make_float4(gacc[mr][m2][0], gacc[mr][m2][1], gacc[mr][m2][2],
+                                     gacc[mr][m2][3]);
+              if (rr > 0) {
+                const float4 o = *q;
+                x.x += o.x; x.y += o.y; x.z += o.z; x.w += o.w;
               }
+              *q = x;
+            }
         }
         __syncthreads();
       }
-      for (int i = tid; i < RP * RP; i += WG) {
-        const int r1 = i >> LRP, r2 = i & (RP - 1);
-        float val = 0.f;
-        for (int k = 0; k < nred; ++k) val += sRed[k * RP * LD + r1 * LD + r2];
-        if (r1 < R1 && r2 < R2) part2[(r1 * q2 + j2) * R2 + r2] = val;
+      // thread t: r2 = t mod RP, r1 = 4 (t / RP) .. +3, summed over the slots in order; the
+      // partial keeps the slice layout [r1][j2][r2] (consecutive threads, consecutive r2)
+      for (int t4 = tid; t4 < RP * RP / 4; t4 += WG) {
+        const int r2 = t4 & (RP - 1), r1 = (t4 >> LRP) * 4;
+        float4 acc = *(const float4 *)&sRed[r2 * LD + r1];
+        for (int k = 1; k < nred; ++k) {
+          const float4 o = *(const float4 *)&sRed[(size_t)k * RP * LD + r2 * LD + r1];
+          acc.x += o.x; acc.y += o.y; acc.z += o.z; acc.w += o.w;
+        }
+        if (r2 < R2) {
+          float *dst = part2 + ((size_t)r1 * q2 + j2) * R2 + r2;
+          const size_t st = (size_t)q2 * R2;
+          if (r1 + 0 < R1) dst[0] = acc.x;
+          if (r1 + 1 < R1) dst[st] = acc.y;
+          if (r1 + 2 < R1) dst[2 * st] = acc.z;
+          if (r1 + 3 < R1) dst[3 * st] = acc.w;
+        }
       }
       __syncthreads();
     }
@@ -485,7 +533,7 @@ void k_bwd(DevArgs a) {
     const int row = mb * 16 + c;
     const int pr = row >> a.lq1, j1 = row & (q1 - 1);
     if (pr < nP) {
-      float *dst = a.part1 + (size_t)(s0 + it_first[pr_it[pr]]) * W1 + (size_t)j1 * R1;
+      float *dst = a.part1 + (size_t)(s0 + M.it_first[M.pr_it[pr]]) * W1 + (size_t)j1 * R1;
 #pragma unroll
       for (int mr = 0; mr < NM; ++mr)
 #pragma unroll
@@ -499,42 +547,43 @@ void k_bwd(DevArgs a) {
     int jr, j3;
     split3(i, jr, j3);
     const int it = jr >> LRP, r2 = jr & (RP - 1);
-    if (r2 < R2) a.part3[(size_t)(s0 + it_first[it]) * W3 + r2 * q3 + j3] = sdA3[i];
+    if (r2 < R2) a.part3[(size_t)(s0 + M.it_first[it]) * W3 + r2 * q3 + j3] = sdA3[i];
   }
 }
 
-template <int RP, int Q3, bool HITS>
+template <int RP, bool F44, bool HITS>
 static hipError_t launch_bwd_k(const DevArgs &a, size_t lds, hipStream_t s) {
   static bool attr_set = false;  // dynamic LDS above 64 KiB is opt-in per kernel
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void *)k_bwd<RP, Q3, HITS>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    (void)hipFuncSetAttribute((const void *)k_bwd<RP, F44, HITS>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, LDS_DYN_MAX);
     attr_set = true;
   }
   // with a cache, extra workgroups (eight 64-position pieces each) sum the hit runs
   const int pieces = HITS ? (a.nnz + PIECE - 1) / PIECE : 0;
   const int grid = items_max(a) + (pieces + NW - 1) / NW;
-  tt_launch(K_BWD, k_bwd<RP, Q3, HITS>, dim3(grid), dim3(WG), lds, s, a);
+  tt_launch(K_BWD, k_bwd<RP, F44, HITS>, dim3(grid), dim3(WG), lds, s, a);
   return hipGetLastError();
 }
 
-template <int RP, int Q3>
+template <int RP, bool F44>
 static hipError_t launch_bwd_t(const DevArgs &a, size_t lds, hipStream_t s) {
-  return a.has_cache ? launch_bwd_k<RP, Q3, true>(a, lds, s)
-                     : launch_bwd_k<RP, Q3, false>(a, lds, s);
+  return a.has_cache ? launch_bwd_k<RP, F44, true>(a, lds, s)
+                     : launch_bwd_k<RP, F44, false>(a, lds, s);
 }
 
-template <int Q3>
+template <bool F44>
 static hipError_t launch_bwd_q(const DevArgs &a, int RP, size_t lds, hipStream_t s) {
   switch (RP) {
-    case 16: return launch_bwd_t<16, Q3>(a, lds, s);
-    case 32: return launch_bwd_t<32, Q3>(a, lds, s);
-    default: return launch_bwd_t<64, Q3>(a, lds, s);
+    case 16: return launch_bwd_t<16, F44>(a, lds, s);
+    case 32: return launch_bwd_t<32, F44>(a, lds, s);
+    default: return launch_bwd_t<64, F44>(a, lds, s);
   }
 }
 
 hipError_t launch_bwd(const DevArgs &a, int RP, size_t lds, hipStream_t s) {
-  return a.q3 == 4 ? launch_bwd_q<4>(a, RP, lds, s) : launch_bwd_q<0>(a, RP, lds, s);
+  return (a.q1 == 4 && a.q3 == 4) ? launch_bwd_q<true>(a, RP, lds, s)
+                                  : launch_bwd_q<false>(a, RP, lds, s);
 }
 
 // ---------------------------------------------------------------- k_seg

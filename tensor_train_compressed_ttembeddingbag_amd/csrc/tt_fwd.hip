@@ -33,7 +33,7 @@ namespace ttb {
 template <int RP>
 struct FwdLds {
   static constexpr int LD = RP + 4;  // row pitch of G2^T [r2][r1]: conflict-free 16-byte reads
-  static constexpr int INTS = 64 * 6 + 65 * 2 + 64 + 16 + 8;
+  static constexpr int INTS = META_INTS;
   __host__ __device__ static size_t g2_floats(int JB) { return (size_t)JB * RP * LD; }
   __host__ __device__ static size_t g3_floats(int P, int q3) { return (size_t)P * q3 * RP; }
   __host__ __device__ static size_t w_floats(int P, int D, int sw) { return sw ? (size_t)P * D : 0; }
@@ -101,24 +101,17 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
   float *sG2 = smem;                                            // [JB][r2 < RP][LD]
   float *sG3 = sG2 + FwdLds<RP>::g2_floats(JB);                 // [item][j3][r2 < RP]
   float *sW = sG3 + FwdLds<RP>::g3_floats(P, q3);               // [item][D]
-  int *e_bag = (int *)(sW + FwdLds<RP>::w_floats(P, D, SW));  // [64]
-  float *e_w = (float *)(e_bag + 64);                           // [64]
-  int *e_it = (int *)(e_w + 64);                                // [64]
-  int *it_i3 = e_it + 64;                                       // [64]
-  int *it_beg = it_i3 + 64;                                     // [65]
-  int *pr_it = it_beg + 65;                                     // [65]
-  int *pr_i1 = pr_it + 65;                                      // [64]
-  int *mb_nk = pr_i1 + 64;                                      // [16]
-  int *s_cnt = mb_nk + 16;                                      // [8]
-  int *e_perm = s_cnt + 8;                                      // [64] item-major elements
-  int *e_n = e_perm + 64;                                       // [64] element positions
+  int *s_meta = (int *)(sW + FwdLds<RP>::w_floats(P, D, SW));  // [META_INTS]
+  const WorkMeta &M = *(const WorkMeta *)s_meta;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int wi = blockIdx.x;
   const bool clearer = a.fzero && wi < fwd_zero_blocks(a);
-  // round 1: plan check and work item (a stale plan leaves out untouched)
+  // round 1: plan check and the work item's metadata (a stale plan leaves out untouched)
   const int plan = a.hdr[H_PLAN], nitems = a.hdr[H_NFWD];
-  const int4 item = a.fitem[wi];
+  __shared__ int s_pl[NW];
+  if (tid < META_INTS) s_meta[tid] = a.meta[(size_t)wi * META_INTS + tid];
+  note_placement(s_pl);
   const bool stale = plan != (int)a.plan_fp;
   if (clearer && !stale) fwd_clear_out(a);
   if (stale || wi >= nitems) {
@@ -126,8 +119,9 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
     if (stale && wi == 0 && tid == 0) set_status(a.status, DEV_STALE_PLAN);
     return;
   }
-  const int grp = item.x, s0 = item.y, s1 = item.z;
-  const int n_el = s1 - s0;
+  __syncthreads();
+  const int grp = M.grp, n_el = M.n_el, nI = M.nI, nP = M.nP;
+  const int wp = placed_mblock<NW>(s_pl);  // this wave's M-block (MBW = 1)
   const int t = grp / a.p2;
   const float *G2g = a.G2 + (size_t)grp * R1 * q2 * R2;  // slice [r1][j2][r2]
   const size_t W3 = (size_t)R2 * q3;
@@ -163,52 +157,13 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
       store2(nj, base, v);
     }
   };
-
-  // round 2: the elements (wave 0) and the first G2 stage (all waves; the first batch
-  // is in flight while wave 0 sorts out the elements)
   const int nj0 = min(JB, q2);
-  float v2[STAGE_U];
-  load2(0, nj0, tid, v2);
-  if (tid < 64) {
-    const int s = s0 + min(tid, n_el - 1);
-    const bool v = tid < n_el;
-    const SPos sp = load_spos(a.srec, s);
-    const int dAv = sp.dA, dIv = sp.dI3, bagv = sp.bag;
-    const float wv = sp.w;
-    const int dA = v ? dAv : -1, i3 = v ? dIv - t * a.p3 : 0;
-    e_bag[tid] = bagv;
-    e_w[tid] = wv;
-    e_n[tid] = sp.n;
-    const WaveItems r = wave_items(v, dA, i3, nbits_for(a.p3));
-    e_it[tid] = r.e_it;
-    if (v) e_perm[r.item_pos] = tid;
-    if (tid < 16) mb_nk[tid] = 0;
-    wave_lds_sync();
-    if (r.item_st) { it_beg[r.it] = r.it_beg; it_i3[r.it] = i3; }
-    if (r.pair_st) {
-      pr_it[r.pr] = r.it;
-      pr_i1[r.pr] = dA - t * a.p1;
-      atomicMax(&mb_nk[(r.pr * q1) >> 4], r.pair_items);
-    }
-    if (tid == 0) {
-      const int nI = __popcll(r.mi), nP = __popcll(r.mp);
-      it_beg[nI] = n_el;
-      pr_it[nP] = nI;
-      s_cnt[0] = nI;
-      s_cnt[1] = nP;
-    }
-  }
-  store2(nj0, tid, v2);
-  stage_g2(0, nj0, tid + WG * STAGE_U);
-  if (clearer) fwd_raise_flag(a);  // (includes the barrier)
-  else __syncthreads();
-  const int nI = s_cnt[0], nP = s_cnt[1];
   const int nmb = (nP * q1 + 15) >> 4;
 
-  // round 3: the G3 slices of the item's indices -> LDS [item][j3][r2 < RP], and the B
-  // operand of stage 1 (G1 rows of the wave's M-blocks, kept for all j2).  The first
-  // G3 batch and all G1 loads are issued before the first wait; rows past the pairs
-  // read a valid row and are zeroed afterwards.
+  // round 2: the first G2 stage, the G3 slices of the item's indices -> LDS
+  // [item][j3][r2 < RP], and the B operand of stage 1 (G1 rows of the wave's M-blocks,
+  // kept for all j2).  The first batch of everything is issued before the first wait;
+  // rows past the pairs read a valid row and are zeroed afterwards.
   const int per_item = RP * q3, total3 = nI * per_item;
   // element i = (item * RP + r2) * q3 + j3: contiguous in the global slice [r2][j3],
   // stored to LDS at (item * q3 + j3) * RP + r2
@@ -217,7 +172,7 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
     for (int u = 0; u < STAGE_U; ++u) {
       const int i = min(base + u * WG, total3 - 1);
       const int jr = fdiv(i, a.mq3), j3 = i - jr * q3, it = jr >> LRP, r2 = jr & (RP - 1);
-      v[u] = G3t[it_i3[it] * (int)W3 + (r2 < R2 ? r2 : 0) * q3 + j3];
+      v[u] = G3t[M.it_i3[it] * (int)W3 + (r2 < R2 ? r2 : 0) * q3 + j3];
     }
   };
   auto store3 = [&](int base, const float *v) {
@@ -230,34 +185,91 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
       }
     }
   };
-  float v3[STAGE_U];
-  load3(tid, v3);
   float bv[MBW][KS];
+  auto load_g1 = [&](bool vec) {
+#pragma unroll
+    for (int mbi = 0; mbi < MBW; ++mbi) {
+      const int row = (wp + mbi * NW) * 16 + c;
+      const int pr = row >> a.lq1, j1 = row & (q1 - 1);
+      const float *src =
+          a.G1 + ((size_t)(t * a.p1 + M.pr_i1[min(pr, nP - 1)]) * q1 + j1) * R1;
+      if (vec) {
+#pragma unroll
+        for (int k4 = 0; k4 < KS / 4; ++k4) {
+          const float4 x = *(const float4 *)&src[g * KS + 4 * k4];
+          bv[mbi][4 * k4] = x.x; bv[mbi][4 * k4 + 1] = x.y;
+          bv[mbi][4 * k4 + 2] = x.z; bv[mbi][4 * k4 + 3] = x.w;
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bv[mbi][ks] = src[min(g * KS + ks, R1 - 1)];
+      }
+    }
+  };
+  if (q3 == 4 && R1 == RP && R2 == RP) {
+    // 16-byte loads (ranks fill RP, q3 = 4): G2 along r2, one (r2, four j3) vector of an
+    // item's G3 slice per lane; the LDS layouts stay those of the general path
+    constexpr int SV = 2;
+    const int n2 = nj0 * RP * RP / 4, n3 = nI * RP;
+    auto ld2 = [&](int i4) {
+      const int jj = i4 >> (2 * LRP - 2), r1 = (i4 >> (LRP - 2)) & (RP - 1);
+      const int r2 = (i4 & (RP / 4 - 1)) * 4;
+      return *(const float4 *)&G2g[((size_t)r1 * q2 + jj) * R2 + r2];
+    };
+    auto st2 = [&](int i4, float4 x) {
+      const int jj = i4 >> (2 * LRP - 2), r1 = (i4 >> (LRP - 2)) & (RP - 1);
+      const int r2 = (i4 & (RP / 4 - 1)) * 4;
+      float *d = &sG2[(size_t)jj * RP * LD + r2 * LD + r1];
+      d[0] = x.x; d[LD] = x.y; d[2 * LD] = x.z; d[3 * LD] = x.w;
+    };
+    auto ld3 = [&](int i4) {
+      return *(const float4 *)&G3t[M.it_i3[i4 >> LRP] * (int)W3 + (i4 & (RP - 1)) * 4];
+    };
+    auto st3 = [&](int i4, float4 x) {  // LDS [item][j3][r2]
+      float *d = &sG3[(size_t)(i4 >> LRP) * 4 * RP + (i4 & (RP - 1))];
+      d[0] = x.x; d[RP] = x.y; d[2 * RP] = x.z; d[3 * RP] = x.w;
+    };
+    float4 v2[SV], v3[SV];
+#pragma unroll
+    for (int u = 0; u < SV; ++u) {
+      v2[u] = ld2(min(tid + u * WG, n2 - 1));
+      v3[u] = ld3(min(tid + u * WG, n3 - 1));
+    }
+    load_g1(true);
+#pragma unroll
+    for (int u = 0; u < SV; ++u) {
+      const int i4 = tid + u * WG;
+      if (i4 < n2) st2(i4, v2[u]);
+      if (i4 < n3) st3(i4, v3[u]);
+    }
+    for (int i4 = tid + SV * WG; i4 < n2; i4 += WG) st2(i4, ld2(i4));
+    for (int i4 = tid + SV * WG; i4 < n3; i4 += WG) st3(i4, ld3(i4));
+  } else {
+    float v2[STAGE_U], v3[STAGE_U];
+    load2(0, nj0, tid, v2);
+    load3(tid, v3);
+    load_g1(false);
+    store2(nj0, tid, v2);
+    stage_g2(0, nj0, tid + WG * STAGE_U);
+    store3(tid, v3);
+    for (int base = tid + WG * STAGE_U; base < total3; base += WG * STAGE_U) {
+      float v[STAGE_U];
+      load3(base, v);
+      store3(base, v);
+    }
+  }
 #pragma unroll
   for (int mbi = 0; mbi < MBW; ++mbi) {
-    const int row = (w + mbi * NW) * 16 + c;
-    const int pr = row >> a.lq1, j1 = row & (q1 - 1);
-    const float *src = a.G1 + ((size_t)(t * a.p1 + pr_i1[min(pr, nP - 1)]) * q1 + j1) * R1;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) bv[mbi][ks] = src[min(g * KS + ks, R1 - 1)];
-  }
-  store3(tid, v3);
-  for (int base = tid + WG * STAGE_U; base < total3; base += WG * STAGE_U) {
-    float v[STAGE_U];
-    load3(base, v);
-    store3(base, v);
-  }
-#pragma unroll
-  for (int mbi = 0; mbi < MBW; ++mbi) {
-    const int row = (w + mbi * NW) * 16 + c;
-    const bool ok = (w + mbi * NW) < nmb && (row >> a.lq1) < nP;
+    const int row = (wp + mbi * NW) * 16 + c;
+    const bool ok = (wp + mbi * NW) < nmb && (row >> a.lq1) < nP;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const float v = keep(bv[mbi][ks]);
       bv[mbi][ks] = (ok && g * KS + ks < R1) ? v : 0.f;
     }
   }
-  __syncthreads();
+  if (clearer) fwd_raise_flag(a);  // (includes the barrier)
+  else __syncthreads();
 
   if (a.fzero && !SW) fwd_wait_out(a);  // stage 2 adds into out directly
   for (int j0 = 0; j0 < q2; j0 += JB) {
@@ -271,7 +283,7 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
       const float *buf = sG2 + (size_t)(j2 - j0) * RP * LD;
 #pragma unroll
       for (int mbi = 0; mbi < MBW; ++mbi) {
-        const int mb = w + mbi * NW;
+        const int mb = wp + mbi * NW;
         if (mb >= nmb) break;
         f4 acc[NM];
 #pragma unroll
@@ -295,9 +307,9 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
           // Lane (g, c) gets rows 4g .. 4g+3 of the M-block (its pair p0 + g, j1 = v) in
           // column c and keeps the columns of its own pair's items.
           const int p0 = mb * 4;  // mb < nmb, so p0 < nP
-          const int it0 = pr_it[p0], it1 = pr_it[min(p0 + 4, nP)];
+          const int it0 = M.pr_it[p0], it1 = M.pr_it[min(p0 + 4, nP)];
           const int myp = p0 + g;
-          const int mib = myp < nP ? pr_it[myp] : 0, mie = myp < nP ? pr_it[myp + 1] : 0;
+          const int mib = myp < nP ? M.pr_it[myp] : 0, mie = myp < nP ? M.pr_it[myp + 1] : 0;
           const int s4 = c >> 2, jc = c & 3;
           for (int nb = it0; nb < it1; nb += 4) {
             const int it = nb + s4;
@@ -325,8 +337,8 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
         const int row = mb * 16 + c;
         const int pr = row >> a.lq1, j1 = row & (q1 - 1);
         const bool okp = pr < nP;
-        const int ib = okp ? pr_it[pr] : 0, ie = okp ? pr_it[pr + 1] : 0;
-        const int nk = mb_nk[mb];
+        const int ib = okp ? M.pr_it[pr] : 0, ie = okp ? M.pr_it[pr + 1] : 0;
+        const int nk = M.mbf[mb];
         const int col0 = (j1 * q2 + j2) * q3;
         for (int kk = 0; kk < nk; ++kk) {
           const int it = ib + kk;
@@ -354,9 +366,9 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
               if (SW) {
                 sW[(size_t)it * D + col0 + j3] = val;
               } else {
-                for (int k = it_beg[it]; k < it_beg[it + 1]; ++k) {
-                  const int e = e_perm[k];
-                  unsafeAtomicAdd(a.Y + (size_t)e_bag[e] * D + col0 + j3, e_w[e] * val);
+                for (int k = M.it_beg[it]; k < M.it_beg[it + 1]; ++k) {
+                  const int e = M.e_perm[k];
+                  unsafeAtomicAdd(a.Y + (size_t)M.e_bag[e] * D + col0 + j3, M.e_w[e] * val);
                 }
               }
             }
@@ -368,7 +380,7 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
   if (DOT) {  // dL/dw per element: one wave per element, row . grad_out[bag]
     __syncthreads();
     for (int e = w; e < n_el; e += NW) {
-      const int it = e_it[e], b = e_bag[e];
+      const int it = M.e_it[e], b = M.e_bag[e];
       float acc = 0.f;
       for (int d = lane; d < D; d += 64) acc += sW[(size_t)it * D + d] * a.dY[(size_t)b * D + d];
 #pragma unroll
@@ -379,7 +391,7 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
           const long long len = a.off[b + 1] - a.off[b];
           scale = 1.f / (float)(len > 0 ? len : 1);
         }
-        a.gw[e_n[e]] = acc * scale;
+        a.gw[a.srec[2 * (size_t)(M.s0 + e)].x] = acc * scale;  // element position n
       }
     }
     return;
@@ -389,9 +401,9 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
   if (a.fzero) fwd_wait_out(a);  // (includes the barrier)
   else __syncthreads();
   for (int e = w; e < n_el; e += NW) {
-    const int it = e_it[e];
-    float *yrow = a.Y + (size_t)e_bag[e] * D;
-    const float we = e_w[e];
+    const int it = M.e_it[e];
+    float *yrow = a.Y + (size_t)M.e_bag[e] * D;
+    const float we = M.e_w[e];
     for (int d = lane; d < D; d += 64) unsafeAtomicAdd(yrow + d, we * sW[(size_t)it * D + d]);
   }
 }
@@ -423,7 +435,7 @@ static hipError_t launch_fwd_k(const DevArgs &a, size_t lds, hipStream_t s) {
   static bool attr_set = false;  // dynamic LDS above 64 KiB is opt-in per kernel
   if (!attr_set) {
     (void)hipFuncSetAttribute((const void *)k_fwd<RP, DOT, MF>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, LDS_DYN_MAX);
     attr_set = true;
   }
   tt_launch(K_FWD, k_fwd<RP, DOT, MF>, dim3(items_max(a)), dim3(WG), lds, s, a);

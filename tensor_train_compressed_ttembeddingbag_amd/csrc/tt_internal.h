@@ -36,6 +36,9 @@ constexpr int COOP_TILES = 256; // blocks of the one-launch grouping kernel (one
 constexpr int FWD_ZERO_BLOCKS = 64;  // forward blocks that clear out when it does
 constexpr int COOP_CELLS = 65536;  // its bins x tiles per digit (each block reads them all)
 constexpr int COOP_LDS_CELLS = 12288;  // (t,i2) x tile counts gathered in LDS up to this size
+// dynamic LDS a contraction workgroup may take: the CU's 160 KiB less room for the
+// kernels' few static LDS words (kept out of the plans, so that static + dynamic fit)
+constexpr int LDS_DYN_MAX = 160 * 1024 - 256;
 
 // header words inside the workspace (after three 64-bit "last block" counters)
 enum {
@@ -45,6 +48,30 @@ enum {
   H_PLAN = 7,       // fingerprint of the call that made the grouping (tt_bag_plan)
   H_WORDS = 64
 };
+
+// Metadata of one contraction work item, written by the grouping (k_meta) and read whole
+// into LDS by the contraction kernels: the item's elements (final-order positions s0 ..
+// s0 + n_el), its "items" (distinct indices, numbered by their first element) and its
+// "pairs" (distinct (i1, i2), runs of the grouping order).  Offsets inside a work item
+// fit a byte (P <= 32 positions); i1 and i3 (< 8192) fit a short.
+constexpr int META_INTS = 192;  // 768 bytes per work item
+struct WorkMeta {
+  int n_el, nI, nP, grp, s0, pad[3];
+  int e_bag[P_MAX];                 // bag of each element
+  float e_w[P_MAX];                 // its weight (times 1 / length with mean pooling)
+  short pr_i1[P_MAX];               // i1 of each pair (inside its table)
+  short it_i3[P_MAX];               // i3 of each item (inside its table)
+  unsigned char e_perm[P_MAX];      // item-major slot -> element
+  unsigned char e_it[P_MAX];        // element -> item
+  unsigned char it_pair[P_MAX];     // item -> pair
+  unsigned char it_first[P_MAX];    // item -> its first element
+  unsigned char it_beg[P_MAX + 4];  // item -> first item-major slot; [nI] = n_el
+  unsigned char pr_it[P_MAX + 4];   // pair -> first item; [nP] = nI
+  unsigned char gcnt[P_MAX];        // lane group (4 rows) -> items of the pairs starting in it
+  unsigned char mbf[8];             // M-block (16 rows) -> most items of one of its pairs
+  unsigned char mbb[8];             // M-block -> most gcnt of its four lane groups
+};
+static_assert(sizeof(WorkMeta) <= META_INTS * 4, "work-item metadata too large");
 
 struct DevArgs {
   // shape
@@ -96,6 +123,7 @@ struct DevArgs {
   int4 *srec;       // final order, 2 int4 per position: (element n, dA, dB, dI3),
                     // (bag, position in orderI3, weight bits, position in orderA)
   int4 *fitem;      // work items: (group, first position, end position, 0)
+  int *meta;        // [items][META_INTS] work-item metadata (WorkMeta)
   int *grp_off;     // [binsB + 1]
   int *chunk_pre;   // [T*p2 + 1]
   int *link1, *link3;  // orderA / orderI3 position -> final position of the partial, or -1
@@ -161,7 +189,7 @@ constexpr int DEV_STALE_PLAN = 16;
 // kernels named by the optional per-kernel timer (tt_prof.hip)
 enum KernelId {
   K_ROUTE_COOP, K_ROUTE_A, K_ROUTE_B, K_ROUTE_C, K_FWD, K_BWD, K_SEG,
-  K_CACHE_LOOKUP, K_YINIT, K_ZERO, K_DMERGE, K_DSPLIT, K_DAPPLY, K_DD_FRAG, K_DD_GU,
+  K_CACHE_LOOKUP, K_YINIT, K_ZERO, K_DMERGE, K_DSPLIT, K_DAPPLY, K_DD_FRAG, K_DD_GU, K_META,
   K_COUNT
 };
 // Start / stop events for one launch of kernel `id`, recorded by the kernel's own

@@ -59,4 +59,38 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// Placement of the M-blocks (16-row blocks) of a contraction workgroup on its waves.  An
+// 8-wave workgroup puts two waves on each SIMD of its CU, but a work item has fewer
+// M-blocks than waves (6 of 8 is typical), so with the identity map two SIMDs carry twice
+// the matrix work of the other two -- in both workgroups that share a CU.  Each wave
+// records where it runs (hardware register HW_ID: wave slot [3:0], SIMD [5:4]); after a
+// barrier every wave derives the same map: M-blocks go round-robin over the SIMDs, the
+// CU's first workgroup (it holds the lowest wave slots) starting at SIMD 0 and the second
+// at SIMD 2, so that the two workgroups' extra M-blocks land on different SIMDs.  Any
+// other placement (not two waves per SIMD) keeps the identity map.  Correctness does not
+// depend on the map: it is a permutation of the waves.
+__device__ __forceinline__ void note_placement(int *s_pl) {  // before a barrier
+  if ((threadIdx.x & 63) == 0)
+    s_pl[threadIdx.x >> 6] = (int)__builtin_amdgcn_s_getreg((5 << 11) | 4);  // HW_ID[5:0]
+}
+template <int NWAVES>
+__device__ __forceinline__ int placed_mblock(const int *s_pl) {  // after the barrier
+  const int w = threadIdx.x >> 6;
+  int cnt[4] = {0, 0, 0, 0}, slot0 = 16;
+#pragma unroll
+  for (int v = 0; v < NWAVES; ++v) {
+    const int sm = (s_pl[v] >> 4) & 3;
+    cnt[sm] += 1;
+    if (sm == 0) slot0 = min(slot0, s_pl[v] & 15);
+  }
+  if (cnt[0] * 4 != NWAVES || cnt[1] * 4 != NWAVES || cnt[2] * 4 != NWAVES ||
+      cnt[3] * 4 != NWAVES)
+    return w;
+  const int my = (s_pl[w] >> 4) & 3;
+  int rank = 0;
+  for (int v = 0; v < w; ++v) rank += ((s_pl[v] >> 4) & 3) == my;
+  const int rot = slot0 >= 2 ? 2 : 0;
+  return rank * 4 + ((my - rot) & 3);
+}
+
 }  // namespace ttb

@@ -25,7 +25,7 @@ long long g_n[K_COUNT] = {0};
 const char *g_names[K_COUNT] = {"k_route_coop", "k_route_a", "k_route_b", "k_route_c",
                                 "k_fwd", "k_bwd", "k_seg", "k_cache_lookup",
                                 "k_yinit", "k_zero", "k_dmerge", "k_dsplit", "k_dapply",
-                                "k_dd_frag", "k_dd_gu"};
+                                "k_dd_frag", "k_dd_gu", "k_meta"};
 
 hipEvent_t take() {
   if (!g_pool.empty()) {

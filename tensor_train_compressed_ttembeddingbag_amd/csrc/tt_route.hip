@@ -752,6 +752,81 @@ hipError_t launch_wgrad_hits(const DevArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Metadata of every work item (WorkMeta), one wave per work item, after the final order
+// and the work items exist: the elements' bags and weights, the items (distinct indices,
+// found by wave ballots on i3 inside each pair) and the pairs (runs of equal (t, i1) in
+// the (t, i2, i1) order), and the per-M-block loop bounds of the contraction kernels.  It
+// also writes the links of the segment sums: the position of each (t,i1)- / (t,i3)-ordered
+// element's partial (its pair's / item's first element), or -1.  The contraction kernels
+// read the metadata in one round of loads instead of working it out themselves.  It runs
+// right after the grouping on the same stream, so a plan marked valid has its metadata.
+constexpr int META_WAVES = 4;
+__global__ __launch_bounds__(64 * META_WAVES) void k_meta(DevArgs a) {
+  __shared__ int s_m[META_WAVES][META_INTS];
+  __shared__ int s_cnt[META_WAVES][P_MAX + 8];  // gcnt [32] | mbf [8] as ints
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wi = blockIdx.x * META_WAVES + w;
+  const int plan = a.hdr[H_PLAN], nitems = a.hdr[H_NFWD];
+  if (plan != (int)a.plan_fp || wi >= nitems) return;  // (wave-uniform)
+  const int4 item = a.fitem[wi];
+  const int grp = item.x, s0 = item.y, n_el = item.z - item.y;
+  const int t = grp / a.p2;
+  const bool v = lane < n_el;
+  const int s = s0 + min(lane, n_el - 1);
+  const SPos sp = load_spos(a.srec, s);
+  const int dA = v ? sp.dA : -1, i3 = v ? sp.dI3 - t * a.p3 : 0;
+  const WaveItems r = wave_items(v, dA, i3, nbits_for(a.p3));
+  WorkMeta &M = *(WorkMeta *)s_m[w];
+  int *cnt = s_cnt[w];
+  for (int k = lane; k < META_INTS; k += 64) s_m[w][k] = 0;
+  if (lane < P_MAX + 8) cnt[lane] = 0;
+  wave_lds_sync();
+  if (v) {
+    a.link1[sp.posA] = r.pair_st ? s : -1;
+    a.link3[sp.posI3] = r.item_st ? s : -1;
+    M.e_perm[r.item_pos] = (unsigned char)lane;
+    M.e_it[lane] = (unsigned char)r.e_it;
+  }
+  if (lane < P_MAX) {
+    M.e_bag[lane] = sp.bag;
+    M.e_w[lane] = sp.w;
+  }
+  if (r.item_st) {
+    M.it_beg[r.it] = (unsigned char)r.it_beg;
+    M.it_first[r.it] = (unsigned char)lane;
+    M.it_i3[r.it] = (short)i3;
+    M.it_pair[r.it] = (unsigned char)r.pair_of;
+  }
+  if (r.pair_st) {
+    M.pr_it[r.pr] = (unsigned char)r.it;
+    M.pr_i1[r.pr] = (short)(dA - t * a.p1);
+    atomicAdd(&cnt[(r.pr * a.q1) >> 2], r.pair_items);       // rows of a lane group
+    atomicMax(&cnt[P_MAX + ((r.pr * a.q1) >> 4)], r.pair_items);  // rows of an M-block
+  }
+  if (lane == 0) {
+    const int nI = __popcll(r.mi), nP = __popcll(r.mp);
+    M.n_el = n_el; M.nI = nI; M.nP = nP; M.grp = grp; M.s0 = s0;
+    M.it_beg[nI] = (unsigned char)n_el;
+    M.pr_it[nP] = (unsigned char)nI;
+  }
+  wave_lds_sync();
+  if (lane < P_MAX) M.gcnt[lane] = (unsigned char)cnt[lane];
+  if (lane < 8) {
+    M.mbf[lane] = (unsigned char)cnt[P_MAX + lane];
+    M.mbb[lane] = (unsigned char)max(max(cnt[4 * lane], cnt[4 * lane + 1]),
+                                     max(cnt[4 * lane + 2], cnt[4 * lane + 3]));
+  }
+  wave_lds_sync();
+  int *dst = a.meta + (size_t)wi * META_INTS;
+  for (int k = lane; k < META_INTS; k += 64) dst[k] = s_m[w][k];
+}
+
+static hipError_t launch_meta(const DevArgs &a, hipStream_t s) {
+  const int nb = (items_max(a) + META_WAVES - 1) / META_WAVES;
+  tt_launch(K_META, k_meta, dim3(nb), dim3(64 * META_WAVES), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const DevArgs &a, hipStream_t s) {
   if (a.nblk == 0) return hipGetLastError();
   if (coop_route_ok(a)) {
@@ -766,13 +841,15 @@ hipError_t launch_route(const DevArgs &a, hipStream_t s) {
     // One block per CU at most (LDS), launched on an otherwise idle stream position:
     // every block is resident at once.  The barriers are bounded waits in any case.
     tt_launch(K_ROUTE_COOP, k_route_coop, dim3(a.nblk), dim3(CT), lds, s, a);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? launch_meta(a, s) : e;
   }
   const size_t bins_ia = (size_t)(a.binsI3 > a.binsA ? a.binsI3 : a.binsA);
   tt_launch(K_ROUTE_A, k_route_a, dim3(a.nblk), dim3(RT), (ROUTE_MAX_BAGS + bins_ia) * 4, s, a);
   tt_launch(K_ROUTE_B, k_route_b, dim3(a.nblk), dim3(RT), bins_ia * 8, s, a);
   tt_launch(K_ROUTE_C, k_route_c, dim3(a.nblk), dim3(RT), (size_t)a.binsB * 8, s, a);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? launch_meta(a, s) : e;
 }
 
 hipError_t launch_yinit(const DevArgs &a, hipStream_t s) {
