@@ -3,16 +3,19 @@ same object, so the launch configuration they check is the one the benchmark mea
 
 Every batch is grouped (tt_bag_plan, or tt_bag_plan_dedup for the backward over distinct
 indices), then runs the planned forward and the planned backward.  Pipelined (default):
-the grouping of batch i+1 is enqueued on a second stream right after the forward of batch i
-(after the backward with the distinct-index grouping, which waits on the host) and runs
-beside the backward; the host waits for a batch's grouping before it enqueues the batch's
-forward.  A grouping must not overwrite a workspace before the last step that used it has
-finished.  An event recorded on the main stream costs several microseconds of that stream's
-time, so it is recorded only after every DONE_EVERY-th step, DONE_EVERY + 1 workspaces
-rotate, and a grouping waits for the latest step with an event, which is at or after the last
-user of its workspace.  With a cache, the lookup of a batch runs on the grouping stream just
-before its grouping and writes that batch's slot buffer, last read two batches back, so
-there an event follows every step.  Argument marshalling only: every step runs in libttbag.
+the grouping of batch i+AHEAD is enqueued on a second stream right after the forward of
+batch i (after the backward with the distinct-index grouping, which waits on the host) and
+runs beside the backward; the host waits for a batch's grouping before it enqueues the
+batch's forward.  Two batches ahead (the plain path), a grouping has a whole step more to
+finish than the host needs to reach it, so the host does not wait on it; with a cache or
+the distinct-index grouping it is one batch ahead.  A grouping must not overwrite a
+workspace before the last step that used it has finished.  An event recorded on the main
+stream costs several microseconds of that stream's time, so it is recorded only after every
+DONE_EVERY-th step, AHEAD + DONE_EVERY workspaces rotate, and a grouping waits for the
+latest step with an event, which is at or after the last user of its workspace.  With a
+cache, the lookup of a batch runs on the grouping stream just before its grouping and
+writes that batch's slot buffer, last read two batches back, so there an event follows
+every step.  Argument marshalling only: every step runs in libttbag.
 """
 from __future__ import annotations
 
@@ -65,20 +68,24 @@ class TrainLoop:
             make_ws = lambda: abi.workspace_dedup(desc, max_nnz, num_bags)  # noqa: E731
         else:
             make_ws = lambda: abi.workspace(desc, max_nnz, num_bags, csize)  # noqa: E731
-        # done events after steps k with k % every == every - 1; workspace of step i:
-        # i % (every + 1), so the latest such k <= i - 2 is at or after i - every - 1
+        # done events after steps k with k % every == every - 1.  The grouping of batch j is
+        # enqueued during step j - ahead and waits for the latest such k <= j - ahead - 1,
+        # which is >= j - ahead - every; batch j's workspace j % (ahead + every) was last
+        # used by step j - ahead - every, so that event covers it.
         self.every = 1 if cache is not None else DONE_EVERY
-        self.wss = [make_ws() for _ in range(self.every + 1 if pipeline else 1)]
+        self.ahead = 2 if (pipeline and cache is None and not dedup) else 1
+        self.wss = [make_ws() for _ in range(self.ahead + self.every if pipeline else 1)]
         self.main = torch.cuda.current_stream()
         self.side = torch.cuda.Stream() if pipeline else self.main  # default priority
-        self.ev_plan = [torch.cuda.Event() for _ in range(2)]
+        self.ev_plan = [torch.cuda.Event() for _ in range(self.ahead + 1)]
         self.ev_done = {-1: torch.cuda.Event()}  # step -> event after its backward
         self.ev_done[-1].record(self.main)
         self.next = 0
         self.cvs = {}
         self.infos = {}
         if pipeline:
-            self.cvs[0] = self._plan(0)
+            for j in range(self.ahead):
+                self.cvs[j] = self._plan(j)
 
     def _plan(self, i: int):
         b = self.batches[i % len(self.batches)]
@@ -107,15 +114,15 @@ class TrainLoop:
                             b["per_sample_weights"], cache=cv, ws=ws, dev_status=self.status,
                             stream=self.side)
         if self.pipeline:
-            self.ev_plan[i % 2].record(self.side)
+            self.ev_plan[i % (self.ahead + 1)].record(self.side)
         return cv
 
     def done_step(self, i: int) -> int:
         """The step whose done event the grouping of batch i waits for: the latest step
-        k <= i - 2 with an event (-1 = before the first step).  Batch i's workspace was
-        last used by step i - every - 1, and k >= i - every - 1."""
+        k <= i - ahead - 1 with an event (-1 = before the first step).  Batch i's workspace
+        was last used by step i - ahead - every, and k >= i - ahead - every."""
         e = self.every
-        k = ((i - 2 + 1) // e) * e - 1
+        k = ((i - self.ahead) // e) * e - 1
         return max(k, -1)
 
     def step(self) -> int:
@@ -127,7 +134,7 @@ class TrainLoop:
             # the host waits for this batch's grouping (it ran beside the previous
             # backward and is normally long done) instead of the device: a cross-stream
             # wait on the device costs about 5 us per step even when the event is done
-            self.ev_plan[i % 2].synchronize()
+            self.ev_plan[i % (self.ahead + 1)].synchronize()
             cv = self.cvs.pop(i)
         else:
             cv = self._plan(i)
@@ -140,9 +147,8 @@ class TrainLoop:
                                cache=cv, out=self.out, ws=ws, dev_status=self.status,
                                planned=True)
         if self.pipeline and not self.dedup:
-            # the next grouping starts now, beside this batch's backward (with a cache its
-            # lookup and grouping take longer than the backward alone)
-            self.cvs[i + 1] = self._plan(i + 1)
+            # the grouping `ahead` batches on starts now, beside this batch's backward
+            self.cvs[i + self.ahead] = self._plan(i + self.ahead)
         if self.dcore:
             if self.update == "sgd":
                 abi.tt_bag_backward_sgd_d(self.desc, self.g, b["indices"], b["offsets"], self.B,

@@ -249,3 +249,22 @@ def test_binding_rejects_mis_sized_buffers_before_any_device_work(monkeypatch):
     with pytest.raises(ValueError):
         abi.tt_bag_forward_d(dd, [torch.zeros(n) for n in nd[:3]] + [torch.zeros(nd[3] + 1)],
                              idx, off, B, ws=ws)
+
+
+@pytest.mark.parametrize("ahead,every", [(1, 1), (1, 4), (2, 1), (2, 4), (2, 3)])
+def test_train_loop_grouping_waits_cover_workspace_reuse(ahead, every):
+    """The pipelined loop's reuse rule, brute force: the grouping of batch j (enqueued
+    during step j - ahead, into workspace j % (ahead + every)) waits for a step whose done
+    event has already been recorded by then (k <= j - ahead - 1, k one of the steps that
+    record one) and that is at or after the last step that used the same workspace."""
+    from tensor_train_compressed_ttembeddingbag_amd.loop import TrainLoop
+    L = object.__new__(TrainLoop)
+    L.ahead, L.every = ahead, every
+    W = ahead + every
+    for j in range(300):
+        k = L.done_step(j)
+        # the first `ahead` groupings are enqueued before step 0, behind the loop's first
+        # event (-1); every later one behind a recorded step
+        assert k == -1 or (k <= j - ahead - 1 and k % every == every - 1)
+        last_user = j - W  # the previous batch in workspace j % W
+        assert k >= last_user or last_user < 0

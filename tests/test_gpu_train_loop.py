@@ -283,16 +283,15 @@ def test_loop_update_modes_match_oracle(update, pipeline):
 
 @pytest.mark.parametrize("dedup", [False, True], ids=["plain", "dedup"])
 def test_loop_reuses_its_workspaces_over_many_steps(dedup):
-    """Eleven pipelined steps over three batches of different sizes, so that every one
+    """Fourteen pipelined steps over three batches of different sizes, so that every one
     of the loop's workspaces is reused (its done events follow only every few steps):
     every step's forward and core update against the oracle."""
     from tensor_train_compressed_ttembeddingbag_amd import loop as L
     print("case train loop reuse", dedup, flush=True)
     wl = W.custom("loop reuse", p=(12, 10, 14), q=(4, 4, 4), ranks=(16, 32), num_tables=2,
                   bags_per_table=48, lengths=("uniform", 0, 30), dist=("zipf", 1.2),
-                  init_std=1 / 32 ** 0.5, lr=0.002, weighted=True)  # stays bounded 11 steps
-    T, B, steps = wl.num_tables, wl.bags_per_table, 11
-    assert steps > 2 * (L.DONE_EVERY + 1)
+                  init_std=1 / 32 ** 0.5, lr=0.002, weighted=True)  # stays bounded 14 steps
+    T, B, steps = wl.num_tables, wl.bags_per_table, 14
     cores = W.make_cores(wl)
     g = gpu_cores(wl, cores)
     desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E, T)
@@ -302,7 +301,9 @@ def test_loop_reuses_its_workspaces_over_many_steps(dedup):
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     loop = TrainLoop(desc, g, [to_dev(b) for b in host_batches], B, wl.lr, out, status,
                      dedup=dedup)
-    assert len(loop.wss) == L.DONE_EVERY + 1
+    assert len(loop.wss) == loop.ahead + L.DONE_EVERY
+    assert loop.ahead == (1 if dedup else 2)
+    assert steps > 2 * len(loop.wss)
     snaps, ys = [[x.clone() for x in g]], []
     for _ in range(steps):
         loop.step()
