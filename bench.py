@@ -149,6 +149,7 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    loop.wait_s = 0.0
     t0 = time.perf_counter()
     done = [step(i) for i in range(args.steps)]
     t_enq = time.perf_counter()
@@ -188,6 +189,8 @@ def main():
                    "update": args.update + (" (backward over distinct indices)"
                                             if args.dedup else ""),
                    "host_enqueue_us_per_step": round((t_enq - t0) * 1e6 / args.steps, 2),
+                   # of which waiting for groupings (the rest is the host's own work)
+                   "host_wait_us_per_step": round(loop.wait_s * 1e6 / args.steps, 2),
                    "pipeline": "grouping of batch i+1 beside the backward of batch i; the "
                                "host waits for it before the forward of batch i+1"
                                if pipeline else "none"},

@@ -848,3 +848,101 @@ def tt_bag_backward_grad_d(desc: TTDescD, cores, indices, offsets, num_bags: int
                                       _ptr(dev_status), _stream(stream, indices))
     _check("tt_bag_backward_grad_d", rc)
     return grad_cores
+
+
+# ------------------------------------------------------------------ prepared calls
+# A training loop repeats the same calls with the same buffers: the checks and the
+# marshalling of a call can be done once, and the call then replayed with its ctypes
+# arguments as they are.  prepare_* validates exactly as the function of the same name
+# (without the "prepare_") and returns a zero-argument callable that enqueues the C call
+# again (on the same stream, with the same pointers: the buffers' contents may change
+# between replays, not their addresses or sizes) and raises TTError on a negative return.
+
+class Prepared:
+    __slots__ = ("fn", "args", "name", "keep")
+
+    def __init__(self, name, args, keep):
+        self.fn = getattr(lib(), name)
+        self.args, self.name, self.keep = args, name, keep
+
+    def __call__(self):
+        rc = self.fn(*self.args)
+        if rc:
+            raise TTError(self.name, rc)
+
+
+def _stream_handle(stream, like):
+    return _stream(stream, like)
+
+
+def prepare_plan(desc: TTDesc, indices, offsets, num_bags: int, per_sample_weights=None,
+                 cache=None, ws=None, dev_status=None, stream=None) -> Prepared:
+    _need(indices, torch.int64, "indices")
+    _need(offsets, torch.int64, "offsets")
+    if per_sample_weights is not None:
+        _need(per_sample_weights, torch.float32, "per_sample_weights")
+    _batch_sizes(desc, indices, offsets, num_bags, per_sample_weights)
+    view, _ = _cache_view(cache, desc, indices.numel())
+    _need(ws, torch.uint8, "ws")
+    if dev_status is not None:
+        _need(dev_status, torch.int32, "dev_status")
+    args = (ctypes.byref(desc), _ptr(indices), indices.numel(), _ptr(offsets), int(num_bags),
+            _ptr(per_sample_weights), None if view is None else ctypes.byref(view), _ptr(ws),
+            ws.numel(), _ptr(dev_status), _stream_handle(stream, indices))
+    return Prepared("tt_bag_plan", args, (desc, indices, offsets, per_sample_weights, cache, ws,
+                                          dev_status, view))
+
+
+def prepare_forward(desc: TTDesc, cores, indices, offsets, num_bags: int, per_sample_weights=None,
+                    cache=None, out=None, ws=None, dev_status=None, stream=None) -> Prepared:
+    """The planned forward (tt_bag_forward_planned) as a prepared call."""
+    _need(indices, torch.int64, "indices")
+    _need(offsets, torch.int64, "offsets")
+    if per_sample_weights is not None:
+        _need(per_sample_weights, torch.float32, "per_sample_weights")
+    _batch_sizes(desc, indices, offsets, num_bags, per_sample_weights)
+    _need(out, torch.float32, "out")
+    _numel(out, desc.num_tables * int(num_bags) * _dim(desc), "out")
+    view, _ = _cache_view(cache, desc, indices.numel())
+    _need(ws, torch.uint8, "ws")
+    if dev_status is not None:
+        _need(dev_status, torch.int32, "dev_status")
+    core_ptrs = _cores(cores, desc)
+    args = (ctypes.byref(desc), core_ptrs, _ptr(indices), indices.numel(), _ptr(offsets),
+            int(num_bags), _ptr(per_sample_weights), None if view is None else ctypes.byref(view),
+            _ptr(out), _ptr(ws), ws.numel(), _ptr(dev_status), _stream_handle(stream, indices))
+    return Prepared("tt_bag_forward_planned", args, (desc, core_ptrs, cores, indices, offsets,
+                                                     per_sample_weights, cache, out, ws,
+                                                     dev_status, view))
+
+
+def prepare_backward(desc: TTDesc, cores, indices, offsets, num_bags: int, grad_out,
+                     update: str = "sgd", lr: float = 0.0, eps: float = 0.0, aux=None,
+                     aux_rows=None, per_sample_weights=None, cache=None, ws=None,
+                     dev_status=None, stream=None) -> Prepared:
+    """The planned backward as a prepared call: update "sgd" (tt_bag_backward_sgd_planned),
+    "adagrad" (aux / aux_rows = running sums) or "grad" (aux / aux_rows = gradient outputs)."""
+    view, csize, ws = _batch_args(desc, indices, offsets, num_bags, grad_out, per_sample_weights,
+                                  cache, ws, dev_status)
+    core_ptrs = _cores(cores, desc)
+    head = (ctypes.byref(desc), core_ptrs, _ptr(indices), indices.numel(), _ptr(offsets),
+            int(num_bags), _ptr(per_sample_weights), None if view is None else ctypes.byref(view),
+            _ptr(grad_out))
+    tail = (_ptr(ws), ws.numel(), _ptr(dev_status), _stream_handle(stream, indices))
+    keep = [desc, core_ptrs, cores, indices, offsets, per_sample_weights, cache, grad_out, ws,
+            dev_status, view]
+    if update == "sgd":
+        name, mid = "tt_bag_backward_sgd_planned", (float(lr),)
+    elif update == "adagrad":
+        st = _cores(aux, desc, "state")
+        sr = _rows_arg(aux_rows, csize, "state_rows", _dim(desc))
+        name, mid = "tt_bag_backward_adagrad_planned", (float(lr), float(eps), st, _ptr(sr))
+        keep += [st, aux, sr]
+    elif update == "grad":
+        gp = _cores(aux, desc, "grad_cores")
+        gr = _rows_arg(aux_rows, csize, "grad_rows", _dim(desc))
+        name, mid = "tt_bag_backward_grad_planned", (gp, _ptr(gr))
+        keep += [gp, aux, gr]
+    else:
+        raise ValueError("update must be sgd, adagrad or grad")
+    return Prepared(name, head + mid + tail, keep)

@@ -19,6 +19,7 @@ every step.  Argument marshalling only: every step runs in libttbag.
 """
 from __future__ import annotations
 
+import time
 from typing import List
 
 import torch
@@ -83,6 +84,11 @@ class TrainLoop:
         self.next = 0
         self.cvs = {}
         self.infos = {}
+        # three-core calls of the plain path are checked and marshalled once per (batch,
+        # workspace) and then replayed (abi.prepare_*): the host work per step is the C calls
+        self.fast = not self.dcore and not dedup
+        self.prepared = {}
+        self.wait_s = 0.0  # host time spent waiting for groupings
         if pipeline:
             for j in range(self.ahead):
                 self.cvs[j] = self._plan(j)
@@ -110,12 +116,39 @@ class TrainLoop:
                                                      b["per_sample_weights"], ws=ws,
                                                      dev_status=self.status, stream=self.side)
         else:
-            abi.tt_bag_plan(self.desc, b["indices"], b["offsets"], self.B,
-                            b["per_sample_weights"], cache=cv, ws=ws, dev_status=self.status,
-                            stream=self.side)
+            key = ("plan", i % len(self.batches), i % len(self.wss))
+            call = self.prepared.get(key)
+            if call is None:
+                call = self.prepared[key] = abi.prepare_plan(
+                    self.desc, b["indices"], b["offsets"], self.B, b["per_sample_weights"],
+                    cache=cv, ws=ws, dev_status=self.status, stream=self.side)
+            call()
         if self.pipeline:
             self.ev_plan[i % (self.ahead + 1)].record(self.side)
         return cv
+
+    def _fast_step(self, i, b, ws, cv):
+        """Planned forward, the grouping `ahead` batches on, planned backward: prepared calls."""
+        bi, wi = i % len(self.batches), i % len(self.wss)
+        fwd = self.prepared.get(("fwd", bi, wi))
+        if fwd is None:
+            w = b["per_sample_weights"]
+            fwd = self.prepared[("fwd", bi, wi)] = abi.prepare_forward(
+                self.desc, self.g, b["indices"], b["offsets"], self.B, w, cache=cv,
+                out=self.out, ws=ws, dev_status=self.status, stream=self.main)
+            eps = 1e-10 if self.update == "adagrad" else 0.0
+            self.prepared[("bwd", bi, wi)] = abi.prepare_backward(
+                self.desc, self.g, b["indices"], b["offsets"], self.B, b["grad_out"],
+                update=self.update, lr=self.lr, eps=eps, aux=self.aux, aux_rows=self.aux_rows,
+                per_sample_weights=w, cache=cv, ws=ws, dev_status=self.status, stream=self.main)
+        fwd()
+        if self.pipeline:
+            self.cvs[i + self.ahead] = self._plan(i + self.ahead)
+        self.prepared[("bwd", bi, wi)]()
+        if self.pipeline and i % self.every == self.every - 1:
+            ev = torch.cuda.Event()
+            ev.record(self.main)
+            self.ev_done[i] = ev
 
     def done_step(self, i: int) -> int:
         """The step whose done event the grouping of batch i waits for: the latest step
@@ -134,11 +167,16 @@ class TrainLoop:
             # the host waits for this batch's grouping (it ran beside the previous
             # backward and is normally long done) instead of the device: a cross-stream
             # wait on the device costs about 5 us per step even when the event is done
+            t = time.perf_counter()
             self.ev_plan[i % (self.ahead + 1)].synchronize()
+            self.wait_s += time.perf_counter() - t
             cv = self.cvs.pop(i)
         else:
             cv = self._plan(i)
         w = b["per_sample_weights"]
+        if self.fast:
+            self._fast_step(i, b, ws, cv)
+            return i
         if self.dcore:
             abi.tt_bag_forward_d(self.desc, self.g, b["indices"], b["offsets"], self.B, w,
                                  out=self.out, ws=ws, dev_status=self.status, planned=True)
