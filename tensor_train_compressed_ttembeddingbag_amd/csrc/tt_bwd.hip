@@ -103,7 +103,7 @@ void k_bwd(DevArgs a) {
   __shared__ int s_pl[NW];
   if (tid < META_INTS) s_meta[tid] = a.meta[(size_t)wi * META_INTS + tid];
   note_placement(s_pl);
-  __syncthreads();
+  lds_barrier();
   if (plan != (int)a.plan_fp || wi >= nitems) return;
   const int grp = M.grp, s0 = M.s0, n_el = M.n_el, nI = M.nI, nP = M.nP;
   const int t = grp / a.p2;
@@ -112,7 +112,7 @@ void k_bwd(DevArgs a) {
   const float *G2g = a.G2 + (size_t)grp * slice2;
   const float *G1t = a.G1 + (size_t)t * a.p1 * W1;
   const float *G3t = a.G3 + (size_t)t * a.p3 * W3;
-  float *part2 = a.part2 + (size_t)wi * slice2;
+  float *part2 = a.part2 + (size_t)M.item * slice2;  // keyed by the item, not the slot
 
   // G2 columns [j0, j0 + nj) -> LDS as G2^T blocks, STAGE_U loads per thread per batch
   auto load2 = [&](int j0, int nj, int base, float *v) {
@@ -316,7 +316,8 @@ void k_bwd(DevArgs a) {
       }
     }
   }
-  __syncthreads();
+  vmem_drain();
+  lds_barrier();
   // G_u of every item: its elements' w * dY rows summed in position order
   for (int i = tid; i < nI * D; i += WG) {
     const int it = fdiv(i, a.mD), d = i - it * D;
@@ -324,7 +325,7 @@ void k_bwd(DevArgs a) {
     for (int k = M.it_beg[it]; k < M.it_beg[it + 1]; ++k) acc += sYe[(size_t)M.e_perm[k] * D + d];
     sGu[i] = acc;
   }
-  __syncthreads();
+  lds_barrier();
 
   f4 dA1[NM];  // dG1^T[r1 = 16mr + 4g + v][row = c]
 #pragma unroll
@@ -340,29 +341,37 @@ void k_bwd(DevArgs a) {
 
   for (int j0 = 0; j0 < q2; j0 += JB) {
     if (j0 > 0) {  // next G2 stage (only when the slice does not fit at once)
-      __syncthreads();
+      lds_barrier();
       stage_g2(j0, min(JB, q2 - j0), tid);
-      __syncthreads();
+      vmem_drain();
+      lds_barrier();
     }
     const int jend = min(q2, j0 + JB);
+    // stage 1 of column j2: T[row = 16mb + 4g + v][r2 = 16m + c] (the first product starts
+    // from 0).  It runs one column ahead: the products of column j2 + 1 are issued before
+    // the reduction of column j2, so the matrix cores work through its barriers.
+    auto stage1 = [&](int j2, f4 *T) {
+      const float *bufj = sG2 + (size_t)(j2 - j0) * RP * LD;
+#pragma unroll
+      for (int kq = 0; kq < KS / 4; ++kq)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          const float4 bv = *(const float4 *)&bufj[(16 * m + c) * LD + g * KS + 4 * kq];
+          T[m] = mfma4(aT[4 * kq + 0], bv.x, kq == 0 ? zero4() : T[m]);
+          T[m] = mfma4(aT[4 * kq + 1], bv.y, T[m]);
+          T[m] = mfma4(aT[4 * kq + 2], bv.z, T[m]);
+          T[m] = mfma4(aT[4 * kq + 3], bv.w, T[m]);
+        }
+    };
+    f4 Tn[NM];
+    if (mb < nmb) stage1(j0, Tn);
     for (int j2 = j0; j2 < jend; ++j2) {
       const float *buf = sG2 + (size_t)(j2 - j0) * RP * LD;
       f4 gacc[NM][NM];  // dG2[r1 = 16mr + 4g + v][r2 = 16m2 + c]
       if (mb < nmb) {
-        // stage 1: T[row = 16mb + 4g + v][r2 = 16m + c] (the first product starts from 0)
         f4 T[NM], dT[NM];
 #pragma unroll
-        for (int kq = 0; kq < KS / 4; ++kq)
-#pragma unroll
-          for (int m = 0; m < NM; ++m) {
-            const float4 bv = *(const float4 *)&buf[(16 * m + c) * LD + g * KS + 4 * kq];
-            T[m] = mfma4(aT[4 * kq + 0], bv.x, kq == 0 ? zero4() : T[m]);
-            T[m] = mfma4(aT[4 * kq + 1], bv.y, T[m]);
-            T[m] = mfma4(aT[4 * kq + 2], bv.z, T[m]);
-            T[m] = mfma4(aT[4 * kq + 3], bv.w, T[m]);
-          }
-#pragma unroll
-        for (int m = 0; m < NM; ++m) dT[m] = zero4();
+        for (int m = 0; m < NM; ++m) { T[m] = Tn[m]; dT[m] = zero4(); }
         // the items of the pairs owning the lane group's rows
         if (F44) {
           // q1 = q3 = 4: a lane group's four rows are one pair (j1 = v); each lane group
@@ -476,6 +485,7 @@ void k_bwd(DevArgs a) {
             dA1[mr] = mfma4(buf[(16 * m + 4 * g + 3) * LD + 16 * mr + c], bT.w, dA1[mr]);
           }
         }
+        if (j2 + 1 < jend) stage1(j2 + 1, Tn);
       } else {
 #pragma unroll
         for (int mr = 0; mr < NM; ++mr)
@@ -487,7 +497,7 @@ void k_bwd(DevArgs a) {
       // mb % nred in round mb / nred, then the slots are summed in slot order.  A slot holds
       // [r2][r1] (row pitch LD), so a lane's four r1 = 16mr + 4g .. +3 of one r2 move as
       // one 16-byte vector.
-      __syncthreads();  // the transpose tiles (aliased by the slots) are free
+      lds_barrier();  // the transpose tiles (aliased by the slots) are free
       for (int rr = 0; rr < NW / nred; ++rr) {
         if (mb / nred == rr) {
           float *slot = sRed + (size_t)(mb % nred) * RP * LD;
@@ -505,7 +515,7 @@ void k_bwd(DevArgs a) {
               *q = x;
             }
         }
-        __syncthreads();
+        lds_barrier();
       }
       // thread t: r2 = t mod RP, r1 = 4 (t / RP) .. +3, summed over the slots in order; the
       // partial keeps the slice layout [r1][j2][r2] (consecutive threads, consecutive r2)
@@ -525,7 +535,7 @@ void k_bwd(DevArgs a) {
           if (r1 + 3 < R1) dst[3 * st] = acc.w;
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
   // dG1 partial per pair, dG3 partial per item, at their first positions

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
     if (stale && wi == 0 && tid == 0) set_status(a.status, DEV_STALE_PLAN);
     return;
   }
-  __syncthreads();
+  lds_barrier();
   const int grp = M.grp, n_el = M.n_el, nI = M.nI, nP = M.nP;
   const int wp = placed_mblock<NW>(s_pl);  // this wave's M-block (MBW = 1)
   const int t = grp / a.p2;
@@ -268,15 +268,17 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
       bv[mbi][ks] = (ok && g * KS + ks < R1) ? v : 0.f;
     }
   }
+  vmem_drain();
   if (clearer) fwd_raise_flag(a);  // (includes the barrier)
-  else __syncthreads();
+  else lds_barrier();
 
   if (a.fzero && !SW) fwd_wait_out(a);  // stage 2 adds into out directly
   for (int j0 = 0; j0 < q2; j0 += JB) {
     if (j0 > 0) {  // next G2 stage (only when the slice does not fit at once)
-      __syncthreads();
+      lds_barrier();
       stage_g2(j0, min(JB, q2 - j0), tid);
-      __syncthreads();
+      vmem_drain();
+      lds_barrier();
     }
     const int jend = min(q2, j0 + JB);
     for (int j2 = j0; j2 < jend; ++j2) {
@@ -378,7 +380,7 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
     }
   }
   if (DOT) {  // dL/dw per element: one wave per element, row . grad_out[bag]
-    __syncthreads();
+    lds_barrier();
     for (int e = w; e < n_el; e += NW) {
       const int it = M.e_it[e], b = M.e_bag[e];
       float acc = 0.f;
@@ -399,7 +401,7 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
   if (!SW) return;
   // pooling: out[bag] += w * W[item], one row-contiguous pass per element
   if (a.fzero) fwd_wait_out(a);  // (includes the barrier)
-  else __syncthreads();
+  else lds_barrier();
   for (int e = w; e < n_el; e += NW) {
     const int it = M.e_it[e];
     float *yrow = a.Y + (size_t)M.e_bag[e] * D;

@@ -46,6 +46,7 @@ enum {
   H_HIT_BEG = 4, H_HIT_END = 5,  // hit region [beg, end) of the final order
   H_VALID = 6,      // number of valid (non-skipped) elements
   H_PLAN = 7,       // fingerprint of the call that made the grouping (tt_bag_plan)
+  H_SIZE0 = 16,     // [P_MAX + 1] work items handed a place so far, per size
   H_WORDS = 64
 };
 
@@ -56,7 +57,9 @@ enum {
 // fit a byte (P <= 32 positions); i1 and i3 (< 8192) fit a short.
 constexpr int META_INTS = 192;  // 768 bytes per work item
 struct WorkMeta {
-  int n_el, nI, nP, grp, s0, pad[3];
+  int n_el, nI, nP, grp, s0;
+  int item;                         // the work item's index (its slot is its workgroup)
+  int pad[2];
   int e_bag[P_MAX];                 // bag of each element
   float e_w[P_MAX];                 // its weight (times 1 / length with mean pooling)
   short pr_i1[P_MAX];               // i1 of each pair (inside its table)
@@ -72,6 +75,7 @@ struct WorkMeta {
   unsigned char mbb[8];             // M-block -> most gcnt of its four lane groups
 };
 static_assert(sizeof(WorkMeta) <= META_INTS * 4, "work-item metadata too large");
+static_assert(H_SIZE0 + P_MAX + 1 <= H_WORDS, "header words");
 
 struct DevArgs {
   // shape
@@ -92,6 +96,7 @@ struct DevArgs {
   double rp23, rp3; // 1 / (p2 * p3), 1 / p3 (row split)
   int fwd_sw;       // forward: 1 = rows of a work item kept in LDS and pooled at the end
   unsigned plan_fp;  // fingerprint of (shape, sizes, input pointers) of the plan
+  int ncu;           // compute units of the device (0: unknown), for the item placement
   // inputs / outputs
   const int64_t *idx;
   const int64_t *off;
@@ -122,7 +127,7 @@ struct DevArgs {
   int *segI3, *segA;  // first position of each (t,i3) / (t,i1) bin in orderI3 / orderA
   int4 *srec;       // final order, 2 int4 per position: (element n, dA, dB, dI3),
                     // (bag, position in orderI3, weight bits, position in orderA)
-  int4 *fitem;      // work items: (group, first position, end position, 0)
+  int4 *fitem;      // work items: (group, first position, end position, workgroup slot)
   int *meta;        // [items][META_INTS] work-item metadata (WorkMeta)
   int *grp_off;     // [binsB + 1]
   int *chunk_pre;   // [T*p2 + 1]

@@ -52,6 +52,24 @@ __device__ __forceinline__ float keep(float v) {
   return v;
 }
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also makes the
+// wave's global stores visible to the workgroup, which on this hardware means waiting for
+// every store in flight to complete (a memory round trip per barrier); the contraction
+// kernels' barriers guard LDS data alone, so they wait for LDS operations only and leave
+// their global stores (partial sums read by a later kernel) in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Wait for every vector-memory operation of the wave (s_waitcnt vmcnt(0), the other
+// counters left alone).  Staging loops whose LDS stores sit in divergent branches leave the
+// compiler unsure whether their loads are done, so it puts a vmcnt(0) wait into the next
+// loop that reuses those registers; that wait then also stalls on the loop's own global
+// stores on every pass.  One wait after staging settles it once.
+__device__ __forceinline__ void vmem_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // LDS ordering between lanes of one wave (write by one lane, read by another).
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");

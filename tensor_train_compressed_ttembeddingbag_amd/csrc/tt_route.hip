@@ -250,6 +250,21 @@ static __device__ void tile_place(const int d[RB / NT], int pos[RB / NT], unsign
   for (int r = 0; r < RB / NT; ++r) pos[r] = d[r] >= 0 ? start[(size_t)d[r] * ss + so] + rk[r] : -1;
 }
 
+// Workgroup slot of the j-th largest of n work items (the contraction kernels run work
+// item k in the workgroup of slot k).  The dispatcher hands out workgroups round-robin
+// over the XCDs and their CUs, so with C CUs, workgroups w and w + C share a CU when a
+// launch has between C and 2C of them.  Then the 2C - n largest items get a CU of their
+// own and the others share one in pairs, the largest with the smallest, so that the CUs
+// finish at about the same time; with n <= C or n > 2C the largest go first.  Only the
+// placement depends on this: every result is keyed by the item, not by its slot.
+__device__ __forceinline__ int item_slot(int j, int n, int C) {
+  if (C <= 0 || n <= C || n > 2 * C) return j;
+  const int pairs = n - C, alone = C - pairs;
+  if (j < alone) return pairs + j;
+  const int k = j - alone;
+  return k < pairs ? k : C + (2 * pairs - 1 - k);
+}
+
 // Work items from the group table gs[0..binsB] (starts of the (t,i2) bins in the final
 // order, gs[binsB] = nnz; LDS or global): a miss group of m elements becomes ceil(m / P)
 // items of near-equal size (at most P positions each), numbered group by group; also
@@ -275,6 +290,29 @@ static __device__ void build_items(const DevArgs &a, const int *gs, int *cnt, in
   }
   __threadfence_block();
   __syncthreads();
+  // items per size (a group of m elements in nc items has m mod nc items of size
+  // m / nc + 1, the rest of size m / nc), then the number of items larger than each size
+  __shared__ int s_above[P_MAX + 2];
+  for (int k = tid; k < P_MAX + 2; k += nt) s_above[k] = 0;
+  __syncthreads();
+  for (int g = tid; g < G; g += nt) {
+    const int nc = cnt[g + 1] - cnt[g], m = gs[g + 1] - gs[g];
+    if (nc == 0) continue;
+    const int q = m / nc, r = m - q * nc;
+    if (r) atomicAdd(&s_above[q + 1], r);
+    if (nc > r) atomicAdd(&s_above[q], nc - r);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int k = P_MAX + 1; k >= 0; --k) {
+      const int c = s_above[k];
+      s_above[k] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  const int nitems = cnt[G];
   for (int b = part + tid * nparts; b <= a.binsB; b += nt * nparts) a.grp_off[b] = gs[b];
   for (int g = part + tid * nparts; g <= G; g += nt * nparts) a.chunk_pre[g] = cnt[g];
   for (int g = part + tid * nparts; g < G; g += nt * nparts) {
@@ -290,7 +328,9 @@ static __device__ void build_items(const DevArgs &a, const int *gs, int *cnt, in
     int lo = gb;
     for (int c = 0; c < nc; ++c) {
       const int hi = c + 1 < nc ? cut(c + 1) : gb + m;
-      a.fitem[first + c] = make_int4(g, lo, hi, 0);
+      // its rank among the items of its size (any order: only the placement uses it)
+      const int j = s_above[hi - lo] + atomicAdd(&a.hdr[H_SIZE0 + hi - lo], 1);
+      a.fitem[first + c] = make_int4(g, lo, hi, item_slot(j, nitems, a.ncu));
       lo = hi;
     }
   }
@@ -520,6 +560,8 @@ __global__ __launch_bounds__(CT) void k_route_coop(DevArgs a) {
 
   // ---- histB cleared for the atomics; decode; (t,i3) and (t,i1) histograms of the tile
   for (int k = blk * CT + tid; k < a.binsB * nblk; k += nblk * CT) st_w<true>(a.histB + k, 0);
+  if (blk == 0)
+    for (int k = tid; k <= P_MAX; k += CT) st_w<true>(a.hdr + H_SIZE0 + k, 0);
   tile_decode<CT>(a, blk, lds_i, s_red, s_b, el);
   check_offsets<CT>(a, blk);
   {
@@ -636,7 +678,8 @@ __global__ __launch_bounds__(RT) void k_route_b(DevArgs a) {
   block_exclusive_scan(a.histB, a.binsB * a.nblk, s_scan);
   for (int d = threadIdx.x; d < a.binsB; d += RT) a.grp_off[d] = a.histB[(size_t)d * a.nblk];
   if (threadIdx.x == 0) a.grp_off[a.binsB] = a.nnz;
-  __threadfence_block();
+  for (int k = threadIdx.x; k <= P_MAX; k += RT) a.hdr[H_SIZE0 + k] = 0;
+  __threadfence();
   __syncthreads();
   build_items(a, a.grp_off, a.chunk_pre, s_scan, 0, 1);
 }
@@ -758,8 +801,9 @@ hipError_t launch_wgrad_hits(const DevArgs &a, hipStream_t s) {
 // the (t, i2, i1) order), and the per-M-block loop bounds of the contraction kernels.  It
 // also writes the links of the segment sums: the position of each (t,i1)- / (t,i3)-ordered
 // element's partial (its pair's / item's first element), or -1.  The contraction kernels
-// read the metadata in one round of loads instead of working it out themselves.  It runs
-// right after the grouping on the same stream, so a plan marked valid has its metadata.
+// read the metadata in one round of loads instead of working it out themselves, from the
+// workgroup slot the grouping gave the item.  It runs right after the grouping on the
+// same stream, so a plan marked valid has its metadata.
 constexpr int META_WAVES = 4;
 __global__ __launch_bounds__(64 * META_WAVES) void k_meta(DevArgs a) {
   __shared__ int s_m[META_WAVES][META_INTS];
@@ -805,7 +849,7 @@ __global__ __launch_bounds__(64 * META_WAVES) void k_meta(DevArgs a) {
   }
   if (lane == 0) {
     const int nI = __popcll(r.mi), nP = __popcll(r.mp);
-    M.n_el = n_el; M.nI = nI; M.nP = nP; M.grp = grp; M.s0 = s0;
+    M.n_el = n_el; M.nI = nI; M.nP = nP; M.grp = grp; M.s0 = s0; M.item = wi;
     M.it_beg[nI] = (unsigned char)n_el;
     M.pr_it[nP] = (unsigned char)nI;
   }
@@ -817,7 +861,8 @@ __global__ __launch_bounds__(64 * META_WAVES) void k_meta(DevArgs a) {
                                      max(cnt[4 * lane + 2], cnt[4 * lane + 3]));
   }
   wave_lds_sync();
-  int *dst = a.meta + (size_t)wi * META_INTS;
+  if ((unsigned)item.w >= (unsigned)nitems) return;  // (the slots are a permutation)
+  int *dst = a.meta + (size_t)item.w * META_INTS;     // the item's workgroup slot
   for (int k = lane; k < META_INTS; k += 64) dst[k] = s_m[w][k];
 }
 
@@ -827,7 +872,9 @@ static hipError_t launch_meta(const DevArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_route(const DevArgs &a, hipStream_t s) {
+hipError_t launch_route(const DevArgs &args, hipStream_t s) {
+  DevArgs a = args;
+  a.ncu = device_cus();
   if (a.nblk == 0) return hipGetLastError();
   if (coop_route_ok(a)) {
     static size_t attr_lds = 64 * 1024;  // dynamic LDS above 64 KiB is opt-in per kernel
