@@ -416,48 +416,95 @@ def run_dcore(args, wl, cores, torch, abi, metrics, W):
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(wl, cores, budget_s):
-    """The oracle, as it stands, on a prefix of the bags of batch 0 of the same
-    workload: the prefix doubles until one fwd+bwd run takes >= budget/8 (or covers
-    the batch), then runs repeat until the budget is spent.  Single-threaded C.  With
-    several tables the prefix is taken from table 0 (bags are table-major), run as a
-    one-table batch with that table's cores."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def _host_threads():
+    """Cores this process may run on (its affinity mask), capped by OMP_NUM_THREADS when
+    the environment sets it (a shared host hands each job a share of its CPUs)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
+
+
+def cpu_baseline(wl, cores, budget_s, reps=5):
+    """The oracle, as it stands (single-threaded fp64 C, untouched), on the host's cores:
+    fwd+bwd of a prefix of the bags of a batch of the same workload, sized so that one run
+    takes about budget / (4 reps) on one core.  One core: reps runs on batch 0's prefix,
+    median.  All cores (cores = the threads this process may use): each run gives every
+    core its own batch's prefix (batches 0 .. cores-1, disjoint bags of the same
+    workload) in its own thread, all at once (the oracle's C calls release the GIL), and
+    takes the wall time; median of reps runs.  Value = time per nnz of the whole run.
+    With several tables the prefix is taken from table 0 (bags are table-major), run as
+    a one-table batch with that table's cores."""
     import oracle
+    from concurrent.futures import ThreadPoolExecutor
     from tensor_train_compressed_ttembeddingbag_amd import workloads as W
     oracle.build()
-    b = W.make_batch(wl, 0)
-    off = b["offsets"]
-    all_bags = wl.bags_per_table  # table 0's bags
+    fwd, bwd = ((oracle.forward, oracle.backward) if len(wl.p) == 3
+                else (oracle.forward_d, oracle.backward_d))
     cores = cores[:1]
-    bags, t_used, nnz_done, runs, sized = min(16, all_bags), 0.0, 0, 0, False
-    while True:
+    all_bags = wl.bags_per_table  # table 0's bags
+
+    def run(b, bags):
+        off = b["offsets"]
         n = int(off[bags])
         psw = None if b["per_sample_weights"] is None else b["per_sample_weights"][:n]
-        t0 = time.perf_counter()
-        fwd, bwd = ((oracle.forward, oracle.backward) if len(wl.p) == 3
-                    else (oracle.forward_d, oracle.backward_d))
         fwd(wl.p, wl.q, wl.ranks, wl.E, cores, b["indices"][:n], off[:bags + 1], bags, psw)
         bwd(wl.p, wl.q, wl.ranks, wl.E, cores, b["indices"][:n], off[:bags + 1], bags,
             b["grad_out"][:bags], psw)
+        return n
+
+    b0 = W.make_batch(wl, 0)
+    bags = min(16, all_bags)
+    while True:  # size the prefix: one run >= budget / (4 reps), or the whole table
+        t0 = time.perf_counter()
+        run(b0, bags)
         dt = time.perf_counter() - t0
-        t_used += dt
-        nnz_done += n
-        runs += 1
-        if not sized:
-            if dt >= budget_s / 8 or bags == all_bags:
-                sized = True
-            else:
-                bags = min(all_bags, bags * 2)
-        if sized and t_used >= budget_s:
+        if dt >= budget_s / (4 * reps) or bags == all_bags:
             break
-    return {"value": round(t_used * 1e6 / nnz_done, 3), "unit": "us/nnz", "cores": 1,
-            "kind": "oracle",
-            "sample": "%d fwd+bwd runs over prefixes of batch 0 (final prefix %d of %d bags%s, "
-                      "%d nnz in total, %.1f s), fp64 C oracle, one thread; host %s, %d CPUs"
-                      % (runs, bags, all_bags,
+        bags = min(all_bags, bags * 2)
+    one = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        n = run(b0, bags)
+        one.append((time.perf_counter() - t0) * 1e6 / n)
+    nt = _host_threads()
+    batches = [b0] + [W.make_batch(wl, k) for k in range(1, nt)]
+    allc = []
+    with ThreadPoolExecutor(max_workers=nt) as ex:
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            nn = sum(ex.map(lambda b: run(b, bags), batches))
+            allc.append((time.perf_counter() - t0) * 1e6 / nn)
+    med1, medn = float(np.median(one)), float(np.median(allc))
+    return {"value": round(medn, 4), "unit": "us/nnz", "cores": nt, "kind": "oracle",
+            "value_1core": round(med1, 3), "cores_1core": 1,
+            "runs_us_per_nnz": {"1": [round(x, 3) for x in one],
+                                str(nt): [round(x, 4) for x in allc]},
+            "cpu_model": _cpu_model(),
+            "sample": "fwd+bwd of the first %d of %d bags%s of a batch (%d nnz): one core, "
+                      "batch 0, median of %d runs; %d cores, batches 0..%d one per thread "
+                      "at once (the oracle's C calls release the GIL), wall time per nnz, "
+                      "median of %d runs; fp64 C oracle unchanged; host: %s, %d CPUs "
+                      "visible, %d usable"
+                      % (bags, all_bags,
                          " of table 0 of %d" % wl.num_tables if wl.num_tables > 1 else "",
-                         nnz_done, t_used,
-                         platform.processor() or platform.machine(), os.cpu_count() or 0)}
+                         int(b0["offsets"][bags]), reps, nt, nt - 1, reps, _cpu_model(),
+                         os.cpu_count() or 0, nt)}
 
 
 if __name__ == "__main__":
