@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-pipeline", action="store_true",
                     help="group each batch right before its forward (no overlap with the "
                          "previous backward)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay one captured HIP graph per step (plain pipelined path) "
+                         "instead of enqueuing each step's calls from the host")
     ap.add_argument("--cache-policy", default="topk", choices=["topk", "lfu32"],
                     help="cached workload: exact top-K or 32-way set-associative LFU")
     ap.add_argument("--update", default="sgd", choices=["sgd", "adagrad", "grad"],
@@ -139,12 +142,23 @@ def main():
         sys.exit(2)
     out = torch.empty(wl.num_tables * B, wl.D, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    # --graph: the plain pipelined path replays one captured HIP graph per step
+    use_graph = args.graph and pipeline and cache is None and not args.dedup
     loop = TrainLoop(desc, g, batches, B, wl.lr, out, status, update=args.update, aux=aux,
                      aux_rows=aux_rows, cache=cache, rows=rows, slots=slots, dedup=args.dedup,
-                     pipeline=pipeline)
+                     pipeline=pipeline, graph=use_graph)
 
     def step(_):
         return loop.step()
+
+    def make_eager_step():
+        """Per-kernel timing needs the library's own launches (a replayed graph records no
+        per-kernel events): the same steps enqueued from the host, on a loop of its own."""
+        if not use_graph:
+            return step
+        le = TrainLoop(desc, g, batches, B, wl.lr, out, status, update=args.update, aux=aux,
+                       aux_rows=aux_rows, pipeline=pipeline)
+        return lambda _: le.step()
 
     for i in range(args.warmup):
         step(i)
@@ -191,9 +205,11 @@ def main():
                    "host_enqueue_us_per_step": round((t_enq - t0) * 1e6 / args.steps, 2),
                    # of which waiting for groupings (the rest is the host's own work)
                    "host_wait_us_per_step": round(loop.wait_s * 1e6 / args.steps, 2),
-                   "pipeline": "grouping of batch i+1 beside the backward of batch i; the "
-                               "host waits for it before the forward of batch i+1"
-                               if pipeline else "none"},
+                   "pipeline": ("grouping of batch i+%d beside the backward of batch i"
+                                % loop.ahead) if pipeline else "none",
+                   "graph": ("one captured HIP graph per step (%d graphs, one per (batch, "
+                             "workspace) pair), replayed" % len(loop.graphs))
+                            if use_graph else "none"},
     }
     # gradient with respect to the per-sample weights of one planned batch (off the
     # default training step)
@@ -251,8 +267,12 @@ def main():
 
     res["config"]["step_us_percentiles"] = step_percentiles(step, min(args.steps, 400), torch)
     if not args.no_roofline:
-        res["roofline"], res["kernels"] = roofline(args, wl, batches, step, torch, abi, metrics,
-                                                   None if cache is None else slots)
+        res["roofline"], res["kernels"] = roofline(args, wl, batches, make_eager_step(), torch,
+                                                   abi, metrics, None if cache is None else slots)
+        if use_graph:
+            res["roofline"]["kernel_timing"] = ("HIP events of the library's launches in a "
+                                                "window of the same steps enqueued eagerly "
+                                                "(the timed steps replay graphs)")
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(wl, cores, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -20,9 +20,15 @@
  *  - Pointers are DEVICE pointers unless the comment says host.  `stream` is a
  *    hipStream_t (NULL = the default stream).  Every call is asynchronous on
  *    `stream` and does not synchronise the host, except tt_cache_populate and
- *    tt_bag_plan_dedup (which read a size back).  Calls must not be captured
- *    into a HIP graph: each launch carries a per-call tag for its grid-wide
- *    flags and counters, and a replayed graph would repeat it.
+ *    tt_bag_plan_dedup (which read a size back).
+ *  - HIP graphs: the calls that enqueue kernels only (the grouping, forward and
+ *    backward calls, planned or not, tt_cache_lookup) may be captured into a HIP
+ *    graph and replayed.  Their grid-wide flags and counters carry a tag made of
+ *    a host part and the workspace's own count of groupings / forwards, which the
+ *    kernels move on themselves, so a replay tags them afresh.  Calls that read
+ *    back or clear memory with a memset (tt_cache_create, tt_cache_populate,
+ *    tt_cache_import, tt_bag_plan_dedup, tt_bag_route with nnz = 0) are not for
+ *    capture.
  *  - Ownership: the caller owns every buffer it passes, including the workspace.
  *    The library allocates device memory only inside tt_cache_create and frees it
  *    only in tt_cache_destroy; it keeps no caller pointer between calls.

@@ -1,7 +1,10 @@
 // tt_api.hip -- the C ABI (include/tt_bag.h): argument checks, workspace layout,
 // launch sequence.  Device work lives in tt_route.hip, tt_fwd.hip, tt_bwd.hip and
 // tt_cache.hip.
+#include <unistd.h>
+
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -189,8 +192,9 @@ void bind_ws(Plan *P, void *ws) {
   a.part3 = (float *)(b + P->o_p3);
   a.frag = (float *)(b + P->o_frag);
   a.part2 = (float *)(b + P->o_p2);
-  a.epoch = g_epoch.fetch_add(1);
-  if (a.epoch == 0) a.epoch = g_epoch.fetch_add(1);
+  a.epoch = g_epoch.fetch_add(1) & 0x7fffffffu;  // (captured launches set the top bit)
+  if (a.epoch == 0) a.epoch = g_epoch.fetch_add(1) & 0x7fffffffu;
+  a.devtag = 0;
   a.sync_polls = g_sync_polls.load(std::memory_order_relaxed);
 }
 
@@ -300,6 +304,23 @@ static int check_cores(const float *const cores[3]) {
 }  // extern "C"
 
 namespace ttb {
+DevArgs tag_for_launch(const DevArgs &a, hipStream_t s) {
+  // one salt for the whole process: every graph captured here, whichever workspace it
+  // uses, adds the same host part to the workspace's own count
+  static const unsigned salt = [] {
+    const unsigned long long t = (unsigned long long)std::chrono::steady_clock::now()
+                                     .time_since_epoch().count();
+    return (unsigned)(t ^ (t >> 32) ^ ((unsigned long long)getpid() << 16)) | 1u;
+  }();
+  DevArgs b = a;
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) == hipSuccess && st == hipStreamCaptureStatusActive) {
+    b.devtag = 1;
+    b.epoch = salt;
+  }
+  return b;
+}
+
 // Where a three-core plan keeps its header inside ws, and the fingerprint a plan made
 // for these arguments carries (no cache).  Used by the backward over distinct indices,
 // whose kernels read the real batch's plan and must see whether it is this batch's.

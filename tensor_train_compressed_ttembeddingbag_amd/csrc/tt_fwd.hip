@@ -90,7 +90,7 @@ static __device__ void fwd_wait_out(const DevArgs &a) {  // whole block
 // MF: stage 2 on the matrix cores (q1 = q3 = 4, rows kept in LDS, RP <= 32), chosen by the
 // host when the work items are expected to be resident at once (see mf_stage2).
 template <int RP, bool DOT, bool MF>
-__global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
+__device__ __forceinline__ void fwd_item(const DevArgs &a) {
   constexpr int KS = RP / 4;   // k-steps: lane group g covers r1 = g*KS + ks
   constexpr int NM = RP / 16;  // 16-row blocks of r2
   constexpr int LD = FwdLds<RP>::LD, LRP = log2_rp<RP>();
@@ -410,6 +410,24 @@ __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
   }
 }
 
+// The forward kernel.  Its flags carry this call's tag.  In a captured launch the tag
+// counts the clearing forwards on the workspace: the last block to finish (counted in
+// hdr[H_FCNT], which the grouping zeroes) moves that count on -- every block has read it
+// by then -- and zeroes the block count for the next forward on the same grouping, so a
+// replayed launch tags its flags afresh.
+template <int RP, bool DOT, bool MF>
+__global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
+  if (a.fzero) a.epoch = launch_tag(a, a.hdr[H_FEPOCH]);
+  fwd_item<RP, DOT, MF>(a);
+  if (a.fzero && a.devtag) {
+    __syncthreads();  // every wave of the block has read the count
+    if (threadIdx.x == 0 && atomicAdd(&a.hdr[H_FCNT], 1) + 1 == (int)gridDim.x) {
+      a.hdr[H_FCNT] = 0;
+      a.hdr[H_FEPOCH] = a.hdr[H_FEPOCH] + 1;
+    }
+  }
+}
+
 size_t fwd_lds_bytes(int RP, int JB, int P, int q3, int D, int sw) {
   switch (RP) {
     case 16: return FwdLds<16>::bytes(JB, P, q3, D, sw);
@@ -440,7 +458,8 @@ static hipError_t launch_fwd_k(const DevArgs &a, size_t lds, hipStream_t s) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS_DYN_MAX);
     attr_set = true;
   }
-  tt_launch(K_FWD, k_fwd<RP, DOT, MF>, dim3(items_max(a)), dim3(WG), lds, s, a);
+  tt_launch(K_FWD, k_fwd<RP, DOT, MF>, dim3(items_max(a)), dim3(WG), lds, s,
+            tag_for_launch(a, s));
   return hipGetLastError();
 }
 

@@ -46,6 +46,11 @@ enum {
   H_HIT_BEG = 4, H_HIT_END = 5,  // hit region [beg, end) of the final order
   H_VALID = 6,      // number of valid (non-skipped) elements
   H_PLAN = 7,       // fingerprint of the call that made the grouping (tt_bag_plan)
+  H_REPOCH = 10,    // groupings run on this workspace (moved on by k_meta)
+  H_FEPOCH = 11,    // forward calls that cleared out on this workspace (moved on by the
+                    // last block of each)
+  H_FCNT = 12,      // blocks of the running forward that are done (zeroed by k_meta and
+                    // by the last block of each forward)
   H_SIZE0 = 16,     // [P_MAX + 1] work items handed a place so far, per size
   H_WORDS = 64
 };
@@ -118,7 +123,13 @@ struct DevArgs {
   unsigned long long *flag;  // [COOP_TILES] grid-barrier arrival words (epoch << 32 | k)
   unsigned long long *fflag; // [FWD_ZERO_BLOCKS] forward: "my slice of out is cleared" words
   int fzero;                 // forward: its first blocks clear out (no separate kernel)
-  unsigned epoch;           // unique per call
+  unsigned epoch;           // tag of the grid-wide flags and counters: unique per call
+                            // (< 2^31) when enqueued directly; in a launch being captured
+                            // into a graph, a per-process salt to which the kernels add the
+                            // workspace's count of groupings / forwards (hdr[H_REPOCH] /
+                            // hdr[H_FEPOCH]) and set the top bit, so that every replay
+                            // tags its flags afresh
+  int devtag;               // 1: the launch is being captured (the device count above)
   unsigned sync_polls;      // bound of every device-side wait (polls before giving up)
   int *hdr;
   int4 *einfo;      // per element: dA (t,i1), dB (t,i2), dI3 (t,i3), bag
@@ -219,6 +230,14 @@ int plan_identity(const tt_desc *desc, int64_t nnz, int64_t num_bags, const void
 
 // compute units of the current device (cached per device; 0 if the query fails)
 int device_cus();
+
+// a copy of the arguments for a launch on stream s: when s is capturing a graph, devtag
+// set and the tag's host part replaced by the per-process salt
+DevArgs tag_for_launch(const DevArgs &a, hipStream_t s);
+// the tag a kernel uses: devtag ? (salt + count) | 2^31 : the call's own
+__device__ __forceinline__ unsigned launch_tag(const DevArgs &a, int count) {
+  return a.devtag ? ((a.epoch + (unsigned)count) | 0x80000000u) : a.epoch;
+}
 
 // stable LSD radix sort of n 64-bit keys by bits [lo, hi); returns a or b (the result)
 unsigned long long *radix_sort64_bits(unsigned long long *a, unsigned long long *b, int n,

@@ -544,6 +544,7 @@ __host__ __device__ inline CoopLds coop_lds(const DevArgs &a) {
 }
 
 __global__ __launch_bounds__(CT) void k_route_coop(DevArgs a) {
+  a.epoch = launch_tag(a, a.hdr[H_REPOCH]);  // this grouping's tag
   extern __shared__ int lds_i[];
   __shared__ int s_scan[2 * (CT / 64) + 1];
   __shared__ int s_red[8];
@@ -617,6 +618,7 @@ __global__ __launch_bounds__(CT) void k_route_coop(DevArgs a) {
 // [bin][tile] matrices (bin-major: entry (d, t) becomes the first position of bin d's
 // elements of tile t) and records the bin starts.
 __global__ __launch_bounds__(RT) void k_route_a(DevArgs a) {
+  a.epoch = launch_tag(a, a.hdr[H_REPOCH]);  // this grouping's tag
   extern __shared__ int lds_i[];  // s_off [ROUTE_MAX_BAGS] | hist [max(binsI3, binsA)]
   __shared__ int s_scan[RT / 64 + 1];
   __shared__ int s_red[8];
@@ -649,6 +651,7 @@ __global__ __launch_bounds__(RT) void k_route_a(DevArgs a) {
 // over the orderA tiles; the last block scans them and builds the group table and the
 // work items.
 __global__ __launch_bounds__(RT) void k_route_b(DevArgs a) {
+  a.epoch = launch_tag(a, a.hdr[H_REPOCH]);  // this grouping's tag
   extern __shared__ unsigned short lds_c[];  // [4][max(binsI3, binsA)]
   __shared__ int s_scan[RT / 64 + 1];
   const int blk = blockIdx.x;
@@ -686,6 +689,7 @@ __global__ __launch_bounds__(RT) void k_route_b(DevArgs a) {
 
 // k_route_c: the orderA tiles placed by (t,i2) into the final order.
 __global__ __launch_bounds__(RT) void k_route_c(DevArgs a) {
+  a.epoch = launch_tag(a, a.hdr[H_REPOCH]);  // this grouping's tag
   extern __shared__ unsigned short lds_c[];  // [4][binsB]
   tile_final<RT>(a, blockIdx.x, lds_c, a.histB, a.nblk, blockIdx.x);
   if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr[H_PLAN] = (int)a.plan_fp;
@@ -811,6 +815,13 @@ __global__ __launch_bounds__(64 * META_WAVES) void k_meta(DevArgs a) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wi = blockIdx.x * META_WAVES + w;
   const int plan = a.hdr[H_PLAN], nitems = a.hdr[H_NFWD];
+  // every grouping kernel of this call is done with its tag: the next grouping on this
+  // workspace counts one more; and a forward after this grouping starts its block count
+  // from zero
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.hdr[H_REPOCH] = a.hdr[H_REPOCH] + 1;
+    a.hdr[H_FCNT] = 0;
+  }
   if (plan != (int)a.plan_fp || wi >= nitems) return;  // (wave-uniform)
   const int4 item = a.fitem[wi];
   const int grp = item.x, s0 = item.y, n_el = item.z - item.y;
@@ -873,7 +884,7 @@ static hipError_t launch_meta(const DevArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_route(const DevArgs &args, hipStream_t s) {
-  DevArgs a = args;
+  DevArgs a = tag_for_launch(args, s);
   a.ncu = device_cus();
   if (a.nblk == 0) return hipGetLastError();
   if (coop_route_ok(a)) {

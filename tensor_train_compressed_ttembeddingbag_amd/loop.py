@@ -16,9 +16,18 @@ latest step with an event, which is at or after the last user of its workspace. 
 cache, the lookup of a batch runs on the grouping stream just before its grouping and
 writes that batch's slot buffer, last read two batches back, so there an event follows
 every step.  Argument marshalling only: every step runs in libttbag.
+
+Captured (graph=True, the plain path): each step -- forward of batch i on the capture
+stream, then the grouping of batch i + AHEAD forked onto the second stream beside the
+backward of batch i, joined back at the end -- is captured once per (batch, workspace)
+combination into a HIP graph (torch.cuda.CUDAGraph), all of them when the loop is built,
+and a step is one replay.  Replays run in order on one stream and every graph joins its
+grouping, so workspace reuse needs no events; the kernels tag their grid-wide flags with
+the workspace's own call counts, so a replayed launch does not see the flags of the last.
 """
 from __future__ import annotations
 
+import math
 import time
 from typing import List
 
@@ -42,7 +51,7 @@ class TrainLoop:
     def __init__(self, desc, cores: List[torch.Tensor], batches, num_bags: int, lr: float,
                  out: torch.Tensor, status: torch.Tensor, update: str = "sgd", aux=None,
                  aux_rows=None, cache=None, rows=None, slots=None, dedup: bool = False,
-                 pipeline: bool = True):
+                 pipeline: bool = True, graph: bool = False):
         if dedup and (cache is not None or update == "adagrad"):
             raise ValueError("the backward over distinct indices takes no cache and updates "
                              "by sgd or grad")
@@ -89,9 +98,61 @@ class TrainLoop:
         self.fast = not self.dcore and not dedup
         self.prepared = {}
         self.wait_s = 0.0  # host time spent waiting for groupings
+        self.graph = graph
+        if graph and not (pipeline and self.fast and cache is None):
+            raise ValueError("a captured loop takes the plain pipelined path: three cores, "
+                             "no cache, no distinct-index backward")
+        if graph:
+            # steps are captured on a stream of their own (default priority) and replayed
+            # on the main stream; the calls are prepared for the capture streams
+            self.cap = torch.cuda.Stream()
+            self.graphs = []
         if pipeline:
             for j in range(self.ahead):
                 self.cvs[j] = self._plan(j)
+        if graph:
+            torch.cuda.synchronize()
+            nb, nw = len(batches), len(self.wss)
+            period = nb * nw // math.gcd(nb, nw)  # (batch, workspace) combinations in turn
+            self.graphs = [self._capture(k) for k in range(period)]
+
+    def _calls(self, i: int, stream):
+        """The prepared forward and backward of batch i (workspace i), on `stream`."""
+        bi, wi = i % len(self.batches), i % len(self.wss)
+        key = ("fwd", bi, wi, id(stream))
+        if key not in self.prepared:
+            b, ws = self.batches[bi], self.wss[wi]
+            w = b["per_sample_weights"]
+            eps = 1e-10 if self.update == "adagrad" else 0.0
+            self.prepared[key] = abi.prepare_forward(
+                self.desc, self.g, b["indices"], b["offsets"], self.B, w, out=self.out, ws=ws,
+                dev_status=self.status, stream=stream)
+            self.prepared[("bwd", bi, wi, id(stream))] = abi.prepare_backward(
+                self.desc, self.g, b["indices"], b["offsets"], self.B, b["grad_out"],
+                update=self.update, lr=self.lr, eps=eps, aux=self.aux, aux_rows=self.aux_rows,
+                per_sample_weights=w, ws=ws, dev_status=self.status, stream=stream)
+        return self.prepared[key], self.prepared[("bwd", bi, wi, id(stream))]
+
+    def _capture(self, k: int):
+        """Graph of step k (and of every step k + period): the forward of batch k, the
+        grouping of batch k + ahead beside the backward of batch k, joined."""
+        j = k + self.ahead
+        bj, wj = self.batches[j % len(self.batches)], self.wss[j % len(self.wss)]
+        plan = abi.prepare_plan(self.desc, bj["indices"], bj["offsets"], self.B,
+                                bj["per_sample_weights"], ws=wj, dev_status=self.status,
+                                stream=self.side)
+        fwd, bwd = self._calls(k, self.cap)
+        fork, join = torch.cuda.Event(), torch.cuda.Event()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=self.cap):
+            fwd()
+            fork.record(self.cap)
+            self.side.wait_event(fork)
+            plan()
+            join.record(self.side)
+            bwd()
+            self.cap.wait_event(join)
+        return gr
 
     def _plan(self, i: int):
         b = self.batches[i % len(self.batches)]
@@ -161,6 +222,9 @@ class TrainLoop:
     def step(self) -> int:
         i = self.next
         self.next += 1
+        if self.graph:
+            self.graphs[i % len(self.graphs)].replay()
+            return i
         b = self.batches[i % len(self.batches)]
         ws = self.wss[i % len(self.wss)]
         if self.pipeline:

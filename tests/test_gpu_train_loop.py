@@ -324,3 +324,60 @@ def test_loop_reuses_its_workspaces_over_many_steps(dedup):
             for k in range(3):
                 delta = end[t][k].astype(np.float64) - start[t][k].astype(np.float64)
                 assert rel_err(delta, -wl.lr * grads[t][k]) <= TOL, (i, t, k)
+
+
+def test_captured_loop_replays_match_the_eager_loop():
+    """The loop captured into HIP graphs (graph=True: one graph per (batch, workspace)
+    pair, the grouping of batch i + 2 forked onto the second stream inside the capture):
+    13 steps replayed, each one checked right after it against the same step enqueued
+    eagerly by a second loop on its own copy of the cores (the host synchronises between
+    them).  The backward is deterministic, so the cores must agree bit for bit after
+    every step; the forward pools with atomics, so its output agrees to rounding.  The
+    first and the last replayed forwards are also checked against the oracle at the cores
+    they started from.  Replays reuse each graph (6 graphs for 13 steps), so the kernels'
+    flag tags must move on without the host."""
+    print("case captured train loop readme 13", flush=True)
+    wl = W.WORKLOADS["readme"]
+    B, steps = wl.bags_per_table, 13
+    cores = W.make_cores(wl)
+    desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E)
+    host_batches = [W.make_batch(wl, k) for k in range(2)]
+    batches = [to_dev(b) for b in host_batches]
+    g_e, g_c = gpu_cores(wl, cores), gpu_cores(wl, cores)
+    out_e, out_c = (torch.empty(B, wl.D, device="cuda") for _ in range(2))
+    st_e, st_c = (torch.zeros(1, dtype=torch.int32, device="cuda") for _ in range(2))
+    eager = TrainLoop(desc, g_e, batches, B, wl.lr, out_e, st_e)
+    cap = TrainLoop(desc, g_c, batches, B, wl.lr, out_c, st_c, graph=True)
+    assert len(cap.graphs) == 6  # lcm(2 batches, 6 workspaces)
+    checks = {}
+    for i in range(steps):
+        start = [x.clone() for x in g_c] if i in (0, steps - 1) else None
+        eager.step()
+        torch.cuda.synchronize()
+        cap.step()
+        torch.cuda.synchronize()
+        assert rel_err(out_c.cpu().numpy(), out_e.cpu().numpy()) <= 1e-6, i
+        for k in range(3):
+            assert torch.equal(g_c[k], g_e[k]), (i, k)
+        if start is not None:
+            checks[i] = (host_cores(wl, start), out_c.cpu().numpy())
+    assert int(st_e.item()) == 0 and int(st_c.item()) == 0
+    for i, (start, y) in checks.items():
+        b = host_batches[i % 2]
+        yref = oracle.forward(wl.p, wl.q, wl.ranks, wl.E, start, b["indices"], b["offsets"], B)
+        assert rel_err(y, yref) <= TOL, i
+
+
+def test_captured_loop_takes_the_plain_path_only():
+    """Graph capture is for the plain pipelined path; the others are rejected up front."""
+    wl = W.custom(p=(8, 9, 10), q=(4, 4, 4), ranks=(16, 16), bags_per_table=8,
+                  lengths=("uniform", 1, 4))
+    desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E)
+    g = gpu_cores(wl, W.make_cores(wl))
+    b = [to_dev(W.make_batch(wl, 0))]
+    out = torch.empty(8, wl.D, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        TrainLoop(desc, g, b, 8, 0.1, out, st, pipeline=False, graph=True)
+    with pytest.raises(ValueError):
+        TrainLoop(desc, g, b, 8, 0.1, out, st, dedup=True, graph=True)
