@@ -645,6 +645,13 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
     const int W = one ? a.q1 * a.R1 : a.R2 * a.q3;
     float *dst = one ? a.G1 + (size_t)seg * W : a.G3 + (size_t)seg * W;
     float *aux = one ? a.X1 + (size_t)seg * W : a.X3 + (size_t)seg * W;
+    // the values the update reads, loaded beside the segment bounds (thread t: column t
+    // of the first column block, where the update puts thread t)
+    float x_pre = 0.f, aux_pre = 0.f;
+    if (tid < W) {
+      if (UPD != UPD_GRAD) x_pre = dst[tid];
+      if (UPD == UPD_ADAGRAD) aux_pre = aux[tid];
+    }
     if (beg >= end) {  // an untouched slice: a zero gradient, no update
       if (UPD == UPD_GRAD)
         for (int c = tid; c < W; c += SEG_T) aux[c] = 0.f;
@@ -703,9 +710,12 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
         const int c = c0 + t2;
         float sum = 0.f;
         for (int r = 0; r < NRG; ++r) sum += s_red[(r * LPR + t2 / VEC) * 4 + t2 % VEC];
-        if (c < W)
-          apply_update<UPD>(a, dst, aux, c, sum, UPD == UPD_GRAD ? 0.f : dst[c],
-                            UPD == UPD_ADAGRAD ? aux[c] : 0.f);
+        if (c < W) {
+          const bool pre = c == tid;  // (the first column block)
+          apply_update<UPD>(a, dst, aux, c, sum,
+                            UPD == UPD_GRAD ? 0.f : (pre ? x_pre : dst[c]),
+                            UPD == UPD_ADAGRAD ? (pre ? aux_pre : aux[c]) : 0.f);
+        }
       }
       __syncthreads();
     }

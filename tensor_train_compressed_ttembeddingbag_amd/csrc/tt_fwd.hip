@@ -62,22 +62,32 @@ static __device__ void fwd_raise_flag(const DevArgs &a) {  // whole block
     __hip_atomic_store(&a.fflag[blockIdx.x], (unsigned long long)a.epoch, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
-static __device__ void fwd_wait_out(const DevArgs &a) {  // whole block
+// one poll of the clearing flags by the first wave (lane k: flag k); issued early, its
+// answer is looked at when the block needs out, so a flag raised by then costs no wait
+static __device__ unsigned long long fwd_poll_flags(const DevArgs &a) {
+  const int lane = threadIdx.x;
+  return (lane < 64 && lane < fwd_zero_blocks(a))
+             ? __hip_atomic_load(&a.fflag[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+             : (unsigned long long)a.epoch;
+}
+// first: an earlier poll's answer (fwd_poll_flags), taken as the first poll
+static __device__ void fwd_wait_out(const DevArgs &a, unsigned long long first) {  // whole block
   __shared__ int s_ok;
   if (threadIdx.x < 64) {
-    const int nz = fwd_zero_blocks(a), lane = threadIdx.x;
+    const int lane = threadIdx.x;
     int ok = 1;
+    unsigned long long v = first;
     for (unsigned polls = 0;; ++polls) {
       if (polls >= a.sync_polls) {  // (a limit of 0 gives up before the first poll)
         ok = 0;
         if (lane == 0) set_status(a.status, TT_DEV_SYNC_TIMEOUT);
         break;
       }
-      const unsigned long long v = lane < nz
-          ? __hip_atomic_load(&a.fflag[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-          : (unsigned long long)a.epoch;
+      if (polls > 0) {
+        __builtin_amdgcn_s_sleep(1);
+        v = fwd_poll_flags(a);
+      }
       if (__ballot(v != (unsigned long long)a.epoch) == 0ull) break;
-      __builtin_amdgcn_s_sleep(1);
     }
     if (lane == 0) s_ok = ok;
   }
@@ -272,7 +282,9 @@ __device__ __forceinline__ void fwd_item(const DevArgs &a) {
   if (clearer) fwd_raise_flag(a);  // (includes the barrier)
   else lds_barrier();
 
-  if (a.fzero && !SW) fwd_wait_out(a);  // stage 2 adds into out directly
+  if (a.fzero && !SW) fwd_wait_out(a, fwd_poll_flags(a));  // stage 2 adds into out directly
+  // rows kept in LDS: the first poll of the clearing flags is in flight during the columns
+  const unsigned long long fpoll = (a.fzero && SW) ? fwd_poll_flags(a) : 0ull;
   for (int j0 = 0; j0 < q2; j0 += JB) {
     if (j0 > 0) {  // next G2 stage (only when the slice does not fit at once)
       lds_barrier();
@@ -400,7 +412,7 @@ __device__ __forceinline__ void fwd_item(const DevArgs &a) {
   }
   if (!SW) return;
   // pooling: out[bag] += w * W[item], one row-contiguous pass per element
-  if (a.fzero) fwd_wait_out(a);  // (includes the barrier)
+  if (a.fzero) fwd_wait_out(a, fpoll);  // (includes the barrier)
   else lds_barrier();
   for (int e = w; e < n_el; e += NW) {
     const int it = M.e_it[e];
