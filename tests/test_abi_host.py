@@ -268,3 +268,18 @@ def test_train_loop_grouping_waits_cover_workspace_reuse(ahead, every):
         assert k == -1 or (k <= j - ahead - 1 and k % every == every - 1)
         last_user = j - W  # the previous batch in workspace j % W
         assert k >= last_user or last_user < 0
+
+
+def test_package_star_import_names_only_existing_modules():
+    """Every name the package exports imports on a host without a GPU (the HIP library
+    itself loads only at the first call)."""
+    import subprocess
+    import sys
+    code = ("from tensor_train_compressed_ttembeddingbag_amd import *\n"
+            "import tensor_train_compressed_ttembeddingbag_amd as p\n"
+            "assert all(hasattr(p, n) for n in p.__all__)\n"
+            "from tensor_train_compressed_ttembeddingbag_amd.module import TTEmbeddingBag, "
+            "TableBatchedTTEmbeddingBag, OptimType\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
