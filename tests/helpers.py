@@ -19,6 +19,41 @@ def rel_err(x, ref) -> float:
     return float(diff / scale)
 
 
+# Elementwise as well (forward rows, returned gradients): a sum of products rounded in
+# fp32 is off its exact value by at most about n * 2^-24 times the sum of the absolute
+# values of its terms (n = the number of roundings along the way; Higham, "Accuracy and
+# Stability of Numerical Algorithms", section 3.1).  The oracle run on the absolute values
+# of every input gives that sum of absolute terms for each element exactly, so each element
+# is checked against its own bound; ELEM_GAMMA = 1024 ulps covers the products over r1 and
+# r2 (up to 64 + 64 roundings) and the sums over a bag or a slice's partials with room to
+# spare, and still fails a dropped or doubled term of ordinary size.
+ELEM_GAMMA = 1024 * 2.0 ** -24
+
+
+def elem_excess(x, ref, absref) -> float:
+    """max over elements of |x - x*| / (ELEM_GAMMA * sum|terms|) (<= 1 passes); elements
+    whose terms are all zero must be exact."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    bound = ELEM_GAMMA * np.asarray(absref, dtype=np.float64)
+    err = np.abs(x - ref)
+    if not err.size:
+        return 0.0
+    zero = bound == 0.0
+    if np.any(err[zero] != 0.0):
+        return float("inf")
+    return float(np.max(err[~zero] / bound[~zero])) if np.any(~zero) else 0.0
+
+
+def abs_inputs(cores, batch):
+    """The cores, per-sample weights and grad_out with every entry replaced by its absolute
+    value (the inputs of the bound above)."""
+    ac = [[np.abs(c) for c in t] for t in cores]
+    psw = batch.get("per_sample_weights")
+    return (ac, None if psw is None else np.abs(psw),
+            None if batch.get("grad_out") is None else np.abs(batch["grad_out"]))
+
+
 def gpu_cores(wl, cores, device="cuda"):
     """Logical per-table cores -> three slice-major device tensors (all tables)."""
     out = []

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from tensor_train_compressed_ttembeddingbag_amd import abi, workloads as W
-from helpers import TOL, gpu_cores, host_cores, rel_err, to_dev
+from helpers import TOL, abs_inputs, elem_excess, gpu_cores, host_cores, rel_err, to_dev
 from test_gpu_parity import SMALL
 
 pytestmark = pytest.mark.gpu
@@ -41,7 +41,9 @@ def _oracle_grads(wl, cores, b, slots=None, cache_size=0):
                            cache_size=cache_size)
 
 
-def _check_grads(wl, gk_dev, grads, touched):
+def _check_grads(wl, gk_dev, grads, touched, agrads=None):
+    """agrads: the oracle's gradients of the absolute-valued inputs (the elementwise
+    rounding bound), or None to check per tensor only."""
     got = host_cores(wl, gk_dev)
     for t in range(wl.num_tables):
         for k in range(3):
@@ -49,6 +51,9 @@ def _check_grads(wl, gk_dev, grads, touched):
             assert not np.isnan(x).any(), (t, k)
             e = rel_err(x, grads[t][k])
             assert e <= TOL, "table %d core %d: gradient rel err %.3g" % (t, k, e)
+            if agrads is not None:
+                e = elem_excess(x, grads[t][k], agrads[t][k])
+                assert e <= 1.0, "table %d core %d: an element exceeds its bound (x%.3g)" % (t, k, e)
             sl = np.moveaxis(x, 1, 0)
             for ik in np.flatnonzero(touched[t][k] == 0):
                 assert np.all(sl[ik] == 0.0), (t, k, ik)
@@ -68,7 +73,10 @@ def _grad_parity(wl, seed=0):
     for x, y in zip(g, bits):  # the cores are only read
         assert torch.equal(x.view(torch.int32), y.view(torch.int32))
     grads, touched, _, _ = _oracle_grads(wl, cores, b)
-    _check_grads(wl, out, grads, touched)
+    ac, apsw, adY = abs_inputs(cores, b)
+    agrads = oracle.backward(wl.p, wl.q, wl.ranks, wl.E, ac, b["indices"], b["offsets"],
+                             b["num_bags"], adY, per_sample_weights=apsw)[0]
+    _check_grads(wl, out, grads, touched, agrads)
     return out
 
 

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from tensor_train_compressed_ttembeddingbag_amd import abi, workloads as W
-from helpers import TOL, gpu_cores, host_cores, rel_err, to_dev
+from helpers import TOL, abs_inputs, elem_excess, gpu_cores, host_cores, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -66,6 +66,11 @@ def _full_parity(wl, batch, seed=None):
                         per_sample_weights=batch["per_sample_weights"])
     e = rel_err(Y, Yo)
     assert e <= TOL, "forward rel err %.3g" % e
+    ac, apsw, _ = abs_inputs(cores, batch)
+    Ya = oracle.forward(wl.p, wl.q, wl.ranks, wl.E, ac, batch["indices"], batch["offsets"], B,
+                        per_sample_weights=apsw)
+    e = elem_excess(Y, Yo, Ya)
+    assert e <= 1.0, "forward: an element exceeds its rounding bound (x%.3g)" % e
     grads, touched, _, _ = oracle.backward(wl.p, wl.q, wl.ranks, wl.E, cores, batch["indices"],
                                            batch["offsets"], B, batch["grad_out"],
                                            per_sample_weights=batch["per_sample_weights"])
