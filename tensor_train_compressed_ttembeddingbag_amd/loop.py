@@ -6,16 +6,19 @@ indices), then runs the planned forward and the planned backward.  Pipelined (de
 the grouping of batch i+AHEAD is enqueued on a second stream right after the forward of
 batch i (after the backward with the distinct-index grouping, which waits on the host) and
 runs beside the backward; the host waits for a batch's grouping before it enqueues the
-batch's forward.  Two batches ahead (the plain path), a grouping has a whole step more to
-finish than the host needs to reach it, so the host does not wait on it; with a cache or
-the distinct-index grouping it is one batch ahead.  A grouping must not overwrite a
+batch's forward.  Two batches ahead, a grouping has a whole step more to finish than the
+host needs to reach it, so the host does not wait on it; with the distinct-index grouping,
+or a cache and fewer than three batches, it is one batch ahead.  A grouping must not
+overwrite a
 workspace before the last step that used it has finished.  An event recorded on the main
 stream costs several microseconds of that stream's time, so it is recorded only after every
 DONE_EVERY-th step, AHEAD + DONE_EVERY workspaces rotate, and a grouping waits for the
 latest step with an event, which is at or after the last user of its workspace.  With a
 cache, the lookup of a batch runs on the grouping stream just before its grouping and
-writes that batch's slot buffer, last read two batches back, so there an event follows
-every step.  Argument marshalling only: every step runs in libttbag.
+writes that batch's slot buffer; the lookup of batch i + AHEAD, enqueued during step i,
+overwrites the buffer step i + AHEAD - len(batches) read, which must be a step the grouping
+waits for (<= i - 1: hence three batches for two ahead), so there an event follows every
+step.  Argument marshalling only: every step runs in libttbag.
 
 Captured (graph=True, the plain path): each step -- forward of batch i on the capture
 stream, then the grouping of batch i + AHEAD forked onto the second stream beside the
@@ -83,7 +86,7 @@ class TrainLoop:
         # which is >= j - ahead - every; batch j's workspace j % (ahead + every) was last
         # used by step j - ahead - every, so that event covers it.
         self.every = 1 if cache is not None else DONE_EVERY
-        self.ahead = 2 if (pipeline and cache is None and not dedup) else 1
+        self.ahead = 2 if (pipeline and not dedup and (cache is None or len(batches) >= 3)) else 1
         self.wss = [make_ws() for _ in range(self.ahead + self.every if pipeline else 1)]
         self.main = torch.cuda.current_stream()
         self.side = torch.cuda.Stream() if pipeline else self.main  # default priority

@@ -51,15 +51,18 @@ def test_pipelined_loop_matches_oracle(name, steps):
                 assert np.array_equal(end[t][k][:, m], start[t][k][:, m]), (i, t, k)
 
 
-def test_pipelined_loop_with_cache_matches_oracle():
+@pytest.mark.parametrize("nb, steps", [(2, 3), (3, 5)])
+def test_pipelined_loop_with_cache_matches_oracle(nb, steps):
     """The loop with a cache (each batch's lookup and grouping on the second stream,
-    started right after the previous forward): every step's forward, core update and
-    cache-row update against the oracle, whose slots come from its own top-K selection."""
-    print("case train loop cache", flush=True)
+    started right after a forward: one batch ahead with two batches, two ahead with three,
+    where the lookup of batch i + 2 reuses the slot buffer of step i - 1): every step's
+    forward, core update and cache-row update against the oracle, whose slots come from
+    its own top-K selection."""
+    print("case train loop cache", nb, steps, flush=True)
     wl = W.custom("cache", p=(20, 22, 25), q=(4, 4, 4), ranks=(32, 32), bags_per_table=256,
                   lengths=("fixed", 20), dist=("zipf", 1.2), init_std=1 / 32 ** 0.5, lr=0.01,
                   weighted=True)
-    K, B, steps = 900, 256, 3
+    K, B = 900, 256
     cores = W.make_cores(wl)
     desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E)
     cache = abi.Cache(desc, K, 1 << 14)
@@ -71,7 +74,7 @@ def test_pipelined_loop_with_cache_matches_oracle():
     nf = cache.populate(g, rows)
     sel = oracle.select_cache(oracle.count_frequencies([bt["indices"] for bt in warm]), K)
     assert nf == len(sel)
-    host_batches = [W.make_batch(wl, k) for k in range(2)]
+    host_batches = [W.make_batch(wl, k) for k in range(nb)]
     batches = [to_dev(b) for b in host_batches]
     slots = [torch.empty(b["indices"].numel(), dtype=torch.int32, device="cuda")
              for b in batches]
@@ -79,6 +82,7 @@ def test_pipelined_loop_with_cache_matches_oracle():
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     loop = TrainLoop(desc, g, batches, B, wl.lr, out, status, cache=cache, rows=rows,
                      slots=slots)
+    assert loop.ahead == (2 if nb >= 3 else 1)
     snaps, rsnaps, ys = [[x.clone() for x in g]], [rows.clone()], []
     for _ in range(steps):
         loop.step()
@@ -88,7 +92,7 @@ def test_pipelined_loop_with_cache_matches_oracle():
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     for i in range(steps):
-        b = host_batches[i % 2]
+        b = host_batches[i % nb]
         ref_slots = oracle.lookup_slots(sel, b["indices"])
         assert (ref_slots >= 0).any() and (ref_slots < 0).any()
         start, end = host_cores(wl, snaps[i]), host_cores(wl, snaps[i + 1])
