@@ -219,12 +219,15 @@ void k_bwd(DevArgs a) {
       for (int mr = 0; mr < NM; ++mr) aG[sr][mr] = src2[min(16 * mr + c, R1 - 1)];
     }
   };
-  if (F44 && R1 == RP && R2 == RP) {
+  const bool vec = F44 && R1 == RP && R2 == RP;
+  if (vec) {
     // 16-byte loads throughout (ranks fill RP, q3 = 4, D a multiple of 4): G2 along r2,
-    // an item's G3 slice as one (r2, four j3) vector per lane, w * dY along d.  The
-    // number of memory instructions, not the bytes, bounds this round.
+    // an item's G3 slice as one (r2, four j3) vector per lane, and G_u of every item
+    // straight from the dY rows of its elements along d (the first element's row in flight
+    // with the other loads; further elements, rare, after).  The number of memory
+    // instructions, not the bytes, bounds this round.
     constexpr int SV = 2;
-    const int n2 = nj0 * RP * RP / 4, n3 = nI * RP, D4 = D >> 2, nY = n_el * D4;
+    const int n2 = nj0 * RP * RP / 4, n3 = nI * RP, D4 = D >> 2, nG = nI * D4;
     auto ld2 = [&](int i4) {
       const int jj = i4 >> (2 * LRP - 2), r1 = (i4 >> (LRP - 2)) & (RP - 1);
       const int r2 = (i4 & (RP / 4 - 1)) * 4;
@@ -239,16 +242,32 @@ void k_bwd(DevArgs a) {
     auto ld3 = [&](int i4) {
       return *(const float4 *)&G3t[M.it_i3[i4 >> LRP] * (int)W3 + (i4 & (RP - 1)) * 4];
     };
-    auto ldY = [&](int i4) {
-      const int e = i4 / D4;
-      return *(const float4 *)&a.dY[(size_t)M.e_bag[e] * D + (i4 - e * D4) * 4];
+    // the dY row (4 columns at d4) of the element in item-major slot k
+    auto ldY = [&](int k, int d4) {
+      return *(const float4 *)&a.dY[(size_t)M.e_bag[M.e_perm[k]] * D + d4 * 4];
+    };
+    // G_u[it][4 d4 ..] = sum over the item's elements, in position order, of w * dY
+    auto finish_gu = [&](int i4, float4 y0) {
+      const int it = i4 / D4, d4 = i4 - it * D4, k0 = M.it_beg[it], k1 = M.it_beg[it + 1];
+      float we = M.e_w[M.e_perm[k0]];
+      float4 acc = make_float4(we * y0.x, we * y0.y, we * y0.z, we * y0.w);
+      for (int k = k0 + 1; k < k1; ++k) {
+        const float4 y = ldY(k, d4);
+        we = M.e_w[M.e_perm[k]];
+        acc.x += we * y.x; acc.y += we * y.y; acc.z += we * y.z; acc.w += we * y.w;
+      }
+      *(float4 *)&sGu[4 * i4] = acc;
+    };
+    auto first_y = [&](int i4) {
+      const int it = i4 / D4;
+      return ldY(M.it_beg[it], i4 - it * D4);
     };
     float4 v2[SV], v3[SV], vy[SV];
 #pragma unroll
     for (int u = 0; u < SV; ++u) {
       v2[u] = ld2(min(tid + u * WG, n2 - 1));
       v3[u] = ld3(min(tid + u * WG, n3 - 1));
-      vy[u] = ldY(min(tid + u * WG, nY - 1));
+      vy[u] = first_y(min(tid + u * WG, nG - 1));
     }
     load_g1(true);
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -260,22 +279,14 @@ void k_bwd(DevArgs a) {
         *(float4 *)&sG3[4 * i4] = v3[u];
         *(float4 *)&sdA3[4 * i4] = z4;
       }
-      if (i4 < nY) {
-        const float we = M.e_w[i4 / D4];
-        *(float4 *)&sYe[4 * i4] = make_float4(we * vy[u].x, we * vy[u].y, we * vy[u].z,
-                                              we * vy[u].w);
-      }
+      if (i4 < nG) finish_gu(i4, vy[u]);
     }
     for (int i4 = tid + SV * WG; i4 < n2; i4 += WG) st2(i4, ld2(i4));
     for (int i4 = tid + SV * WG; i4 < n3; i4 += WG) {
       *(float4 *)&sG3[4 * i4] = ld3(i4);
       *(float4 *)&sdA3[4 * i4] = z4;
     }
-    for (int i4 = tid + SV * WG; i4 < nY; i4 += WG) {
-      const float4 x = ldY(i4);
-      const float we = M.e_w[i4 / D4];
-      *(float4 *)&sYe[4 * i4] = make_float4(we * x.x, we * x.y, we * x.z, we * x.w);
-    }
+    for (int i4 = tid + SV * WG; i4 < nG; i4 += WG) finish_gu(i4, first_y(i4));
   } else {
     float v2[STAGE_U], v3[STAGE_U], vy[STAGE_U];
     load2(0, nj0, tid, v2);
@@ -318,14 +329,17 @@ void k_bwd(DevArgs a) {
   }
   vmem_drain();
   lds_barrier();
-  // G_u of every item: its elements' w * dY rows summed in position order
-  for (int i = tid; i < nI * D; i += WG) {
-    const int it = fdiv(i, a.mD), d = i - it * D;
-    float acc = 0.f;
-    for (int k = M.it_beg[it]; k < M.it_beg[it + 1]; ++k) acc += sYe[(size_t)M.e_perm[k] * D + d];
-    sGu[i] = acc;
+  if (!vec) {
+    // G_u of every item: its elements' w * dY rows summed in position order
+    for (int i = tid; i < nI * D; i += WG) {
+      const int it = fdiv(i, a.mD), d = i - it * D;
+      float acc = 0.f;
+      for (int k = M.it_beg[it]; k < M.it_beg[it + 1]; ++k)
+        acc += sYe[(size_t)M.e_perm[k] * D + d];
+      sGu[i] = acc;
+    }
+    lds_barrier();
   }
-  lds_barrier();
 
   f4 dA1[NM];  // dG1^T[r1 = 16mr + 4g + v][row = c]
 #pragma unroll
@@ -545,19 +559,33 @@ void k_bwd(DevArgs a) {
     if (pr < nP) {
       float *dst = a.part1 + (size_t)(s0 + M.it_first[M.pr_it[pr]]) * W1 + (size_t)j1 * R1;
 #pragma unroll
-      for (int mr = 0; mr < NM; ++mr)
+      for (int mr = 0; mr < NM; ++mr) {
+        if (vec) {  // four r1 of the lane as one 16-byte store (R1 = RP)
+          *(float4 *)&dst[16 * mr + 4 * g] =
+              make_float4(dA1[mr][0], dA1[mr][1], dA1[mr][2], dA1[mr][3]);
+        } else {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r1 = 16 * mr + 4 * g + v;
-          if (r1 < R1) dst[r1] = dA1[mr][v];
+          for (int v = 0; v < 4; ++v) {
+            const int r1 = 16 * mr + 4 * g + v;
+            if (r1 < R1) dst[r1] = dA1[mr][v];
+          }
         }
+      }
     }
   }
-  for (int i = tid; i < total3; i += WG) {  // i = (item * RP + r2) * q3 + j3
-    int jr, j3;
-    split3(i, jr, j3);
-    const int it = jr >> LRP, r2 = jr & (RP - 1);
-    if (r2 < R2) a.part3[(size_t)(s0 + M.it_first[it]) * W3 + r2 * q3 + j3] = sdA3[i];
+  if (vec) {  // q3 = 4, R2 = RP: an (item, r2) row of four j3 per 16-byte store
+    for (int i4 = tid; i4 < total3 / 4; i4 += WG) {
+      const int it = i4 >> LRP, r2 = i4 & (RP - 1);
+      *(float4 *)&a.part3[(size_t)(s0 + M.it_first[it]) * W3 + r2 * 4] =
+          *(const float4 *)&sdA3[4 * i4];
+    }
+  } else {
+    for (int i = tid; i < total3; i += WG) {  // i = (item * RP + r2) * q3 + j3
+      int jr, j3;
+      split3(i, jr, j3);
+      const int it = jr >> LRP, r2 = jr & (RP - 1);
+      if (r2 < R2) a.part3[(size_t)(s0 + M.it_first[it]) * W3 + r2 * q3 + j3] = sdA3[i];
+    }
   }
 }
 
