@@ -429,7 +429,7 @@ __device__ __forceinline__ void fwd_item(const DevArgs &a) {
 // replayed launch tags its flags afresh.
 template <int RP, bool DOT, bool MF>
 __global__ __launch_bounds__(WG) void k_fwd(DevArgs a) {
-  if (a.fzero) a.epoch = launch_tag(a, a.hdr[H_FEPOCH]);
+  if (a.fzero) a.epoch = launch_tag(a, a.hdr + H_FEPOCH);
   fwd_item<RP, DOT, MF>(a);
   if (a.fzero && a.devtag) {
     __syncthreads();  // every wave of the block has read the count

@@ -234,9 +234,10 @@ int device_cus();
 // a copy of the arguments for a launch on stream s: when s is capturing a graph, devtag
 // set and the tag's host part replaced by the per-process salt
 DevArgs tag_for_launch(const DevArgs &a, hipStream_t s);
-// the tag a kernel uses: devtag ? (salt + count) | 2^31 : the call's own
-__device__ __forceinline__ unsigned launch_tag(const DevArgs &a, int count) {
-  return a.devtag ? ((a.epoch + (unsigned)count) | 0x80000000u) : a.epoch;
+// the tag a kernel uses: the call's own, or in a captured launch (salt + the workspace's
+// count in *count) | 2^31 -- the count is read only then (a load at kernel start otherwise)
+__device__ __forceinline__ unsigned launch_tag(const DevArgs &a, const int *count) {
+  return a.devtag ? ((a.epoch + (unsigned)*count) | 0x80000000u) : a.epoch;
 }
 
 // stable LSD radix sort of n 64-bit keys by bits [lo, hi); returns a or b (the result)

@@ -544,7 +544,7 @@ __host__ __device__ inline CoopLds coop_lds(const DevArgs &a) {
 }
 
 __global__ __launch_bounds__(CT) void k_route_coop(DevArgs a) {
-  a.epoch = launch_tag(a, a.hdr[H_REPOCH]);  // this grouping's tag
+  a.epoch = launch_tag(a, a.hdr + H_REPOCH);  // this grouping's tag
   extern __shared__ int lds_i[];
   __shared__ int s_scan[2 * (CT / 64) + 1];
   __shared__ int s_red[8];
@@ -618,7 +618,7 @@ __global__ __launch_bounds__(CT) void k_route_coop(DevArgs a) {
 // [bin][tile] matrices (bin-major: entry (d, t) becomes the first position of bin d's
 // elements of tile t) and records the bin starts.
 __global__ __launch_bounds__(RT) void k_route_a(DevArgs a) {
-  a.epoch = launch_tag(a, a.hdr[H_REPOCH]);  // this grouping's tag
+  a.epoch = launch_tag(a, a.hdr + H_REPOCH);  // this grouping's tag
   extern __shared__ int lds_i[];  // s_off [ROUTE_MAX_BAGS] | hist [max(binsI3, binsA)]
   __shared__ int s_scan[RT / 64 + 1];
   __shared__ int s_red[8];
@@ -651,7 +651,7 @@ __global__ __launch_bounds__(RT) void k_route_a(DevArgs a) {
 // over the orderA tiles; the last block scans them and builds the group table and the
 // work items.
 __global__ __launch_bounds__(RT) void k_route_b(DevArgs a) {
-  a.epoch = launch_tag(a, a.hdr[H_REPOCH]);  // this grouping's tag
+  a.epoch = launch_tag(a, a.hdr + H_REPOCH);  // this grouping's tag
   extern __shared__ unsigned short lds_c[];  // [4][max(binsI3, binsA)]
   __shared__ int s_scan[RT / 64 + 1];
   const int blk = blockIdx.x;
@@ -689,7 +689,7 @@ __global__ __launch_bounds__(RT) void k_route_b(DevArgs a) {
 
 // k_route_c: the orderA tiles placed by (t,i2) into the final order.
 __global__ __launch_bounds__(RT) void k_route_c(DevArgs a) {
-  a.epoch = launch_tag(a, a.hdr[H_REPOCH]);  // this grouping's tag
+  a.epoch = launch_tag(a, a.hdr + H_REPOCH);  // this grouping's tag
   extern __shared__ unsigned short lds_c[];  // [4][binsB]
   tile_final<RT>(a, blockIdx.x, lds_c, a.histB, a.nblk, blockIdx.x);
   if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr[H_PLAN] = (int)a.plan_fp;
