@@ -220,14 +220,18 @@ void k_bwd(DevArgs a) {
     }
   };
   const bool vec = F44 && R1 == RP && R2 == RP;
+  const bool rep = n_el > nI;  // some index repeats in the work item
   if (vec) {
     // 16-byte loads throughout (ranks fill RP, q3 = 4, D a multiple of 4): G2 along r2,
-    // an item's G3 slice as one (r2, four j3) vector per lane, and G_u of every item
-    // straight from the dY rows of its elements along d (the first element's row in flight
-    // with the other loads; further elements, rare, after).  The number of memory
-    // instructions, not the bytes, bounds this round.
+    // an item's G3 slice as one (r2, four j3) vector per lane, and the dY rows along d.
+    // When every element of the work item is a distinct index (the usual case) the weighted
+    // row of each element is its item's G_u and goes straight to sGu; when an index repeats,
+    // the weighted rows go to sYe in position order, every row in flight at once, and each
+    // item's rows are summed after the barrier.  The number of memory instructions, not the
+    // bytes, bounds this round.
     constexpr int SV = 2;
-    const int n2 = nj0 * RP * RP / 4, n3 = nI * RP, D4 = D >> 2, nG = nI * D4;
+    float *sWY = rep ? sYe : sGu;
+    const int n2 = nj0 * RP * RP / 4, n3 = nI * RP, D4 = D >> 2, nY = n_el * D4;
     auto ld2 = [&](int i4) {
       const int jj = i4 >> (2 * LRP - 2), r1 = (i4 >> (LRP - 2)) & (RP - 1);
       const int r2 = (i4 & (RP / 4 - 1)) * 4;
@@ -242,32 +246,23 @@ void k_bwd(DevArgs a) {
     auto ld3 = [&](int i4) {
       return *(const float4 *)&G3t[M.it_i3[i4 >> LRP] * (int)W3 + (i4 & (RP - 1)) * 4];
     };
-    // the dY row (4 columns at d4) of the element in item-major slot k
-    auto ldY = [&](int k, int d4) {
-      return *(const float4 *)&a.dY[(size_t)M.e_bag[M.e_perm[k]] * D + d4 * 4];
+    // vector i4 = (q, d4): row q of sWY -- element q in position order, or, with no repeated
+    // index, item q (whose one element sits at item-major slot q)
+    auto elem_of = [&](int q) { return rep ? q : (int)M.e_perm[q]; };
+    auto ldY = [&](int i4) {
+      const int q = i4 / D4, d4 = i4 - q * D4;
+      return *(const float4 *)&a.dY[(size_t)M.e_bag[elem_of(q)] * D + d4 * 4];
     };
-    // G_u[it][4 d4 ..] = sum over the item's elements, in position order, of w * dY
-    auto finish_gu = [&](int i4, float4 y0) {
-      const int it = i4 / D4, d4 = i4 - it * D4, k0 = M.it_beg[it], k1 = M.it_beg[it + 1];
-      float we = M.e_w[M.e_perm[k0]];
-      float4 acc = make_float4(we * y0.x, we * y0.y, we * y0.z, we * y0.w);
-      for (int k = k0 + 1; k < k1; ++k) {
-        const float4 y = ldY(k, d4);
-        we = M.e_w[M.e_perm[k]];
-        acc.x += we * y.x; acc.y += we * y.y; acc.z += we * y.z; acc.w += we * y.w;
-      }
-      *(float4 *)&sGu[4 * i4] = acc;
-    };
-    auto first_y = [&](int i4) {
-      const int it = i4 / D4;
-      return ldY(M.it_beg[it], i4 - it * D4);
+    auto stY = [&](int i4, float4 y) {
+      const float w = M.e_w[elem_of(i4 / D4)];
+      *(float4 *)&sWY[4 * i4] = make_float4(w * y.x, w * y.y, w * y.z, w * y.w);
     };
     float4 v2[SV], v3[SV], vy[SV];
 #pragma unroll
     for (int u = 0; u < SV; ++u) {
       v2[u] = ld2(min(tid + u * WG, n2 - 1));
       v3[u] = ld3(min(tid + u * WG, n3 - 1));
-      vy[u] = first_y(min(tid + u * WG, nG - 1));
+      vy[u] = ldY(min(tid + u * WG, nY - 1));
     }
     load_g1(true);
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -279,14 +274,14 @@ void k_bwd(DevArgs a) {
         *(float4 *)&sG3[4 * i4] = v3[u];
         *(float4 *)&sdA3[4 * i4] = z4;
       }
-      if (i4 < nG) finish_gu(i4, vy[u]);
+      if (i4 < nY) stY(i4, vy[u]);
     }
     for (int i4 = tid + SV * WG; i4 < n2; i4 += WG) st2(i4, ld2(i4));
     for (int i4 = tid + SV * WG; i4 < n3; i4 += WG) {
       *(float4 *)&sG3[4 * i4] = ld3(i4);
       *(float4 *)&sdA3[4 * i4] = z4;
     }
-    for (int i4 = tid + SV * WG; i4 < nG; i4 += WG) finish_gu(i4, first_y(i4));
+    for (int i4 = tid + SV * WG; i4 < nY; i4 += WG) stY(i4, ldY(i4));
   } else {
     float v2[STAGE_U], v3[STAGE_U], vy[STAGE_U];
     load2(0, nj0, tid, v2);
@@ -329,7 +324,7 @@ void k_bwd(DevArgs a) {
   }
   vmem_drain();
   lds_barrier();
-  if (!vec) {
+  if (!vec || rep) {
     // G_u of every item: its elements' w * dY rows summed in position order
     for (int i = tid; i < nI * D; i += WG) {
       const int it = fdiv(i, a.mD), d = i - it * D;
