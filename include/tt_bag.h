@@ -19,16 +19,15 @@
  * Conventions for every entry point
  *  - Pointers are DEVICE pointers unless the comment says host.  `stream` is a
  *    hipStream_t (NULL = the default stream).  Every call is asynchronous on
- *    `stream` and does not synchronise the host, except tt_cache_populate and
- *    tt_bag_plan_dedup (which read a size back).
+ *    `stream` and does not synchronise the host, except tt_cache_populate (which
+ *    reads a size back) and the diagnostic tt_bag_dedup_counts.
  *  - HIP graphs: the calls that enqueue kernels only (the grouping, forward and
  *    backward calls, planned or not, tt_cache_lookup) may be captured into a HIP
  *    graph and replayed.  Their grid-wide flags and counters carry a tag made of
  *    a host part and the workspace's own count of groupings / forwards, which the
  *    kernels move on themselves, so a replay tags them afresh.  Calls that read
  *    back or clear memory with a memset (tt_cache_create, tt_cache_populate,
- *    tt_cache_import, tt_bag_plan_dedup, tt_bag_route with nnz = 0) are not for
- *    capture.
+ *    tt_cache_import, tt_bag_route with nnz = 0) are not for capture.
  *  - Ownership: the caller owns every buffer it passes, including the workspace.
  *    The library allocates device memory only inside tt_cache_create and frees it
  *    only in tt_cache_destroy; it keeps no caller pointer between calls.
@@ -409,9 +408,11 @@ int tt_full_weight(const tt_desc *desc, const float *const cores[3], int table, 
  * costs one element.  No cache.
  *   tt_bag_plan_dedup: the grouping of the batch (as tt_bag_plan, so tt_bag_forward_planned
  *     on the same ws runs the forward), the sort by index, the runs of equal indices, and
- *     the grouping of the virtual batch.  HOST-SYNCHRONOUS: it waits for the number of
- *     distinct indices and returns info[0] = that number, info[1] = the largest per table
- *     (host array; pass it unchanged to the backward).
+ *     the grouping of the virtual batch.  The number of distinct indices stays on the
+ *     device: the virtual batch's launches are sized by its bounds (nnz elements, nnz bags
+ *     per table) and its kernels read the count, so the call does not wait on the device
+ *     and may be captured.  info (host array) receives those bounds, info[0] = info[1] =
+ *     nnz; pass it unchanged to the backward, which rejects anything else (TT_EINVAL).
  *   tt_bag_backward_sgd_dedup / _grad_dedup: the grad_out sums of the runs (fixed order:
  *     32-element chunks of the sorted order, then each run's pieces in order), then the
  *     planned three-core backward (SGD, or dense gradients fully overwritten) on the
@@ -434,6 +435,12 @@ int tt_bag_backward_grad_dedup(const tt_desc *desc, const float *const cores[3],
                                const float *grad_out, float *const grad_cores[3],
                                const int64_t info[2], void *ws, size_t ws_bytes,
                                int32_t *dev_status, void *stream);
+/* Diagnostics (host-synchronous: waits for `stream`): the distinct-index counts of the
+ * batch last planned by tt_bag_plan_dedup in ws, into the host array counts[T + 1]:
+ * counts[t] = distinct (index) of the tables before t, counts[T] = all of them (invalid
+ * indices not counted).  Same sizes as the plan; not for capture. */
+int tt_bag_dedup_counts(const tt_desc *desc, int64_t nnz, int64_t num_bags, const void *ws,
+                        size_t ws_bytes, int64_t *counts, void *stream);
 
 /* ---------------------------------------------------------------- d-core tables
  * Tables of any number d of cores ("FBTT-Embedding" README, "Parameters": tt_p_shapes,

@@ -103,6 +103,7 @@ _SIG = {
                                                  _P]),
     "tt_bag_backward_grad_dedup": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P, _P, _P,
                                                   ctypes.c_size_t, _P, _P]),
+    "tt_bag_dedup_counts": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_size_t, _P, _P]),
     "tt_bag_workspace_size_d": (ctypes.c_size_t, [_P, _I64, _I64]),
     "tt_bag_groups_d": (ctypes.c_int, [_P, _P]),
     "tt_bag_forward_d": (ctypes.c_int, [_P, _P, _P, _I64, _P, _I64, _P, _P, _P, ctypes.c_size_t,
@@ -643,8 +644,9 @@ def workspace_dedup(desc: TTDesc, nnz: int, num_bags: int, device=None) -> torch
 
 def tt_bag_plan_dedup(desc: TTDesc, indices, offsets, num_bags: int, per_sample_weights=None,
                       ws=None, dev_status=None, stream=None):
-    """Group the batch and its distinct indices (host-synchronous).  Returns (ws, info):
-    pass both to tt_bag_forward(planned=True) / tt_bag_backward_*_dedup."""
+    """Group the batch and its distinct indices (asynchronous: the number of distinct
+    indices stays on the device).  Returns (ws, info), info = the virtual batch's bounds
+    (nnz, nnz): pass both to tt_bag_forward(planned=True) / tt_bag_backward_*_dedup."""
     _need(indices, torch.int64, "indices")
     _need(offsets, torch.int64, "offsets")
     if per_sample_weights is not None:
@@ -661,6 +663,17 @@ def tt_bag_plan_dedup(desc: TTDesc, indices, offsets, num_bags: int, per_sample_
                                  ws.numel(), _ptr(dev_status), info, _stream(stream, indices))
     _check("tt_bag_plan_dedup", rc)
     return ws, (int(info[0]), int(info[1]))
+
+
+def tt_bag_dedup_counts(desc: TTDesc, nnz: int, num_bags: int, ws, stream=None):
+    """Distinct-index counts of the batch last planned in ws by tt_bag_plan_dedup (waits for
+    the stream): [before table 0, ..., before table T-1, all]."""
+    _need(ws, torch.uint8, "ws")
+    out = (ctypes.c_int64 * (desc.num_tables + 1))()
+    rc = lib().tt_bag_dedup_counts(ctypes.byref(desc), int(nnz), int(num_bags), _ptr(ws),
+                                   ws.numel(), out, _stream(stream, ws))
+    _check("tt_bag_dedup_counts", rc)
+    return [int(x) for x in out]
 
 
 def _dedup_args(desc, indices, offsets, num_bags, grad_out, per_sample_weights, ws, dev_status):

@@ -347,6 +347,20 @@ static int plan_call(const tt_desc *desc, const int64_t *indices, int64_t nnz,
   return finish(launch_route(P.a, (hipStream_t)stream));
 }
 
+namespace ttb {
+int plan_devcount(const tt_desc *desc, const int64_t *indices, int64_t nnz,
+                  const int64_t *offsets, int64_t num_bags, const int64_t *nnz_dev, void *ws,
+                  size_t ws_bytes, int32_t *dev_status, void *stream) {
+  if (!nnz_dev) return TT_EINVAL;
+  Plan P;
+  int rc = prepare(&P, desc, indices, nnz, offsets, num_bags, nullptr, nullptr, ws, ws_bytes,
+                   dev_status);
+  if (rc) return rc;
+  P.a.nnz_dev = nnz_dev;
+  return finish(launch_route(P.a, (hipStream_t)stream));
+}
+}  // namespace ttb
+
 static int forward_planned_call(const tt_desc *desc, const float *const cores[3],
                                 const int64_t *indices, int64_t nnz, const int64_t *offsets,
                                 int64_t num_bags, const float *per_sample_weights,

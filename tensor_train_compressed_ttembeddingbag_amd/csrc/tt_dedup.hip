@@ -6,17 +6,16 @@
 // sum.  When indices repeat (Zipf-skewed batches) the virtual batch is much smaller, and
 // a hot index costs one element instead of thousands.
 //
-// Plan (host-synchronous once, for the size of the virtual batch): keys (table*E + index,
-// position) sorted stably by the key's index bits, runs of equal keys, the virtual
-// indices and offsets (table-major, B' = the largest per-table count of distinct
-// indices), and the grouping of both the real batch (for the forward) and the virtual
-// one.  Backward: the grad_out sums of the runs in two fixed-order passes (32-element
+// Plan (no host synchronisation): keys (table*E + index, position) sorted stably by the
+// key's index bits, runs of equal keys, the virtual indices and offsets (table-major,
+// nnz bags per table -- a bound on every table's count of distinct indices -- of which
+// the first count are filled), and the grouping of both the real batch (for the forward)
+// and the virtual one, whose element count the grouping kernels read from the device.  Backward: the grad_out sums of the runs in two fixed-order passes (32-element
 // chunks of the sorted order, then each run's chunk pieces in order), then the planned
 // three-core backward on the virtual batch.
 #include <algorithm>
 #include <cmath>
 #include <cstring>
-#include <vector>
 
 #include "tt_device.h"
 
@@ -240,14 +239,15 @@ __global__ __launch_bounds__(DD_T) void k_dd_frag(const unsigned long long *__re
 __global__ __launch_bounds__(DD_T) void k_dd_gu(const int *__restrict__ rstart,
                                                 const int *__restrict__ rend,
                                                 const int *__restrict__ rtab,
-                                                const int64_t *__restrict__ Rt, int Bp, int D,
-                                                const float *__restrict__ frag,
+                                                const int64_t *__restrict__ Rt, int T, int Bp,
+                                                int D, const float *__restrict__ frag,
                                                 float *__restrict__ Gu, const int *rhdr,
                                                 unsigned rfp, int *vhdr, unsigned vfp,
                                                 int32_t *status) {
   __shared__ float s_part[DD_T];
   if (!dd_plan_ok(rhdr, rfp, vhdr, vfp, status)) return;
   const int u = blockIdx.x;
+  if (u >= Rt[T]) return;  // (the launch covers every position; the runs are Rt[T])
   const int a = rstart[u], z = rend[u], t = rtab[u];
   const long long vb = (long long)t * Bp + (u - Rt[t]);
   const int c0 = a / DD_CH, nf = (z - 1) / DD_CH - c0 + 1;
@@ -408,24 +408,19 @@ int tt_bag_plan_dedup(const tt_desc *desc, const int64_t *indices, int64_t nnz,
                      (long long)desc->num_embeddings, P.T, cnt, P.nblk, at<int64_t>(ws, P.o_vidx),
                      at<int>(ws, P.o_rtab), at<int>(ws, P.o_rs), at<int>(ws, P.o_re), Rt);
   if (hipGetLastError() != hipSuccess) return TT_EHIP;
-  // the size of the virtual batch, on the host
-  std::vector<int64_t> hRt((size_t)P.T + 1);
-  if (hipMemcpyAsync(hRt.data(), Rt, (size_t)(P.T + 1) * 8, hipMemcpyDeviceToHost, s) != hipSuccess ||
-      hipStreamSynchronize(s) != hipSuccess)
-    return TT_EHIP;
-  int64_t U = hRt[P.T], Bp = 0;
-  for (int t = 0; t < P.T; ++t) Bp = std::max<int64_t>(Bp, hRt[t + 1] - hRt[t]);
-  if (U == 0) return TT_OK;
-  info[0] = U;
-  info[1] = Bp;
-  const long long nvb = (long long)P.T * Bp + 1;
+  // the virtual batch: one element per distinct index, Rt[T] of them (a device word: the
+  // host never reads it), sized here by its bounds -- nnz elements, vb bags per table
+  const int64_t vb = nnz;
+  const long long nvb = (long long)P.T * vb + 1;
   int64_t *voff = at<int64_t>(ws, P.o_voff);
   hipLaunchKernelGGL(k_dd_voff, dim3((unsigned)((nvb + DD_T - 1) / DD_T)), dim3(DD_T), 0, s, Rt,
-                     P.T, (int)Bp, voff);
+                     P.T, (int)vb, voff);
   if (hipGetLastError() != hipSuccess) return TT_EHIP;
-  // the virtual batch's grouping
-  return tt_bag_plan(&P.vdesc, at<int64_t>(ws, P.o_vidx), U, voff, Bp, nullptr, nullptr,
-                     at<char>(ws, P.o_ws2), P.ws2, dev_status, stream);
+  info[0] = nnz;
+  info[1] = vb;
+  // the virtual batch's grouping, its element count read on the device
+  return plan_devcount(&P.vdesc, at<int64_t>(ws, P.o_vidx), nnz, voff, vb, Rt + P.T,
+                       at<char>(ws, P.o_ws2), P.ws2, dev_status, stream);
 }
 
 static int backward_dedup(const tt_desc *desc, float *const cores[3], const int64_t *indices,
@@ -438,14 +433,14 @@ static int backward_dedup(const tt_desc *desc, float *const cores[3], const int6
   int rc = make_ddplan(desc, nnz, num_bags, &P);
   if (rc != TT_OK) return rc;
   if ((rc = check_ws_dd(P, ws, ws_bytes)) != TT_OK) return rc;
-  const int64_t U = info[0], Bp = info[1];
-  if (U < 0 || U > nnz || Bp < 0 || Bp > (nnz > 0 ? nnz : 1) || (U > 0) != (Bp > 0))
-    return TT_EINVAL;
+  // info: the virtual batch's bounds from tt_bag_plan_dedup (nnz elements and nnz bags
+  // per table; 0 and 0 for an empty batch)
+  if (info[0] != nnz || info[1] != nnz) return TT_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   float *Gu = at<float>(ws, P.o_gu);
-  const int64_t vb = Bp > 0 ? Bp : 1;
+  const int64_t U = nnz, vb = nnz;
   int64_t *vidx = at<int64_t>(ws, P.o_vidx), *voff = at<int64_t>(ws, P.o_voff);
-  if (U > 0) {
+  if (nnz > 0) {
     // the plans the passes check: the real batch's (this call's inputs) and the virtual one's
     int *rhdr = nullptr, *vhdr = nullptr;
     unsigned rfp = 0, vfp = 0;
@@ -464,17 +459,24 @@ static int backward_dedup(const tt_desc *desc, float *const cores[3], const int6
     tt_launch(K_DD_GU, k_dd_gu, dim3((unsigned)U), dim3(DD_T), 0, s,
               (const int *)at<int>(ws, P.o_rs), (const int *)at<int>(ws, P.o_re),
               (const int *)at<int>(ws, P.o_rtab), (const int64_t *)at<int64_t>(ws, P.o_Rt),
-              (int)Bp, P.D, (const float *)frag, Gu, (const int *)rhdr, rfp, vhdr, vfp,
+              P.T, (int)vb, P.D, (const float *)frag, Gu, (const int *)rhdr, rfp, vhdr, vfp,
               dev_status);
     if (hipGetLastError() != hipSuccess) return TT_EHIP;
   }
-  if (U == 0 && fill64(voff, (long long)P.T * vb + 1, 0, s) != TT_OK)  // an empty virtual batch
-    return TT_EHIP;
+  if (nnz == 0) {  // an empty batch: zero gradients, no update
+    if (!grad_cores) return TT_OK;
+    if (fill64(voff, P.T + 1, 0, s) != TT_OK) return TT_EHIP;  // T tables of one empty bag
+    return tt_bag_backward_grad(&P.vdesc, cores, vidx, 0, voff, 1, nullptr, nullptr, Gu,
+                                grad_cores, nullptr, at<char>(ws, P.o_ws2), P.ws2, dev_status,
+                                stream);
+  }
+  // the virtual batch's planned backward (its element count on the device: a batch with
+  // no valid index has no work item, the update leaves the cores alone and the gradient
+  // mode writes zeros)
   if (grad_cores)
-    return (U > 0 ? tt_bag_backward_grad_planned : tt_bag_backward_grad)(
-        &P.vdesc, cores, vidx, U, voff, vb, nullptr, nullptr, Gu, grad_cores, nullptr,
-        at<char>(ws, P.o_ws2), P.ws2, dev_status, stream);
-  if (U == 0) return TT_OK;
+    return tt_bag_backward_grad_planned(&P.vdesc, cores, vidx, U, voff, vb, nullptr, nullptr, Gu,
+                                        grad_cores, nullptr, at<char>(ws, P.o_ws2), P.ws2,
+                                        dev_status, stream);
   return tt_bag_backward_sgd_planned(&P.vdesc, cores, vidx, U, voff, vb, nullptr, nullptr, Gu, lr,
                                      at<char>(ws, P.o_ws2), P.ws2, dev_status, stream);
 }
@@ -487,6 +489,25 @@ int tt_bag_backward_sgd_dedup(const tt_desc *desc, float *const cores[3], const 
   if (!std::isfinite(lr)) return TT_EINVAL;
   return backward_dedup(desc, cores, indices, nnz, offsets, num_bags, per_sample_weights,
                         grad_out, lr, nullptr, info, ws, ws_bytes, dev_status, stream);
+}
+
+int tt_bag_dedup_counts(const tt_desc *desc, int64_t nnz, int64_t num_bags, const void *ws,
+                        size_t ws_bytes, int64_t *counts, void *stream) {
+  if (!counts) return TT_EINVAL;
+  DDPlan P;
+  int rc = make_ddplan(desc, nnz, num_bags, &P);
+  if (rc != TT_OK) return rc;
+  if ((rc = check_ws_dd(P, (void *)ws, ws_bytes)) != TT_OK) return rc;
+  if (nnz == 0) {
+    for (int t = 0; t <= P.T; ++t) counts[t] = 0;
+    return TT_OK;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t *Rt = at<int64_t>((void *)ws, P.o_Rt);
+  if (hipMemcpyAsync(counts, Rt, (size_t)(P.T + 1) * 8, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return TT_EHIP;
+  return TT_OK;
 }
 
 int tt_bag_backward_grad_dedup(const tt_desc *desc, const float *const cores[3],

@@ -105,6 +105,7 @@ struct DevArgs {
   // inputs / outputs
   const int64_t *idx;
   const int64_t *off;
+  const int64_t *nnz_dev;  // element count decided on the device (<= nnz), or null
   const float *psw;
   const int32_t *slots;
   float *crows;
@@ -223,6 +224,13 @@ inline void tt_launch(int id, void (*kernel)(KArgs...), dim3 grid, dim3 block, s
     hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
 }
 
+// The grouping of a batch whose element count only the device knows: nnz (host) bounds it,
+// *nnz_dev (device, read by the grouping kernels) is the count; positions from *nnz_dev on
+// are not elements.  Offsets end at *nnz_dev.  No host synchronisation.
+int plan_devcount(const tt_desc *desc, const int64_t *indices, int64_t nnz,
+                  const int64_t *offsets, int64_t num_bags, const int64_t *nnz_dev, void *ws,
+                  size_t ws_bytes, int32_t *dev_status, void *stream);
+
 // header pointer and fingerprint of the three-core plan of these arguments in ws (no
 // cache); TT_OK or the descriptor's rejection code
 int plan_identity(const tt_desc *desc, int64_t nnz, int64_t num_bags, const void *idx,
@@ -256,6 +264,14 @@ hipError_t launch_wgrad_hits(const DevArgs &a, hipStream_t s);
 hipError_t launch_bwd(const DevArgs &a, int RP, size_t lds, hipStream_t s);
 size_t fwd_lds_bytes(int RP, int JB, int P, int q3, int D, int sw);
 size_t bwd_lds_bytes(int RP, int JB, int P, int q3, int D, int nred);
+
+// the batch's element count in the grouping kernels: the host's, or the device word of a
+// batch sized on the device (at most the host's)
+__device__ __forceinline__ int elem_count(const DevArgs &a) {
+  if (!a.nnz_dev) return a.nnz;
+  const int64_t n = *a.nnz_dev;
+  return n < 0 ? 0 : (n < a.nnz ? (int)n : a.nnz);
+}
 
 // Work items of both contraction kernels: every overlap of a miss group with a
 // P-aligned piece of the final order.  Upper bound of their number:

@@ -175,6 +175,7 @@ static __device__ void tile_decode(const DevArgs &a, int blk, int *s_off, int *s
   }
   const int dropA = a.binsA - 1, dropB = a.binsB - 1, dropI = a.binsI3 - 1;
   const int64_t p23 = (int64_t)a.p2 * a.p3;
+  const int n = elem_count(a);
   bool bad_slot = false, bad_index = false;
 #pragma unroll
   for (int r = 0; r < RB / NT; ++r) {
@@ -184,7 +185,7 @@ static __device__ void tile_decode(const DevArgs &a, int blk, int *s_off, int *s
     x.bag = bag[r];
     x.posI3 = -1;
     x.dA = x.dB = x.dI = -1;
-    if (e >= a.nnz) continue;
+    if (e >= n) continue;
     const int t = a.T == 1 ? 0 : bag[r] / a.B;
     const int slot = sv[r];
     const int64_t i = iv[r];
@@ -215,10 +216,10 @@ static __device__ void tile_decode(const DevArgs &a, int blk, int *s_off, int *s
 // Offsets must be a CSR over [0, nnz]; checked grid-strided by the nblk blocks.
 template <int NT>
 static __device__ void check_offsets(const DevArgs &a, int blk) {
-  const int gt = blk * NT + threadIdx.x, gn = a.nblk * NT;
+  const int gt = blk * NT + threadIdx.x, gn = a.nblk * NT, n = elem_count(a);
   for (int k = gt; k <= a.NB; k += gn) {
     const int64_t o = a.off[k], o1 = a.off[min(k + 1, a.NB)];
-    if ((k == 0 && o != 0) || (k == a.NB && o != (int64_t)a.nnz) || (k < a.NB && o1 < o))
+    if ((k == 0 && o != 0) || (k == a.NB && o != (int64_t)n) || (k < a.NB && o1 < o))
       set_status(a.status, TT_DEV_BAD_OFFSETS);
   }
 }
@@ -369,10 +370,11 @@ static __device__ void tile_final(const DevArgs &a, int blk, unsigned short *lds
                                   const int *start, int ss, int so) {
   Rec x[RB / NT];
   int d[RB / NT], pos[RB / NT];
+  const int n = elem_count(a);
 #pragma unroll
   for (int r = 0; r < RB / NT; ++r) x[r] = load_rec(a.rec, min(tile_pos<NT>(blk, r), a.nnz - 1));
 #pragma unroll
-  for (int r = 0; r < RB / NT; ++r) d[r] = tile_pos<NT>(blk, r) < a.nnz ? x[r].dB : -1;
+  for (int r = 0; r < RB / NT; ++r) d[r] = tile_pos<NT>(blk, r) < n ? x[r].dB : -1;
   tile_place<NT>(d, pos, lds_c, a.binsB, start, ss, so);
 #pragma unroll
   for (int r = 0; r < RB / NT; ++r) {
@@ -606,7 +608,7 @@ __global__ __launch_bounds__(CT) void k_route_coop(DevArgs a) {
   // ---- work items (each block writes its share); final order: the orderA tiles placed
   //      by (t,i2)
   tile_starts2(a.histB, a.binsB, startI, gsI, nullptr, 0, nullptr, nullptr, blk, s_scan);
-  if (tid == 0) gsI[a.binsB] = a.nnz;
+  if (tid == 0) gsI[a.binsB] = elem_count(a);
   __syncthreads();
   build_items(a, gsI, startA, s_scan, blk, nblk);
   tile_final<CT>(a, blk, lds_c, startI, 1, 0);
@@ -631,7 +633,7 @@ __global__ __launch_bounds__(RT) void k_route_a(DevArgs a) {
   for (int k = blk * RT + tid; k < a.binsB * a.nblk; k += a.nblk * RT) a.histB[k] = 0;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
-    if (el[r].e < a.nnz) a.einfo[el[r].e] = make_int4(el[r].dA, el[r].dB, el[r].dI, el[r].bag);
+    if (el[r].e < elem_count(a)) a.einfo[el[r].e] = make_int4(el[r].dA, el[r].dB, el[r].dI, el[r].bag);
   int d[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) d[r] = el[r].dI;
@@ -654,13 +656,13 @@ __global__ __launch_bounds__(RT) void k_route_b(DevArgs a) {
   a.epoch = launch_tag(a, a.hdr + H_REPOCH);  // this grouping's tag
   extern __shared__ unsigned short lds_c[];  // [4][max(binsI3, binsA)]
   __shared__ int s_scan[RT / 64 + 1];
-  const int blk = blockIdx.x;
+  const int blk = blockIdx.x, n = elem_count(a);
   Rec el[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int e = tile_pos<RT>(blk, r), ec = min(e, a.nnz - 1);
     const int4 info = a.einfo[ec];
-    const bool v = e < a.nnz;
+    const bool v = e < n;
     el[r].e = e;
     el[r].dA = v ? info.x : -1;
     el[r].dB = v ? info.y : -1;
@@ -680,7 +682,7 @@ __global__ __launch_bounds__(RT) void k_route_b(DevArgs a) {
   if (!last_block(&a.ctr[1], a.nblk, a.epoch)) return;
   block_exclusive_scan(a.histB, a.binsB * a.nblk, s_scan);
   for (int d = threadIdx.x; d < a.binsB; d += RT) a.grp_off[d] = a.histB[(size_t)d * a.nblk];
-  if (threadIdx.x == 0) a.grp_off[a.binsB] = a.nnz;
+  if (threadIdx.x == 0) a.grp_off[a.binsB] = elem_count(a);
   for (int k = threadIdx.x; k <= P_MAX; k += RT) a.hdr[H_SIZE0 + k] = 0;
   __threadfence();
   __syncthreads();

@@ -4,11 +4,10 @@ same object, so the launch configuration they check is the one the benchmark mea
 Every batch is grouped (tt_bag_plan, or tt_bag_plan_dedup for the backward over distinct
 indices), then runs the planned forward and the planned backward.  Pipelined (default):
 the grouping of batch i+AHEAD is enqueued on a second stream right after the forward of
-batch i (after the backward with the distinct-index grouping, which waits on the host) and
-runs beside the backward; the host waits for a batch's grouping before it enqueues the
-batch's forward.  Two batches ahead, a grouping has a whole step more to finish than the
-host needs to reach it, so the host does not wait on it; with the distinct-index grouping,
-or a cache and fewer than three batches, it is one batch ahead.  A grouping must not
+batch i and runs beside the backward; the host waits for a batch's grouping before it
+enqueues the batch's forward.  Two batches ahead, a grouping has a whole step more to
+finish than the host needs to reach it, so the host does not wait on it; with a cache and
+fewer than three batches it is one batch ahead.  A grouping must not
 overwrite a
 workspace before the last step that used it has finished.  An event recorded on the main
 stream costs several microseconds of that stream's time, so it is recorded only after every
@@ -86,7 +85,7 @@ class TrainLoop:
         # which is >= j - ahead - every; batch j's workspace j % (ahead + every) was last
         # used by step j - ahead - every, so that event covers it.
         self.every = 1 if cache is not None else DONE_EVERY
-        self.ahead = 2 if (pipeline and not dedup and (cache is None or len(batches) >= 3)) else 1
+        self.ahead = 2 if (pipeline and (cache is None or len(batches) >= 3)) else 1
         self.wss = [make_ws() for _ in range(self.ahead + self.every if pipeline else 1)]
         self.main = torch.cuda.current_stream()
         self.side = torch.cuda.Stream() if pipeline else self.main  # default priority
@@ -175,7 +174,7 @@ class TrainLoop:
             abi.tt_bag_plan_d(self.desc, b["indices"], b["offsets"], self.B,
                               b["per_sample_weights"], ws=ws, dev_status=self.status,
                               stream=self.side)
-        elif self.dedup:  # host-synchronous: returns the size of the distinct-index batch
+        elif self.dedup:  # returns the virtual batch's bounds (the count stays on the device)
             _, self.infos[i] = abi.tt_bag_plan_dedup(self.desc, b["indices"], b["offsets"], self.B,
                                                      b["per_sample_weights"], ws=ws,
                                                      dev_status=self.status, stream=self.side)
@@ -251,7 +250,7 @@ class TrainLoop:
             abi.tt_bag_forward(self.desc, self.g, b["indices"], b["offsets"], self.B, w,
                                cache=cv, out=self.out, ws=ws, dev_status=self.status,
                                planned=True)
-        if self.pipeline and not self.dedup:
+        if self.pipeline:
             # the grouping `ahead` batches on starts now, beside this batch's backward
             self.cvs[i + self.ahead] = self._plan(i + self.ahead)
         if self.dcore:
@@ -295,8 +294,4 @@ class TrainLoop:
                 ev = torch.cuda.Event()
                 ev.record(self.main)
                 self.ev_done[i] = ev
-            if self.dedup:
-                # the distinct-index grouping waits on the host for its size, so it is
-                # enqueued after this backward, which then runs meanwhile
-                self.cvs[i + 1] = self._plan(i + 1)
         return i

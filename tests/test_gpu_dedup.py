@@ -1,8 +1,10 @@
 """Backward over distinct indices (tt_bag_plan_dedup + tt_bag_backward_*_dedup): the
 gradients and the SGD step against the oracle on small Zipf-skewed batches (two tables,
-weights, sum and mean pooling, empty bags), the distinct-index counts bit-exact against
-numpy, and, at the skewed and table-batched workloads' full sizes, against the
-three-core backward over every element."""
+weights, sum and mean pooling, empty bags), the distinct-index counts (kept on the device,
+read by the diagnostic query) bit-exact against numpy, and, at the skewed and
+table-batched workloads' full sizes, against the three-core backward over every element.
+The plan does not synchronise the host: a captured plan + backward replays like the
+eager calls."""
 import numpy as np
 import pytest
 import torch
@@ -29,11 +31,13 @@ def _host(t, cores, k):
     return out
 
 
-def _distinct(idx, off, B, T):
+def _check_counts(desc, nnz, B, ws, idx, off, T):
+    """The device's distinct-index counts (the diagnostic query) bit-exact against numpy."""
+    got = abi.tt_bag_dedup_counts(desc, nnz, B, ws)
     bag = np.searchsorted(off, np.arange(len(idx)), side="right") - 1
     t = bag // B
     per = [len(np.unique(idx[t == x])) for x in range(T)]
-    return sum(per), max(per) if per else 0
+    assert got == list(np.concatenate([[0], np.cumsum(per)])), (got, per)
 
 
 @pytest.mark.parametrize("pooling", [0, 1])
@@ -58,8 +62,9 @@ def test_dedup_matches_oracle_small(pooling):
     d_w, d_dY = torch.from_numpy(w).cuda(), torch.from_numpy(dY).cuda()
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
     ws, info = abi.tt_bag_plan_dedup(desc, d_idx, d_off, B, d_w, dev_status=st)
-    assert info == _distinct(idx, off, B, T)
-    assert info[0] < len(idx) // 2
+    assert info == (len(idx), len(idx))
+    _check_counts(desc, len(idx), B, ws, idx, off, T)
+    assert abi.tt_bag_dedup_counts(desc, len(idx), B, ws)[T] < len(idx) // 2
     Y = abi.tt_bag_forward(desc, g, d_idx, d_off, B, d_w, ws=ws, dev_status=st, planned=True)
     Yref = oracle.forward(p, q, ranks, E, cores, idx, off, B, per_sample_weights=w,
                           pooling=pooling)
@@ -106,7 +111,9 @@ def test_dedup_full_size_matches_every_element_backward(name):
     d_w = None if b["per_sample_weights"] is None else torch.from_numpy(b["per_sample_weights"]).cuda()
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
     ws, info = abi.tt_bag_plan_dedup(desc, d_idx, d_off, B, d_w, dev_status=st)
-    assert info == _distinct(b["indices"], b["offsets"], B, wl.num_tables)
+    nnz = len(b["indices"])
+    assert info == (nnz, nnz)  # the bounds: the counts stay on the device
+    _check_counts(desc, nnz, B, ws, b["indices"], b["offsets"], wl.num_tables)
     gd = abi.tt_bag_backward_grad_dedup(desc, g, d_idx, d_off, B, d_dY, info,
                                         per_sample_weights=d_w, ws=ws, dev_status=st)
     ge, _ = abi.tt_bag_backward_grad(desc, g, d_idx, d_off, B, d_dY, per_sample_weights=d_w)
@@ -176,3 +183,46 @@ def test_dedup_backward_refuses_another_batchs_plan():
     for k in range(3):
         got = _host(g[k], cores, k)[0].astype(np.float64)
         assert rel_err(got - cores[0][k], -wl.lr * grads[0][k]) <= TOL, k
+
+
+def test_dedup_plan_and_backward_replay_from_a_graph():
+    """The distinct-index plan does not wait on the host, so the plan and the SGD backward
+    can be captured into one HIP graph: three replays (with eager work and a
+    synchronisation between them) leave the cores bit for bit equal to the same calls made
+    eagerly, and the counts on the device equal numpy's."""
+    print("case dedup graph replay", flush=True)
+    wl = W.custom(p=(6, 5, 7), q=(2, 4, 2), ranks=(8, 6), bags_per_table=30,
+                  lengths=("fixed", 6), dist=("zipf", 1.2), lr=0.05)
+    cores = W.make_cores(wl)
+    desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E)
+    b = W.make_batch(wl, 3)
+    idx, off = torch.from_numpy(b["indices"]).cuda(), torch.from_numpy(b["offsets"]).cuda()
+    dY = torch.from_numpy(b["grad_out"]).cuda()
+    nnz = len(b["indices"])
+    g_e = [_dev(cores, k) for k in range(3)]
+    g_c = [x.clone() for x in g_e]
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws_e = abi.workspace_dedup(desc, nnz, 30, idx.device)
+    ws_c = abi.workspace_dedup(desc, nnz, 30, idx.device)
+    info = (nnz, nnz)
+    cap = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=cap):
+        _, ic = abi.tt_bag_plan_dedup(desc, idx, off, 30, ws=ws_c, dev_status=st, stream=cap)
+        abi.tt_bag_backward_sgd_dedup(desc, g_c, idx, off, 30, dY, wl.lr, info, ws=ws_c,
+                                      dev_status=st, stream=cap)
+    assert ic == info
+    for rep in range(3):
+        _, ie = abi.tt_bag_plan_dedup(desc, idx, off, 30, ws=ws_e, dev_status=st)
+        abi.tt_bag_backward_sgd_dedup(desc, g_e, idx, off, 30, dY, wl.lr, ie, ws=ws_e,
+                                      dev_status=st)
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0, rep
+        for k in range(3):
+            assert torch.equal(g_c[k], g_e[k]), (rep, k)
+        _check_counts(desc, nnz, 30, ws_c, b["indices"], b["offsets"], 1)
+        # eager work between replays
+        (g_e[0] * 2.0).sum().item()
