@@ -105,14 +105,16 @@ void k_bwd(DevArgs a) {
   note_placement(s_pl);
   lds_barrier();
   if (plan != (int)a.plan_fp || wi >= nitems) return;
-  const int grp = M.grp, s0 = M.s0, n_el = M.n_el, nI = M.nI, nP = M.nP;
-  const int t = grp / a.p2;
+  // the record's counts are the same for the whole workgroup: scalar registers
+  const int grp = wave_uniform(M.grp), s0 = wave_uniform(M.s0), n_el = wave_uniform(M.n_el);
+  const int nI = wave_uniform(M.nI), nP = wave_uniform(M.nP);
+  const int t = wave_uniform(M.t);
   const size_t W1 = (size_t)q1 * R1, W3 = (size_t)R2 * q3;
   const size_t slice2 = (size_t)R1 * q2 * R2;
   const float *G2g = a.G2 + (size_t)grp * slice2;
   const float *G1t = a.G1 + (size_t)t * a.p1 * W1;
   const float *G3t = a.G3 + (size_t)t * a.p3 * W3;
-  float *part2 = a.part2 + (size_t)M.item * slice2;  // keyed by the item, not the slot
+  float *part2 = a.part2 + (size_t)wave_uniform(M.item) * slice2;  // keyed by the item
 
   // G2 columns [j0, j0 + nj) -> LDS as G2^T blocks, STAGE_U loads per thread per batch
   auto load2 = [&](int j0, int nj, int base, float *v) {
@@ -197,6 +199,28 @@ void k_bwd(DevArgs a) {
   float aG[4][NM];       // A1[row = 16mb + 4g + sr][r1 = 16mr + c] (dG2)
   // G1 rows of the wave's M-block: aT as 16-byte vectors when the ranks fill RP
   auto load_g1 = [&](bool vec) {
+    if (F44) {
+      // q1 = 4: row r of the M-block is j1 = r % 4 of pair 4 mb + r / 4, so lane group g's
+      // rows 4g .. 4g+3 are the four j1 of pair 4 mb + g (offsets under 2^21: i1 < 2^13)
+      const unsigned oA = __umul24((unsigned)M.pr_i1[min(mb * 4 + (c >> 2), nP - 1)] * 4u +
+                                       (unsigned)(c & 3), (unsigned)R1);
+      const unsigned oB = __umul24((unsigned)M.pr_i1[min(mb * 4 + g, nP - 1)] * 4u, (unsigned)R1);
+      if (vec) {
+#pragma unroll
+        for (int k4 = 0; k4 < KS / 4; ++k4) {
+          const float4 x = *(const float4 *)&G1t[oA + g * KS + 4 * k4];
+          aT[4 * k4] = x.x; aT[4 * k4 + 1] = x.y; aT[4 * k4 + 2] = x.z; aT[4 * k4 + 3] = x.w;
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) aT[ks] = G1t[oA + min(g * KS + ks, R1 - 1)];
+      }
+#pragma unroll
+      for (int sr = 0; sr < 4; ++sr)
+#pragma unroll
+        for (int mr = 0; mr < NM; ++mr) aG[sr][mr] = G1t[oB + sr * R1 + min(16 * mr + c, R1 - 1)];
+      return;
+    }
     const int row = mb * 16 + c;
     const int pr = row >> a.lq1, j1 = row & (q1 - 1);
     const float *src = G1t + ((size_t)M.pr_i1[min(pr, nP - 1)] * q1 + j1) * R1;
@@ -232,10 +256,12 @@ void k_bwd(DevArgs a) {
     constexpr int SV = 2;
     float *sWY = rep ? sYe : sGu;
     const int n2 = nj0 * RP * RP / 4, n3 = nI * RP, D4 = D >> 2, nY = n_el * D4;
+    // 32-bit offsets from the slices' bases (a G2 slice is under 2^18 floats, a G3 table
+    // under 2^21 here)
     auto ld2 = [&](int i4) {
       const int jj = i4 >> (2 * LRP - 2), r1 = (i4 >> (LRP - 2)) & (RP - 1);
       const int r2 = (i4 & (RP / 4 - 1)) * 4;
-      return *(const float4 *)&G2g[((size_t)r1 * q2 + jj) * R2 + r2];
+      return *(const float4 *)&G2g[((__umul24((unsigned)r1, (unsigned)q2) + jj) << LRP) + r2];
     };
     auto st2 = [&](int i4, float4 x) {
       const int jj = i4 >> (2 * LRP - 2), r1 = (i4 >> (LRP - 2)) & (RP - 1);
@@ -244,25 +270,33 @@ void k_bwd(DevArgs a) {
       d[0] = x.x; d[LD] = x.y; d[2 * LD] = x.z; d[3 * LD] = x.w;
     };
     auto ld3 = [&](int i4) {
-      return *(const float4 *)&G3t[M.it_i3[i4 >> LRP] * (int)W3 + (i4 & (RP - 1)) * 4];
+      return *(const float4 *)&G3t[((unsigned)M.it_i3[i4 >> LRP] << (LRP + 2)) +
+                                   (i4 & (RP - 1)) * 4];  // (W3 = 4 RP)
     };
     // vector i4 = (q, d4): row q of sWY -- element q in position order, or, with no repeated
     // index, item q (whose one element sits at item-major slot q)
-    auto elem_of = [&](int q) { return rep ? q : (int)M.e_perm[q]; };
-    auto ldY = [&](int i4) {
-      const int q = i4 / D4, d4 = i4 - q * D4;
-      return *(const float4 *)&a.dY[(size_t)M.e_bag[elem_of(q)] * D + d4 * 4];
+    auto row_of = [&](int i4) { return fdiv(i4 << 2, a.mD); };  // i4 / D4 (4 i4 < P D < 2^16)
+    auto elem_of = [&](int i4) {
+      const int q = row_of(i4);
+      return rep ? q : (int)M.e_perm[q];
     };
-    auto stY = [&](int i4, float4 y) {
-      const float w = M.e_w[elem_of(i4 / D4)];
+    auto ldY = [&](int i4, int e) {
+      const int d4 = i4 - (int)__umul24((unsigned)row_of(i4), (unsigned)D4);
+      return *(const float4 *)&a.dY[(size_t)M.e_bag[e] * D + d4 * 4];
+    };
+    auto stY = [&](int i4, int e, float4 y) {
+      const float w = M.e_w[e];
       *(float4 *)&sWY[4 * i4] = make_float4(w * y.x, w * y.y, w * y.z, w * y.w);
     };
     float4 v2[SV], v3[SV], vy[SV];
+    int ey[SV];
 #pragma unroll
     for (int u = 0; u < SV; ++u) {
+      const int iy = min(tid + u * WG, nY - 1);
+      ey[u] = elem_of(iy);
       v2[u] = ld2(min(tid + u * WG, n2 - 1));
       v3[u] = ld3(min(tid + u * WG, n3 - 1));
-      vy[u] = ldY(min(tid + u * WG, nY - 1));
+      vy[u] = ldY(iy, ey[u]);
     }
     load_g1(true);
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -274,14 +308,17 @@ void k_bwd(DevArgs a) {
         *(float4 *)&sG3[4 * i4] = v3[u];
         *(float4 *)&sdA3[4 * i4] = z4;
       }
-      if (i4 < nY) stY(i4, vy[u]);
+      if (i4 < nY) stY(i4, ey[u], vy[u]);
     }
     for (int i4 = tid + SV * WG; i4 < n2; i4 += WG) st2(i4, ld2(i4));
     for (int i4 = tid + SV * WG; i4 < n3; i4 += WG) {
       *(float4 *)&sG3[4 * i4] = ld3(i4);
       *(float4 *)&sdA3[4 * i4] = z4;
     }
-    for (int i4 = tid + SV * WG; i4 < nY; i4 += WG) stY(i4, ldY(i4));
+    for (int i4 = tid + SV * WG; i4 < nY; i4 += WG) {
+      const int e = elem_of(i4);
+      stY(i4, e, ldY(i4, e));
+    }
   } else {
     float v2[STAGE_U], v3[STAGE_U], vy[STAGE_U];
     load2(0, nj0, tid, v2);

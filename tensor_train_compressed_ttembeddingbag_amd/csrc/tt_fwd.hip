@@ -130,9 +130,11 @@ __device__ __forceinline__ void fwd_item(const DevArgs &a) {
     return;
   }
   lds_barrier();
-  const int grp = M.grp, n_el = M.n_el, nI = M.nI, nP = M.nP;
+  // the record's counts are the same for the whole workgroup: scalar registers
+  const int grp = wave_uniform(M.grp), n_el = wave_uniform(M.n_el), nI = wave_uniform(M.nI);
+  const int nP = wave_uniform(M.nP);
   const int wp = placed_mblock<NW>(s_pl);  // this wave's M-block (MBW = 1)
-  const int t = grp / a.p2;
+  const int t = wave_uniform(M.t);
   const float *G2g = a.G2 + (size_t)grp * R1 * q2 * R2;  // slice [r1][j2][r2]
   const size_t W3 = (size_t)R2 * q3;
   const float *G3t = a.G3 + (size_t)t * a.p3 * W3;

@@ -64,7 +64,8 @@ constexpr int META_INTS = 192;  // 768 bytes per work item
 struct WorkMeta {
   int n_el, nI, nP, grp, s0;
   int item;                         // the work item's index (its slot is its workgroup)
-  int pad[2];
+  int t;                            // the table of its group
+  int pad;
   int e_bag[P_MAX];                 // bag of each element
   float e_w[P_MAX];                 // its weight (times 1 / length with mean pooling)
   short pr_i1[P_MAX];               // i1 of each pair (inside its table)

@@ -91,22 +91,26 @@ __device__ __forceinline__ void note_placement(int *s_pl) {  // before a barrier
   if ((threadIdx.x & 63) == 0)
     s_pl[threadIdx.x >> 6] = (int)__builtin_amdgcn_s_getreg((5 << 11) | 4);  // HW_ID[5:0]
 }
+// the same value on every lane of the wave, held in a scalar register (values read from
+// LDS or derived from threadIdx.x / 64 that the compiler cannot prove uniform otherwise)
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 template <int NWAVES>
 __device__ __forceinline__ int placed_mblock(const int *s_pl) {  // after the barrier
-  const int w = threadIdx.x >> 6;
-  int cnt[4] = {0, 0, 0, 0}, slot0 = 16;
+  const int w = wave_uniform(threadIdx.x >> 6);
+  const int my = wave_uniform((s_pl[w] >> 4) & 3);
+  // waves per SIMD packed 8 bits each, the lowest wave slot on SIMD 0, and this wave's rank
+  // among the waves of its SIMD (all uniform over the wave)
+  unsigned per = 0u;
+  int slot0 = 16, rank = 0;
 #pragma unroll
   for (int v = 0; v < NWAVES; ++v) {
-    const int sm = (s_pl[v] >> 4) & 3;
-    cnt[sm] += 1;
-    if (sm == 0) slot0 = min(slot0, s_pl[v] & 15);
+    const int x = wave_uniform(s_pl[v]), sm = (x >> 4) & 3;
+    per += 1u << (8 * sm);
+    if (sm == 0) slot0 = min(slot0, x & 15);
+    rank += (v < w && sm == my) ? 1 : 0;
   }
-  if (cnt[0] * 4 != NWAVES || cnt[1] * 4 != NWAVES || cnt[2] * 4 != NWAVES ||
-      cnt[3] * 4 != NWAVES)
-    return w;
-  const int my = (s_pl[w] >> 4) & 3;
-  int rank = 0;
-  for (int v = 0; v < w; ++v) rank += ((s_pl[v] >> 4) & 3) == my;
+  if (per != (unsigned)(NWAVES / 4) * 0x01010101u || NWAVES % 4) return w;
   const int rot = slot0 >= 2 ? 2 : 0;
   return rank * 4 + ((my - rot) & 3);
 }

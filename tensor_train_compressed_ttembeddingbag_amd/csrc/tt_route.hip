@@ -862,7 +862,7 @@ __global__ __launch_bounds__(64 * META_WAVES) void k_meta(DevArgs a) {
   }
   if (lane == 0) {
     const int nI = __popcll(r.mi), nP = __popcll(r.mp);
-    M.n_el = n_el; M.nI = nI; M.nP = nP; M.grp = grp; M.s0 = s0; M.item = wi;
+    M.n_el = n_el; M.nI = nI; M.nP = nP; M.grp = grp; M.s0 = s0; M.item = wi; M.t = t;
     M.it_beg[nI] = (unsigned char)n_el;
     M.pr_it[nP] = (unsigned char)nI;
   }
