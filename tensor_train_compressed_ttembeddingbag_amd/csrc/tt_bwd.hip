@@ -547,34 +547,58 @@ void k_bwd(DevArgs a) {
       for (int rr = 0; rr < NW / nred; ++rr) {
         if (mb / nred == rr) {
           float *slot = sRed + (size_t)(mb % nred) * RP * LD;
+          // the slot's partial sums of one row of tiles (all of them up to RP = 32) read
+          // before any is written
+          constexpr int MRB = NM <= 2 ? NM : 1;
 #pragma unroll
-          for (int mr = 0; mr < NM; ++mr)
+          for (int mr0 = 0; mr0 < NM; mr0 += MRB) {
+            float4 o[MRB][NM];
+            if (rr > 0)
 #pragma unroll
-            for (int m2 = 0; m2 < NM; ++m2) {
-              float4 *q = (float4 *)&slot[(16 * m2 + c) * LD + 16 * mr + 4 * g];
-              float4 x = make_float4(gacc[mr][m2][0], gacc[mr][m2][1], gacc[mr][m2][2],
-                                     gacc[mr][m2][3]);
-              if (rr > 0) {
-                const float4 o = *q;
-                x.x += o.x; x.y += o.y; x.z += o.z; x.w += o.w;
+              for (int mr = 0; mr < MRB; ++mr)
+#pragma unroll
+                for (int m2 = 0; m2 < NM; ++m2)
+                  o[mr][m2] = *(const float4 *)&slot[(16 * m2 + c) * LD + 16 * (mr0 + mr) + 4 * g];
+#pragma unroll
+            for (int mr = 0; mr < MRB; ++mr)
+#pragma unroll
+              for (int m2 = 0; m2 < NM; ++m2) {
+                const f4 &ga = gacc[mr0 + mr][m2];
+                float4 x = make_float4(ga[0], ga[1], ga[2], ga[3]);
+                if (rr > 0) {
+                  x.x += o[mr][m2].x; x.y += o[mr][m2].y; x.z += o[mr][m2].z; x.w += o[mr][m2].w;
+                }
+                *(float4 *)&slot[(16 * m2 + c) * LD + 16 * (mr0 + mr) + 4 * g] = x;
               }
-              *q = x;
-            }
+          }
         }
         lds_barrier();
       }
-      // thread t: r2 = t mod RP, r1 = 4 (t / RP) .. +3, summed over the slots in order; the
-      // partial keeps the slice layout [r1][j2][r2] (consecutive threads, consecutive r2)
+      // thread t: r2 = t mod RP, r1 = 4 (t / RP) .. +3, summed over the slots in order (all
+      // slots read at once); the partial keeps the slice layout [r1][j2][r2] (consecutive
+      // threads, consecutive r2; offsets inside the slice fit 32 bits)
       for (int t4 = tid; t4 < RP * RP / 4; t4 += WG) {
         const int r2 = t4 & (RP - 1), r1 = (t4 >> LRP) * 4;
-        float4 acc = *(const float4 *)&sRed[r2 * LD + r1];
-        for (int k = 1; k < nred; ++k) {
-          const float4 o = *(const float4 *)&sRed[(size_t)k * RP * LD + r2 * LD + r1];
-          acc.x += o.x; acc.y += o.y; acc.z += o.z; acc.w += o.w;
+        constexpr int KF = F44 ? 4 : 1;  // slots in flight (the F44 instances have the room)
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int k0 = 0; k0 < nred; k0 += KF) {
+          float4 o[KF];
+#pragma unroll
+          for (int k = 0; k < KF; ++k)
+            if (k0 + k < nred)
+              o[k] = *(const float4 *)&sRed[(size_t)(k0 + k) * RP * LD + r2 * LD + r1];
+#pragma unroll
+          for (int k = 0; k < KF; ++k)
+            if (k0 + k < nred) {
+              if (k0 + k == 0) acc = o[0];
+              else { acc.x += o[k].x; acc.y += o[k].y; acc.z += o[k].z; acc.w += o[k].w; }
+            }
         }
-        if (r2 < R2) {
-          float *dst = part2 + ((size_t)r1 * q2 + j2) * R2 + r2;
-          const size_t st = (size_t)q2 * R2;
+        const unsigned st = (unsigned)(q2 * R2);
+        float *dst = part2 + (__umul24((unsigned)r1, (unsigned)q2) + j2) * (unsigned)R2 + r2;
+        if (R1 == RP && R2 == RP) {  // (every r1, r2 of the slot is in the slice)
+          dst[0] = acc.x; dst[st] = acc.y; dst[2 * st] = acc.z; dst[3 * st] = acc.w;
+        } else if (r2 < R2) {
           if (r1 + 0 < R1) dst[0] = acc.x;
           if (r1 + 1 < R1) dst[st] = acc.y;
           if (r1 + 2 < R1) dst[2 * st] = acc.z;

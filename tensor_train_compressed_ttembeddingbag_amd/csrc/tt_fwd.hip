@@ -198,13 +198,16 @@ __device__ __forceinline__ void fwd_item(const DevArgs &a) {
     }
   };
   float bv[MBW][KS];
+  const float *G1t = a.G1 + (size_t)t * a.p1 * q1 * R1;  // the table's core 1
   auto load_g1 = [&](bool vec) {
 #pragma unroll
     for (int mbi = 0; mbi < MBW; ++mbi) {
       const int row = (wp + mbi * NW) * 16 + c;
       const int pr = row >> a.lq1, j1 = row & (q1 - 1);
+      // a 32-bit offset inside the table (i1 < 2^13, q1 R1 <= 2^12)
       const float *src =
-          a.G1 + ((size_t)(t * a.p1 + M.pr_i1[min(pr, nP - 1)]) * q1 + j1) * R1;
+          G1t + __umul24((unsigned)M.pr_i1[min(pr, nP - 1)] * (unsigned)q1 + (unsigned)j1,
+                         (unsigned)R1);
       if (vec) {
 #pragma unroll
         for (int k4 = 0; k4 < KS / 4; ++k4) {
@@ -223,10 +226,12 @@ __device__ __forceinline__ void fwd_item(const DevArgs &a) {
     // item's G3 slice per lane; the LDS layouts stay those of the general path
     constexpr int SV = 2;
     const int n2 = nj0 * RP * RP / 4, n3 = nI * RP;
+    // 32-bit offsets from the slices' bases (a G2 slice is under 2^18 floats, a G3 table
+    // under 2^21 here)
     auto ld2 = [&](int i4) {
       const int jj = i4 >> (2 * LRP - 2), r1 = (i4 >> (LRP - 2)) & (RP - 1);
       const int r2 = (i4 & (RP / 4 - 1)) * 4;
-      return *(const float4 *)&G2g[((size_t)r1 * q2 + jj) * R2 + r2];
+      return *(const float4 *)&G2g[((__umul24((unsigned)r1, (unsigned)q2) + jj) << LRP) + r2];
     };
     auto st2 = [&](int i4, float4 x) {
       const int jj = i4 >> (2 * LRP - 2), r1 = (i4 >> (LRP - 2)) & (RP - 1);
@@ -235,7 +240,8 @@ __device__ __forceinline__ void fwd_item(const DevArgs &a) {
       d[0] = x.x; d[LD] = x.y; d[2 * LD] = x.z; d[3 * LD] = x.w;
     };
     auto ld3 = [&](int i4) {
-      return *(const float4 *)&G3t[M.it_i3[i4 >> LRP] * (int)W3 + (i4 & (RP - 1)) * 4];
+      return *(const float4 *)&G3t[((unsigned)M.it_i3[i4 >> LRP] << (LRP + 2)) +
+                                   (i4 & (RP - 1)) * 4];  // (W3 = 4 RP)
     };
     auto st3 = [&](int i4, float4 x) {  // LDS [item][j3][r2]
       float *d = &sG3[(size_t)(i4 >> LRP) * 4 * RP + (i4 & (RP - 1))];
