@@ -929,6 +929,50 @@ def prepare_forward(desc: TTDesc, cores, indices, offsets, num_bags: int, per_sa
                                                      dev_status, view))
 
 
+def prepare_plan_dedup(desc: TTDesc, indices, offsets, num_bags: int, per_sample_weights=None,
+                       ws=None, dev_status=None, stream=None):
+    """tt_bag_plan_dedup as a prepared call.  Returns (call, info): info = the virtual
+    batch's bounds (nnz, nnz) that every replay writes, for prepare_backward_dedup."""
+    _need(indices, torch.int64, "indices")
+    _need(offsets, torch.int64, "offsets")
+    if per_sample_weights is not None:
+        _need(per_sample_weights, torch.float32, "per_sample_weights")
+    _batch_sizes(desc, indices, offsets, num_bags, per_sample_weights)
+    _need(ws, torch.uint8, "ws")
+    if dev_status is not None:
+        _need(dev_status, torch.int32, "dev_status")
+    out = (ctypes.c_int64 * 2)()
+    args = (ctypes.byref(desc), _ptr(indices), indices.numel(), _ptr(offsets), int(num_bags),
+            _ptr(per_sample_weights), _ptr(ws), ws.numel(), _ptr(dev_status), out,
+            _stream_handle(stream, indices))
+    n = int(indices.numel())
+    return (Prepared("tt_bag_plan_dedup", args, (desc, indices, offsets, per_sample_weights, ws,
+                                                 dev_status, out)), (n, n))
+
+
+def prepare_backward_dedup(desc: TTDesc, cores, indices, offsets, num_bags: int, grad_out, info,
+                           update: str = "sgd", lr: float = 0.0, aux=None,
+                           per_sample_weights=None, ws=None, dev_status=None,
+                           stream=None) -> Prepared:
+    """The backward over distinct indices as a prepared call: update "sgd"
+    (tt_bag_backward_sgd_dedup) or "grad" (aux = the gradient outputs,
+    tt_bag_backward_grad_dedup)."""
+    _dedup_args(desc, indices, offsets, num_bags, grad_out, per_sample_weights, ws, dev_status)
+    core_ptrs = _cores(cores, desc)
+    head = (ctypes.byref(desc), core_ptrs, _ptr(indices), indices.numel(), _ptr(offsets),
+            int(num_bags), _ptr(per_sample_weights), _ptr(grad_out))
+    inf = _info(info)
+    tail = (inf, _ptr(ws), ws.numel(), _ptr(dev_status), _stream_handle(stream, indices))
+    keep = [desc, core_ptrs, cores, indices, offsets, per_sample_weights, grad_out, ws,
+            dev_status, inf]
+    if update == "sgd":
+        return Prepared("tt_bag_backward_sgd_dedup", head + (float(lr),) + tail, keep)
+    if update == "grad":
+        gp = _cores(aux, desc, "grad_cores")
+        return Prepared("tt_bag_backward_grad_dedup", head + (gp,) + tail, keep + [gp, aux])
+    raise ValueError("the backward over distinct indices updates by sgd or grad")
+
+
 def prepare_backward(desc: TTDesc, cores, indices, offsets, num_bags: int, grad_out,
                      update: str = "sgd", lr: float = 0.0, eps: float = 0.0, aux=None,
                      aux_rows=None, per_sample_weights=None, cache=None, ws=None,

@@ -95,13 +95,14 @@ class TrainLoop:
         self.next = 0
         self.cvs = {}
         self.infos = {}
-        # three-core calls of the plain path are checked and marshalled once per (batch,
-        # workspace) and then replayed (abi.prepare_*): the host work per step is the C calls
-        self.fast = not self.dcore and not dedup
+        # three-core calls (the plain path and the backward over distinct indices) are checked
+        # and marshalled once per (batch, workspace) and then replayed (abi.prepare_*): the
+        # host work per step is the C calls
+        self.fast = not self.dcore
         self.prepared = {}
         self.wait_s = 0.0  # host time spent waiting for groupings
         self.graph = graph
-        if graph and not (pipeline and self.fast and cache is None):
+        if graph and not (pipeline and self.fast and cache is None and not dedup):
             raise ValueError("a captured loop takes the plain pipelined path: three cores, "
                              "no cache, no distinct-index backward")
         if graph:
@@ -174,10 +175,15 @@ class TrainLoop:
             abi.tt_bag_plan_d(self.desc, b["indices"], b["offsets"], self.B,
                               b["per_sample_weights"], ws=ws, dev_status=self.status,
                               stream=self.side)
-        elif self.dedup:  # returns the virtual batch's bounds (the count stays on the device)
-            _, self.infos[i] = abi.tt_bag_plan_dedup(self.desc, b["indices"], b["offsets"], self.B,
-                                                     b["per_sample_weights"], ws=ws,
-                                                     dev_status=self.status, stream=self.side)
+        elif self.dedup:  # the virtual batch's bounds come back (the count stays on the device)
+            key = ("pland", i % len(self.batches), i % len(self.wss))
+            call = self.prepared.get(key)
+            if call is None:
+                call = self.prepared[key] = abi.prepare_plan_dedup(
+                    self.desc, b["indices"], b["offsets"], self.B, b["per_sample_weights"],
+                    ws=ws, dev_status=self.status, stream=self.side)
+            call[0]()
+            self.infos[i] = call[1]
         else:
             key = ("plan", i % len(self.batches), i % len(self.wss))
             call = self.prepared.get(key)
@@ -200,10 +206,19 @@ class TrainLoop:
                 self.desc, self.g, b["indices"], b["offsets"], self.B, w, cache=cv,
                 out=self.out, ws=ws, dev_status=self.status, stream=self.main)
             eps = 1e-10 if self.update == "adagrad" else 0.0
-            self.prepared[("bwd", bi, wi)] = abi.prepare_backward(
-                self.desc, self.g, b["indices"], b["offsets"], self.B, b["grad_out"],
-                update=self.update, lr=self.lr, eps=eps, aux=self.aux, aux_rows=self.aux_rows,
-                per_sample_weights=w, cache=cv, ws=ws, dev_status=self.status, stream=self.main)
+            if self.dedup:
+                self.prepared[("bwd", bi, wi)] = abi.prepare_backward_dedup(
+                    self.desc, self.g, b["indices"], b["offsets"], self.B, b["grad_out"],
+                    self.infos[i], update=self.update, lr=self.lr, aux=self.aux,
+                    per_sample_weights=w, ws=ws, dev_status=self.status, stream=self.main)
+            else:
+                self.prepared[("bwd", bi, wi)] = abi.prepare_backward(
+                    self.desc, self.g, b["indices"], b["offsets"], self.B, b["grad_out"],
+                    update=self.update, lr=self.lr, eps=eps, aux=self.aux,
+                    aux_rows=self.aux_rows, per_sample_weights=w, cache=cv, ws=ws,
+                    dev_status=self.status, stream=self.main)
+        if self.dedup:
+            self.infos.pop(i)  # (the prepared backward holds the bounds)
         fwd()
         if self.pipeline:
             self.cvs[i + self.ahead] = self._plan(i + self.ahead)
