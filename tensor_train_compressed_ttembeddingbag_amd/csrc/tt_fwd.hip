@@ -33,9 +33,13 @@ namespace ttb {
 template <int RP>
 struct FwdLds {
   static constexpr int LD = RP + 4;  // row pitch of G2^T [r2][r1]: conflict-free 16-byte reads
+  // j3 pitch of the staged G3 slices [item][j3][r2]: with RP + 4 the sixteen lanes of a lane
+  // group (four items x four j3 in the matrix-core stage 2) read sixteen different bank
+  // quadruples instead of one
+  static constexpr int GS = RP + 4;
   static constexpr int INTS = META_INTS;
   __host__ __device__ static size_t g2_floats(int JB) { return (size_t)JB * RP * LD; }
-  __host__ __device__ static size_t g3_floats(int P, int q3) { return (size_t)P * q3 * RP; }
+  __host__ __device__ static size_t g3_floats(int P, int q3) { return (size_t)P * q3 * GS; }
   __host__ __device__ static size_t w_floats(int P, int D, int sw) { return sw ? (size_t)P * D : 0; }
   static size_t bytes(int JB, int P, int q3, int D, int sw) {
     return (g2_floats(JB) + g3_floats(P, q3) + w_floats(P, D, sw)) * 4 + INTS * 4;
@@ -103,13 +107,13 @@ template <int RP, bool DOT, bool MF>
 __device__ __forceinline__ void fwd_item(const DevArgs &a) {
   constexpr int KS = RP / 4;   // k-steps: lane group g covers r1 = g*KS + ks
   constexpr int NM = RP / 16;  // 16-row blocks of r2
-  constexpr int LD = FwdLds<RP>::LD, LRP = log2_rp<RP>();
+  constexpr int LD = FwdLds<RP>::LD, GS = FwdLds<RP>::GS, LRP = log2_rp<RP>();
   extern __shared__ float4 smem4[];
   float *smem = (float *)smem4;
   const int q1 = a.q1, q2 = a.q2, q3 = a.q3, R1 = a.R1, R2 = a.R2, D = a.D;
   const int JB = a.JBf, P = a.P, SW = DOT ? 1 : a.fwd_sw;
   float *sG2 = smem;                                            // [JB][r2 < RP][LD]
-  float *sG3 = sG2 + FwdLds<RP>::g2_floats(JB);                 // [item][j3][r2 < RP]
+  float *sG3 = sG2 + FwdLds<RP>::g2_floats(JB);                 // [item][j3][r2 < RP], pitch GS
   float *sW = sG3 + FwdLds<RP>::g3_floats(P, q3);               // [item][D]
   int *s_meta = (int *)(sW + FwdLds<RP>::w_floats(P, D, SW));  // [META_INTS]
   const WorkMeta &M = *(const WorkMeta *)s_meta;
@@ -193,7 +197,7 @@ __device__ __forceinline__ void fwd_item(const DevArgs &a) {
       const int i = base + u * WG;
       if (i < total3) {
         const int jr = fdiv(i, a.mq3), j3 = i - jr * q3, it = jr >> LRP, r2 = jr & (RP - 1);
-        sG3[(it * q3 + j3) * RP + r2] = r2 < R2 ? v[u] : 0.f;
+        sG3[(it * q3 + j3) * GS + r2] = r2 < R2 ? v[u] : 0.f;
       }
     }
   };
@@ -244,8 +248,8 @@ __device__ __forceinline__ void fwd_item(const DevArgs &a) {
                                    (i4 & (RP - 1)) * 4];  // (W3 = 4 RP)
     };
     auto st3 = [&](int i4, float4 x) {  // LDS [item][j3][r2]
-      float *d = &sG3[(size_t)(i4 >> LRP) * 4 * RP + (i4 & (RP - 1))];
-      d[0] = x.x; d[RP] = x.y; d[2 * RP] = x.z; d[3 * RP] = x.w;
+      float *d = &sG3[(size_t)(i4 >> LRP) * 4 * GS + (i4 & (RP - 1))];
+      d[0] = x.x; d[GS] = x.y; d[2 * GS] = x.z; d[3 * GS] = x.w;
     };
     float4 v2[SV], v3[SV];
 #pragma unroll
@@ -336,7 +340,7 @@ __device__ __forceinline__ void fwd_item(const DevArgs &a) {
           for (int nb = it0; nb < it1; nb += 4) {
             const int it = nb + s4;
             const bool okit = it < it1;
-            const float *g3p = sG3 + (size_t)(okit ? it : it0) * RP * 4 + jc * RP + 4 * g;
+            const float *g3p = sG3 + (size_t)(okit ? it : it0) * GS * 4 + jc * GS + 4 * g;
             f4 dW = zero4();
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
@@ -365,7 +369,7 @@ __device__ __forceinline__ void fwd_item(const DevArgs &a) {
         for (int kk = 0; kk < nk; ++kk) {
           const int it = ib + kk;
           const bool act = it < ie;
-          const float *g3 = sG3 + (size_t)(act ? it : 0) * RP * q3 + 4 * g;
+          const float *g3 = sG3 + (size_t)(act ? it : 0) * GS * q3 + 4 * g;
           // four j3 at a time: independent sums, then lane group g keeps j3 = j30 + g
           for (int j30 = 0; j30 < q3; j30 += 4) {
             float sacc[4];
@@ -375,7 +379,7 @@ __device__ __forceinline__ void fwd_item(const DevArgs &a) {
               float x = 0.f;
 #pragma unroll
               for (int m = 0; m < NM; ++m) {
-                const float4 gv = *(const float4 *)&g3[j3 * RP + 16 * m];
+                const float4 gv = *(const float4 *)&g3[j3 * GS + 16 * m];
                 x += acc[m][0] * gv.x + acc[m][1] * gv.y + acc[m][2] * gv.z + acc[m][3] * gv.w;
               }
               sacc[u] = x;
