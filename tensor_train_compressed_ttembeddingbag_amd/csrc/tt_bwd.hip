@@ -151,7 +151,8 @@ void k_bwd(DevArgs a) {
   // the first batch of everything in flight at once
   const int nj0 = min(JB, q2);
   const int nmb = (nP * q1 + 15) >> 4;
-  const int mb = placed_mblock<NW>(s_pl);  // one M-block per wave (P * q1 <= 16 * NW)
+  // one M-block per wave (P * q1 <= 16 * NW), by the slot the grouping gave it
+  const int mb = wave_uniform(M.mb_slot[placed_mblock<NW>(s_pl)]);
   const int per_item = RP * q3, total3 = nI * per_item, totalY = n_el * D;
   // i = (item * RP + r2) * q3 + j3 -> (item * RP + r2, j3)
   auto split3 = [&](int i, int &jr, int &j3) {

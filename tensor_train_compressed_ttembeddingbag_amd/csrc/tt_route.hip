@@ -813,7 +813,7 @@ hipError_t launch_wgrad_hits(const DevArgs &a, hipStream_t s) {
 constexpr int META_WAVES = 4;
 __global__ __launch_bounds__(64 * META_WAVES) void k_meta(DevArgs a) {
   __shared__ int s_m[META_WAVES][META_INTS];
-  __shared__ int s_cnt[META_WAVES][P_MAX + 8];  // gcnt [32] | mbf [8] as ints
+  __shared__ int s_cnt[META_WAVES][P_MAX + 16];  // gcnt [32] | mbf [8] | mbb [8] as ints
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wi = blockIdx.x * META_WAVES + w;
   const int plan = a.hdr[H_PLAN], nitems = a.hdr[H_NFWD];
@@ -869,9 +869,33 @@ __global__ __launch_bounds__(64 * META_WAVES) void k_meta(DevArgs a) {
   wave_lds_sync();
   if (lane < P_MAX) M.gcnt[lane] = (unsigned char)cnt[lane];
   if (lane < 8) {
+    const int mbb = max(max(cnt[4 * lane], cnt[4 * lane + 1]),
+                        max(cnt[4 * lane + 2], cnt[4 * lane + 3]));
     M.mbf[lane] = (unsigned char)cnt[P_MAX + lane];
-    M.mbb[lane] = (unsigned char)max(max(cnt[4 * lane], cnt[4 * lane + 1]),
-                                     max(cnt[4 * lane + 2], cnt[4 * lane + 3]));
+    M.mbb[lane] = (unsigned char)mbb;
+    cnt[P_MAX + 8 + lane] = mbb;
+  }
+  wave_lds_sync();
+  // The backward's M-blocks by placement slot.  Its waves take slots 0 .. 7, slots s and s + 4
+  // on one SIMD (placed_mblock), and every column ends at a workgroup barrier, so a column
+  // lasts as long as the busiest SIMD.  The item loop of an M-block runs mbb times: the
+  // heaviest M-blocks get the slots that have a SIMD of their own (nmb - 4 .. 3 when there
+  // are more than four), the others share one in pairs, the heaviest left with the lightest
+  // left.  Only the placement depends on this.
+  if (lane < 8) {  // lane k: M-block k, its rank by mbb (larger first, ties by index)
+    const int nmb = min((__popcll(r.mp) * a.q1 + 15) >> 4, 8);
+    int slot = lane;
+    if (lane < nmb) {
+      const int wk = cnt[P_MAX + 8 + lane];
+      int p = 0;
+      for (int k = 0; k < nmb; ++k) {
+        const int wo = cnt[P_MAX + 8 + k];
+        p += (wo > wk || (wo == wk && k < lane)) ? 1 : 0;
+      }
+      const int sh = max(nmb - 4, 0), al = min(nmb, 4), q = p - (al - sh);
+      slot = q < 0 ? sh + p : (q < sh ? q : (2 * sh - 1 - q) + 4);
+    }
+    M.mb_slot[slot] = (unsigned char)lane;
   }
   wave_lds_sync();
   if ((unsigned)item.w >= (unsigned)nitems) return;  // (the slots are a permutation)
