@@ -137,7 +137,8 @@ __device__ __forceinline__ void fwd_item(const DevArgs &a) {
   // the record's counts are the same for the whole workgroup: scalar registers
   const int grp = wave_uniform(M.grp), n_el = wave_uniform(M.n_el), nI = wave_uniform(M.nI);
   const int nP = wave_uniform(M.nP);
-  const int wp = placed_mblock<NW>(s_pl);  // this wave's M-block (MBW = 1)
+  // this wave's M-block (MBW = 1), by the slot the grouping gave it
+  const int wp = wave_uniform(M.mb_fslot[placed_mblock<NW>(s_pl)]);
   const int t = wave_uniform(M.t);
   const float *G2g = a.G2 + (size_t)grp * R1 * q2 * R2;  // slice [r1][j2][r2]
   const size_t W3 = (size_t)R2 * q3;

@@ -80,6 +80,7 @@ struct WorkMeta {
   unsigned char mbf[8];             // M-block (16 rows) -> most items of one of its pairs
   unsigned char mbb[8];             // M-block -> most gcnt of its four lane groups
   unsigned char mb_slot[8];         // backward: placement slot -> M-block (see k_meta)
+  unsigned char mb_fslot[8];        // forward: the same, by its stage-2 work
 };
 static_assert(sizeof(WorkMeta) <= META_INTS * 4, "work-item metadata too large");
 static_assert(H_SIZE0 + P_MAX + 1 <= H_WORDS, "header words");

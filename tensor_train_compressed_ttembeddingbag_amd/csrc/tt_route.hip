@@ -810,10 +810,27 @@ hipError_t launch_wgrad_hits(const DevArgs &a, hipStream_t s) {
 // read the metadata in one round of loads instead of working it out themselves, from the
 // workgroup slot the grouping gave the item.  It runs right after the grouping on the
 // same stream, so a plan marked valid has its metadata.
+// Slot of M-block k among nmb by weight w[0 .. nmb) (larger first, ties by index): the
+// heaviest get the slots with a SIMD of their own (sh .. al - 1), the others the shared
+// pairs (j, j + 4), the heaviest left in j and the lightest left in j + 4.  Slots >= nmb
+// keep their idle M-block.  (All eight weights are read at once.)
+__device__ __forceinline__ int weighted_slot(int k, int nmb, const int *w) {
+  int x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = w[i];
+  const int wk = w[k];
+  int p = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p += (i < nmb && (x[i] > wk || (x[i] == wk && i < k))) ? 1 : 0;
+  const int sh = max(nmb - 4, 0), al = min(nmb, 4), q = p - (al - sh);
+  if (k >= nmb) return k;
+  return q < 0 ? sh + p : (q < sh ? q : (2 * sh - 1 - q) + 4);
+}
+
 constexpr int META_WAVES = 4;
 __global__ __launch_bounds__(64 * META_WAVES) void k_meta(DevArgs a) {
   __shared__ int s_m[META_WAVES][META_INTS];
-  __shared__ int s_cnt[META_WAVES][P_MAX + 16];  // gcnt [32] | mbf [8] | mbb [8] as ints
+  __shared__ int s_cnt[META_WAVES][P_MAX + 24];  // gcnt [32] | mbf [8] | mbb [8] | fwd [8]
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wi = blockIdx.x * META_WAVES + w;
   const int plan = a.hdr[H_PLAN], nitems = a.hdr[H_NFWD];
@@ -873,29 +890,26 @@ __global__ __launch_bounds__(64 * META_WAVES) void k_meta(DevArgs a) {
                         max(cnt[4 * lane + 2], cnt[4 * lane + 3]));
     M.mbf[lane] = (unsigned char)cnt[P_MAX + lane];
     M.mbb[lane] = (unsigned char)mbb;
-    cnt[P_MAX + 8 + lane] = mbb;
+    cnt[P_MAX + 8 + lane] = mbb;  // backward weight
+    // forward weight: matrix-core stage 2 once per four items of the M-block (q1 = q3 = 4),
+    // else the VALU stage 2's mbf
+    const int nP = __popcll(r.mp), ppm = 16 >> a.lq1;  // pairs per M-block
+    const int p0 = min(lane * ppm, nP), p1 = min(p0 + ppm, nP);
+    cnt[P_MAX + 16 + lane] = (a.q1 == 4 && a.q3 == 4) ? (M.pr_it[p1] - M.pr_it[p0] + 3) >> 2
+                                                       : cnt[P_MAX + lane];
   }
   wave_lds_sync();
-  // The backward's M-blocks by placement slot.  Its waves take slots 0 .. 7, slots s and s + 4
-  // on one SIMD (placed_mblock), and every column ends at a workgroup barrier, so a column
-  // lasts as long as the busiest SIMD.  The item loop of an M-block runs mbb times: the
-  // heaviest M-blocks get the slots that have a SIMD of their own (nmb - 4 .. 3 when there
-  // are more than four), the others share one in pairs, the heaviest left with the lightest
-  // left.  Only the placement depends on this.
-  if (lane < 8) {  // lane k: M-block k, its rank by mbb (larger first, ties by index)
+  // M-blocks by placement slot.  The contraction kernels' waves take slots 0 .. 7, slots s
+  // and s + 4 on one SIMD (placed_mblock), and a workgroup waits for its slowest SIMD (the
+  // backward at every column's barrier, the forward before pooling).  The weights above: the
+  // backward's item loop runs mbb times, the forward's stage 2 as noted.  The heaviest
+  // M-blocks get the slots that have a SIMD of their own (nmb - 4 .. 3 when there are more
+  // than four), the others share one in pairs, the heaviest left with the lightest left.
+  // Only the placement depends on this.
+  if (lane < 8) {
     const int nmb = min((__popcll(r.mp) * a.q1 + 15) >> 4, 8);
-    int slot = lane;
-    if (lane < nmb) {
-      const int wk = cnt[P_MAX + 8 + lane];
-      int p = 0;
-      for (int k = 0; k < nmb; ++k) {
-        const int wo = cnt[P_MAX + 8 + k];
-        p += (wo > wk || (wo == wk && k < lane)) ? 1 : 0;
-      }
-      const int sh = max(nmb - 4, 0), al = min(nmb, 4), q = p - (al - sh);
-      slot = q < 0 ? sh + p : (q < sh ? q : (2 * sh - 1 - q) + 4);
-    }
-    M.mb_slot[slot] = (unsigned char)lane;
+    M.mb_slot[weighted_slot(lane, nmb, cnt + P_MAX + 8)] = (unsigned char)lane;
+    M.mb_fslot[weighted_slot(lane, nmb, cnt + P_MAX + 16)] = (unsigned char)lane;
   }
   wave_lds_sync();
   if ((unsigned)item.w >= (unsigned)nitems) return;  // (the slots are a permutation)
