@@ -545,8 +545,10 @@ void k_bwd(DevArgs a) {
       // [r2][r1] (row pitch LD), so a lane's four r1 = 16mr + 4g .. +3 of one r2 move as
       // one 16-byte vector.
       lds_barrier();  // the transpose tiles (aliased by the slots) are free
-      for (int rr = 0; rr < NW / nred; ++rr) {
-        if (mb / nred == rr) {
+      // (round 0 fills every slot, idle M-blocks with zeros; a later round runs only for the
+      // M-blocks with rows, and not at all when there are none: nmb is the workgroup's)
+      for (int rr = 0; rr < NW / nred && (rr == 0 || rr * nred < nmb); ++rr) {
+        if (mb / nred == rr && (rr == 0 || mb < nmb)) {
           float *slot = sRed + (size_t)(mb % nred) * RP * LD;
           // the slot's partial sums of one row of tiles (all of them up to RP = 32) read
           // before any is written
