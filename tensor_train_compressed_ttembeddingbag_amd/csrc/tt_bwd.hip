@@ -545,10 +545,11 @@ void k_bwd(DevArgs a) {
       // [r2][r1] (row pitch LD), so a lane's four r1 = 16mr + 4g .. +3 of one r2 move as
       // one 16-byte vector.
       lds_barrier();  // the transpose tiles (aliased by the slots) are free
-      // (round 0 fills every slot, idle M-blocks with zeros; a later round runs only for the
-      // M-blocks with rows, and not at all when there are none: nmb is the workgroup's)
-      for (int rr = 0; rr < NW / nred && (rr == 0 || rr * nred < nmb); ++rr) {
-        if (mb / nred == rr && (rr == 0 || mb < nmb)) {
+      const int nsl = min(nmb, nred);  // slots in use
+      // (only the M-blocks with rows take part: the first min(nmb, nred) slots, and a round
+      // only when an M-block has it; nmb is the workgroup's)
+      for (int rr = 0; rr < NW / nred && rr * nred < nmb; ++rr) {
+        if (mb / nred == rr && mb < nmb) {
           float *slot = sRed + (size_t)(mb % nred) * RP * LD;
           // the slot's partial sums of one row of tiles (all of them up to RP = 32) read
           // before any is written
@@ -584,15 +585,15 @@ void k_bwd(DevArgs a) {
         const int r2 = t4 & (RP - 1), r1 = (t4 >> LRP) * 4;
         constexpr int KF = F44 ? 4 : 1;  // slots in flight (the F44 instances have the room)
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int k0 = 0; k0 < nred; k0 += KF) {
+        for (int k0 = 0; k0 < nsl; k0 += KF) {
           float4 o[KF];
 #pragma unroll
           for (int k = 0; k < KF; ++k)
-            if (k0 + k < nred)
+            if (k0 + k < nsl)
               o[k] = *(const float4 *)&sRed[(size_t)(k0 + k) * RP * LD + r2 * LD + r1];
 #pragma unroll
           for (int k = 0; k < KF; ++k)
-            if (k0 + k < nred) {
+            if (k0 + k < nsl) {
               if (k0 + k == 0) acc = o[0];
               else { acc.x += o[k].x; acc.y += o[k].y; acc.z += o[k].z; acc.w += o[k].w; }
             }
