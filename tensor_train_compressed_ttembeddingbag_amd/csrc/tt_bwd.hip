@@ -688,9 +688,10 @@ hipError_t launch_bwd(const DevArgs &a, int RP, size_t lds, hipStream_t s) {
 // Blocks of 256 threads, three kinds of task:
 //  * one block = one core-1 slice (t, i1) or core-3 slice (t, i3): the slice's segment
 //    of the (t,i1)- / (t,i3)-ordered element list names, through the links, the final-
-//    order positions of its partials; they are listed in segment order, then summed by
-//    8 row groups (row group k takes rows k, k+8, ...; a fixed assignment), the group
-//    sums added in group order, and SGD applied;
+//    order positions of its partials; they are listed in segment order (up to 1024
+//    positions per pass), then summed by 8 row groups (row group k takes the pass's rows
+//    k, k+8, ...; a fixed assignment), the group sums added in group order, and SGD
+//    applied;
 //  * one block = one column chunk of a core-2 slice (t, i2): the dG2 partials of the
 //    group's work items are summed in item order, then the update;
 //  * four waves = four 64-position pieces of the cache-hit region: a cache run (one
@@ -699,6 +700,7 @@ hipError_t launch_bwd(const DevArgs &a, int RP, size_t lds, hipStream_t s) {
 //    position order.
 constexpr int SEG_T = 256;
 constexpr int SEG_ROWS = 8;   // partial rows in flight per thread
+constexpr int SEG_LPT = 4;    // core-1/3 slices: links per thread per pass
 constexpr int SEG_CW = 4;     // core-2 slices: columns per thread,
 constexpr int SEG_IB = 8;     // work items in flight,
 constexpr int SEG_COLS = SEG_T * SEG_CW;  // and columns per block
@@ -708,8 +710,8 @@ __host__ __device__ inline int seg_chunks(const DevArgs &a) {
 
 template <int UPD>
 __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
-  __shared__ int s_rows[SEG_T];
-  __shared__ int s_wc[SEG_T / 64 + 1];
+  __shared__ int s_rows[SEG_T * SEG_LPT];
+  __shared__ int s_wc[SEG_LPT][SEG_T / 64];
   __shared__ float s_red[SEG_T * 4];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int nA = a.T * a.p1, nC = a.T * a.p3, G = a.T * a.p2;
@@ -752,19 +754,34 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
     for (int c0 = 0; c0 < W; c0 += LPR * VEC) {  // column blocks (one unless W > 1024)
       const int col = c0 + cl * VEC;
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int p0 = beg; p0 < end; p0 += SEG_T) {
-        // the chunk's partial rows, in segment order
-        const int lk = p0 + tid < end ? link[p0 + tid] : -1;
-        const unsigned long long m = __ballot(lk >= 0);
-        const unsigned long long lt = (1ull << lane) - 1ull;
-        if (lane == 0) s_wc[w] = __popcll(m);
-        __syncthreads();
-        int before = 0, n = 0;
-        for (int v = 0; v < SEG_T / 64; ++v) {
-          before += v < w ? s_wc[v] : 0;
-          n += s_wc[v];
+      for (int p0 = beg; p0 < end; p0 += SEG_T * SEG_LPT) {
+        // the pass's partial rows, in segment order (thread t takes positions
+        // p0 + u SEG_T + t, all loads of the pass in flight at once)
+        int lk[SEG_LPT];
+#pragma unroll
+        for (int u = 0; u < SEG_LPT; ++u) {
+          const int p = p0 + u * SEG_T + tid;
+          lk[u] = p < end ? link[p] : -1;
         }
-        if (lk >= 0) s_rows[before + __popcll(m & lt)] = lk;
+        const unsigned long long lt = (1ull << lane) - 1ull;
+        unsigned long long m[SEG_LPT];
+#pragma unroll
+        for (int u = 0; u < SEG_LPT; ++u) {
+          m[u] = __ballot(lk[u] >= 0);
+          if (lane == 0) s_wc[u][w] = __popcll(m[u]);
+        }
+        __syncthreads();
+        int n = 0;
+#pragma unroll
+        for (int u = 0; u < SEG_LPT; ++u) {
+          int before = n, tot = 0;
+          for (int v = 0; v < SEG_T / 64; ++v) {
+            before += v < w ? s_wc[u][v] : 0;
+            tot += s_wc[u][v];
+          }
+          if (lk[u] >= 0) s_rows[before + __popcll(m[u] & lt)] = lk[u];
+          n += tot;
+        }
         __syncthreads();
         if (rg < NRG && col < W) {
           for (int k0 = rg; k0 < n; k0 += NRG * SEG_ROWS) {
