@@ -852,9 +852,11 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
       float v[SEG_IB][SEG_CW];
 #pragma unroll
       for (int k = 0; k < SEG_IB; ++k) {
-        const float *src = a.part2 + (size_t)min(it0 + k, i1 - 1) * slice2;
+        if (it0 + k < i1) {  // (uniform: only the items there are)
+          const float *src = a.part2 + (size_t)(it0 + k) * slice2;
 #pragma unroll
-        for (int u = 0; u < SEG_CW; ++u) v[k][u] = src[min(c0 + u * SEG_T, slice2 - 1)];
+          for (int u = 0; u < SEG_CW; ++u) v[k][u] = src[min(c0 + u * SEG_T, slice2 - 1)];
+        }
       }
 #pragma unroll
       for (int k = 0; k < SEG_IB; ++k)
