@@ -788,13 +788,11 @@ __global__ __launch_bounds__(SEG_T) void k_seg(DevArgs a) {
             float4 v[SEG_ROWS];
 #pragma unroll
             for (int u = 0; u < SEG_ROWS; ++u) {
-              const int k = min(k0 + u * NRG, n - 1);
-              const float *row = part + (size_t)s_rows[k] * W + col;
-              if (VEC == 4) {
-                v[u] = *(const float4 *)row;
-              } else {
-                v[u].x = row[0];
-                v[u].y = v[u].z = v[u].w = 0.f;
+              v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+              if (k0 + u * NRG < n) {  // only the rows there are
+                const float *row = part + (size_t)s_rows[k0 + u * NRG] * W + col;
+                if (VEC == 4) v[u] = *(const float4 *)row;
+                else v[u].x = row[0];
               }
             }
 #pragma unroll
