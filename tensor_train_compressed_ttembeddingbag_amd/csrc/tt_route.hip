@@ -268,7 +268,8 @@ __device__ __forceinline__ int item_slot(int j, int n, int C) {
 
 // Work items from the group table gs[0..binsB] (starts of the (t,i2) bins in the final
 // order, gs[binsB] = nnz; LDS or global): a miss group of m elements becomes ceil(m / P)
-// items of near-equal size (at most P positions each), numbered group by group; also
+// items (two near-equal halves, or P positions each but the last when there are three or
+// more), numbered group by group; also
 // grp_off, chunk_pre and the header words.  Every block of a launch may call it with
 // its own part: all compute the item numbering (cnt: G + 1 ints of scratch, LDS or
 // global), part k of nparts writes the entries of the groups g = k (mod nparts).
@@ -291,17 +292,21 @@ static __device__ void build_items(const DevArgs &a, const int *gs, int *cnt, in
   }
   __threadfence_block();
   __syncthreads();
-  // items per size (a group of m elements in nc items has m mod nc items of size
-  // m / nc + 1, the rest of size m / nc), then the number of items larger than each size
+  // items per size (piece_cut below), then the number of items larger than each size
   __shared__ int s_above[P_MAX + 2];
   for (int k = tid; k < P_MAX + 2; k += nt) s_above[k] = 0;
   __syncthreads();
   for (int g = tid; g < G; g += nt) {
     const int nc = cnt[g + 1] - cnt[g], m = gs[g + 1] - gs[g];
     if (nc == 0) continue;
-    const int q = m / nc, r = m - q * nc;
-    if (r) atomicAdd(&s_above[q + 1], r);
-    if (nc > r) atomicAdd(&s_above[q], nc - r);
+    if (nc <= 2) {  // near-equal: m mod nc of size m / nc + 1, the rest m / nc
+      const int q = m / nc, r = m - q * nc;
+      if (r) atomicAdd(&s_above[q + 1], r);
+      if (nc > r) atomicAdd(&s_above[q], nc - r);
+    } else {  // nc - 1 of P and the rest
+      atomicAdd(&s_above[a.P], nc - 1);
+      atomicAdd(&s_above[m - (nc - 1) * a.P], 1);
+    }
   }
   __syncthreads();
   if (tid == 0) {
@@ -320,12 +325,10 @@ static __device__ void build_items(const DevArgs &a, const int *gs, int *cnt, in
     const int first = cnt[g], nc = cnt[g + 1] - first;
     const int gb = gs[g], m = gs[g + 1] - gb;
     if (nc == 0) continue;
-    // item c spans [m c / nc, m (c + 1) / nc) of the group; m c / nc = q c + r c / nc
+    // piece_cut: a group in two items is cut in near-equal halves; a larger one into items of
+    // P positions and the rest (fewer partly filled M-blocks where groups are large)
     const int q = m / nc, r = m - q * nc;
-    auto cut = [&](int c) {
-      return gb + q * c + (nc < 65536 ? (int)((unsigned)r * (unsigned)c / (unsigned)nc)
-                                      : (int)((long long)r * c / nc));
-    };
+    auto cut = [&](int c) { return nc <= 2 ? gb + q * c + (r * c) / nc : gb + c * a.P; };
     int lo = gb;
     for (int c = 0; c < nc; ++c) {
       const int hi = c + 1 < nc ? cut(c + 1) : gb + m;
