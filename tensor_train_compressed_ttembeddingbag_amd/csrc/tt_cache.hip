@@ -53,20 +53,32 @@ static __device__ int map_find(const long long *mkeys, const int *mslot, long lo
 }
 
 // slot lookup + frequency count.  Duplicated keys inside a wave are merged first
-// (match on 16 hash bits with ballots, confirmed against the group leader's key), so
-// a hot index costs one atomic per wave instead of one per occurrence.
-__global__ __launch_bounds__(256) void k_cache_lookup(const int64_t *idx, int nnz, int64_t E,
-                                                       long long *hkeys, int *hcnt, long long H,
-                                                       const long long *mkeys, const int *mslot,
-                                                       long long M, int32_t *slot_out,
-                                                       int count_freq, int32_t *status) {
-  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+// (match on 16 hash bits with ballots, confirmed against the group leader's key), then the
+// block's waves in a small LDS table (one entry per distinct key of the block), so a hot
+// index costs one atomic on the count table per 1024 positions instead of one per
+// occurrence (same-address atomics serialise in the L2).  The counts are integer sums:
+// the same whatever the merging.
+constexpr int LK_T = 1024;   // positions per lookup block (16 waves)
+constexpr int LK_HT = 2048;  // its merge table: a power of two, at least twice LK_T
+__global__ __launch_bounds__(LK_T) void k_cache_lookup(const int64_t *idx, int nnz, int64_t E,
+                                                        long long *hkeys, int *hcnt, long long H,
+                                                        const long long *mkeys, const int *mslot,
+                                                        long long M, int32_t *slot_out,
+                                                        int count_freq, int32_t *status) {
+  __shared__ long long s_key[LK_HT];
+  __shared__ int s_add[LK_HT];
+  const int n = blockIdx.x * LK_T + threadIdx.x;
   const int lane = threadIdx.x & 63;
   const bool in = n < nnz;
   const long long key = in ? (long long)idx[n] : -1;
   const bool valid = in && key >= 0 && key < E;
-  if (count_freq) {
-    const unsigned h16 = (unsigned)(mix64((unsigned long long)key) >> 48);
+  if (count_freq) {  // (uniform)
+    for (int i = threadIdx.x; i < LK_HT; i += LK_T) {
+      s_key[i] = EMPTY_KEY;
+      s_add[i] = 0;
+    }
+    const unsigned long long hk = mix64((unsigned long long)key);
+    const unsigned h16 = (unsigned)(hk >> 48);
     unsigned long long m = __ballot(valid);
     for (int b = 0; b < 16; ++b) {
       const bool bit = valid && ((h16 >> b) & 1u);
@@ -81,10 +93,27 @@ __global__ __launch_bounds__(256) void k_cache_lookup(const int64_t *idx, int nn
       if (lane == leader) add = __popcll(same);
       else if (key != lk) add = 1;
     }
-    if (add > 0) {
-      const long long e = count_slot(hkeys, H, key);
+    __syncthreads();  // the table is clear
+    if (add > 0) {    // at most LK_T keys in LK_HT entries: a free entry is always found
+      unsigned h = (unsigned)hk & (LK_HT - 1);
+      for (;;) {
+        const long long prev = (long long)atomicCAS((unsigned long long *)&s_key[h],
+                                                    (unsigned long long)EMPTY_KEY,
+                                                    (unsigned long long)key);
+        if (prev == EMPTY_KEY || prev == key) {
+          atomicAdd(&s_add[h], add);
+          break;
+        }
+        h = (h + 1) & (LK_HT - 1);
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < LK_HT; i += LK_T) {
+      const long long k2 = s_key[i];
+      if (k2 == EMPTY_KEY) continue;
+      const long long e = count_slot(hkeys, H, k2);
       if (e < 0) { if (status) atomicOr(status, TT_DEV_HASH_FULL); }
-      else atomicAdd(&hcnt[e], add);
+      else atomicAdd(&hcnt[e], s_add[i]);
     }
   }
   if (in) slot_out[n] = valid ? map_find(mkeys, mslot, M, key) : -1;
@@ -293,7 +322,8 @@ hipError_t cache_lookup_launch(const int64_t *idx, int nnz, int64_t E, long long
                                long long M, int32_t *slot_out, int count_freq, int32_t *status,
                                hipStream_t s) {
   if (nnz > 0) {
-    tt_launch(K_CACHE_LOOKUP, k_cache_lookup, dim3((nnz + 255) / 256), dim3(256), 0, s, idx, nnz, E,
+    tt_launch(K_CACHE_LOOKUP, k_cache_lookup, dim3((nnz + LK_T - 1) / LK_T), dim3(LK_T), 0, s,
+              idx, nnz, E,
                        hkeys, hcnt, H, mkeys, mslot, M, slot_out, count_freq, status);
   }
   return hipGetLastError();
