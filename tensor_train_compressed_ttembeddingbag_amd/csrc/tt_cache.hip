@@ -40,12 +40,17 @@ static __device__ long long count_slot(long long *keys, long long H, long long k
   return -1;
 }
 
+// slot of key in the index -> slot map (M a power of two), or -1.  h: the key's home
+// entry; k, sl: that entry's key and slot, loaded by the caller together with its other
+// loads (later probes load an entry's key and slot together).
 static __device__ int map_find(const long long *mkeys, const int *mslot, long long M,
-                               long long key) {
-  long long h = (long long)(mix64((unsigned long long)key) & (unsigned long long)(M - 1));
+                               long long key, long long h, long long k, int sl) {
   for (long long probe = 0; probe < M; ++probe) {
-    const long long k = mkeys[h];
-    if (k == key) return mslot[h];
+    if (probe > 0) {
+      k = mkeys[h];
+      sl = mslot[h];
+    }
+    if (k == key) return sl;
     if (k == EMPTY_KEY) return -1;
     h = (h + 1) & (M - 1);
   }
@@ -72,12 +77,20 @@ __global__ __launch_bounds__(LK_T) void k_cache_lookup(const int64_t *idx, int n
   const bool in = n < nnz;
   const long long key = in ? (long long)idx[n] : -1;
   const bool valid = in && key >= 0 && key < E;
+  // the slot map's first probe goes out now and is looked at after the counting
+  const unsigned long long hk = mix64((unsigned long long)key);
+  const long long hm = (long long)(hk & (unsigned long long)(M - 1));
+  long long km = EMPTY_KEY;
+  int sm = -1;
+  if (valid) {
+    km = mkeys[hm];
+    sm = mslot[hm];
+  }
   if (count_freq) {  // (uniform)
     for (int i = threadIdx.x; i < LK_HT; i += LK_T) {
       s_key[i] = EMPTY_KEY;
       s_add[i] = 0;
     }
-    const unsigned long long hk = mix64((unsigned long long)key);
     const unsigned h16 = (unsigned)(hk >> 48);
     unsigned long long m = __ballot(valid);
     for (int b = 0; b < 16; ++b) {
@@ -116,7 +129,7 @@ __global__ __launch_bounds__(LK_T) void k_cache_lookup(const int64_t *idx, int n
       else atomicAdd(&hcnt[e], s_add[i]);
     }
   }
-  if (in) slot_out[n] = valid ? map_find(mkeys, mslot, M, key) : -1;
+  if (in) slot_out[n] = valid ? map_find(mkeys, mslot, M, key, hm, km, sm) : -1;
 }
 
 // populate, step 1: compact the used count entries into sortable 64-bit keys
