@@ -367,15 +367,20 @@ static __device__ void tile_place_ia(const DevArgs &a, Rec el[RB / NT], int pA[R
   }
 }
 
-// Final pass of a tile of orderA: its records placed by (t,i2) into the final order.
+// The records of tile blk of orderA (positions past the end repeat the last record).
 template <int NT>
-static __device__ void tile_final(const DevArgs &a, int blk, unsigned short *lds_c,
-                                  const int *start, int ss, int so) {
-  Rec x[RB / NT];
-  int d[RB / NT], pos[RB / NT];
-  const int n = elem_count(a);
+static __device__ void tile_load(const DevArgs &a, int blk, Rec x[RB / NT]) {
 #pragma unroll
   for (int r = 0; r < RB / NT; ++r) x[r] = load_rec(a.rec, min(tile_pos<NT>(blk, r), a.nnz - 1));
+}
+
+// Final pass of a tile of orderA (its records x, from tile_load): placed by (t,i2) into
+// the final order.
+template <int NT>
+static __device__ void tile_final(const DevArgs &a, int blk, unsigned short *lds_c,
+                                  const int *start, int ss, int so, const Rec x[RB / NT]) {
+  int d[RB / NT], pos[RB / NT];
+  const int n = elem_count(a);
 #pragma unroll
   for (int r = 0; r < RB / NT; ++r) d[r] = tile_pos<NT>(blk, r) < n ? x[r].dB : -1;
   tile_place<NT>(d, pos, lds_c, a.binsB, start, ss, so);
@@ -530,6 +535,7 @@ static __device__ void tile_starts2(const int *h0, int nb0, int *start0, int *gs
 // LDS of the one-launch kernel (ints, sized by the call's bins and tiles), phases overlap:
 //   decode:  s_off [ROUTE_MAX_BAGS] | hist [max(binsI3, binsA)]
 //   passes:  rank counts (u16, waves x bins) | startI, gsI | startA, gsA | (t,i2) cells
+//            (the tiles' matrix, or this tile's row)
 struct CoopLds {
   int c, sI, gI, sA, gA, cell, total;
 };
@@ -543,7 +549,8 @@ __host__ __device__ inline CoopLds coop_lds(const DevArgs &a) {
   L.sA = L.gI + nX;
   L.gA = L.sA + nY;
   L.cell = L.gA + nY;
-  const int cells = a.binsB * a.nblk <= COOP_LDS_CELLS ? a.binsB * a.nblk : 0;
+  // the [tile][bin] (t,i2) counts, or one row of them
+  const int cells = a.binsB * a.nblk <= COOP_LDS_CELLS ? a.binsB * a.nblk : a.binsB;
   L.total = max(L.cell + cells, ROUTE_MAX_BAGS + max(a.binsI3, a.binsA));
   return L;
 }
@@ -564,8 +571,16 @@ __global__ __launch_bounds__(CT) void k_route_coop(DevArgs a) {
   // that gives up at a barrier then leaves no plan that a later call could take for whole)
   if (blk == 0 && tid == 0) a.hdr[H_PLAN] = (int)~a.plan_fp;
 
+  // (t,i2) counts per orderA tile: when that [tile][bin] matrix fits in LDS, each block
+  // gathers its elements' contributions there and adds them to histB (cleared first)
+  // before the second barrier; otherwise (most of a block's elements would need an atomic
+  // of their own) a third barrier follows the placing, and each block counts its own
+  // orderA tile and writes its row of histB whole
+  const bool in_lds = a.binsB * nblk <= COOP_LDS_CELLS;
+
   // ---- histB cleared for the atomics; decode; (t,i3) and (t,i1) histograms of the tile
-  for (int k = blk * CT + tid; k < a.binsB * nblk; k += nblk * CT) st_w<true>(a.histB + k, 0);
+  if (in_lds)
+    for (int k = blk * CT + tid; k < a.binsB * nblk; k += nblk * CT) st_w<true>(a.histB + k, 0);
   if (blk == 0)
     for (int k = tid; k <= P_MAX; k += CT) st_w<true>(a.hdr + H_SIZE0 + k, 0);
   tile_decode<CT>(a, blk, lds_i, s_red, s_b, el);
@@ -589,24 +604,29 @@ __global__ __launch_bounds__(CT) void k_route_coop(DevArgs a) {
     for (int d = tid; d < a.binsI3; d += CT) a.segI3[d] = gsI[d];
     for (int d = tid; d < a.binsA; d += CT) a.segA[d] = gsA[d];
   }
-  // (t,i2) counts per orderA tile: gathered in LDS when the matrix fits, else added to
-  // histB directly
-  const bool in_lds = a.binsB * nblk <= COOP_LDS_CELLS;
   if (in_lds)
     for (int i = tid; i < a.binsB * nblk; i += CT) cellB[i] = 0;
   int pA[RB / CT];
   tile_place_ia<CT>(a, el, pA, lds_c, startI, startA, 1, 0);
+  if (in_lds) {
 #pragma unroll
-  for (int r = 0; r < RB / CT; ++r)
-    if (pA[r] >= 0) {
-      if (in_lds) atomicAdd(&cellB[el[r].dB * nblk + pA[r] / RB], 1);
-      else atomicAdd(&a.histB[(pA[r] / RB) * a.binsB + el[r].dB], 1);
-    }
-  __syncthreads();
-  if (in_lds)
+    for (int r = 0; r < RB / CT; ++r)
+      if (pA[r] >= 0) atomicAdd(&cellB[el[r].dB * nblk + pA[r] / RB], 1);
+    __syncthreads();
     for (int i = tid; i < a.binsB * nblk; i += CT)
       if (cellB[i]) atomicAdd(&a.histB[(i % nblk) * a.binsB + i / nblk], cellB[i]);
+  }
   if (!grid_sync<true>(a, 2)) return;
+  Rec x[RB / CT];  // this block's tile of orderA
+  tile_load<CT>(a, blk, x);
+  if (!in_lds) {
+    const int n = elem_count(a);
+    int d[RB / CT];
+#pragma unroll
+    for (int r = 0; r < RB / CT; ++r) d[r] = tile_pos<CT>(blk, r) < n ? x[r].dB : -1;
+    tile_hist<CT, true, true>(d, lds_i + L.cell, a.binsB, a.histB, blk);
+    if (!grid_sync<false>(a, 3)) return;
+  }
 
   // ---- work items (each block writes its share); final order: the orderA tiles placed
   //      by (t,i2)
@@ -614,7 +634,7 @@ __global__ __launch_bounds__(CT) void k_route_coop(DevArgs a) {
   if (tid == 0) gsI[a.binsB] = elem_count(a);
   __syncthreads();
   build_items(a, gsI, startA, s_scan, blk, nblk);
-  tile_final<CT>(a, blk, lds_c, startI, 1, 0);
+  tile_final<CT>(a, blk, lds_c, startI, 1, 0, x);
   if (blk == 0 && tid == 0) a.hdr[H_PLAN] = (int)a.plan_fp;
 }
 
@@ -696,7 +716,9 @@ __global__ __launch_bounds__(RT) void k_route_b(DevArgs a) {
 __global__ __launch_bounds__(RT) void k_route_c(DevArgs a) {
   a.epoch = launch_tag(a, a.hdr + H_REPOCH);  // this grouping's tag
   extern __shared__ unsigned short lds_c[];  // [4][binsB]
-  tile_final<RT>(a, blockIdx.x, lds_c, a.histB, a.nblk, blockIdx.x);
+  Rec x[RB / RT];
+  tile_load<RT>(a, blockIdx.x, x);
+  tile_final<RT>(a, blockIdx.x, lds_c, a.histB, a.nblk, blockIdx.x, x);
   if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr[H_PLAN] = (int)a.plan_fp;
 }
 

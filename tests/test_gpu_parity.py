@@ -195,22 +195,26 @@ def test_many_tiles_use_the_three_kernel_grouping():
     _full_parity(wl, b)
 
 
-@pytest.mark.parametrize("bags", [None, 4000], ids=["one-block", "multi-block"])
-def test_route_with_cache_slots_bit_exact(bags):
+@pytest.mark.parametrize("bags,csize", [(None, 700), (4000, 700), (4000, 400_000)],
+                         ids=["one-block", "multi-block", "multi-block-wide"])
+def test_route_with_cache_slots_bit_exact(bags, csize):
     """Cache slots, skipped invalid indices; small batches are grouped by one
-    workgroup, larger ones by the multi-block passes: both must give the same order."""
+    workgroup, larger ones by the multi-block passes: both must give the same order.
+    With 400,000 slots (782 hit bins of the (t,i2) digit over 18 tiles) the per-tile
+    (t,i2) counts no longer fit in the multi-block kernel's LDS, and each tile counts
+    its own elements after a third barrier instead."""
     wl = SMALL[1]
-    _say("case route+cache", bags)
+    _say("case route+cache", bags, csize)
     b = W.make_batch(wl, 3, bags_per_table=bags)
     rng = np.random.Generator(np.random.PCG64(5))
     n = len(b["indices"])
-    slots = np.where(rng.random(n) < 0.4, rng.integers(0, 700, n), -1).astype(np.int32)
+    slots = np.where(rng.random(n) < 0.4, rng.integers(0, csize, n), -1).astype(np.int32)
     b["indices"][rng.random(n) < 0.05] = wl.E + 3  # invalid indices are skipped
     d = to_dev(b)
     desc = abi.make_desc(wl.p, wl.q, wl.ranks, wl.E, wl.num_tables)
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
     order, goff = abi.tt_bag_route(desc, d["indices"], d["offsets"], b["num_bags"],
-                                   slots=torch.from_numpy(slots).cuda(), cache_size=700,
+                                   slots=torch.from_numpy(slots).cuda(), cache_size=csize,
                                    dev_status=st)
     ref, counts = oracle.route_order(wl.p, wl.E, 1, b["num_bags"], b["indices"], b["offsets"], slots)
     assert np.array_equal(order.cpu().numpy()[:len(ref)], ref)
