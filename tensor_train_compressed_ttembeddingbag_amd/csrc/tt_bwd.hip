@@ -699,7 +699,7 @@ hipError_t launch_bwd(const DevArgs &a, int RP, size_t lds, hipStream_t s) {
 //    run's fragments (its first position, then every piece start inside the run) in
 //    position order.
 constexpr int SEG_T = 256;
-constexpr int SEG_ROWS = 8;   // partial rows in flight per thread
+constexpr int SEG_ROWS = 4;   // partial rows in flight per thread
 constexpr int SEG_LPT = 4;    // core-1/3 slices: links per thread per pass
 constexpr int SEG_CW = 4;     // core-2 slices: columns per thread,
 constexpr int SEG_IB = 8;     // work items in flight,
